@@ -1,0 +1,219 @@
+"""Seeded synthetic inputs for the NVFP4 mixture-of-experts layer.
+
+This module only draws random inputs of the right shapes, dtypes and
+distributions; it holds none of the layer's arithmetic.  Both the HIP path and
+the CPU oracle are fed from it (it is the only code they share).
+
+Distributions (per workload):
+  * activations x: bf16 draws of N(0, 1) (fp32 draw, converted by torch);
+  * router weight: fp32 N(0, 0.02) (0.02 is the standard deviation), [E, H];
+  * router bias: absent, or +hot_bias on ``hot_experts`` experts picked at random;
+  * expert codes: uniform random bytes (two uniform 4-bit e2m1 codes per byte);
+  * block scales: one e4m3 byte per 16 K-elements, uniform over the encodings
+    of 2^-4 .. 2^2 (exponent field n + 7, mantissa 0);
+  * per-tensor global scales (gate, up, down) all equal to ``global_scale``;
+  * shared-expert gate vector: bf16 draws of N(0, 0.02).
+
+Canonical weight layout (what ``ft_nvfp4_repack`` takes):
+  w13 codes [n, 2I, H/2] (gate rows 0..I-1, then up rows), w13 scales [n, 2I, H/16],
+  w2 codes [n, H, I/2], w2 scales [n, H, I/16], global scales fp32 [n, 3];
+  byte k/2 of a row holds element k in its low nibble when k is even.
+
+Layer instance ``l`` of a workload uses seed ``workload.seed + 7919 * l``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import zlib
+from typing import Optional
+
+import numpy as np
+
+# e4m3 encodings of 2^-4, 2^-3, ..., 2^2: sign 0, exponent field n + 7, mantissa 0.
+SCALE_BYTES = np.array([(n + 7) << 3 for n in range(-4, 3)], dtype=np.uint8)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    num_experts: int
+    hidden: int
+    inter: int
+    top_k: int
+    tokens: int
+    clamped: bool
+    global_scale: float
+    seed: int
+    shared_inter: int = 0
+    hot_experts: int = 0
+    hot_bias: float = 0.0
+    gate_max: float = 7.0
+    up_absmax: float = 7.0
+    router_std: float = 0.02
+    shared_gate_std: float = 0.02
+
+    @property
+    def act(self) -> int:
+        return 1 if self.clamped else 0
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        # Tiny layer: 8 experts, H=256, I=128, top-2, plain SwiGLU, global scale 1.
+        Workload("tiny_e8_top2", 8, 256, 128, 2, 1, False, 1.0, seed=1000),
+        # Batch-1 decode over the 288-expert layer: H=2048, I=768, top-8, clamped.
+        Workload("decode_e288_top8", 288, 2048, 768, 8, 1, True, 2.0 ** -6, seed=1001),
+        # Batch-1 decode over the 512-expert layer with a gated shared expert.
+        Workload("decode_e512_top10_shared", 512, 2048, 512, 10, 1, True, 2.0 ** -6,
+                 seed=1002, shared_inter=512),
+        # 32 concurrent decode tokens; 64 seeded hot experts get +2.0 on their logit.
+        Workload("batched_decode_t32_hot64", 512, 2048, 512, 10, 32, True, 2.0 ** -6,
+                 seed=1003, shared_inter=512, hot_experts=64, hot_bias=2.0),
+        # Prefill chunk of 8192 tokens through the 512-expert layer.
+        Workload("prefill_t8192", 512, 2048, 512, 10, 8192, True, 2.0 ** -6, seed=1004,
+                 shared_inter=512),
+    ]
+}
+
+
+@dataclasses.dataclass
+class Layer:
+    """One layer's weights (numpy, canonical layout) plus its workload shape."""
+    workload: Workload
+    w_router: np.ndarray
+    bias: Optional[np.ndarray]
+    w13_codes: np.ndarray
+    w13_scales: np.ndarray
+    w2_codes: np.ndarray
+    w2_scales: np.ndarray
+    global_scale: np.ndarray
+    s13_codes: Optional[np.ndarray] = None
+    s13_scales: Optional[np.ndarray] = None
+    s2_codes: Optional[np.ndarray] = None
+    s2_scales: Optional[np.ndarray] = None
+    s_global: Optional[np.ndarray] = None
+    shared_gate: Optional[np.ndarray] = None
+
+    # shape accessors used by the oracle wrapper and the binding
+    num_experts = property(lambda s: s.workload.num_experts)
+    hidden = property(lambda s: s.workload.hidden)
+    inter = property(lambda s: s.workload.inter)
+    top_k = property(lambda s: s.workload.top_k)
+    act = property(lambda s: s.workload.act)
+    gate_max = property(lambda s: s.workload.gate_max)
+    up_absmax = property(lambda s: s.workload.up_absmax)
+    shared_inter = property(lambda s: s.workload.shared_inter)
+
+
+def _rng(seed: int, name: str) -> np.random.Generator:
+    return np.random.default_rng([seed, zlib.crc32(name.encode())])
+
+
+def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """Round fp32 draws to bf16 (torch's conversion, nearest-even) and return the bits."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _codes(rng, shape):
+    n = int(np.prod(shape))
+    return np.frombuffer(rng.bytes(n), dtype=np.uint8).reshape(shape).copy()
+
+
+def _scales(rng, shape):
+    return SCALE_BYTES[rng.integers(0, len(SCALE_BYTES), size=shape)]
+
+
+def _bank(seed: int, prefix: str, n: int, H: int, I: int, g: float):
+    return dict(
+        w13_codes=_codes(_rng(seed, prefix + "w13_codes"), (n, 2 * I, H // 2)),
+        w13_scales=_scales(_rng(seed, prefix + "w13_scales"), (n, 2 * I, H // 16)),
+        w2_codes=_codes(_rng(seed, prefix + "w2_codes"), (n, H, I // 2)),
+        w2_scales=_scales(_rng(seed, prefix + "w2_scales"), (n, H, I // 16)),
+        global_scale=np.full((n, 3), g, dtype=np.float32),
+    )
+
+
+def make_layer(w: Workload, instance: int = 0, num_experts: Optional[int] = None) -> Layer:
+    """Host (numpy) weights of layer instance ``instance``.
+
+    ``num_experts`` overrides the routed bank size (tests use it to build small
+    variants of a workload); by default the workload's own count is used.
+    """
+    seed = w.seed + 7919 * instance
+    E = w.num_experts if num_experts is None else num_experts
+    if num_experts is not None:
+        w = dataclasses.replace(w, num_experts=E)
+    H, I = w.hidden, w.inter
+    wr = (_rng(seed, "w_router").standard_normal((E, H), dtype=np.float32)
+          * np.float32(w.router_std)).astype(np.float32)
+    bias = None
+    if w.hot_experts > 0:
+        bias = np.zeros(E, np.float32)
+        hot = _rng(seed, "hot").choice(E, size=min(w.hot_experts, E), replace=False)
+        bias[hot] = np.float32(w.hot_bias)
+    bank = _bank(seed, "", E, H, I, w.global_scale)
+    layer = Layer(workload=w, w_router=wr, bias=bias, **bank)
+    if w.shared_inter > 0:
+        sb = _bank(seed, "shared_", 1, H, w.shared_inter, w.global_scale)
+        layer.s13_codes = sb["w13_codes"]
+        layer.s13_scales = sb["w13_scales"]
+        layer.s2_codes = sb["w2_codes"]
+        layer.s2_scales = sb["w2_scales"]
+        layer.s_global = sb["global_scale"]
+        gs = _rng(seed, "shared_gate").standard_normal(H, dtype=np.float32)
+        layer.shared_gate = bf16_bits_from_f32(gs * np.float32(w.shared_gate_std))
+    return layer
+
+
+def make_tokens(w: Workload, instance: int = 0, tokens: Optional[int] = None,
+                stream: str = "x") -> np.ndarray:
+    """bf16 bits u16 [T, H] of N(0, 1) draws."""
+    T = w.tokens if tokens is None else tokens
+    seed = w.seed + 7919 * instance
+    a = _rng(seed, stream).standard_normal((T, w.hidden), dtype=np.float32)
+    return bf16_bits_from_f32(a)
+
+
+def make_layer_device(w: Workload, instance: int, device):
+    """Draw one layer instance directly in device memory with torch's generator.
+
+    Same shapes and distributions as ``make_layer`` (different draws); used to
+    fill many distinct layer instances for timing without host round trips.
+    Returns a dict of torch tensors in the canonical layout.
+    """
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed + 7919 * instance)
+    E, H, I = w.num_experts, w.hidden, w.inter
+    table = torch.tensor(SCALE_BYTES, dtype=torch.uint8, device=device)
+
+    def codes(shape):
+        return torch.randint(0, 256, shape, generator=gen, device=device, dtype=torch.uint8)
+
+    def scales(shape):
+        idx = torch.randint(0, len(SCALE_BYTES), shape, generator=gen, device=device)
+        return table[idx]
+
+    def bank(n, inter):
+        return dict(w13_codes=codes((n, 2 * inter, H // 2)),
+                    w13_scales=scales((n, 2 * inter, H // 16)),
+                    w2_codes=codes((n, H, inter // 2)),
+                    w2_scales=scales((n, H, inter // 16)),
+                    global_scale=torch.full((n, 3), w.global_scale, dtype=torch.float32,
+                                            device=device))
+
+    out = dict(w_router=torch.randn((E, H), generator=gen, device=device) * w.router_std,
+               bias=None, routed=bank(E, I), shared=None, shared_gate=None)
+    if w.hot_experts > 0:
+        bias = torch.zeros(E, dtype=torch.float32, device=device)
+        hot = torch.randperm(E, generator=gen, device=device)[: w.hot_experts]
+        bias[hot] = w.hot_bias
+        out["bias"] = bias
+    if w.shared_inter > 0:
+        out["shared"] = bank(1, w.shared_inter)
+        out["shared_gate"] = (torch.randn(H, generator=gen, device=device)
+                              * w.shared_gate_std).to(torch.bfloat16)
+    return out

@@ -1,0 +1,211 @@
+"""CPU oracle for the NVFP4 mixture-of-experts layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product (the HIP library and its
+Python binding) never imports, links or runs it, and it never imports the
+product: the two sides meet only in the seeded input arrays of
+``nvfp4_mixture_experts_amd.synth``.
+
+The arithmetic lives in ``ftmoe_oracle.c`` (plain C, binary64, one element at a
+time); this module only compiles it with gcc and marshals numpy arrays through
+ctypes.  Definitions and the readings taken where the pages are silent are
+documented at the top of the C file.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ftmoe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_ftmoe_oracle.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F32 = ctypes.c_float
+_F64 = ctypes.c_double
+
+
+def build() -> str:
+    """Compile the oracle into ``oracle/_ftmoe_oracle.so`` (gcc, no fast-math, no contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.or_e2m1.restype = _F64
+    lib.or_e2m1.argtypes = [ctypes.c_uint32]
+    lib.or_e4m3.restype = _F64
+    lib.or_e4m3.argtypes = [ctypes.c_uint32]
+    lib.or_dequant_value.restype = _F32
+    lib.or_dequant_value.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _F32]
+    lib.or_dequant_matrix.restype = None
+    lib.or_dequant_matrix.argtypes = [_P, _P, _I64, _I64, _F32, _P]
+    lib.or_bf16_to_double.restype = _F64
+    lib.or_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.or_bf16_from_double.restype = ctypes.c_uint16
+    lib.or_bf16_from_double.argtypes = [_F64]
+    lib.or_router_logits.restype = None
+    lib.or_router_logits.argtypes = [_I64, _I32, _I32, _P, _P, _P, _P]
+    lib.or_topk.restype = None
+    lib.or_topk.argtypes = [_I64, _I32, _I32, _P, _P, _P]
+    lib.or_silu.restype = _F64
+    lib.or_silu.argtypes = [_F64]
+    lib.or_swiglu.restype = _F64
+    lib.or_swiglu.argtypes = [_I32, _F64, _F64, _F64, _F64]
+    lib.or_expert_output.restype = None
+    lib.or_expert_output.argtypes = [_I32, _I32, _I64, _P, _P, _P, _P, _P, _I32, _F32, _F32,
+                                     _P, _P]
+    lib.or_moe_layer.restype = _I32
+    lib.or_moe_layer.argtypes = ([_I32, _I32, _I32, _I32, _I32, _F32, _F32, _I64, _P, _P, _P]
+                                 + [_P] * 5 + [_I32] + [_P] * 6 + [_P] * 6)
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "oracle needs C-contiguous arrays"
+    return a.ctypes.data
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------------ codecs --
+
+def e2m1(code: int) -> float:
+    return _load().or_e2m1(int(code))
+
+
+def e4m3(byte: int) -> float:
+    return _load().or_e4m3(int(byte))
+
+
+def dequant_value(code: int, scale_byte: int, g: float) -> np.float32:
+    return np.float32(_load().or_dequant_value(int(code), int(scale_byte), float(g)))
+
+
+def dequant_matrix(codes: np.ndarray, scales: np.ndarray, g: float) -> np.ndarray:
+    """codes u8 [rows, K/2], scales u8 [rows, K/16] -> fp32 [rows, K]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    rows, half = codes.shape
+    K = 2 * half
+    assert scales.shape == (rows, K // 16)
+    out = np.empty((rows, K), np.float32)
+    _load().or_dequant_matrix(_ptr(codes), _ptr(scales), rows, K, float(g), _ptr(out))
+    return out
+
+
+def bf16_to_double(b: int) -> float:
+    return _load().or_bf16_to_double(int(b))
+
+
+def bf16_from_double(v: float) -> int:
+    return int(_load().or_bf16_from_double(float(v)))
+
+
+# ------------------------------------------------------------------ router --
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:
+    """x bf16 bits u16 [T, H]; w_router fp32 [E, H]; bias fp32 [E] or None -> fp32 [T, E]."""
+    x = _c(x, np.uint16)
+    w_router = _c(w_router, np.float32)
+    bias = _c(bias, np.float32)
+    T, H = x.shape
+    E = w_router.shape[0]
+    out = np.empty((T, E), np.float32)
+    _load().or_router_logits(T, E, H, _ptr(x), _ptr(w_router), _ptr(bias), _ptr(out))
+    return out
+
+
+def topk(logits: np.ndarray, k: int):
+    """fp32 [T, E] -> (ids int32 [T, k], weights fp32 [T, k])."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    _load().or_topk(T, E, int(k), _ptr(logits), _ptr(ids), _ptr(w))
+    return ids, w
+
+
+def silu(z: float) -> float:
+    return _load().or_silu(float(z))
+
+
+def swiglu(act: int, g: float, u: float, gate_max: float = 7.0, up_absmax: float = 7.0) -> float:
+    return _load().or_swiglu(int(act), float(g), float(u), float(gate_max), float(up_absmax))
+
+
+# ------------------------------------------------------------------ layer --
+
+def expert_output(layer, e: int, x_row: np.ndarray, shared: bool = False) -> np.ndarray:
+    """One expert's binary64 output [H] for one bf16 token row."""
+    x_row = _c(x_row, np.uint16)
+    if shared:
+        I = layer.shared_inter
+        bank = (layer.s13_codes, layer.s13_scales, layer.s2_codes, layer.s2_scales,
+                layer.s_global)
+    else:
+        I = layer.inter
+        bank = (layer.w13_codes, layer.w13_scales, layer.w2_codes, layer.w2_scales,
+                layer.global_scale)
+    bank = [_c(a, np.uint8) for a in bank[:4]] + [_c(bank[4], np.float32)]
+    out = np.empty(layer.hidden, np.float64)
+    _load().or_expert_output(layer.hidden, I, int(e), *[_ptr(a) for a in bank], layer.act,
+                             layer.gate_max, layer.up_absmax, _ptr(x_row), _ptr(out))
+    return out
+
+
+def moe_layer(layer, x: np.ndarray, ids=None, weights=None) -> dict:
+    """Run the whole layer for the tokens in ``x`` (bf16 bits u16 [T, H]).
+
+    ``layer`` carries the weights (see ``nvfp4_mixture_experts_amd.synth.Layer``).
+    With ``ids``/``weights`` given, those routes are used instead of the router.
+    Returns ``{"ids", "weights", "y64", "y"}``.
+    """
+    x = _c(x, np.uint16)
+    T = x.shape[0]
+    k = layer.top_k
+    ids_in = _c(ids, np.int32)
+    w_in = _c(weights, np.float32)
+    ids_out = np.empty((T, k), np.int32)
+    w_out = np.empty((T, k), np.float32)
+    y64 = np.empty((T, layer.hidden), np.float64)
+    y = np.empty((T, layer.hidden), np.uint16)
+    Is = layer.shared_inter
+    sh = [None] * 6
+    if Is > 0:
+        sh = [_c(layer.s13_codes, np.uint8), _c(layer.s13_scales, np.uint8),
+              _c(layer.s2_codes, np.uint8), _c(layer.s2_scales, np.uint8),
+              _c(layer.s_global, np.float32), _c(layer.shared_gate, np.uint16)]
+    bank = [_c(layer.w13_codes, np.uint8), _c(layer.w13_scales, np.uint8),
+            _c(layer.w2_codes, np.uint8), _c(layer.w2_scales, np.uint8),
+            _c(layer.global_scale, np.float32)]
+    wr = _c(layer.w_router, np.float32)
+    bias = _c(layer.bias, np.float32)
+    rc = _load().or_moe_layer(layer.num_experts, layer.hidden, layer.inter, k, layer.act,
+                              layer.gate_max, layer.up_absmax, T, _ptr(x), _ptr(wr), _ptr(bias),
+                              *[_ptr(a) for a in bank], Is, *[_ptr(a) for a in sh],
+                              _ptr(ids_in), _ptr(w_in), _ptr(ids_out), _ptr(w_out), _ptr(y64),
+                              _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle rejected the layer shape")
+    return {"ids": ids_out, "weights": w_out, "y64": y64, "y": y}

@@ -1,0 +1,378 @@
+/*
+ * ftmoe_oracle.c -- plain, slow CPU oracle for the NVFP4-weight mixture-of-experts
+ * layer (router, top-k, renormalised weights, clamped-SwiGLU experts, down
+ * projection, weighted combine and gated shared expert).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load this library.  It shares no source, header,
+ * table or helper with the HIP library; the two meet only in the seeded input
+ * arrays that the tests hand to both.
+ *
+ * Every function computes the plain definition, one element at a time, in
+ * IEEE binary64 (products of the fp32/bf16/e2m1/e4m3 operands are exact in
+ * binary64), and rounds once at the end where a narrower type is stored.
+ *
+ * Sources of the definitions:
+ *  - "FreeToken fork PR #84" (page 1), bullet on #631: the NVFP4 MoE decode GEMV
+ *    that runs in every layer at every decode step; bullet on #578: NVFP4 prefill
+ *    experts dequantised by bit placement.
+ *  - "FreeToken commit log" (page 2): 288-expert NVFP4 MoE; clamped-SwiGLU
+ *    activation across the MoE stack; 512 routed experts, top-10, plus a gated
+ *    shared expert; MoE router / shared gate kernels; non-power-of-2 top-k.
+ *  - NVFP4 codec: e2m1 element codes (OCP Microscaling Formats v1.0, FP4 E2M1),
+ *    one e4m3 scale per 16 consecutive K elements (OCP 8-bit Floating Point,
+ *    E4M3: bias 7, no infinities, S.1111.111 is NaN), one fp32 global scale per
+ *    tensor.  The dequantised weight is fp32(fp32(e2m1 x e4m3) x global).
+ *
+ * Readings where the pages are silent (each is also listed in the design notes):
+ *  - the low nibble of a code byte holds the even K index;
+ *  - w13 stacks gate rows [0, I) over up rows [I, 2I); per-expert global scales
+ *    are stored as [gate, up, down];
+ *  - router logits are accumulated in binary64 in index order, plus the optional
+ *    bias, and rounded once to fp32; top-k orders by (logit desc, index asc), a
+ *    NaN logit ranks below every number;
+ *  - routing weights are the softmax over the selected logits (equal, in exact
+ *    arithmetic, to a softmax over all experts renormalised over the top-k),
+ *    evaluated in binary64 and stored as fp32; the layer combines with the
+ *    stored fp32 weights;
+ *  - clamped SwiGLU is silu(min(g, gate_max)) * clamp(u, -up_absmax, up_absmax)
+ *    with silu(z) = z / (1 + exp(-z)); plain SwiGLU is silu(g) * u; comparisons
+ *    are written so that a NaN propagates;
+ *  - the expert intermediate h is kept unrounded (binary64 here);
+ *  - the shared expert's gate is sigmoid(sum_h gs[h] * x[h]);
+ *  - the output is bf16, rounded to nearest-even once from the binary64 sum
+ *    sum_i w_i * o_i + gamma * o_shared (routed slots in rank order, then the
+ *    shared expert).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- codecs -- */
+
+/* e2m1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+ * Normal (e > 0): 2^(e-1) * (1 + m/2).  Subnormal (e == 0): m * 0.5. */
+double or_e2m1(uint32_t code)
+{
+    uint32_t s = (code >> 3) & 1u;
+    uint32_t e = (code >> 1) & 3u;
+    uint32_t m = code & 1u;
+    double mag;
+    if (e == 0)
+        mag = 0.5 * (double)m;
+    else
+        mag = ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+    return s ? -mag : mag;
+}
+
+/* e4m3 (OCP FP8 E4M3): sign bit 7, exponent bits 6..3 (bias 7), mantissa 2..0.
+ * S.1111.111 is NaN; there are no infinities.  Subnormal: m/8 * 2^-6. */
+double or_e4m3(uint32_t byte)
+{
+    uint32_t s = (byte >> 7) & 1u;
+    uint32_t e = (byte >> 3) & 15u;
+    uint32_t m = byte & 7u;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, -6);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -mag : mag;
+}
+
+/* One dequantised NVFP4 weight: fp32(fp32(e2m1 * e4m3) * g).
+ * The inner product has at most 2 + 4 significant bits and an exponent inside
+ * fp32's normal range, so its conversion to fp32 is exact; the product with the
+ * fp32 global scale is exact in binary64 and rounds once (to nearest-even) when
+ * converted to fp32, which is the correctly rounded fp32 multiplication. */
+float or_dequant_value(uint32_t code, uint32_t scale_byte, float g)
+{
+    float p = (float)(or_e2m1(code) * or_e4m3(scale_byte));
+    return (float)((double)p * (double)g);
+}
+
+/* Code of element k of a row: byte k/2 of the row, low nibble for even k. */
+static uint32_t row_code(const uint8_t *row_codes, int64_t k)
+{
+    uint8_t b = row_codes[k / 2];
+    return (k % 2 == 0) ? (uint32_t)(b & 0x0F) : (uint32_t)(b >> 4);
+}
+
+/* Dequantise a [rows, K] NVFP4 matrix stored as codes [rows, K/2] and scales
+ * [rows, K/16] (row-major) with global scale g, into fp32 out[rows, K]. */
+void or_dequant_matrix(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
+                       float g, float *out)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint8_t *rc = codes + r * (K / 2);
+        const uint8_t *rs = scales + r * (K / 16);
+        for (int64_t k = 0; k < K; ++k)
+            out[r * K + k] = or_dequant_value(row_code(rc, k), rs[k / 16], g);
+    }
+}
+
+/* bf16 -> binary64 (exact). */
+double or_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* binary64 -> bf16, round to nearest, ties to even, in one step (no detour
+ * through fp32, which could round twice).  bf16 has 8 significant bits, normal
+ * exponents down to -126 and subnormals spaced 2^-133. */
+uint16_t or_bf16_from_double(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80u);
+    int ex;
+    frexp(a, &ex);           /* a in [2^(ex-1), 2^ex) */
+    int q = ex - 1 - 7;      /* exponent of one unit in the last place */
+    if (q < -133)
+        q = -133;
+    double r = ldexp(nearbyint(ldexp(a, -q)), q); /* default rounding: nearest-even */
+    const double bf16_max = ldexp(255.0, 120);     /* 0x7F7F = (2 - 2^-7) * 2^127 */
+    if (r > bf16_max)
+        return (uint16_t)(sign | 0x7F80u);
+    float f = (float)r;      /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7FFFu));
+}
+
+/* ---------------------------------------------------------------- router -- */
+
+/* logits[t, e] = fp32( sum_h W[e, h] * x[t, h]  (+ bias[e]) ), binary64 sum in
+ * index order.  x is bf16 [T, H]; W fp32 [E, H]; bias fp32 [E] or NULL. */
+void or_router_logits(int64_t T, int32_t E, int32_t H, const uint16_t *x, const float *W,
+                      const float *bias, float *logits)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int32_t h = 0; h < H; ++h)
+                acc += (double)W[(int64_t)e * H + h] * or_bf16_to_double(x[t * H + h]);
+            if (bias)
+                acc += (double)bias[e];
+            logits[t * E + e] = (float)acc;
+        }
+    }
+}
+
+/* Rank key: a NaN logit ranks below every number (it is kept, not skipped). */
+static int ranks_above(float a, int32_t ia, float b, int32_t ib)
+{
+    int an = isnan(a), bn = isnan(b);
+    if (an || bn) {
+        if (an && bn)
+            return ia < ib;
+        return bn; /* the number ranks above the NaN */
+    }
+    if (a != b)
+        return a > b;
+    return ia < ib;
+}
+
+/* Top-k by (logit descending, index ascending), emitted in that order, and the
+ * softmax of the selected logits in binary64, stored as fp32. */
+void or_topk(int64_t T, int32_t E, int32_t k, const float *logits, int32_t *ids, float *w)
+{
+    char *taken = (char *)malloc((size_t)E);
+    double *d = (double *)malloc(sizeof(double) * (size_t)k);
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * E;
+        memset(taken, 0, (size_t)E);
+        for (int32_t i = 0; i < k; ++i) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || ranks_above(l[e], e, l[best], best))
+                    best = e;
+            }
+            taken[best] = 1;
+            ids[t * k + i] = best;
+        }
+        double top = (double)l[ids[t * k]];
+        double sum = 0.0;
+        for (int32_t i = 0; i < k; ++i) {
+            d[i] = exp((double)l[ids[t * k + i]] - top);
+            sum += d[i];
+        }
+        for (int32_t i = 0; i < k; ++i)
+            w[t * k + i] = (float)(d[i] / sum);
+    }
+    free(taken);
+    free(d);
+}
+
+/* ------------------------------------------------------------ activations -- */
+
+double or_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* act 0: silu(g) * u.  act 1: silu(min(g, gate_max)) * clamp(u, -up_absmax, up_absmax). */
+double or_swiglu(int32_t act, double g, double u, double gate_max, double up_absmax)
+{
+    if (act == 1) {
+        if (g > gate_max)
+            g = gate_max;
+        if (u > up_absmax)
+            u = up_absmax;
+        if (u < -up_absmax)
+            u = -up_absmax;
+    }
+    return or_silu(g) * u;
+}
+
+/* ---------------------------------------------------------------- experts -- */
+
+/* One expert's MLP on one token, from its dequantised fp32 matrices:
+ *   gate_r = sum_h Wg[r, h] x_h,  up_r = sum_h Wu[r, h] x_h,
+ *   h_r = swiglu(gate_r, up_r),   o_c = sum_r Wd[c, r] h_r.
+ * wg, wu: [I, H]; wd: [H, I] (fp32, already dequantised); x: binary64 [H]. */
+static void expert_forward(int32_t H, int32_t I, const float *wg, const float *wu, const float *wd,
+                           int32_t act, double gate_max, double up_absmax, const double *x,
+                           double *hbuf, double *o)
+{
+    for (int32_t r = 0; r < I; ++r) {
+        double g = 0.0, u = 0.0;
+        for (int32_t h = 0; h < H; ++h) {
+            g += (double)wg[(int64_t)r * H + h] * x[h];
+            u += (double)wu[(int64_t)r * H + h] * x[h];
+        }
+        hbuf[r] = or_swiglu(act, g, u, gate_max, up_absmax);
+    }
+    for (int32_t c = 0; c < H; ++c) {
+        double acc = 0.0;
+        for (int32_t r = 0; r < I; ++r)
+            acc += (double)wd[(int64_t)c * I + r] * hbuf[r];
+        o[c] = acc;
+    }
+}
+
+/* Dequantise expert e of a canonical NVFP4 expert bank into wg, wu [I, H] and
+ * wd [H, I].  Bank layout: w13 codes [n][2I][H/2], w13 scales [n][2I][H/16],
+ * w2 codes [n][H][I/2], w2 scales [n][H][I/16], global scales [n][3]. */
+static void dequant_expert(int32_t H, int32_t I, int64_t e, const uint8_t *w13c,
+                           const uint8_t *w13s, const uint8_t *w2c, const uint8_t *w2s,
+                           const float *gsc, float *wg, float *wu, float *wd)
+{
+    int64_t rows13 = 2 * (int64_t)I;
+    const uint8_t *c13 = w13c + e * rows13 * (H / 2);
+    const uint8_t *s13 = w13s + e * rows13 * (H / 16);
+    or_dequant_matrix(c13, s13, I, H, gsc[e * 3 + 0], wg);
+    or_dequant_matrix(c13 + (int64_t)I * (H / 2), s13 + (int64_t)I * (H / 16), I, H,
+                      gsc[e * 3 + 1], wu);
+    or_dequant_matrix(w2c + e * (int64_t)H * (I / 2), w2s + e * (int64_t)H * (I / 16), H, I,
+                      gsc[e * 3 + 2], wd);
+}
+
+/* One expert's output o[H] for one token x (bf16 [H]).  Exported for tests. */
+void or_expert_output(int32_t H, int32_t I, int64_t e, const uint8_t *w13c, const uint8_t *w13s,
+                      const uint8_t *w2c, const uint8_t *w2s, const float *gsc, int32_t act,
+                      float gate_max, float up_absmax, const uint16_t *x, double *o)
+{
+    float *wg = (float *)malloc(sizeof(float) * (size_t)I * H);
+    float *wu = (float *)malloc(sizeof(float) * (size_t)I * H);
+    float *wd = (float *)malloc(sizeof(float) * (size_t)I * H);
+    double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+    double *hb = (double *)malloc(sizeof(double) * (size_t)I);
+    for (int32_t h = 0; h < H; ++h)
+        xd[h] = or_bf16_to_double(x[h]);
+    dequant_expert(H, I, e, w13c, w13s, w2c, w2s, gsc, wg, wu, wd);
+    expert_forward(H, I, wg, wu, wd, act, gate_max, up_absmax, xd, hb, o);
+    free(wg); free(wu); free(wd); free(xd); free(hb);
+}
+
+/* ------------------------------------------------------------------ layer -- */
+
+/* The whole MoE layer for T tokens.
+ *   Routed bank: E experts of intermediate size I (canonical layout above).
+ *   Shared expert (optional, Is > 0): one expert of intermediate size Is in the
+ *   same layout, gated by sigmoid(sum_h sgate[h] x[h]).
+ *   Routing: if ids_in/w_in are given they are used as the routes; otherwise the
+ *   router logits, top-k and weights are computed here (and written to
+ *   ids_out / w_out when those are non-NULL).
+ * Outputs: y bf16 [T, H]; y64 (optional) the binary64 value before rounding. */
+int32_t or_moe_layer(int32_t E, int32_t H, int32_t I, int32_t k, int32_t act, float gate_max,
+                     float up_absmax, int64_t T, const uint16_t *x, const float *Wr,
+                     const float *bias, const uint8_t *w13c, const uint8_t *w13s,
+                     const uint8_t *w2c, const uint8_t *w2s, const float *gsc, int32_t Is,
+                     const uint8_t *s13c, const uint8_t *s13s, const uint8_t *s2c,
+                     const uint8_t *s2s, const float *sgsc, const uint16_t *sgate,
+                     const int32_t *ids_in, const float *w_in, int32_t *ids_out, float *w_out,
+                     double *y64, uint16_t *y)
+{
+    if (E <= 0 || H <= 0 || I <= 0 || k <= 0 || k > E || T < 0 || H % 16 || I % 16 ||
+        (Is > 0 && Is % 16))
+        return -1;
+    int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1) * k);
+    float *wts = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * k);
+    if (ids_in && w_in) {
+        memcpy(ids, ids_in, sizeof(int32_t) * (size_t)T * k);
+        memcpy(wts, w_in, sizeof(float) * (size_t)T * k);
+    } else {
+        float *logits = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * E);
+        or_router_logits(T, E, H, x, Wr, bias, logits);
+        or_topk(T, E, k, logits, ids, wts);
+        free(logits);
+    }
+    if (ids_out)
+        memcpy(ids_out, ids, sizeof(int32_t) * (size_t)T * k);
+    if (w_out)
+        memcpy(w_out, wts, sizeof(float) * (size_t)T * k);
+
+    int32_t Imax = (Is > I) ? Is : I;
+    float *wg = (float *)malloc(sizeof(float) * (size_t)Imax * H);
+    float *wu = (float *)malloc(sizeof(float) * (size_t)Imax * H);
+    float *wd = (float *)malloc(sizeof(float) * (size_t)Imax * H);
+    double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+    double *hb = (double *)malloc(sizeof(double) * (size_t)Imax);
+    double *o = (double *)malloc(sizeof(double) * (size_t)H);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)H);
+
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            xd[h] = or_bf16_to_double(x[t * H + h]);
+            acc[h] = 0.0;
+        }
+        for (int32_t i = 0; i < k; ++i) {
+            int64_t e = ids[t * k + i];
+            dequant_expert(H, I, e, w13c, w13s, w2c, w2s, gsc, wg, wu, wd);
+            expert_forward(H, I, wg, wu, wd, act, gate_max, up_absmax, xd, hb, o);
+            double wi = (double)wts[t * k + i];
+            for (int32_t h = 0; h < H; ++h)
+                acc[h] += wi * o[h];
+        }
+        if (Is > 0) {
+            double z = 0.0;
+            for (int32_t h = 0; h < H; ++h)
+                z += or_bf16_to_double(sgate[h]) * xd[h];
+            double gamma = 1.0 / (1.0 + exp(-z));
+            dequant_expert(H, Is, 0, s13c, s13s, s2c, s2s, sgsc, wg, wu, wd);
+            expert_forward(H, Is, wg, wu, wd, act, gate_max, up_absmax, xd, hb, o);
+            for (int32_t h = 0; h < H; ++h)
+                acc[h] += gamma * o[h];
+        }
+        for (int32_t h = 0; h < H; ++h) {
+            if (y64)
+                y64[t * H + h] = acc[h];
+            if (y)
+                y[t * H + h] = or_bf16_from_double(acc[h]);
+        }
+    }
+    free(ids); free(wts); free(wg); free(wu); free(wd);
+    free(xd); free(hb); free(o); free(acc);
+    return 0;
+}

@@ -1,0 +1,362 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against what the format or the mathematics fixes:
+the published E2M1/E4M3 tables, a library decoder (torch's float8_e4m3fn), the
+exactness of the code x scale product, library routines (numpy matmul and
+argsort, scipy softmax) on the special cases that reduce to them, a
+hand-derived worked example, and closed forms.  Together they are chosen so
+that a plausible slip in the oracle (swapped nibbles, a wrong scale-block index,
+gate and up swapped, a missing clamp, a wrong sign, double rounding to bf16,
+ties broken toward the higher index) fails at least one of them.
+"""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from nvfp4_mixture_experts_amd import synth
+from tests.conftest import GOLDEN
+
+
+def _golden_e2m1():
+    vals = []
+    with open(os.path.join(GOLDEN, "e2m1_table.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            code, v = line.split()
+            vals.append((int(code), float(v)))
+    assert [c for c, _ in vals] == list(range(16))
+    return np.array([v for _, v in vals], dtype=np.float64)
+
+
+E2M1 = _golden_e2m1()
+
+
+def _torch_e4m3_all():
+    b = torch.arange(256, dtype=torch.uint8)
+    return b.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+E4M3 = _torch_e4m3_all()
+
+
+def _f32_bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+# ------------------------------------------------------------------ codecs --
+
+def test_e2m1_matches_published_table_bitwise():
+    got = np.array([oracle.e2m1(c) for c in range(16)])
+    # bitwise (so -0.0 for code 8 is checked too)
+    assert np.array_equal(got.view(np.uint64), E2M1.view(np.uint64))
+
+
+def test_e4m3_matches_torch_for_all_256_bytes():
+    got = np.array([oracle.e4m3(b) for b in range(256)])
+    nan = np.isnan(E4M3)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(got[~nan].view(np.uint64), E4M3[~nan].view(np.uint64))
+
+
+def test_e4m3_named_points():
+    with open(os.path.join(GOLDEN, "e4m3_points.txt")) as f:
+        rows = [ln.split()[:2] for ln in f if ln.strip() and not ln.startswith("#")]
+    assert len(rows) >= 10
+    for hexbyte, val in rows:
+        got = oracle.e4m3(int(hexbyte, 16))
+        want = float(val)
+        if math.isnan(want):
+            assert math.isnan(got)
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), hexbyte
+
+
+def test_synthetic_scale_bytes_are_the_powers_of_two_the_workloads_name():
+    got = [oracle.e4m3(int(b)) for b in synth.SCALE_BYTES]
+    assert got == [2.0 ** n for n in range(-4, 3)]
+
+
+@pytest.mark.parametrize("g", [1.0, 2.0 ** -6, 0.3, 3.0e-3])
+def test_dequant_is_one_rounding_of_the_exact_product(g):
+    g32 = np.float32(g)
+    for b in range(256):
+        s = E4M3[b]
+        if math.isnan(s):
+            continue
+        for c in range(16):
+            exact = E2M1[c] * s
+            # code x scale is exact in fp32 (at most 6 significant bits)
+            assert np.float64(np.float32(exact)) == exact
+            want = np.float32(exact) * g32            # numpy: one IEEE fp32 multiply
+            got = oracle.dequant_value(c, b, float(g32))
+            assert _f32_bits(got) == _f32_bits(want), (c, b, g)
+
+
+def test_dequant_matrix_nibble_order_and_block_index():
+    rng = np.random.default_rng(7)
+    rows, K = 5, 64
+    codes = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    scales = synth.SCALE_BYTES[rng.integers(0, 7, (rows, K // 16))]
+    g = np.float32(2.0 ** -6)
+    got = oracle.dequant_matrix(codes, scales, float(g))
+    # independent unpack: low nibble -> even k, high nibble -> odd k; block k // 16
+    nib = np.empty((rows, K), np.int64)
+    nib[:, 0::2] = codes & 0x0F
+    nib[:, 1::2] = codes >> 4
+    blk = np.repeat(scales, 16, axis=1)
+    want = (E2M1[nib] * E4M3[blk]).astype(np.float32) * g
+    assert np.array_equal(_f32_bits(got), _f32_bits(want))
+
+
+# ------------------------------------------------------------- bf16 output --
+
+def test_bf16_rounding_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    # torch rounds fp32 -> bf16 to nearest-even; on fp32 inputs one rounding is all there is
+    want = torch.from_numpy(vals.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_from_double(float(v)) for v in vals], np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_bf16_rounding_is_a_single_rounding_from_binary64():
+    # 1 + 2^-8 is halfway between bf16 1.0 and 1.0078125: ties to even -> 1.0
+    assert oracle.bf16_from_double(1.0 + 2.0 ** -8) == 0x3F80
+    # just above the tie rounds up; via fp32 the 2^-40 would be lost and tie down
+    assert oracle.bf16_from_double(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81
+    assert oracle.bf16_from_double(1.0 + 3 * 2.0 ** -8) == 0x3F82
+    assert oracle.bf16_from_double(-0.0) == 0x8000
+    assert oracle.bf16_from_double(3.5e38) == 0x7F80
+    assert oracle.bf16_from_double(2.0 ** -133) == 0x0001   # smallest subnormal
+    assert oracle.bf16_from_double(2.0 ** -135) == 0x0000   # below half of it
+
+
+# ------------------------------------------------------------------ router --
+
+def test_router_logits_exact_on_integer_data():
+    # small integers: every partial sum is exact in binary64 whatever the order,
+    # so numpy's matmul must agree bit for bit
+    rng = np.random.default_rng(3)
+    T, E, H = 3, 37, 256
+    xf = rng.integers(-4, 5, (T, H)).astype(np.float32)
+    x = synth.bf16_bits_from_f32(xf)
+    W = rng.integers(-8, 9, (E, H)).astype(np.float32)
+    bias = rng.integers(-3, 4, E).astype(np.float32)
+    got = oracle.router_logits(x, W, bias)
+    want = (xf.astype(np.float64) @ W.astype(np.float64).T + bias).astype(np.float32)
+    assert np.array_equal(got, want)
+
+
+def test_router_logits_match_library_matmul():
+    w = synth.WORKLOADS["decode_e288_top8"]
+    L = synth.make_layer(w, num_experts=64)
+    x = synth.make_tokens(w, tokens=4)
+    xf = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.router_logits(x, L.w_router)
+    want = (xf @ L.w_router.astype(np.float64).T).astype(np.float32)
+    ulps = np.abs(_f32_bits(got).astype(np.int64) - _f32_bits(want).astype(np.int64))
+    assert ulps.max() <= 1 and (ulps == 0).mean() > 0.99
+
+
+def test_topk_matches_stable_argsort_with_ties():
+    rng = np.random.default_rng(5)
+    T, E = 200, 50
+    # few distinct values -> many exact ties; lowest index must win
+    logits = rng.integers(0, 6, (T, E)).astype(np.float32) * np.float32(0.25)
+    for k in (1, 3, 10, 16, 50):
+        ids, w = oracle.topk(logits, k)
+        want = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, want), k
+
+
+def test_topk_weights_softmax_and_renormalisation():
+    rng = np.random.default_rng(9)
+    T, E = 64, 288
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    for k in (1, 2, 8, 10, E):
+        ids, w = oracle.topk(logits, k)
+        sel = np.take_along_axis(logits, ids, axis=1).astype(np.float64)
+        want = scipy.special.softmax(sel, axis=1)
+        assert np.allclose(w, want, rtol=2 ** -23, atol=0)
+        # renormalising a softmax over all experts gives the same weights
+        full = scipy.special.softmax(logits.astype(np.float64), axis=1)
+        ren = np.take_along_axis(full, ids, axis=1)
+        ren /= ren.sum(axis=1, keepdims=True)
+        assert np.allclose(w, ren, rtol=2 ** -22, atol=0)
+        assert np.all(np.abs(w.astype(np.float64).sum(axis=1) - 1.0) <= k * 2.0 ** -24)
+        if k == 1:
+            assert np.all(w == 1.0)
+
+
+def test_topk_nan_ranks_last():
+    logits = np.array([[np.nan, 1.0, np.nan, 0.5]], np.float32)
+    ids, _ = oracle.topk(logits, 3)
+    assert ids.tolist() == [[1, 3, 0]]
+
+
+# ------------------------------------------------------------- activations --
+
+def test_silu_closed_forms():
+    getcontext().prec = 40
+    s7 = Decimal(7) / (1 + Decimal(-7).exp())
+    assert oracle.silu(7.0) == pytest.approx(float(s7), rel=1e-15)
+    assert oracle.silu(0.0) == 0.0
+    for z in (-1000.0, -800.0):
+        v = oracle.silu(z)
+        assert not math.isnan(v) and v == 0.0 and math.copysign(1, v) < 0
+    assert oracle.silu(1000.0) == 1000.0
+
+
+def test_swiglu_clamps():
+    s7 = oracle.silu(7.0)
+    # clamped: gate capped above at 7, up clamped to [-7, 7]
+    assert oracle.swiglu(1, 100.0, 100.0) == s7 * 7.0
+    assert oracle.swiglu(1, 100.0, -100.0) == -s7 * 7.0
+    assert oracle.swiglu(1, 3.0, 2.0) == oracle.silu(3.0) * 2.0
+    assert oracle.swiglu(1, -50.0, 5.0) == oracle.silu(-50.0) * 5.0   # no lower gate clamp
+    # plain: no clamps, gate and up are not interchangeable
+    assert oracle.swiglu(0, 100.0, 100.0) == pytest.approx(100.0 * 100.0, rel=1e-15)
+    assert oracle.swiglu(0, 2.0, 5.0) != oracle.swiglu(0, 5.0, 2.0)
+    assert math.isnan(oracle.swiglu(1, float("nan"), 1.0))
+
+
+# ---------------------------------------------------------- whole layer --
+
+def _dense_reference(layer, x):
+    """k = E: y = sum_e softmax_e(logits) * MLP_e(x), from library routines only."""
+    H, I, E = layer.hidden, layer.inter, layer.num_experts
+    xf = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    logits = (xf @ layer.w_router.astype(np.float64).T).astype(np.float32)
+    probs = scipy.special.softmax(logits.astype(np.float64), axis=1).astype(np.float32)
+
+    def unpack(codes, scales, g):
+        rows = codes.shape[0]
+        nib = np.empty((rows, codes.shape[1] * 2), np.int64)
+        nib[:, 0::2] = codes & 0x0F
+        nib[:, 1::2] = codes >> 4
+        return (E2M1[nib] * E4M3[np.repeat(scales, 16, axis=1)]).astype(np.float32) * np.float32(g)
+
+    y = np.zeros((x.shape[0], H))
+    clamped = False
+    for e in range(E):
+        g13 = layer.global_scale[e]
+        wg = unpack(layer.w13_codes[e, :I], layer.w13_scales[e, :I], g13[0]).astype(np.float64)
+        wu = unpack(layer.w13_codes[e, I:], layer.w13_scales[e, I:], g13[1]).astype(np.float64)
+        wd = unpack(layer.w2_codes[e], layer.w2_scales[e], g13[2]).astype(np.float64)
+        gate = xf @ wg.T
+        up = xf @ wu.T
+        if layer.act == 1:
+            clamped |= bool((gate > layer.gate_max).any() or (np.abs(up) > layer.up_absmax).any())
+            gate = np.minimum(gate, layer.gate_max)
+            up = np.clip(up, -layer.up_absmax, layer.up_absmax)
+        h = scipy.special.expit(gate) * gate * up
+        y += probs[:, e:e + 1].astype(np.float64) * (h @ wd.T)
+    return y, clamped
+
+
+@pytest.mark.parametrize("name", ["tiny_e8_top2", "decode_e288_top8"])
+def test_all_experts_selected_equals_dense_layer(name):
+    w = synth.WORKLOADS[name]
+    E = 8 if name == "tiny_e8_top2" else 6
+    # the clamped case uses a larger global scale so that both clamps engage
+    g = w.global_scale if w.act == 0 else 2.0 ** -3
+    w = synth.dataclasses.replace(w, num_experts=E, top_k=E, hidden=256, inter=128,
+                                  global_scale=g)
+    layer = synth.make_layer(w)
+    x = synth.make_tokens(w, tokens=2)
+    got = oracle.moe_layer(layer, x)
+    want, clamped = _dense_reference(layer, x)
+    scale = np.abs(want).max()
+    assert np.abs(got["y64"] - want).max() <= 1e-12 * scale
+    assert clamped == (w.act == 1)
+
+
+def test_clamp_engages_on_decode_workload_shape():
+    # with global scale 2^-6 some pre-activations exceed 7: dropping the clamp changes y
+    w = synth.dataclasses.replace(synth.WORKLOADS["decode_e288_top8"], num_experts=4, top_k=4)
+    layer = synth.make_layer(w)
+    x = synth.make_tokens(w, tokens=1)
+    clamped = oracle.moe_layer(layer, x)["y64"]
+    w_plain = synth.dataclasses.replace(w, clamped=False)
+    plain = oracle.moe_layer(synth.dataclasses.replace(layer, workload=w_plain), x)["y64"]
+    assert not np.allclose(clamped, plain, rtol=1e-6)
+
+
+def test_worked_example():
+    spec = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    sh = spec["shape"]
+    E, H, I = sh["num_experts"], sh["hidden"], sh["inter"]
+    w = synth.Workload("worked_example", E, H, I, sh["top_k"], 1, True, 1.0, seed=0)
+    w13c = np.full((E, 2 * I, H // 2), 0x77, np.uint8)
+    w13s = np.full((E, 2 * I, H // 16), 0x38, np.uint8)
+    w2c = np.full((E, H, I // 2), 0x77, np.uint8)
+    w2s = np.full((E, H, I // 16), 0x38, np.uint8)
+    gsc = np.ones((E, 3), np.float32)
+    w13c[0, :I] = 0x62
+    w13s[0, :I] = [0x38, 0x30]
+    w13c[0, I:] = 0xB3
+    w13s[0, I:] = [0x38, 0x38]
+    w2c[0] = 0x02
+    w2s[0, 0::2] = 0x40
+    w2s[0, 1::2] = 0x48
+    gsc[0] = [0.5, 1.0, 0.25]
+    wr = np.empty((E, H), np.float32)
+    wr[0] = 0.01
+    wr[1] = -0.01
+    layer = synth.Layer(w, wr, None, w13c, w13s, w2c, w2s, gsc)
+    x = np.zeros((1, H), np.uint16)
+    x[0, 0::2] = 0x3F80
+    out = oracle.moe_layer(layer, x)
+    ex = spec["expected"]
+    assert out["ids"].tolist() == [ex["ids"]]
+    assert out["weights"].tolist() == [ex["weights"]]
+    assert np.allclose(out["y64"][0, 0::2], ex["y64_even_c"], rtol=1e-14, atol=0)
+    assert np.allclose(out["y64"][0, 1::2], ex["y64_odd_c"], rtol=1e-14, atol=0)
+    assert np.all(out["y"][0, 0::2] == int(ex["y_bf16_even_c"], 16))
+    assert np.all(out["y"][0, 1::2] == int(ex["y_bf16_odd_c"], 16))
+
+
+def test_shared_gate_of_zero_vector_is_one_half():
+    w = synth.dataclasses.replace(synth.WORKLOADS["decode_e512_top10_shared"], num_experts=12,
+                                  hidden=256, inter=128, shared_inter=128)
+    layer = synth.make_layer(w)
+    x = synth.make_tokens(w, tokens=1)
+    layer.shared_gate = np.zeros_like(layer.shared_gate)
+    with_shared = oracle.moe_layer(layer, x)
+    w0 = synth.dataclasses.replace(w, shared_inter=0)
+    routed_only = oracle.moe_layer(synth.dataclasses.replace(layer, workload=w0), x)
+    o_s = oracle.expert_output(layer, 0, x[0], shared=True)
+    diff = with_shared["y64"][0] - routed_only["y64"][0]
+    assert np.allclose(diff, 0.5 * o_s, rtol=1e-9, atol=1e-12 * np.abs(o_s).max())
+    assert np.array_equal(with_shared["ids"], routed_only["ids"])
+
+
+def test_given_routes_reproduce_computed_routes():
+    w = synth.WORKLOADS["tiny_e8_top2"]
+    layer = synth.make_layer(w)
+    x = synth.make_tokens(w, tokens=3)
+    a = oracle.moe_layer(layer, x)
+    b = oracle.moe_layer(layer, x, ids=a["ids"], weights=a["weights"])
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["y64"], b["y64"])
+
+
+def test_expert_output_matches_layer_with_single_route():
+    w = synth.WORKLOADS["tiny_e8_top2"]
+    layer = synth.make_layer(w)
+    x = synth.make_tokens(w, tokens=1)
+    ids = np.array([[5, 2]], np.int32)
+    wts = np.array([[1.0, 0.0]], np.float32)
+    out = oracle.moe_layer(layer, x, ids=ids, weights=wts)
+    o5 = oracle.expert_output(layer, 5, x[0])
+    assert np.array_equal(out["y64"][0], o5)
