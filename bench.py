@@ -1,0 +1,184 @@
+"""Benchmark: NVFP4 MoE decode layer calls/s and achieved HBM bandwidth, batch 1.
+
+One step = one call of the whole decode hot path (router, top-k, gate|up GEMV
+with in-register dequant and clamped SwiGLU, down GEMV, weighted combine and
+shared expert) on one token, through the C ABI (ft_moe_nvfp4_decode).
+
+Inputs are synthetic and already resident in HBM when timing starts.  Calls
+cycle over L distinct layer instances (different weights and activations) so
+that the bytes touched per cycle exceed 4x the 256 MB Infinity Cache: the
+measured bandwidth is HBM bandwidth, not cache bandwidth.
+
+Prints one JSON line (rank 0, N = 1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E peak, 8 TB/s
+MALL_BYTES = 256 << 20      # Infinity Cache
+METRIC = "NVFP4 MoE decode: layer calls/s + achieved HBM GB/s (% of peak), batch 1"
+
+
+def algorithmic_bytes(w, ids: np.ndarray) -> int:
+    """Bytes a call must move at least once: the router weights, the activations
+    in and out, and the codes, scales and global scales of every distinct
+    selected expert (plus the shared expert and its gate vector)."""
+    H, I = w.hidden, w.inter
+    per_expert = (2 * I * H) // 2 + (2 * I * H) // 16 + (H * I) // 2 + (H * I) // 16 + 12
+    b = w.num_experts * H * 4                  # router weights, fp32
+    if w.hot_experts > 0:
+        b += w.num_experts * 4                 # router bias
+    T = ids.shape[0]
+    b += 2 * T * H * 2                         # x in, y out (bf16)
+    b += len(np.unique(ids)) * per_expert
+    if w.shared_inter > 0:
+        Is = w.shared_inter
+        b += (2 * Is * H) // 2 + (2 * Is * H) // 16 + (H * Is) // 2 + (H * Is) // 16 + 12
+        b += H * 2                             # shared gate vector
+    return b
+
+
+def cpu_baseline(w, seconds: float = 12.0) -> dict:
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    from nvfp4_mixture_experts_amd import synth
+    layer = synth.make_layer(w)
+    x = synth.make_tokens(w, tokens=64, stream="cpu_baseline")
+    oracle.moe_layer(layer, x[:1])                    # warm-up (and library load)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        i = n % x.shape[0]
+        oracle.moe_layer(layer, x[i:i + w.tokens])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n / el, "unit": "calls/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} single-token calls of {w.name} on instance 0, {el:.1f} s, "
+                      f"single-threaded C oracle (fp64), host {platform.processor() or 'cpu'}, "
+                      f"nproc {os.cpu_count()}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4800)
+    ap.add_argument("--warmup", type=int, default=480)
+    ap.add_argument("--workload", default="decode_e288_top8")
+    ap.add_argument("--instances", type=int, default=0,
+                    help="distinct layer instances to cycle (0 = enough to exceed 4x the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the layer's sharding is described in DESIGN.md); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from nvfp4_mixture_experts_amd import device, ftmoe, synth
+
+    w = synth.WORKLOADS[args.workload]
+    if w.tokens > 64:
+        print(f"{w.name} is not a decode workload", file=sys.stderr)
+        return 2
+    ftmoe.ft_init(0)
+    dev = torch.device("cuda:0")
+
+    # ---- layer instances, generated and repacked on the device
+    per_call_guess = algorithmic_bytes(w, np.zeros((w.tokens, w.top_k)) + np.arange(w.top_k))
+    L = args.instances or max(2, math.ceil(4 * MALL_BYTES / per_call_guess))
+    layers, xs = [], []
+    for l in range(L):
+        d = synth.make_layer_device(w, l, dev)
+        dl = device.upload_canonical(w, d["w_router"], d["bias"], d["routed"], d["shared"],
+                                     d["shared_gate"], dev)
+        del d
+        layers.append(dl)
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed + 7919 * l + 1)
+        xs.append(torch.randn((w.tokens, w.hidden), generator=g, device=dev).to(torch.bfloat16))
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    desc = layers[0].desc
+    ws = ftmoe.alloc_workspace(desc, w.tokens, ftmoe.PATH_DECODE, dev)
+    y = torch.empty((w.tokens, w.hidden), dtype=torch.bfloat16, device=dev)
+    ids_all = torch.empty((L, w.tokens, w.top_k), dtype=torch.int32, device=dev)
+    wts = torch.empty((w.tokens, w.top_k), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        dl = layers[i % L]
+        ftmoe.ft_moe_nvfp4_decode(desc, xs[i % L], dl.w_router, dl.bias, dl.routed, dl.shared,
+                                  dl.shared_gate, y, ws, ids_all[i % L], wts, stream=stream)
+
+    for i in range(max(args.warmup, L)):
+        call(i)
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+    calls_per_s = 1000.0 / ms_per_step
+
+    ids_np = ids_all.cpu().numpy()
+    bytes_per_call = float(np.mean([algorithmic_bytes(w, ids_np[l]) for l in range(L)]))
+    gbps = bytes_per_call / (ms_per_step * 1e-3) / 1e9
+    touched = bytes_per_call * L
+
+    out = {
+        "metric": METRIC,
+        "value": round(calls_per_s, 1),
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "experts": w.num_experts, "hidden": w.hidden,
+                   "inter": w.inter, "top_k": w.top_k, "tokens": w.tokens,
+                   "shared_inter": w.shared_inter, "layer_instances": L,
+                   "bytes_touched_per_cycle": int(touched)},
+        "achieved_gbps": round(gbps, 1),
+        "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"kernel": "ft_moe_nvfp4_decode (whole call)", "bound": "hbm",
+                     "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(round(bytes_per_call))},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,180 @@
+/*
+ * ftmoe.h -- C ABI of libftmoe.so: the NVFP4-weight mixture-of-experts layer
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (FreeToken commit log, page 2: the 288-expert NVFP4 MoE entry, and
+ * the entry with 512 routed experts, top-10, plus a gated shared expert; the
+ * clamped-SwiGLU entry; the MoE router / shared gate kernels and the
+ * non-power-of-2 top-k router entry.  FreeToken fork PR #84, page 1: the bullet
+ * on #631, the NVFP4 MoE decode GEMV run in every layer at every decode step,
+ * and the bullet on #578, NVFP4 prefill experts):
+ *
+ *   logit[t,e] = sum_h Wr[e,h] x[t,h] (+ bias[e])          router, fp64 sum, one fp32 rounding
+ *   ids[t,:]   = top-k experts by (logit desc, index asc)   a NaN logit ranks below every number
+ *   w[t,i]     = softmax over the k selected logits          fp32
+ *   for each selected expert e (NVFP4 weights, see below):
+ *     gate_r = sum_h Wg[r,h] x_h,  up_r = sum_h Wu[r,h] x_h
+ *     h_r    = silu(gate_r) * up_r                                       (act 0)
+ *            = silu(min(gate_r, gate_max)) * clamp(up_r, -up_absmax, up_absmax)  (act 1)
+ *     o_c    = sum_r Wd[c,r] h_r
+ *   y[t,c] = bf16( sum_i w[t,i] o_{ids[t,i]}[c]  +  sigmoid(sum_h gs[h] x[t,h]) o_shared[c] )
+ *
+ * NVFP4 weights: each element is a 4-bit e2m1 code (OCP Microscaling v1.0), each
+ * run of 16 consecutive K elements of a row shares one e4m3 scale byte (OCP 8-bit
+ * Floating Point), and each tensor (gate, up, down of each expert) has one fp32
+ * global scale.  The dequantised weight is fp32(fp32(e2m1 * e4m3) * global).
+ *
+ * Canonical layout (the input of ft_nvfp4_repack), per bank of n experts with
+ * hidden size H and intermediate size I:
+ *   w13 codes   u8  [n][2I][H/2]   rows 0..I-1 are gate, rows I..2I-1 are up;
+ *                                  byte k/2 of a row holds element k in its low
+ *                                  nibble when k is even, in its high nibble when odd
+ *   w13 scales  u8  [n][2I][H/16]  e4m3, scale of elements 16j..16j+15 at byte j
+ *   w2 codes    u8  [n][H][I/2]
+ *   w2 scales   u8  [n][H][I/16]
+ *   global      f32 [n][3]         (gate, up, down)
+ * The repacked layout that the compute entry points read is private to the
+ * library; its sizes come from ft_nvfp4_repacked_bytes.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless the comment says host.  The caller
+ *    allocates every buffer and keeps it alive until the work enqueued on the
+ *    stream has finished; the library keeps no pointer after it returns.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every compute call only
+ *    enqueues work on it: it never synchronises, never copies between host and
+ *    device and never allocates, so it may be captured into a HIP graph.
+ *  - Return value: FT_OK, or a negative ft_status; ft_last_error() then holds a
+ *    message (thread-local, valid until the next call on the same thread).
+ *    Arguments are checked on the host before anything is enqueued; values that
+ *    live in device memory (for example ids passed to ft_moe_nvfp4_prefill) are
+ *    the caller's responsibility and are not checked.
+ *  - Identical inputs give identical output bits, independent of buffer
+ *    addresses, stream and graph replay (no floating-point atomics).
+ *  - Supported shapes: hidden % 256 == 0 and hidden <= 8192; inter % 64 == 0 and
+ *    inter <= 4096 (shared_inter likewise, or 0); 1 <= top_k <= min(E, 16);
+ *    E <= 1024.  Other shapes return FT_EUNSUPPORTED.
+ */
+#ifndef FTMOE_H
+#define FTMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FT_ABI_VERSION 1
+
+typedef int32_t ft_status;
+#define FT_OK 0
+#define FT_EINVAL (-1)        /* null pointer, negative size, inconsistent arguments */
+#define FT_EUNSUPPORTED (-2)  /* valid but outside the supported shapes */
+#define FT_EWORKSPACE (-3)    /* workspace missing or smaller than ft_moe_workspace_bytes */
+#define FT_EHIP (-4)          /* a HIP runtime call failed; the message names it */
+
+typedef struct ft_moe_desc {
+    int32_t num_experts;   /* E, routed experts */
+    int32_t hidden;        /* H */
+    int32_t inter;         /* I, intermediate size of each routed expert */
+    int32_t top_k;         /* k */
+    int32_t act;           /* 0 = SwiGLU, 1 = clamped SwiGLU */
+    float gate_max;        /* act 1: gate is clamped above at gate_max (7.0 in the workloads) */
+    float up_absmax;       /* act 1: up is clamped to [-up_absmax, up_absmax] (7.0) */
+    int32_t shared_inter;  /* intermediate size of the gated shared expert; 0 = none */
+} ft_moe_desc;
+
+/* One repacked NVFP4 expert bank (routed: n = num_experts; shared: n = 1). */
+typedef struct ft_nvfp4_experts {
+    const uint8_t *w13;        /* repacked gate|up codes */
+    const uint8_t *w13_scale;  /* repacked gate|up e4m3 scales */
+    const uint8_t *w2;         /* repacked down codes */
+    const uint8_t *w2_scale;   /* repacked down e4m3 scales */
+    const float *global_scale; /* f32 [n][3]: gate, up, down */
+} ft_nvfp4_experts;
+
+/* FT_ABI_VERSION of the library that was loaded. */
+int32_t ft_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none).  Host string. */
+const char *ft_last_error(void);
+
+/* Makes `device` current and caches its properties (CU count).  Call once per
+ * device before the compute calls, outside stream capture. */
+ft_status ft_init(int32_t device);
+
+/* Bytes of repacked part `part` (0 w13 codes, 1 w13 scales, 2 w2 codes,
+ * 3 w2 scales) for a bank of n experts of size (hidden, inter).  Returns 0 for
+ * invalid arguments. */
+size_t ft_nvfp4_repacked_bytes(int32_t hidden, int32_t inter, int32_t n_experts, int32_t part);
+
+/* Load-time layout conversion, from the canonical layout above into the layout
+ * the compute entry points read ("avoid layout conversions in nvfp4 marlin
+ * decode": FreeToken fork PR #84, bullet on #631 -- the conversion moves to
+ * load time).  Byte-preserving: every code and scale byte is moved, none is
+ * changed.  The gate|up tensors stay row-major (one wave reads a row's codes as
+ * contiguous 16-byte lanes); the down tensors become K-chunk-major, [n][I/32][H]
+ * records of 16 code bytes and [n][I/32][H] records of 2 scale bytes, so that 64
+ * lanes reading 64 consecutive output rows read 1 KiB contiguous.
+ * Inputs are canonical device buffers; outputs are device buffers of
+ * ft_nvfp4_repacked_bytes() bytes each (no overlap with the inputs). */
+ft_status ft_nvfp4_repack(int32_t hidden, int32_t inter, int32_t n_experts,
+                          const uint8_t *w13, const uint8_t *w13_scale,
+                          const uint8_t *w2, const uint8_t *w2_scale,
+                          uint8_t *out_w13, uint8_t *out_w13_scale,
+                          uint8_t *out_w2, uint8_t *out_w2_scale, void *stream);
+
+/* Workspace bytes needed by ft_moe_route (path 0), ft_moe_nvfp4_decode (path 1)
+ * or ft_moe_nvfp4_prefill (path 2) for `tokens` tokens.  Returns 0 for invalid
+ * arguments.  The workspace must be zero-filled once before its first use; the
+ * library leaves it reusable after every call that returned FT_OK.  Calls that
+ * share one workspace must not run concurrently. */
+size_t ft_moe_workspace_bytes(const ft_moe_desc *desc, int64_t tokens, int32_t path);
+
+/* Router only: fp64 logits, top-k (ties to the lower index) and softmax
+ * weights of the selected logits.
+ *   x         bf16 [T][H]      w_router f32 [E][H]      bias f32 [E] or NULL
+ *   topk_ids  i32  [T][k]      topk_w   f32 [T][k]      (outputs, rank order)
+ * T >= 0 (T == 0 enqueues nothing). */
+ft_status ft_moe_route(const ft_moe_desc *desc, int64_t tokens, const uint16_t *x,
+                       const float *w_router, const float *bias, int32_t *topk_ids,
+                       float *topk_w, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The whole layer for decode batches (1 <= T <= 64): routing, the gate|up GEMV
+ * with in-register dequantisation and (clamped) SwiGLU, the down GEMV, the
+ * weighted combine and the gated shared expert.
+ *   x bf16 [T][H]; w_router f32 [E][H]; bias f32 [E] or NULL
+ *   routed: repacked bank of E experts; shared: repacked bank of 1 expert, or
+ *   NULL when desc->shared_inter == 0; shared_gate bf16 [H] (NULL when no shared)
+ *   topk_ids_out i32 [T][k], topk_w_out f32 [T][k]: optional side outputs (NULL ok)
+ *   y bf16 [T][H] (output) */
+ft_status ft_moe_nvfp4_decode(const ft_moe_desc *desc, int64_t tokens, const uint16_t *x,
+                              const float *w_router, const float *bias,
+                              const ft_nvfp4_experts *routed, const ft_nvfp4_experts *shared,
+                              const uint16_t *shared_gate, int32_t *topk_ids_out,
+                              float *topk_w_out, uint16_t *y, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* The expert part of the layer for prefill chunks, given routes from
+ * ft_moe_route (ids must lie in [0, E); not checked on the host).
+ *   x bf16 [T][H]; topk_ids i32 [T][k]; topk_w f32 [T][k]; y bf16 [T][H] (output)
+ *   shared / shared_gate as for decode. */
+ft_status ft_moe_nvfp4_prefill(const ft_moe_desc *desc, int64_t tokens, const uint16_t *x,
+                               const int32_t *topk_ids, const float *topk_w,
+                               const ft_nvfp4_experts *routed, const ft_nvfp4_experts *shared,
+                               const uint16_t *shared_gate, uint16_t *y, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Test export: dequantise tensor `tensor` (0 gate [I][H], 1 up [I][H],
+ * 2 down [H][I]) of expert `expert` of a repacked bank into a row-major fp32
+ * (out_dtype 0) or bf16 (out_dtype 1) matrix, with the same device routine the
+ * compute kernels use.  `inter` is the bank's intermediate size. */
+ft_status ft_nvfp4_dequant(int32_t hidden, int32_t inter, int32_t n_experts,
+                           const ft_nvfp4_experts *bank, int32_t expert, int32_t tensor,
+                           int32_t out_dtype, void *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FTMOE_H */

@@ -1,0 +1,403 @@
+// abi.cpp -- the exported C ABI of libftmoe.so (declared in include/ftmoe.h):
+// argument validation, workspace layout and kernel dispatch.  Everything here
+// runs on the host; compute calls only enqueue kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/ftmoe.h"
+#include "ftmoe_kernels.hpp"
+
+using namespace ftmoe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ft_status fail(ft_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+ft_status ok() {
+  g_err[0] = '\0';
+  return FT_OK;
+}
+
+ft_status hip_fail(hipError_t e, const char* what) {
+  return fail(FT_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxDecodeTokens = 64;
+constexpr int kRowGroup = 64;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+bool inter_ok(int I) { return I >= 64 && I <= 4096 && I % 64 == 0; }
+
+ft_status check_desc(const ft_moe_desc* d) {
+  if (!d) return fail(FT_EINVAL, "desc is NULL");
+  if (d->num_experts <= 0 || d->hidden <= 0 || d->inter <= 0 || d->top_k <= 0 ||
+      d->shared_inter < 0)
+    return fail(FT_EINVAL, "desc has a non-positive size");
+  if (d->top_k > d->num_experts)
+    return fail(FT_EINVAL, "top_k %d exceeds num_experts %d", d->top_k, d->num_experts);
+  if (d->act != 0 && d->act != 1) return fail(FT_EINVAL, "act must be 0 or 1");
+  if (d->num_experts > kMaxExperts)
+    return fail(FT_EUNSUPPORTED, "num_experts %d > %d", d->num_experts, kMaxExperts);
+  if (d->top_k > kMaxTopK) return fail(FT_EUNSUPPORTED, "top_k %d > %d", d->top_k, kMaxTopK);
+  int lpr = 0, cpl = 0;
+  gateup_geometry(d->hidden, &lpr, &cpl);
+  if (d->hidden % 256 != 0 || d->hidden > 8192 || lpr == 0 || cpl < 1 || cpl > 4)
+    return fail(FT_EUNSUPPORTED, "hidden %d unsupported (multiple of 256, <= 8192)", d->hidden);
+  if (!inter_ok(d->inter))
+    return fail(FT_EUNSUPPORTED, "inter %d unsupported (multiple of 64 in [64, 4096])", d->inter);
+  if (d->shared_inter != 0 && !inter_ok(d->shared_inter))
+    return fail(FT_EUNSUPPORTED, "shared_inter %d unsupported", d->shared_inter);
+  return FT_OK;
+}
+
+ft_status check_bank(const ft_nvfp4_experts* b, const char* name) {
+  if (!b) return fail(FT_EINVAL, "%s bank is NULL", name);
+  if (!b->w13 || !b->w13_scale || !b->w2 || !b->w2_scale || !b->global_scale)
+    return fail(FT_EINVAL, "%s bank has a NULL pointer", name);
+  if (!aligned16(b->w13) || !aligned16(b->w13_scale) || !aligned16(b->w2) ||
+      !aligned16(b->w2_scale) || !aligned16(b->global_scale))
+    return fail(FT_EINVAL, "%s bank pointers must be 16-byte aligned", name);
+  return FT_OK;
+}
+
+Bank to_bank(const ft_nvfp4_experts* b, int inter) {
+  Bank r{};
+  if (b) {
+    r.w13 = b->w13;
+    r.w13s = b->w13_scale;
+    r.w2 = b->w2;
+    r.w2s = b->w2_scale;
+    r.gsc = b->global_scale;
+    r.inter = inter;
+  }
+  return r;
+}
+
+// Workspace regions.  The route counter sits at offset 0 for every path and is
+// reset by the kernel that uses it; the down-projection counters are cleared by
+// the first kernel of each call, so a workspace may be shared between paths
+// and token counts once it has been zero-filled.
+struct Layout {
+  size_t cnt_route, cnt_down, logits, gamma, ids, w, h, part, total;
+};
+
+Layout layout(const ft_moe_desc& d, int64_t T, int path) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t t = static_cast<size_t>(T);
+  const size_t nrg = static_cast<size_t>(d.hidden / kRowGroup);
+  const size_t k = static_cast<size_t>(d.top_k);
+  const size_t imax = static_cast<size_t>(d.inter > d.shared_inter ? d.inter : d.shared_inter);
+  const size_t nslots = k + (d.shared_inter > 0 ? 1 : 0);
+  L.cnt_route = take(256);
+  L.cnt_down = take(path == 0 ? 0 : t * nrg * 4);
+  L.logits = take(path == 2 ? 0 : t * static_cast<size_t>(d.num_experts) * 4);
+  L.gamma = take(t * 4);
+  L.ids = take(t * k * 4);
+  L.w = take(t * k * 4);
+  L.h = take(path == 0 ? 0 : t * (k + 1) * imax * 4);
+  L.part = take(path == 0 ? 0 : t * nrg * nslots * kRowGroup * 4);
+  L.total = off;
+  return L;
+}
+
+ft_status check_ws(const ft_moe_desc* d, int64_t T, int path, void* ws, size_t ws_bytes,
+                          Layout* L) {
+  *L = layout(*d, T, path);
+  if (!ws) return fail(FT_EWORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u)
+    return fail(FT_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < L->total)
+    return fail(FT_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, L->total);
+  return FT_OK;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+ft_status check_layer_args(const ft_moe_desc* desc, const uint16_t* x,
+                                  const ft_nvfp4_experts* routed, const ft_nvfp4_experts* shared,
+                                  const uint16_t* shared_gate, const uint16_t* y) {
+  ft_status st;
+  if (!x || !y) return fail(FT_EINVAL, "x or y is NULL");
+  if (!aligned16(x)) return fail(FT_EINVAL, "x must be 16-byte aligned");
+  if (!aligned16(y)) return fail(FT_EINVAL, "y must be 16-byte aligned");
+  if ((st = check_bank(routed, "routed")) != FT_OK) return st;
+  if (desc->shared_inter > 0) {
+    if ((st = check_bank(shared, "shared")) != FT_OK) return st;
+    if (!shared_gate) return fail(FT_EINVAL, "shared_gate is NULL with a shared expert");
+    if (!aligned16(shared_gate)) return fail(FT_EINVAL, "shared_gate must be 16-byte aligned");
+  }
+  return FT_OK;
+}
+
+// gate|up then down/combine, given routes in ids/w and gamma in the workspace.
+ft_status run_experts(const ft_moe_desc* desc, int T, const uint16_t* x,
+                             const int32_t* ids, const float* w, const ft_nvfp4_experts* routed,
+                             const ft_nvfp4_experts* shared, uint16_t* y, void* ws,
+                             const Layout& L, hipStream_t s) {
+  const bool has_shared = desc->shared_inter > 0;
+  GateUpParams g{};
+  g.x = x;
+  g.T = T;
+  g.H = desc->hidden;
+  g.k = desc->top_k;
+  g.routed = to_bank(routed, desc->inter);
+  g.shared = has_shared ? to_bank(shared, desc->shared_inter) : Bank{};
+  g.ids = ids;
+  g.h = at<float>(ws, L.h);
+  g.Imax = desc->inter > desc->shared_inter ? desc->inter : desc->shared_inter;
+  g.act = desc->act;
+  g.gate_max = desc->gate_max;
+  g.up_absmax = desc->up_absmax;
+  hipError_t e = launch_gateup(g, s);
+  if (e != hipSuccess) return hip_fail(e, "gate|up kernel");
+
+  DownParams d{};
+  d.T = T;
+  d.H = desc->hidden;
+  d.k = desc->top_k;
+  d.nslots = desc->top_k + (has_shared ? 1 : 0);
+  d.routed = g.routed;
+  d.shared = g.shared;
+  d.ids = ids;
+  d.w = w;
+  d.gamma = has_shared ? at<float>(ws, L.gamma) : nullptr;
+  d.h = g.h;
+  d.Imax = g.Imax;
+  d.part = at<float>(ws, L.part);
+  d.cnt = at<uint32_t>(ws, L.cnt_down);
+  d.y = y;
+  e = launch_down(d, s);
+  if (e != hipSuccess) return hip_fail(e, "down kernel");
+  return FT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ft_abi_version(void) { return FT_ABI_VERSION; }
+
+const char* ft_last_error(void) { return g_err; }
+
+ft_status ft_init(int32_t device) {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device < 0 || device >= n) return fail(FT_EINVAL, "device %d out of range [0, %d)", device, n);
+  e = hipSetDevice(device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(FT_EUNSUPPORTED, "device %d is %s; this library is built for gfx950", device,
+                prop.gcnArchName);
+  return ok();
+}
+
+size_t ft_nvfp4_repacked_bytes(int32_t hidden, int32_t inter, int32_t n_experts, int32_t part) {
+  if (hidden <= 0 || inter <= 0 || n_experts <= 0 || hidden % 32 || inter % 32) return 0;
+  const size_t n = static_cast<size_t>(n_experts), H = static_cast<size_t>(hidden),
+               I = static_cast<size_t>(inter);
+  switch (part) {
+    case 0: return n * 2 * I * H / 2;
+    case 1: return n * 2 * I * H / 16;
+    case 2: return n * H * I / 2;
+    case 3: return n * H * I / 16;
+    default: return 0;
+  }
+}
+
+ft_status ft_nvfp4_repack(int32_t hidden, int32_t inter, int32_t n_experts, const uint8_t* w13,
+                          const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                          uint8_t* out_w13, uint8_t* out_w13_scale, uint8_t* out_w2,
+                          uint8_t* out_w2_scale, void* stream) {
+  if (hidden <= 0 || inter <= 0 || n_experts <= 0)
+    return fail(FT_EINVAL, "repack: non-positive size");
+  if (hidden % 256 || !inter_ok(inter))
+    return fail(FT_EUNSUPPORTED, "repack: hidden %d / inter %d unsupported", hidden, inter);
+  const void* ptrs[8] = {w13, w13_scale, w2, w2_scale, out_w13, out_w13_scale, out_w2, out_w2_scale};
+  for (const void* p : ptrs) {
+    if (!p) return fail(FT_EINVAL, "repack: NULL pointer");
+    if (!aligned16(p)) return fail(FT_EINVAL, "repack: pointers must be 16-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(out_w13, w13, ft_nvfp4_repacked_bytes(hidden, inter, n_experts, 0),
+                                hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "repack w13");
+  e = hipMemcpyAsync(out_w13_scale, w13_scale, ft_nvfp4_repacked_bytes(hidden, inter, n_experts, 1),
+                     hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "repack w13 scales");
+  e = launch_repack_w2(hidden, inter, n_experts, w2, w2_scale, out_w2, out_w2_scale, s);
+  if (e != hipSuccess) return hip_fail(e, "repack w2");
+  return ok();
+}
+
+size_t ft_moe_workspace_bytes(const ft_moe_desc* desc, int64_t tokens, int32_t path) {
+  if (check_desc(desc) != FT_OK || tokens < 0 || path < 0 || path > 2) return 0;
+  return layout(*desc, tokens, path).total;
+}
+
+ft_status ft_moe_route(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,
+                       const float* w_router, const float* bias, int32_t* topk_ids, float* topk_w,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  ft_status st = check_desc(desc);
+  if (st != FT_OK) return st;
+  if (tokens < 0) return fail(FT_EINVAL, "tokens < 0");
+  if (tokens > (1 << 24)) return fail(FT_EUNSUPPORTED, "tokens > 2^24");
+  if (!x || !w_router || !topk_ids || !topk_w) return fail(FT_EINVAL, "route: NULL pointer");
+  if (!aligned16(x) || !aligned16(w_router))
+    return fail(FT_EINVAL, "route: x and w_router must be 16-byte aligned");
+  Layout L;
+  if ((st = check_ws(desc, tokens, 0, workspace, workspace_bytes, &L)) != FT_OK) return st;
+  if (tokens == 0) return ok();
+  RouteParams p{};
+  p.x = x;
+  p.wr = w_router;
+  p.bias = bias;
+  p.shared_gate = nullptr;
+  p.T = static_cast<int>(tokens);
+  p.E = desc->num_experts;
+  p.H = desc->hidden;
+  p.k = desc->top_k;
+  p.logits = at<float>(workspace, L.logits);
+  p.gamma = nullptr;
+  p.ids = topk_ids;
+  p.w = topk_w;
+  p.counter = at<uint32_t>(workspace, L.cnt_route);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fuse = tokens <= kMaxDecodeTokens;
+  hipError_t e = launch_route(p, fuse, s);
+  if (e != hipSuccess) return hip_fail(e, "route kernel");
+  if (!fuse) {
+    e = launch_topk(p, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k kernel");
+  }
+  return ok();
+}
+
+ft_status ft_moe_nvfp4_decode(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,
+                              const float* w_router, const float* bias,
+                              const ft_nvfp4_experts* routed, const ft_nvfp4_experts* shared,
+                              const uint16_t* shared_gate, int32_t* topk_ids_out,
+                              float* topk_w_out, uint16_t* y, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  ft_status st = check_desc(desc);
+  if (st != FT_OK) return st;
+  if (tokens < 1 || tokens > kMaxDecodeTokens)
+    return fail(tokens < 1 ? FT_EINVAL : FT_EUNSUPPORTED, "decode takes 1..%d tokens, got %lld",
+                kMaxDecodeTokens, static_cast<long long>(tokens));
+  if (!w_router) return fail(FT_EINVAL, "w_router is NULL");
+  if (!aligned16(w_router)) return fail(FT_EINVAL, "w_router must be 16-byte aligned");
+  if ((st = check_layer_args(desc, x, routed, shared, shared_gate, y)) != FT_OK) return st;
+  Layout L;
+  if ((st = check_ws(desc, tokens, 1, workspace, workspace_bytes, &L)) != FT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool has_shared = desc->shared_inter > 0;
+
+  RouteParams p{};
+  p.x = x;
+  p.wr = w_router;
+  p.bias = bias;
+  p.shared_gate = has_shared ? shared_gate : nullptr;
+  p.T = static_cast<int>(tokens);
+  p.E = desc->num_experts;
+  p.H = desc->hidden;
+  p.k = desc->top_k;
+  p.logits = at<float>(workspace, L.logits);
+  p.gamma = at<float>(workspace, L.gamma);
+  p.ids = at<int32_t>(workspace, L.ids);
+  p.w = at<float>(workspace, L.w);
+  p.ids_copy = topk_ids_out;
+  p.w_copy = topk_w_out;
+  p.counter = at<uint32_t>(workspace, L.cnt_route);
+  p.zero = at<uint32_t>(workspace, L.cnt_down);
+  p.nzero = static_cast<int>(tokens) * (desc->hidden / kRowGroup);
+  hipError_t e = launch_route(p, true, s);
+  if (e != hipSuccess) return hip_fail(e, "route kernel");
+  st = run_experts(desc, p.T, x, p.ids, p.w, routed, shared, y, workspace, L, s);
+  if (st != FT_OK) return st;
+  return ok();
+}
+
+ft_status ft_moe_nvfp4_prefill(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,
+                               const int32_t* topk_ids, const float* topk_w,
+                               const ft_nvfp4_experts* routed, const ft_nvfp4_experts* shared,
+                               const uint16_t* shared_gate, uint16_t* y, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  ft_status st = check_desc(desc);
+  if (st != FT_OK) return st;
+  if (tokens < 0) return fail(FT_EINVAL, "tokens < 0");
+  if (tokens > 65535) return fail(FT_EUNSUPPORTED, "prefill takes at most 65535 tokens per call");
+  if (!topk_ids || !topk_w) return fail(FT_EINVAL, "topk_ids or topk_w is NULL");
+  if ((st = check_layer_args(desc, x, routed, shared, shared_gate, y)) != FT_OK) return st;
+  Layout L;
+  if ((st = check_ws(desc, tokens, 2, workspace, workspace_bytes, &L)) != FT_OK) return st;
+  if (tokens == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool has_shared = desc->shared_inter > 0;
+  {
+    // shared expert gate (when there is one) and the clearing of this call's counters
+    RouteParams p{};
+    p.x = x;
+    p.shared_gate = has_shared ? shared_gate : nullptr;
+    p.T = static_cast<int>(tokens);
+    p.E = 0;
+    p.H = desc->hidden;
+    p.k = desc->top_k;
+    p.gamma = at<float>(workspace, L.gamma);
+    p.zero = at<uint32_t>(workspace, L.cnt_down);
+    p.nzero = static_cast<int>(tokens) * (desc->hidden / kRowGroup);
+    hipError_t e = launch_route(p, false, s);
+    if (e != hipSuccess) return hip_fail(e, "shared gate kernel");
+  }
+  st = run_experts(desc, static_cast<int>(tokens), x, topk_ids, topk_w, routed, shared, y,
+                   workspace, L, s);
+  if (st != FT_OK) return st;
+  return ok();
+}
+
+ft_status ft_nvfp4_dequant(int32_t hidden, int32_t inter, int32_t n_experts,
+                           const ft_nvfp4_experts* bank, int32_t expert, int32_t tensor,
+                           int32_t out_dtype, void* out, void* stream) {
+  if (hidden <= 0 || inter <= 0 || n_experts <= 0) return fail(FT_EINVAL, "dequant: bad size");
+  if (hidden % 256 || !inter_ok(inter))
+    return fail(FT_EUNSUPPORTED, "dequant: hidden %d / inter %d unsupported", hidden, inter);
+  if (expert < 0 || expert >= n_experts) return fail(FT_EINVAL, "dequant: expert out of range");
+  if (tensor < 0 || tensor > 2) return fail(FT_EINVAL, "dequant: tensor must be 0, 1 or 2");
+  if (out_dtype != 0 && out_dtype != 1) return fail(FT_EINVAL, "dequant: out_dtype must be 0 or 1");
+  if (!out) return fail(FT_EINVAL, "dequant: out is NULL");
+  ft_status st = check_bank(bank, "dequant");
+  if (st != FT_OK) return st;
+  hipError_t e = launch_dequant(hidden, inter, to_bank(bank, inter), expert, tensor, out_dtype, out,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dequant kernel");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,163 @@
+// ftmoe_device.hpp -- device helpers shared by every gfx950 kernel of libftmoe:
+// the NVFP4 decode routine (the only place where codes and scales become
+// numbers), bf16 conversions and wave-level reductions.
+//
+// NVFP4 element codes are OCP e2m1 (Microscaling v1.0); block scales are OCP
+// e4m3 (8-bit Floating Point spec), one per 16 consecutive K elements; each
+// tensor carries one fp32 global scale.  The codes are the weights of the
+// NVFP4 MoE experts (FreeToken commit log, page 2, the 288- and 512-expert
+// NVFP4 MoE entries); decoding them in registers by bit placement rather than
+// through a lookup follows FreeToken fork PR #84 (page 1), the bullet on #578.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ftmoe {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ NVFP4 codec --
+
+// e4m3 byte (bits 7..0 of `b`) -> fp32, exactly (v_cvt_f32_fp8 decodes the OCP
+// E4M3 encoding on gfx950, subnormals and NaN included).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(b), 0);
+}
+
+// e4m3 byte `sel` (0..3) of a 32-bit word -> fp32.
+template <int Sel>
+__device__ __forceinline__ float e4m3_byte_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), Sel);
+}
+
+// Byte `Sel` of `w` holds two e2m1 codes (low nibble = even element): decode
+// both to fp32, exactly.  The hardware scale operand is 1.0 (an identity), the
+// NVFP4 e4m3 block scale is applied by the caller.
+template <int Sel>
+__device__ __forceinline__ f32x2 e2m1x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, Sel);
+}
+
+// Same two codes decoded to a packed bf16 pair (every e2m1 value is exact in bf16).
+template <int Sel>
+__device__ __forceinline__ bf16x2 e2m1x2_to_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, Sel);
+}
+
+// One dequantised weight: fp32(fp32(e2m1 * e4m3) * g).  The first product is
+// exact (at most 6 significant bits), so this is one rounding of the exact
+// value code * scale * g.  `pair` is the e2m1 pair decoded by e2m1x2_to_f32.
+__device__ __forceinline__ float dequant_one(float code_value, float scale, float g) {
+  return (code_value * scale) * g;
+}
+
+// ------------------------------------------------------------ bf16 helpers --
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ------------------------------------------------------- wave reductions --
+
+// Sum over aligned groups of `Width` lanes (Width a power of two <= 64); every
+// lane of a group ends with the group's sum.  Fixed butterfly order, so the
+// result does not depend on timing.
+template <int Width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = Width / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+template <int Width>
+__device__ __forceinline__ double group_sum(double v) {
+#pragma unroll
+  for (int off = Width / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// ------------------------------------------------------- chunk dot kernels --
+
+// A chunk is 32 consecutive K elements of one weight row: 16 code bytes (a
+// uint4) and 2 e4m3 scale bytes (one per 16 elements).
+//
+// bf16 activations: x2[m] holds elements (2m, 2m+1) of the chunk as a packed bf16
+// pair.  Each e2m1 x bf16 product is exact in fp32; the 16-element block sums
+// are scaled by their e4m3 scale.  Returns sum_k code_k * scale_k * x_k.
+__device__ __forceinline__ float chunk_dot_bf16(const uint4 q, uint32_t sc2, const bf16x2* x2) {
+  float b0 = 0.0f, b1 = 0.0f;
+  b0 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<0>(q.x), x2[0], b0, false);
+  b0 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<1>(q.x), x2[1], b0, false);
+  b0 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<2>(q.x), x2[2], b0, false);
+  b0 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<3>(q.x), x2[3], b0, false);
+  b0 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<0>(q.y), x2[4], b0, false);
+  b0 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<1>(q.y), x2[5], b0, false);
+  b0 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<2>(q.y), x2[6], b0, false);
+  b0 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<3>(q.y), x2[7], b0, false);
+  b1 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<0>(q.z), x2[8], b1, false);
+  b1 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<1>(q.z), x2[9], b1, false);
+  b1 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<2>(q.z), x2[10], b1, false);
+  b1 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<3>(q.z), x2[11], b1, false);
+  b1 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<0>(q.w), x2[12], b1, false);
+  b1 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<1>(q.w), x2[13], b1, false);
+  b1 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<2>(q.w), x2[14], b1, false);
+  b1 = __builtin_amdgcn_fdot2_f32_bf16(e2m1x2_to_bf16<3>(q.w), x2[15], b1, false);
+  return b0 * e4m3_byte_to_f32<0>(sc2) + b1 * e4m3_byte_to_f32<1>(sc2);
+}
+
+// Four code bytes (8 elements) against 8 fp32 activations.
+__device__ __forceinline__ float word_dot_f32(uint32_t w, const float* h, float acc) {
+  f32x2 p0 = e2m1x2_to_f32<0>(w), p1 = e2m1x2_to_f32<1>(w);
+  f32x2 p2 = e2m1x2_to_f32<2>(w), p3 = e2m1x2_to_f32<3>(w);
+  acc = fmaf(p0.x, h[0], acc);
+  acc = fmaf(p0.y, h[1], acc);
+  acc = fmaf(p1.x, h[2], acc);
+  acc = fmaf(p1.y, h[3], acc);
+  acc = fmaf(p2.x, h[4], acc);
+  acc = fmaf(p2.y, h[5], acc);
+  acc = fmaf(p3.x, h[6], acc);
+  acc = fmaf(p3.y, h[7], acc);
+  return acc;
+}
+
+// fp32 activations h[0..31] (the SwiGLU output): the e2m1 codes are decoded to
+// fp32 and accumulated with fp32 FMAs, block sums scaled by their e4m3 scale.
+__device__ __forceinline__ float chunk_dot_f32(const uint4 q, uint32_t sc2, const float* h) {
+  float b0 = word_dot_f32(q.x, h, 0.0f);
+  b0 = word_dot_f32(q.y, h + 8, b0);
+  float b1 = word_dot_f32(q.z, h + 16, 0.0f);
+  b1 = word_dot_f32(q.w, h + 24, b1);
+  return b0 * e4m3_byte_to_f32<0>(sc2) + b1 * e4m3_byte_to_f32<1>(sc2);
+}
+
+// ------------------------------------------------------------- activation --
+
+// silu(z) = z / (1 + exp(-z)); for very negative z, exp(-z) overflows to +inf and
+// the quotient is -0 (never NaN).
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// act 0: silu(g) * u.  act 1: silu(min(g, gate_max)) * clamp(u, -up_absmax, up_absmax).
+// Written as compare-and-select so that a NaN input stays NaN.
+__device__ __forceinline__ float swiglu(int act, float g, float u, float gate_max,
+                                        float up_absmax) {
+  if (act == 1) {
+    g = (g > gate_max) ? gate_max : g;
+    u = (u > up_absmax) ? up_absmax : u;
+    u = (u < -up_absmax) ? -up_absmax : u;
+  }
+  return silu(g) * u;
+}
+
+}  // namespace ftmoe

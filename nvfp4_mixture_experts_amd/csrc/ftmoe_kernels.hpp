@@ -1,0 +1,76 @@
+// ftmoe_kernels.hpp -- internal interface between the C ABI layer (abi.cpp) and
+// the gfx950 kernels: parameter blocks and launchers.  Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ftmoe {
+
+// One repacked NVFP4 expert bank (see ft_nvfp4_repack for the layout).
+struct Bank {
+  const uint8_t* w13;   // [n][2I][H/2] row-major codes
+  const uint8_t* w13s;  // [n][2I][H/16] row-major e4m3 scales
+  const uint8_t* w2;    // [n][I/32][H][16] K-chunk-major codes
+  const uint8_t* w2s;   // [n][I/32][H][2] K-chunk-major e4m3 scales
+  const float* gsc;     // [n][3] gate, up, down global scales
+  int inter;            // I of this bank (0 = no bank)
+};
+
+// Router: logits, the shared expert's gate, and top-k with softmax weights.
+struct RouteParams {
+  const uint16_t* x;            // bf16 [T][H]
+  const float* wr;              // f32 [E][H]
+  const float* bias;            // f32 [E] or null
+  const uint16_t* shared_gate;  // bf16 [H] or null
+  int T, E, H, k;
+  float* logits;                // f32 [T][E]
+  float* gamma;                 // f32 [T] (sigmoid of the shared gate) or null
+  int32_t* ids;                 // i32 [T][k]
+  float* w;                     // f32 [T][k]
+  int32_t* ids_copy;            // optional second copy of ids (caller's side output)
+  float* w_copy;                // optional second copy of w
+  uint32_t* counter;            // last-arriver counter for the fused top-k
+  uint32_t* zero;               // counters of later kernels of the same call, cleared here
+  int nzero;
+};
+
+// Gate|up GEMV with in-register dequantisation and (clamped) SwiGLU.
+struct GateUpParams {
+  const uint16_t* x;  // bf16 [T][H]
+  int T, H, k;
+  Bank routed, shared;
+  const int32_t* ids; // i32 [T][k]
+  float* h;           // f32 [T][k+1][Imax]
+  int Imax;
+  int act;
+  float gate_max, up_absmax;
+};
+
+// Down GEMV, weighted combine over the selected experts and the shared expert.
+struct DownParams {
+  int T, H, k, nslots;  // nslots = k (+1 with a shared expert)
+  Bank routed, shared;
+  const int32_t* ids;   // i32 [T][k]
+  const float* w;       // f32 [T][k]
+  const float* gamma;   // f32 [T] or null
+  const float* h;       // f32 [T][k+1][Imax]
+  int Imax;
+  float* part;          // f32 [T][H/64][nslots][64] per-slot partial outputs
+  uint32_t* cnt;        // u32 [T][H/64] last-arriver counters
+  uint16_t* y;          // bf16 [T][H]
+};
+
+// Launchers: return the launch status (hipGetLastError after the launch).
+hipError_t launch_route(const RouteParams& p, bool fuse_topk, hipStream_t s);
+hipError_t launch_topk(const RouteParams& p, hipStream_t s);
+hipError_t launch_gateup(const GateUpParams& p, hipStream_t s);
+void gateup_geometry(int H, int* lpr, int* cpl);  // supported when lpr > 0 and 1 <= cpl <= 4
+hipError_t launch_down(const DownParams& p, hipStream_t s);
+hipError_t launch_repack_w2(int H, int I, int n, const uint8_t* w2, const uint8_t* w2s,
+                            uint8_t* out_w2, uint8_t* out_w2s, hipStream_t s);
+hipError_t launch_dequant(int H, int I, const Bank& b, int expert, int tensor, int out_dtype,
+                          void* out, hipStream_t s);
+
+}  // namespace ftmoe

@@ -1,0 +1,110 @@
+// repack.hip -- load-time NVFP4 layout conversion and the dequantisation test
+// export, gfx950.
+//
+// FreeToken fork PR #84 (page 1), bullet on #631 ("avoid layout conversions in
+// nvfp4 marlin decode"): the decode GEMV reads weights already arranged for it,
+// so the conversion happens once, when the weights are loaded.  The gate|up
+// tensors are already in the order the gate|up GEMV reads (row-major, 16-byte
+// chunks per lane); the down tensors are moved to K-chunk-major order so that 64
+// lanes owning 64 consecutive output rows read 1 KiB contiguous per load.
+#include "ftmoe_device.hpp"
+#include "ftmoe_kernels.hpp"
+
+namespace ftmoe {
+
+// canonical w2 codes [n][H][I/2] -> [n][I/32][H][16]; scales [n][H][I/16] -> [n][I/32][H][2]
+__global__ __launch_bounds__(256) void repack_w2_kernel(int H, int I, int n,
+                                                        const uint8_t* __restrict__ w2,
+                                                        const uint8_t* __restrict__ w2s,
+                                                        uint8_t* __restrict__ out_w2,
+                                                        uint8_t* __restrict__ out_w2s) {
+  const int nch = I / 32;
+  const size_t total = static_cast<size_t>(n) * H * nch;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    // destination order: (e, j, c)
+    const size_t c = i % H;
+    const size_t j = (i / H) % nch;
+    const size_t e = i / (static_cast<size_t>(H) * nch);
+    const size_t src_row = e * H + c;
+    const uint4 q = *reinterpret_cast<const uint4*>(w2 + src_row * (I / 2) + 16 * j);
+    *reinterpret_cast<uint4*>(out_w2 + i * 16) = q;
+    const uint8_t* ss = w2s + src_row * (I / 16) + 2 * j;
+    out_w2s[i * 2 + 0] = ss[0];
+    out_w2s[i * 2 + 1] = ss[1];
+  }
+}
+
+hipError_t launch_repack_w2(int H, int I, int n, const uint8_t* w2, const uint8_t* w2s,
+                            uint8_t* out_w2, uint8_t* out_w2s, hipStream_t s) {
+  const size_t total = static_cast<size_t>(n) * H * (I / 32);
+  if (total == 0) return hipSuccess;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  repack_w2_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(H, I, n, w2, w2s,
+                                                                            out_w2, out_w2s);
+  return hipGetLastError();
+}
+
+// Dequantise one tensor of one expert of a repacked bank.  Each thread decodes
+// one 32-bit word of codes (8 elements, inside one 16-element scale block) with
+// the same routines the GEMV kernels use (e2m1x2_to_f32, e4m3_byte_to_f32).
+// out: row-major [rows][K], fp32 (out_dtype 0) or bf16 (out_dtype 1).
+__global__ __launch_bounds__(256) void dequant_kernel(int H, int I, Bank b, int e, int tensor,
+                                                      int out_dtype, void* out) {
+  const bool down = (tensor == 2);
+  const int rows = down ? H : I;
+  const int K = down ? I : H;
+  const int words_per_row = K / 8;
+  const size_t total = static_cast<size_t>(rows) * words_per_row;
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int r = static_cast<int>(idx / words_per_row);
+  const int wd = static_cast<int>(idx % words_per_row);
+  const int k0 = 8 * wd;  // first element of the word
+  uint32_t code_word, scale_byte;
+  if (!down) {
+    const size_t row = static_cast<size_t>(e) * 2 * I + (tensor == 1 ? I : 0) + r;
+    code_word = *reinterpret_cast<const uint32_t*>(b.w13 + row * (H / 2) + 4 * wd);
+    scale_byte = b.w13s[row * (H / 16) + k0 / 16];
+  } else {
+    const int nch = I / 32;
+    const int j = k0 / 32;
+    const size_t rec = (static_cast<size_t>(e) * nch + j) * H + r;
+    code_word = *reinterpret_cast<const uint32_t*>(b.w2 + rec * 16 + (k0 % 32) / 2);
+    scale_byte = b.w2s[rec * 2 + (k0 % 32) / 16];
+  }
+  const float s = e4m3_byte_to_f32<0>(scale_byte);
+  const float g = b.gsc[3 * e + tensor];
+  float v[8];
+  const f32x2 p0 = e2m1x2_to_f32<0>(code_word), p1 = e2m1x2_to_f32<1>(code_word);
+  const f32x2 p2 = e2m1x2_to_f32<2>(code_word), p3 = e2m1x2_to_f32<3>(code_word);
+  v[0] = dequant_one(p0.x, s, g);
+  v[1] = dequant_one(p0.y, s, g);
+  v[2] = dequant_one(p1.x, s, g);
+  v[3] = dequant_one(p1.y, s, g);
+  v[4] = dequant_one(p2.x, s, g);
+  v[5] = dequant_one(p2.y, s, g);
+  v[6] = dequant_one(p3.x, s, g);
+  v[7] = dequant_one(p3.y, s, g);
+  const size_t o = static_cast<size_t>(r) * K + k0;
+  if (out_dtype == 0) {
+    float* of = static_cast<float*>(out) + o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) of[i] = v[i];
+  } else {
+    uint16_t* ob = static_cast<uint16_t*>(out) + o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ob[i] = f32_to_bf16_bits(v[i]);
+  }
+}
+
+hipError_t launch_dequant(int H, int I, const Bank& b, int expert, int tensor, int out_dtype,
+                          void* out, hipStream_t s) {
+  const size_t total = static_cast<size_t>(H) * I / 8;
+  const unsigned blocks = static_cast<unsigned>((total + 255) / 256);
+  dequant_kernel<<<dim3(blocks), dim3(256), 0, s>>>(H, I, b, expert, tensor, out_dtype, out);
+  return hipGetLastError();
+}
+
+}  // namespace ftmoe

@@ -1,0 +1,214 @@
+// route.hip -- MoE router for gfx950: logits in fp64, the shared expert's
+// sigmoid gate, and top-k selection with softmax weights over the selected
+// logits.
+//
+// FreeToken commit log (page 2): "moe router / shared gate" kernels and the
+// "non-power-of-2 top-k router" (k = 10 of 512 experts); the 288-expert layer
+// routes top-8.  Logits are accumulated in fp64 (every fp32 x bf16 product is
+// exact in fp64) and rounded once to fp32, so the selection does not depend on
+// the summation order; ties go to the lower expert index.
+#include "ftmoe_device.hpp"
+#include "ftmoe_kernels.hpp"
+
+namespace ftmoe {
+
+constexpr int kRouteWaves = 4;   // one expert row per wave
+constexpr int kRouteTokTile = 64;
+constexpr int kMaxExperts = 1024;
+constexpr int kTopkSlotsPerLane = kMaxExperts / kWave;
+
+// Rank order of the top-k: larger logit first, then lower index; a NaN logit
+// ranks below every number; index -1 means "no candidate".
+__device__ __forceinline__ bool ranks_above(float a, int ia, float b, int ib) {
+  if (ia < 0) return false;
+  if (ib < 0) return true;
+  const bool an = __builtin_isnan(a), bn = __builtin_isnan(b);
+  if (an || bn) return (an && bn) ? (ia < ib) : bn;
+  if (a != b) return a > b;
+  return ia < ib;
+}
+
+// Top-k of one token's E logits by one wave, then the softmax of the selected
+// logits (fp64 exp, stored as fp32).  ids/w are emitted in rank order.
+__device__ void topk_one_token(const float* __restrict__ lg, int E, int k, int32_t* ids,
+                               float* w, int32_t* ids2, float* w2) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float v[kTopkSlotsPerLane];
+#pragma unroll
+  for (int m = 0; m < kTopkSlotsPerLane; ++m) {
+    const int e = lane + kWave * m;
+    v[m] = (e < E) ? lg[e] : 0.0f;
+  }
+  uint32_t taken = 0;
+  float mine = 0.0f;  // lane i keeps the logit of rank i
+  for (int i = 0; i < k; ++i) {
+    float bv = 0.0f;
+    int be = -1;
+#pragma unroll
+    for (int m = 0; m < kTopkSlotsPerLane; ++m) {
+      const int e = lane + kWave * m;
+      if (e < E && !((taken >> m) & 1u) && ranks_above(v[m], e, bv, be)) {
+        bv = v[m];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, kWave);
+      const int oe = __shfl_xor(be, off, kWave);
+      if (ranks_above(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
+    if (lane == i) mine = bv;
+    if (lane == 0) {
+      ids[i] = be;
+      if (ids2) ids2[i] = be;
+    }
+  }
+  const double top = static_cast<double>(__shfl(mine, 0, kWave));
+  const double d = (lane < k) ? exp(static_cast<double>(mine) - top) : 0.0;
+  const double sum = group_sum<kWave>(d);
+  if (lane < k) {
+    const float wi = static_cast<float>(d / sum);
+    w[lane] = wi;
+    if (w2) w2[lane] = wi;
+  }
+}
+
+// logits[t][e] for expert row e = blockIdx.x * kRouteWaves + wave; row E is the
+// shared expert's gate (gamma[t] = sigmoid(sum_h gs[h] x[t][h])).  Each lane
+// holds NC float4 pieces of the row (interleaved by lane so that every wave load
+// reads 1 KiB contiguous) and reuses them across the token tile.
+template <int NC>
+__global__ __launch_bounds__(kRouteWaves* kWave) void route_logits_kernel(RouteParams p,
+                                                                          int fuse_topk) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x * kRouteWaves + wave;
+  const int t0 = blockIdx.y * kRouteTokTile;
+  const int t1 = min(p.T, t0 + kRouteTokTile);
+  const int H = p.H;
+
+  // clear the down-projection counters of this call (their users run later on the stream)
+  {
+    const int nthreads = gridDim.x * gridDim.y * blockDim.x;
+    const int tid = (blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    for (int i = tid; i < p.nzero; i += nthreads) p.zero[i] = 0u;
+  }
+
+  if (row < p.E) {
+    const float* __restrict__ wrow = p.wr + static_cast<size_t>(row) * H;
+    float4 wv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      wv[c] = *reinterpret_cast<const float4*>(wrow + 4 * lane + 4 * kWave * c);
+    const double b = p.bias ? static_cast<double>(p.bias[row]) : 0.0;
+    for (int t = t0; t < t1; ++t) {
+      const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
+      double acc = 0.0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint2 xb = *reinterpret_cast<const uint2*>(xt + 4 * lane + 4 * kWave * c);
+        acc = fma(static_cast<double>(wv[c].x), static_cast<double>(bf16_bits_to_f32(xb.x & 0xFFFFu)), acc);
+        acc = fma(static_cast<double>(wv[c].y), static_cast<double>(bf16_bits_to_f32(xb.x >> 16)), acc);
+        acc = fma(static_cast<double>(wv[c].z), static_cast<double>(bf16_bits_to_f32(xb.y & 0xFFFFu)), acc);
+        acc = fma(static_cast<double>(wv[c].w), static_cast<double>(bf16_bits_to_f32(xb.y >> 16)), acc);
+      }
+      acc = group_sum<kWave>(acc);
+      if (lane == 0) {
+        if (p.bias) acc += b;
+        p.logits[static_cast<size_t>(t) * p.E + row] = static_cast<float>(acc);
+      }
+    }
+  } else if (row == p.E && p.shared_gate != nullptr) {
+    uint2 gv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      gv[c] = *reinterpret_cast<const uint2*>(p.shared_gate + 4 * lane + 4 * kWave * c);
+    for (int t = t0; t < t1; ++t) {
+      const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
+      double acc = 0.0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint2 xb = *reinterpret_cast<const uint2*>(xt + 4 * lane + 4 * kWave * c);
+        acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].x & 0xFFFFu)),
+                  static_cast<double>(bf16_bits_to_f32(xb.x & 0xFFFFu)), acc);
+        acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].x >> 16)),
+                  static_cast<double>(bf16_bits_to_f32(xb.x >> 16)), acc);
+        acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].y & 0xFFFFu)),
+                  static_cast<double>(bf16_bits_to_f32(xb.y & 0xFFFFu)), acc);
+        acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].y >> 16)),
+                  static_cast<double>(bf16_bits_to_f32(xb.y >> 16)), acc);
+      }
+      acc = group_sum<kWave>(acc);
+      if (lane == 0) p.gamma[t] = static_cast<float>(1.0 / (1.0 + exp(-acc)));
+    }
+  }
+
+  if (!fuse_topk) return;
+  // Last-arriver top-k: every block publishes its logits, and the block that
+  // arrives last (one device-scope counter) selects the experts of all tokens.
+  // No block waits for another, so the grid needs no co-residency.
+  __shared__ uint32_t s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t nblocks = gridDim.x * gridDim.y;
+    const uint32_t old = atomicAdd(p.counter, 1u);
+    s_last = (old == nblocks - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int t = wave; t < p.T; t += kRouteWaves)
+    topk_one_token(p.logits + static_cast<size_t>(t) * p.E, p.E, p.k,
+                   p.ids + static_cast<size_t>(t) * p.k, p.w + static_cast<size_t>(t) * p.k,
+                   p.ids_copy ? p.ids_copy + static_cast<size_t>(t) * p.k : nullptr,
+                   p.w_copy ? p.w_copy + static_cast<size_t>(t) * p.k : nullptr);
+  if (threadIdx.x == 0) atomicExch(p.counter, 0u);
+}
+
+// One wave per token (used when the token count is too large for one block).
+__global__ __launch_bounds__(kRouteWaves* kWave) void topk_kernel(RouteParams p) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = blockIdx.x * kRouteWaves + wave;
+  if (t >= p.T) return;
+  topk_one_token(p.logits + static_cast<size_t>(t) * p.E, p.E, p.k,
+                 p.ids + static_cast<size_t>(t) * p.k, p.w + static_cast<size_t>(t) * p.k,
+                 p.ids_copy ? p.ids_copy + static_cast<size_t>(t) * p.k : nullptr,
+                 p.w_copy ? p.w_copy + static_cast<size_t>(t) * p.k : nullptr);
+}
+
+hipError_t launch_route(const RouteParams& p, bool fuse_topk, hipStream_t s) {
+  const int rows = p.E + (p.shared_gate ? 1 : 0);
+  const int gx = rows > 0 ? (rows + kRouteWaves - 1) / kRouteWaves : 1;
+  dim3 grid(gx, (p.T + kRouteTokTile - 1) / kRouteTokTile);
+  dim3 block(kRouteWaves * kWave);
+  const int fuse = fuse_topk ? 1 : 0;
+  switch (p.H / (4 * kWave)) {
+#define FTMOE_ROUTE_CASE(n) \
+  case n: route_logits_kernel<n><<<grid, block, 0, s>>>(p, fuse); break;
+    FTMOE_ROUTE_CASE(1) FTMOE_ROUTE_CASE(2) FTMOE_ROUTE_CASE(3) FTMOE_ROUTE_CASE(4)
+    FTMOE_ROUTE_CASE(5) FTMOE_ROUTE_CASE(6) FTMOE_ROUTE_CASE(7) FTMOE_ROUTE_CASE(8)
+    FTMOE_ROUTE_CASE(9) FTMOE_ROUTE_CASE(10) FTMOE_ROUTE_CASE(11) FTMOE_ROUTE_CASE(12)
+    FTMOE_ROUTE_CASE(13) FTMOE_ROUTE_CASE(14) FTMOE_ROUTE_CASE(15) FTMOE_ROUTE_CASE(16)
+    FTMOE_ROUTE_CASE(17) FTMOE_ROUTE_CASE(18) FTMOE_ROUTE_CASE(19) FTMOE_ROUTE_CASE(20)
+    FTMOE_ROUTE_CASE(21) FTMOE_ROUTE_CASE(22) FTMOE_ROUTE_CASE(23) FTMOE_ROUTE_CASE(24)
+    FTMOE_ROUTE_CASE(25) FTMOE_ROUTE_CASE(26) FTMOE_ROUTE_CASE(27) FTMOE_ROUTE_CASE(28)
+    FTMOE_ROUTE_CASE(29) FTMOE_ROUTE_CASE(30) FTMOE_ROUTE_CASE(31) FTMOE_ROUTE_CASE(32)
+#undef FTMOE_ROUTE_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const RouteParams& p, hipStream_t s) {
+  dim3 grid((p.T + kRouteWaves - 1) / kRouteWaves);
+  topk_kernel<<<grid, dim3(kRouteWaves * kWave), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace ftmoe

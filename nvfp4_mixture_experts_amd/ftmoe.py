@@ -1,0 +1,224 @@
+"""Python binding of libftmoe.so (the C ABI in include/ftmoe.h).
+
+Argument marshalling only: every function takes torch tensors (or plain ints),
+checks dtype, device and contiguity, and passes raw pointers plus the current
+HIP stream to the function of the same name in the library.  All compute runs in
+the library's gfx950 kernels; there is no fallback: if libftmoe.so is missing or
+cannot be loaded, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libftmoe.so")
+FT_ABI_VERSION = 1
+
+FT_OK = 0
+FT_EINVAL = -1
+FT_EUNSUPPORTED = -2
+FT_EWORKSPACE = -3
+FT_EHIP = -4
+
+PATH_ROUTE, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+
+
+class FtError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where} failed with status {status}: {message}")
+        self.status = status
+
+
+class FtMoeDesc(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("top_k", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("gate_max", ctypes.c_float), ("up_absmax", ctypes.c_float),
+                ("shared_inter", ctypes.c_int32)]
+
+
+class FtNvfp4Experts(ctypes.Structure):
+    _fields_ = [("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run nvfp4_mixture_experts_amd.build.build() "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D = ctypes.POINTER(FtMoeDesc)
+    B = ctypes.POINTER(FtNvfp4Experts)
+    sig = {
+        "ft_abi_version": (I32, []),
+        "ft_last_error": (ctypes.c_char_p, []),
+        "ft_init": (I32, [I32]),
+        "ft_nvfp4_repacked_bytes": (SZ, [I32, I32, I32, I32]),
+        "ft_nvfp4_repack": (I32, [I32, I32, I32] + [P] * 8 + [P]),
+        "ft_moe_workspace_bytes": (SZ, [D, I64, I32]),
+        "ft_moe_route": (I32, [D, I64, P, P, P, P, P, P, SZ, P]),
+        "ft_moe_nvfp4_decode": (I32, [D, I64, P, P, P, B, B, P, P, P, P, P, SZ, P]),
+        "ft_moe_nvfp4_prefill": (I32, [D, I64, P, P, P, B, B, P, P, P, SZ, P]),
+        "ft_nvfp4_dequant": (I32, [I32, I32, I32, B, I32, I32, I32, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.ft_abi_version() != FT_ABI_VERSION:
+        raise ImportError(f"libftmoe.so ABI {lib.ft_abi_version()} != {FT_ABI_VERSION}")
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("ft_abi_version", "ft_last_error", "ft_init", "ft_nvfp4_repacked_bytes",
+            "ft_nvfp4_repack", "ft_moe_workspace_bytes", "ft_moe_route", "ft_moe_nvfp4_decode",
+            "ft_moe_nvfp4_prefill", "ft_nvfp4_dequant")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _check(status: int, where: str) -> None:
+    if status != FT_OK:
+        raise FtError(status, where, _lib.ft_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_desc(num_experts: int, hidden: int, inter: int, top_k: int, act: int,
+              gate_max: float = 7.0, up_absmax: float = 7.0, shared_inter: int = 0) -> FtMoeDesc:
+    return FtMoeDesc(num_experts, hidden, inter, top_k, act, gate_max, up_absmax, shared_inter)
+
+
+class Bank:
+    """A repacked NVFP4 expert bank (device tensors) and its C view."""
+
+    def __init__(self, hidden: int, inter: int, n: int, w13, w13_scale, w2, w2_scale,
+                 global_scale):
+        self.hidden, self.inter, self.n = hidden, inter, n
+        self.w13, self.w13_scale, self.w2, self.w2_scale = w13, w13_scale, w2, w2_scale
+        self.global_scale = global_scale
+        self.c = FtNvfp4Experts(_ptr(w13, torch.uint8, "w13"), _ptr(w13_scale, torch.uint8),
+                                _ptr(w2, torch.uint8, "w2"), _ptr(w2_scale, torch.uint8),
+                                _ptr(global_scale, torch.float32, "global_scale"))
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+# ------------------------------------------------------------- entry points --
+
+def ft_abi_version() -> int:
+    return _lib.ft_abi_version()
+
+
+def ft_last_error() -> str:
+    return _lib.ft_last_error().decode()
+
+
+def ft_init(device: int = 0) -> None:
+    _check(_lib.ft_init(device), "ft_init")
+
+
+def ft_nvfp4_repacked_bytes(hidden: int, inter: int, n_experts: int, part: int) -> int:
+    return _lib.ft_nvfp4_repacked_bytes(hidden, inter, n_experts, part)
+
+
+def ft_nvfp4_repack(hidden: int, inter: int, n_experts: int, w13, w13_scale, w2, w2_scale,
+                    global_scale, stream=None) -> Bank:
+    """Repack a canonical bank (device uint8 tensors) into newly allocated device buffers."""
+    dev = w13.device
+    outs = [torch.empty(ft_nvfp4_repacked_bytes(hidden, inter, n_experts, p), dtype=torch.uint8,
+                        device=dev) for p in range(4)]
+    _check(_lib.ft_nvfp4_repack(hidden, inter, n_experts,
+                                _ptr(w13, torch.uint8, "w13"), _ptr(w13_scale, torch.uint8),
+                                _ptr(w2, torch.uint8, "w2"), _ptr(w2_scale, torch.uint8),
+                                *[o.data_ptr() for o in outs], _stream(stream)),
+           "ft_nvfp4_repack")
+    return Bank(hidden, inter, n_experts, *outs, global_scale.contiguous())
+
+
+def ft_moe_workspace_bytes(desc: FtMoeDesc, tokens: int, path: int) -> int:
+    return _lib.ft_moe_workspace_bytes(ctypes.byref(desc), tokens, path)
+
+
+def alloc_workspace(desc: FtMoeDesc, tokens: int, path: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (zero fill is required once, before first use)."""
+    n = ft_moe_workspace_bytes(desc, tokens, path)
+    if n == 0:
+        raise FtError(FT_EINVAL, "ft_moe_workspace_bytes", "invalid descriptor or token count")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def ft_moe_route(desc: FtMoeDesc, x, w_router, bias, topk_ids, topk_w, workspace,
+                 stream=None) -> None:
+    _check(_lib.ft_moe_route(ctypes.byref(desc), x.shape[0], _ptr(x, torch.bfloat16, "x"),
+                             _ptr(w_router, torch.float32, "w_router"),
+                             _ptr(bias, torch.float32, "bias"),
+                             _ptr(topk_ids, torch.int32, "topk_ids"),
+                             _ptr(topk_w, torch.float32, "topk_w"),
+                             _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                             _stream(stream)), "ft_moe_route")
+
+
+def ft_moe_nvfp4_decode(desc: FtMoeDesc, x, w_router, bias, routed: Bank, shared: Optional[Bank],
+                        shared_gate, y, workspace, topk_ids_out=None, topk_w_out=None,
+                        stream=None) -> None:
+    _check(_lib.ft_moe_nvfp4_decode(ctypes.byref(desc), x.shape[0], _ptr(x, torch.bfloat16, "x"),
+                                    _ptr(w_router, torch.float32, "w_router"),
+                                    _ptr(bias, torch.float32, "bias"), routed.ref(),
+                                    shared.ref() if shared is not None else None,
+                                    _ptr(shared_gate, torch.bfloat16, "shared_gate"),
+                                    _ptr(topk_ids_out, torch.int32, "topk_ids_out"),
+                                    _ptr(topk_w_out, torch.float32, "topk_w_out"),
+                                    _ptr(y, torch.bfloat16, "y"),
+                                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                    _stream(stream)), "ft_moe_nvfp4_decode")
+
+
+def ft_moe_nvfp4_prefill(desc: FtMoeDesc, x, topk_ids, topk_w, routed: Bank,
+                         shared: Optional[Bank], shared_gate, y, workspace, stream=None) -> None:
+    _check(_lib.ft_moe_nvfp4_prefill(ctypes.byref(desc), x.shape[0], _ptr(x, torch.bfloat16, "x"),
+                                     _ptr(topk_ids, torch.int32, "topk_ids"),
+                                     _ptr(topk_w, torch.float32, "topk_w"), routed.ref(),
+                                     shared.ref() if shared is not None else None,
+                                     _ptr(shared_gate, torch.bfloat16, "shared_gate"),
+                                     _ptr(y, torch.bfloat16, "y"),
+                                     _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                     _stream(stream)), "ft_moe_nvfp4_prefill")
+
+
+def ft_nvfp4_dequant(bank: Bank, expert: int, tensor: int, out, stream=None) -> None:
+    """out: fp32 or bf16 [rows][K] device tensor (gate/up [I][H], down [H][I])."""
+    if out.dtype == torch.float32:
+        dt = 0
+    elif out.dtype == torch.bfloat16:
+        dt = 1
+    else:
+        raise TypeError("out must be float32 or bfloat16")
+    _check(_lib.ft_nvfp4_dequant(bank.hidden, bank.inter, bank.n, bank.ref(), expert, tensor, dt,
+                                 _ptr(out, None, "out"), _stream(stream)), "ft_nvfp4_dequant")

@@ -1,0 +1,141 @@
+"""Host-side checks of libftmoe.so that need no GPU: the library loads, exports
+every entry point include/ftmoe.h declares, and its host validation rejects bad
+arguments with the documented status codes before anything is enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "ftmoe.h")
+
+
+def _lib_path():
+    from nvfp4_mixture_experts_amd import build
+    if not os.path.exists(build.LIB_PATH):
+        build.build()
+    return build.LIB_PATH
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ft_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("ft_moe_route", "ft_moe_nvfp4_decode", "ft_moe_nvfp4_prefill", "ft_nvfp4_repack",
+              "ft_nvfp4_dequant", "ft_moe_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    path = _lib_path()
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (ft_[a-z0-9_]+)$", out, flags=re.M))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(path)
+    for n in _declared():
+        assert hasattr(lib, n)
+
+
+@pytest.fixture(scope="module")
+def ft():
+    _lib_path()
+    from nvfp4_mixture_experts_amd import ftmoe
+    return ftmoe
+
+
+def test_abi_version(ft):
+    assert ft.ft_abi_version() == ft.FT_ABI_VERSION == 1
+
+
+def test_repacked_sizes(ft):
+    H, I, n = 2048, 768, 288
+    assert ft.ft_nvfp4_repacked_bytes(H, I, n, 0) == n * 2 * I * H // 2
+    assert ft.ft_nvfp4_repacked_bytes(H, I, n, 1) == n * 2 * I * H // 16
+    assert ft.ft_nvfp4_repacked_bytes(H, I, n, 2) == n * H * I // 2
+    assert ft.ft_nvfp4_repacked_bytes(H, I, n, 3) == n * H * I // 16
+    assert ft.ft_nvfp4_repacked_bytes(H, I, n, 4) == 0
+    assert ft.ft_nvfp4_repacked_bytes(0, I, n, 0) == 0
+
+
+def test_workspace_bytes_and_desc_validation(ft):
+    good = ft.make_desc(288, 2048, 768, 8, 1)
+    for path in (0, 1, 2):
+        assert ft.ft_moe_workspace_bytes(good, 1, path) > 0
+    assert ft.ft_moe_workspace_bytes(good, 32, 1) > ft.ft_moe_workspace_bytes(good, 1, 1)
+    assert ft.ft_moe_workspace_bytes(good, -1, 1) == 0
+    assert ft.ft_moe_workspace_bytes(good, 1, 3) == 0
+    bad = [
+        ft.make_desc(8, 2048, 768, 9, 1),      # k > E
+        ft.make_desc(8, 2048, 768, 0, 1),      # k = 0
+        ft.make_desc(2048, 2048, 768, 8, 1),   # E > 1024
+        ft.make_desc(288, 2048, 768, 17, 1),   # k > 16
+        ft.make_desc(288, 2000, 768, 8, 1),    # H not a multiple of 256
+        ft.make_desc(288, 2048, 760, 8, 1),    # I not a multiple of 64
+        ft.make_desc(288, 2048, 768, 8, 2),    # act
+        ft.make_desc(288, 2048, 768, 8, 1, shared_inter=100),
+    ]
+    for d in bad:
+        assert ft.ft_moe_workspace_bytes(d, 1, 1) == 0
+
+
+def _raw(ft):
+    return ft._lib
+
+
+def test_host_validation_status_codes(ft):
+    lib = _raw(ft)
+    d = ft.make_desc(288, 2048, 768, 8, 1)
+    dp = ctypes.byref(d)
+    # NULL descriptor
+    assert lib.ft_moe_route(None, 1, 16, 16, None, 16, 16, 256, 1 << 20, None) == ft.FT_EINVAL
+    assert "desc" in ft.ft_last_error()
+    # NULL x
+    assert lib.ft_moe_route(dp, 1, None, 16, None, 16, 16, 256, 1 << 20, None) == ft.FT_EINVAL
+    # misaligned x
+    assert lib.ft_moe_route(dp, 1, 18, 16, None, 16, 16, 256, 1 << 20, None) == ft.FT_EINVAL
+    # workspace too small / misaligned / NULL
+    assert lib.ft_moe_route(dp, 1, 16, 16, None, 16, 16, 256, 8, None) == ft.FT_EWORKSPACE
+    assert lib.ft_moe_route(dp, 1, 16, 16, None, 16, 16, 272, 1 << 20, None) == ft.FT_EWORKSPACE
+    assert lib.ft_moe_route(dp, 1, 16, 16, None, 16, 16, None, 1 << 20, None) == ft.FT_EWORKSPACE
+    # decode token range
+    bank = ft.FtNvfp4Experts(256, 256, 256, 256, 256)
+    b = ctypes.byref(bank)
+    args = (16, None, b, None, None, None, None, 16, 256, 1 << 24, None)
+    assert lib.ft_moe_nvfp4_decode(dp, 0, 16, *args) == ft.FT_EINVAL
+    assert lib.ft_moe_nvfp4_decode(dp, 65, 16, *args) == ft.FT_EUNSUPPORTED
+    # shared expert declared but no bank
+    ds = ft.make_desc(512, 2048, 512, 10, 1, shared_inter=512)
+    assert lib.ft_moe_nvfp4_decode(ctypes.byref(ds), 1, 16, 16, None, b, None, 16, None, None,
+                                   16, 256, 1 << 24, None) == ft.FT_EINVAL
+    assert "shared" in ft.ft_last_error()
+    # routed bank with a NULL part
+    nb = ft.FtNvfp4Experts(256, None, 256, 256, 256)
+    assert lib.ft_moe_nvfp4_decode(dp, 1, 16, 16, None, ctypes.byref(nb), None, None, None,
+                                   None, 16, 256, 1 << 24, None) == ft.FT_EINVAL
+    # prefill needs routes
+    assert lib.ft_moe_nvfp4_prefill(dp, 4, 16, None, 16, b, None, None, 16, 256, 1 << 24,
+                                    None) == ft.FT_EINVAL
+    # dequant argument checks
+    assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 8, 0, 0, 16, None) == ft.FT_EINVAL
+    assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 0, 3, 0, 16, None) == ft.FT_EINVAL
+    assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 0, 0, 2, 16, None) == ft.FT_EINVAL
+    assert lib.ft_nvfp4_dequant(2000, 768, 8, b, 0, 0, 0, 16, None) == ft.FT_EUNSUPPORTED
+    # repack argument checks
+    assert lib.ft_nvfp4_repack(2048, 768, 8, *([16] * 7), None, None) == ft.FT_EINVAL
+    assert lib.ft_nvfp4_repack(2048, 100, 8, *([16] * 8), None) == ft.FT_EUNSUPPORTED
+
+
+def test_zero_tokens_route_enqueues_nothing(ft):
+    lib = _raw(ft)
+    d = ft.make_desc(288, 2048, 768, 8, 1)
+    n = ft.ft_moe_workspace_bytes(d, 0, 0)
+    assert lib.ft_moe_route(ctypes.byref(d), 0, 16, 16, None, 16, 16, 256, n, None) == ft.FT_OK

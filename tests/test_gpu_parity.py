@@ -1,0 +1,305 @@
+"""GPU parity of libftmoe.so against the CPU oracle, through the C ABI.
+
+Bit-exact: dequantised weights (all 16 codes x all 256 scale bytes, and random
+banks through the repack) and top-k expert ids.  Routing weights: within 2 fp32
+ulps.  bf16 layer outputs: max_abs_rel <= 1e-2 and rel_l2 <= 2e-3 against the
+oracle's bf16-rounded output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from nvfp4_mixture_experts_amd import synth
+from tests.gpu_util import (assert_output_close, f32_ulp_diff, host_layer, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from nvfp4_mixture_experts_amd import device, ftmoe
+    ftmoe.ft_init(0)
+    say(f"libftmoe: {ftmoe.library_path()}")
+    return device
+
+
+_uploaded = {}
+
+
+def dev_layer(gpu, name, **overrides):
+    key = (name, tuple(sorted(overrides.items())))
+    if key not in _uploaded:
+        if len(_uploaded) >= 3:
+            _uploaded.clear()
+            torch.cuda.empty_cache()
+        say(f"  upload {name} {overrides}")
+        _uploaded[key] = gpu.upload_layer(host_layer(name, **overrides))
+    return _uploaded[key]
+
+
+# ---------------------------------------------------------------- dequant --
+
+def _all_codes_bank(H=256, I=64, n=2, g=(1.0, 0.3, 2.0 ** -6)):
+    """Gate rows 0..15 of expert 0 carry all 256 scale bytes, each block all 16 codes."""
+    rng = np.random.default_rng(42)
+    w13c = rng.integers(0, 256, (n, 2 * I, H // 2), dtype=np.uint8)
+    w13s = synth.SCALE_BYTES[rng.integers(0, 7, (n, 2 * I, H // 16))]
+    w13c[0, :16, :] = np.tile(np.array([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE],
+                                       np.uint8), H // 16)
+    w13s[0, :16, :] = np.arange(256, dtype=np.uint8).reshape(16, 16)
+    w2c = rng.integers(0, 256, (n, H, I // 2), dtype=np.uint8)
+    w2s = synth.SCALE_BYTES[rng.integers(0, 7, (n, H, I // 16))]
+    w2s[0, :64, :] = np.arange(256, dtype=np.uint8).reshape(64, 4)
+    gsc = np.tile(np.array(g, np.float32), (n, 1))
+    return dict(w13_codes=w13c, w13_scales=w13s, w2_codes=w2c, w2_scales=w2s, global_scale=gsc)
+
+
+def _bits_equal_with_nan(got, want):
+    gn, wn = np.isnan(got), np.isnan(want)
+    assert np.array_equal(gn, wn)
+    assert np.array_equal(got[~gn].view(np.uint32), want[~wn].view(np.uint32))
+
+
+@pytest.mark.parametrize("tensor", [0, 1, 2])
+def test_dequant_bit_exact_all_codes_and_scales(gpu, tensor):
+    from nvfp4_mixture_experts_amd import ftmoe
+    H, I, n = 256, 64, 2
+    b = _all_codes_bank(H, I, n)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    bank = ftmoe.ft_nvfp4_repack(H, I, n, dev(b["w13_codes"]), dev(b["w13_scales"]),
+                                 dev(b["w2_codes"]), dev(b["w2_scales"]), dev(b["global_scale"]))
+    for e in range(n):
+        rows, K = (H, I) if tensor == 2 else (I, H)
+        out = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+        ftmoe.ft_nvfp4_dequant(bank, e, tensor, out)
+        outb = torch.empty((rows, K), dtype=torch.bfloat16, device="cuda")
+        ftmoe.ft_nvfp4_dequant(bank, e, tensor, outb)
+        torch.cuda.synchronize()
+        g = float(b["global_scale"][e, tensor])
+        if tensor == 2:
+            want = oracle.dequant_matrix(b["w2_codes"][e], b["w2_scales"][e], g)
+        else:
+            sl = slice(0, I) if tensor == 0 else slice(I, 2 * I)
+            want = oracle.dequant_matrix(b["w13_codes"][e, sl], b["w13_scales"][e, sl], g)
+        got = out.cpu().numpy()
+        _bits_equal_with_nan(got, want)
+        wantb = np.array([oracle.bf16_from_double(float(v)) for v in want.ravel()],
+                         np.uint16).reshape(want.shape)
+        gotb = outb.cpu().view(torch.int16).numpy().view(np.uint16)
+        nanb = np.isnan(want)
+        assert np.array_equal(gotb[~nanb], wantb[~nanb])
+
+
+def test_dequant_bit_exact_workload_bank(gpu):
+    """Every tensor of two experts of the 288-expert decode layer, after the repack."""
+    from nvfp4_mixture_experts_amd import ftmoe
+    dl = dev_layer(gpu, "decode_e288_top8")
+    L = host_layer("decode_e288_top8")
+    I, H = L.inter, L.hidden
+    for e in (0, 287):
+        for tensor in (0, 1, 2):
+            rows, K = (H, I) if tensor == 2 else (I, H)
+            out = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+            ftmoe.ft_nvfp4_dequant(dl.routed, e, tensor, out)
+            g = float(L.global_scale[e, tensor])
+            if tensor == 2:
+                want = oracle.dequant_matrix(L.w2_codes[e], L.w2_scales[e], g)
+            else:
+                sl = slice(0, I) if tensor == 0 else slice(I, 2 * I)
+                want = oracle.dequant_matrix(L.w13_codes[e, sl], L.w13_scales[e, sl], g)
+            assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+# ------------------------------------------------------------------ route --
+
+def _check_routes(ids, w, ref_ids, ref_w, what):
+    ids = ids.cpu().numpy()
+    w = w.cpu().numpy()
+    assert np.array_equal(ids, ref_ids), f"{what}: ids differ"
+    ulps = f32_ulp_diff(w, ref_w)
+    say(f"  {what}: ids exact, weights max ulp diff {ulps.max()}, exact {np.mean(ulps == 0):.4f}")
+    assert ulps.max() <= 2
+
+
+@pytest.mark.parametrize("name,tokens", [("tiny_e8_top2", 1), ("decode_e288_top8", 1),
+                                         ("decode_e512_top10_shared", 1),
+                                         ("batched_decode_t32_hot64", 32),
+                                         ("decode_e512_top10_shared", 64),
+                                         ("decode_e512_top10_shared", 333)])
+def test_route_matches_oracle(gpu, name, tokens):
+    w = synth.WORKLOADS[name]
+    dl = dev_layer(gpu, name)
+    L = host_layer(name)
+    x = synth.make_tokens(w, tokens=tokens, stream=f"route{tokens}")
+    ids, wt = gpu.route(dl, gpu.tokens_to_device(x))
+    torch.cuda.synchronize()
+    logits = oracle.router_logits(x, L.w_router, L.bias)
+    ref_ids, ref_w = oracle.topk(logits, w.top_k)
+    _check_routes(ids, wt, ref_ids, ref_w, f"{name} T={tokens}")
+
+
+def test_route_ties_go_to_lowest_index(gpu):
+    """Duplicated router rows give exactly equal logits; the lower index must win."""
+    from nvfp4_mixture_experts_amd import ftmoe
+    w = synth.dataclasses.replace(synth.WORKLOADS["decode_e288_top8"], num_experts=96)
+    L = synth.make_layer(w)
+    wr = L.w_router.copy()
+    wr[50:96] = wr[0:46]                      # experts 50.. duplicate 0..45
+    wr[10] = wr[70]                           # and a tie inside the copy
+    x = synth.make_tokens(w, tokens=16, stream="ties")
+    xd = gpu.tokens_to_device(x)
+    desc = ftmoe.make_desc(96, w.hidden, w.inter, w.top_k, 1)
+    wsp = ftmoe.alloc_workspace(desc, 16, ftmoe.PATH_ROUTE)
+    ids = torch.empty((16, w.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((16, w.top_k), dtype=torch.float32, device="cuda")
+    ftmoe.ft_moe_route(desc, xd, torch.from_numpy(wr).cuda(), None, ids, wt, wsp)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.topk(oracle.router_logits(x, wr), w.top_k)
+    # every token must have at least one tie inside its top-k for the test to bite
+    lg = oracle.router_logits(x, wr)
+    ties = sum(len(set(lg[t, ref_ids[t]].tolist())) < w.top_k for t in range(16))
+    assert ties > 0
+    _check_routes(ids, wt, ref_ids, ref_w, "ties")
+
+
+# ----------------------------------------------------------------- decode --
+
+@pytest.mark.parametrize("name,tokens,sample", [
+    ("tiny_e8_top2", 1, None),
+    ("decode_e288_top8", 1, None),
+    ("decode_e512_top10_shared", 1, None),
+    ("batched_decode_t32_hot64", 32, [0, 9, 22, 31]),
+    ("tiny_e8_top2", 64, [0, 63]),
+])
+def test_decode_matches_oracle(gpu, name, tokens, sample):
+    w = synth.WORKLOADS[name]
+    dl = dev_layer(gpu, name)
+    L = host_layer(name)
+    x = synth.make_tokens(w, tokens=tokens)
+    y, ids, wt = gpu.decode(dl, gpu.tokens_to_device(x))
+    torch.cuda.synchronize()
+    yb = gpu.bf16_bits(y)
+    rows = list(range(tokens)) if sample is None else sample
+    ref = oracle.moe_layer(L, x[rows])
+    assert np.array_equal(ids.cpu().numpy()[rows], ref["ids"])
+    assert f32_ulp_diff(wt.cpu().numpy()[rows], ref["weights"]).max() <= 2
+    assert_output_close(yb[rows], ref["y"], f"{name} T={tokens}")
+    if sample is not None:   # the other tokens: routes checked against the oracle router
+        ref_ids, _ = oracle.topk(oracle.router_logits(x, L.w_router, L.bias), w.top_k)
+        assert np.array_equal(ids.cpu().numpy(), ref_ids)
+
+
+def test_decode_all_experts_selected(gpu):
+    """k = E: the layer is the dense softmax mixture of every expert."""
+    w = synth.dataclasses.replace(synth.WORKLOADS["decode_e512_top10_shared"], num_experts=16,
+                                  top_k=16, global_scale=2.0 ** -4)
+    L = synth.make_layer(w)
+    dl = gpu.upload_layer(L)
+    x = synth.make_tokens(w, tokens=3)
+    y, ids, _ = gpu.decode(dl, gpu.tokens_to_device(x))
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(L, x)
+    assert np.array_equal(np.sort(ids.cpu().numpy(), axis=1), np.tile(np.arange(16), (3, 1)))
+    assert_output_close(gpu.bf16_bits(y), ref["y"], "all experts")
+
+
+def test_decode_shapes_outside_the_workloads(gpu):
+    """H = 512 (16 lanes per row), I = 192, shared I = 128 != I, T = 5, plain SwiGLU."""
+    w = synth.Workload("odd_shapes", 24, 512, 192, 5, 5, False, 2.0 ** -5, seed=77,
+                       shared_inter=128)
+    L = synth.make_layer(w)
+    dl = gpu.upload_layer(L)
+    x = synth.make_tokens(w)
+    y, ids, _ = gpu.decode(dl, gpu.tokens_to_device(x))
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(L, x)
+    assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+    assert_output_close(gpu.bf16_bits(y), ref["y"], "odd shapes")
+
+
+def test_decode_is_deterministic(gpu):
+    """Same inputs -> same bits, across workspace addresses and streams."""
+    from nvfp4_mixture_experts_amd import ftmoe
+    name = "decode_e512_top10_shared"
+    dl = dev_layer(gpu, name)
+    x = gpu.tokens_to_device(synth.make_tokens(synth.WORKLOADS[name], tokens=4, stream="det"))
+    n = ftmoe.ft_moe_workspace_bytes(dl.desc, 4, ftmoe.PATH_DECODE)
+    big = torch.zeros(n + 4096, dtype=torch.uint8, device="cuda")
+    y0, _, _ = gpu.decode(dl, x)
+    y1, _, _ = gpu.decode(dl, x, workspace=big[1024:1024 + n])
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y2, _, _ = gpu.decode(dl, x, workspace=big[2048:2048 + n], stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert torch.equal(y0.view(torch.int16), y2.view(torch.int16))
+
+
+def test_decode_graph_replays_match_eager(gpu):
+    from nvfp4_mixture_experts_amd import ftmoe
+    name = "decode_e288_top8"
+    w = synth.WORKLOADS[name]
+    dl = dev_layer(gpu, name)
+    xs = [gpu.tokens_to_device(synth.make_tokens(w, tokens=1, stream=f"g{i}")) for i in range(3)]
+    ws = ftmoe.alloc_workspace(dl.desc, 1, ftmoe.PATH_DECODE)
+    eager = []
+    for x in xs:
+        y, _, _ = gpu.decode(dl, x, workspace=ws)
+        eager.append(y.clone())
+    torch.cuda.synchronize()
+    xin = xs[0].clone()
+    yout = torch.empty_like(eager[0])
+    ids = torch.empty((1, w.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((1, w.top_k), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            ftmoe.ft_moe_nvfp4_decode(dl.desc, xin, dl.w_router, dl.bias, dl.routed, dl.shared,
+                                      dl.shared_gate, yout, ws, ids, wt, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        i = rep % 3
+        xin.copy_(xs[i])
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yout.view(torch.int16), eager[i].view(torch.int16)), rep
+        # eager work between replays
+        gpu.decode(dl, xs[(i + 1) % 3], workspace=ws)
+        torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- prefill --
+
+def test_prefill_matches_oracle_small(gpu):
+    w = synth.dataclasses.replace(synth.WORKLOADS["prefill_t8192"], num_experts=32, tokens=97)
+    L = synth.make_layer(w)
+    dl = gpu.upload_layer(L)
+    x = synth.make_tokens(w)
+    xd = gpu.tokens_to_device(x)
+    ids, wt = gpu.route(dl, xd)
+    y = gpu.prefill(dl, xd, ids, wt)
+    torch.cuda.synchronize()
+    rows = [0, 1, 48, 96]
+    ref = oracle.moe_layer(L, x[rows])
+    assert np.array_equal(ids.cpu().numpy()[rows], ref["ids"])
+    assert_output_close(gpu.bf16_bits(y)[rows], ref["y"], "prefill T=97")
+
+
+def test_prefill_uses_given_routes(gpu):
+    """Routes passed in (not the router's) decide which experts run."""
+    w = synth.dataclasses.replace(synth.WORKLOADS["prefill_t8192"], num_experts=16, tokens=8)
+    L = synth.make_layer(w)
+    dl = gpu.upload_layer(L)
+    x = synth.make_tokens(w)
+    rng = np.random.default_rng(3)
+    ids = np.stack([rng.permutation(16)[: w.top_k] for _ in range(8)]).astype(np.int32)
+    wts = rng.dirichlet(np.ones(w.top_k), size=8).astype(np.float32)
+    y = gpu.prefill(dl, gpu.tokens_to_device(x), torch.from_numpy(ids).cuda(),
+                    torch.from_numpy(wts).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(L, x, ids=ids, weights=wts)
+    assert_output_close(gpu.bf16_bits(y), ref["y"], "prefill given routes")
