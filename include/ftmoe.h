@@ -47,7 +47,8 @@
  *    message (thread-local, valid until the next call on the same thread).
  *    Arguments are checked on the host before anything is enqueued; values that
  *    live in device memory (for example ids passed to ft_moe_nvfp4_prefill) are
- *    the caller's responsibility and are not checked.
+ *    the caller's responsibility (see ft_moe_nvfp4_prefill for bad ids).
+ *  - Every device pointer must be 16-byte aligned; the workspace 256-byte aligned.
  *  - Identical inputs give identical output bits, independent of buffer
  *    addresses, stream and graph replay (no floating-point atomics).
  *  - Supported shapes: hidden % 256 == 0 and hidden <= 8192; inter % 64 == 0 and
@@ -156,7 +157,9 @@ ft_status ft_moe_nvfp4_decode(const ft_moe_desc *desc, int64_t tokens, const uin
                               size_t workspace_bytes, void *stream);
 
 /* The expert part of the layer for prefill chunks, given routes from
- * ft_moe_route (ids must lie in [0, E); not checked on the host).
+ * ft_moe_route.  Ids live in device memory and are not checked on the host; a
+ * token whose ids include a value outside [0, E) gets NaN outputs (the kernels
+ * never read outside the bank).
  *   x bf16 [T][H]; topk_ids i32 [T][k]; topk_w f32 [T][k]; y bf16 [T][H] (output)
  *   shared / shared_gate as for decode. */
 ft_status ft_moe_nvfp4_prefill(const ft_moe_desc *desc, int64_t tokens, const uint16_t *x,

@@ -165,6 +165,7 @@ ft_status run_experts(const ft_moe_desc* desc, int T, const uint16_t* x,
   g.T = T;
   g.H = desc->hidden;
   g.k = desc->top_k;
+  g.E = desc->num_experts;
   g.routed = to_bank(routed, desc->inter);
   g.shared = has_shared ? to_bank(shared, desc->shared_inter) : Bank{};
   g.ids = ids;
@@ -181,6 +182,7 @@ ft_status run_experts(const ft_moe_desc* desc, int T, const uint16_t* x,
   d.H = desc->hidden;
   d.k = desc->top_k;
   d.nslots = desc->top_k + (has_shared ? 1 : 0);
+  d.E = desc->num_experts;
   d.routed = g.routed;
   d.shared = g.shared;
   d.ids = ids;

@@ -47,6 +47,13 @@ __global__ __launch_bounds__(kGUWaves* kWave) void gateup_kernel(GateUpParams p)
   const int H = p.H;
   const int group = lane / LPR, col = lane % LPR;
   const int pair0 = blockIdx.x * PAIRS_PER_BLOCK + (wave * GPW + group) * kGUPairsPerGroup;
+  float* __restrict__ hout = p.h + (static_cast<size_t>(t) * (p.k + 1) + slot) * p.Imax;
+  if (!is_shared && static_cast<unsigned>(e) >= static_cast<unsigned>(p.E)) {
+    // an expert id outside the bank: poison this slot's h instead of reading out of bounds
+    for (int q = 0; q < kGUPairsPerGroup; ++q)
+      if (col == 0 && pair0 + q < I) hout[pair0 + q] = __builtin_nanf("");
+    return;
+  }
 
   // activation chunks of this lane: x[t][32 j .. 32 j + 31], j = col + LPR c
   bf16x2 xr[CPL][16];
@@ -87,7 +94,6 @@ __global__ __launch_bounds__(kGUWaves* kWave) void gateup_kernel(GateUpParams p)
   }
   const float g_gate = b.gsc[3 * e + 0];
   const float g_up = b.gsc[3 * e + 1];
-  float* __restrict__ hout = p.h + (static_cast<size_t>(t) * (p.k + 1) + slot) * p.Imax;
 #pragma unroll
   for (int q = 0; q < kGUPairsPerGroup; ++q) {
     float ag = 0.0f, au = 0.0f;
@@ -114,8 +120,11 @@ __global__ __launch_bounds__(kDownWaves* kWave) void down_kernel(DownParams p) {
   const int nrg = H / kWave;
   const bool is_shared = (slot == p.k);
   const Bank b = is_shared ? p.shared : p.routed;
-  const int e = is_shared ? 0 : p.ids[t * p.k + slot];
-  const int nch = b.inter / 32;
+  const int e_in = is_shared ? 0 : p.ids[t * p.k + slot];
+  // an expert id outside the bank contributes NaN and reads nothing of the bank
+  const bool bad = !is_shared && static_cast<unsigned>(e_in) >= static_cast<unsigned>(p.E);
+  const int e = bad ? 0 : e_in;
+  const int nch = bad ? 0 : b.inter / 32;
   const int cpw = (nch + kDownWaves - 1) / kDownWaves;
   const int j0 = wave * cpw;
   const int j1 = min(nch, j0 + cpw);
@@ -143,7 +152,7 @@ __global__ __launch_bounds__(kDownWaves* kWave) void down_kernel(DownParams p) {
 #pragma unroll
   for (int w = 1; w < kDownWaves; ++w) o += red[w][lane];
   const float ws = is_shared ? p.gamma[t] : p.w[t * p.k + slot];
-  o = (o * b.gsc[3 * e + 2]) * ws;
+  o = bad ? __builtin_nanf("") : (o * b.gsc[3 * e + 2]) * ws;
 
   const size_t pbase = (static_cast<size_t>(t) * nrg + rg) * p.nslots;
   p.part[(pbase + slot) * kWave + lane] = o;

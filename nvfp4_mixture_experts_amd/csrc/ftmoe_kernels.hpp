@@ -40,6 +40,7 @@ struct RouteParams {
 struct GateUpParams {
   const uint16_t* x;  // bf16 [T][H]
   int T, H, k;
+  int E;              // routed experts: an id outside [0, E) yields NaN, never a load
   Bank routed, shared;
   const int32_t* ids; // i32 [T][k]
   float* h;           // f32 [T][k+1][Imax]
@@ -51,6 +52,7 @@ struct GateUpParams {
 // Down GEMV, weighted combine over the selected experts and the shared expert.
 struct DownParams {
   int T, H, k, nslots;  // nslots = k (+1 with a shared expert)
+  int E;                // routed experts: an id outside [0, E) yields NaN, never a load
   Bank routed, shared;
   const int32_t* ids;   // i32 [T][k]
   const float* w;       // f32 [T][k]

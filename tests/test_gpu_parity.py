@@ -226,13 +226,18 @@ def test_decode_is_deterministic(gpu):
     dl = dev_layer(gpu, name)
     x = gpu.tokens_to_device(synth.make_tokens(synth.WORKLOADS[name], tokens=4, stream="det"))
     n = ftmoe.ft_moe_workspace_bytes(dl.desc, 4, ftmoe.PATH_DECODE)
-    big = torch.zeros(n + 4096, dtype=torch.uint8, device="cuda")
+    span = (n + 255) // 256 * 256 + 1024
+    big = torch.zeros(3 * span, dtype=torch.uint8, device="cuda")
+    # disjoint workspaces at different offsets; calls ordered (a workspace is never
+    # shared by calls that may run at the same time)
     y0, _, _ = gpu.decode(dl, x)
     y1, _, _ = gpu.decode(dl, x, workspace=big[1024:1024 + n])
+    main = torch.cuda.current_stream()
     s = torch.cuda.Stream()
+    s.wait_stream(main)
     with torch.cuda.stream(s):
-        y2, _, _ = gpu.decode(dl, x, workspace=big[2048:2048 + n], stream=s)
-    s.synchronize()
+        y2, _, _ = gpu.decode(dl, x, workspace=big[span + 2048:span + 2048 + n], stream=s)
+    main.wait_stream(s)
     torch.cuda.synchronize()
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
     assert torch.equal(y0.view(torch.int16), y2.view(torch.int16))
