@@ -167,7 +167,7 @@ def main() -> int:
                    "bytes_touched_per_cycle": int(touched)},
         "achieved_gbps": round(gbps, 1),
         "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"kernel": "ft_moe_nvfp4_decode (whole call)", "bound": "hbm",
+        "roofline": {"kernel": "moe_decode_fused_kernel", "bound": "hbm",
                      "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": int(round(bytes_per_call))},

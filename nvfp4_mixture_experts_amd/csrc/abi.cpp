@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 
 #include "../../include/ftmoe.h"
 #include "ftmoe_kernels.hpp"
@@ -34,6 +35,28 @@ ft_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int kMaxExperts = 1024;
+constexpr int kMaxDevices = 64;
+constexpr int kMaxFusedGrid = 1024;  // blocks of the fused decode kernel, at most
+constexpr int kSpinLimit = 1 << 20;  // grid-barrier polls (~1 s) before the kernel gives up
+
+// Per-device launch geometry of the fused decode kernel (one block per CU).
+int g_fused_grid[kMaxDevices] = {0};
+
+ft_status fused_grid(int* grid) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FT_EUNSUPPORTED, "device index %d", dev);
+  if (g_fused_grid[dev] == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    if (cus <= 0) return fail(FT_EHIP, "device reports %d compute units", cus);
+    g_fused_grid[dev] = cus < kMaxFusedGrid ? cus : kMaxFusedGrid;
+  }
+  *grid = g_fused_grid[dev];
+  return FT_OK;
+}
 constexpr int kMaxTopK = 16;
 constexpr int kMaxDecodeTokens = 64;
 constexpr int kRowGroup = 64;
@@ -110,14 +133,16 @@ Layout layout(const ft_moe_desc& d, int64_t T, int path) {
   const size_t k = static_cast<size_t>(d.top_k);
   const size_t imax = static_cast<size_t>(d.inter > d.shared_inter ? d.inter : d.shared_inter);
   const size_t nslots = k + (d.shared_inter > 0 ? 1 : 0);
-  L.cnt_route = take(256);
+  L.cnt_route = take(256);  // route counter / fused-decode barrier words
   L.cnt_down = take(path == 0 ? 0 : t * nrg * 4);
   L.logits = take(path == 2 ? 0 : t * static_cast<size_t>(d.num_experts) * 4);
   L.gamma = take(t * 4);
   L.ids = take(t * k * 4);
   L.w = take(t * k * 4);
   L.h = take(path == 0 ? 0 : t * (k + 1) * imax * 4);
-  L.part = take(path == 0 ? 0 : t * nrg * nslots * kRowGroup * 4);
+  const size_t part_multi = t * nrg * nslots * kRowGroup * 4;
+  const size_t part_fused = static_cast<size_t>(kMaxFusedGrid) * kRowGroup * 4;
+  L.part = take(path == 0 ? 0 : (path == 1 ? std::max(part_fused, part_multi) : part_multi));
   L.total = off;
   return L;
 }
@@ -219,6 +244,9 @@ ft_status ft_init(int32_t device) {
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(FT_EUNSUPPORTED, "device %d is %s; this library is built for gfx950", device,
                 prop.gcnArchName);
+  int grid = 0;
+  ft_status st = fused_grid(&grid);
+  if (st != FT_OK) return st;
   return ok();
 }
 
@@ -319,31 +347,44 @@ ft_status ft_moe_nvfp4_decode(const ft_moe_desc* desc, int64_t tokens, const uin
   if ((st = check_layer_args(desc, x, routed, shared, shared_gate, y)) != FT_OK) return st;
   Layout L;
   if ((st = check_ws(desc, tokens, 1, workspace, workspace_bytes, &L)) != FT_OK) return st;
+  int grid = 0;
+  if ((st = fused_grid(&grid)) != FT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool has_shared = desc->shared_inter > 0;
+  const int T = static_cast<int>(tokens);
+  const int nrg = desc->hidden / kRowGroup;
 
-  RouteParams p{};
+  FusedParams p{};
   p.x = x;
   p.wr = w_router;
   p.bias = bias;
   p.shared_gate = has_shared ? shared_gate : nullptr;
-  p.T = static_cast<int>(tokens);
+  p.T = T;
   p.E = desc->num_experts;
   p.H = desc->hidden;
   p.k = desc->top_k;
+  p.act = desc->act;
+  p.gate_max = desc->gate_max;
+  p.up_absmax = desc->up_absmax;
+  p.routed = to_bank(routed, desc->inter);
+  p.shared = has_shared ? to_bank(shared, desc->shared_inter) : Bank{};
+  p.nslots = desc->top_k + (has_shared ? 1 : 0);
+  p.Imax = desc->inter > desc->shared_inter ? desc->inter : desc->shared_inter;
+  p.y = y;
+  p.ids_out = topk_ids_out;
+  p.w_out = topk_w_out;
   p.logits = at<float>(workspace, L.logits);
   p.gamma = at<float>(workspace, L.gamma);
-  p.ids = at<int32_t>(workspace, L.ids);
-  p.w = at<float>(workspace, L.w);
-  p.ids_copy = topk_ids_out;
-  p.w_copy = topk_w_out;
-  p.counter = at<uint32_t>(workspace, L.cnt_route);
-  p.zero = at<uint32_t>(workspace, L.cnt_down);
-  p.nzero = static_cast<int>(tokens) * (desc->hidden / kRowGroup);
-  hipError_t e = launch_route(p, true, s);
-  if (e != hipSuccess) return hip_fail(e, "route kernel");
-  st = run_experts(desc, p.T, x, p.ids, p.w, routed, shared, y, workspace, L, s);
-  if (st != FT_OK) return st;
+  p.h = at<float>(workspace, L.h);
+  p.part = at<float>(workspace, L.part);
+  p.sync = at<uint32_t>(workspace, L.cnt_route);
+  p.cnt = at<uint32_t>(workspace, L.cnt_down);
+  p.d_groups = T * nrg;
+  const int upg = desc->top_k * (desc->inter / 32) + desc->shared_inter / 32;
+  p.blocks_per_group = p.d_groups >= grid ? 1 : std::min(grid / p.d_groups, upg);
+  p.spin_limit = kSpinLimit;
+  hipError_t e = launch_decode_fused(p, grid, s);
+  if (e != hipSuccess) return hip_fail(e, "fused decode kernel");
   return ok();
 }
 

@@ -155,18 +155,17 @@ __global__ __launch_bounds__(kDownWaves* kWave) void down_kernel(DownParams p) {
   o = bad ? __builtin_nanf("") : (o * b.gsc[3 * e + 2]) * ws;
 
   const size_t pbase = (static_cast<size_t>(t) * nrg + rg) * p.nslots;
-  p.part[(pbase + slot) * kWave + lane] = o;
-  __threadfence();
+  st_dev(&p.part[(pbase + slot) * kWave + lane], o);
+  wait_mem();
   uint32_t old = 0;
-  if (lane == 0) old = atomicAdd(&p.cnt[t * nrg + rg], 1u);
-  old = __shfl(old, 0, kWave);
+  if (lane == 0) old = add_dev(&p.cnt[t * nrg + rg], 1u);
+  old = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(old)));
   if (old != static_cast<uint32_t>(p.nslots - 1)) return;
   // last of the nslots blocks of this row group: combine in slot order
-  __threadfence();
   float y = 0.0f;
-  for (int sl = 0; sl < p.nslots; ++sl) y += p.part[(pbase + sl) * kWave + lane];
+  for (int sl = 0; sl < p.nslots; ++sl) y += ld_dev(&p.part[(pbase + sl) * kWave + lane]);
   p.y[static_cast<size_t>(t) * H + c] = f32_to_bf16_bits(y);
-  if (lane == 0) atomicExch(&p.cnt[t * nrg + rg], 0u);
+  if (lane == 0) st_dev(&p.cnt[t * nrg + rg], 0u);
 }
 
 template <int LPR>

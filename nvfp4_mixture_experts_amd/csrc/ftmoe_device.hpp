@@ -142,6 +142,142 @@ __device__ __forceinline__ float chunk_dot_f32(const uint4 q, uint32_t sc2, cons
   return b0 * e4m3_byte_to_f32<0>(sc2) + b1 * e4m3_byte_to_f32<1>(sc2);
 }
 
+// ------------------------------------------- device-coherent hand-offs --
+//
+// Data that one block of a kernel hands to another block of the same kernel is
+// written and read with device-scope relaxed atomics: on gfx950 these are plain
+// loads/stores carrying the device-coherence cache policy (they bypass the
+// per-XCD L2 copies), so no cache-wide write-back or invalidate is needed.
+// The producer waits for its stores to complete (wait_mem) before it signals a
+// counter; the consumer reads the counter, then the data.
+
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ------------------------------------------------------ DPP wave reductions --
+//
+// Reductions across the 64 lanes of a wave with DPP row shifts and row
+// broadcasts (no LDS round trip); the result is returned to every lane.
+
+template <uint32_t Identity, class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(Identity), static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(Identity), static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(Identity), static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(Identity), static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(Identity), static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(Identity), static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// Lane `src` (wave-uniform) of a double, broadcast through scalar registers.
+__device__ __forceinline__ double readlane_f64(double v, int src) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), src));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), src));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_u32<0u>(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32<0xFFFFFFFFu>(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+
+// ------------------------------------------------------------------ top-k --
+//
+// Rank key of a logit: an unsigned integer that orders like the logit, with
+// -0 folded onto +0 (they compare equal) and a NaN below every number (key 1).
+// Key 0 marks "no candidate".
+__device__ __forceinline__ uint32_t rank_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 1u;  // NaN
+  if ((u & 0x7FFFFFFFu) == 0u) u = 0u;              // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+  if (key == 1u) return __builtin_nanf("");
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Top-k of one token's E (<= 64 * SLOTS) logits by one wave: experts ordered by
+// (logit descending, index ascending), then the softmax of the selected logits
+// (fp64 exp, stored as fp32).  Lane l holds experts l, l + 64, ...  Returns the
+// rank-i expert and weight in lane i (i < k); other lanes return -1 / 0.
+template <int SLOTS, class Load>
+__device__ __forceinline__ void wave_topk(int E, int k, Load load_logit, int* out_id,
+                                          float* out_w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t key[SLOTS];
+#pragma unroll
+  for (int m = 0; m < SLOTS; ++m) {
+    const int e = lane + kWave * m;
+    key[m] = (e < E) ? rank_key(load_logit(e)) : 0u;
+  }
+  // the lane's best untaken candidate (lowest slot among equal keys)
+  auto local_best = [&](uint32_t& bk, uint32_t& be) {
+    bk = 0u;
+    be = 0xFFFFFFFFu;
+#pragma unroll
+    for (int m = SLOTS - 1; m >= 0; --m) {
+      if (key[m] >= bk && key[m] != 0u) {
+        bk = key[m];
+        be = static_cast<uint32_t>(lane + kWave * m);
+      }
+    }
+  };
+  uint32_t lk, le;
+  local_best(lk, le);
+  int my_id = -1;
+  uint32_t my_key = 0u;
+  for (int i = 0; i < k; ++i) {
+    const uint32_t K = wave_max_u32(lk);
+    const uint64_t holders = __ballot(lk == K);
+    uint32_t win;
+    if (__popcll(holders) == 1) {
+      const int wl = __ffsll(static_cast<unsigned long long>(holders)) - 1;
+      win = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(le), wl));
+    } else {
+      win = wave_min_u32(lk == K ? le : 0xFFFFFFFFu);
+    }
+    if (lane == i) {
+      my_id = static_cast<int>(win);
+      my_key = K;
+    }
+    if (static_cast<int>(win & (kWave - 1)) == lane) {
+      const int wm = static_cast<int>(win) / kWave;
+#pragma unroll
+      for (int m = 0; m < SLOTS; ++m)
+        if (m == wm) key[m] = 0u;
+      local_best(lk, le);
+    }
+  }
+  // softmax over the selected logits, in fp64, summed in rank order
+  const double top = static_cast<double>(key_value(static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(my_key), 0))));
+  const double d = (lane < k) ? exp(static_cast<double>(key_value(my_key)) - top) : 0.0;
+  double sum = 0.0;
+  for (int i = 0; i < k; ++i) sum += readlane_f64(d, i);
+  *out_id = my_id;
+  *out_w = (lane < k) ? static_cast<float>(d / sum) : 0.0f;
+}
+
 // ------------------------------------------------------------- activation --
 
 // silu(z) = z / (1 + exp(-z)); for very negative z, exp(-z) overflows to +inf and

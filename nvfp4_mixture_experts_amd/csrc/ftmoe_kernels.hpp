@@ -64,7 +64,33 @@ struct DownParams {
   uint16_t* y;          // bf16 [T][H]
 };
 
+// The whole decode layer in one persistent launch (one block per CU).
+struct FusedParams {
+  const uint16_t* x;            // bf16 [T][H]
+  const float* wr;              // f32 [E][H]
+  const float* bias;            // f32 [E] or null
+  const uint16_t* shared_gate;  // bf16 [H] or null
+  int T, E, H, k, act;
+  float gate_max, up_absmax;
+  Bank routed, shared;          // shared.inter == 0: no shared expert
+  int nslots, Imax;
+  uint16_t* y;                  // bf16 [T][H]
+  int32_t* ids_out;             // optional i32 [T][k]
+  float* w_out;                 // optional f32 [T][k]
+  float* logits;                // f32 [T][E]
+  float* gamma;                 // f32 [T]
+  float* h;                     // f32 [T][nslots][Imax]
+  float* part;                  // f32 [d_groups][blocks_per_group][64]
+  uint32_t* sync;               // [0] barrier 1, [1] barrier 2, [2] exits, [3] error flag
+  uint32_t* cnt;                // u32 [d_groups] combine counters
+  int d_groups;                 // T * H / 64 (token, row group) pairs of the down GEMV
+  int blocks_per_group;         // blocks sharing one group when d_groups < grid
+  int spin_limit;               // barrier polls before giving up (error flag)
+};
+
 // Launchers: return the launch status (hipGetLastError after the launch).
+hipError_t launch_decode_fused(const FusedParams& p, int grid, hipStream_t s);
+int fused_block_threads();
 hipError_t launch_route(const RouteParams& p, bool fuse_topk, hipStream_t s);
 hipError_t launch_topk(const RouteParams& p, hipStream_t s);
 hipError_t launch_gateup(const GateUpParams& p, hipStream_t s);

@@ -14,67 +14,25 @@ namespace ftmoe {
 
 constexpr int kRouteWaves = 4;   // one expert row per wave
 constexpr int kRouteTokTile = 64;
-constexpr int kMaxExperts = 1024;
-constexpr int kTopkSlotsPerLane = kMaxExperts / kWave;
 
-// Rank order of the top-k: larger logit first, then lower index; a NaN logit
-// ranks below every number; index -1 means "no candidate".
-__device__ __forceinline__ bool ranks_above(float a, int ia, float b, int ib) {
-  if (ia < 0) return false;
-  if (ib < 0) return true;
-  const bool an = __builtin_isnan(a), bn = __builtin_isnan(b);
-  if (an || bn) return (an && bn) ? (ia < ib) : bn;
-  if (a != b) return a > b;
-  return ia < ib;
-}
-
-// Top-k of one token's E logits by one wave, then the softmax of the selected
-// logits (fp64 exp, stored as fp32).  ids/w are emitted in rank order.
-__device__ void topk_one_token(const float* __restrict__ lg, int E, int k, int32_t* ids,
-                               float* w, int32_t* ids2, float* w2) {
+// Top-k of one token by one wave (wave_topk), written in rank order.
+template <class Load>
+__device__ void topk_one_token(int E, int k, Load load, int32_t* ids, float* w, int32_t* ids2,
+                               float* w2) {
   const int lane = threadIdx.x & (kWave - 1);
-  float v[kTopkSlotsPerLane];
-#pragma unroll
-  for (int m = 0; m < kTopkSlotsPerLane; ++m) {
-    const int e = lane + kWave * m;
-    v[m] = (e < E) ? lg[e] : 0.0f;
-  }
-  uint32_t taken = 0;
-  float mine = 0.0f;  // lane i keeps the logit of rank i
-  for (int i = 0; i < k; ++i) {
-    float bv = 0.0f;
-    int be = -1;
-#pragma unroll
-    for (int m = 0; m < kTopkSlotsPerLane; ++m) {
-      const int e = lane + kWave * m;
-      if (e < E && !((taken >> m) & 1u) && ranks_above(v[m], e, bv, be)) {
-        bv = v[m];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oe = __shfl_xor(be, off, kWave);
-      if (ranks_above(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
-    if (lane == i) mine = bv;
-    if (lane == 0) {
-      ids[i] = be;
-      if (ids2) ids2[i] = be;
-    }
-  }
-  const double top = static_cast<double>(__shfl(mine, 0, kWave));
-  const double d = (lane < k) ? exp(static_cast<double>(mine) - top) : 0.0;
-  const double sum = group_sum<kWave>(d);
+  int id;
+  float wt;
+  if (E <= 4 * kWave)
+    wave_topk<4>(E, k, load, &id, &wt);
+  else if (E <= 8 * kWave)
+    wave_topk<8>(E, k, load, &id, &wt);
+  else
+    wave_topk<16>(E, k, load, &id, &wt);
   if (lane < k) {
-    const float wi = static_cast<float>(d / sum);
-    w[lane] = wi;
-    if (w2) w2[lane] = wi;
+    ids[lane] = id;
+    w[lane] = wt;
+    if (ids2) ids2[lane] = id;
+    if (w2) w2[lane] = wt;
   }
 }
 
@@ -120,7 +78,7 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_logits_kernel(RouteP
       acc = group_sum<kWave>(acc);
       if (lane == 0) {
         if (p.bias) acc += b;
-        p.logits[static_cast<size_t>(t) * p.E + row] = static_cast<float>(acc);
+        st_dev(&p.logits[static_cast<size_t>(t) * p.E + row], static_cast<float>(acc));
       }
     }
   } else if (row == p.E && p.shared_gate != nullptr) {
@@ -149,26 +107,27 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_logits_kernel(RouteP
   }
 
   if (!fuse_topk) return;
-  // Last-arriver top-k: every block publishes its logits, and the block that
-  // arrives last (one device-scope counter) selects the experts of all tokens.
-  // No block waits for another, so the grid needs no co-residency.
+  // Last-arriver top-k: every block publishes its logits (device-coherent
+  // stores), and the block that arrives last at one device-scope counter selects
+  // the experts of all tokens.  No block waits for another.
   __shared__ uint32_t s_last;
-  __threadfence();
+  wait_mem();
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t nblocks = gridDim.x * gridDim.y;
-    const uint32_t old = atomicAdd(p.counter, 1u);
+    const uint32_t old = add_dev(p.counter, 1u);
     s_last = (old == nblocks - 1) ? 1u : 0u;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-  for (int t = wave; t < p.T; t += kRouteWaves)
-    topk_one_token(p.logits + static_cast<size_t>(t) * p.E, p.E, p.k,
+  for (int t = wave; t < p.T; t += kRouteWaves) {
+    const float* lg = p.logits + static_cast<size_t>(t) * p.E;
+    topk_one_token(p.E, p.k, [&](int e) { return ld_dev(lg + e); },
                    p.ids + static_cast<size_t>(t) * p.k, p.w + static_cast<size_t>(t) * p.k,
                    p.ids_copy ? p.ids_copy + static_cast<size_t>(t) * p.k : nullptr,
                    p.w_copy ? p.w_copy + static_cast<size_t>(t) * p.k : nullptr);
-  if (threadIdx.x == 0) atomicExch(p.counter, 0u);
+  }
+  if (threadIdx.x == 0) st_dev(p.counter, 0u);
 }
 
 // One wave per token (used when the token count is too large for one block).
@@ -176,7 +135,8 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void topk_kernel(RouteParams p)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = blockIdx.x * kRouteWaves + wave;
   if (t >= p.T) return;
-  topk_one_token(p.logits + static_cast<size_t>(t) * p.E, p.E, p.k,
+  const float* __restrict__ lg = p.logits + static_cast<size_t>(t) * p.E;
+  topk_one_token(p.E, p.k, [&](int e) { return lg[e]; },
                  p.ids + static_cast<size_t>(t) * p.k, p.w + static_cast<size_t>(t) * p.k,
                  p.ids_copy ? p.ids_copy + static_cast<size_t>(t) * p.k : nullptr,
                  p.w_copy ? p.w_copy + static_cast<size_t>(t) * p.k : nullptr);
