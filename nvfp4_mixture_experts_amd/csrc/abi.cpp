@@ -8,7 +8,7 @@
 #include <cstring>
 #include <algorithm>
 
-#include "../../include/ftmoe.h"
+#include "ftmoe.h"
 #include "ftmoe_kernels.hpp"
 
 using namespace ftmoe;
@@ -36,7 +36,6 @@ ft_status hip_fail(hipError_t e, const char* what) {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxDevices = 64;
-constexpr int kMaxFusedGrid = 1024;  // blocks of the fused decode kernel, at most
 constexpr int kSpinLimit = 1 << 20;  // grid-barrier polls (~1 s) before the kernel gives up
 
 // Per-device launch geometry of the fused decode kernel (one block per CU).
@@ -117,8 +116,11 @@ Bank to_bank(const ft_nvfp4_experts* b, int inter) {
 // the first kernel of each call, so a workspace may be shared between paths
 // and token counts once it has been zero-filled.
 struct Layout {
-  size_t cnt_route, cnt_down, logits, gamma, ids, w, h, part, total;
+  size_t sync, gen, cnt_down, logits, gamma, ids, w, h, part, total;
 };
+
+constexpr int kRouteCounterWord = 0;  // in the sync region
+constexpr int kErrorWord = 32;        // in the sync region (its own cache line)
 
 Layout layout(const ft_moe_desc& d, int64_t T, int path) {
   Layout L{};
@@ -131,18 +133,21 @@ Layout layout(const ft_moe_desc& d, int64_t T, int path) {
   const size_t t = static_cast<size_t>(T);
   const size_t nrg = static_cast<size_t>(d.hidden / kRowGroup);
   const size_t k = static_cast<size_t>(d.top_k);
+  const size_t E = static_cast<size_t>(d.num_experts);
   const size_t imax = static_cast<size_t>(d.inter > d.shared_inter ? d.inter : d.shared_inter);
   const size_t nslots = k + (d.shared_inter > 0 ? 1 : 0);
-  L.cnt_route = take(256);  // route counter / fused-decode barrier words
-  L.cnt_down = take(path == 0 ? 0 : t * nrg * 4);
-  L.logits = take(path == 2 ? 0 : t * static_cast<size_t>(d.num_experts) * 4);
-  L.gamma = take(t * 4);
-  L.ids = take(t * k * 4);
-  L.w = take(t * k * 4);
-  L.h = take(path == 0 ? 0 : t * (k + 1) * imax * 4);
-  const size_t part_multi = t * nrg * nslots * kRowGroup * 4;
-  const size_t part_fused = static_cast<size_t>(kMaxFusedGrid) * kRowGroup * 4;
-  L.part = take(path == 0 ? 0 : (path == 1 ? std::max(part_fused, part_multi) : part_multi));
+  const bool fused = (path == 1);
+  L.sync = take(256);  // route counter, error word
+  L.gen = take(fused ? static_cast<size_t>(kMaxFusedGrid) * 4 : 0);
+  L.cnt_down = take(path == 2 ? t * nrg * 4 : 0);
+  L.logits = take(path == 0 ? t * E * 4
+                            : (fused ? static_cast<size_t>(kLogitCopies) * t * (E + 1) * 8 : 0));
+  L.gamma = take(path == 2 ? t * 4 : 0);
+  L.ids = take(0);
+  L.w = take(0);
+  L.h = take(fused ? t * nslots * imax * 8 : (path == 2 ? t * (k + 1) * imax * 4 : 0));
+  L.part = take(fused ? static_cast<size_t>(kMaxFusedGrid) * kRowGroup * 8
+                      : (path == 2 ? t * nrg * nslots * kRowGroup * 4 : 0));
   L.total = off;
   return L;
 }
@@ -319,7 +324,7 @@ ft_status ft_moe_route(const ft_moe_desc* desc, int64_t tokens, const uint16_t* 
   p.gamma = nullptr;
   p.ids = topk_ids;
   p.w = topk_w;
-  p.counter = at<uint32_t>(workspace, L.cnt_route);
+  p.counter = at<uint32_t>(workspace, L.sync) + kRouteCounterWord;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fuse = tokens <= kMaxDecodeTokens;
   hipError_t e = launch_route(p, fuse, s);
@@ -373,12 +378,11 @@ ft_status ft_moe_nvfp4_decode(const ft_moe_desc* desc, int64_t tokens, const uin
   p.y = y;
   p.ids_out = topk_ids_out;
   p.w_out = topk_w_out;
-  p.logits = at<float>(workspace, L.logits);
-  p.gamma = at<float>(workspace, L.gamma);
-  p.h = at<float>(workspace, L.h);
-  p.part = at<float>(workspace, L.part);
-  p.sync = at<uint32_t>(workspace, L.cnt_route);
-  p.cnt = at<uint32_t>(workspace, L.cnt_down);
+  p.logits = at<uint64_t>(workspace, L.logits);
+  p.h = at<uint64_t>(workspace, L.h);
+  p.part = at<uint64_t>(workspace, L.part);
+  p.gen = at<uint32_t>(workspace, L.gen);
+  p.err = at<uint32_t>(workspace, L.sync) + kErrorWord;
   p.d_groups = T * nrg;
   const int upg = desc->top_k * (desc->inter / 32) + desc->shared_inter / 32;
   p.blocks_per_group = p.d_groups >= grid ? 1 : std::min(grid / p.d_groups, upg);

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kGUWaves* kWave) void gateup_kernel(GateUpParams p)
   if (!is_shared && static_cast<unsigned>(e) >= static_cast<unsigned>(p.E)) {
     // an expert id outside the bank: poison this slot's h instead of reading out of bounds
     for (int q = 0; q < kGUPairsPerGroup; ++q)
-      if (col == 0 && pair0 + q < I) hout[pair0 + q] = __builtin_nanf("");
+      if (col == LPR - 1 && pair0 + q < I) hout[pair0 + q] = __builtin_nanf("");
     return;
   }
 
@@ -102,10 +102,10 @@ __global__ __launch_bounds__(kGUWaves* kWave) void gateup_kernel(GateUpParams p)
       ag += chunk_dot_bf16(qg[q][c], sg[q][c], xr[c]);
       au += chunk_dot_bf16(qu[q][c], su[q][c], xr[c]);
     }
-    ag = group_sum<LPR>(ag);
-    au = group_sum<LPR>(au);
+    ag = group_sum_last<LPR>(ag);
+    au = group_sum_last<LPR>(au);
     const int r = pair0 + q;
-    if (col == 0 && r < I)
+    if (col == LPR - 1 && r < I)
       hout[r] = swiglu(p.act, ag * g_gate, au * g_up, p.gate_max, p.up_absmax);
   }
 }

@@ -6,26 +6,33 @@
 // and shared-gate kernels, non-power-of-2 top-k, clamped SwiGLU, 512 routed
 // experts with top-10 plus a gated shared expert, a "deep-K" decode config.
 //
-// At batch 1 the layer moves ~24 MB and the HBM floor is ~3 us, the same order
-// as a kernel boundary, so the layer runs as one launch of one block per CU:
+// At batch 1 the layer moves ~24 MB: about 3 us of HBM time, the same order as
+// one kernel launch or one grid-wide barrier.  So the layer is one launch of one
+// block per CU, and no phase waits on a barrier: every value one block hands to
+// another is TAGGED with the call's generation number (value in the low half of
+// an 8-byte word, generation in the high half, written and read with single
+// device-coherent 8-byte accesses), and a consumer polls exactly the values it
+// needs until their tags match.  Each block counts its own calls, so all blocks
+// agree on the generation without talking to each other, and nothing needs
+// resetting between calls.
 //
-//   R  router rows (fp64 dot products, one per wave) and the shared gate;
-//      logits published with device-coherent stores.          -> grid barrier 1
-//   S  every block selects the top-k of every token itself (DPP wave reductions,
-//      no second barrier) and keeps ids, weights and gates in LDS.
-//   W  every wave issues the loads of its down-projection chunks (kept in
-//      registers across the next barrier), then streams its gate|up rows:
+//   R  router rows (one row per wave, rows spread one per CU; fp64 dot products
+//      with a DPP tree sum) and the shared gate; each logit is published in
+//      kLogitCopies replicas so that 256 blocks do not read the same lines.
+//   S  every block selects the experts itself from its replica: 8 waves each
+//      take the top-k of 64 experts, one wave merges the candidates (DPP max
+//      reductions and ballots; ties go to the lower index).
+//   W  every wave issues its gate|up loads, then the loads of its first
+//      down-projection chunks (kept in registers for D), then computes:
 //      e2m1 -> bf16 in registers, v_dot2_f32_bf16 against bf16 x, per-16 e4m3
-//      block scales, global scales, (clamped) SwiGLU; h published.
-//                                                              -> grid barrier 2
+//      block scales, global scales, (clamped) SwiGLU; h published tagged.
 //   D  down GEMV from the prefetched chunks (lane = output row, K-chunk-major
-//      codes, h read as wave-uniform device-coherent loads), weighted by the
-//      routing weight / shared gate; blocks of one row group combine through
-//      device-coherent partials and a last-arriver counter, in a fixed order.
+//      codes, h polled as wave-uniform loads), weighted by routing weight or
+//      shared gate; the blocks of one row group publish tagged partials and one
+//      of them sums them in a fixed order into bf16 y.
 //
-// Grid barriers are device-scope counters polled with a bounded spin (a grid
-// that is not co-resident cannot hang: the spin gives up and flags an error).
-// Every counter is back at zero when the kernel ends.
+// Every poll is bounded: if a value never arrives (a grid that is not
+// co-resident), the kernel stops waiting, raises the error word and finishes.
 #include "ftmoe_device.hpp"
 #include "ftmoe_kernels.hpp"
 
@@ -35,53 +42,231 @@ constexpr int kFWaves = 8;     // waves per block
 constexpr int kUW = 3;         // gate|up units per wave and batch
 constexpr int kUD = 3;         // down units per wave and batch (first batch prefetched)
 constexpr int kMaxTK = 64 * 16;
+constexpr int kMaxChunks = 16; // 64-expert chunks of the first top-k stage (E <= 1024)
+constexpr int kMaxK = 16;
 
-// 16 bytes at base + byte_off (wave-uniform base and offset), device-coherent.
-__device__ __forceinline__ float4 ld_dev_x4_uniform(const float* base, uint32_t byte_off) {
-  __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), static_cast<short>(0), 0x7fffffff,
-                                        0x00020000);
-  typedef int int4v __attribute__((ext_vector_type(4)));
-  const int4v v = __builtin_amdgcn_raw_buffer_load_b128(r, 0, static_cast<int>(byte_off), 16);
-  return __builtin_bit_cast(float4, v);
+// ------------------------------------------------------------ tagged words --
+
+__device__ __forceinline__ uint64_t tagged(float v, uint32_t gen) {
+  return (static_cast<uint64_t>(gen) << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ void st_tag(uint64_t* p, float v, uint32_t gen) {
+  __hip_atomic_store(p, tagged(v, gen), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tag(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_is(uint64_t w, uint32_t gen) {
+  return static_cast<uint32_t>(w >> 32) == gen;
+}
+__device__ __forceinline__ float tag_value(uint64_t w) {
+  return __uint_as_float(static_cast<uint32_t>(w));
 }
 
-__device__ __forceinline__ void grid_barrier(uint32_t* counter, uint32_t target, uint32_t* err,
-                                             int spin_limit) {
-  wait_mem();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    add_dev(counter, 1u);
-    int spins = 0;
-    while (ld_dev(counter) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > spin_limit) {
-        st_dev(err, 1u);
-        break;
+// 16 bytes (two tagged words) at base + byte_off, wave-uniform, device-coherent.
+__device__ __forceinline__ uint4 ld_dev_x4_uniform(const void* base, uint32_t byte_off) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(base), static_cast<short>(0), 0x7fffffff, 0x00020000);
+  typedef int int4v __attribute__((ext_vector_type(4)));
+  const int4v v = __builtin_amdgcn_raw_buffer_load_b128(r, 0, static_cast<int>(byte_off), 16);
+  return __builtin_bit_cast(uint4, v);
+}
+
+// Reads one tagged word per lane, polling until every lane's word carries `gen`.
+__device__ __forceinline__ uint64_t poll_tag(const uint64_t* p, uint32_t gen, int spin_limit,
+                                             uint32_t* err) {
+  uint64_t wd = ld_tag(p);
+  for (int spins = 0; __ballot(!tag_is(wd, gen)) != 0; ++spins) {
+    if (spins >= spin_limit) {
+      st_dev(err, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    if (!tag_is(wd, gen)) wd = ld_tag(p);
+  }
+  return wd;
+}
+
+// Reads the 32 tagged h values of one down unit (wave-uniform address) into hv,
+// polling until all carry `gen`.
+__device__ __forceinline__ void poll_h_chunk(const uint64_t* hrow, uint32_t gen, float* hv,
+                                             int spin_limit, uint32_t* err) {
+  for (int spins = 0;; ++spins) {
+    bool ok = true;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const uint4 v = ld_dev_x4_uniform(hrow, static_cast<uint32_t>(16 * m));
+      hv[2 * m] = __uint_as_float(v.x);
+      hv[2 * m + 1] = __uint_as_float(v.z);
+      ok = ok && (v.y == gen) && (v.w == gen);
+    }
+    if (__ballot(!ok) == 0) return;
+    if (spins >= spin_limit) {
+      st_dev(err, 1u);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// ------------------------------------------------------------- top-k --
+
+// The shared expert's gate of one token (word E of its logits row), by one lane.
+__device__ __forceinline__ float poll_gate(const uint64_t* lg, int E, uint32_t gen,
+                                           int spin_limit, uint32_t* err) {
+  uint64_t wd = ld_tag(lg + E);
+  for (int spins = 0; !tag_is(wd, gen); ++spins) {
+    if (spins >= spin_limit) {
+      st_dev(err, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    wd = ld_tag(lg + E);
+  }
+  return tag_value(wd);
+}
+
+// The experts of one token's logits row (tagged, E + 1 words; word E is the
+// shared gate) by all waves of the block.  Stage 1: wave w takes 64-expert
+// chunks w, w + 8: k rounds of (wave max key, lowest lane holding it) give the
+// chunk's top-k in rank order.  Stage 2: wave 0 merges the candidates, ordered
+// (chunk, rank), with the same rounds; in that order equal keys appear by
+// ascending expert index, so ties go to the lower index.  Results go to ids,
+// w (softmax of the selected logits, fp64 exp) and gamma.
+__device__ void block_topk_one_token(const uint64_t* lg, int E, int k, uint32_t gen,
+                                     int spin_limit, uint32_t* err, uint32_t (*s_ck)[kMaxK],
+                                     int (*s_ci)[kMaxK], int* ids, float* w, float* gamma,
+                                     bool has_shared) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nchunks = (E + kWave - 1) / kWave;
+  for (int c = wave; c < nchunks; c += kFWaves) {
+    const int e = c * kWave + lane;
+    const uint64_t wd = poll_tag(lg + (e < E ? e : E - 1), gen, spin_limit, err);
+    uint32_t key = (e < E) ? rank_key(tag_value(wd)) : 0u;
+    for (int i = 0; i < k; ++i) {
+      const uint32_t K = wave_max_u32(key);
+      const uint64_t b = __ballot(key == K && K != 0u);
+      const int wl = (b != 0) ? __ffsll(static_cast<unsigned long long>(b)) - 1 : -1;
+      if (lane == 0) {
+        s_ck[c][i] = K;
+        s_ci[c][i] = (wl >= 0) ? c * kWave + wl : -1;
       }
+      if (lane == wl) key = 0u;
     }
   }
   __syncthreads();
+  if (wave == 0) {
+    const int n2 = nchunks * k;  // <= 256 candidates
+    uint32_t key2[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int j = lane + kWave * m;
+      key2[m] = (j < n2) ? s_ck[j / k][j % k] : 0u;
+    }
+    int my_id = -1;
+    uint32_t my_key = 0u;
+    uint32_t lmax = key2[0];
+#pragma unroll
+    for (int m = 1; m < 4; ++m) lmax = key2[m] > lmax ? key2[m] : lmax;
+    for (int i = 0; i < k; ++i) {
+      const uint32_t K = wave_max_u32(lmax);
+      int win = -1;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (win < 0) {
+          const uint64_t b = __ballot(key2[m] == K);
+          if (b != 0) win = kWave * m + __ffsll(static_cast<unsigned long long>(b)) - 1;
+        }
+      }
+      if (lane == i) {
+        my_id = s_ci[win / k][win % k];
+        my_key = K;
+      }
+      if ((win & (kWave - 1)) == lane) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          if (m == (win >> 6)) key2[m] = 0u;
+        lmax = key2[0];
+#pragma unroll
+        for (int m = 1; m < 4; ++m) lmax = key2[m] > lmax ? key2[m] : lmax;
+      }
+    }
+    const double top = static_cast<double>(key_value(static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(my_key), 0))));
+    const double d = (lane < k) ? exp(static_cast<double>(key_value(my_key)) - top) : 0.0;
+    double sum = 0.0;
+    for (int i = 0; i < k; ++i) sum += readlane_f64(d, i);
+    if (lane < k) {
+      ids[lane] = my_id;
+      w[lane] = static_cast<float>(d / sum);
+    }
+    if (lane == 0) *gamma = has_shared ? poll_gate(lg, E, gen, spin_limit, err) : 0.0f;
+  }
 }
+
+// One token's experts by one wave (used when the block handles several tokens).
+template <int SLOTS>
+__device__ void wave_topk_tagged(const uint64_t* lg, int E, int k, uint32_t gen, int spin_limit,
+                                 uint32_t* err, int* ids, float* w, float* gamma,
+                                 bool has_shared) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t wd[SLOTS];
+#pragma unroll
+  for (int m = 0; m < SLOTS; ++m) {
+    const int e = lane + kWave * m;
+    wd[m] = ld_tag(lg + (e < E ? e : E - 1));
+  }
+  for (int spins = 0;; ++spins) {
+    bool ok = true;
+#pragma unroll
+    for (int m = 0; m < SLOTS; ++m) ok = ok && tag_is(wd[m], gen);
+    if (__ballot(!ok) == 0) break;
+    if (spins >= spin_limit) {
+      st_dev(err, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int m = 0; m < SLOTS; ++m) {
+      const int e = lane + kWave * m;
+      if (!tag_is(wd[m], gen)) wd[m] = ld_tag(lg + (e < E ? e : E - 1));
+    }
+  }
+  float lv[SLOTS];
+#pragma unroll
+  for (int m = 0; m < SLOTS; ++m) lv[m] = tag_value(wd[m]);
+  int id;
+  float wt;
+  wave_topk_vals<SLOTS>(E, k, lv, &id, &wt);
+  if (lane < k) {
+    ids[lane] = id;
+    w[lane] = wt;
+  }
+  if (lane == 0) *gamma = has_shared ? poll_gate(lg, E, gen, spin_limit, err) : 0.0f;
+}
+
+// --------------------------------------------------------------- units --
 
 struct Unit13 {  // one (token, slot, pair) of the gate|up GEMV, for one lane group
   int t, slot, r;
   bool valid;
 };
 
-__device__ __forceinline__ Unit13 unit13(const FusedParams& p, int u, int total) {
+// Pair u of the flattened (token, slot, row) space: per token, the k routed
+// experts' I rows, then the shared expert's Is rows.
+__device__ __forceinline__ Unit13 unit13(int u, int total, int k, int kI, FastDiv ppt,
+                                         FastDiv inter) {
   Unit13 o;
   o.valid = u < total;
   if (!o.valid) u = 0;
-  const int ppt = p.k * p.routed.inter + p.shared.inter;
-  o.t = u / ppt;
-  const int rem = u - o.t * ppt;
-  const int kI = p.k * p.routed.inter;
+  o.t = fdiv(u, ppt);
+  const int rem = u - o.t * ppt.d;
   if (rem < kI) {
-    o.slot = rem / p.routed.inter;
-    o.r = rem - o.slot * p.routed.inter;
+    o.slot = fdiv(rem, inter);
+    o.r = rem - o.slot * inter.d;
   } else {
-    o.slot = p.k;
+    o.slot = k;
     o.r = rem - kI;
   }
   return o;
@@ -91,23 +276,24 @@ struct Unit2 {  // one (slot, K-chunk) of the down GEMV of one row group
   int slot, chunk;
 };
 
-__device__ __forceinline__ Unit2 unit2(const FusedParams& p, int v) {
-  const int nch = p.routed.inter / 32;
+__device__ __forceinline__ Unit2 unit2(int v, int k, FastDiv nch) {
   Unit2 o;
-  if (v < p.k * nch) {
-    o.slot = v / nch;
-    o.chunk = v - o.slot * nch;
+  if (v < k * nch.d) {
+    o.slot = fdiv(v, nch);
+    o.chunk = v - o.slot * nch.d;
   } else {
-    o.slot = p.k;
-    o.chunk = v - p.k * nch;
+    o.slot = k;
+    o.chunk = v - k * nch.d;
   }
   return o;
 }
 
+// ---------------------------------------------------------------- kernel --
+
 template <int LPR, int CPL>
 __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(FusedParams p) {
-  constexpr int GPW = kWave / LPR;      // lane groups per wave
-  constexpr int NC = LPR * CPL / 8;     // float4 pieces of a router row per lane (H / 256)
+  constexpr int GPW = kWave / LPR;   // lane groups per wave
+  constexpr int NC = LPR * CPL / 8;  // float4 pieces of a router row per lane (H / 256)
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x;
@@ -115,97 +301,109 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   const int NW = G * kFWaves;
   const int H = p.H, E = p.E, T = p.T, k = p.k;
   const int nrg = H / kWave;
+  const int E1 = E + 1;
 
   __shared__ int s_ids[kMaxTK];
   __shared__ float s_w[kMaxTK];
   __shared__ float s_gamma[64];
   __shared__ float s_red[kFWaves][kWave];
+  __shared__ uint32_t s_ck[kMaxChunks][kMaxK];
+  __shared__ int s_ci[kMaxChunks][kMaxK];
+  __shared__ uint32_t s_gen;
 
-  // ---------------------------------------------------------------- R --
-  // clear the combine counters of this call (used only after barrier 2)
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < p.d_groups; i += G * blockDim.x)
-    st_dev(&p.cnt[i], 0u);
-  {
-    const int rows = E + (p.shared_gate ? 1 : 0);
-    for (int row = gw; row < rows; row += NW) {
-      if (row < E) {
-        const float* __restrict__ wrow = p.wr + static_cast<size_t>(row) * H;
-        float4 wv[NC];
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          wv[c] = *reinterpret_cast<const float4*>(wrow + 4 * lane + 4 * kWave * c);
-        for (int t = 0; t < T; ++t) {
-          const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
-          double acc = 0.0;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const uint2 xb = *reinterpret_cast<const uint2*>(xt + 4 * lane + 4 * kWave * c);
-            acc = fma(static_cast<double>(wv[c].x), static_cast<double>(bf16_bits_to_f32(xb.x & 0xFFFFu)), acc);
-            acc = fma(static_cast<double>(wv[c].y), static_cast<double>(bf16_bits_to_f32(xb.x >> 16)), acc);
-            acc = fma(static_cast<double>(wv[c].z), static_cast<double>(bf16_bits_to_f32(xb.y & 0xFFFFu)), acc);
-            acc = fma(static_cast<double>(wv[c].w), static_cast<double>(bf16_bits_to_f32(xb.y >> 16)), acc);
-          }
-          acc = group_sum<kWave>(acc);
-          if (lane == 0) {
-            if (p.bias) acc += static_cast<double>(p.bias[row]);
-            st_dev(&p.logits[static_cast<size_t>(t) * E + row], static_cast<float>(acc));
-          }
-        }
-      } else {
-        uint2 gv[NC];
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          gv[c] = *reinterpret_cast<const uint2*>(p.shared_gate + 4 * lane + 4 * kWave * c);
-        for (int t = 0; t < T; ++t) {
-          const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
-          double acc = 0.0;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const uint2 xb = *reinterpret_cast<const uint2*>(xt + 4 * lane + 4 * kWave * c);
-            acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].x & 0xFFFFu)),
-                      static_cast<double>(bf16_bits_to_f32(xb.x & 0xFFFFu)), acc);
-            acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].x >> 16)),
-                      static_cast<double>(bf16_bits_to_f32(xb.x >> 16)), acc);
-            acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].y & 0xFFFFu)),
-                      static_cast<double>(bf16_bits_to_f32(xb.y & 0xFFFFu)), acc);
-            acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].y >> 16)),
-                      static_cast<double>(bf16_bits_to_f32(xb.y >> 16)), acc);
-          }
-          acc = group_sum<kWave>(acc);
-          if (lane == 0) st_dev(&p.gamma[t], static_cast<float>(1.0 / (1.0 + exp(-acc))));
-        }
-      }
-    }
-  }
-  grid_barrier(&p.sync[0], static_cast<uint32_t>(G), &p.sync[3], p.spin_limit);
-
-  // ---------------------------------------------------------------- S --
-  for (int t = wave; t < T; t += kFWaves) {
-    const float* lg = p.logits + static_cast<size_t>(t) * E;
-    auto load = [&](int e) { return ld_dev(lg + e); };
-    int id;
-    float wt;
-    if (E <= 4 * kWave)
-      wave_topk<4>(E, k, load, &id, &wt);
-    else if (E <= 8 * kWave)
-      wave_topk<8>(E, k, load, &id, &wt);
-    else
-      wave_topk<16>(E, k, load, &id, &wt);
-    if (lane < k) {
-      s_ids[t * k + lane] = id;
-      s_w[t * k + lane] = wt;
-      if (blockIdx.x == 0) {
-        if (p.ids_out) p.ids_out[t * k + lane] = id;
-        if (p.w_out) p.w_out[t * k + lane] = wt;
-      }
-    }
-    if (lane == 0) s_gamma[t] = p.shared_gate ? ld_dev(&p.gamma[t]) : 0.0f;
+  // generation of this call: this block's own call count
+  if (threadIdx.x == 0) {
+    const uint32_t g = ld_dev(&p.gen[blockIdx.x]) + 1u;
+    st_dev(&p.gen[blockIdx.x], g);
+    s_gen = g;
   }
   __syncthreads();
+  const uint32_t gen = s_gen;
+
+  // ---------------------------------------------------------------- R --
+  {
+    // row r goes to block r % G, wave r / G: consecutive rows on different CUs
+    const int rows = E + (p.shared_gate ? 1 : 0);
+    for (int row = wave * G + blockIdx.x; row < rows; row += kFWaves * G) {
+      const bool gate_row = (row == E);
+      float4 wv[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (!gate_row) {
+          wv[c] = *reinterpret_cast<const float4*>(p.wr + static_cast<size_t>(row) * H +
+                                                   4 * lane + 4 * kWave * c);
+        } else {
+          const uint2 g2 =
+              *reinterpret_cast<const uint2*>(p.shared_gate + 4 * lane + 4 * kWave * c);
+          wv[c] = make_float4(bf16_bits_to_f32(g2.x & 0xFFFFu), bf16_bits_to_f32(g2.x >> 16),
+                              bf16_bits_to_f32(g2.y & 0xFFFFu), bf16_bits_to_f32(g2.y >> 16));
+        }
+      }
+      const double bias = (!gate_row && p.bias) ? static_cast<double>(p.bias[row]) : 0.0;
+      for (int t = 0; t < T; ++t) {
+        const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
+        uint2 xv[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          xv[c] = *reinterpret_cast<const uint2*>(xt + 4 * lane + 4 * kWave * c);
+        double acc = 0.0;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const uint2 xb = xv[c];
+          acc = fma(static_cast<double>(wv[c].x), static_cast<double>(bf16_bits_to_f32(xb.x & 0xFFFFu)), acc);
+          acc = fma(static_cast<double>(wv[c].y), static_cast<double>(bf16_bits_to_f32(xb.x >> 16)), acc);
+          acc = fma(static_cast<double>(wv[c].z), static_cast<double>(bf16_bits_to_f32(xb.y & 0xFFFFu)), acc);
+          acc = fma(static_cast<double>(wv[c].w), static_cast<double>(bf16_bits_to_f32(xb.y >> 16)), acc);
+        }
+        acc = wave_sum_f64(acc);
+        float v;
+        if (!gate_row) {
+          if (p.bias) acc += bias;
+          v = static_cast<float>(acc);
+        } else {
+          v = static_cast<float>(1.0 / (1.0 + exp(-acc)));
+        }
+        if (lane < kLogitCopies)
+          st_tag(&p.logits[(static_cast<size_t>(lane) * T + t) * E1 + row], v, gen);
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- S --
+  {
+    const uint64_t* lgc = p.logits + static_cast<size_t>(blockIdx.x % kLogitCopies) * T * E1;
+    const bool has_shared = p.shared_gate != nullptr;
+    if (T == 1) {
+      block_topk_one_token(lgc, E, k, gen, p.spin_limit, p.err, s_ck, s_ci, s_ids, s_w,
+                           &s_gamma[0], has_shared);
+    } else {
+      for (int t = wave; t < T; t += kFWaves) {
+        const uint64_t* lg = lgc + static_cast<size_t>(t) * E1;
+        if (E <= 4 * kWave)
+          wave_topk_tagged<4>(lg, E, k, gen, p.spin_limit, p.err, &s_ids[t * k], &s_w[t * k],
+                              &s_gamma[t], has_shared);
+        else if (E <= 8 * kWave)
+          wave_topk_tagged<8>(lg, E, k, gen, p.spin_limit, p.err, &s_ids[t * k], &s_w[t * k],
+                              &s_gamma[t], has_shared);
+        else
+          wave_topk_tagged<16>(lg, E, k, gen, p.spin_limit, p.err, &s_ids[t * k], &s_w[t * k],
+                               &s_gamma[t], has_shared);
+      }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
+        if (p.ids_out) p.ids_out[i] = s_ids[i];
+        if (p.w_out) p.w_out[i] = s_w[i];
+      }
+    }
+  }
 
   // ------------------------------------------------ D assignment (prefetch) --
   const int nch = p.routed.inter / 32;
   const int nch_s = p.shared.inter / 32;
+  const FastDiv fd_nch = make_fastdiv(nch);
+  const FastDiv fd_nrg = make_fastdiv(nrg);
   const int upg = k * nch + nch_s;  // down units per (token, row group)
   int bpg, g_first, g_step, sub;
   if (p.d_groups >= G) {
@@ -219,43 +417,59 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     g_step = p.d_groups;  // one group per block
     sub = blockIdx.x - g_first * bpg;
   }
-  const uint8_t* __restrict__ w2r = p.routed.w2;
-  const uint8_t* __restrict__ w2sr = p.routed.w2s;
 
-  auto down_ptrs = [&](int t, int v, int c, const uint8_t*& cp, const uint8_t*& sp, int& nch_u) {
-    const Unit2 u = unit2(p, v);
+  // Everything a down unit needs except h: code/scale addresses, its weight
+  // (routing weight x down global scale) and where its h chunk lives.  All
+  // wave-uniform except the row; computed and loaded at issue time.
+  struct DownUnit {
+    const uint8_t* cp;
+    const uint8_t* sp;
+    const uint64_t* hrow;  // 32 tagged h values of this unit
+    float scale;
+    bool valid;
+  };
+  auto down_unit = [&](int t, int v, int c) {
+    DownUnit d;
+    d.valid = v < upg;
+    const int vv = d.valid ? v : upg - 1;  // clamped: addresses stay in range
+    const Unit2 u = unit2(vv, k, fd_nch);
     const bool sh = (u.slot == k);
-    const int e = sh ? 0 : s_ids[t * k + u.slot];
-    nch_u = sh ? nch_s : nch;
-    const size_t rec = (static_cast<size_t>(e) * nch_u + u.chunk) * H + c;
-    cp = (sh ? p.shared.w2 : w2r) + rec * 16;
-    sp = (sh ? p.shared.w2s : w2sr) + rec * 2;
+    const int e = __builtin_amdgcn_readfirstlane(sh ? 0 : s_ids[t * k + u.slot]);
+    const int nu = sh ? nch_s : nch;
+    const size_t rec = (static_cast<size_t>(e) * nu + u.chunk) * H + c;
+    d.cp = (sh ? p.shared.w2 : p.routed.w2) + rec * 16;
+    d.sp = (sh ? p.shared.w2s : p.routed.w2s) + rec * 2;
+    d.hrow = p.h + (static_cast<size_t>(t) * p.nslots + u.slot) * p.Imax + 32 * u.chunk;
+    const float wslot = sh ? s_gamma[t] : s_w[t * k + u.slot];
+    d.scale = d.valid ? wslot * (sh ? p.shared.gsc : p.routed.gsc)[3 * e + 2] : 0.0f;
+    return d;
   };
 
   uint4 pq[kUD];
   uint32_t ps[kUD];
+  DownUnit pdu[kUD];
   const bool have_first = g_first < p.d_groups;
-  if (have_first) {
-    const int t = g_first / nrg;
+  // issues the loads of this wave's first down units (kept in registers until D)
+  auto prefetch_down = [&]() {
+    if (!have_first) return;
+    const int t = fdiv(g_first, fd_nrg);
     const int c = (g_first - t * nrg) * kWave + lane;
 #pragma unroll
     for (int i = 0; i < kUD; ++i) {
-      const int v = sub + bpg * (wave + kFWaves * i);
-      if (v < upg) {
-        const uint8_t *cp, *sp;
-        int nu;
-        down_ptrs(t, v, c, cp, sp, nu);
-        pq[i] = *reinterpret_cast<const uint4*>(cp);
-        ps[i] = *reinterpret_cast<const uint16_t*>(sp);
-      }
+      pdu[i] = down_unit(t, sub + bpg * (wave + kFWaves * i), c);
+      pq[i] = *reinterpret_cast<const uint4*>(pdu[i].cp);
+      ps[i] = *reinterpret_cast<const uint16_t*>(pdu[i].sp);
     }
-  }
+  };
 
   // ---------------------------------------------------------------- W --
   {
     const int group = lane / LPR, col = lane % LPR;
     const int NG = NW * GPW;
-    const int total = T * (k * p.routed.inter + p.shared.inter);
+    const int kI = k * p.routed.inter;
+    const FastDiv fd_ppt = make_fastdiv(kI + p.shared.inter);
+    const FastDiv fd_inter = make_fastdiv(p.routed.inter);
+    const int total = T * fd_ppt.d;
     const size_t row_bytes = static_cast<size_t>(H) / 2;
     const size_t srow_bytes = static_cast<size_t>(H) / 16;
     bf16x2 xr[CPL][16];
@@ -275,20 +489,26 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
       }
     };
     if (T == 1) load_x(0);
+    bool prefetched = false;
     for (int j0 = 0; (gw * GPW) + NG * j0 < total; j0 += kUW) {
       Unit13 un[kUW];
+      float g_gate[kUW], g_up[kUW];
       uint4 qg[kUW][CPL], qu[kUW][CPL];
       uint32_t sg[kUW][CPL], su[kUW][CPL];
 #pragma unroll
       for (int jj = 0; jj < kUW; ++jj) {
-        un[jj] = unit13(p, gw * GPW + group + NG * (j0 + jj), total);
+        un[jj] = unit13(gw * GPW + group + NG * (j0 + jj), total, k, kI, fd_ppt, fd_inter);
         const bool sh = (un[jj].slot == k);
         const int I = sh ? p.shared.inter : p.routed.inter;
-        const int e = sh ? 0 : s_ids[un[jj].t * k + un[jj].slot];
+        int e = sh ? 0 : s_ids[un[jj].t * k + un[jj].slot];
+        if (LPR == kWave) e = __builtin_amdgcn_readfirstlane(e);  // one unit per wave
         const uint8_t* __restrict__ codes =
             (sh ? p.shared.w13 : p.routed.w13) + static_cast<size_t>(e) * 2 * I * row_bytes;
         const uint8_t* __restrict__ scales =
             (sh ? p.shared.w13s : p.routed.w13s) + static_cast<size_t>(e) * 2 * I * srow_bytes;
+        const float* gsc = (sh ? p.shared.gsc : p.routed.gsc) + 3 * e;
+        g_gate[jj] = gsc[0];
+        g_up[jj] = gsc[1];
         const size_t rr = static_cast<size_t>(un[jj].r);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
@@ -299,6 +519,10 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
           su[jj][c] = *reinterpret_cast<const uint16_t*>(scales + (I + rr) * srow_bytes + 2 * j);
         }
       }
+      if (!prefetched) {  // behind the first gate|up loads, ahead of their use
+        prefetch_down();
+        prefetched = true;
+      }
 #pragma unroll
       for (int jj = 0; jj < kUW; ++jj) {
         if (T != 1) load_x(un[jj].t);
@@ -308,78 +532,51 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
           ag += chunk_dot_bf16(qg[jj][c], sg[jj][c], xr[c]);
           au += chunk_dot_bf16(qu[jj][c], su[jj][c], xr[c]);
         }
-        ag = group_sum<LPR>(ag);
-        au = group_sum<LPR>(au);
-        if (col == 0 && un[jj].valid) {
-          const bool sh = (un[jj].slot == k);
-          const int e = sh ? 0 : s_ids[un[jj].t * k + un[jj].slot];
-          const float* gsc = (sh ? p.shared.gsc : p.routed.gsc) + 3 * e;
-          const float hv = swiglu(p.act, ag * gsc[0], au * gsc[1], p.gate_max, p.up_absmax);
-          st_dev(&p.h[(static_cast<size_t>(un[jj].t) * p.nslots + un[jj].slot) * p.Imax + un[jj].r],
-                 hv);
+        ag = group_sum_last<LPR>(ag);
+        au = group_sum_last<LPR>(au);
+        if (col == LPR - 1 && un[jj].valid) {
+          const float hv = swiglu(p.act, ag * g_gate[jj], au * g_up[jj], p.gate_max, p.up_absmax);
+          st_tag(&p.h[(static_cast<size_t>(un[jj].t) * p.nslots + un[jj].slot) * p.Imax +
+                      un[jj].r],
+                 hv, gen);
         }
       }
     }
+    if (!prefetched) prefetch_down();
   }
-  grid_barrier(&p.sync[1], static_cast<uint32_t>(G), &p.sync[3], p.spin_limit);
 
   // ---------------------------------------------------------------- D --
   bool first = true;
   for (int g = g_first; g < p.d_groups; g += g_step) {
-    const int t = g / nrg;
+    const int t = fdiv(g, fd_nrg);
     const int rg = g - t * nrg;
     const int c = rg * kWave + lane;
     float acc = 0.0f;
     for (int i0 = 0; sub + bpg * (wave + kFWaves * i0) < upg; i0 += kUD) {
       uint4 q[kUD];
       uint32_t sc[kUD];
+      DownUnit du[kUD];
       if (first && i0 == 0) {
 #pragma unroll
         for (int ii = 0; ii < kUD; ++ii) {
           q[ii] = pq[ii];
           sc[ii] = ps[ii];
+          du[ii] = pdu[ii];
         }
       } else {
 #pragma unroll
         for (int ii = 0; ii < kUD; ++ii) {
-          const int v = sub + bpg * (wave + kFWaves * (i0 + ii));
-          if (v < upg) {
-            const uint8_t *cp, *sp;
-            int nu;
-            down_ptrs(t, v, c, cp, sp, nu);
-            q[ii] = *reinterpret_cast<const uint4*>(cp);
-            sc[ii] = *reinterpret_cast<const uint16_t*>(sp);
-          }
-        }
-      }
-      float hv[kUD][32];
-#pragma unroll
-      for (int ii = 0; ii < kUD; ++ii) {
-        const int v = sub + bpg * (wave + kFWaves * (i0 + ii));
-        if (v < upg) {
-          const Unit2 u = unit2(p, v);
-          const float* hrow = p.h + (static_cast<size_t>(t) * p.nslots + u.slot) * p.Imax;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const float4 f =
-                ld_dev_x4_uniform(hrow, static_cast<uint32_t>((32 * u.chunk + 4 * m) * 4));
-            hv[ii][4 * m + 0] = f.x;
-            hv[ii][4 * m + 1] = f.y;
-            hv[ii][4 * m + 2] = f.z;
-            hv[ii][4 * m + 3] = f.w;
-          }
+          du[ii] = down_unit(t, sub + bpg * (wave + kFWaves * (i0 + ii)), c);
+          q[ii] = *reinterpret_cast<const uint4*>(du[ii].cp);
+          sc[ii] = *reinterpret_cast<const uint16_t*>(du[ii].sp);
         }
       }
 #pragma unroll
       for (int ii = 0; ii < kUD; ++ii) {
-        const int v = sub + bpg * (wave + kFWaves * (i0 + ii));
-        if (v < upg) {
-          const Unit2 u = unit2(p, v);
-          const bool sh = (u.slot == k);
-          const int e = sh ? 0 : s_ids[t * k + u.slot];
-          const float wslot = sh ? s_gamma[t] : s_w[t * k + u.slot];
-          const float gd = (sh ? p.shared.gsc : p.routed.gsc)[3 * e + 2];
-          acc = fmaf(chunk_dot_f32(q[ii], sc[ii], hv[ii]), wslot * gd, acc);
+        if (du[ii].valid) {
+          float hv[32];
+          poll_h_chunk(du[ii].hrow, gen, hv, p.spin_limit, p.err);
+          acc = fmaf(chunk_dot_f32(q[ii], sc[ii], hv), du[ii].scale, acc);
         }
       }
     }
@@ -394,33 +591,38 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
       if (bpg == 1) {
         *yout = f32_to_bf16_bits(o);
       } else {
-        float* part = p.part + (static_cast<size_t>(g) * bpg) * kWave;
-        st_dev(&part[sub * kWave + lane], o);
-        wait_mem();
-        uint32_t old = 0;
-        if (lane == 0) old = add_dev(&p.cnt[g], 1u);
-        old = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(old)));
-        if (old == static_cast<uint32_t>(bpg - 1)) {
-          float ysum = 0.0f;
-          for (int s2 = 0; s2 < bpg; ++s2) ysum += ld_dev(&part[s2 * kWave + lane]);
+        uint64_t* part = p.part + static_cast<size_t>(g) * bpg * kWave;
+        st_tag(&part[sub * kWave + lane], o, gen);
+        if (sub == 0) {
+          // the group's combining block: every partial, in block order
+          float ysum = o;
+          for (int s0 = 1; s0 < bpg; s0 += 8) {
+            uint64_t pv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pv[i] = ld_tag(&part[min(s0 + i, bpg - 1) * kWave + lane]);
+            for (int spins = 0;; ++spins) {
+              bool ok = true;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) ok = ok && tag_is(pv[i], gen);
+              if (__ballot(!ok) == 0) break;
+              if (spins >= p.spin_limit) {
+                st_dev(p.err, 1u);
+                break;
+              }
+              __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+              for (int i = 0; i < 8; ++i)
+                if (!tag_is(pv[i], gen)) pv[i] = ld_tag(&part[min(s0 + i, bpg - 1) * kWave + lane]);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (s0 + i < bpg) ysum += tag_value(pv[i]);
+          }
           *yout = f32_to_bf16_bits(ysum);
-          if (lane == 0) st_dev(&p.cnt[g], 0u);
         }
       }
     }
     __syncthreads();
-  }
-
-  // -------------------------------------------------------------- exit --
-  wait_mem();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = add_dev(&p.sync[2], 1u);
-    if (old == static_cast<uint32_t>(G - 1)) {
-      st_dev(&p.sync[0], 0u);
-      st_dev(&p.sync[1], 0u);
-      st_dev(&p.sync[2], 0u);
-    }
   }
 }
 

@@ -55,6 +55,23 @@ __device__ __forceinline__ float dequant_one(float code_value, float scale, floa
   return (code_value * scale) * g;
 }
 
+// ------------------------------------------------------- small divisions --
+//
+// n / d for 0 <= n < 2^24 and d >= 1 through an fp32 reciprocal: the estimate is
+// within one of the quotient, and one correction step makes it exact.
+struct FastDiv {
+  int d;
+  float inv;
+};
+__host__ __device__ inline FastDiv make_fastdiv(int d) { return FastDiv{d, 1.0f / static_cast<float>(d)}; }
+__device__ __forceinline__ int fdiv(int n, FastDiv f) {
+  int q = static_cast<int>(static_cast<float>(n) * f.inv);
+  const int r = n - q * f.d;
+  q += (r >= f.d) ? 1 : 0;
+  q -= (r < 0) ? 1 : 0;
+  return q;
+}
+
 // ------------------------------------------------------------ bf16 helpers --
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
@@ -85,6 +102,27 @@ template <int Width>
 __device__ __forceinline__ double group_sum(double v) {
 #pragma unroll
   for (int off = Width / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Sum over aligned groups of `Width` lanes (8, 16, 32 or 64) with DPP row shifts
+// and broadcasts; the sum lands in the LAST lane of each group (other lanes hold
+// partial sums).  Fixed order.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ float dpp_shift_f32(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, RowMask, 0xf, false));
+}
+
+template <int Width>
+__device__ __forceinline__ float group_sum_last(float v) {
+  static_assert(Width == 8 || Width == 16 || Width == 32 || Width == 64, "group width");
+  v += dpp_shift_f32<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_shift_f32<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_shift_f32<0x114, 0xf>(v);  // row_shr:4  -> lane 8j+7 holds its 8-lane group
+  if (Width >= 16) v += dpp_shift_f32<0x118, 0xf>(v);  // row_shr:8 -> lane 15 of each row
+  if (Width >= 32) v += dpp_shift_f32<0x142, 0xa>(v);  // row_bcast:15 -> lanes 31, 63
+  if (Width >= 64) v += dpp_shift_f32<0x143, 0xc>(v);  // row_bcast:31 -> lane 63
   return v;
 }
 
@@ -185,6 +223,31 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
+// Sum of a double over the 64 lanes of a wave (fixed DPP tree), returned to
+// every lane.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ double dpp_shift_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(u), Ctrl, RowMask, 0xf, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), Ctrl, RowMask, 0xf, false));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_shift_f64<0x111, 0xf>(v);
+  v += dpp_shift_f64<0x112, 0xf>(v);
+  v += dpp_shift_f64<0x114, 0xf>(v);
+  v += dpp_shift_f64<0x118, 0xf>(v);
+  v += dpp_shift_f64<0x142, 0xa>(v);
+  v += dpp_shift_f64<0x143, 0xc>(v);
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 63));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), 63));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Lane `src` (wave-uniform) of a double, broadcast through scalar registers.
 __device__ __forceinline__ double readlane_f64(double v, int src) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
@@ -218,54 +281,45 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 
 // Top-k of one token's E (<= 64 * SLOTS) logits by one wave: experts ordered by
 // (logit descending, index ascending), then the softmax of the selected logits
-// (fp64 exp, stored as fp32).  Lane l holds experts l, l + 64, ...  Returns the
-// rank-i expert and weight in lane i (i < k); other lanes return -1 / 0.
-template <int SLOTS, class Load>
-__device__ __forceinline__ void wave_topk(int E, int k, Load load_logit, int* out_id,
-                                          float* out_w) {
+// (fp64 exp, stored as fp32).  Lane l holds experts l, l + 64, ... in slots
+// 0, 1, ..., so scanning the slots in order and taking the lowest set lane of
+// the first non-empty ballot finds the lowest index among equal keys.  Returns
+// the rank-i expert and weight in lane i (i < k); other lanes return -1 / 0.
+template <int SLOTS>
+__device__ __forceinline__ void wave_topk_vals(int E, int k, const float* lv, int* out_id,
+                                               float* out_w) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t key[SLOTS];
 #pragma unroll
-  for (int m = 0; m < SLOTS; ++m) {
-    const int e = lane + kWave * m;
-    key[m] = (e < E) ? rank_key(load_logit(e)) : 0u;
-  }
-  // the lane's best untaken candidate (lowest slot among equal keys)
-  auto local_best = [&](uint32_t& bk, uint32_t& be) {
-    bk = 0u;
-    be = 0xFFFFFFFFu;
+  for (int m = 0; m < SLOTS; ++m) key[m] = (lane + kWave * m < E) ? rank_key(lv[m]) : 0u;
+  auto local_max = [&]() {
+    uint32_t mx = key[0];
 #pragma unroll
-    for (int m = SLOTS - 1; m >= 0; --m) {
-      if (key[m] >= bk && key[m] != 0u) {
-        bk = key[m];
-        be = static_cast<uint32_t>(lane + kWave * m);
-      }
-    }
+    for (int m = 1; m < SLOTS; ++m) mx = key[m] > mx ? key[m] : mx;
+    return mx;
   };
-  uint32_t lk, le;
-  local_best(lk, le);
+  uint32_t lmax = local_max();
   int my_id = -1;
   uint32_t my_key = 0u;
   for (int i = 0; i < k; ++i) {
-    const uint32_t K = wave_max_u32(lk);
-    const uint64_t holders = __ballot(lk == K);
-    uint32_t win;
-    if (__popcll(holders) == 1) {
-      const int wl = __ffsll(static_cast<unsigned long long>(holders)) - 1;
-      win = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(le), wl));
-    } else {
-      win = wave_min_u32(lk == K ? le : 0xFFFFFFFFu);
+    const uint32_t K = wave_max_u32(lmax);
+    int win = -1;
+#pragma unroll
+    for (int m = 0; m < SLOTS; ++m) {
+      if (win < 0) {
+        const uint64_t b = __ballot(key[m] == K);
+        if (b != 0) win = kWave * m + __ffsll(static_cast<unsigned long long>(b)) - 1;
+      }
     }
     if (lane == i) {
-      my_id = static_cast<int>(win);
+      my_id = win;
       my_key = K;
     }
-    if (static_cast<int>(win & (kWave - 1)) == lane) {
-      const int wm = static_cast<int>(win) / kWave;
+    if ((win & (kWave - 1)) == lane) {
 #pragma unroll
       for (int m = 0; m < SLOTS; ++m)
-        if (m == wm) key[m] = 0u;
-      local_best(lk, le);
+        if (m == (win >> 6)) key[m] = 0u;
+      lmax = local_max();
     }
   }
   // softmax over the selected logits, in fp64, summed in rank order
@@ -276,6 +330,21 @@ __device__ __forceinline__ void wave_topk(int E, int k, Load load_logit, int* ou
   for (int i = 0; i < k; ++i) sum += readlane_f64(d, i);
   *out_id = my_id;
   *out_w = (lane < k) ? static_cast<float>(d / sum) : 0.0f;
+}
+
+// Same, loading the logits through `load_logit(e)` (every load issued first,
+// indices clamped into range).
+template <int SLOTS, class Load>
+__device__ __forceinline__ void wave_topk(int E, int k, Load load_logit, int* out_id,
+                                          float* out_w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float lv[SLOTS];
+#pragma unroll
+  for (int m = 0; m < SLOTS; ++m) {
+    const int e = lane + kWave * m;
+    lv[m] = load_logit(e < E ? e : E - 1);
+  }
+  wave_topk_vals<SLOTS>(E, k, lv, out_id, out_w);
 }
 
 // ------------------------------------------------------------- activation --

@@ -64,7 +64,13 @@ struct DownParams {
   uint16_t* y;          // bf16 [T][H]
 };
 
-// The whole decode layer in one persistent launch (one block per CU).
+// The whole decode layer in one persistent launch (one block per CU).  Values
+// handed from one block to another are "tagged": an 8-byte word holding the fp32
+// value in its low half and the call's generation number in its high half,
+// written and read with single 8-byte device-coherent accesses.
+constexpr int kLogitCopies = 16;    // replicas of the router logits (spreads the reads)
+constexpr int kMaxFusedGrid = 1024;
+
 struct FusedParams {
   const uint16_t* x;            // bf16 [T][H]
   const float* wr;              // f32 [E][H]
@@ -77,15 +83,14 @@ struct FusedParams {
   uint16_t* y;                  // bf16 [T][H]
   int32_t* ids_out;             // optional i32 [T][k]
   float* w_out;                 // optional f32 [T][k]
-  float* logits;                // f32 [T][E]
-  float* gamma;                 // f32 [T]
-  float* h;                     // f32 [T][nslots][Imax]
-  float* part;                  // f32 [d_groups][blocks_per_group][64]
-  uint32_t* sync;               // [0] barrier 1, [1] barrier 2, [2] exits, [3] error flag
-  uint32_t* cnt;                // u32 [d_groups] combine counters
+  uint64_t* logits;             // tagged [kLogitCopies][T][E + 1] (column E: shared gate)
+  uint64_t* h;                  // tagged [T][nslots][Imax]
+  uint64_t* part;               // tagged [d_groups][blocks_per_group][64]
+  uint32_t* gen;                // per-block call counters [grid]
+  uint32_t* err;                // set when a poll gives up (the result is then invalid)
   int d_groups;                 // T * H / 64 (token, row group) pairs of the down GEMV
   int blocks_per_group;         // blocks sharing one group when d_groups < grid
-  int spin_limit;               // barrier polls before giving up (error flag)
+  int spin_limit;               // polls of one value before giving up
 };
 
 // Launchers: return the launch status (hipGetLastError after the launch).

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_logits_kernel(RouteP
         acc = fma(static_cast<double>(wv[c].z), static_cast<double>(bf16_bits_to_f32(xb.y & 0xFFFFu)), acc);
         acc = fma(static_cast<double>(wv[c].w), static_cast<double>(bf16_bits_to_f32(xb.y >> 16)), acc);
       }
-      acc = group_sum<kWave>(acc);
+      acc = wave_sum_f64(acc);
       if (lane == 0) {
         if (p.bias) acc += b;
         st_dev(&p.logits[static_cast<size_t>(t) * p.E + row], static_cast<float>(acc));
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_logits_kernel(RouteP
         acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].y >> 16)),
                   static_cast<double>(bf16_bits_to_f32(xb.y >> 16)), acc);
       }
-      acc = group_sum<kWave>(acc);
+      acc = wave_sum_f64(acc);
       if (lane == 0) p.gamma[t] = static_cast<float>(1.0 / (1.0 + exp(-acc)));
     }
   }
