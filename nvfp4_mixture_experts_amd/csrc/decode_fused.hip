@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
                               bf16_bits_to_f32(g2.y & 0xFFFFu), bf16_bits_to_f32(g2.y >> 16));
         }
       }
-      const double bias = (!gate_row && p.bias) ? static_cast<double>(p.bias[row]) : 0.0;
+      const double bias = (!gate_row && p.bias) ? static_cast<double>(ld_vmem_f32(p.bias, row)) : 0.0;
       for (int t = 0; t < T; ++t) {
         const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
         uint2 xv[NC];
@@ -425,7 +425,10 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     const uint8_t* cp;
     const uint8_t* sp;
     const uint64_t* hrow;  // 32 tagged h values of this unit
-    float scale;
+    float wslot;           // routing weight (or shared gate) of the unit's slot
+    float gdown;           // down global scale of the unit's expert (multiplied at use:
+                           // using a load result at issue time would wait for every
+                           // load issued before it)
     bool valid;
   };
   auto down_unit = [&](int t, int v, int c) {
@@ -440,8 +443,8 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     d.cp = (sh ? p.shared.w2 : p.routed.w2) + rec * 16;
     d.sp = (sh ? p.shared.w2s : p.routed.w2s) + rec * 2;
     d.hrow = p.h + (static_cast<size_t>(t) * p.nslots + u.slot) * p.Imax + 32 * u.chunk;
-    const float wslot = sh ? s_gamma[t] : s_w[t * k + u.slot];
-    d.scale = d.valid ? wslot * (sh ? p.shared.gsc : p.routed.gsc)[3 * e + 2] : 0.0f;
+    d.wslot = d.valid ? (sh ? s_gamma[t] : s_w[t * k + u.slot]) : 0.0f;
+    d.gdown = ld_vmem_f32(sh ? p.shared.gsc : p.routed.gsc, 3 * e + 2);
     return d;
   };
 
@@ -506,9 +509,9 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
             (sh ? p.shared.w13 : p.routed.w13) + static_cast<size_t>(e) * 2 * I * row_bytes;
         const uint8_t* __restrict__ scales =
             (sh ? p.shared.w13s : p.routed.w13s) + static_cast<size_t>(e) * 2 * I * srow_bytes;
-        const float* gsc = (sh ? p.shared.gsc : p.routed.gsc) + 3 * e;
-        g_gate[jj] = gsc[0];
-        g_up[jj] = gsc[1];
+        const float* gsc = sh ? p.shared.gsc : p.routed.gsc;
+        g_gate[jj] = ld_vmem_f32(gsc, 3 * e + 0);
+        g_up[jj] = ld_vmem_f32(gsc, 3 * e + 1);
         const size_t rr = static_cast<size_t>(un[jj].r);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         if (du[ii].valid) {
           float hv[32];
           poll_h_chunk(du[ii].hrow, gen, hv, p.spin_limit, p.err);
-          acc = fmaf(chunk_dot_f32(q[ii], sc[ii], hv), du[ii].scale, acc);
+          acc = fmaf(chunk_dot_f32(q[ii], sc[ii], hv), du[ii].wslot * du[ii].gdown, acc);
         }
       }
     }

@@ -347,6 +347,18 @@ __device__ __forceinline__ void wave_topk(int E, int k, Load load_logit, int* ou
   wave_topk_vals<SLOTS>(E, k, lv, out_id, out_w);
 }
 
+// ------------------------------------------------------ vector-memory loads --
+//
+// base[index] through a buffer load (the vector memory path).  A wave-uniform
+// fp32 load would otherwise be issued on the scalar path, whose completion
+// counter is shared with LDS reads: every later LDS read would then wait for it.
+__device__ __forceinline__ float ld_vmem_f32(const float* base, int index) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(base), static_cast<short>(0), 0x7fffffff, 0x00020000);
+  return __uint_as_float(
+      static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * index, 0, 0)));
+}
+
 // ------------------------------------------------------------- activation --
 
 // silu(z) = z / (1 + exp(-z)); for very negative z, exp(-z) overflows to +inf and
