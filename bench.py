@@ -14,6 +14,7 @@ Prints one JSON line (rank 0, N = 1).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -45,6 +46,44 @@ def algorithmic_bytes(w, ids: np.ndarray) -> int:
         b += (2 * Is * H) // 2 + (2 * Is * H) // 16 + (H * Is) // 2 + (H * Is) // 16 + 12
         b += H * 2                             # shared gate vector
     return b
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+DECODE_KERNEL = "moe_decode_fused_kernel"
+DECODE_SOURCES = ("nvfp4_mixture_experts_amd/csrc/decode_fused.hip",
+                  "nvfp4_mixture_experts_amd/csrc/ftmoe_device.hpp",
+                  "nvfp4_mixture_experts_amd/csrc/ftmoe_kernels.hpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3 --pmc
+    summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a plain copy of known size),
+    or None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{DECODE_KERNEL}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                kv[k.strip()] = v.strip().strip("`")
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        fetch = float(kv["fetch_bytes_per_launch"])
+        write = float(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+    return {"bytes": fetch + write, "fetch": fetch, "write": write}
 
 
 def cpu_baseline(w, seconds: float = 12.0) -> dict:
@@ -79,6 +118,9 @@ def main() -> int:
                     help="distinct layer instances to cycle (0 = enough to exceed 4x the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one plain elementwise copy (negation) of this many "
+                         "MiB, as the known-size reference for HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -169,10 +211,20 @@ def main() -> int:
     ms_per_step = ms_total / steps
     calls_per_s = 1000.0 / ms_per_step
 
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 18
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     ids_np = ids_all.cpu().numpy()
     bytes_per_call = float(np.mean([algorithmic_bytes(w, ids_np[l]) for l in range(L)]))
     gbps = bytes_per_call / (ms_per_step * 1e-3) / 1e9
     touched = bytes_per_call * L
+    traffic = measured_traffic(w.name)
 
     out = {
         "metric": METRIC,
@@ -193,9 +245,12 @@ def main() -> int:
                    "bytes_touched_per_cycle": int(touched)},
         "achieved_gbps": round(gbps, 1),
         "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"kernel": "moe_decode_fused_kernel", "bound": "hbm",
+        "roofline": {"kernel": DECODE_KERNEL, "bound": "hbm",
                      "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else int(round(traffic["bytes"])),
+                     "traffic_fetch": None if traffic is None else int(round(traffic["fetch"])),
+                     "traffic_write": None if traffic is None else int(round(traffic["write"])),
                      "algorithmic_bytes_per_launch": int(round(bytes_per_call))},
         "wall_s_timed": round(wall, 3),
         "launch": "hip graph of one call per layer instance, replayed",

@@ -34,7 +34,6 @@ ft_status hip_fail(hipError_t e, const char* what) {
   return fail(FT_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int kMaxExperts = 1024;
 constexpr int kMaxDevices = 64;
 constexpr int kSpinLimit = 1 << 20;  // grid-barrier polls (~1 s) before the kernel gives up
 
@@ -112,11 +111,12 @@ Bank to_bank(const ft_nvfp4_experts* b, int inter) {
 }
 
 // Workspace regions.  The route counter sits at offset 0 for every path and is
-// reset by the kernel that uses it; the down-projection counters are cleared by
-// the first kernel of each call, so a workspace may be shared between paths
-// and token counts once it has been zero-filled.
+// reset by the kernel that uses it, so a route workspace may be reused across
+// token counts once it has been zero-filled.
 struct Layout {
-  size_t sync, gen, cnt_down, logits, gamma, ids, w, h, part, total;
+  size_t sync, gen, logits, h, part;                               // route / decode
+  size_t gamma, blk_count, offset, units, nunits, sorted, hhi, hlo, out;  // prefill
+  size_t total;
 };
 
 constexpr int kRouteCounterWord = 0;  // in the sync region
@@ -131,23 +131,33 @@ Layout layout(const ft_moe_desc& d, int64_t T, int path) {
     return o;
   };
   const size_t t = static_cast<size_t>(T);
-  const size_t nrg = static_cast<size_t>(d.hidden / kRowGroup);
   const size_t k = static_cast<size_t>(d.top_k);
   const size_t E = static_cast<size_t>(d.num_experts);
+  const size_t H = static_cast<size_t>(d.hidden);
   const size_t imax = static_cast<size_t>(d.inter > d.shared_inter ? d.inter : d.shared_inter);
   const size_t nslots = k + (d.shared_inter > 0 ? 1 : 0);
-  const bool fused = (path == 1);
   L.sync = take(256);  // route counter, error word
-  L.gen = take(fused ? static_cast<size_t>(kMaxFusedGrid) * 4 : 0);
-  L.cnt_down = take(path == 2 ? t * nrg * 4 : 0);
-  L.logits = take(path == 0 ? t * E * 4
-                            : (fused ? static_cast<size_t>(kLogitCopies) * t * (E + 1) * 8 : 0));
-  L.gamma = take(path == 2 ? t * 4 : 0);
-  L.ids = take(0);
-  L.w = take(0);
-  L.h = take(fused ? t * nslots * imax * 8 : (path == 2 ? t * (k + 1) * imax * 4 : 0));
-  L.part = take(fused ? static_cast<size_t>(kMaxFusedGrid) * kRowGroup * 8
-                      : (path == 2 ? t * nrg * nslots * kRowGroup * 4 : 0));
+  if (path == 0) {
+    L.logits = take(t * E * 4);
+  } else if (path == 1) {
+    L.gen = take(static_cast<size_t>(kMaxFusedGrid) * 4);
+    L.logits = take(static_cast<size_t>(kLogitCopies) * t * (E + 1) * 8);
+    L.h = take(t * nslots * imax * 8);
+    L.part = take(static_cast<size_t>(kMaxFusedGrid) * kRowGroup * 8);
+  } else {
+    const int Ti = static_cast<int>(T), ki = d.top_k;
+    const size_t P = t * k;
+    L.gamma = take(t * 4);
+    L.blk_count = take(static_cast<size_t>(prefill_group_blocks(Ti, ki)) * E * 4);
+    L.offset = take(E * 4);
+    L.units = take(static_cast<size_t>(prefill_max_units(d.num_experts, Ti, ki,
+                                                         d.shared_inter > 0)) * sizeof(PfUnit));
+    L.nunits = take(4);
+    L.sorted = take(P * 4);
+    L.hhi = take((P + t) * imax * 2);
+    L.hlo = take((P + t) * imax * 2);
+    L.out = take(t * nslots * H * 4);
+  }
   L.total = off;
   return L;
 }
@@ -181,50 +191,6 @@ ft_status check_layer_args(const ft_moe_desc* desc, const uint16_t* x,
     if (!shared_gate) return fail(FT_EINVAL, "shared_gate is NULL with a shared expert");
     if (!aligned16(shared_gate)) return fail(FT_EINVAL, "shared_gate must be 16-byte aligned");
   }
-  return FT_OK;
-}
-
-// gate|up then down/combine, given routes in ids/w and gamma in the workspace.
-ft_status run_experts(const ft_moe_desc* desc, int T, const uint16_t* x,
-                             const int32_t* ids, const float* w, const ft_nvfp4_experts* routed,
-                             const ft_nvfp4_experts* shared, uint16_t* y, void* ws,
-                             const Layout& L, hipStream_t s) {
-  const bool has_shared = desc->shared_inter > 0;
-  GateUpParams g{};
-  g.x = x;
-  g.T = T;
-  g.H = desc->hidden;
-  g.k = desc->top_k;
-  g.E = desc->num_experts;
-  g.routed = to_bank(routed, desc->inter);
-  g.shared = has_shared ? to_bank(shared, desc->shared_inter) : Bank{};
-  g.ids = ids;
-  g.h = at<float>(ws, L.h);
-  g.Imax = desc->inter > desc->shared_inter ? desc->inter : desc->shared_inter;
-  g.act = desc->act;
-  g.gate_max = desc->gate_max;
-  g.up_absmax = desc->up_absmax;
-  hipError_t e = launch_gateup(g, s);
-  if (e != hipSuccess) return hip_fail(e, "gate|up kernel");
-
-  DownParams d{};
-  d.T = T;
-  d.H = desc->hidden;
-  d.k = desc->top_k;
-  d.nslots = desc->top_k + (has_shared ? 1 : 0);
-  d.E = desc->num_experts;
-  d.routed = g.routed;
-  d.shared = g.shared;
-  d.ids = ids;
-  d.w = w;
-  d.gamma = has_shared ? at<float>(ws, L.gamma) : nullptr;
-  d.h = g.h;
-  d.Imax = g.Imax;
-  d.part = at<float>(ws, L.part);
-  d.cnt = at<uint32_t>(ws, L.cnt_down);
-  d.y = y;
-  e = launch_down(d, s);
-  if (e != hipSuccess) return hip_fail(e, "down kernel");
   return FT_OK;
 }
 
@@ -408,24 +374,48 @@ ft_status ft_moe_nvfp4_prefill(const ft_moe_desc* desc, int64_t tokens, const ui
   if (tokens == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool has_shared = desc->shared_inter > 0;
-  {
-    // shared expert gate (when there is one) and the clearing of this call's counters
+  const int T = static_cast<int>(tokens);
+  if (has_shared) {
+    // sigmoid of the shared expert's gate for every token
     RouteParams p{};
     p.x = x;
-    p.shared_gate = has_shared ? shared_gate : nullptr;
-    p.T = static_cast<int>(tokens);
+    p.shared_gate = shared_gate;
+    p.T = T;
     p.E = 0;
     p.H = desc->hidden;
     p.k = desc->top_k;
     p.gamma = at<float>(workspace, L.gamma);
-    p.zero = at<uint32_t>(workspace, L.cnt_down);
-    p.nzero = static_cast<int>(tokens) * (desc->hidden / kRowGroup);
     hipError_t e = launch_route(p, false, s);
     if (e != hipSuccess) return hip_fail(e, "shared gate kernel");
   }
-  st = run_experts(desc, static_cast<int>(tokens), x, topk_ids, topk_w, routed, shared, y,
-                   workspace, L, s);
-  if (st != FT_OK) return st;
+  PrefillParams p{};
+  p.x = x;
+  p.T = T;
+  p.H = desc->hidden;
+  p.k = desc->top_k;
+  p.E = desc->num_experts;
+  p.P = T * desc->top_k;
+  p.routed = to_bank(routed, desc->inter);
+  p.shared = has_shared ? to_bank(shared, desc->shared_inter) : Bank{};
+  p.ids = topk_ids;
+  p.w = topk_w;
+  p.gamma = has_shared ? at<float>(workspace, L.gamma) : nullptr;
+  p.blk_count = at<int32_t>(workspace, L.blk_count);
+  p.offset = at<int32_t>(workspace, L.offset);
+  p.sorted = at<int32_t>(workspace, L.sorted);
+  p.units = at<PfUnit>(workspace, L.units);
+  p.nunits = at<int32_t>(workspace, L.nunits);
+  p.Imax = desc->inter > desc->shared_inter ? desc->inter : desc->shared_inter;
+  p.hhi = at<uint16_t>(workspace, L.hhi);
+  p.hlo = at<uint16_t>(workspace, L.hlo);
+  p.out = at<float>(workspace, L.out);
+  p.nslots = desc->top_k + (has_shared ? 1 : 0);
+  p.act = desc->act;
+  p.gate_max = desc->gate_max;
+  p.up_absmax = desc->up_absmax;
+  p.y = y;
+  hipError_t e = launch_prefill(p, s);
+  if (e != hipSuccess) return hip_fail(e, "prefill kernels");
   return ok();
 }
 

@@ -657,4 +657,14 @@ hipError_t launch_decode_fused(const FusedParams& p, int grid, hipStream_t s) {
 
 int fused_block_threads() { return kFWaves * kWave; }
 
+// The widest power of two <= 64 lanes per row that divides the H/32 chunks of a
+// gate|up row, and the chunks each lane then owns.
+void gateup_geometry(int H, int* lpr, int* cpl) {
+  const int chunks = H / 32;
+  int l = 64;
+  while (l > 8 && chunks % l != 0) l >>= 1;
+  *lpr = (chunks % l == 0) ? l : 0;
+  *cpl = (*lpr > 0) ? chunks / l : 0;
+}
+
 }  // namespace ftmoe

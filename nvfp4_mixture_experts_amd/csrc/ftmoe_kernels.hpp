@@ -36,34 +36,6 @@ struct RouteParams {
   int nzero;
 };
 
-// Gate|up GEMV with in-register dequantisation and (clamped) SwiGLU.
-struct GateUpParams {
-  const uint16_t* x;  // bf16 [T][H]
-  int T, H, k;
-  int E;              // routed experts: an id outside [0, E) yields NaN, never a load
-  Bank routed, shared;
-  const int32_t* ids; // i32 [T][k]
-  float* h;           // f32 [T][k+1][Imax]
-  int Imax;
-  int act;
-  float gate_max, up_absmax;
-};
-
-// Down GEMV, weighted combine over the selected experts and the shared expert.
-struct DownParams {
-  int T, H, k, nslots;  // nslots = k (+1 with a shared expert)
-  int E;                // routed experts: an id outside [0, E) yields NaN, never a load
-  Bank routed, shared;
-  const int32_t* ids;   // i32 [T][k]
-  const float* w;       // f32 [T][k]
-  const float* gamma;   // f32 [T] or null
-  const float* h;       // f32 [T][k+1][Imax]
-  int Imax;
-  float* part;          // f32 [T][H/64][nslots][64] per-slot partial outputs
-  uint32_t* cnt;        // u32 [T][H/64] last-arriver counters
-  uint16_t* y;          // bf16 [T][H]
-};
-
 // The whole decode layer in one persistent launch (one block per CU).  Values
 // handed from one block to another are "tagged": an 8-byte word holding the fp32
 // value in its low half and the call's generation number in its high half,
@@ -93,14 +65,53 @@ struct FusedParams {
   int spin_limit;               // polls of one value before giving up
 };
 
+// Many-token path (grouped GEMMs over the routed (token, slot) pairs).
+constexpr int kMaxExperts = 1024;   // experts per bank supported by the grouping kernels
+constexpr int kGroupPairs = 1024;   // pairs per grouping block
+constexpr int kPfUnitTokens = 256;  // tokens per work unit (4 waves x 64)
+
+struct PfUnit {
+  int bank;    // 0 routed, 1 shared
+  int expert;  // routed expert id (0 for the shared bank)
+  int start;   // routed: first position in `sorted`; shared: first token
+  int count;   // 1 .. kPfUnitTokens
+};
+
+struct PrefillParams {
+  const uint16_t* x;       // bf16 [T][H]
+  int T, H, k, E, P;       // P = T * k routed pairs; pair = t * k + slot
+  Bank routed, shared;
+  const int32_t* ids;      // i32 [T][k]
+  const float* w;          // f32 [T][k]
+  const float* gamma;      // f32 [T] shared-expert gate, or null
+  int32_t* blk_count;      // i32 [grouping blocks][E]
+  int32_t* offset;         // i32 [E] first sorted position of each expert
+  int32_t* sorted;         // i32 [P] pairs grouped by expert, ascending within one
+  PfUnit* units;           // [max units]
+  int32_t* nunits;         // number of valid units
+  int Imax;                // row stride of hhi / hlo
+  uint16_t* hhi;           // bf16 [P + T][Imax] h rounded to bf16 ...
+  uint16_t* hlo;           // bf16 [P + T][Imax] ... and the rounded remainder
+  float* out;              // f32 [T][nslots][H] weighted expert outputs
+  int nslots;              // k (+1 with a shared expert)
+  int act;
+  float gate_max, up_absmax;
+  int ntiles1, ntiles2;    // column tiles per unit of the two GEMMs (set by the launcher)
+  uint16_t* y;             // bf16 [T][H]
+};
+
+int prefill_max_units(int E, int T, int k, bool shared);
+int prefill_group_blocks(int T, int k);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+
 // Launchers: return the launch status (hipGetLastError after the launch).
 hipError_t launch_decode_fused(const FusedParams& p, int grid, hipStream_t s);
 int fused_block_threads();
 hipError_t launch_route(const RouteParams& p, bool fuse_topk, hipStream_t s);
 hipError_t launch_topk(const RouteParams& p, hipStream_t s);
-hipError_t launch_gateup(const GateUpParams& p, hipStream_t s);
-void gateup_geometry(int H, int* lpr, int* cpl);  // supported when lpr > 0 and 1 <= cpl <= 4
-hipError_t launch_down(const DownParams& p, hipStream_t s);
+// Lanes per row and chunks per lane of the decode gate|up GEMV for hidden size H
+// (supported when lpr > 0 and 1 <= cpl <= 4).
+void gateup_geometry(int H, int* lpr, int* cpl);
 hipError_t launch_repack_w2(int H, int I, int n, const uint8_t* w2, const uint8_t* w2s,
                             uint8_t* out_w2, uint8_t* out_w2s, hipStream_t s);
 hipError_t launch_dequant(int H, int I, const Bank& b, int expert, int tensor, int out_dtype,

@@ -1,0 +1,526 @@
+// prefill.hip -- the many-token path: routed (token, slot) pairs grouped by
+// expert, then two bf16 MFMA grouped GEMMs per expert and a combine.
+//
+// FreeToken fork PR #84 (page 1), the bullet on #578: NVFP4 prefill experts are
+// dequantised and run as dense products; 1Cat-vLLM PR #525 (page 3) runs NVFP4
+// experts as weight-only 4-bit GEMMs with 16-bit activations.  Here the dense
+// product is a gfx950 MFMA (v_mfma_f32_16x16x32_bf16).  Every e2m1 x e4m3
+// product has at most 6 significant bits, so the dequantised tile values
+// code * scale are exact in bf16; the fp32 global scale multiplies the fp32
+// accumulator instead.
+//
+//  1. pf_hist_kernel     per block of 1024 pairs, a histogram of expert ids
+//  2. pf_scan_kernel     per-expert bases, expert offsets and the work-unit table
+//  3. pf_scatter_kernel  stable scatter: pairs of one expert in ascending pair order
+//  4. pf_gateup_kernel   h = SwiGLU(W_gate x, W_up x) per unit of <= 256 tokens
+//                        and 64 h columns; h stored as a bf16 (hi, lo) pair
+//  5. pf_down_kernel     o = W_down (h_hi + h_lo) per unit and 128 output rows,
+//                        times the global scale and the routing weight (or the
+//                        shared gate), into a per-(token, slot) buffer
+//  6. pf_combine_kernel  y = bf16(sum over slots in slot order)
+//
+// Work unit: (bank, expert, first sorted position, count <= 256).  The shared
+// expert is one more bank whose units take consecutive tokens.  Blocks are
+// mapped so that the tiles of one unit land on one XCD (dispatch is round-robin
+// over the 8 XCDs), where they share the unit's activation rows in L2.
+#include "ftmoe_device.hpp"
+#include "ftmoe_kernels.hpp"
+
+namespace ftmoe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+namespace {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfRows = 128;               // weight rows per block tile
+constexpr int kPfSlab = 64;                // K elements per LDS slab
+constexpr int kLdsRowU4 = kPfSlab / 8 + 1; // 16-byte words per LDS row (one of padding)
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Eight e2m1 codes (one 32-bit word, low nibble first) times one e4m3 block scale
+// -> eight bf16 values.  The products are exact in fp32 and in bf16, so the bf16
+// is the upper half of the fp32 bits (a truncation that loses nothing).
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+__device__ __forceinline__ uint4 dequant8_bf16(uint32_t codes, float scale) {
+  const f32x2 a = e2m1x2_to_f32<0>(codes), b = e2m1x2_to_f32<1>(codes);
+  const f32x2 c = e2m1x2_to_f32<2>(codes), d = e2m1x2_to_f32<3>(codes);
+  uint4 r;
+  r.x = pack_hi16(a.x * scale, a.y * scale);
+  r.y = pack_hi16(b.x * scale, b.y * scale);
+  r.z = pack_hi16(c.x * scale, c.y * scale);
+  r.w = pack_hi16(d.x * scale, d.y * scale);
+  return r;
+}
+
+// 32 consecutive K elements of one row (16 code bytes, 2 scale bytes) -> 4 x 16 B of bf16.
+__device__ __forceinline__ void dequant32_to_lds(uint4 q, uint32_t sc2, uint4* dst) {
+  const float s0 = e4m3_byte_to_f32<0>(sc2), s1 = e4m3_byte_to_f32<1>(sc2);
+  dst[0] = dequant8_bf16(q.x, s0);
+  dst[1] = dequant8_bf16(q.y, s0);
+  dst[2] = dequant8_bf16(q.z, s1);
+  dst[3] = dequant8_bf16(q.w, s1);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint32_t ld_u16(const void* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+
+// Block -> (unit, tile): blocks b = 8 * ntiles * q + 8 * tile + x run unit 8q + x.
+__device__ __forceinline__ void unit_tile(int ntiles, int* u, int* tile) {
+  const int b = blockIdx.x;
+  *u = (b / (8 * ntiles)) * 8 + (b & 7);
+  *tile = (b >> 3) % ntiles;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------- grouping --
+
+__global__ __launch_bounds__(256) void pf_hist_kernel(PrefillParams p) {
+  __shared__ int hist[kMaxExperts];
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * kGroupPairs;
+  for (int i = threadIdx.x; i < kGroupPairs; i += blockDim.x) {
+    const int pair = p0 + i;
+    if (pair < p.P) {
+      const int e = p.ids[pair];
+      if (e >= 0 && e < p.E) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x)
+    p.blk_count[static_cast<size_t>(blockIdx.x) * p.E + e] = hist[e];
+}
+
+// One block of kMaxExperts threads.  blk_count[b][e] becomes the number of pairs
+// of expert e in blocks before b; expert e's pairs start at offset[e].
+__global__ __launch_bounds__(kMaxExperts) void pf_scan_kernel(PrefillParams p, int nblk) {
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_units[kMaxExperts];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < p.E) {
+    for (int b = 0; b < nblk; ++b) {
+      int* c = p.blk_count + static_cast<size_t>(b) * p.E + e;
+      const int v = *c;
+      *c = total;
+      total += v;
+    }
+  }
+  const int nu = (total + kPfUnitTokens - 1) / kPfUnitTokens;
+  s_cnt[e] = total;
+  s_units[e] = nu;
+  __syncthreads();
+  // inclusive scans (Hillis-Steele) of counts and unit counts
+  for (int off = 1; off < kMaxExperts; off <<= 1) {
+    const int a = (e >= off) ? s_cnt[e - off] : 0;
+    const int b = (e >= off) ? s_units[e - off] : 0;
+    __syncthreads();
+    s_cnt[e] += a;
+    s_units[e] += b;
+    __syncthreads();
+  }
+  if (e < p.E) {
+    const int off = s_cnt[e] - total;
+    const int ubase = s_units[e] - nu;
+    p.offset[e] = off;
+    for (int c = 0; c < nu; ++c) {
+      PfUnit un;
+      un.bank = 0;
+      un.expert = e;
+      un.start = off + c * kPfUnitTokens;
+      un.count = min(kPfUnitTokens, total - c * kPfUnitTokens);
+      p.units[ubase + c] = un;
+    }
+  }
+  if (e == 0) {
+    const int routed_units = s_units[kMaxExperts - 1];
+    int n = routed_units;
+    if (p.shared.inter > 0) {
+      for (int t0 = 0; t0 < p.T; t0 += kPfUnitTokens) {
+        PfUnit un;
+        un.bank = 1;
+        un.expert = 0;
+        un.start = t0;
+        un.count = min(kPfUnitTokens, p.T - t0);
+        p.units[n++] = un;
+      }
+    }
+    *p.nunits = n;
+  }
+}
+
+// One wave per block of kGroupPairs pairs, taken 64 at a time in pair order; a
+// pair's position is its expert's running count plus the number of lower lanes
+// with the same expert, so the pairs of one expert stay in ascending order.
+__global__ __launch_bounds__(kWave) void pf_scatter_kernel(PrefillParams p) {
+  __shared__ int pos[kMaxExperts];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < p.E; e += kWave)
+    pos[e] = p.offset[e] + p.blk_count[static_cast<size_t>(blockIdx.x) * p.E + e];
+  __syncthreads();
+  const int p0 = blockIdx.x * kGroupPairs;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = 0; r < kGroupPairs / kWave; ++r) {
+    const int pair = p0 + r * kWave + lane;
+    int e = (pair < p.P) ? p.ids[pair] : -1;
+    if (e < 0 || e >= p.E) e = -1;
+    uint64_t same = 0;
+#pragma unroll 8
+    for (int j = 0; j < kWave; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      same |= (ej == e) ? (1ull << j) : 0ull;
+    }
+    if (e >= 0) {
+      const int rank = __popcll(same & below);
+      p.sorted[pos[e] + rank] = pair;
+    }
+    __syncthreads();  // every lane has read pos[] before it moves on
+    if (e >= 0 && (same & below) == 0) pos[e] += __popcll(same);
+    __syncthreads();
+  }
+}
+
+// --------------------------------------------------------------- GEMMs --
+//
+// MFMA v_mfma_f32_16x16x32_bf16: A is 16 rows x 32 K, lane l holding row l % 16
+// and 8 K values of group l / 16; B is 32 K x 16 columns, lane l holding column
+// l % 16 and the same 8 K positions; C lane l holds rows 4 (l / 16) + j, j < 4, of
+// column l % 16.  Which 8 of the 32 K positions a lane group holds only has to
+// agree between A and B: here group g of a 64-wide slab holds K = 16 g + 8 j .. +8
+// in step j (j = 0, 1), so a lane reads 32 contiguous bytes of a token row.
+//
+// A = dequantised weights (LDS, shared by the 4 waves), B = activations (token
+// rows straight from global memory into registers, 64 tokens per wave).
+
+__global__ __launch_bounds__(kPfThreads, 1) void pf_gateup_kernel(PrefillParams p) {
+  __shared__ uint4 lds[2][kPfRows * kLdsRowU4];
+  int u, tile;
+  unit_tile(p.ntiles1, &u, &tile);
+  if (u >= *p.nunits) return;
+  const PfUnit un = p.units[u];
+  const Bank bank = un.bank ? p.shared : p.routed;
+  const int I = bank.inter;
+  const int n0 = tile * 64;
+  if (n0 >= I) return;
+  const int H = p.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // dequantisation assignment: row drow of the tile (0..63 gate, 64..127 up), half dhalf
+  const int drow = tid >> 1, dhalf = tid & 1;
+  const int grow = drow < 64 ? n0 + drow : I + n0 + (drow - 64);
+  const size_t rowg = static_cast<size_t>(un.expert) * 2 * I + grow;
+  const uint8_t* wc = bank.w13 + rowg * (H / 2) + dhalf * 16;
+  const uint8_t* ws = bank.w13s + rowg * (H / 16) + dhalf * 2;
+  uint4* my_lds0 = &lds[0][drow * kLdsRowU4 + dhalf * 4];
+  uint4* my_lds1 = &lds[1][drow * kLdsRowU4 + dhalf * 4];
+
+  // this lane's token rows (B operand); rows past the unit's count repeat the last token
+  const int nfr = min(4, max(0, (un.count - wave * 64 + 15) >> 4));
+  const uint16_t* xr[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    int m = min(wave * 64 + f * 16 + (lane & 15), un.count - 1);
+    const int t = un.bank ? un.start + m : p.sorted[un.start + m] / p.k;
+    xr[f] = p.x + static_cast<size_t>(t) * H + (lane >> 4) * 16;
+  }
+
+  const int nslab = H / kPfSlab;
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // slab s: codes at wc + 32 s, scales at ws + 4 s, activations at xr[f] + 64 s
+  uint4 q_n = ld16(wc);
+  uint32_t sc_n = ld_u16(ws);
+  uint4 xa_n[4], xb_n[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    xa_n[f] = ld16(xr[f]);
+    xb_n[f] = ld16(xr[f] + 8);
+  }
+  for (int s = 0; s < nslab; ++s) {
+    const uint4 q = q_n;
+    const uint32_t sc = sc_n;
+    uint4 xa[4], xb[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      xa[f] = xa_n[f];
+      xb[f] = xb_n[f];
+    }
+    if (s + 1 < nslab) {
+      q_n = ld16(wc + (s + 1) * 32);
+      sc_n = ld_u16(ws + (s + 1) * 4);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        if (f < nfr) {
+          xa_n[f] = ld16(xr[f] + (s + 1) * kPfSlab);
+          xb_n[f] = ld16(xr[f] + (s + 1) * kPfSlab + 8);
+        }
+      }
+    }
+    uint4* buf = (s & 1) ? my_lds1 : my_lds0;
+    dequant32_to_lds(q, sc, buf);
+    __syncthreads();
+    const uint4* tile_lds = lds[s & 1];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint4 a[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        a[r] = tile_lds[(r * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + j];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        if (f < nfr) {
+          const uint4 bx = j ? xb[f] : xa[f];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) acc[f][r] = mfma_bf16(a[r], bx, acc[f][r]);
+        }
+      }
+    }
+  }
+
+  // epilogue: rows r < 4 are gate columns n0 + 16 r + 4 (lane / 16) + jj, r + 4 the
+  // matching up columns; token m = 64 wave + 16 f + lane % 16.
+  const float gg = bank.gsc[un.expert * 3 + 0], gu = bank.gsc[un.expert * 3 + 1];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int m = wave * 64 + f * 16 + (lane & 15);
+    if (f >= nfr || m >= un.count) continue;
+    const size_t row = un.bank ? static_cast<size_t>(p.P) + un.start + m
+                               : static_cast<size_t>(un.start) + m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int col = n0 + r * 16 + (lane >> 4) * 4;
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int jj = 0; jj < 4; jj += 2) {
+        float hv[2];
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const float g = acc[f][r][jj + q2] * gg;
+          const float up = acc[f][r + 4][jj + q2] * gu;
+          hv[q2] = swiglu(p.act, g, up, p.gate_max, p.up_absmax);
+        }
+        const uint32_t h0 = f32_to_bf16_bits(hv[0]), h1 = f32_to_bf16_bits(hv[1]);
+        const uint32_t l0 = f32_to_bf16_bits(hv[0] - bf16_bits_to_f32(h0));
+        const uint32_t l1 = f32_to_bf16_bits(hv[1] - bf16_bits_to_f32(h1));
+        hi[jj >> 1] = h0 | (h1 << 16);
+        lo[jj >> 1] = l0 | (l1 << 16);
+      }
+      *reinterpret_cast<uint2*>(p.hhi + row * p.Imax + col) = make_uint2(hi[0], hi[1]);
+      *reinterpret_cast<uint2*>(p.hlo + row * p.Imax + col) = make_uint2(lo[0], lo[1]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kPfThreads, 1) void pf_down_kernel(PrefillParams p) {
+  __shared__ uint4 lds[2][kPfRows * kLdsRowU4];
+  int u, tile;
+  unit_tile(p.ntiles2, &u, &tile);
+  if (u >= *p.nunits) return;
+  const PfUnit un = p.units[u];
+  const Bank bank = un.bank ? p.shared : p.routed;
+  const int I = bank.inter;
+  const int H = p.H;
+  const int h0 = tile * kPfRows;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // dequantisation: output row drow of the tile, K chunk dhalf of each slab
+  // (K-chunk-major layout: chunk c of row h at ((e * I/32 + c) * H + h) * 16)
+  const int drow = tid >> 1, dhalf = tid & 1;
+  const size_t cbase = static_cast<size_t>(un.expert) * (I / 32);
+  const uint8_t* wc = bank.w2 + ((cbase + dhalf) * H + h0 + drow) * 16;
+  const uint8_t* ws = bank.w2s + ((cbase + dhalf) * H + h0 + drow) * 2;
+  const size_t cstep_c = static_cast<size_t>(2) * H * 16;  // two chunks per slab
+  const size_t cstep_s = static_cast<size_t>(2) * H * 2;
+  uint4* my_lds0 = &lds[0][drow * kLdsRowU4 + dhalf * 4];
+  uint4* my_lds1 = &lds[1][drow * kLdsRowU4 + dhalf * 4];
+
+  const int nfr = min(4, max(0, (un.count - wave * 64 + 15) >> 4));
+  const uint16_t* hr[4];
+  const uint16_t* lr[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int m = min(wave * 64 + f * 16 + (lane & 15), un.count - 1);
+    const size_t row = un.bank ? static_cast<size_t>(p.P) + un.start + m
+                               : static_cast<size_t>(un.start) + m;
+    hr[f] = p.hhi + row * p.Imax + (lane >> 4) * 16;
+    lr[f] = p.hlo + row * p.Imax + (lane >> 4) * 16;
+  }
+
+  const int nslab = I / kPfSlab;
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 q_n = ld16(wc);
+  uint32_t sc_n = ld_u16(ws);
+  uint4 ha_n[4], hb_n[4], la_n[4], lb_n[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    ha_n[f] = ld16(hr[f]);
+    hb_n[f] = ld16(hr[f] + 8);
+    la_n[f] = ld16(lr[f]);
+    lb_n[f] = ld16(lr[f] + 8);
+  }
+  for (int s = 0; s < nslab; ++s) {
+    const uint4 q = q_n;
+    const uint32_t sc = sc_n;
+    uint4 ha[4], hb[4], la[4], lb[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      ha[f] = ha_n[f];
+      hb[f] = hb_n[f];
+      la[f] = la_n[f];
+      lb[f] = lb_n[f];
+    }
+    if (s + 1 < nslab) {
+      q_n = ld16(wc + (s + 1) * cstep_c);
+      sc_n = ld_u16(ws + (s + 1) * cstep_s);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        if (f < nfr) {
+          ha_n[f] = ld16(hr[f] + (s + 1) * kPfSlab);
+          hb_n[f] = ld16(hr[f] + (s + 1) * kPfSlab + 8);
+          la_n[f] = ld16(lr[f] + (s + 1) * kPfSlab);
+          lb_n[f] = ld16(lr[f] + (s + 1) * kPfSlab + 8);
+        }
+      }
+    }
+    uint4* buf = (s & 1) ? my_lds1 : my_lds0;
+    dequant32_to_lds(q, sc, buf);
+    __syncthreads();
+    const uint4* tile_lds = lds[s & 1];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint4 a[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        a[r] = tile_lds[(r * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + j];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        if (f < nfr) {
+          const uint4 bh = j ? hb[f] : ha[f];
+          const uint4 bl = j ? lb[f] : la[f];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            acc[f][r] = mfma_bf16(a[r], bh, acc[f][r]);
+            acc[f][r] = mfma_bf16(a[r], bl, acc[f][r]);
+          }
+        }
+      }
+    }
+  }
+
+  // epilogue: output rows h0 + 16 r + 4 (lane / 16) + jj of token m
+  const float gd = bank.gsc[un.expert * 3 + 2];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int m = wave * 64 + f * 16 + (lane & 15);
+    if (f >= nfr || m >= un.count) continue;
+    int t, slot;
+    float wt;
+    if (un.bank) {
+      t = un.start + m;
+      slot = p.k;
+      wt = p.gamma[t];
+    } else {
+      const int pair = p.sorted[un.start + m];
+      t = pair / p.k;
+      slot = pair - t * p.k;
+      wt = p.w[pair];
+    }
+    float* dst = p.out + (static_cast<size_t>(t) * p.nslots + slot) * H + h0 + (lane >> 4) * 4;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      float4 v;
+      v.x = (acc[f][r][0] * gd) * wt;
+      v.y = (acc[f][r][1] * gd) * wt;
+      v.z = (acc[f][r][2] * gd) * wt;
+      v.w = (acc[f][r][3] * gd) * wt;
+      *reinterpret_cast<float4*>(dst + r * 16) = v;
+    }
+  }
+}
+
+// y[t] = bf16(sum over slots, in slot order); a pair whose expert id is out of
+// range was never computed and makes its token's row NaN.
+__global__ __launch_bounds__(256) void pf_combine_kernel(PrefillParams p) {
+  const int H4 = p.H / 4;
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<size_t>(p.T) * H4) return;
+  const int t = static_cast<int>(i / H4);
+  const int c = static_cast<int>(i - static_cast<size_t>(t) * H4) * 4;
+  bool bad = false;
+  for (int s = 0; s < p.k; ++s) {
+    const int e = p.ids[static_cast<size_t>(t) * p.k + s];
+    bad |= (e < 0 || e >= p.E);
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* src = p.out + static_cast<size_t>(t) * p.nslots * p.H + c;
+  for (int s = 0; s < p.nslots; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(src + static_cast<size_t>(s) * p.H);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  if (bad) acc = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                             __builtin_nanf(""));
+  const uint32_t lo = f32_to_bf16_bits(acc.x) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.y)) << 16);
+  const uint32_t hi = f32_to_bf16_bits(acc.z) | (static_cast<uint32_t>(f32_to_bf16_bits(acc.w)) << 16);
+  *reinterpret_cast<uint2*>(p.y + static_cast<size_t>(t) * p.H + c) = make_uint2(lo, hi);
+}
+
+// ------------------------------------------------------------ launchers --
+
+int prefill_max_units(int E, int T, int k, bool shared) {
+  const long long P = static_cast<long long>(T) * k;
+  long long n = E + P / kPfUnitTokens + (shared ? (T + kPfUnitTokens - 1) / kPfUnitTokens : 0);
+  return static_cast<int>(n);
+}
+
+int prefill_group_blocks(int T, int k) {
+  const long long P = static_cast<long long>(T) * k;
+  return static_cast<int>((P + kGroupPairs - 1) / kGroupPairs);
+}
+
+hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
+  PrefillParams p = p0;
+  const int nblk = prefill_group_blocks(p.T, p.k);
+  const int maxu = prefill_max_units(p.E, p.T, p.k, p.shared.inter > 0);
+  const int ugroups = (maxu + 7) / 8;
+  p.ntiles1 = p.Imax / 64;
+  p.ntiles2 = p.H / kPfRows;
+  if (nblk > 0) {
+    pf_hist_kernel<<<nblk, 256, 0, s>>>(p);
+  }
+  pf_scan_kernel<<<1, kMaxExperts, 0, s>>>(p, nblk);
+  if (nblk > 0) {
+    pf_scatter_kernel<<<nblk, kWave, 0, s>>>(p);
+  }
+  pf_gateup_kernel<<<ugroups * 8 * p.ntiles1, kPfThreads, 0, s>>>(p);
+  pf_down_kernel<<<ugroups * 8 * p.ntiles2, kPfThreads, 0, s>>>(p);
+  const size_t n4 = static_cast<size_t>(p.T) * (p.H / 4);
+  pf_combine_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace ftmoe
