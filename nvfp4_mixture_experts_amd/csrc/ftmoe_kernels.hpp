@@ -68,7 +68,7 @@ struct FusedParams {
 // Many-token path (grouped GEMMs over the routed (token, slot) pairs).
 constexpr int kMaxExperts = 1024;   // experts per bank supported by the grouping kernels
 constexpr int kGroupPairs = 1024;   // pairs per grouping block
-constexpr int kPfUnitTokens = 256;  // tokens per work unit (4 waves x 64)
+constexpr int kPfUnitTokens = 256;  // tokens per work unit (8 waves x 2 fragments of 16)
 
 struct PfUnit {
   int bank;    // 0 routed, 1 shared

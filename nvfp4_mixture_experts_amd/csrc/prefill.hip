@@ -33,8 +33,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 namespace {
 
-constexpr int kPfWaves = 4;
-constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfRows = 128;               // weight rows per block tile
 constexpr int kPfSlab = 64;                // K elements per LDS slab
 constexpr int kLdsRowU4 = kPfSlab / 8 + 1; // 16-byte words per LDS row (one of padding)
@@ -62,19 +60,39 @@ __device__ __forceinline__ uint4 dequant8_bf16(uint32_t codes, float scale) {
   return r;
 }
 
-// 32 consecutive K elements of one row (16 code bytes, 2 scale bytes) -> 4 x 16 B of bf16.
-__device__ __forceinline__ void dequant32_to_lds(uint4 q, uint32_t sc2, uint4* dst) {
-  const float s0 = e4m3_byte_to_f32<0>(sc2), s1 = e4m3_byte_to_f32<1>(sc2);
-  dst[0] = dequant8_bf16(q.x, s0);
-  dst[1] = dequant8_bf16(q.y, s0);
-  dst[2] = dequant8_bf16(q.z, s1);
-  dst[3] = dequant8_bf16(q.w, s1);
-}
+// KPT = 16 or 32 consecutive K elements of one row (KPT/2 code bytes, KPT/16 scale
+// bytes) -> KPT/8 x 16 B of bf16.
+template <int KPT> struct Codes;
+template <> struct Codes<16> {
+  uint2 q;
+  uint32_t s;
+  __device__ __forceinline__ void load(const uint8_t* c, const uint8_t* sc) {
+    q = *reinterpret_cast<const uint2*>(c);
+    s = *sc;
+  }
+  __device__ __forceinline__ void to_lds(uint4* dst) const {
+    const float s0 = e4m3_byte_to_f32<0>(s);
+    dst[0] = dequant8_bf16(q.x, s0);
+    dst[1] = dequant8_bf16(q.y, s0);
+  }
+};
+template <> struct Codes<32> {
+  uint4 q;
+  uint32_t s;
+  __device__ __forceinline__ void load(const uint8_t* c, const uint8_t* sc) {
+    q = *reinterpret_cast<const uint4*>(c);
+    s = *reinterpret_cast<const uint16_t*>(sc);
+  }
+  __device__ __forceinline__ void to_lds(uint4* dst) const {
+    const float s0 = e4m3_byte_to_f32<0>(s), s1 = e4m3_byte_to_f32<1>(s);
+    dst[0] = dequant8_bf16(q.x, s0);
+    dst[1] = dequant8_bf16(q.y, s0);
+    dst[2] = dequant8_bf16(q.z, s1);
+    dst[3] = dequant8_bf16(q.w, s1);
+  }
+};
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ uint32_t ld_u16(const void* p) {
-  return *reinterpret_cast<const uint16_t*>(p);
-}
 
 // Block -> (unit, tile): blocks b = 8 * ntiles * q + 8 * tile + x run unit 8q + x.
 __device__ __forceinline__ void unit_tile(int ntiles, int* u, int* tile) {
@@ -202,10 +220,122 @@ __global__ __launch_bounds__(kWave) void pf_scatter_kernel(PrefillParams p) {
 // agree between A and B: here group g of a 64-wide slab holds K = 16 g + 8 j .. +8
 // in step j (j = 0, 1), so a lane reads 32 contiguous bytes of a token row.
 //
-// A = dequantised weights (LDS, shared by the 4 waves), B = activations (token
-// rows straight from global memory into registers, 64 tokens per wave).
+// A = dequantised weights: a 128-row x 64-K slab in LDS, written by all threads
+// of the block and read by all its waves.  B = token rows straight from global
+// memory into registers.  The 16 fragments of 16 tokens of a unit are dealt to
+// the W waves round-robin (wave w takes fragments w, w + W, ...), so every wave
+// computes a 128-row x (256 / W)-token tile.  Per 64-K slab a CU then reads
+// W x 16 KB of A from LDS and 256 x 128 B of B through L1: W = 4 keeps both
+// well inside their bandwidth at full MFMA rate.  Token rows run R slabs ahead in
+// a register ring and weight codes R slabs ahead.
 
-__global__ __launch_bounds__(kPfThreads, 1) void pf_gateup_kernel(PrefillParams p) {
+namespace {
+
+template <int W>
+struct Geometry {
+  static constexpr int kThreads = W * kWave;
+  static constexpr int kFrags = kPfUnitTokens / 16 / W;  // token fragments per wave
+  static constexpr int kTpr = kThreads / kPfRows;        // dequantising threads per row
+  static constexpr int kKpt = kPfSlab / kTpr;            // K elements each per slab
+};
+
+// Number of this wave's fragments (<= kFrags) in a unit of `count` tokens.
+template <int W>
+__device__ __forceinline__ int wave_fragments(int count, int wave) {
+  const int nf = (count + 15) >> 4;
+  return __builtin_amdgcn_readfirstlane(
+      nf > wave ? min(Geometry<W>::kFrags, (nf - wave + W - 1) / W) : 0);
+}
+
+// Token index (within the unit) of this lane's column in fragment f.
+template <int W>
+__device__ __forceinline__ int frag_token(int wave, int f, int lane) {
+  return (wave + W * f) * 16 + (lane & 15);
+}
+
+// The K loop shared by both GEMMs.  NB = 1: B is bf16 activations; NB = 2: B is a
+// (hi, lo) bf16 pair whose two products are accumulated into the same C.
+// brow[b][f]: this lane's B row for fragment f (slab 0, lane group offset applied).
+// wc / ws: this thread's codes and scales of slab 0 (kKpt K elements of tile row
+// drow, part dpart of the slab); wc_step / ws_step: their slab strides.
+template <int W, int NB, int R>
+__device__ __forceinline__ void pf_mainloop(
+    const uint8_t* wc, size_t wc_step, const uint8_t* ws, size_t ws_step,
+    const uint16_t* const (&brow)[NB][Geometry<W>::kFrags], int nfr, int nslab,
+    uint4 (*lds)[kPfRows * kLdsRowU4], int drow, int dpart, int lane,
+    f32x4 (&acc)[Geometry<W>::kFrags][8]) {
+  constexpr int FR = Geometry<W>::kFrags;
+  constexpr int KPT = Geometry<W>::kKpt;
+  uint4 xr[R][NB][FR][2];
+  Codes<KPT> cr[R];
+  // Every load is unconditional (a slab index past the end is clamped to the last
+  // slab, a fragment past the unit repeats a valid row): a load under a branch
+  // makes the compiler's wait counting fall back to waiting for every load.
+  auto clampslab = [&](int s) { return s < nslab ? s : nslab - 1; };
+  auto load_b = [&](int s, uint4 (&dst)[NB][FR][2]) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int f = 0; f < FR; ++f) {
+        dst[b][f][0] = ld16(brow[b][f] + s * kPfSlab);
+        dst[b][f][1] = ld16(brow[b][f] + s * kPfSlab + 8);
+      }
+  };
+  auto load_codes = [&](int s, Codes<KPT>& c) {
+    c.load(wc + clampslab(s) * wc_step, ws + clampslab(s) * ws_step);
+  };
+  uint4* const my0 = &lds[0][drow * kLdsRowU4 + dpart * (KPT / 8)];
+  uint4* const my1 = &lds[1][drow * kLdsRowU4 + dpart * (KPT / 8)];
+
+  // prologue: activations of slabs 0 .. R-2, then codes of slabs 0 .. R-1
+#pragma unroll
+  for (int r = 0; r < R - 1; ++r) load_b(clampslab(r), xr[r]);
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_codes(r, cr[r]);
+  cr[0].to_lds(my0);
+  load_codes(R, cr[0]);
+
+  for (int s0 = 0; s0 < nslab; s0 += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int s = s0 + r;
+      if (s >= nslab) break;
+      __syncthreads();  // weights of slab s are in LDS; slab s - 1's buffer is free
+      load_b(clampslab(s + R - 1), xr[(r + R - 1) % R]);
+      const uint4* tile = lds[s & 1];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint4 a[8];
+#pragma unroll
+        for (int rf = 0; rf < 8; ++rf)
+          a[rf] = tile[(rf * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + j];
+#pragma unroll
+        for (int f = 0; f < FR; ++f) {
+          if (f < nfr) {
+#pragma unroll
+            for (int rf = 0; rf < 8; ++rf)
+#pragma unroll
+              for (int b = 0; b < NB; ++b) acc[f][rf] = mfma_bf16(a[rf], xr[r][b][f][j], acc[f][rf]);
+          }
+        }
+      }
+      // weights of slab s + 1 (its buffer was last read in iteration s - 1), then
+      // the codes of slab s + 1 + R into the freed ring slot
+      const int c = (r + 1) % R;
+      cr[c].to_lds((s & 1) ? my0 : my1);
+      load_codes(s + 1 + R, cr[c]);
+    }
+  }
+}
+
+}  // namespace
+
+constexpr int kGateUpWaves = 4;
+constexpr int kDownWaves = 8;  // twice the MFMAs per A read (hi and lo): 8 waves stay within LDS bandwidth
+
+__global__ __launch_bounds__(kGateUpWaves * kWave, 2) void pf_gateup_kernel(PrefillParams p) {
+  constexpr int W = kGateUpWaves;
+  using G = Geometry<W>;
   __shared__ uint4 lds[2][kPfRows * kLdsRowU4];
   int u, tile;
   unit_tile(p.ntiles1, &u, &tile);
@@ -216,90 +346,39 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gateup_kernel(PrefillParams 
   const int n0 = tile * 64;
   if (n0 >= I) return;
   const int H = p.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // dequantisation assignment: row drow of the tile (0..63 gate, 64..127 up), half dhalf
-  const int drow = tid >> 1, dhalf = tid & 1;
+  // dequantisation: row drow of the tile (0..63 gate, 64..127 up), part dpart of a slab
+  const int drow = tid / G::kTpr, dpart = tid % G::kTpr;
   const int grow = drow < 64 ? n0 + drow : I + n0 + (drow - 64);
   const size_t rowg = static_cast<size_t>(un.expert) * 2 * I + grow;
-  const uint8_t* wc = bank.w13 + rowg * (H / 2) + dhalf * 16;
-  const uint8_t* ws = bank.w13s + rowg * (H / 16) + dhalf * 2;
-  uint4* my_lds0 = &lds[0][drow * kLdsRowU4 + dhalf * 4];
-  uint4* my_lds1 = &lds[1][drow * kLdsRowU4 + dhalf * 4];
+  const uint8_t* wc = bank.w13 + rowg * (H / 2) + dpart * (G::kKpt / 2);
+  const uint8_t* ws = bank.w13s + rowg * (H / 16) + dpart * (G::kKpt / 16);
 
-  // this lane's token rows (B operand); rows past the unit's count repeat the last token
-  const int nfr = min(4, max(0, (un.count - wave * 64 + 15) >> 4));
-  const uint16_t* xr[4];
+  // B rows: this lane's tokens; columns past the unit's count repeat its last token
+  const int nfr = wave_fragments<W>(un.count, wave);
+  const uint16_t* brow[1][G::kFrags];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    int m = min(wave * 64 + f * 16 + (lane & 15), un.count - 1);
+  for (int f = 0; f < G::kFrags; ++f) {
+    const int m = min(frag_token<W>(wave, f, lane), un.count - 1);
     const int t = un.bank ? un.start + m : p.sorted[un.start + m] / p.k;
-    xr[f] = p.x + static_cast<size_t>(t) * H + (lane >> 4) * 16;
+    brow[0][f] = p.x + static_cast<size_t>(t) * H + (lane >> 4) * 16;
   }
 
-  const int nslab = H / kPfSlab;
-  f32x4 acc[4][8];
+  f32x4 acc[G::kFrags][8];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < G::kFrags; ++f)
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // slab s: codes at wc + 32 s, scales at ws + 4 s, activations at xr[f] + 64 s
-  uint4 q_n = ld16(wc);
-  uint32_t sc_n = ld_u16(ws);
-  uint4 xa_n[4], xb_n[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    xa_n[f] = ld16(xr[f]);
-    xb_n[f] = ld16(xr[f] + 8);
-  }
-  for (int s = 0; s < nslab; ++s) {
-    const uint4 q = q_n;
-    const uint32_t sc = sc_n;
-    uint4 xa[4], xb[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      xa[f] = xa_n[f];
-      xb[f] = xb_n[f];
-    }
-    if (s + 1 < nslab) {
-      q_n = ld16(wc + (s + 1) * 32);
-      sc_n = ld_u16(ws + (s + 1) * 4);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if (f < nfr) {
-          xa_n[f] = ld16(xr[f] + (s + 1) * kPfSlab);
-          xb_n[f] = ld16(xr[f] + (s + 1) * kPfSlab + 8);
-        }
-      }
-    }
-    uint4* buf = (s & 1) ? my_lds1 : my_lds0;
-    dequant32_to_lds(q, sc, buf);
-    __syncthreads();
-    const uint4* tile_lds = lds[s & 1];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint4 a[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        a[r] = tile_lds[(r * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + j];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if (f < nfr) {
-          const uint4 bx = j ? xb[f] : xa[f];
-#pragma unroll
-          for (int r = 0; r < 8; ++r) acc[f][r] = mfma_bf16(a[r], bx, acc[f][r]);
-        }
-      }
-    }
-  }
+  pf_mainloop<W, 1, 2>(wc, 32, ws, 4, brow, nfr, H / kPfSlab, lds, drow, dpart, lane, acc);
 
   // epilogue: rows r < 4 are gate columns n0 + 16 r + 4 (lane / 16) + jj, r + 4 the
-  // matching up columns; token m = 64 wave + 16 f + lane % 16.
+  // matching up columns
   const float gg = bank.gsc[un.expert * 3 + 0], gu = bank.gsc[un.expert * 3 + 1];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int m = wave * 64 + f * 16 + (lane & 15);
+  for (int f = 0; f < G::kFrags; ++f) {
+    const int m = frag_token<W>(wave, f, lane);
     if (f >= nfr || m >= un.count) continue;
     const size_t row = un.bank ? static_cast<size_t>(p.P) + un.start + m
                                : static_cast<size_t>(un.start) + m;
@@ -328,7 +407,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_gateup_kernel(PrefillParams 
   }
 }
 
-__global__ __launch_bounds__(kPfThreads, 1) void pf_down_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kDownWaves * kWave, 1) void pf_down_kernel(PrefillParams p) {
+  constexpr int W = kDownWaves;
+  using G = Geometry<W>;
   __shared__ uint4 lds[2][kPfRows * kLdsRowU4];
   int u, tile;
   unit_tile(p.ntiles2, &u, &tile);
@@ -338,102 +419,42 @@ __global__ __launch_bounds__(kPfThreads, 1) void pf_down_kernel(PrefillParams p)
   const int I = bank.inter;
   const int H = p.H;
   const int h0 = tile * kPfRows;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // dequantisation: output row drow of the tile, K chunk dhalf of each slab
-  // (K-chunk-major layout: chunk c of row h at ((e * I/32 + c) * H + h) * 16)
-  const int drow = tid >> 1, dhalf = tid & 1;
-  const size_t cbase = static_cast<size_t>(un.expert) * (I / 32);
-  const uint8_t* wc = bank.w2 + ((cbase + dhalf) * H + h0 + drow) * 16;
-  const uint8_t* ws = bank.w2s + ((cbase + dhalf) * H + h0 + drow) * 2;
-  const size_t cstep_c = static_cast<size_t>(2) * H * 16;  // two chunks per slab
-  const size_t cstep_s = static_cast<size_t>(2) * H * 2;
-  uint4* my_lds0 = &lds[0][drow * kLdsRowU4 + dhalf * 4];
-  uint4* my_lds1 = &lds[1][drow * kLdsRowU4 + dhalf * 4];
+  // dequantisation: output row drow of the tile, kKpt K elements at part dpart of
+  // each 64-K slab (two 32-K chunks, K-chunk-major: chunk c of row h at
+  // ((e * I/32 + c) * H + h) * 16, its two scale bytes at (...) * 2)
+  const int drow = tid / G::kTpr, dpart = tid % G::kTpr;
+  const int kofs = dpart * G::kKpt;  // K offset within the slab
+  const size_t chunk0 = static_cast<size_t>(un.expert) * (I / 32) + (kofs >> 5);
+  const uint8_t* wc = bank.w2 + (chunk0 * H + h0 + drow) * 16 + (kofs & 31) / 2;
+  const uint8_t* ws = bank.w2s + (chunk0 * H + h0 + drow) * 2 + (kofs & 31) / 16;
 
-  const int nfr = min(4, max(0, (un.count - wave * 64 + 15) >> 4));
-  const uint16_t* hr[4];
-  const uint16_t* lr[4];
+  const int nfr = wave_fragments<W>(un.count, wave);
+  const uint16_t* brow[2][G::kFrags];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int m = min(wave * 64 + f * 16 + (lane & 15), un.count - 1);
+  for (int f = 0; f < G::kFrags; ++f) {
+    const int m = min(frag_token<W>(wave, f, lane), un.count - 1);
     const size_t row = un.bank ? static_cast<size_t>(p.P) + un.start + m
                                : static_cast<size_t>(un.start) + m;
-    hr[f] = p.hhi + row * p.Imax + (lane >> 4) * 16;
-    lr[f] = p.hlo + row * p.Imax + (lane >> 4) * 16;
+    brow[0][f] = p.hhi + row * p.Imax + (lane >> 4) * 16;
+    brow[1][f] = p.hlo + row * p.Imax + (lane >> 4) * 16;
   }
 
-  const int nslab = I / kPfSlab;
-  f32x4 acc[4][8];
+  f32x4 acc[G::kFrags][8];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < G::kFrags; ++f)
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  uint4 q_n = ld16(wc);
-  uint32_t sc_n = ld_u16(ws);
-  uint4 ha_n[4], hb_n[4], la_n[4], lb_n[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    ha_n[f] = ld16(hr[f]);
-    hb_n[f] = ld16(hr[f] + 8);
-    la_n[f] = ld16(lr[f]);
-    lb_n[f] = ld16(lr[f] + 8);
-  }
-  for (int s = 0; s < nslab; ++s) {
-    const uint4 q = q_n;
-    const uint32_t sc = sc_n;
-    uint4 ha[4], hb[4], la[4], lb[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      ha[f] = ha_n[f];
-      hb[f] = hb_n[f];
-      la[f] = la_n[f];
-      lb[f] = lb_n[f];
-    }
-    if (s + 1 < nslab) {
-      q_n = ld16(wc + (s + 1) * cstep_c);
-      sc_n = ld_u16(ws + (s + 1) * cstep_s);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if (f < nfr) {
-          ha_n[f] = ld16(hr[f] + (s + 1) * kPfSlab);
-          hb_n[f] = ld16(hr[f] + (s + 1) * kPfSlab + 8);
-          la_n[f] = ld16(lr[f] + (s + 1) * kPfSlab);
-          lb_n[f] = ld16(lr[f] + (s + 1) * kPfSlab + 8);
-        }
-      }
-    }
-    uint4* buf = (s & 1) ? my_lds1 : my_lds0;
-    dequant32_to_lds(q, sc, buf);
-    __syncthreads();
-    const uint4* tile_lds = lds[s & 1];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint4 a[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        a[r] = tile_lds[(r * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + j];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if (f < nfr) {
-          const uint4 bh = j ? hb[f] : ha[f];
-          const uint4 bl = j ? lb[f] : la[f];
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            acc[f][r] = mfma_bf16(a[r], bh, acc[f][r]);
-            acc[f][r] = mfma_bf16(a[r], bl, acc[f][r]);
-          }
-        }
-      }
-    }
-  }
+  pf_mainloop<W, 2, 2>(wc, static_cast<size_t>(2) * H * 16, ws, static_cast<size_t>(2) * H * 2,
+                       brow, nfr, I / kPfSlab, lds, drow, dpart, lane, acc);
 
   // epilogue: output rows h0 + 16 r + 4 (lane / 16) + jj of token m
   const float gd = bank.gsc[un.expert * 3 + 2];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int m = wave * 64 + f * 16 + (lane & 15);
+  for (int f = 0; f < G::kFrags; ++f) {
+    const int m = frag_token<W>(wave, f, lane);
     if (f >= nfr || m >= un.count) continue;
     int t, slot;
     float wt;
@@ -516,8 +537,8 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
   if (nblk > 0) {
     pf_scatter_kernel<<<nblk, kWave, 0, s>>>(p);
   }
-  pf_gateup_kernel<<<ugroups * 8 * p.ntiles1, kPfThreads, 0, s>>>(p);
-  pf_down_kernel<<<ugroups * 8 * p.ntiles2, kPfThreads, 0, s>>>(p);
+  pf_gateup_kernel<<<ugroups * 8 * p.ntiles1, kGateUpWaves * kWave, 0, s>>>(p);
+  pf_down_kernel<<<ugroups * 8 * p.ntiles2, kDownWaves * kWave, 0, s>>>(p);
   const size_t n4 = static_cast<size_t>(p.T) * (p.H / 4);
   pf_combine_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, s>>>(p);
   return hipGetLastError();
