@@ -57,6 +57,10 @@ ft_status fused_grid(int* grid) {
 }
 constexpr int kMaxTopK = 16;
 constexpr int kMaxDecodeTokens = 64;
+// Decode calls of at least this many tokens run the grouped path (route, grouping,
+// gate|up and down grouped GEMMs, combine), where every selected expert's weights
+// are read once for all of its tokens; fewer tokens run the fused one-launch kernel.
+constexpr int kGroupedDecodeMinTokens = 8;
 constexpr int kRowGroup = 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -114,8 +118,9 @@ Bank to_bank(const ft_nvfp4_experts* b, int inter) {
 // reset by the kernel that uses it, so a route workspace may be reused across
 // token counts once it has been zero-filled.
 struct Layout {
-  size_t sync, gen, logits, h, part;                               // route / decode
-  size_t gamma, blk_count, offset, units, nunits, sorted, hhi, hlo, out;  // prefill
+  size_t sync, gen, logits, h, part;                                 // route / fused decode
+  size_t ids, w;                                                     // routes of a grouped decode
+  size_t gamma, count, cursor, offset, units, nunits, sorted, hhi, hlo, out;  // grouped experts
   size_t total;
 };
 
@@ -137,18 +142,12 @@ Layout layout(const ft_moe_desc& d, int64_t T, int path) {
   const size_t imax = static_cast<size_t>(d.inter > d.shared_inter ? d.inter : d.shared_inter);
   const size_t nslots = k + (d.shared_inter > 0 ? 1 : 0);
   L.sync = take(256);  // route counter, error word
-  if (path == 0) {
-    L.logits = take(t * E * 4);
-  } else if (path == 1) {
-    L.gen = take(static_cast<size_t>(kMaxFusedGrid) * 4);
-    L.logits = take(static_cast<size_t>(kLogitCopies) * t * (E + 1) * 8);
-    L.h = take(t * nslots * imax * 8);
-    L.part = take(static_cast<size_t>(kMaxFusedGrid) * kRowGroup * 8);
-  } else {
+  auto grouped = [&]() {
     const int Ti = static_cast<int>(T), ki = d.top_k;
     const size_t P = t * k;
     L.gamma = take(t * 4);
-    L.blk_count = take(static_cast<size_t>(prefill_group_blocks(Ti, ki)) * E * 4);
+    L.count = take(E * 4);
+    L.cursor = take(E * 4);
     L.offset = take(E * 4);
     L.units = take(static_cast<size_t>(prefill_max_units(d.num_experts, Ti, ki,
                                                          d.shared_inter > 0)) * sizeof(PfUnit));
@@ -157,6 +156,25 @@ Layout layout(const ft_moe_desc& d, int64_t T, int path) {
     L.hhi = take((P + t) * imax * 2);
     L.hlo = take((P + t) * imax * 2);
     L.out = take(t * nslots * H * 4);
+  };
+  if (path == 0) {
+    L.logits = take(t * E * 4);
+  } else if (path == 1) {
+    // the fused kernel's regions, then (for token counts that take the grouped
+    // path) router logits, routes and the grouped regions
+    L.gen = take(static_cast<size_t>(kMaxFusedGrid) * 4);
+    const size_t fused_logits = static_cast<size_t>(kLogitCopies) * t * (E + 1) * 8;
+    const size_t route_logits = t * E * 4;
+    L.logits = take(fused_logits > route_logits ? fused_logits : route_logits);
+    L.h = take(t * nslots * imax * 8);
+    L.part = take(static_cast<size_t>(kMaxFusedGrid) * kRowGroup * 8);
+    if (T >= kGroupedDecodeMinTokens) {
+      L.ids = take(t * k * 4);
+      L.w = take(t * k * 4);
+      grouped();
+    }
+  } else {
+    grouped();
   }
   L.total = off;
   return L;
@@ -191,6 +209,79 @@ ft_status check_layer_args(const ft_moe_desc* desc, const uint16_t* x,
     if (!shared_gate) return fail(FT_EINVAL, "shared_gate is NULL with a shared expert");
     if (!aligned16(shared_gate)) return fail(FT_EINVAL, "shared_gate must be 16-byte aligned");
   }
+  return FT_OK;
+}
+
+// Router logits (fp64, one fp32 rounding), the shared gate when `gamma` is set,
+// and top-k with softmax weights into ids / w (and the optional copies).
+ft_status run_route(const ft_moe_desc* desc, int T, const uint16_t* x, const float* w_router,
+                    const float* bias, const uint16_t* shared_gate, float* logits, float* gamma,
+                    int32_t* ids, float* w, int32_t* ids_copy, float* w_copy, uint32_t* counter,
+                    hipStream_t s) {
+  RouteParams p{};
+  p.x = x;
+  p.wr = w_router;
+  p.bias = bias;
+  p.shared_gate = gamma ? shared_gate : nullptr;
+  p.T = T;
+  p.E = desc->num_experts;
+  p.H = desc->hidden;
+  p.k = desc->top_k;
+  p.logits = logits;
+  p.gamma = gamma;
+  p.ids = ids;
+  p.w = w;
+  p.ids_copy = ids_copy;
+  p.w_copy = w_copy;
+  p.counter = counter;
+  // the last block to finish selects the experts when it has a wave per token;
+  // otherwise a top-k kernel with one wave per token follows
+  const bool fuse = T <= route_fused_topk_tokens();
+  hipError_t e = launch_route(p, fuse, s);
+  if (e != hipSuccess) return hip_fail(e, "route kernel");
+  if (!fuse) {
+    e = launch_topk(p, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k kernel");
+  }
+  return FT_OK;
+}
+
+// Grouped experts: pairs grouped by expert, gate|up and down grouped GEMMs, combine.
+// gamma (the shared gate) must already be in the workspace when there is a shared expert.
+ft_status run_grouped(const ft_moe_desc* desc, int T, const uint16_t* x, const int32_t* ids,
+                      const float* w, const ft_nvfp4_experts* routed,
+                      const ft_nvfp4_experts* shared, uint16_t* y, void* workspace,
+                      const Layout& L, hipStream_t s) {
+  const bool has_shared = desc->shared_inter > 0;
+  PrefillParams p{};
+  p.x = x;
+  p.T = T;
+  p.H = desc->hidden;
+  p.k = desc->top_k;
+  p.E = desc->num_experts;
+  p.P = T * desc->top_k;
+  p.routed = to_bank(routed, desc->inter);
+  p.shared = has_shared ? to_bank(shared, desc->shared_inter) : Bank{};
+  p.ids = ids;
+  p.w = w;
+  p.gamma = has_shared ? at<float>(workspace, L.gamma) : nullptr;
+  p.count = at<int32_t>(workspace, L.count);
+  p.cursor = at<int32_t>(workspace, L.cursor);
+  p.offset = at<int32_t>(workspace, L.offset);
+  p.sorted = at<int32_t>(workspace, L.sorted);
+  p.units = at<PfUnit>(workspace, L.units);
+  p.nunits = at<int32_t>(workspace, L.nunits);
+  p.Imax = desc->inter > desc->shared_inter ? desc->inter : desc->shared_inter;
+  p.hhi = at<uint16_t>(workspace, L.hhi);
+  p.hlo = at<uint16_t>(workspace, L.hlo);
+  p.out = at<float>(workspace, L.out);
+  p.nslots = desc->top_k + (has_shared ? 1 : 0);
+  p.act = desc->act;
+  p.gate_max = desc->gate_max;
+  p.up_absmax = desc->up_absmax;
+  p.y = y;
+  hipError_t e = launch_prefill(p, s);
+  if (e != hipSuccess) return hip_fail(e, "grouped expert kernels");
   return FT_OK;
 }
 
@@ -277,28 +368,11 @@ ft_status ft_moe_route(const ft_moe_desc* desc, int64_t tokens, const uint16_t* 
   Layout L;
   if ((st = check_ws(desc, tokens, 0, workspace, workspace_bytes, &L)) != FT_OK) return st;
   if (tokens == 0) return ok();
-  RouteParams p{};
-  p.x = x;
-  p.wr = w_router;
-  p.bias = bias;
-  p.shared_gate = nullptr;
-  p.T = static_cast<int>(tokens);
-  p.E = desc->num_experts;
-  p.H = desc->hidden;
-  p.k = desc->top_k;
-  p.logits = at<float>(workspace, L.logits);
-  p.gamma = nullptr;
-  p.ids = topk_ids;
-  p.w = topk_w;
-  p.counter = at<uint32_t>(workspace, L.sync) + kRouteCounterWord;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fuse = tokens <= kMaxDecodeTokens;
-  hipError_t e = launch_route(p, fuse, s);
-  if (e != hipSuccess) return hip_fail(e, "route kernel");
-  if (!fuse) {
-    e = launch_topk(p, s);
-    if (e != hipSuccess) return hip_fail(e, "top-k kernel");
-  }
+  st = run_route(desc, static_cast<int>(tokens), x, w_router, bias, nullptr,
+                 at<float>(workspace, L.logits), nullptr, topk_ids, topk_w, nullptr, nullptr,
+                 at<uint32_t>(workspace, L.sync) + kRouteCounterWord,
+                 static_cast<hipStream_t>(stream));
+  if (st != FT_OK) return st;
   return ok();
 }
 
@@ -324,6 +398,17 @@ ft_status ft_moe_nvfp4_decode(const ft_moe_desc* desc, int64_t tokens, const uin
   const bool has_shared = desc->shared_inter > 0;
   const int T = static_cast<int>(tokens);
   const int nrg = desc->hidden / kRowGroup;
+  if (T >= kGroupedDecodeMinTokens) {
+    int32_t* ids = at<int32_t>(workspace, L.ids);
+    float* wts = at<float>(workspace, L.w);
+    st = run_route(desc, T, x, w_router, bias, shared_gate, at<float>(workspace, L.logits),
+                   has_shared ? at<float>(workspace, L.gamma) : nullptr, ids, wts, topk_ids_out,
+                   topk_w_out, at<uint32_t>(workspace, L.sync) + kRouteCounterWord, s);
+    if (st != FT_OK) return st;
+    st = run_grouped(desc, T, x, ids, wts, routed, shared, y, workspace, L, s);
+    if (st != FT_OK) return st;
+    return ok();
+  }
 
   FusedParams p{};
   p.x = x;
@@ -373,9 +458,8 @@ ft_status ft_moe_nvfp4_prefill(const ft_moe_desc* desc, int64_t tokens, const ui
   if ((st = check_ws(desc, tokens, 2, workspace, workspace_bytes, &L)) != FT_OK) return st;
   if (tokens == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool has_shared = desc->shared_inter > 0;
   const int T = static_cast<int>(tokens);
-  if (has_shared) {
+  if (desc->shared_inter > 0) {
     // sigmoid of the shared expert's gate for every token
     RouteParams p{};
     p.x = x;
@@ -388,34 +472,8 @@ ft_status ft_moe_nvfp4_prefill(const ft_moe_desc* desc, int64_t tokens, const ui
     hipError_t e = launch_route(p, false, s);
     if (e != hipSuccess) return hip_fail(e, "shared gate kernel");
   }
-  PrefillParams p{};
-  p.x = x;
-  p.T = T;
-  p.H = desc->hidden;
-  p.k = desc->top_k;
-  p.E = desc->num_experts;
-  p.P = T * desc->top_k;
-  p.routed = to_bank(routed, desc->inter);
-  p.shared = has_shared ? to_bank(shared, desc->shared_inter) : Bank{};
-  p.ids = topk_ids;
-  p.w = topk_w;
-  p.gamma = has_shared ? at<float>(workspace, L.gamma) : nullptr;
-  p.blk_count = at<int32_t>(workspace, L.blk_count);
-  p.offset = at<int32_t>(workspace, L.offset);
-  p.sorted = at<int32_t>(workspace, L.sorted);
-  p.units = at<PfUnit>(workspace, L.units);
-  p.nunits = at<int32_t>(workspace, L.nunits);
-  p.Imax = desc->inter > desc->shared_inter ? desc->inter : desc->shared_inter;
-  p.hhi = at<uint16_t>(workspace, L.hhi);
-  p.hlo = at<uint16_t>(workspace, L.hlo);
-  p.out = at<float>(workspace, L.out);
-  p.nslots = desc->top_k + (has_shared ? 1 : 0);
-  p.act = desc->act;
-  p.gate_max = desc->gate_max;
-  p.up_absmax = desc->up_absmax;
-  p.y = y;
-  hipError_t e = launch_prefill(p, s);
-  if (e != hipSuccess) return hip_fail(e, "prefill kernels");
+  st = run_grouped(desc, T, x, topk_ids, topk_w, routed, shared, y, workspace, L, s);
+  if (st != FT_OK) return st;
   return ok();
 }
 

@@ -32,8 +32,7 @@ struct RouteParams {
   int32_t* ids_copy;            // optional second copy of ids (caller's side output)
   float* w_copy;                // optional second copy of w
   uint32_t* counter;            // last-arriver counter for the fused top-k
-  uint32_t* zero;               // counters of later kernels of the same call, cleared here
-  int nzero;
+  int tok_tile;                 // tokens per wave (set by the launcher)
 };
 
 // The whole decode layer in one persistent launch (one block per CU).  Values
@@ -67,14 +66,16 @@ struct FusedParams {
 
 // Many-token path (grouped GEMMs over the routed (token, slot) pairs).
 constexpr int kMaxExperts = 1024;   // experts per bank supported by the grouping kernels
-constexpr int kGroupPairs = 1024;   // pairs per grouping block
-constexpr int kPfUnitTokens = 256;  // tokens per work unit (8 waves x 2 fragments of 16)
+constexpr int kGroupPairs = 1024;   // pairs per histogram block
+constexpr int kGroupOneBlockPairs = 16384;  // up to this many pairs are grouped by one block
+constexpr int kPfUnitTokens = 256;    // tokens per work unit of a many-token call
+constexpr int kSmallUnitTokens = 64;  // ... and of a call of at most this many tokens
 
 struct PfUnit {
   int bank;    // 0 routed, 1 shared
   int expert;  // routed expert id (0 for the shared bank)
   int start;   // routed: first position in `sorted`; shared: first token
-  int count;   // 1 .. kPfUnitTokens
+  int count;   // 1 .. unit_tokens
 };
 
 struct PrefillParams {
@@ -84,9 +85,10 @@ struct PrefillParams {
   const int32_t* ids;      // i32 [T][k]
   const float* w;          // f32 [T][k]
   const float* gamma;      // f32 [T] shared-expert gate, or null
-  int32_t* blk_count;      // i32 [grouping blocks][E]
+  int32_t* count;          // i32 [E] pairs per expert (zero between calls)
+  int32_t* cursor;         // i32 [E] fill positions of the groups
   int32_t* offset;         // i32 [E] first sorted position of each expert
-  int32_t* sorted;         // i32 [P] pairs grouped by expert, ascending within one
+  int32_t* sorted;         // i32 [P] pairs grouped by expert (in no particular order within one)
   PfUnit* units;           // [max units]
   int32_t* nunits;         // number of valid units
   int Imax;                // row stride of hhi / hlo
@@ -97,9 +99,11 @@ struct PrefillParams {
   int act;
   float gate_max, up_absmax;
   int ntiles1, ntiles2;    // column tiles per unit of the two GEMMs (set by the launcher)
+  int unit_tokens;         // tokens per work unit (set by the launcher)
   uint16_t* y;             // bf16 [T][H]
 };
 
+int prefill_unit_tokens(int T);
 int prefill_max_units(int E, int T, int k, bool shared);
 int prefill_group_blocks(int T, int k);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
@@ -108,6 +112,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 hipError_t launch_decode_fused(const FusedParams& p, int grid, hipStream_t s);
 int fused_block_threads();
 hipError_t launch_route(const RouteParams& p, bool fuse_topk, hipStream_t s);
+int route_fused_topk_tokens();  // the fused top-k handles at most this many tokens
 hipError_t launch_topk(const RouteParams& p, hipStream_t s);
 // Lanes per row and chunks per lane of the decode gate|up GEMV for hidden size H
 // (supported when lpr > 0 and 1 <= cpl <= 4).

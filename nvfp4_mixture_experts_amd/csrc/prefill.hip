@@ -9,15 +9,15 @@
 // code * scale are exact in bf16; the fp32 global scale multiplies the fp32
 // accumulator instead.
 //
-//  1. pf_hist_kernel     per block of 1024 pairs, a histogram of expert ids
-//  2. pf_scan_kernel     per-expert bases, expert offsets and the work-unit table
-//  3. pf_scatter_kernel  stable scatter: pairs of one expert in ascending pair order
-//  4. pf_gateup_kernel   h = SwiGLU(W_gate x, W_up x) per unit of <= 256 tokens
+//  1. grouping          per-expert counts, offsets and the work-unit table, and the
+//                        pairs scattered into per-expert groups (one block for few
+//                        pairs; histogram, scan and scatter kernels for many)
+//  2. pf_gateup_kernel   h = SwiGLU(W_gate x, W_up x) per unit of <= 256 tokens
 //                        and 64 h columns; h stored as a bf16 (hi, lo) pair
-//  5. pf_down_kernel     o = W_down (h_hi + h_lo) per unit and 128 output rows,
+//  3. pf_down_kernel     o = W_down (h_hi + h_lo) per unit and 128 output rows,
 //                        times the global scale and the routing weight (or the
 //                        shared gate), into a per-(token, slot) buffer
-//  6. pf_combine_kernel  y = bf16(sum over slots in slot order)
+//  4. pf_combine_kernel  y = bf16(sum over slots in slot order)
 //
 // Work unit: (bank, expert, first sorted position, count <= 256).  The shared
 // expert is one more bank whose units take consecutive tokens.  Blocks are
@@ -104,41 +104,24 @@ __device__ __forceinline__ void unit_tile(int ntiles, int* u, int* tile) {
 }  // namespace
 
 // ------------------------------------------------------------- grouping --
+//
+// The position of a pair inside its expert's group does not change any result:
+// every token is one MFMA column, computed with the same operands and the same K
+// order wherever it sits, and the combine sums a token's slots in slot order.  So
+// the groups are filled with atomic cursors (any order is as good as another).
 
-__global__ __launch_bounds__(256) void pf_hist_kernel(PrefillParams p) {
-  __shared__ int hist[kMaxExperts];
-  for (int e = threadIdx.x; e < p.E; e += blockDim.x) hist[e] = 0;
-  __syncthreads();
-  const int p0 = blockIdx.x * kGroupPairs;
-  for (int i = threadIdx.x; i < kGroupPairs; i += blockDim.x) {
-    const int pair = p0 + i;
-    if (pair < p.P) {
-      const int e = p.ids[pair];
-      if (e >= 0 && e < p.E) atomicAdd(&hist[e], 1);
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < p.E; e += blockDim.x)
-    p.blk_count[static_cast<size_t>(blockIdx.x) * p.E + e] = hist[e];
-}
+namespace {
 
-// One block of kMaxExperts threads.  blk_count[b][e] becomes the number of pairs
-// of expert e in blocks before b; expert e's pairs start at offset[e].
-__global__ __launch_bounds__(kMaxExperts) void pf_scan_kernel(PrefillParams p, int nblk) {
+// Exclusive offsets of the per-expert counts and the work-unit table, by one block
+// of kMaxExperts threads; count[e] is thread e's count (0 for e >= E).  Writes
+// offset[], cursor[] (= offset) and units[] / nunits.
+__device__ void group_units(const PrefillParams& p, int count, int* cursor) {
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_units[kMaxExperts];
   const int e = threadIdx.x;
-  int total = 0;
-  if (e < p.E) {
-    for (int b = 0; b < nblk; ++b) {
-      int* c = p.blk_count + static_cast<size_t>(b) * p.E + e;
-      const int v = *c;
-      *c = total;
-      total += v;
-    }
-  }
-  const int nu = (total + kPfUnitTokens - 1) / kPfUnitTokens;
-  s_cnt[e] = total;
+  const int ut = p.unit_tokens;
+  const int nu = (count + ut - 1) / ut;
+  s_cnt[e] = count;
   s_units[e] = nu;
   __syncthreads();
   // inclusive scans (Hillis-Steele) of counts and unit counts
@@ -151,28 +134,28 @@ __global__ __launch_bounds__(kMaxExperts) void pf_scan_kernel(PrefillParams p, i
     __syncthreads();
   }
   if (e < p.E) {
-    const int off = s_cnt[e] - total;
+    const int off = s_cnt[e] - count;
     const int ubase = s_units[e] - nu;
     p.offset[e] = off;
+    cursor[e] = off;
     for (int c = 0; c < nu; ++c) {
       PfUnit un;
       un.bank = 0;
       un.expert = e;
-      un.start = off + c * kPfUnitTokens;
-      un.count = min(kPfUnitTokens, total - c * kPfUnitTokens);
+      un.start = off + c * ut;
+      un.count = min(ut, count - c * ut);
       p.units[ubase + c] = un;
     }
   }
   if (e == 0) {
-    const int routed_units = s_units[kMaxExperts - 1];
-    int n = routed_units;
+    int n = s_units[kMaxExperts - 1];
     if (p.shared.inter > 0) {
-      for (int t0 = 0; t0 < p.T; t0 += kPfUnitTokens) {
+      for (int t0 = 0; t0 < p.T; t0 += ut) {
         PfUnit un;
         un.bank = 1;
         un.expert = 0;
         un.start = t0;
-        un.count = min(kPfUnitTokens, p.T - t0);
+        un.count = min(ut, p.T - t0);
         p.units[n++] = un;
       }
     }
@@ -180,35 +163,68 @@ __global__ __launch_bounds__(kMaxExperts) void pf_scan_kernel(PrefillParams p, i
   }
 }
 
-// One wave per block of kGroupPairs pairs, taken 64 at a time in pair order; a
-// pair's position is its expert's running count plus the number of lower lanes
-// with the same expert, so the pairs of one expert stay in ascending order.
-__global__ __launch_bounds__(kWave) void pf_scatter_kernel(PrefillParams p) {
-  __shared__ int pos[kMaxExperts];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < p.E; e += kWave)
-    pos[e] = p.offset[e] + p.blk_count[static_cast<size_t>(blockIdx.x) * p.E + e];
+__device__ __forceinline__ int valid_expert(const PrefillParams& p, int pair) {
+  const int e = p.ids[pair];
+  return (e >= 0 && e < p.E) ? e : -1;
+}
+
+}  // namespace
+
+// Whole grouping in one block (few pairs): LDS counts, offsets, LDS cursors.
+__global__ __launch_bounds__(kMaxExperts) void pf_group_one_block_kernel(PrefillParams p) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int cur[kMaxExperts];
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  for (int pair = tid; pair < p.P; pair += kMaxExperts) {
+    const int e = valid_expert(p, pair);
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  group_units(p, cnt[tid], cur);
+  __syncthreads();
+  for (int pair = tid; pair < p.P; pair += kMaxExperts) {
+    const int e = valid_expert(p, pair);
+    if (e >= 0) p.sorted[atomicAdd(&cur[e], 1)] = pair;
+  }
+}
+
+// Many pairs: per-block LDS histograms added into count[] ...
+__global__ __launch_bounds__(256) void pf_hist_kernel(PrefillParams p) {
+  __shared__ int hist[kMaxExperts];
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
   const int p0 = blockIdx.x * kGroupPairs;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int r = 0; r < kGroupPairs / kWave; ++r) {
-    const int pair = p0 + r * kWave + lane;
-    int e = (pair < p.P) ? p.ids[pair] : -1;
-    if (e < 0 || e >= p.E) e = -1;
-    uint64_t same = 0;
-#pragma unroll 8
-    for (int j = 0; j < kWave; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      same |= (ej == e) ? (1ull << j) : 0ull;
+  for (int i = threadIdx.x; i < kGroupPairs; i += blockDim.x) {
+    const int pair = p0 + i;
+    if (pair < p.P) {
+      const int e = valid_expert(p, pair);
+      if (e >= 0) atomicAdd(&hist[e], 1);
     }
-    if (e >= 0) {
-      const int rank = __popcll(same & below);
-      p.sorted[pos[e] + rank] = pair;
-    }
-    __syncthreads();  // every lane has read pos[] before it moves on
-    if (e >= 0 && (same & below) == 0) pos[e] += __popcll(same);
-    __syncthreads();
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < p.E; e += blockDim.x)
+    if (hist[e]) atomicAdd(&p.count[e], hist[e]);
+}
+
+// ... offsets and units by one block, which also clears count[] for the next call ...
+__global__ __launch_bounds__(kMaxExperts) void pf_scan_kernel(PrefillParams p) {
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < p.E) {
+    c = p.count[e];
+    p.count[e] = 0;
+  }
+  group_units(p, c, p.cursor);
+}
+
+// ... and a scatter through global cursors.
+__global__ __launch_bounds__(256) void pf_scatter_kernel(PrefillParams p) {
+  const int pair = blockIdx.x * blockDim.x + threadIdx.x;
+  if (pair >= p.P) return;
+  const int e = valid_expert(p, pair);
+  if (e >= 0) p.sorted[atomicAdd(&p.cursor[e], 1)] = pair;
 }
 
 // --------------------------------------------------------------- GEMMs --
@@ -231,20 +247,21 @@ __global__ __launch_bounds__(kWave) void pf_scatter_kernel(PrefillParams p) {
 
 namespace {
 
-template <int W>
+// W waves of up to FR token fragments each: a unit holds up to 16 W FR tokens.
+template <int W, int FR>
 struct Geometry {
   static constexpr int kThreads = W * kWave;
-  static constexpr int kFrags = kPfUnitTokens / 16 / W;  // token fragments per wave
+  static constexpr int kFrags = FR;                      // token fragments per wave
+  static constexpr int kUnitTokens = 16 * W * FR;
   static constexpr int kTpr = kThreads / kPfRows;        // dequantising threads per row
   static constexpr int kKpt = kPfSlab / kTpr;            // K elements each per slab
 };
 
-// Number of this wave's fragments (<= kFrags) in a unit of `count` tokens.
-template <int W>
+// Number of this wave's fragments (<= FR) in a unit of `count` tokens.
+template <int W, int FR>
 __device__ __forceinline__ int wave_fragments(int count, int wave) {
   const int nf = (count + 15) >> 4;
-  return __builtin_amdgcn_readfirstlane(
-      nf > wave ? min(Geometry<W>::kFrags, (nf - wave + W - 1) / W) : 0);
+  return __builtin_amdgcn_readfirstlane(nf > wave ? min(FR, (nf - wave + W - 1) / W) : 0);
 }
 
 // Token index (within the unit) of this lane's column in fragment f.
@@ -258,16 +275,18 @@ __device__ __forceinline__ int frag_token(int wave, int f, int lane) {
 // brow[b][f]: this lane's B row for fragment f (slab 0, lane group offset applied).
 // wc / ws: this thread's codes and scales of slab 0 (kKpt K elements of tile row
 // drow, part dpart of the slab); wc_step / ws_step: their slab strides.
-template <int W, int NB, int R>
+// Token rows run R - 1 slabs ahead (a ring of R), weight codes RW slabs ahead (a
+// ring of RW; RW is a multiple of R and even, and the loop is unrolled RW times so
+// that every ring slot and LDS buffer index is a compile-time constant).
+template <int W, int FR, int NB, int R, int RW>
 __device__ __forceinline__ void pf_mainloop(
     const uint8_t* wc, size_t wc_step, const uint8_t* ws, size_t ws_step,
-    const uint16_t* const (&brow)[NB][Geometry<W>::kFrags], int nfr, int nslab,
-    uint4 (*lds)[kPfRows * kLdsRowU4], int drow, int dpart, int lane,
-    f32x4 (&acc)[Geometry<W>::kFrags][8]) {
-  constexpr int FR = Geometry<W>::kFrags;
-  constexpr int KPT = Geometry<W>::kKpt;
+    const uint16_t* const (&brow)[NB][FR], int nfr, int nslab,
+    uint4 (*lds)[kPfRows * kLdsRowU4], int drow, int dpart, int lane, f32x4 (&acc)[FR][8]) {
+  static_assert(RW % R == 0 && RW % 2 == 0, "ring depths");
+  constexpr int KPT = Geometry<W, FR>::kKpt;
   uint4 xr[R][NB][FR][2];
-  Codes<KPT> cr[R];
+  Codes<KPT> cr[RW];
   // Every load is unconditional (a slab index past the end is clamped to the last
   // slab, a fragment past the unit repeats a valid row): a load under a branch
   // makes the compiler's wait counting fall back to waiting for every load.
@@ -287,22 +306,22 @@ __device__ __forceinline__ void pf_mainloop(
   uint4* const my0 = &lds[0][drow * kLdsRowU4 + dpart * (KPT / 8)];
   uint4* const my1 = &lds[1][drow * kLdsRowU4 + dpart * (KPT / 8)];
 
-  // prologue: activations of slabs 0 .. R-2, then codes of slabs 0 .. R-1
+  // prologue: codes of slabs 0 .. RW-1, activations of slabs 0 .. R-2, weights of slab 0
+#pragma unroll
+  for (int r = 0; r < RW; ++r) load_codes(r, cr[r]);
 #pragma unroll
   for (int r = 0; r < R - 1; ++r) load_b(clampslab(r), xr[r]);
-#pragma unroll
-  for (int r = 0; r < R; ++r) load_codes(r, cr[r]);
   cr[0].to_lds(my0);
-  load_codes(R, cr[0]);
+  load_codes(RW, cr[0]);
 
-  for (int s0 = 0; s0 < nslab; s0 += R) {
+  for (int s0 = 0; s0 < nslab; s0 += RW) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RW; ++r) {
       const int s = s0 + r;
       if (s >= nslab) break;
       __syncthreads();  // weights of slab s are in LDS; slab s - 1's buffer is free
       load_b(clampslab(s + R - 1), xr[(r + R - 1) % R]);
-      const uint4* tile = lds[s & 1];
+      const uint4* tile = lds[r & 1];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         uint4 a[8];
@@ -315,27 +334,29 @@ __device__ __forceinline__ void pf_mainloop(
 #pragma unroll
             for (int rf = 0; rf < 8; ++rf)
 #pragma unroll
-              for (int b = 0; b < NB; ++b) acc[f][rf] = mfma_bf16(a[rf], xr[r][b][f][j], acc[f][rf]);
+              for (int b = 0; b < NB; ++b)
+                acc[f][rf] = mfma_bf16(a[rf], xr[r % R][b][f][j], acc[f][rf]);
           }
         }
       }
       // weights of slab s + 1 (its buffer was last read in iteration s - 1), then
-      // the codes of slab s + 1 + R into the freed ring slot
-      const int c = (r + 1) % R;
-      cr[c].to_lds((s & 1) ? my0 : my1);
-      load_codes(s + 1 + R, cr[c]);
+      // the codes of slab s + 1 + RW into the freed ring slot
+      const int c = (r + 1) % RW;
+      cr[c].to_lds((r & 1) ? my0 : my1);
+      load_codes(s + 1 + RW, cr[c]);
     }
   }
 }
 
 }  // namespace
 
-constexpr int kGateUpWaves = 4;
-constexpr int kDownWaves = 8;  // twice the MFMAs per A read (hi and lo): 8 waves stay within LDS bandwidth
+// Blocks of 4 waves run two per CU, blocks of 8 waves one per CU.
+template <int W>
+constexpr int kBlocksPerCu = W == 4 ? 2 : 1;
 
-__global__ __launch_bounds__(kGateUpWaves * kWave, 2) void pf_gateup_kernel(PrefillParams p) {
-  constexpr int W = kGateUpWaves;
-  using G = Geometry<W>;
+template <int W, int FR, int RW>
+__global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_gateup_kernel(PrefillParams p) {
+  using G = Geometry<W, FR>;
   __shared__ uint4 lds[2][kPfRows * kLdsRowU4];
   int u, tile;
   unit_tile(p.ntiles1, &u, &tile);
@@ -357,27 +378,27 @@ __global__ __launch_bounds__(kGateUpWaves * kWave, 2) void pf_gateup_kernel(Pref
   const uint8_t* ws = bank.w13s + rowg * (H / 16) + dpart * (G::kKpt / 16);
 
   // B rows: this lane's tokens; columns past the unit's count repeat its last token
-  const int nfr = wave_fragments<W>(un.count, wave);
-  const uint16_t* brow[1][G::kFrags];
+  const int nfr = wave_fragments<W, FR>(un.count, wave);
+  const uint16_t* brow[1][FR];
 #pragma unroll
-  for (int f = 0; f < G::kFrags; ++f) {
+  for (int f = 0; f < FR; ++f) {
     const int m = min(frag_token<W>(wave, f, lane), un.count - 1);
     const int t = un.bank ? un.start + m : p.sorted[un.start + m] / p.k;
     brow[0][f] = p.x + static_cast<size_t>(t) * H + (lane >> 4) * 16;
   }
 
-  f32x4 acc[G::kFrags][8];
+  f32x4 acc[FR][8];
 #pragma unroll
-  for (int f = 0; f < G::kFrags; ++f)
+  for (int f = 0; f < FR; ++f)
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  pf_mainloop<W, 1, 2>(wc, 32, ws, 4, brow, nfr, H / kPfSlab, lds, drow, dpart, lane, acc);
+  pf_mainloop<W, FR, 1, 2, RW>(wc, 32, ws, 4, brow, nfr, H / kPfSlab, lds, drow, dpart, lane, acc);
 
   // epilogue: rows r < 4 are gate columns n0 + 16 r + 4 (lane / 16) + jj, r + 4 the
   // matching up columns
   const float gg = bank.gsc[un.expert * 3 + 0], gu = bank.gsc[un.expert * 3 + 1];
 #pragma unroll
-  for (int f = 0; f < G::kFrags; ++f) {
+  for (int f = 0; f < FR; ++f) {
     const int m = frag_token<W>(wave, f, lane);
     if (f >= nfr || m >= un.count) continue;
     const size_t row = un.bank ? static_cast<size_t>(p.P) + un.start + m
@@ -407,9 +428,9 @@ __global__ __launch_bounds__(kGateUpWaves * kWave, 2) void pf_gateup_kernel(Pref
   }
 }
 
-__global__ __launch_bounds__(kDownWaves * kWave, 1) void pf_down_kernel(PrefillParams p) {
-  constexpr int W = kDownWaves;
-  using G = Geometry<W>;
+template <int W, int FR, int RW>
+__global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(PrefillParams p) {
+  using G = Geometry<W, FR>;
   __shared__ uint4 lds[2][kPfRows * kLdsRowU4];
   int u, tile;
   unit_tile(p.ntiles2, &u, &tile);
@@ -431,10 +452,10 @@ __global__ __launch_bounds__(kDownWaves * kWave, 1) void pf_down_kernel(PrefillP
   const uint8_t* wc = bank.w2 + (chunk0 * H + h0 + drow) * 16 + (kofs & 31) / 2;
   const uint8_t* ws = bank.w2s + (chunk0 * H + h0 + drow) * 2 + (kofs & 31) / 16;
 
-  const int nfr = wave_fragments<W>(un.count, wave);
-  const uint16_t* brow[2][G::kFrags];
+  const int nfr = wave_fragments<W, FR>(un.count, wave);
+  const uint16_t* brow[2][FR];
 #pragma unroll
-  for (int f = 0; f < G::kFrags; ++f) {
+  for (int f = 0; f < FR; ++f) {
     const int m = min(frag_token<W>(wave, f, lane), un.count - 1);
     const size_t row = un.bank ? static_cast<size_t>(p.P) + un.start + m
                                : static_cast<size_t>(un.start) + m;
@@ -442,18 +463,18 @@ __global__ __launch_bounds__(kDownWaves * kWave, 1) void pf_down_kernel(PrefillP
     brow[1][f] = p.hlo + row * p.Imax + (lane >> 4) * 16;
   }
 
-  f32x4 acc[G::kFrags][8];
+  f32x4 acc[FR][8];
 #pragma unroll
-  for (int f = 0; f < G::kFrags; ++f)
+  for (int f = 0; f < FR; ++f)
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  pf_mainloop<W, 2, 2>(wc, static_cast<size_t>(2) * H * 16, ws, static_cast<size_t>(2) * H * 2,
+  pf_mainloop<W, FR, 2, 2, RW>(wc, static_cast<size_t>(2) * H * 16, ws, static_cast<size_t>(2) * H * 2,
                        brow, nfr, I / kPfSlab, lds, drow, dpart, lane, acc);
 
   // epilogue: output rows h0 + 16 r + 4 (lane / 16) + jj of token m
   const float gd = bank.gsc[un.expert * 3 + 2];
 #pragma unroll
-  for (int f = 0; f < G::kFrags; ++f) {
+  for (int f = 0; f < FR; ++f) {
     const int m = frag_token<W>(wave, f, lane);
     if (f >= nfr || m >= un.count) continue;
     int t, slot;
@@ -512,9 +533,12 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PrefillParams p) {
 
 // ------------------------------------------------------------ launchers --
 
+int prefill_unit_tokens(int T) { return T <= kSmallUnitTokens ? kSmallUnitTokens : kPfUnitTokens; }
+
 int prefill_max_units(int E, int T, int k, bool shared) {
   const long long P = static_cast<long long>(T) * k;
-  long long n = E + P / kPfUnitTokens + (shared ? (T + kPfUnitTokens - 1) / kPfUnitTokens : 0);
+  const int ut = prefill_unit_tokens(T);
+  long long n = E + P / ut + (shared ? (T + ut - 1) / ut : 0);
   return static_cast<int>(n);
 }
 
@@ -528,17 +552,28 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
   const int nblk = prefill_group_blocks(p.T, p.k);
   const int maxu = prefill_max_units(p.E, p.T, p.k, p.shared.inter > 0);
   const int ugroups = (maxu + 7) / 8;
+  p.unit_tokens = prefill_unit_tokens(p.T);
   p.ntiles1 = p.Imax / 64;
   p.ntiles2 = p.H / kPfRows;
-  if (nblk > 0) {
+  if (p.P <= kGroupOneBlockPairs) {
+    pf_group_one_block_kernel<<<1, kMaxExperts, 0, s>>>(p);
+  } else {
     pf_hist_kernel<<<nblk, 256, 0, s>>>(p);
+    pf_scan_kernel<<<1, kMaxExperts, 0, s>>>(p);
+    pf_scatter_kernel<<<(p.P + 255) / 256, 256, 0, s>>>(p);
   }
-  pf_scan_kernel<<<1, kMaxExperts, 0, s>>>(p, nblk);
-  if (nblk > 0) {
-    pf_scatter_kernel<<<nblk, kWave, 0, s>>>(p);
+  const unsigned g1 = ugroups * 8 * p.ntiles1, g2 = ugroups * 8 * p.ntiles2;
+  if (p.unit_tokens == kPfUnitTokens) {
+    static_assert(Geometry<4, 4>::kUnitTokens == kPfUnitTokens, "unit size");
+    static_assert(Geometry<8, 2>::kUnitTokens == kPfUnitTokens, "unit size");
+    pf_gateup_kernel<4, 4, 2><<<g1, 4 * kWave, 0, s>>>(p);
+    pf_down_kernel<8, 2, 4><<<g2, 8 * kWave, 0, s>>>(p);
+  } else {
+    // few tokens per expert: the weight stream dominates, so the codes run 8 slabs ahead
+    static_assert(Geometry<4, 1>::kUnitTokens == kSmallUnitTokens, "unit size");
+    pf_gateup_kernel<4, 1, 8><<<g1, 4 * kWave, 0, s>>>(p);
+    pf_down_kernel<4, 1, 8><<<g2, 4 * kWave, 0, s>>>(p);
   }
-  pf_gateup_kernel<<<ugroups * 8 * p.ntiles1, kGateUpWaves * kWave, 0, s>>>(p);
-  pf_down_kernel<<<ugroups * 8 * p.ntiles2, kDownWaves * kWave, 0, s>>>(p);
   const size_t n4 = static_cast<size_t>(p.T) * (p.H / 4);
   pf_combine_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, s>>>(p);
   return hipGetLastError();

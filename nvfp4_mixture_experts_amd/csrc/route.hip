@@ -12,8 +12,9 @@
 
 namespace ftmoe {
 
-constexpr int kRouteWaves = 4;   // one expert row per wave
-constexpr int kRouteTokTile = 64;
+constexpr int kRouteWaves = 4;     // one expert row per wave
+constexpr int kRouteMaxTokTile = 64;
+constexpr int kRouteTargetWaves = 2048;  // enough waves to fill 256 CUs several times
 
 // Top-k of one token by one wave (wave_topk), written in rank order.
 template <class Load>
@@ -46,16 +47,9 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_logits_kernel(RouteP
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x * kRouteWaves + wave;
-  const int t0 = blockIdx.y * kRouteTokTile;
-  const int t1 = min(p.T, t0 + kRouteTokTile);
+  const int t0 = blockIdx.y * p.tok_tile;
+  const int t1 = min(p.T, t0 + p.tok_tile);
   const int H = p.H;
-
-  // clear the down-projection counters of this call (their users run later on the stream)
-  {
-    const int nthreads = gridDim.x * gridDim.y * blockDim.x;
-    const int tid = (blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-    for (int i = tid; i < p.nzero; i += nthreads) p.zero[i] = 0u;
-  }
 
   if (row < p.E) {
     const float* __restrict__ wrow = p.wr + static_cast<size_t>(row) * H;
@@ -142,10 +136,18 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void topk_kernel(RouteParams p)
                  p.w_copy ? p.w_copy + static_cast<size_t>(t) * p.k : nullptr);
 }
 
-hipError_t launch_route(const RouteParams& p, bool fuse_topk, hipStream_t s) {
+int route_fused_topk_tokens() { return kRouteWaves; }
+
+hipError_t launch_route(const RouteParams& p0, bool fuse_topk, hipStream_t s) {
+  RouteParams p = p0;
   const int rows = p.E + (p.shared_gate ? 1 : 0);
   const int gx = rows > 0 ? (rows + kRouteWaves - 1) / kRouteWaves : 1;
-  dim3 grid(gx, (p.T + kRouteTokTile - 1) / kRouteTokTile);
+  // tokens per wave: as few as keep about kRouteTargetWaves waves busy (each
+  // wave keeps its row in registers across its tokens)
+  const long long work = static_cast<long long>(rows > 0 ? rows : 1) * p.T;
+  p.tok_tile = static_cast<int>((work + kRouteTargetWaves - 1) / kRouteTargetWaves);
+  p.tok_tile = p.tok_tile < 1 ? 1 : (p.tok_tile > kRouteMaxTokTile ? kRouteMaxTokTile : p.tok_tile);
+  dim3 grid(gx, (p.T + p.tok_tile - 1) / p.tok_tile);
   dim3 block(kRouteWaves * kWave);
   const int fuse = fuse_topk ? 1 : 0;
   switch (p.H / (4 * kWave)) {

@@ -171,6 +171,8 @@ def test_route_ties_go_to_lowest_index(gpu):
     ("decode_e288_top8", 1, None),
     ("decode_e512_top10_shared", 1, None),
     ("batched_decode_t32_hot64", 32, [0, 9, 22, 31]),
+    ("batched_decode_t32_hot64", 7, [0, 6]),     # largest count on the fused kernel
+    ("batched_decode_t32_hot64", 8, [0, 7]),     # smallest count on the grouped path
     ("tiny_e8_top2", 64, [0, 63]),
 ])
 def test_decode_matches_oracle(gpu, name, tokens, sample):
@@ -219,13 +221,15 @@ def test_decode_shapes_outside_the_workloads(gpu):
     assert_output_close(gpu.bf16_bits(y), ref["y"], "odd shapes")
 
 
-def test_decode_is_deterministic(gpu):
+@pytest.mark.parametrize("tokens", [4, 16])   # fused kernel, grouped path
+def test_decode_is_deterministic(gpu, tokens):
     """Same inputs -> same bits, across workspace addresses and streams."""
     from nvfp4_mixture_experts_amd import ftmoe
     name = "decode_e512_top10_shared"
     dl = dev_layer(gpu, name)
-    x = gpu.tokens_to_device(synth.make_tokens(synth.WORKLOADS[name], tokens=4, stream="det"))
-    n = ftmoe.ft_moe_workspace_bytes(dl.desc, 4, ftmoe.PATH_DECODE)
+    x = gpu.tokens_to_device(synth.make_tokens(synth.WORKLOADS[name], tokens=tokens,
+                                               stream="det"))
+    n = ftmoe.ft_moe_workspace_bytes(dl.desc, tokens, ftmoe.PATH_DECODE)
     span = (n + 255) // 256 * 256 + 1024
     big = torch.zeros(3 * span, dtype=torch.uint8, device="cuda")
     # disjoint workspaces at different offsets; calls ordered (a workspace is never
@@ -243,13 +247,15 @@ def test_decode_is_deterministic(gpu):
     assert torch.equal(y0.view(torch.int16), y2.view(torch.int16))
 
 
-def test_decode_graph_replays_match_eager(gpu):
+@pytest.mark.parametrize("tokens", [1, 12])   # fused kernel, grouped path
+def test_decode_graph_replays_match_eager(gpu, tokens):
     from nvfp4_mixture_experts_amd import ftmoe
     name = "decode_e288_top8"
     w = synth.WORKLOADS[name]
     dl = dev_layer(gpu, name)
-    xs = [gpu.tokens_to_device(synth.make_tokens(w, tokens=1, stream=f"g{i}")) for i in range(3)]
-    ws = ftmoe.alloc_workspace(dl.desc, 1, ftmoe.PATH_DECODE)
+    xs = [gpu.tokens_to_device(synth.make_tokens(w, tokens=tokens, stream=f"g{i}"))
+          for i in range(3)]
+    ws = ftmoe.alloc_workspace(dl.desc, tokens, ftmoe.PATH_DECODE)
     eager = []
     for x in xs:
         y, _, _ = gpu.decode(dl, x, workspace=ws)
@@ -257,8 +263,8 @@ def test_decode_graph_replays_match_eager(gpu):
     torch.cuda.synchronize()
     xin = xs[0].clone()
     yout = torch.empty_like(eager[0])
-    ids = torch.empty((1, w.top_k), dtype=torch.int32, device="cuda")
-    wt = torch.empty((1, w.top_k), dtype=torch.float32, device="cuda")
+    ids = torch.empty((tokens, w.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((tokens, w.top_k), dtype=torch.float32, device="cuda")
     s = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
@@ -308,3 +314,25 @@ def test_prefill_uses_given_routes(gpu):
     torch.cuda.synchronize()
     ref = oracle.moe_layer(L, x, ids=ids, weights=wts)
     assert_output_close(gpu.bf16_bits(y), ref["y"], "prefill given routes")
+
+
+@pytest.mark.parametrize("tokens", [24, 300])   # grouped decode, prefill
+def test_token_order_does_not_change_results(gpu, tokens):
+    """Permuting the tokens permutes the outputs bit for bit: where a pair lands in
+    its expert's group (which the grouping leaves unspecified) changes nothing."""
+    name = "decode_e512_top10_shared"
+    w = synth.WORKLOADS[name]
+    dl = dev_layer(gpu, name)
+    x = synth.make_tokens(w, tokens=tokens, stream="perm")
+    perm = np.random.default_rng(9).permutation(tokens)
+    xd, xpd = gpu.tokens_to_device(x), gpu.tokens_to_device(x[perm])
+    if tokens <= 64:
+        y, _, _ = gpu.decode(dl, xd)
+        yp, _, _ = gpu.decode(dl, xpd)
+    else:
+        ids, wt = gpu.route(dl, xd)
+        y = gpu.prefill(dl, xd, ids, wt)
+        idsp, wtp = gpu.route(dl, xpd)
+        yp = gpu.prefill(dl, xpd, idsp, wtp)
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu.bf16_bits(y)[perm], gpu.bf16_bits(yp))
