@@ -306,19 +306,34 @@ __device__ __forceinline__ void pf_mainloop(
   uint4* const my0 = &lds[0][drow * kLdsRowU4 + dpart * (KPT / 8)];
   uint4* const my1 = &lds[1][drow * kLdsRowU4 + dpart * (KPT / 8)];
 
-  // prologue: codes of slabs 0 .. RW-1, activations of slabs 0 .. R-2, weights of slab 0
+  // prologue: codes of slabs 0 .. RW-1, activations of slabs 0 .. R-2, weights of
+  // slab 0.  The loads keep this order (scheduling barriers): the compiler's wait
+  // counts at the loop head take the worse of this path and the loop's own, so a
+  // late-issued early slab here would make every pass of the loop wait for all
+  // loads in flight.
 #pragma unroll
-  for (int r = 0; r < RW; ++r) load_codes(r, cr[r]);
+  for (int r = 0; r < RW; ++r) {
+    load_codes(r, cr[r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
-  for (int r = 0; r < R - 1; ++r) load_b(clampslab(r), xr[r]);
+  for (int r = 0; r < R - 1; ++r) {
+    load_b(clampslab(r), xr[r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   cr[0].to_lds(my0);
   load_codes(RW, cr[0]);
+  __builtin_amdgcn_sched_barrier(0);
 
+  // Whole passes of RW slabs; in the last pass the slabs past the end repeat the
+  // last slab's loads and dequantisation but add nothing.  (An early exit inside
+  // the unrolled pass would give the compiler paths into the loop head with fewer
+  // loads in flight, and it would then wait for every load at each pass.)
   for (int s0 = 0; s0 < nslab; s0 += RW) {
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       const int s = s0 + r;
-      if (s >= nslab) break;
+      const bool live = s < nslab;
       __syncthreads();  // weights of slab s are in LDS; slab s - 1's buffer is free
       load_b(clampslab(s + R - 1), xr[(r + R - 1) % R]);
       const uint4* tile = lds[r & 1];
@@ -330,7 +345,7 @@ __device__ __forceinline__ void pf_mainloop(
           a[rf] = tile[(rf * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + j];
 #pragma unroll
         for (int f = 0; f < FR; ++f) {
-          if (f < nfr) {
+          if (live && f < nfr) {
 #pragma unroll
             for (int rf = 0; rf < 8; ++rf)
 #pragma unroll
@@ -354,7 +369,7 @@ __device__ __forceinline__ void pf_mainloop(
 template <int W>
 constexpr int kBlocksPerCu = W == 4 ? 2 : 1;
 
-template <int W, int FR, int RW>
+template <int W, int FR, int R, int RW>
 __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_gateup_kernel(PrefillParams p) {
   using G = Geometry<W, FR>;
   __shared__ uint4 lds[2][kPfRows * kLdsRowU4];
@@ -392,7 +407,7 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_gateup_kernel(P
   for (int f = 0; f < FR; ++f)
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  pf_mainloop<W, FR, 1, 2, RW>(wc, 32, ws, 4, brow, nfr, H / kPfSlab, lds, drow, dpart, lane, acc);
+  pf_mainloop<W, FR, 1, R, RW>(wc, 32, ws, 4, brow, nfr, H / kPfSlab, lds, drow, dpart, lane, acc);
 
   // epilogue: rows r < 4 are gate columns n0 + 16 r + 4 (lane / 16) + jj, r + 4 the
   // matching up columns
@@ -428,7 +443,7 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_gateup_kernel(P
   }
 }
 
-template <int W, int FR, int RW>
+template <int W, int FR, int R, int RW>
 __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(PrefillParams p) {
   using G = Geometry<W, FR>;
   __shared__ uint4 lds[2][kPfRows * kLdsRowU4];
@@ -468,7 +483,7 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(Pre
   for (int f = 0; f < FR; ++f)
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  pf_mainloop<W, FR, 2, 2, RW>(wc, static_cast<size_t>(2) * H * 16, ws, static_cast<size_t>(2) * H * 2,
+  pf_mainloop<W, FR, 2, R, RW>(wc, static_cast<size_t>(2) * H * 16, ws, static_cast<size_t>(2) * H * 2,
                        brow, nfr, I / kPfSlab, lds, drow, dpart, lane, acc);
 
   // epilogue: output rows h0 + 16 r + 4 (lane / 16) + jj of token m
@@ -536,9 +551,10 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PrefillParams p) {
 int prefill_unit_tokens(int T) { return T <= kSmallUnitTokens ? kSmallUnitTokens : kPfUnitTokens; }
 
 int prefill_max_units(int E, int T, int k, bool shared) {
+  // sum over experts of ceil(n_e / ut) <= (experts with a pair) + P / ut
   const long long P = static_cast<long long>(T) * k;
   const int ut = prefill_unit_tokens(T);
-  long long n = E + P / ut + (shared ? (T + ut - 1) / ut : 0);
+  long long n = (P < E ? P : E) + P / ut + (shared ? (T + ut - 1) / ut : 0);
   return static_cast<int>(n);
 }
 
@@ -566,13 +582,14 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
   if (p.unit_tokens == kPfUnitTokens) {
     static_assert(Geometry<4, 4>::kUnitTokens == kPfUnitTokens, "unit size");
     static_assert(Geometry<8, 2>::kUnitTokens == kPfUnitTokens, "unit size");
-    pf_gateup_kernel<4, 4, 2><<<g1, 4 * kWave, 0, s>>>(p);
-    pf_down_kernel<8, 2, 4><<<g2, 8 * kWave, 0, s>>>(p);
+    pf_gateup_kernel<4, 4, 2, 2><<<g1, 4 * kWave, 0, s>>>(p);
+    pf_down_kernel<8, 2, 2, 4><<<g2, 8 * kWave, 0, s>>>(p);
   } else {
-    // few tokens per expert: the weight stream dominates, so the codes run 8 slabs ahead
+    // few tokens per expert: the weight stream dominates; codes run 8 slabs ahead,
+    // token rows 7 (gate|up) or 3 (down, whose (hi, lo) rows are twice as large)
     static_assert(Geometry<4, 1>::kUnitTokens == kSmallUnitTokens, "unit size");
-    pf_gateup_kernel<4, 1, 8><<<g1, 4 * kWave, 0, s>>>(p);
-    pf_down_kernel<4, 1, 8><<<g2, 4 * kWave, 0, s>>>(p);
+    pf_gateup_kernel<4, 1, 8, 8><<<g1, 4 * kWave, 0, s>>>(p);
+    pf_down_kernel<4, 1, 4, 8><<<g2, 4 * kWave, 0, s>>>(p);
   }
   const size_t n4 = static_cast<size_t>(p.T) * (p.H / 4);
   pf_combine_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, s>>>(p);
