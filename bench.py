@@ -108,6 +108,105 @@ def cpu_baseline(w, seconds: float = 12.0) -> dict:
                       f"nproc {os.cpu_count()}"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def prefill_flops(w, T: int) -> float:
+    """Useful expert FLOP of one prefill chunk: every routed (token, slot) pair and
+    every token of the shared expert runs gate|up (2I x H) and down (H x I)."""
+    per_routed = 2.0 * (2 * w.inter * w.hidden + w.hidden * w.inter)
+    per_shared = 2.0 * (2 * w.shared_inter * w.hidden + w.hidden * w.shared_inter)
+    return T * w.top_k * per_routed + T * per_shared
+
+
+def cpu_baseline_prefill(w, seconds: float) -> dict:
+    import oracle
+    from nvfp4_mixture_experts_amd import synth
+    layer = synth.make_layer(w)
+    x = synth.make_tokens(w, tokens=64, stream="cpu_baseline")
+    oracle.moe_layer(layer, x[:1])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.moe_layer(layer, x[n % 64:n % 64 + 1])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} tokens of {w.name} (routing, experts, shared expert) one at a time on "
+                      f"instance 0, {el:.1f} s, single-threaded C oracle (fp64), nproc {os.cpu_count()}"}
+
+
+def run_prefill(args, w) -> int:
+    """A prefill chunk: ft_moe_route then ft_moe_nvfp4_prefill over w.tokens tokens,
+    cycling over layer instances; reports tokens/s and MFMA utilisation of the
+    useful expert FLOP against the dense bf16 peak (whole call, router included)."""
+    import torch
+    from nvfp4_mixture_experts_amd import device, ftmoe, synth
+    dev = torch.device("cuda:0")
+    T = w.tokens
+    L = args.instances or 2
+    layers, xs = [], []
+    for l in range(L):
+        d = synth.make_layer_device(w, l, dev)
+        layers.append(device.upload_canonical(w, d["w_router"], d["bias"], d["routed"], d["shared"],
+                                              d["shared_gate"], dev))
+        del d
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed + 7919 * l + 1)
+        xs.append(torch.randn((T, w.hidden), generator=g, device=dev).to(torch.bfloat16))
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    desc = layers[0].desc
+    wsr = ftmoe.alloc_workspace(desc, T, ftmoe.PATH_ROUTE, dev)
+    wsp = ftmoe.alloc_workspace(desc, T, ftmoe.PATH_PREFILL, dev)
+    y = torch.empty((T, w.hidden), dtype=torch.bfloat16, device=dev)
+    ids = torch.empty((T, w.top_k), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, w.top_k), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        dl = layers[i % L]
+        ftmoe.ft_moe_route(desc, xs[i % L], dl.w_router, dl.bias, ids, wt, wsr, stream=stream)
+        ftmoe.ft_moe_nvfp4_prefill(desc, xs[i % L], ids, wt, dl.routed, dl.shared, dl.shared_gate,
+                                   y, wsp, stream=stream)
+
+    warm = max(min(args.warmup, 8), L)
+    for i in range(warm):
+        call(i)
+    torch.cuda.synchronize()
+    steps = max(L, min(args.steps, 40))
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    flops = prefill_flops(w, T)
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "NVFP4 MoE prefill chunk: tokens/s + MFMA utilisation of useful expert FLOP",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "experts": w.num_experts, "hidden": w.hidden,
+                   "inter": w.inter, "top_k": w.top_k, "tokens": T,
+                   "shared_inter": w.shared_inter, "layer_instances": L},
+        "roofline": {"kernel": "route + grouped GEMMs (whole call)", "bound": "mfma",
+                     "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "useful_flop_per_call": flops},
+        "launch": "eager, one route and one prefill call per step",
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,10 +232,9 @@ def main() -> int:
     from nvfp4_mixture_experts_amd import device, ftmoe, synth
 
     w = synth.WORKLOADS[args.workload]
-    if w.tokens > 64:
-        print(f"{w.name} is not a decode workload", file=sys.stderr)
-        return 2
     ftmoe.ft_init(0)
+    if w.tokens > 64:
+        return run_prefill(args, w)
     dev = torch.device("cuda:0")
 
     # ---- layer instances, generated and repacked on the device
@@ -224,7 +322,10 @@ def main() -> int:
     bytes_per_call = float(np.mean([algorithmic_bytes(w, ids_np[l]) for l in range(L)]))
     gbps = bytes_per_call / (ms_per_step * 1e-3) / 1e9
     touched = bytes_per_call * L
-    traffic = measured_traffic(w.name)
+    grouped = w.tokens >= ftmoe.GROUPED_DECODE_MIN_TOKENS
+    traffic = None if grouped else measured_traffic(w.name)
+    kernel = ("grouped decode path: route, grouping, gate|up, down, combine (whole call)"
+              if grouped else DECODE_KERNEL)
 
     out = {
         "metric": METRIC,
@@ -245,7 +346,7 @@ def main() -> int:
                    "bytes_touched_per_cycle": int(touched)},
         "achieved_gbps": round(gbps, 1),
         "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"kernel": DECODE_KERNEL, "bound": "hbm",
+        "roofline": {"kernel": kernel, "bound": "hbm",
                      "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else int(round(traffic["bytes"])),

@@ -23,6 +23,9 @@ FT_EUNSUPPORTED = -2
 FT_EWORKSPACE = -3
 FT_EHIP = -4
 
+# Decode calls of at least this many tokens take the grouped path inside
+# ft_moe_nvfp4_decode (the library's kGroupedDecodeMinTokens; informational).
+GROUPED_DECODE_MIN_TOKENS = 8
 PATH_ROUTE, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 
 
