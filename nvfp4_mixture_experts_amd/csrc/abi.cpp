@@ -61,6 +61,8 @@ constexpr int kMaxDecodeTokens = 64;
 // gate|up and down grouped GEMMs, combine), where every selected expert's weights
 // are read once for all of its tokens; fewer tokens run the fused one-launch kernel.
 constexpr int kGroupedDecodeMinTokens = 8;
+// Router calls of at least this many tokens compute the logits on the MFMA units.
+constexpr int kRouteMfmaMinTokens = 1024;
 constexpr int kRowGroup = 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -234,10 +236,26 @@ ft_status run_route(const ft_moe_desc* desc, int T, const uint16_t* x, const flo
   p.ids_copy = ids_copy;
   p.w_copy = w_copy;
   p.counter = counter;
+  hipError_t e;
+  if (T >= kRouteMfmaMinTokens) {
+    // many tokens: logits as an fp64 MFMA product, the shared gate by the row
+    // kernel (as its only row), then top-k with one wave per token
+    e = launch_route_mfma(p, s);
+    if (e != hipSuccess) return hip_fail(e, "route kernel");
+    if (gamma) {
+      RouteParams q = p;
+      q.E = 0;
+      e = launch_route(q, false, s);
+      if (e != hipSuccess) return hip_fail(e, "shared gate kernel");
+    }
+    e = launch_topk(p, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k kernel");
+    return FT_OK;
+  }
   // the last block to finish selects the experts when it has a wave per token;
   // otherwise a top-k kernel with one wave per token follows
   const bool fuse = T <= route_fused_topk_tokens();
-  hipError_t e = launch_route(p, fuse, s);
+  e = launch_route(p, fuse, s);
   if (e != hipSuccess) return hip_fail(e, "route kernel");
   if (!fuse) {
     e = launch_topk(p, s);

@@ -114,6 +114,8 @@ int fused_block_threads();
 hipError_t launch_route(const RouteParams& p, bool fuse_topk, hipStream_t s);
 int route_fused_topk_tokens();  // the fused top-k handles at most this many tokens
 hipError_t launch_topk(const RouteParams& p, hipStream_t s);
+// logits only (no shared gate, no top-k), as an fp64 MFMA product; H % 64 == 0
+hipError_t launch_route_mfma(const RouteParams& p, hipStream_t s);
 // Lanes per row and chunks per lane of the decode gate|up GEMV for hidden size H
 // (supported when lpr > 0 and 1 <= cpl <= 4).
 void gateup_geometry(int H, int* lpr, int* cpl);

@@ -363,16 +363,117 @@ __device__ __forceinline__ void pf_mainloop(
   }
 }
 
+// The gate|up K loop.  Row-major weights are fetched per super-slab of 256 K
+// elements: 8 lanes read the 128 code bytes of one row (one whole cache line), so
+// a wave load covers 8 rows in full lines, and the HBM stream is line-sized runs
+// instead of 32-byte pieces.  Each of the 256 threads fetches 4 such pieces (rows
+// (tid >> 3) + 32 i, K segment tid & 7), RS super-slabs ahead in a register ring,
+// and dequantises them into the four 64-K slab tiles of the super-slab in LDS.
+// Token rows run R - 1 slabs ahead (R divides 4, so every ring slot is a
+// compile-time constant in the unrolled loop).
+constexpr int kSuperSlab = 4 * kPfSlab;  // 256 K elements: 128 code bytes per row
+
+template <int FR, int R, int RS>
+__device__ __forceinline__ void pf_mainloop_rows(
+    const uint8_t* wc, const uint8_t* ws, const long long (&rowoff)[4], int H,
+    const uint16_t* const (&brow)[1][FR], int nfr, int nslab,
+    uint4 (*tiles)[kPfRows * kLdsRowU4], int lane, f32x4 (&acc)[FR][8]) {
+  static_assert(4 % R == 0, "token ring depth divides the slabs of a super-slab");
+  const int tid = threadIdx.x;
+  const int seg = tid & 7;  // 32-K segment of the super-slab
+  const int nss = nslab / 4;
+  uint4 xr[R][FR][2];
+  uint4 qr[RS][4];
+  uint32_t sr[RS][4];
+  auto clampslab = [&](int s) { return s < nslab ? s : nslab - 1; };
+  auto clampss = [&](int ss) { return ss < nss ? ss : nss - 1; };
+  // every load unconditional (see pf_mainloop)
+  auto load_b = [&](int s, uint4 (&dst)[FR][2]) {
+#pragma unroll
+    for (int f = 0; f < FR; ++f) {
+      dst[f][0] = ld16(brow[0][f] + s * kPfSlab);
+      dst[f][1] = ld16(brow[0][f] + s * kPfSlab + 8);
+    }
+  };
+  auto load_w = [&](int ss, uint4 (&q)[4], uint32_t (&sc)[4]) {
+    const int c = clampss(ss);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q[i] = ld16(wc + rowoff[i] * (H / 2) + c * (kSuperSlab / 2));
+      sc[i] = *reinterpret_cast<const uint16_t*>(ws + rowoff[i] * (H / 16) + c * (kSuperSlab / 16));
+    }
+  };
+  auto dequant = [&](const uint4 (&q)[4], const uint32_t (&sc)[4]) {
+    uint4* const t = tiles[seg >> 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      uint4* dst = t + row * kLdsRowU4 + (seg & 1) * 4;
+      const float s0 = e4m3_byte_to_f32<0>(sc[i]), s1 = e4m3_byte_to_f32<1>(sc[i]);
+      dst[0] = dequant8_bf16(q[i].x, s0);
+      dst[1] = dequant8_bf16(q[i].y, s0);
+      dst[2] = dequant8_bf16(q[i].z, s1);
+      dst[3] = dequant8_bf16(q[i].w, s1);
+    }
+  };
+
+  // prologue: weights of super-slabs 0 .. RS-1, token rows of slabs 0 .. R-2, in
+  // this order (see pf_mainloop)
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    load_w(r, qr[r], sr[r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int r = 0; r < R - 1; ++r) {
+    load_b(clampslab(r), xr[r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  for (int ss0 = 0; ss0 < nss; ss0 += RS) {
+#pragma unroll
+    for (int rr = 0; rr < RS; ++rr) {
+      const int ss = ss0 + rr;
+      const bool live = ss < nss;  // the last pass may run past the end (see pf_mainloop)
+      __syncthreads();  // the previous super-slab's MFMAs are done with the tiles
+      dequant(qr[rr], sr[rr]);
+      load_w(ss + RS, qr[rr], sr[rr]);
+      __syncthreads();  // this super-slab's tiles are written
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = 4 * ss + j;
+        load_b(clampslab(s + R - 1), xr[(j + R - 1) % R]);
+        const uint4* tile = tiles[j];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          uint4 a[8];
+#pragma unroll
+          for (int rf = 0; rf < 8; ++rf)
+            a[rf] = tile[(rf * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + st];
+#pragma unroll
+          for (int f = 0; f < FR; ++f) {
+            if (live && f < nfr) {
+#pragma unroll
+              for (int rf = 0; rf < 8; ++rf)
+                acc[f][rf] = mfma_bf16(a[rf], xr[j % R][f][st], acc[f][rf]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // Blocks of 4 waves run two per CU, blocks of 8 waves one per CU.
 template <int W>
 constexpr int kBlocksPerCu = W == 4 ? 2 : 1;
 
-template <int W, int FR, int R, int RW>
-__global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_gateup_kernel(PrefillParams p) {
-  using G = Geometry<W, FR>;
-  __shared__ uint4 lds[2][kPfRows * kLdsRowU4];
+template <int FR, int R, int RS, int BPC>
+__global__ __launch_bounds__(256, BPC) void pf_gateup_kernel(PrefillParams p) {
+  constexpr int W = 4;
+  __shared__ uint4 tiles[4][kPfRows * kLdsRowU4];
   int u, tile;
   unit_tile(p.ntiles1, &u, &tile);
   if (u >= *p.nunits) return;
@@ -385,12 +486,13 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_gateup_kernel(P
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // dequantisation: row drow of the tile (0..63 gate, 64..127 up), part dpart of a slab
-  const int drow = tid / G::kTpr, dpart = tid % G::kTpr;
-  const int grow = drow < 64 ? n0 + drow : I + n0 + (drow - 64);
-  const size_t rowg = static_cast<size_t>(un.expert) * 2 * I + grow;
-  const uint8_t* wc = bank.w13 + rowg * (H / 2) + dpart * (G::kKpt / 2);
-  const uint8_t* ws = bank.w13s + rowg * (H / 16) + dpart * (G::kKpt / 16);
+  // weight fetch: tile rows (tid >> 3) + 32 i (gate rows n0 + (tid >> 3) + 32 i for
+  // i < 2, up rows I + n0 + (tid >> 3) + 32 (i - 2)), segment tid & 7; the row
+  // offsets of the four pieces are the same for every thread
+  const size_t row0 = static_cast<size_t>(un.expert) * 2 * I + n0 + (tid >> 3);
+  const uint8_t* wc = bank.w13 + row0 * (H / 2) + (tid & 7) * 16;
+  const uint8_t* ws = bank.w13s + row0 * (H / 16) + (tid & 7) * 2;
+  const long long rowoff[4] = {0, 32, I, I + 32};
 
   // B rows: this lane's tokens; columns past the unit's count repeat its last token
   const int nfr = wave_fragments<W, FR>(un.count, wave);
@@ -407,7 +509,7 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_gateup_kernel(P
   for (int f = 0; f < FR; ++f)
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  pf_mainloop<W, FR, 1, R, RW>(wc, 32, ws, 4, brow, nfr, H / kPfSlab, lds, drow, dpart, lane, acc);
+  pf_mainloop_rows<FR, R, RS>(wc, ws, rowoff, H, brow, nfr, H / kPfSlab, tiles, lane, acc);
 
   // epilogue: rows r < 4 are gate columns n0 + 16 r + 4 (lane / 16) + jj, r + 4 the
   // matching up columns
@@ -582,13 +684,13 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
   if (p.unit_tokens == kPfUnitTokens) {
     static_assert(Geometry<4, 4>::kUnitTokens == kPfUnitTokens, "unit size");
     static_assert(Geometry<8, 2>::kUnitTokens == kPfUnitTokens, "unit size");
-    pf_gateup_kernel<4, 4, 2, 2><<<g1, 4 * kWave, 0, s>>>(p);
+    pf_gateup_kernel<4, 2, 1, 1><<<g1, 4 * kWave, 0, s>>>(p);
     pf_down_kernel<8, 2, 2, 4><<<g2, 8 * kWave, 0, s>>>(p);
   } else {
-    // few tokens per expert: the weight stream dominates; codes run 8 slabs ahead,
-    // token rows 7 (gate|up) or 3 (down, whose (hi, lo) rows are twice as large)
+    // few tokens per expert: the weight stream dominates; gate|up weights run 3
+    // super-slabs ahead, down codes 8 slabs ahead, token rows 3 slabs ahead
     static_assert(Geometry<4, 1>::kUnitTokens == kSmallUnitTokens, "unit size");
-    pf_gateup_kernel<4, 1, 8, 8><<<g1, 4 * kWave, 0, s>>>(p);
+    pf_gateup_kernel<1, 4, 3, 2><<<g1, 4 * kWave, 0, s>>>(p);
     pf_down_kernel<4, 1, 4, 8><<<g2, 4 * kWave, 0, s>>>(p);
   }
   const size_t n4 = static_cast<size_t>(p.T) * (p.H / 4);

@@ -136,6 +136,92 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void topk_kernel(RouteParams p)
                  p.w_copy ? p.w_copy + static_cast<size_t>(t) * p.k : nullptr);
 }
 
+// Many tokens: logits as an fp64 matrix product on the MFMA units
+// (v_mfma_f64_16x16x4f64).  A = router rows (16 experts x 4 K, lane l holding
+// expert l % 16 at K group l / 16), B = token rows (4 K x 16 tokens, lane l
+// holding token l % 16 at the same K group), C lane l holds experts l / 16 + 4 j,
+// j < 4, of token l % 16.  Every fp32 x bf16 product is exact in fp64 and the sum
+// is kept in fp64, then rounded once to fp32, as in the kernel above; only the
+// order of the fp64 additions differs.  Which K a lane group holds only has to
+// agree between A and B: in a 64-K block, group g holds K = 16 g + m in step m.
+// A wave computes 16 experts x 64 tokens; a block of 4 waves 64 experts x 64
+// tokens, so the 4 waves read the same token rows.
+constexpr int kRouteMmExperts = 64;  // per block
+constexpr int kRouteMmTokens = 64;   // per block (4 fragments of 16 per wave)
+
+typedef __attribute__((__vector_size__(4 * sizeof(double)))) double f64x4;
+
+__global__ __launch_bounds__(256) void route_mfma_kernel(RouteParams p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e0 = blockIdx.x * kRouteMmExperts + wave * 16;
+  const int t0 = blockIdx.y * kRouteMmTokens;
+  const int H = p.H;
+  const int g = lane >> 4, i = lane & 15;
+  // rows past the end repeat the last valid row (their results are not stored)
+  const float* wrow = p.wr + static_cast<size_t>(min(e0 + i, p.E - 1)) * H + 16 * g;
+  const uint16_t* xrow[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+    xrow[f] = p.x + static_cast<size_t>(min(t0 + 16 * f + i, p.T - 1)) * H + 16 * g;
+
+  f64x4 acc[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) acc[f] = f64x4{0.0, 0.0, 0.0, 0.0};
+  float4 wa[4];
+  uint4 xa[4][2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) wa[c] = *reinterpret_cast<const float4*>(wrow + k0 + 4 * c);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      xa[f][0] = *reinterpret_cast<const uint4*>(xrow[f] + k0);
+      xa[f][1] = *reinterpret_cast<const uint4*>(xrow[f] + k0 + 8);
+    }
+  };
+  load(0);
+  for (int k0 = 0; k0 < H; k0 += 64) {
+    float w[16];
+    uint32_t xw[4][8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      w[4 * c + 0] = wa[c].x;
+      w[4 * c + 1] = wa[c].y;
+      w[4 * c + 2] = wa[c].z;
+      w[4 * c + 3] = wa[c].w;
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      xw[f][0] = xa[f][0].x; xw[f][1] = xa[f][0].y; xw[f][2] = xa[f][0].z; xw[f][3] = xa[f][0].w;
+      xw[f][4] = xa[f][1].x; xw[f][5] = xa[f][1].y; xw[f][6] = xa[f][1].z; xw[f][7] = xa[f][1].w;
+    }
+    if (k0 + 64 < H) load(k0 + 64);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const double a = static_cast<double>(w[m]);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const uint32_t pair = xw[f][m >> 1];
+        const double b = static_cast<double>(bf16_bits_to_f32((m & 1) ? (pair >> 16) : (pair & 0xFFFFu)));
+        acc[f] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[f], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int t = t0 + 16 * f + i;
+    if (t >= p.T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + g + 4 * j;
+      if (e >= p.E) continue;
+      double v = acc[f][j];
+      if (p.bias) v += static_cast<double>(p.bias[e]);
+      p.logits[static_cast<size_t>(t) * p.E + e] = static_cast<float>(v);
+    }
+  }
+}
+
 int route_fused_topk_tokens() { return kRouteWaves; }
 
 hipError_t launch_route(const RouteParams& p0, bool fuse_topk, hipStream_t s) {
@@ -164,6 +250,13 @@ hipError_t launch_route(const RouteParams& p0, bool fuse_topk, hipStream_t s) {
 #undef FTMOE_ROUTE_CASE
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_mfma(const RouteParams& p, hipStream_t s) {
+  dim3 grid((p.E + kRouteMmExperts - 1) / kRouteMmExperts,
+            (p.T + kRouteMmTokens - 1) / kRouteMmTokens);
+  route_mfma_kernel<<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -127,7 +127,9 @@ def _check_routes(ids, w, ref_ids, ref_w, what):
                                          ("decode_e512_top10_shared", 1),
                                          ("batched_decode_t32_hot64", 32),
                                          ("decode_e512_top10_shared", 64),
-                                         ("decode_e512_top10_shared", 333)])
+                                         ("decode_e512_top10_shared", 333),
+                                         # MFMA router; experts not a multiple of 64
+                                         ("decode_e288_top8", 1100)])
 def test_route_matches_oracle(gpu, name, tokens):
     w = synth.WORKLOADS[name]
     dl = dev_layer(gpu, name)
