@@ -126,24 +126,34 @@ ft_status ft_nvfp4_repack(int32_t hidden, int32_t inter, int32_t n_experts,
                           uint8_t *out_w2, uint8_t *out_w2_scale, void *stream);
 
 /* Workspace bytes needed by ft_moe_route (path 0), ft_moe_nvfp4_decode (path 1)
- * or ft_moe_nvfp4_prefill (path 2) for `tokens` tokens.  Returns 0 for invalid
- * arguments.  The workspace must be zero-filled once before its first use; the
- * library leaves it reusable after every call that returned FT_OK.  Calls that
- * share one workspace must not run concurrently. */
+ * or ft_moe_nvfp4_prefill (path 2) for `tokens` tokens; a workspace sized for T
+ * tokens serves every smaller token count of the same path.  Returns 0 for
+ * invalid arguments.  Ownership: the caller allocates it (device memory) and
+ * zero-fills it once before its first use; every call that returned FT_OK leaves
+ * it ready for the next call of the same path (counters are reset by the kernels
+ * that use them, never by a memset).  Use one workspace per path, on one device;
+ * calls that share a workspace must not run concurrently. */
 size_t ft_moe_workspace_bytes(const ft_moe_desc *desc, int64_t tokens, int32_t path);
 
-/* Router only: fp64 logits, top-k (ties to the lower index) and softmax
- * weights of the selected logits.
+/* Router only (FreeToken commit log, page 2: the MoE router / shared gate kernels
+ * entry and the non-power-of-2 top-k router entry): logits with exact fp32 x bf16
+ * products summed in fp64 and rounded once to fp32 (from 1024 tokens on the fp64
+ * MFMA units), top-k (ties to the lower index) and softmax weights of the
+ * selected logits.
  *   x         bf16 [T][H]      w_router f32 [E][H]      bias f32 [E] or NULL
  *   topk_ids  i32  [T][k]      topk_w   f32 [T][k]      (outputs, rank order)
- * T >= 0 (T == 0 enqueues nothing). */
+ * 0 <= T <= 2^24 (T == 0 enqueues nothing). */
 ft_status ft_moe_route(const ft_moe_desc *desc, int64_t tokens, const uint16_t *x,
                        const float *w_router, const float *bias, int32_t *topk_ids,
                        float *topk_w, void *workspace, size_t workspace_bytes, void *stream);
 
-/* The whole layer for decode batches (1 <= T <= 64): routing, the gate|up GEMV
- * with in-register dequantisation and (clamped) SwiGLU, the down GEMV, the
- * weighted combine and the gated shared expert.
+/* The whole layer for decode batches (1 <= T <= 64; FreeToken fork PR #84,
+ * page 1, the bullet on #631): routing, the gate|up GEMV with in-register
+ * dequantisation and (clamped) SwiGLU, the down GEMV, the weighted combine and
+ * the gated shared expert.  T < 8 runs as one persistent kernel; T >= 8 routes,
+ * groups the (token, slot) pairs by expert and runs the grouped kernels of
+ * ft_moe_nvfp4_prefill, so each selected expert's weights are read once for all
+ * of its tokens.
  *   x bf16 [T][H]; w_router f32 [E][H]; bias f32 [E] or NULL
  *   routed: repacked bank of E experts; shared: repacked bank of 1 expert, or
  *   NULL when desc->shared_inter == 0; shared_gate bf16 [H] (NULL when no shared)
@@ -156,10 +166,13 @@ ft_status ft_moe_nvfp4_decode(const ft_moe_desc *desc, int64_t tokens, const uin
                               float *topk_w_out, uint16_t *y, void *workspace,
                               size_t workspace_bytes, void *stream);
 
-/* The expert part of the layer for prefill chunks, given routes from
- * ft_moe_route.  Ids live in device memory and are not checked on the host; a
- * token whose ids include a value outside [0, E) gets NaN outputs (the kernels
- * never read outside the bank).
+/* The expert part of the layer for prefill chunks (FreeToken fork PR #84,
+ * page 1, the bullet on #578), given routes (for example from ft_moe_route):
+ * pairs grouped by expert, gate|up and down as grouped bf16 MFMA GEMMs (exact
+ * bf16 code x scale tiles, fp32 accumulation, h carried as a bf16 hi + lo pair),
+ * combine in slot order.  0 <= T <= 65535.  Ids live in device memory and are not
+ * checked on the host; a token whose ids include a value outside [0, E) gets NaN
+ * outputs (the kernels never read outside the bank).
  *   x bf16 [T][H]; topk_ids i32 [T][k]; topk_w f32 [T][k]; y bf16 [T][H] (output)
  *   shared / shared_gate as for decode. */
 ft_status ft_moe_nvfp4_prefill(const ft_moe_desc *desc, int64_t tokens, const uint16_t *x,
