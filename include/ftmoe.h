@@ -142,7 +142,7 @@ size_t ft_moe_workspace_bytes(const ft_moe_desc *desc, int64_t tokens, int32_t p
  * selected logits.
  *   x         bf16 [T][H]      w_router f32 [E][H]      bias f32 [E] or NULL
  *   topk_ids  i32  [T][k]      topk_w   f32 [T][k]      (outputs, rank order)
- * 0 <= T <= 2^24 (T == 0 enqueues nothing). */
+ * 0 <= T <= 2^21 (T == 0 enqueues nothing). */
 ft_status ft_moe_route(const ft_moe_desc *desc, int64_t tokens, const uint16_t *x,
                        const float *w_router, const float *bias, int32_t *topk_ids,
                        float *topk_w, void *workspace, size_t workspace_bytes, void *stream);

@@ -379,7 +379,8 @@ ft_status ft_moe_route(const ft_moe_desc* desc, int64_t tokens, const uint16_t* 
   ft_status st = check_desc(desc);
   if (st != FT_OK) return st;
   if (tokens < 0) return fail(FT_EINVAL, "tokens < 0");
-  if (tokens > (1 << 24)) return fail(FT_EUNSUPPORTED, "tokens > 2^24");
+  // the router grids carry tokens / 64 in their y dimension (at most 65535)
+  if (tokens > (1 << 21)) return fail(FT_EUNSUPPORTED, "route takes at most 2^21 tokens per call");
   if (!x || !w_router || !topk_ids || !topk_w) return fail(FT_EINVAL, "route: NULL pointer");
   if (!aligned16(x) || !aligned16(w_router))
     return fail(FT_EINVAL, "route: x and w_router must be 16-byte aligned");

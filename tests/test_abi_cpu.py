@@ -104,6 +104,8 @@ def test_host_validation_status_codes(ft):
     assert lib.ft_moe_route(dp, 1, 18, 16, None, 16, 16, 256, 1 << 20, None) == ft.FT_EINVAL
     # workspace too small / misaligned / NULL
     assert lib.ft_moe_route(dp, 1, 16, 16, None, 16, 16, 256, 8, None) == ft.FT_EWORKSPACE
+    assert lib.ft_moe_route(dp, (1 << 21) + 1, 16, 16, None, 16, 16, 256, 1 << 62,
+                            None) == ft.FT_EUNSUPPORTED
     assert lib.ft_moe_route(dp, 1, 16, 16, None, 16, 16, 272, 1 << 20, None) == ft.FT_EWORKSPACE
     assert lib.ft_moe_route(dp, 1, 16, 16, None, 16, 16, None, 1 << 20, None) == ft.FT_EWORKSPACE
     # decode token range
