@@ -107,6 +107,8 @@ int prefill_unit_tokens(int T);
 int prefill_max_units(int E, int T, int k, bool shared);
 int prefill_group_blocks(int T, int k);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+// expert GEMMs of the grouped path for few tokens (after grouping, before combine)
+hipError_t launch_grouped_small(const PrefillParams& p, int ugroups, hipStream_t s);
 
 // Launchers: return the launch status (hipGetLastError after the launch).
 hipError_t launch_decode_fused(const FusedParams& p, int grid, hipStream_t s);

@@ -687,11 +687,10 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
     pf_gateup_kernel<4, 2, 1, 1><<<g1, 4 * kWave, 0, s>>>(p);
     pf_down_kernel<8, 2, 2, 4><<<g2, 8 * kWave, 0, s>>>(p);
   } else {
-    // few tokens per expert: the weight stream dominates; gate|up weights run 3
-    // super-slabs ahead, down codes 8 slabs ahead, token rows 3 slabs ahead
-    static_assert(Geometry<4, 1>::kUnitTokens == kSmallUnitTokens, "unit size");
-    pf_gateup_kernel<1, 4, 3, 2><<<g1, 4 * kWave, 0, s>>>(p);
-    pf_down_kernel<4, 1, 4, 8><<<g2, 4 * kWave, 0, s>>>(p);
+    // few tokens per expert: each wave holds its rows' codes for the whole K in
+    // registers (no K-loop prefetch)
+    hipError_t e = launch_grouped_small(p, ugroups, s);
+    if (e != hipSuccess) return e;
   }
   const size_t n4 = static_cast<size_t>(p.T) * (p.H / 4);
   pf_combine_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, s>>>(p);

@@ -223,6 +223,22 @@ def test_decode_shapes_outside_the_workloads(gpu):
     assert_output_close(gpu.bf16_bits(y), ref["y"], "odd shapes")
 
 
+def test_grouped_decode_shapes_outside_the_workloads(gpu):
+    """Grouped path with H = 768 (8 lanes x 3 chunks per row), I = 192, shared
+    I = 128 != I, T = 12, clamped SwiGLU; and H = 4096 (64 lanes x 2 chunks)."""
+    for H, I, Is, seed in ((768, 192, 128, 78), (4096, 128, 64, 79)):
+        w = synth.Workload(f"odd_{H}", 20, H, I, 4, 12, True, 2.0 ** -6, seed=seed,
+                           shared_inter=Is)
+        L = synth.make_layer(w)
+        dl = gpu.upload_layer(L)
+        x = synth.make_tokens(w)
+        y, ids, _ = gpu.decode(dl, gpu.tokens_to_device(x))
+        torch.cuda.synchronize()
+        ref = oracle.moe_layer(L, x)
+        assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+        assert_output_close(gpu.bf16_bits(y), ref["y"], f"grouped odd shapes H={H}")
+
+
 @pytest.mark.parametrize("tokens", [4, 16])   # fused kernel, grouped path
 def test_decode_is_deterministic(gpu, tokens):
     """Same inputs -> same bits, across workspace addresses and streams."""
