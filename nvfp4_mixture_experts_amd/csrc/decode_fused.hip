@@ -19,15 +19,17 @@
 //   R  router rows (one row per wave, rows spread one per CU; fp64 dot products
 //      with a DPP tree sum) and the shared gate; each logit is published in
 //      kLogitCopies replicas so that 256 blocks do not read the same lines.
-//   S  every block selects the experts itself from its replica: 8 waves each
-//      take the top-k of 64 experts, one wave merges the candidates (DPP max
-//      reductions and ballots; ties go to the lower index).
+//   S  every block selects the experts itself from its replica by counting,
+//      for each expert, the keys above its own: first inside its 64-expert
+//      chunk, then among the chunks' candidates (no serial select rounds; ties
+//      go to the lower index).
 //   W  every wave issues its gate|up loads, then the loads of its first
 //      down-projection chunks (kept in registers for D), then computes:
 //      e2m1 -> bf16 in registers, v_dot2_f32_bf16 against bf16 x, per-16 e4m3
 //      block scales, global scales, (clamped) SwiGLU; h published tagged.
 //   D  down GEMV from the prefetched chunks (lane = output row, K-chunk-major
-//      codes, h polled as wave-uniform loads), weighted by routing weight or
+//      codes; the h chunks of a wave's units polled together, one round trip,
+//      and broadcast from LDS), weighted by routing weight or
 //      shared gate; the blocks of one row group publish tagged partials and one
 //      of them sums them in a fixed order into bf16 y.
 //
@@ -42,8 +44,9 @@ constexpr int kFWaves = 8;     // waves per block
 constexpr int kUW = 3;         // gate|up units per wave and batch
 constexpr int kUD = 3;         // down units per wave and batch (first batch prefetched)
 constexpr int kMaxTK = 64 * 16;
-constexpr int kMaxChunks = 16; // 64-expert chunks of the first top-k stage (E <= 1024)
+constexpr int kMaxChunks = 16; // 64-expert chunks of the one-token top-k (E <= 1024)
 constexpr int kMaxK = 16;
+static_assert(kMaxChunks * kMaxK <= kFWaves * 64, "one candidate per thread");
 
 // ------------------------------------------------------------ tagged words --
 
@@ -63,15 +66,6 @@ __device__ __forceinline__ float tag_value(uint64_t w) {
   return __uint_as_float(static_cast<uint32_t>(w));
 }
 
-// 16 bytes (two tagged words) at base + byte_off, wave-uniform, device-coherent.
-__device__ __forceinline__ uint4 ld_dev_x4_uniform(const void* base, uint32_t byte_off) {
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(base), static_cast<short>(0), 0x7fffffff, 0x00020000);
-  typedef int int4v __attribute__((ext_vector_type(4)));
-  const int4v v = __builtin_amdgcn_raw_buffer_load_b128(r, 0, static_cast<int>(byte_off), 16);
-  return __builtin_bit_cast(uint4, v);
-}
-
 // Reads one tagged word per lane, polling until every lane's word carries `gen`.
 __device__ __forceinline__ uint64_t poll_tag(const uint64_t* p, uint32_t gen, int spin_limit,
                                              uint32_t* err) {
@@ -87,25 +81,55 @@ __device__ __forceinline__ uint64_t poll_tag(const uint64_t* p, uint32_t gen, in
   return wd;
 }
 
-// Reads the 32 tagged h values of one down unit (wave-uniform address) into hv,
-// polling until all carry `gen`.
-__device__ __forceinline__ void poll_h_chunk(const uint64_t* hrow, uint32_t gen, float* hv,
+// Orders this wave's LDS accesses before and after the call for all of its lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The 32 tagged h values of each of the N units of a down batch, polled together
+// so that the batch costs one round trip, not one per unit.  Word w of the batch
+// (unit w / 32, value w % 32) is read by lane w % 64 and its value stored to
+// hs[w] (this wave's LDS slice); units with need[u] false are not waited for
+// (their addresses are still in range).
+template <int N>
+__device__ __forceinline__ void poll_h_batch(const uint64_t* const (&hrow)[N],
+                                             const bool (&need)[N], uint32_t gen, float* hs,
                                              int spin_limit, uint32_t* err) {
+  constexpr int kL = (32 * N + kWave - 1) / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool upper = lane >= 32;
+  const uint64_t* addr[kL];
+  bool want[kL];
+  uint64_t wd[kL];
+#pragma unroll
+  for (int m = 0; m < kL; ++m) {
+    const int u0 = 2 * m;
+    const int u1 = (2 * m + 1 < N) ? 2 * m + 1 : u0;  // the upper half's unit
+    const bool has1 = 2 * m + 1 < N;
+    addr[m] = (upper ? hrow[u1] : hrow[u0]) + (lane & 31);
+    want[m] = upper ? (has1 && need[u1]) : need[u0];
+    wd[m] = ld_tag(addr[m]);
+  }
   for (int spins = 0;; ++spins) {
     bool ok = true;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const uint4 v = ld_dev_x4_uniform(hrow, static_cast<uint32_t>(16 * m));
-      hv[2 * m] = __uint_as_float(v.x);
-      hv[2 * m + 1] = __uint_as_float(v.z);
-      ok = ok && (v.y == gen) && (v.w == gen);
-    }
-    if (__ballot(!ok) == 0) return;
+    for (int m = 0; m < kL; ++m) ok = ok && (!want[m] || tag_is(wd[m], gen));
+    if (__ballot(!ok) == 0) break;
     if (spins >= spin_limit) {
       st_dev(err, 1u);
-      return;
+      break;
     }
     __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int m = 0; m < kL; ++m)
+      if (want[m] && !tag_is(wd[m], gen)) wd[m] = ld_tag(addr[m]);
+  }
+#pragma unroll
+  for (int m = 0; m < kL; ++m) {
+    const int w = m * kWave + lane;
+    if (w < 32 * N) hs[w] = tag_value(wd[m]);
   }
 }
 
@@ -126,79 +150,108 @@ __device__ __forceinline__ float poll_gate(const uint64_t* lg, int E, uint32_t g
   return tag_value(wd);
 }
 
+// How many of the 64 keys at p (LDS, read at the same address by every lane: a
+// broadcast) lie above key.  The reads go out 16 at a time ahead of their
+// compares, so the 64 keys cost two LDS latencies rather than one per read.
+__device__ __forceinline__ int count_above64(const uint64_t* p, uint64_t key) {
+  const ulonglong2* p2 = reinterpret_cast<const ulonglong2*>(p);
+  int above = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    ulonglong2 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = p2[16 * h + j];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      above += (v[j].x > key) ? 1 : 0;
+      above += (v[j].y > key) ? 1 : 0;
+    }
+  }
+  return above;
+}
+
 // The experts of one token's logits row (tagged, E + 1 words; word E is the
-// shared gate) by all waves of the block.  Stage 1: wave w takes 64-expert
-// chunks w, w + 8: k rounds of (wave max key, lowest lane holding it) give the
-// chunk's top-k in rank order.  Stage 2: wave 0 merges the candidates, ordered
-// (chunk, rank), with the same rounds; in that order equal keys appear by
-// ascending expert index, so ties go to the lower index.  Results go to ids,
-// w (softmax of the selected logits, fp64 exp) and gamma.
-__device__ void block_topk_one_token(const uint64_t* lg, int E, int k, uint32_t gen,
-                                     int spin_limit, uint32_t* err, uint32_t (*s_ck)[kMaxK],
-                                     int (*s_ci)[kMaxK], int* ids, float* w, float* gamma,
-                                     bool has_shared) {
+// shared gate) by all waves of the block, with no serial select rounds.  Expert
+// e carries the 64-bit key (rank_key(logit) << 32) | ~e: a larger key is a larger
+// logit, or an equal logit at a lower index, and no two keys are equal.
+// 1. Wave w polls the 64-expert chunks w, w + 8, ... and counts, for each expert,
+//    the keys of its own chunk above its key.  An expert with fewer than k above
+//    it is a candidate, stored at (chunk, count).
+// 2. Each candidate counts the candidates above it (4 lanes per candidate, over
+//    all waves).  For an expert of the top k every key above it is itself a
+//    candidate (fewer than k keys lie above it in all), so the count is its
+//    place; any other candidate counts at least k (some chunk holds k candidates
+//    above it).  A count below k is the expert's place.
+// 3. Each candidate also takes exp(logit - top logit) in fp64 (the top logit is
+//    the largest chunk maximum); wave 0 sums the selected terms in place order
+//    and divides (the softmax of the selected logits), and reads gamma.
+// Results go to ids, w and gamma.
+__device__ __forceinline__ void block_topk_one_token(const uint64_t* lg, int E, int k, uint32_t gen,
+                                     int spin_limit, uint32_t* err, uint64_t (*s_key)[kWave],
+                                     uint64_t* s_cand, uint64_t* s_sel, double* s_d, int* ids,
+                                     float* w, float* gamma, bool has_shared) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nchunks = (E + kWave - 1) / kWave;
+  const int nc = nchunks * k;                     // <= kMaxChunks * kMaxK <= blockDim.x
+  const int nc64 = (nc + kWave - 1) & ~(kWave - 1);
+  for (int i = nc + static_cast<int>(threadIdx.x); i < nc64; i += blockDim.x) s_cand[i] = 0ull;
   for (int c = wave; c < nchunks; c += kFWaves) {
     const int e = c * kWave + lane;
     const uint64_t wd = poll_tag(lg + (e < E ? e : E - 1), gen, spin_limit, err);
-    uint32_t key = (e < E) ? rank_key(tag_value(wd)) : 0u;
-    for (int i = 0; i < k; ++i) {
-      const uint32_t K = wave_max_u32(key);
-      const uint64_t b = __ballot(key == K && K != 0u);
-      const int wl = (b != 0) ? __ffsll(static_cast<unsigned long long>(b)) - 1 : -1;
-      if (lane == 0) {
-        s_ck[c][i] = K;
-        s_ci[c][i] = (wl >= 0) ? c * kWave + wl : -1;
+    const uint64_t key =
+        (e < E) ? (static_cast<uint64_t>(rank_key(tag_value(wd))) << 32) | static_cast<uint32_t>(~e)
+                : 0ull;
+    uint64_t* ck = s_key[wave];
+    ck[lane] = key;
+    if (lane < k) s_cand[c * k + lane] = 0ull;  // places a short chunk leaves empty
+    wave_lds_sync();
+    const int above = count_above64(ck, key);
+    if (key != 0ull && above < k) s_cand[c * k + above] = key;
+    wave_lds_sync();  // ck is rewritten by this wave's next chunk
+  }
+  __syncthreads();
+  // Candidate i is counted by the 4 lanes 4i .. 4i + 3 (a quad, inside one wave):
+  // lane q of the quad compares it with entries 16q .. 16q + 15 of every 64.
+  for (int c0 = 0; c0 < nc; c0 += kFWaves * kWave / 4) {
+    const int cand = c0 + static_cast<int>(threadIdx.x >> 2);
+    const int q = threadIdx.x & 3;
+    const uint64_t mine = s_cand[cand < nc ? cand : 0];
+    uint64_t top = 0ull;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {  // chunk maxima sit at place 0 of each chunk
+      const uint64_t v = s_cand[(c < nchunks ? c : nchunks - 1) * k];
+      top = v > top ? v : top;
+    }
+    const double d = exp(static_cast<double>(key_value(static_cast<uint32_t>(mine >> 32))) -
+                         static_cast<double>(key_value(static_cast<uint32_t>(top >> 32))));
+    int above = 0;  // zero entries count for nothing
+    for (int j0 = 0; j0 < nc64; j0 += kWave) {
+      const ulonglong2* p2 = reinterpret_cast<const ulonglong2*>(s_cand + j0 + 16 * q);
+      ulonglong2 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = p2[j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        above += (v[j].x > mine) ? 1 : 0;
+        above += (v[j].y > mine) ? 1 : 0;
       }
-      if (lane == wl) key = 0u;
+    }
+    above += __builtin_amdgcn_update_dpp(0, above, 0xB1, 0xf, 0xf, false);  // lanes ^ 1
+    above += __builtin_amdgcn_update_dpp(0, above, 0x4E, 0xf, 0xf, false);  // lanes ^ 2
+    if (cand < nc && q == 0 && mine != 0ull && above < k) {
+      s_sel[above] = mine;
+      s_d[above] = d;
     }
   }
   __syncthreads();
   if (wave == 0) {
-    const int n2 = nchunks * k;  // <= 256 candidates
-    uint32_t key2[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int j = lane + kWave * m;
-      key2[m] = (j < n2) ? s_ck[j / k][j % k] : 0u;
-    }
-    int my_id = -1;
-    uint32_t my_key = 0u;
-    uint32_t lmax = key2[0];
-#pragma unroll
-    for (int m = 1; m < 4; ++m) lmax = key2[m] > lmax ? key2[m] : lmax;
-    for (int i = 0; i < k; ++i) {
-      const uint32_t K = wave_max_u32(lmax);
-      int win = -1;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (win < 0) {
-          const uint64_t b = __ballot(key2[m] == K);
-          if (b != 0) win = kWave * m + __ffsll(static_cast<unsigned long long>(b)) - 1;
-        }
-      }
-      if (lane == i) {
-        my_id = s_ci[win / k][win % k];
-        my_key = K;
-      }
-      if ((win & (kWave - 1)) == lane) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          if (m == (win >> 6)) key2[m] = 0u;
-        lmax = key2[0];
-#pragma unroll
-        for (int m = 1; m < 4; ++m) lmax = key2[m] > lmax ? key2[m] : lmax;
-      }
-    }
-    const double top = static_cast<double>(key_value(static_cast<uint32_t>(
-        __builtin_amdgcn_readlane(static_cast<int>(my_key), 0))));
-    const double d = (lane < k) ? exp(static_cast<double>(key_value(my_key)) - top) : 0.0;
+    const uint64_t sel = (lane < k) ? s_sel[lane] : 0ull;
+    const double d = (lane < k) ? s_d[lane] : 0.0;
     double sum = 0.0;
     for (int i = 0; i < k; ++i) sum += readlane_f64(d, i);
     if (lane < k) {
-      ids[lane] = my_id;
+      ids[lane] = static_cast<int>(~static_cast<uint32_t>(sel));
       w[lane] = static_cast<float>(d / sum);
     }
     if (lane == 0) *gamma = has_shared ? poll_gate(lg, E, gen, spin_limit, err) : 0.0f;
@@ -307,8 +360,11 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   __shared__ float s_w[kMaxTK];
   __shared__ float s_gamma[64];
   __shared__ float s_red[kFWaves][kWave];
-  __shared__ uint32_t s_ck[kMaxChunks][kMaxK];
-  __shared__ int s_ci[kMaxChunks][kMaxK];
+  __shared__ __align__(16) uint64_t s_key[kFWaves][kWave];
+  __shared__ __align__(16) uint64_t s_cand[kMaxChunks * kMaxK];
+  __shared__ uint64_t s_sel[kMaxK];
+  __shared__ double s_d[kMaxK];
+  __shared__ __align__(16) float s_hb[kFWaves][32 * kUD];  // h values of a down batch
   __shared__ uint32_t s_gen;
 
   // generation of this call: this block's own call count
@@ -374,7 +430,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     const uint64_t* lgc = p.logits + static_cast<size_t>(blockIdx.x % kLogitCopies) * T * E1;
     const bool has_shared = p.shared_gate != nullptr;
     if (T == 1) {
-      block_topk_one_token(lgc, E, k, gen, p.spin_limit, p.err, s_ck, s_ci, s_ids, s_w,
+      block_topk_one_token(lgc, E, k, gen, p.spin_limit, p.err, s_key, s_cand, s_sel, s_d, s_ids, s_w,
                            &s_gamma[0], has_shared);
     } else {
       for (int t = wave; t < T; t += kFWaves) {
@@ -574,14 +630,34 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
           sc[ii] = *reinterpret_cast<const uint16_t*>(du[ii].sp);
         }
       }
+      {
+        const uint64_t* hrow[kUD];
+        bool need[kUD];
+#pragma unroll
+        for (int ii = 0; ii < kUD; ++ii) {
+          hrow[ii] = du[ii].hrow;
+          need[ii] = du[ii].valid;
+        }
+        poll_h_batch<kUD>(hrow, need, gen, s_hb[wave], p.spin_limit, p.err);
+      }
+      wave_lds_sync();
 #pragma unroll
       for (int ii = 0; ii < kUD; ++ii) {
         if (du[ii].valid) {
           float hv[32];
-          poll_h_chunk(du[ii].hrow, gen, hv, p.spin_limit, p.err);
+          const float4* h4 = reinterpret_cast<const float4*>(&s_hb[wave][32 * ii]);
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {  // same address in every lane: LDS broadcast
+            const float4 v = h4[m];
+            hv[4 * m] = v.x;
+            hv[4 * m + 1] = v.y;
+            hv[4 * m + 2] = v.z;
+            hv[4 * m + 3] = v.w;
+          }
           acc = fmaf(chunk_dot_f32(q[ii], sc[ii], hv), du[ii].wslot * du[ii].gdown, acc);
         }
       }
+      wave_lds_sync();  // the next batch rewrites s_hb[wave]
     }
     first = false;
     s_red[wave][lane] = acc;
