@@ -183,13 +183,14 @@ __device__ __forceinline__ int count_above64(const uint64_t* p, uint64_t key) {
 //    place; any other candidate counts at least k (some chunk holds k candidates
 //    above it).  A count below k is the expert's place.
 // 3. Each candidate also takes exp(logit - top logit) in fp64 (the top logit is
-//    the largest chunk maximum); wave 0 sums the selected terms in place order
-//    and divides (the softmax of the selected logits), and reads gamma.
-// Results go to ids, w and gamma.
-__device__ __forceinline__ void block_topk_one_token(const uint64_t* lg, int E, int k, uint32_t gen,
-                                     int spin_limit, uint32_t* err, uint64_t (*s_key)[kWave],
-                                     uint64_t* s_cand, uint64_t* s_sel, double* s_d, int* ids,
-                                     float* w, float* gamma, bool has_shared) {
+//    the largest chunk maximum).
+// Results: ids[place] and s_d[place] (the exp term), complete for every wave on
+// return.  The softmax itself (softmax_from_terms) is left to the caller, which
+// needs only the ids to start streaming the experts' weights.
+__device__ __forceinline__ void block_topk_one_token(const uint64_t* lg, int E, int k,
+                                                     uint32_t gen, int spin_limit, uint32_t* err,
+                                                     uint64_t (*s_key)[kWave], uint64_t* s_cand,
+                                                     double* s_d, int* ids) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nchunks = (E + kWave - 1) / kWave;
@@ -240,22 +241,22 @@ __device__ __forceinline__ void block_topk_one_token(const uint64_t* lg, int E, 
     above += __builtin_amdgcn_update_dpp(0, above, 0xB1, 0xf, 0xf, false);  // lanes ^ 1
     above += __builtin_amdgcn_update_dpp(0, above, 0x4E, 0xf, 0xf, false);  // lanes ^ 2
     if (cand < nc && q == 0 && mine != 0ull && above < k) {
-      s_sel[above] = mine;
+      ids[above] = static_cast<int>(~static_cast<uint32_t>(mine));
       s_d[above] = d;
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    const uint64_t sel = (lane < k) ? s_sel[lane] : 0ull;
-    const double d = (lane < k) ? s_d[lane] : 0.0;
-    double sum = 0.0;
-    for (int i = 0; i < k; ++i) sum += readlane_f64(d, i);
-    if (lane < k) {
-      ids[lane] = static_cast<int>(~static_cast<uint32_t>(sel));
-      w[lane] = static_cast<float>(d / sum);
-    }
-    if (lane == 0) *gamma = has_shared ? poll_gate(lg, E, gen, spin_limit, err) : 0.0f;
-  }
+}
+
+// The routing weights of one token from the exp terms d[0..k) in place order
+// (their sum in that order, then each term over it), by one wave in its own
+// registers: lane i returns the weight of place i (0 from lane k on).
+__device__ __forceinline__ float softmax_from_terms(const double* s_d, int k) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const double d = (lane < k) ? s_d[lane] : 0.0;
+  double sum = 0.0;
+  for (int i = 0; i < k; ++i) sum += readlane_f64(d, i);
+  return (lane < k) ? static_cast<float>(d / sum) : 0.0f;
 }
 
 // One token's experts by one wave (used when the block handles several tokens).
@@ -362,7 +363,6 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   __shared__ float s_red[kFWaves][kWave];
   __shared__ __align__(16) uint64_t s_key[kFWaves][kWave];
   __shared__ __align__(16) uint64_t s_cand[kMaxChunks * kMaxK];
-  __shared__ uint64_t s_sel[kMaxK];
   __shared__ double s_d[kMaxK];
   __shared__ __align__(16) float s_hb[kFWaves][32 * kUD];  // h values of a down batch
   __shared__ uint32_t s_gen;
@@ -430,8 +430,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     const uint64_t* lgc = p.logits + static_cast<size_t>(blockIdx.x % kLogitCopies) * T * E1;
     const bool has_shared = p.shared_gate != nullptr;
     if (T == 1) {
-      block_topk_one_token(lgc, E, k, gen, p.spin_limit, p.err, s_key, s_cand, s_sel, s_d, s_ids, s_w,
-                           &s_gamma[0], has_shared);
+      block_topk_one_token(lgc, E, k, gen, p.spin_limit, p.err, s_key, s_cand, s_d, s_ids);
     } else {
       for (int t = wave; t < T; t += kFWaves) {
         const uint64_t* lg = lgc + static_cast<size_t>(t) * E1;
@@ -445,15 +444,39 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
           wave_topk_tagged<16>(lg, E, k, gen, p.spin_limit, p.err, &s_ids[t * k], &s_w[t * k],
                                &s_gamma[t], has_shared);
       }
-    }
-    __syncthreads();
-    if (blockIdx.x == 0) {
-      for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
-        if (p.ids_out) p.ids_out[i] = s_ids[i];
-        if (p.w_out) p.w_out[i] = s_w[i];
+      __syncthreads();
+      if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
+          if (p.ids_out) p.ids_out[i] = s_ids[i];
+          if (p.w_out) p.w_out[i] = s_w[i];
+        }
       }
     }
   }
+
+  // One token: the routing weights (lane i: place i) and the shared gate, taken
+  // by every wave in its own registers once its first expert loads are out.
+  float w1 = 0.0f, gamma1 = 0.0f;
+  bool have_w1 = T != 1;
+  auto weights_one_token = [&]() {
+    if (have_w1) return;
+    have_w1 = true;
+    w1 = softmax_from_terms(s_d, k);
+    gamma1 = p.shared_gate ? poll_gate(p.logits + static_cast<size_t>(blockIdx.x % kLogitCopies) * E1,
+                                       E, gen, p.spin_limit, p.err)
+                           : 0.0f;
+    if (blockIdx.x == 0 && wave == 0 && lane < k) {
+      if (p.ids_out) p.ids_out[lane] = s_ids[lane];
+      if (p.w_out) p.w_out[lane] = w1;
+    }
+  };
+  // routing weight (or shared gate) of slot `slot` (k: the shared expert) of token t
+  auto slot_weight = [&](int t, int slot) -> float {
+    if (T == 1)
+      return slot == k ? gamma1
+                       : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w1), slot));
+    return slot == k ? s_gamma[t] : s_w[t * k + slot];
+  };
 
   // ------------------------------------------------ D assignment (prefetch) --
   const int nch = p.routed.inter / 32;
@@ -481,7 +504,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     const uint8_t* cp;
     const uint8_t* sp;
     const uint64_t* hrow;  // 32 tagged h values of this unit
-    float wslot;           // routing weight (or shared gate) of the unit's slot
+    int slot;              // the unit's slot (k: the shared expert)
     float gdown;           // down global scale of the unit's expert (multiplied at use:
                            // using a load result at issue time would wait for every
                            // load issued before it)
@@ -499,7 +522,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     d.cp = (sh ? p.shared.w2 : p.routed.w2) + rec * 16;
     d.sp = (sh ? p.shared.w2s : p.routed.w2s) + rec * 2;
     d.hrow = p.h + (static_cast<size_t>(t) * p.nslots + u.slot) * p.Imax + 32 * u.chunk;
-    d.wslot = d.valid ? (sh ? s_gamma[t] : s_w[t * k + u.slot]) : 0.0f;
+    d.slot = u.slot;
     d.gdown = ld_vmem_f32(sh ? p.shared.gsc : p.routed.gsc, 3 * e + 2);
     return d;
   };
@@ -581,6 +604,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
       if (!prefetched) {  // behind the first gate|up loads, ahead of their use
         prefetch_down();
         prefetched = true;
+        weights_one_token();
       }
 #pragma unroll
       for (int jj = 0; jj < kUW; ++jj) {
@@ -602,6 +626,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
       }
     }
     if (!prefetched) prefetch_down();
+    weights_one_token();
   }
 
   // ---------------------------------------------------------------- D --
@@ -654,7 +679,8 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
             hv[4 * m + 2] = v.z;
             hv[4 * m + 3] = v.w;
           }
-          acc = fmaf(chunk_dot_f32(q[ii], sc[ii], hv), du[ii].wslot * du[ii].gdown, acc);
+          acc = fmaf(chunk_dot_f32(q[ii], sc[ii], hv), slot_weight(t, du[ii].slot) * du[ii].gdown,
+                     acc);
         }
       }
       wave_lds_sync();  // the next batch rewrites s_hb[wave]

@@ -69,7 +69,9 @@ constexpr int kMaxExperts = 1024;   // experts per bank supported by the groupin
 constexpr int kGroupPairs = 1024;   // pairs per histogram block
 constexpr int kGroupOneBlockPairs = 16384;  // up to this many pairs are grouped by one block
 constexpr int kPfUnitTokens = 256;    // tokens per work unit of a many-token call
-constexpr int kSmallUnitTokens = 64;  // ... and of a call of at most this many tokens
+constexpr int kSmallCallTokens = 64;  // calls of at most this many tokens take the few-token
+constexpr int kSmallUnitTokens = 16;  // kernels, with units of at most this many tokens (one
+                                      // MFMA column block: a unit's tokens share one weight pass)
 
 struct PfUnit {
   int bank;    // 0 routed, 1 shared

@@ -66,6 +66,10 @@ __device__ __forceinline__ uint32_t word(const uint4& q, int j) {
   return j == 0 ? q.x : (j == 1 ? q.y : (j == 2 ? q.z : q.w));
 }
 
+// Row tiles of 64 per block in the pipelined down product: their codes are all in
+// registers at once (NKC 16-byte words per tile and lane).
+constexpr int down_pipe_tiles(int nkc) { return nkc <= 4 ? 4 : 2; }
+
 __device__ __forceinline__ void sg_unit_tile(int ntiles, int* u, int* tile) {
   const int b = blockIdx.x;
   *u = (b / (8 * ntiles)) * 8 + (b & 7);
@@ -150,6 +154,113 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_kernel(PrefillParams 
             ag = mfma(dq8(word(qg[q], j), j < 2 ? g0 : g1), b, ag);
             au = mfma(dq8(word(qu[q], j), j < 2 ? u0 : u1), b, au);
           }
+        }
+      }
+    }
+    // C lane l: rows 4 (l / 16) + jj (h columns), token l % 16 of the fragment
+    const int m = f0 + i;
+    if (m < un.count) {
+      const int t = un.bank ? un.start + m : 0;
+      const size_t row = un.bank ? static_cast<size_t>(p.P) + t : static_cast<size_t>(un.start) + m;
+      const int col = n0 + wave * 16 + 4 * g;
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int jj = 0; jj < 4; jj += 2) {
+        float hv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          hv[e] = swiglu(p.act, ag[jj + e] * gg, au[jj + e] * gu, p.gate_max, p.up_absmax);
+        const uint32_t h0 = f32_to_bf16_bits(hv[0]), h1 = f32_to_bf16_bits(hv[1]);
+        const uint32_t l0 = f32_to_bf16_bits(hv[0] - bf16_bits_to_f32(h0));
+        const uint32_t l1 = f32_to_bf16_bits(hv[1] - bf16_bits_to_f32(h1));
+        hi[jj >> 1] = h0 | (h1 << 16);
+        lo[jj >> 1] = l0 | (l1 << 16);
+      }
+      *reinterpret_cast<uint2*>(p.hhi + row * p.Imax + col) = make_uint2(hi[0], hi[1]);
+      *reinterpret_cast<uint2*>(p.hlo + row * p.Imax + col) = make_uint2(lo[0], lo[1]);
+    }
+  }
+}
+
+// The same product for H = NKB * 512, software-pipelined: the K loop is unrolled
+// so that K block kb + 1's token rows and codes are in flight while K block kb is
+// computed (every block of the grid is resident at once for these sizes, so
+// without this all of them issue, drain and compute in lockstep and HBM idles
+// between K blocks).  K mapping inside a 512-K block: lane group g takes the four
+// consecutive 32-K chunks 4 g .. 4 g + 3 of its row (64 contiguous code bytes, 8
+// contiguous scale bytes: one 8-byte scale load per row instead of four).
+template <int NKB>
+__global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_pipe_kernel(PrefillParams p) {
+  constexpr int kKB = 512;
+  constexpr int kRowU4 = kKB / 8 + 1;                  // 16-byte words per staged row (+1 pad)
+  constexpr int kXL = 16 * (kKB / 8) / kSgThreads;     // token-row loads per thread per K block
+  __shared__ uint4 xs[16 * kRowU4];
+  int u, tile;
+  sg_unit_tile(p.ntiles1, &u, &tile);
+  if (u >= *p.nunits) return;
+  const PfUnit un = p.units[u];
+  const Bank bank = un.bank ? p.shared : p.routed;
+  const int I = bank.inter;
+  const int n0 = tile * 64;
+  if (n0 >= I) return;
+  constexpr int H = NKB * kKB;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, g = lane >> 4;
+  const int grow = n0 + wave * 16 + i;  // gate row; up row I + grow
+  const size_t ebase = static_cast<size_t>(un.expert) * 2 * I;
+  const uint8_t* gc = bank.w13 + (ebase + grow) * (H / 2) + 64 * g;
+  const uint8_t* uc = bank.w13 + (ebase + I + grow) * (H / 2) + 64 * g;
+  const uint8_t* gsp = bank.w13s + (ebase + grow) * (H / 16) + 8 * g;
+  const uint8_t* usp = bank.w13s + (ebase + I + grow) * (H / 16) + 8 * g;
+  const float gg = bank.gsc[un.expert * 3 + 0], gu = bank.gsc[un.expert * 3 + 1];
+  // staged layout: thread tid moves word c8 = tid % 64 of token rows n = tid / 64 + 4 r
+  const int c8 = tid & 63;
+  for (int f0 = 0; f0 < un.count; f0 += 16) {
+    const uint16_t* xrow[kXL];
+#pragma unroll
+    for (int r = 0; r < kXL; ++r) {
+      const int m = min(f0 + (tid >> 6) + 4 * r, un.count - 1);  // past the unit: its last token
+      const int t = un.bank ? un.start + m : p.sorted[un.start + m] / p.k;
+      xrow[r] = p.x + static_cast<size_t>(t) * H + 8 * c8;
+    }
+    uint4 xv[2][kXL], qg[2][4], qu[2][4];
+    uint2 sg[2], su[2];
+    auto issue = [&](int kb, int b) {
+#pragma unroll
+      for (int r = 0; r < kXL; ++r) xv[b][r] = ldg16(xrow[r] + kb * kKB);
+      __builtin_amdgcn_sched_barrier(0);  // token rows first: the staging waits for them
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        qg[b][q] = ldg16(gc + kb * (kKB / 2) + 16 * q);
+        qu[b][q] = ldg16(uc + kb * (kKB / 2) + 16 * q);
+      }
+      sg[b] = *reinterpret_cast<const uint2*>(gsp + kb * (kKB / 16));
+      su[b] = *reinterpret_cast<const uint2*>(usp + kb * (kKB / 16));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    sg_f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+    issue(0, 0);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int b = kb & 1;
+      if (kb + 1 < NKB) issue(kb + 1, b ^ 1);
+      __syncthreads();  // the previous K block (or fragment) is done with xs
+#pragma unroll
+      for (int r = 0; r < kXL; ++r) xs[((tid >> 6) + 4 * r) * kRowU4 + c8] = xv[b][r];
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t gw = q < 2 ? sg[b].x : sg[b].y, uw = q < 2 ? su[b].x : su[b].y;
+        const float g0 = (q & 1) ? e4m3_byte_to_f32<2>(gw) : e4m3_byte_to_f32<0>(gw);
+        const float g1 = (q & 1) ? e4m3_byte_to_f32<3>(gw) : e4m3_byte_to_f32<1>(gw);
+        const float u0 = (q & 1) ? e4m3_byte_to_f32<2>(uw) : e4m3_byte_to_f32<0>(uw);
+        const float u1 = (q & 1) ? e4m3_byte_to_f32<3>(uw) : e4m3_byte_to_f32<1>(uw);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 bx = xs[i * kRowU4 + (4 * g + q) * 4 + j];
+          ag = mfma(dq8(word(qg[b][q], j), j < 2 ? g0 : g1), bx, ag);
+          au = mfma(dq8(word(qu[b][q], j), j < 2 ? u0 : u1), bx, au);
         }
       }
     }
@@ -286,12 +397,147 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_kernel(PrefillParams p)
   }
 }
 
+// The down product for I = 128 * NKC (both banks), one block per kRT row tiles of
+// 64: the fragment's h (hi and lo, all of K) is staged in LDS once and serves the
+// kRT tiles, and the codes of all kRT tiles are issued up front, so a block pays
+// one memory latency, not one per tile.
+template <int NKC>
+__global__ __launch_bounds__(kSgThreads, 2) void sg_down_pipe_kernel(PrefillParams p) {
+  constexpr int kI = 128 * NKC;
+  constexpr int kRowU4 = kI / 8 + 1;
+  constexpr int kRT = down_pipe_tiles(NKC);                // row tiles per block
+  constexpr int kHL = 2 * 16 * (kI / 8) / kSgThreads;      // h loads per thread
+  static_assert(kHL * kSgThreads == 2 * 16 * (kI / 8), "whole staging rounds");
+  __shared__ uint4 hs[2][16 * kRowU4];
+  int u, tg;
+  sg_unit_tile(p.ntiles2, &u, &tg);
+  if (u >= *p.nunits) return;
+  const PfUnit un = p.units[u];
+  const Bank bank = un.bank ? p.shared : p.routed;
+  const int H = p.H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, g = lane >> 4;
+  const size_t cbase = static_cast<size_t>(un.expert) * (kI / 32);
+  const float gd = bank.gsc[un.expert * 3 + 2];
+  const int row0 = tg * (64 * kRT) + wave * 16;  // + 64 rt + i: this lane's weight row
+  for (int f0 = 0; f0 < un.count; f0 += 16) {
+    // C lane l: output rows 4 (l / 16) + jj of the wave's 16, token l % 16.  The
+    // (token, slot) pair is loaded first, its weight (which depends on it) after
+    // the h and code loads, so that neither waits in front of them.
+    const int m = f0 + i;
+    const int mm = min(m, un.count - 1);
+    const int pair = un.bank ? 0 : p.sorted[un.start + mm];
+    uint4 hv[kHL];
+#pragma unroll
+    for (int r = 0; r < kHL; ++r) {
+      const int v = tid + r * kSgThreads;
+      const int which = v / (16 * (kI / 8));
+      const int rr = v - which * 16 * (kI / 8);
+      const int n = rr / (kI / 8), c8 = rr - n * (kI / 8);
+      const int mh = min(f0 + n, un.count - 1);
+      const size_t hrow = un.bank ? static_cast<size_t>(p.P) + un.start + mh
+                                  : static_cast<size_t>(un.start) + mh;
+      hv[r] = ldg16((which ? p.hlo : p.hhi) + hrow * p.Imax + 8 * c8);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // h first (the staging waits for it)
+    // scales: the 4-byte word holding this row's and its even/odd neighbour's two
+    // bytes (a 2-byte load would be widened right at the load, which waits for it)
+    uint4 q[kRT][NKC];
+    uint32_t sc[kRT][NKC];
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      const int row = row0 + 64 * rt + i;
+#pragma unroll
+      for (int s = 0; s < NKC; ++s) {
+        const size_t c = cbase + 4 * s + g;  // chunk 4 s + g of 32 K
+        q[rt][s] = ldg16(bank.w2 + (c * H + row) * 16);
+        sc[rt][s] = *reinterpret_cast<const uint32_t*>(bank.w2s + (c * H + (row & ~1)) * 2);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int t, slot;
+    float wt;
+    if (un.bank) {
+      t = un.start + mm;
+      slot = p.k;
+      wt = p.gamma[t];
+    } else {
+      t = pair / p.k;
+      slot = pair - t * p.k;
+      wt = p.w[pair];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // the previous fragment is done with hs
+#pragma unroll
+    for (int r = 0; r < kHL; ++r) {
+      const int v = tid + r * kSgThreads;
+      const int which = v / (16 * (kI / 8));
+      const int rr = v - which * 16 * (kI / 8);
+      const int n = rr / (kI / 8), c8 = rr - n * (kI / 8);
+      hs[which][n * kRowU4 + c8] = hv[r];
+    }
+    __syncthreads();
+    sg_f32x4 acc[kRT];
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      // the tiles read the same h words: re-read them per tile rather than let the
+      // compiler keep all of them live across the tiles (it would run out of registers)
+      asm volatile("" ::: "memory");
+      acc[rt] = sg_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NKC; ++s) {
+        const uint32_t sw = sc[rt][s] >> (16 * (i & 1));  // rows are even + i
+        const float s0 = e4m3_byte_to_f32<0>(sw), s1 = e4m3_byte_to_f32<1>(sw);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 a = dq8(word(q[rt][s], j), j < 2 ? s0 : s1);
+          const int kk = (4 * s + g) * 4 + j;  // 16-byte word of the staged row
+          acc[rt] = mfma(a, hs[0][i * kRowU4 + kk], acc[rt]);
+          acc[rt] = mfma(a, hs[1][i * kRowU4 + kk], acc[rt]);
+        }
+      }
+    }
+    if (m < un.count) {
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        float4 v;
+        v.x = (acc[rt][0] * gd) * wt;
+        v.y = (acc[rt][1] * gd) * wt;
+        v.z = (acc[rt][2] * gd) * wt;
+        v.w = (acc[rt][3] * gd) * wt;
+        *reinterpret_cast<float4*>(p.out + (static_cast<size_t>(t) * p.nslots + slot) * H + row0 +
+                                   64 * rt + 4 * g) = v;
+      }
+    }
+  }
+}
+
 hipError_t launch_grouped_small(const PrefillParams& p0, int ugroups, hipStream_t s) {
   PrefillParams p = p0;
   p.ntiles1 = p.Imax / 64;
   p.ntiles2 = p.H / 64;
-  sg_gateup_kernel<<<ugroups * 8 * p.ntiles1, kSgThreads, 0, s>>>(p);
-  sg_down_kernel<<<ugroups * 8 * p.ntiles2, kSgThreads, 0, s>>>(p);
+  const dim3 g1(ugroups * 8 * p.ntiles1), blk(kSgThreads);
+  switch (p.H) {
+    case 1024: sg_gateup_pipe_kernel<2><<<g1, blk, 0, s>>>(p); break;
+    case 2048: sg_gateup_pipe_kernel<4><<<g1, blk, 0, s>>>(p); break;
+    case 3072: sg_gateup_pipe_kernel<6><<<g1, blk, 0, s>>>(p); break;
+    case 4096: sg_gateup_pipe_kernel<8><<<g1, blk, 0, s>>>(p); break;
+    default: sg_gateup_kernel<<<g1, blk, 0, s>>>(p); break;
+  }
+  // the pipelined down product needs one I for both banks and H in whole row-tile groups
+  const int I = p.routed.inter;
+  const bool one_i = p.shared.inter == 0 || p.shared.inter == I;
+  const int nkc = (one_i && p.H % 256 == 0 && I % 128 == 0) ? I / 128 : 0;
+  if (nkc == 4 || nkc == 6 || nkc == 8) {
+    p.ntiles2 = p.H / (64 * down_pipe_tiles(nkc));
+    const dim3 g2(ugroups * 8 * p.ntiles2);
+    if (nkc == 4) sg_down_pipe_kernel<4><<<g2, blk, 0, s>>>(p);
+    else if (nkc == 6) sg_down_pipe_kernel<6><<<g2, blk, 0, s>>>(p);
+    else sg_down_pipe_kernel<8><<<g2, blk, 0, s>>>(p);
+  } else {
+    sg_down_kernel<<<ugroups * 8 * p.ntiles2, blk, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 

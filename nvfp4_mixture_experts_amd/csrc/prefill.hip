@@ -650,7 +650,7 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PrefillParams p) {
 
 // ------------------------------------------------------------ launchers --
 
-int prefill_unit_tokens(int T) { return T <= kSmallUnitTokens ? kSmallUnitTokens : kPfUnitTokens; }
+int prefill_unit_tokens(int T) { return T <= kSmallCallTokens ? kSmallUnitTokens : kPfUnitTokens; }
 
 int prefill_max_units(int E, int T, int k, bool shared) {
   // sum over experts of ceil(n_e / ut) <= (experts with a pair) + P / ut
@@ -687,8 +687,8 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
     pf_gateup_kernel<4, 2, 1, 1><<<g1, 4 * kWave, 0, s>>>(p);
     pf_down_kernel<8, 2, 2, 4><<<g2, 8 * kWave, 0, s>>>(p);
   } else {
-    // few tokens per expert: each wave holds its rows' codes for the whole K in
-    // registers (no K-loop prefetch)
+    // few tokens per expert: units of at most 16 tokens, each a separate pass over
+    // its expert's weights (the passes of one expert run side by side)
     hipError_t e = launch_grouped_small(p, ugroups, s);
     if (e != hipSuccess) return e;
   }
