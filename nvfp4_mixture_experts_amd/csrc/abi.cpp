@@ -239,7 +239,7 @@ ft_status run_route(const ft_moe_desc* desc, int T, const uint16_t* x, const flo
   hipError_t e;
   if (T >= kRouteMfmaMinTokens) {
     // many tokens: logits as an fp64 MFMA product, the shared gate by the row
-    // kernel (as its only row), then top-k with one wave per token
+    // kernel (as its only row), then the top-k kernel
     e = launch_route_mfma(p, s);
     if (e != hipSuccess) return hip_fail(e, "route kernel");
     if (gamma) {
@@ -253,7 +253,8 @@ ft_status run_route(const ft_moe_desc* desc, int T, const uint16_t* x, const flo
     return FT_OK;
   }
   // the last block to finish selects the experts when it has a wave per token;
-  // otherwise a top-k kernel with one wave per token follows
+  // otherwise a top-k kernel follows (a block per token up to 256 tokens, else a
+  // wave per token)
   const bool fuse = T <= route_fused_topk_tokens();
   e = launch_route(p, fuse, s);
   if (e != hipSuccess) return hip_fail(e, "route kernel");

@@ -44,9 +44,7 @@ constexpr int kFWaves = 8;     // waves per block
 constexpr int kUW = 3;         // gate|up units per wave and batch
 constexpr int kUD = 3;         // down units per wave and batch (first batch prefetched)
 constexpr int kMaxTK = 64 * 16;
-constexpr int kMaxChunks = 16; // 64-expert chunks of the one-token top-k (E <= 1024)
-constexpr int kMaxK = 16;
-static_assert(kMaxChunks * kMaxK <= kFWaves * 64, "one candidate per thread");
+constexpr int kMaxK = kTopkMaxK;
 
 // ------------------------------------------------------------ tagged words --
 
@@ -79,13 +77,6 @@ __device__ __forceinline__ uint64_t poll_tag(const uint64_t* p, uint32_t gen, in
     if (!tag_is(wd, gen)) wd = ld_tag(p);
   }
   return wd;
-}
-
-// Orders this wave's LDS accesses before and after the call for all of its lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // The 32 tagged h values of each of the N units of a down batch, polled together
@@ -150,113 +141,18 @@ __device__ __forceinline__ float poll_gate(const uint64_t* lg, int E, uint32_t g
   return tag_value(wd);
 }
 
-// How many of the 64 keys at p (LDS, read at the same address by every lane: a
-// broadcast) lie above key.  The reads go out 16 at a time ahead of their
-// compares, so the 64 keys cost two LDS latencies rather than one per read.
-__device__ __forceinline__ int count_above64(const uint64_t* p, uint64_t key) {
-  const ulonglong2* p2 = reinterpret_cast<const ulonglong2*>(p);
-  int above = 0;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    ulonglong2 v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = p2[16 * h + j];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      above += (v[j].x > key) ? 1 : 0;
-      above += (v[j].y > key) ? 1 : 0;
-    }
-  }
-  return above;
-}
-
 // The experts of one token's logits row (tagged, E + 1 words; word E is the
-// shared gate) by all waves of the block, with no serial select rounds.  Expert
-// e carries the 64-bit key (rank_key(logit) << 32) | ~e: a larger key is a larger
-// logit, or an equal logit at a lower index, and no two keys are equal.
-// 1. Wave w polls the 64-expert chunks w, w + 8, ... and counts, for each expert,
-//    the keys of its own chunk above its key.  An expert with fewer than k above
-//    it is a candidate, stored at (chunk, count).
-// 2. Each candidate counts the candidates above it (4 lanes per candidate, over
-//    all waves).  For an expert of the top k every key above it is itself a
-//    candidate (fewer than k keys lie above it in all), so the count is its
-//    place; any other candidate counts at least k (some chunk holds k candidates
-//    above it).  A count below k is the expert's place.
-// 3. Each candidate also takes exp(logit - top logit) in fp64 (the top logit is
-//    the largest chunk maximum).
-// Results: ids[place] and s_d[place] (the exp term), complete for every wave on
-// return.  The softmax itself (softmax_from_terms) is left to the caller, which
-// needs only the ids to start streaming the experts' weights.
+// shared gate) by all waves of the block: block_topk_rank with each chunk's
+// logits polled until they carry this call's generation.  ids[place] and
+// s_d[place] are complete for every wave on return.
 __device__ __forceinline__ void block_topk_one_token(const uint64_t* lg, int E, int k,
                                                      uint32_t gen, int spin_limit, uint32_t* err,
                                                      uint64_t (*s_key)[kWave], uint64_t* s_cand,
                                                      double* s_d, int* ids) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nchunks = (E + kWave - 1) / kWave;
-  const int nc = nchunks * k;                     // <= kMaxChunks * kMaxK <= blockDim.x
-  const int nc64 = (nc + kWave - 1) & ~(kWave - 1);
-  for (int i = nc + static_cast<int>(threadIdx.x); i < nc64; i += blockDim.x) s_cand[i] = 0ull;
-  for (int c = wave; c < nchunks; c += kFWaves) {
-    const int e = c * kWave + lane;
-    const uint64_t wd = poll_tag(lg + (e < E ? e : E - 1), gen, spin_limit, err);
-    const uint64_t key =
-        (e < E) ? (static_cast<uint64_t>(rank_key(tag_value(wd))) << 32) | static_cast<uint32_t>(~e)
-                : 0ull;
-    uint64_t* ck = s_key[wave];
-    ck[lane] = key;
-    if (lane < k) s_cand[c * k + lane] = 0ull;  // places a short chunk leaves empty
-    wave_lds_sync();
-    const int above = count_above64(ck, key);
-    if (key != 0ull && above < k) s_cand[c * k + above] = key;
-    wave_lds_sync();  // ck is rewritten by this wave's next chunk
-  }
-  __syncthreads();
-  // Candidate i is counted by the 4 lanes 4i .. 4i + 3 (a quad, inside one wave):
-  // lane q of the quad compares it with entries 16q .. 16q + 15 of every 64.
-  for (int c0 = 0; c0 < nc; c0 += kFWaves * kWave / 4) {
-    const int cand = c0 + static_cast<int>(threadIdx.x >> 2);
-    const int q = threadIdx.x & 3;
-    const uint64_t mine = s_cand[cand < nc ? cand : 0];
-    uint64_t top = 0ull;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {  // chunk maxima sit at place 0 of each chunk
-      const uint64_t v = s_cand[(c < nchunks ? c : nchunks - 1) * k];
-      top = v > top ? v : top;
-    }
-    const double d = exp(static_cast<double>(key_value(static_cast<uint32_t>(mine >> 32))) -
-                         static_cast<double>(key_value(static_cast<uint32_t>(top >> 32))));
-    int above = 0;  // zero entries count for nothing
-    for (int j0 = 0; j0 < nc64; j0 += kWave) {
-      const ulonglong2* p2 = reinterpret_cast<const ulonglong2*>(s_cand + j0 + 16 * q);
-      ulonglong2 v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = p2[j];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        above += (v[j].x > mine) ? 1 : 0;
-        above += (v[j].y > mine) ? 1 : 0;
-      }
-    }
-    above += __builtin_amdgcn_update_dpp(0, above, 0xB1, 0xf, 0xf, false);  // lanes ^ 1
-    above += __builtin_amdgcn_update_dpp(0, above, 0x4E, 0xf, 0xf, false);  // lanes ^ 2
-    if (cand < nc && q == 0 && mine != 0ull && above < k) {
-      ids[above] = static_cast<int>(~static_cast<uint32_t>(mine));
-      s_d[above] = d;
-    }
-  }
-  __syncthreads();
-}
-
-// The routing weights of one token from the exp terms d[0..k) in place order
-// (their sum in that order, then each term over it), by one wave in its own
-// registers: lane i returns the weight of place i (0 from lane k on).
-__device__ __forceinline__ float softmax_from_terms(const double* s_d, int k) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const double d = (lane < k) ? s_d[lane] : 0.0;
-  double sum = 0.0;
-  for (int i = 0; i < k; ++i) sum += readlane_f64(d, i);
-  return (lane < k) ? static_cast<float>(d / sum) : 0.0f;
+  block_topk_rank<kFWaves>(
+      E, k,
+      [&](int e) { return tag_value(poll_tag(lg + e, gen, spin_limit, err)); },
+      s_key, s_cand, s_d, ids);
 }
 
 // One token's experts by one wave (used when the block handles several tokens).
@@ -362,7 +258,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   __shared__ float s_gamma[64];
   __shared__ float s_red[kFWaves][kWave];
   __shared__ __align__(16) uint64_t s_key[kFWaves][kWave];
-  __shared__ __align__(16) uint64_t s_cand[kMaxChunks * kMaxK];
+  __shared__ __align__(16) uint64_t s_cand[kTopkMaxChunks * kTopkMaxK];
   __shared__ double s_d[kMaxK];
   __shared__ __align__(16) float s_hb[kFWaves][32 * kUD];  // h values of a down batch
   __shared__ uint32_t s_gen;

@@ -347,6 +347,129 @@ __device__ __forceinline__ void wave_topk(int E, int k, Load load_logit, int* ou
   wave_topk_vals<SLOTS>(E, k, lv, out_id, out_w);
 }
 
+// ------------------------------------------------- block top-k (rank counting) --
+
+constexpr int kTopkMaxChunks = 16;  // 64-expert chunks (E <= 1024)
+constexpr int kTopkMaxK = 16;
+
+// Orders this wave's LDS accesses before and after the call for all of its lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// How many of the 64 keys at p (LDS, read at the same address by every lane: a
+// broadcast) lie above key.  The reads go out 16 at a time ahead of their
+// compares, so the 64 keys cost two LDS latencies rather than one per read.
+__device__ __forceinline__ int count_above64(const uint64_t* p, uint64_t key) {
+  const ulonglong2* p2 = reinterpret_cast<const ulonglong2*>(p);
+  int above = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    ulonglong2 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = p2[16 * h + j];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      above += (v[j].x > key) ? 1 : 0;
+      above += (v[j].y > key) ? 1 : 0;
+    }
+  }
+  return above;
+}
+
+// The top k of one token's E logits by all BW waves of a block, with no serial
+// select rounds.  Expert e carries the 64-bit key (rank_key(logit) << 32) | ~e: a
+// larger key is a larger logit, or an equal logit at a lower index, and no two
+// keys are equal.  fetch(e) returns logit e; every lane of a wave calls it at once
+// for the wave's chunk (so it may poll with wave-wide votes).
+// 1. Wave w fetches the 64-expert chunks w, w + BW, ... and counts, for each expert,
+//    the keys of its own chunk above its key.  An expert with fewer than k above
+//    it is a candidate, stored at (chunk, count).
+// 2. Each candidate counts the candidates above it (4 lanes per candidate, over
+//    all waves).  For an expert of the top k every key above it is itself a
+//    candidate (fewer than k keys lie above it in all), so the count is its
+//    place; any other candidate counts at least k (some chunk holds k candidates
+//    above it).  A count below k is the expert's place.
+// 3. Each candidate also takes exp(logit - top logit) in fp64 (the top logit is
+//    the largest chunk maximum).
+// Results: ids[place] and s_d[place] (the exp term), complete for every wave on
+// return.  The softmax itself (softmax_from_terms) is left to the caller (the
+// decode kernel needs only the ids to start streaming the experts' weights).
+// LDS: s_key[BW][64], s_cand[kTopkMaxChunks * kTopkMaxK] (16-byte aligned), s_d[k].
+template <int BW, class Fetch>
+__device__ __forceinline__ void block_topk_rank(int E, int k, Fetch fetch,
+                                                uint64_t (*s_key)[kWave], uint64_t* s_cand,
+                                                double* s_d, int* ids) {
+  static_assert(kTopkMaxChunks * kTopkMaxK <= BW * kWave, "one candidate per thread");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nchunks = (E + kWave - 1) / kWave;
+  const int nc = nchunks * k;                     // <= kTopkMaxChunks * kTopkMaxK
+  const int nc64 = (nc + kWave - 1) & ~(kWave - 1);
+  for (int i = nc + static_cast<int>(threadIdx.x); i < nc64; i += blockDim.x) s_cand[i] = 0ull;
+  for (int c = wave; c < nchunks; c += BW) {
+    const int e = c * kWave + lane;
+    const float v = fetch(e < E ? e : E - 1);
+    const uint64_t key =
+        (e < E) ? (static_cast<uint64_t>(rank_key(v)) << 32) | static_cast<uint32_t>(~e) : 0ull;
+    uint64_t* ck = s_key[wave];
+    ck[lane] = key;
+    if (lane < k) s_cand[c * k + lane] = 0ull;  // places a short chunk leaves empty
+    wave_lds_sync();
+    const int above = count_above64(ck, key);
+    if (key != 0ull && above < k) s_cand[c * k + above] = key;
+    wave_lds_sync();  // ck is rewritten by this wave's next chunk
+  }
+  __syncthreads();
+  // Candidate i is counted by the 4 lanes 4i .. 4i + 3 (a quad, inside one wave):
+  // lane q of the quad compares it with entries 16q .. 16q + 15 of every 64.
+  for (int c0 = 0; c0 < nc; c0 += BW * kWave / 4) {
+    const int cand = c0 + static_cast<int>(threadIdx.x >> 2);
+    const int q = threadIdx.x & 3;
+    const uint64_t mine = s_cand[cand < nc ? cand : 0];
+    uint64_t top = 0ull;
+#pragma unroll
+    for (int c = 0; c < kTopkMaxChunks; ++c) {  // chunk maxima sit at place 0 of each chunk
+      const uint64_t v = s_cand[(c < nchunks ? c : nchunks - 1) * k];
+      top = v > top ? v : top;
+    }
+    const double d = exp(static_cast<double>(key_value(static_cast<uint32_t>(mine >> 32))) -
+                         static_cast<double>(key_value(static_cast<uint32_t>(top >> 32))));
+    int above = 0;  // zero entries count for nothing
+    for (int j0 = 0; j0 < nc64; j0 += kWave) {
+      const ulonglong2* p2 = reinterpret_cast<const ulonglong2*>(s_cand + j0 + 16 * q);
+      ulonglong2 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = p2[j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        above += (v[j].x > mine) ? 1 : 0;
+        above += (v[j].y > mine) ? 1 : 0;
+      }
+    }
+    above += __builtin_amdgcn_update_dpp(0, above, 0xB1, 0xf, 0xf, false);  // lanes ^ 1
+    above += __builtin_amdgcn_update_dpp(0, above, 0x4E, 0xf, 0xf, false);  // lanes ^ 2
+    if (cand < nc && q == 0 && mine != 0ull && above < k) {
+      ids[above] = static_cast<int>(~static_cast<uint32_t>(mine));
+      s_d[above] = d;
+    }
+  }
+  __syncthreads();
+}
+
+// The routing weights of one token from the exp terms d[0..k) in place order
+// (their sum in that order, then each term over it), by one wave in its own
+// registers: lane i returns the weight of place i (0 from lane k on).
+__device__ __forceinline__ float softmax_from_terms(const double* s_d, int k) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const double d = (lane < k) ? s_d[lane] : 0.0;
+  double sum = 0.0;
+  for (int i = 0; i < k; ++i) sum += readlane_f64(d, i);
+  return (lane < k) ? static_cast<float>(d / sum) : 0.0f;
+}
+
 // ------------------------------------------------------ vector-memory loads --
 //
 // base[index] through a buffer load (the vector memory path).  A wave-uniform

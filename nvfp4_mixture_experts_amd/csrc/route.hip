@@ -14,7 +14,10 @@ namespace ftmoe {
 
 constexpr int kRouteWaves = 4;     // one expert row per wave
 constexpr int kRouteMaxTokTile = 64;
-constexpr int kRouteTargetWaves = 2048;  // enough waves to fill 256 CUs several times
+constexpr int kRouteTargetWaves = 8192;  // enough waves to fill 256 CUs several times
+
+// Tokens a router wave takes at once (their x pieces are held in registers together).
+constexpr int route_token_group(int nc) { return nc <= 8 ? 4 : (nc <= 16 ? 2 : 1); }
 
 // Top-k of one token by one wave (wave_topk), written in rank order.
 template <class Load>
@@ -40,63 +43,75 @@ __device__ void topk_one_token(int E, int k, Load load, int32_t* ids, float* w, 
 // logits[t][e] for expert row e = blockIdx.x * kRouteWaves + wave; row E is the
 // shared expert's gate (gamma[t] = sigmoid(sum_h gs[h] x[t][h])).  Each lane
 // holds NC float4 pieces of the row (interleaved by lane so that every wave load
-// reads 1 KiB contiguous) and reuses them across the token tile.
+// reads 1 KiB contiguous) and reuses them across the token tile.  Tokens go in
+// groups of G: the x loads of a group are issued together and the G dot
+// products interleave (each still sums its own terms in the same order), so a
+// group costs one load latency, not G.
 template <int NC>
 __global__ __launch_bounds__(kRouteWaves* kWave) void route_logits_kernel(RouteParams p,
                                                                           int fuse_topk) {
+  constexpr int G = route_token_group(NC);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x * kRouteWaves + wave;
   const int t0 = blockIdx.y * p.tok_tile;
   const int t1 = min(p.T, t0 + p.tok_tile);
   const int H = p.H;
+  const bool gate_row = row == p.E;
 
-  if (row < p.E) {
-    const float* __restrict__ wrow = p.wr + static_cast<size_t>(row) * H;
+  if (row < p.E || (gate_row && p.shared_gate != nullptr)) {
     float4 wv[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      wv[c] = *reinterpret_cast<const float4*>(wrow + 4 * lane + 4 * kWave * c);
-    const double b = p.bias ? static_cast<double>(p.bias[row]) : 0.0;
-    for (int t = t0; t < t1; ++t) {
-      const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
-      double acc = 0.0;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const uint2 xb = *reinterpret_cast<const uint2*>(xt + 4 * lane + 4 * kWave * c);
-        acc = fma(static_cast<double>(wv[c].x), static_cast<double>(bf16_bits_to_f32(xb.x & 0xFFFFu)), acc);
-        acc = fma(static_cast<double>(wv[c].y), static_cast<double>(bf16_bits_to_f32(xb.x >> 16)), acc);
-        acc = fma(static_cast<double>(wv[c].z), static_cast<double>(bf16_bits_to_f32(xb.y & 0xFFFFu)), acc);
-        acc = fma(static_cast<double>(wv[c].w), static_cast<double>(bf16_bits_to_f32(xb.y >> 16)), acc);
-      }
-      acc = wave_sum_f64(acc);
-      if (lane == 0) {
-        if (p.bias) acc += b;
-        st_dev(&p.logits[static_cast<size_t>(t) * p.E + row], static_cast<float>(acc));
+    for (int c = 0; c < NC; ++c) {
+      if (!gate_row) {
+        wv[c] = *reinterpret_cast<const float4*>(p.wr + static_cast<size_t>(row) * H + 4 * lane +
+                                                 4 * kWave * c);
+      } else {
+        const uint2 g2 = *reinterpret_cast<const uint2*>(p.shared_gate + 4 * lane + 4 * kWave * c);
+        wv[c] = make_float4(bf16_bits_to_f32(g2.x & 0xFFFFu), bf16_bits_to_f32(g2.x >> 16),
+                            bf16_bits_to_f32(g2.y & 0xFFFFu), bf16_bits_to_f32(g2.y >> 16));
       }
     }
-  } else if (row == p.E && p.shared_gate != nullptr) {
-    uint2 gv[NC];
+    const double b = (!gate_row && p.bias) ? static_cast<double>(p.bias[row]) : 0.0;
+    for (int tg = t0; tg < t1; tg += G) {
+      uint2 xb[G][NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      gv[c] = *reinterpret_cast<const uint2*>(p.shared_gate + 4 * lane + 4 * kWave * c);
-    for (int t = t0; t < t1; ++t) {
-      const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
-      double acc = 0.0;
+      for (int j = 0; j < G; ++j) {
+        const int t = min(tg + j, t1 - 1);  // past the tile: repeat its last token
+        const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          xb[j][c] = *reinterpret_cast<const uint2*>(xt + 4 * lane + 4 * kWave * c);
+      }
+      double acc[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) acc[j] = 0.0;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint2 xb = *reinterpret_cast<const uint2*>(xt + 4 * lane + 4 * kWave * c);
-        acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].x & 0xFFFFu)),
-                  static_cast<double>(bf16_bits_to_f32(xb.x & 0xFFFFu)), acc);
-        acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].x >> 16)),
-                  static_cast<double>(bf16_bits_to_f32(xb.x >> 16)), acc);
-        acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].y & 0xFFFFu)),
-                  static_cast<double>(bf16_bits_to_f32(xb.y & 0xFFFFu)), acc);
-        acc = fma(static_cast<double>(bf16_bits_to_f32(gv[c].y >> 16)),
-                  static_cast<double>(bf16_bits_to_f32(xb.y >> 16)), acc);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const uint2 x2 = xb[j][c];
+          acc[j] = fma(static_cast<double>(wv[c].x), static_cast<double>(bf16_bits_to_f32(x2.x & 0xFFFFu)), acc[j]);
+          acc[j] = fma(static_cast<double>(wv[c].y), static_cast<double>(bf16_bits_to_f32(x2.x >> 16)), acc[j]);
+          acc[j] = fma(static_cast<double>(wv[c].z), static_cast<double>(bf16_bits_to_f32(x2.y & 0xFFFFu)), acc[j]);
+          acc[j] = fma(static_cast<double>(wv[c].w), static_cast<double>(bf16_bits_to_f32(x2.y >> 16)), acc[j]);
+        }
       }
-      acc = wave_sum_f64(acc);
-      if (lane == 0) p.gamma[t] = static_cast<float>(1.0 / (1.0 + exp(-acc)));
+#pragma unroll
+      for (int j = 0; j < G; ++j) acc[j] = wave_sum_f64(acc[j]);
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const int t = tg + j;
+          if (t >= t1) break;
+          if (!gate_row) {
+            st_dev(&p.logits[static_cast<size_t>(t) * p.E + row],
+                   static_cast<float>(p.bias ? acc[j] + b : acc[j]));
+          } else {
+            p.gamma[t] = static_cast<float>(1.0 / (1.0 + exp(-acc[j])));
+          }
+        }
+      }
     }
   }
 
@@ -134,6 +149,32 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void topk_kernel(RouteParams p)
                  p.ids + static_cast<size_t>(t) * p.k, p.w + static_cast<size_t>(t) * p.k,
                  p.ids_copy ? p.ids_copy + static_cast<size_t>(t) * p.k : nullptr,
                  p.w_copy ? p.w_copy + static_cast<size_t>(t) * p.k : nullptr);
+}
+
+// One block of kTopkWaves waves per token, by rank counting (block_topk_rank):
+// lower latency than a wave per token, which a call of few tokens waits on.
+constexpr int kTopkWaves = 8;
+constexpr int kTopkBlockMaxTokens = 256;  // above this a wave per token (less work in all)
+
+__global__ __launch_bounds__(kTopkWaves* kWave) void topk_block_kernel(RouteParams p) {
+  __shared__ __align__(16) uint64_t s_key[kTopkWaves][kWave];
+  __shared__ __align__(16) uint64_t s_cand[kTopkMaxChunks * kTopkMaxK];
+  __shared__ double s_d[kTopkMaxK];
+  __shared__ int s_ids[kTopkMaxK];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const float* __restrict__ lg = p.logits + static_cast<size_t>(t) * p.E;
+  block_topk_rank<kTopkWaves>(p.E, p.k, [&](int e) { return lg[e]; }, s_key, s_cand, s_d, s_ids);
+  if (threadIdx.x < kWave) {
+    const float wt = softmax_from_terms(s_d, p.k);
+    if (lane < p.k) {
+      const size_t o = static_cast<size_t>(t) * p.k + lane;
+      p.ids[o] = s_ids[lane];
+      p.w[o] = wt;
+      if (p.ids_copy) p.ids_copy[o] = s_ids[lane];
+      if (p.w_copy) p.w_copy[o] = wt;
+    }
+  }
 }
 
 // Many tokens: logits as an fp64 matrix product on the MFMA units
@@ -231,7 +272,9 @@ hipError_t launch_route(const RouteParams& p0, bool fuse_topk, hipStream_t s) {
   // tokens per wave: as few as keep about kRouteTargetWaves waves busy (each
   // wave keeps its row in registers across its tokens)
   const long long work = static_cast<long long>(rows > 0 ? rows : 1) * p.T;
+  const int grp = route_token_group(p.H / (4 * kWave));
   p.tok_tile = static_cast<int>((work + kRouteTargetWaves - 1) / kRouteTargetWaves);
+  p.tok_tile = (p.tok_tile + grp - 1) / grp * grp;  // whole token groups
   p.tok_tile = p.tok_tile < 1 ? 1 : (p.tok_tile > kRouteMaxTokTile ? kRouteMaxTokTile : p.tok_tile);
   dim3 grid(gx, (p.T + p.tok_tile - 1) / p.tok_tile);
   dim3 block(kRouteWaves * kWave);
@@ -261,8 +304,12 @@ hipError_t launch_route_mfma(const RouteParams& p, hipStream_t s) {
 }
 
 hipError_t launch_topk(const RouteParams& p, hipStream_t s) {
-  dim3 grid((p.T + kRouteWaves - 1) / kRouteWaves);
-  topk_kernel<<<grid, dim3(kRouteWaves * kWave), 0, s>>>(p);
+  if (p.T <= kTopkBlockMaxTokens) {
+    topk_block_kernel<<<dim3(p.T), dim3(kTopkWaves * kWave), 0, s>>>(p);
+  } else {
+    dim3 grid((p.T + kRouteWaves - 1) / kRouteWaves);
+    topk_kernel<<<grid, dim3(kRouteWaves * kWave), 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 
