@@ -79,11 +79,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
 }
 
 // fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+// Written as a select (no branch: a wave stays converged).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = (u >> 16) | 0x0040u;
+  return static_cast<uint16_t>((u & 0x7FFFFFFFu) > 0x7F800000u ? quiet_nan : rounded);
 }
 
 // ------------------------------------------------------- wave reductions --
@@ -484,9 +485,14 @@ __device__ __forceinline__ float ld_vmem_f32(const float* base, int index) {
 
 // ------------------------------------------------------------- activation --
 
-// silu(z) = z / (1 + exp(-z)); for very negative z, exp(-z) overflows to +inf and
-// the quotient is -0 (never NaN).
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z / (1 + exp(-z)), with the hardware base-2 exponential and
+// reciprocal (each about 1 ulp; the result within a few fp32 ulp, far below the
+// bf16 resolution of the outputs).  For very negative z, exp(-z) overflows to +inf,
+// its reciprocal is 0 and the result is -0 (never NaN); NaN stays NaN.
+__device__ __forceinline__ float silu(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // act 0: silu(g) * u.  act 1: silu(min(g, gate_max)) * clamp(u, -up_absmax, up_absmax).
 // Written as compare-and-select so that a NaN input stays NaN.

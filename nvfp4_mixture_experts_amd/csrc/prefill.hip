@@ -464,16 +464,107 @@ __device__ __forceinline__ void pf_mainloop_rows(
   }
 }
 
+// The gate|up K loop for H = 256 NSS, fully unrolled (no loop back edge, so the
+// register rings below need no copies and every slot index is a constant): the
+// weight tiles are double-buffered in LDS (8 slab tiles), so super-slab ss + 1 is
+// dequantised, a quarter before each slab's MFMAs, while super-slab ss is being
+// multiplied, with one barrier per super-slab; token rows run R - 1 slabs ahead,
+// weight codes RS super-slabs ahead.
+template <int NSS, int FR, int R, int RS>
+__device__ __forceinline__ void pf_mainloop_rows_unrolled(
+    const uint8_t* wc, const uint8_t* ws, const long long (&rowoff)[4], int H,
+    const uint16_t* const (&brow)[1][FR], int nfr, uint4 (*tiles)[kPfRows * kLdsRowU4],
+    int lane, f32x4 (&acc)[FR][8]) {
+  constexpr int NS = 4 * NSS;  // 64-K slabs
+  static_assert(RS >= 1 && RS <= NSS && R >= 2, "ring depths");
+  const int tid = threadIdx.x;
+  const int seg = tid & 7;  // 32-K segment of the super-slab
+  uint4 xr[R][FR][2];
+  uint4 qr[RS][4];
+  uint32_t sr[RS][4];
+  auto load_b = [&](int s, uint4 (&dst)[FR][2]) {
+#pragma unroll
+    for (int f = 0; f < FR; ++f) {
+      dst[f][0] = ld16(brow[0][f] + s * kPfSlab);
+      dst[f][1] = ld16(brow[0][f] + s * kPfSlab + 8);
+    }
+  };
+  auto load_w = [&](int ss, uint4 (&q)[4], uint32_t (&sc)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q[i] = ld16(wc + rowoff[i] * (H / 2) + ss * (kSuperSlab / 2));
+      sc[i] = *reinterpret_cast<const uint16_t*>(ws + rowoff[i] * (H / 16) + ss * (kSuperSlab / 16));
+    }
+  };
+  // piece i (tile rows (tid >> 3) + 32 i) of a super-slab into LDS buffer `buf`
+  auto dequant_piece = [&](const uint4 (&q)[4], const uint32_t (&sc)[4], int i, int buf) {
+    uint4* dst = tiles[4 * buf + (seg >> 1)] + ((tid >> 3) + 32 * i) * kLdsRowU4 + (seg & 1) * 4;
+    const float s0 = e4m3_byte_to_f32<0>(sc[i]), s1 = e4m3_byte_to_f32<1>(sc[i]);
+    dst[0] = dequant8_bf16(q[i].x, s0);
+    dst[1] = dequant8_bf16(q[i].y, s0);
+    dst[2] = dequant8_bf16(q[i].z, s1);
+    dst[3] = dequant8_bf16(q[i].w, s1);
+  };
+
+  // prologue: weights of super-slabs 0 .. RS-1, token rows of slabs 0 .. R-2,
+  // super-slab 0 dequantised into buffer 0
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    load_w(r, qr[r], sr[r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int r = 0; r < R - 1 && r < NS; ++r) {
+    load_b(r, xr[r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dequant_piece(qr[0], sr[0], i, 0);
+  if (RS < NSS) load_w(RS, qr[0], sr[0]);
+  __syncthreads();
+
+#pragma unroll
+  for (int ss = 0; ss < NSS; ++ss) {
+    const int nx = (ss + 1) % RS;  // ring slot of super-slab ss + 1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 4 * ss + j;
+      if (s + R - 1 < NS) load_b(s + R - 1, xr[(s + R - 1) % R]);
+      if (ss + 1 < NSS) dequant_piece(qr[nx], sr[nx], j, (ss + 1) & 1);
+      const uint4* tile = tiles[4 * (ss & 1) + j];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        uint4 a[8];
+#pragma unroll
+        for (int rf = 0; rf < 8; ++rf)
+          a[rf] = tile[(rf * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + st];
+#pragma unroll
+        for (int f = 0; f < FR; ++f) {
+          if (f < nfr) {
+#pragma unroll
+            for (int rf = 0; rf < 8; ++rf)
+              acc[f][rf] = mfma_bf16(a[rf], xr[s % R][f][st], acc[f][rf]);
+          }
+        }
+      }
+    }
+    if (ss + 1 + RS < NSS) load_w(ss + 1 + RS, qr[nx], sr[nx]);
+    __syncthreads();  // buffer (ss + 1) & 1 written; buffer ss & 1 free
+  }
+}
+
 }  // namespace
 
 // Blocks of 4 waves run two per CU, blocks of 8 waves one per CU.
 template <int W>
 constexpr int kBlocksPerCu = W == 4 ? 2 : 1;
 
-template <int FR, int R, int RS, int BPC>
+// NSS > 0: H = 256 NSS with the unrolled K loop (R, RS its ring depths); NSS = 0:
+// any H with the looped one.
+template <int FR, int R, int RS, int BPC, int NSS>
 __global__ __launch_bounds__(256, BPC) void pf_gateup_kernel(PrefillParams p) {
   constexpr int W = 4;
-  __shared__ uint4 tiles[4][kPfRows * kLdsRowU4];
+  __shared__ uint4 tiles[NSS > 0 ? 8 : 4][kPfRows * kLdsRowU4];
   int u, tile;
   unit_tile(p.ntiles1, &u, &tile);
   if (u >= *p.nunits) return;
@@ -509,7 +600,10 @@ __global__ __launch_bounds__(256, BPC) void pf_gateup_kernel(PrefillParams p) {
   for (int f = 0; f < FR; ++f)
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  pf_mainloop_rows<FR, R, RS>(wc, ws, rowoff, H, brow, nfr, H / kPfSlab, tiles, lane, acc);
+  if constexpr (NSS > 0)
+    pf_mainloop_rows_unrolled<NSS, FR, R, RS>(wc, ws, rowoff, H, brow, nfr, tiles, lane, acc);
+  else
+    pf_mainloop_rows<FR, R, RS>(wc, ws, rowoff, H, brow, nfr, H / kPfSlab, tiles, lane, acc);
 
   // epilogue: rows r < 4 are gate columns n0 + 16 r + 4 (lane / 16) + jj, r + 4 the
   // matching up columns
@@ -684,7 +778,12 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
   if (p.unit_tokens == kPfUnitTokens) {
     static_assert(Geometry<4, 4>::kUnitTokens == kPfUnitTokens, "unit size");
     static_assert(Geometry<8, 2>::kUnitTokens == kPfUnitTokens, "unit size");
-    pf_gateup_kernel<4, 2, 1, 1><<<g1, 4 * kWave, 0, s>>>(p);
+    switch (p.H) {
+      case 1024: pf_gateup_kernel<4, 4, 2, 1, 4><<<g1, 4 * kWave, 0, s>>>(p); break;
+      case 2048: pf_gateup_kernel<4, 4, 2, 1, 8><<<g1, 4 * kWave, 0, s>>>(p); break;
+      case 4096: pf_gateup_kernel<4, 4, 2, 1, 16><<<g1, 4 * kWave, 0, s>>>(p); break;
+      default: pf_gateup_kernel<4, 2, 1, 1, 0><<<g1, 4 * kWave, 0, s>>>(p); break;
+    }
     pf_down_kernel<8, 2, 2, 4><<<g2, 8 * kWave, 0, s>>>(p);
   } else {
     // few tokens per expert: units of at most 16 tokens, each a separate pass over
