@@ -464,6 +464,63 @@ __device__ __forceinline__ void pf_mainloop_rows(
   }
 }
 
+// The down K loop for K = 64 NS with the whole weight tile in LDS: every thread's
+// codes of all NS slabs are loaded and dequantised up front (one barrier), then the
+// MFMAs run over the NS slabs with no further barrier, token rows (NB operands)
+// R - 1 slabs ahead in a ring whose slots are constants (the loop is unrolled).
+template <int W, int FR, int NB, int R, int NS>
+__device__ __forceinline__ void pf_mainloop_whole_a(
+    const uint8_t* wc, size_t wc_step, const uint8_t* ws, size_t ws_step,
+    const uint16_t* const (&brow)[NB][FR], int nfr, uint4 (*lds)[kPfRows * kLdsRowU4],
+    int drow, int dpart, int lane, f32x4 (&acc)[FR][8]) {
+  constexpr int KPT = Geometry<W, FR>::kKpt;
+  static_assert(R >= 2 && R <= NS, "ring depth");
+  Codes<KPT> cr[NS];
+  uint4 xr[R][NB][FR][2];
+  auto load_b = [&](int s, uint4 (&dst)[NB][FR][2]) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int f = 0; f < FR; ++f) {
+        dst[b][f][0] = ld16(brow[b][f] + s * kPfSlab);
+        dst[b][f][1] = ld16(brow[b][f] + s * kPfSlab + 8);
+      }
+  };
+#pragma unroll
+  for (int s = 0; s < NS; ++s) cr[s].load(wc + s * wc_step, ws + s * ws_step);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < R - 1; ++r) {
+    load_b(r, xr[r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) cr[s].to_lds(&lds[s][drow * kLdsRowU4 + dpart * (KPT / 8)]);
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s + R - 1 < NS) load_b(s + R - 1, xr[(s + R - 1) % R]);
+    const uint4* tile = lds[s];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint4 a[8];
+#pragma unroll
+      for (int rf = 0; rf < 8; ++rf)
+        a[rf] = tile[(rf * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + j];
+#pragma unroll
+      for (int f = 0; f < FR; ++f) {
+        if (f < nfr) {
+#pragma unroll
+          for (int rf = 0; rf < 8; ++rf)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+              acc[f][rf] = mfma_bf16(a[rf], xr[s % R][b][f][j], acc[f][rf]);
+        }
+      }
+    }
+  }
+}
+
 // The gate|up K loop for H = 256 NSS, fully unrolled (no loop back edge, so the
 // register rings below need no copies and every slot index is a constant): the
 // weight tiles are double-buffered in LDS (8 slab tiles), so super-slab ss + 1 is
@@ -639,10 +696,12 @@ __global__ __launch_bounds__(256, BPC) void pf_gateup_kernel(PrefillParams p) {
   }
 }
 
-template <int W, int FR, int R, int RW>
+// NS > 0: I = 64 NS for both banks, the whole weight tile in LDS
+// (pf_mainloop_whole_a, R its token ring depth); NS = 0: any I, looped.
+template <int W, int FR, int R, int RW, int NS>
 __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(PrefillParams p) {
   using G = Geometry<W, FR>;
-  __shared__ uint4 lds[2][kPfRows * kLdsRowU4];
+  __shared__ uint4 lds[NS > 0 ? NS : 2][kPfRows * kLdsRowU4];
   int u, tile;
   unit_tile(p.ntiles2, &u, &tile);
   if (u >= *p.nunits) return;
@@ -674,13 +733,38 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(Pre
     brow[1][f] = p.hlo + row * p.Imax + (lane >> 4) * 16;
   }
 
+  // where each fragment's outputs go, and their weights: looked up before the main
+  // loop, so that the epilogue does not wait on a chain of dependent loads
+  int ot[FR], oslot[FR];
+  float owt[FR];
+#pragma unroll
+  for (int f = 0; f < FR; ++f) {
+    const int m = min(frag_token<W>(wave, f, lane), un.count - 1);
+    if (un.bank) {
+      ot[f] = un.start + m;
+      oslot[f] = p.k;
+      owt[f] = p.gamma[ot[f]];
+    } else {
+      const int pair = p.sorted[un.start + m];
+      ot[f] = pair / p.k;
+      oslot[f] = pair - ot[f] * p.k;
+      owt[f] = p.w[pair];
+    }
+  }
+
   f32x4 acc[FR][8];
 #pragma unroll
   for (int f = 0; f < FR; ++f)
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  pf_mainloop<W, FR, 2, R, RW>(wc, static_cast<size_t>(2) * H * 16, ws, static_cast<size_t>(2) * H * 2,
-                       brow, nfr, I / kPfSlab, lds, drow, dpart, lane, acc);
+  if constexpr (NS > 0)
+    pf_mainloop_whole_a<W, FR, 2, R, NS>(wc, static_cast<size_t>(2) * H * 16, ws,
+                                         static_cast<size_t>(2) * H * 2, brow, nfr, lds, drow,
+                                         dpart, lane, acc);
+  else
+    pf_mainloop<W, FR, 2, R, RW>(wc, static_cast<size_t>(2) * H * 16, ws,
+                                 static_cast<size_t>(2) * H * 2, brow, nfr, I / kPfSlab, lds, drow,
+                                 dpart, lane, acc);
 
   // epilogue: output rows h0 + 16 r + 4 (lane / 16) + jj of token m
   const float gd = bank.gsc[un.expert * 3 + 2];
@@ -688,18 +772,8 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(Pre
   for (int f = 0; f < FR; ++f) {
     const int m = frag_token<W>(wave, f, lane);
     if (f >= nfr || m >= un.count) continue;
-    int t, slot;
-    float wt;
-    if (un.bank) {
-      t = un.start + m;
-      slot = p.k;
-      wt = p.gamma[t];
-    } else {
-      const int pair = p.sorted[un.start + m];
-      t = pair / p.k;
-      slot = pair - t * p.k;
-      wt = p.w[pair];
-    }
+    const int t = ot[f], slot = oslot[f];
+    const float wt = owt[f];
     float* dst = p.out + (static_cast<size_t>(t) * p.nslots + slot) * H + h0 + (lane >> 4) * 4;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -784,7 +858,10 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
       case 4096: pf_gateup_kernel<4, 4, 2, 1, 16><<<g1, 4 * kWave, 0, s>>>(p); break;
       default: pf_gateup_kernel<4, 2, 1, 1, 0><<<g1, 4 * kWave, 0, s>>>(p); break;
     }
-    pf_down_kernel<8, 2, 2, 4><<<g2, 8 * kWave, 0, s>>>(p);
+    if (p.routed.inter == 512 && (p.shared.inter == 0 || p.shared.inter == 512))
+      pf_down_kernel<8, 2, 3, 4, 8><<<g2, 8 * kWave, 0, s>>>(p);
+    else
+      pf_down_kernel<8, 2, 2, 4, 0><<<g2, 8 * kWave, 0, s>>>(p);
   } else {
     // few tokens per expert: units of at most 16 tokens, each a separate pass over
     // its expert's weights (the passes of one expert run side by side)

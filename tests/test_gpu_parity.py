@@ -239,6 +239,24 @@ def test_grouped_decode_shapes_outside_the_workloads(gpu):
         assert_output_close(gpu.bf16_bits(y), ref["y"], f"grouped odd shapes H={H}")
 
 
+@pytest.mark.parametrize("H,I,Is,T", [(1024, 768, 768, 16), (3072, 1024, 1024, 24),
+                                      (2048, 512, 0, 40), (4096, 512, 512, 64)])
+def test_grouped_decode_pipelined_shapes(gpu, H, I, Is, T):
+    """The few-token grouped kernels at every width they are unrolled for: gate|up
+    with H / 512 = 2, 6, 4, 8 K blocks, down with I / 128 = 6, 8, 4, 4 pieces (one
+    case without a shared expert), T up to 64."""
+    w = synth.Workload(f"pipe_{H}_{I}", 24, H, I, 4, T, True, 2.0 ** -6, seed=H + I + T,
+                       shared_inter=Is)
+    L = synth.make_layer(w)
+    dl = gpu.upload_layer(L)
+    x = synth.make_tokens(w)
+    y, ids, _ = gpu.decode(dl, gpu.tokens_to_device(x))
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(L, x)
+    assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+    assert_output_close(gpu.bf16_bits(y), ref["y"], f"grouped pipelined H={H} I={I}")
+
+
 @pytest.mark.parametrize("tokens", [4, 16])   # fused kernel, grouped path
 def test_decode_is_deterministic(gpu, tokens):
     """Same inputs -> same bits, across workspace addresses and streams."""

@@ -121,6 +121,27 @@ def test_prefill_is_deterministic(gpu):
     assert np.array_equal(a, b) and np.array_equal(a, c)
 
 
+@pytest.mark.parametrize("H,Is", [(1024, 512), (2048, 512), (4096, 0)])
+def test_prefill_unrolled_widths(gpu, H, Is):
+    """The many-token kernels with the unrolled gate|up K loop (H / 256 = 4, 8, 16
+    super-slabs) and the whole-tile down product (I = 512 for both banks; one case
+    without a shared expert): T = 300, so the shared unit holds 256 tokens."""
+    w = synth.dataclasses.replace(synth.WORKLOADS["prefill_t8192"], num_experts=16, top_k=4,
+                                  tokens=300, hidden=H, inter=512, shared_inter=Is,
+                                  seed=600 + H + Is)
+    L = synth.make_layer(w)
+    x = synth.make_tokens(w)
+    dl = gpu.upload_layer(L)
+    xd = gpu.tokens_to_device(x)
+    ids, wt = gpu.route(dl, xd)
+    y = gpu.prefill(dl, xd, ids, wt)
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 64, 127, 128, 200, 255, 256, 299]
+    ref = oracle.moe_layer(L, x[rows])
+    assert np.array_equal(ids.cpu().numpy()[rows], ref["ids"])
+    assert_output_close(gpu.bf16_bits(y)[rows], ref["y"], f"prefill unrolled H={H}")
+
+
 @pytest.mark.slow
 def test_prefill_full_chunk_sampled(gpu):
     """The 8192-token chunk at full size: routes of sampled tokens bit-exact, and
