@@ -498,7 +498,6 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         }
       }
       if (!prefetched) {  // behind the first gate|up loads, ahead of their use
-        prefetch_down();
         prefetched = true;
         weights_one_token();
       }
@@ -521,7 +520,10 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         }
       }
     }
-    if (!prefetched) prefetch_down();
+    // the down chunks only now: the gate|up stream (which every h, and so every
+    // down unit, waits for) has the memory system to itself, and the down loads
+    // are in flight while the h values travel between blocks
+    prefetch_down();
     weights_one_token();
   }
 
