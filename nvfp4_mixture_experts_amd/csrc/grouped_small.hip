@@ -67,8 +67,11 @@ __device__ __forceinline__ uint32_t word(const uint4& q, int j) {
 }
 
 // Row tiles of 64 per block in the pipelined down product: their codes are all in
-// registers at once (NKC 16-byte words per tile and lane).
-constexpr int down_pipe_tiles(int nkc) { return nkc <= 4 ? 4 : 2; }
+// registers at once (NKC 16-byte words per tile and lane).  Two keep a block small
+// enough in registers for 3 waves per SIMD, so the whole grid of a decode batch is
+// resident at once (4 tiles share the staged h better but fit only 2 waves per SIMD,
+// and the grid then ran in two rounds).
+constexpr int kDownPipeTiles = 2;
 
 __device__ __forceinline__ void sg_unit_tile(int ntiles, int* u, int* tile) {
   const int b = blockIdx.x;
@@ -405,7 +408,7 @@ template <int NKC>
 __global__ __launch_bounds__(kSgThreads, 2) void sg_down_pipe_kernel(PrefillParams p) {
   constexpr int kI = 128 * NKC;
   constexpr int kRowU4 = kI / 8 + 1;
-  constexpr int kRT = down_pipe_tiles(NKC);                // row tiles per block
+  constexpr int kRT = kDownPipeTiles;                      // row tiles per block
   constexpr int kHL = 2 * 16 * (kI / 8) / kSgThreads;      // h loads per thread
   static_assert(kHL * kSgThreads == 2 * 16 * (kI / 8), "whole staging rounds");
   __shared__ uint4 hs[2][16 * kRowU4];
@@ -530,7 +533,7 @@ hipError_t launch_grouped_small(const PrefillParams& p0, int ugroups, hipStream_
   const bool one_i = p.shared.inter == 0 || p.shared.inter == I;
   const int nkc = (one_i && p.H % 256 == 0 && I % 128 == 0) ? I / 128 : 0;
   if (nkc == 4 || nkc == 6 || nkc == 8) {
-    p.ntiles2 = p.H / (64 * down_pipe_tiles(nkc));
+    p.ntiles2 = p.H / (64 * kDownPipeTiles);
     const dim3 g2(ugroups * 8 * p.ntiles2);
     if (nkc == 4) sg_down_pipe_kernel<4><<<g2, blk, 0, s>>>(p);
     else if (nkc == 6) sg_down_pipe_kernel<6><<<g2, blk, 0, s>>>(p);
