@@ -137,9 +137,10 @@ size_t ft_moe_workspace_bytes(const ft_moe_desc *desc, int64_t tokens, int32_t p
 
 /* Router only (FreeToken commit log, page 2: the MoE router / shared gate kernels
  * entry and the non-power-of-2 top-k router entry): logits with exact fp32 x bf16
- * products summed in fp64 and rounded once to fp32 (from 1024 tokens on the fp64
- * MFMA units), top-k (ties to the lower index) and softmax weights of the
- * selected logits.
+ * products summed in fp64 and rounded once to fp32 (from 24 tokens on the fp64
+ * MFMA units, split along K below 1024 tokens; the splits summed in a fixed
+ * order), top-k (ties to the lower index) and softmax weights of the selected
+ * logits.
  *   x         bf16 [T][H]      w_router f32 [E][H]      bias f32 [E] or NULL
  *   topk_ids  i32  [T][k]      topk_w   f32 [T][k]      (outputs, rank order)
  * 0 <= T <= 2^21 (T == 0 enqueues nothing). */

@@ -63,6 +63,24 @@ constexpr int kMaxDecodeTokens = 64;
 constexpr int kGroupedDecodeMinTokens = 8;
 // Router calls of at least this many tokens compute the logits on the MFMA units.
 constexpr int kRouteMfmaMinTokens = 1024;
+// From this many tokens (and below kRouteMfmaMinTokens) the router is the split-K
+// fp64 MFMA product; below it the row kernel (its last block selecting up to
+// route_fused_topk_tokens() tokens, else a top-k kernel).  Measured on the batched
+// decode workload: the split router saves 2-5 us from 32 tokens on and costs
+// 1-2 us at 8 and 16 (its two kernels each pay a memory round trip).
+int route_split_min_tokens() { return 24; }
+
+// Bytes of the split router's partial sums for up to T tokens (the largest over
+// every token count it serves, so that a workspace for T serves smaller T).
+size_t route_split_cap(const ft_moe_desc& d, int64_t T) {
+  size_t cap = 0;
+  const int64_t hi = T < kRouteMfmaMinTokens ? T : kRouteMfmaMinTokens - 1;
+  for (int64_t t = route_split_min_tokens(); t <= hi; ++t) {
+    const size_t b = route_split_bytes(d.num_experts, static_cast<int>(t), d.hidden);
+    cap = b > cap ? b : cap;
+  }
+  return cap;
+}
 constexpr int kRowGroup = 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -121,6 +139,7 @@ Bank to_bank(const ft_nvfp4_experts* b, int inter) {
 // token counts once it has been zero-filled.
 struct Layout {
   size_t sync, gen, logits, h, part;                                 // route / fused decode
+  size_t rsplit;                                                     // split-K router partials
   size_t ids, w;                                                     // routes of a grouped decode
   size_t gamma, count, cursor, offset, units, nunits, sorted, hhi, hlo, out;  // grouped experts
   size_t total;
@@ -161,6 +180,7 @@ Layout layout(const ft_moe_desc& d, int64_t T, int path) {
   };
   if (path == 0) {
     L.logits = take(t * E * 4);
+    L.rsplit = take(route_split_cap(d, T));
   } else if (path == 1) {
     // the fused kernel's regions, then (for token counts that take the grouped
     // path) router logits, routes and the grouped regions
@@ -173,6 +193,7 @@ Layout layout(const ft_moe_desc& d, int64_t T, int path) {
     if (T >= kGroupedDecodeMinTokens) {
       L.ids = take(t * k * 4);
       L.w = take(t * k * 4);
+      L.rsplit = take(route_split_cap(d, T));
       grouped();
     }
   } else {
@@ -219,7 +240,7 @@ ft_status check_layer_args(const ft_moe_desc* desc, const uint16_t* x,
 ft_status run_route(const ft_moe_desc* desc, int T, const uint16_t* x, const float* w_router,
                     const float* bias, const uint16_t* shared_gate, float* logits, float* gamma,
                     int32_t* ids, float* w, int32_t* ids_copy, float* w_copy, uint32_t* counter,
-                    hipStream_t s) {
+                    double* split_part, hipStream_t s) {
   RouteParams p{};
   p.x = x;
   p.wr = w_router;
@@ -250,6 +271,14 @@ ft_status run_route(const ft_moe_desc* desc, int T, const uint16_t* x, const flo
     }
     e = launch_topk(p, s);
     if (e != hipSuccess) return hip_fail(e, "top-k kernel");
+    return FT_OK;
+  }
+  if (T >= route_split_min_tokens()) {
+    // split-K fp64 MFMA partial sums, then a block per token sums them (in split
+    // order), rounds once to fp32 and selects
+    p.part = split_part;
+    e = launch_route_split(p, s);
+    if (e != hipSuccess) return hip_fail(e, "split router kernels");
     return FT_OK;
   }
   // the last block to finish selects the experts when it has a wave per token;
@@ -391,7 +420,7 @@ ft_status ft_moe_route(const ft_moe_desc* desc, int64_t tokens, const uint16_t* 
   st = run_route(desc, static_cast<int>(tokens), x, w_router, bias, nullptr,
                  at<float>(workspace, L.logits), nullptr, topk_ids, topk_w, nullptr, nullptr,
                  at<uint32_t>(workspace, L.sync) + kRouteCounterWord,
-                 static_cast<hipStream_t>(stream));
+                 at<double>(workspace, L.rsplit), static_cast<hipStream_t>(stream));
   if (st != FT_OK) return st;
   return ok();
 }
@@ -423,7 +452,8 @@ ft_status ft_moe_nvfp4_decode(const ft_moe_desc* desc, int64_t tokens, const uin
     float* wts = at<float>(workspace, L.w);
     st = run_route(desc, T, x, w_router, bias, shared_gate, at<float>(workspace, L.logits),
                    has_shared ? at<float>(workspace, L.gamma) : nullptr, ids, wts, topk_ids_out,
-                   topk_w_out, at<uint32_t>(workspace, L.sync) + kRouteCounterWord, s);
+                   topk_w_out, at<uint32_t>(workspace, L.sync) + kRouteCounterWord,
+                   at<double>(workspace, L.rsplit), s);
     if (st != FT_OK) return st;
     st = run_grouped(desc, T, x, ids, wts, routed, shared, y, workspace, L, s);
     if (st != FT_OK) return st;

@@ -33,6 +33,8 @@ struct RouteParams {
   float* w_copy;                // optional second copy of w
   uint32_t* counter;            // last-arriver counter for the fused top-k
   int tok_tile;                 // tokens per wave (set by the launcher)
+  double* part;                 // split-K router: f64 [ksplit][T][E + 1] partial sums
+  int ksplit;                   // K splits (set by the launcher)
 };
 
 // The whole decode layer in one persistent launch (one block per CU).  Values
@@ -117,6 +119,11 @@ hipError_t launch_decode_fused(const FusedParams& p, int grid, hipStream_t s);
 int fused_block_threads();
 hipError_t launch_route(const RouteParams& p, bool fuse_topk, hipStream_t s);
 int route_fused_topk_tokens();  // the fused top-k handles at most this many tokens
+// Split-K fp64 MFMA router (for a few to a thousand tokens): K splits it uses for
+// (E, T, H), and the bytes of its partial sums.
+int route_split_k(int E, int T, int H);
+size_t route_split_bytes(int E, int T, int H);
+hipError_t launch_route_split(const RouteParams& p, hipStream_t s);
 hipError_t launch_topk(const RouteParams& p, hipStream_t s);
 // logits only (no shared gate, no top-k), as an fp64 MFMA product; H % 64 == 0
 hipError_t launch_route_mfma(const RouteParams& p, hipStream_t s);

@@ -73,6 +73,15 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_logits_kernel(RouteP
       }
     }
     const double b = (!gate_row && p.bias) ? static_cast<double>(p.bias[row]) : 0.0;
+    // the row in fp64 once, not once per token
+    double wd[NC][4];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      wd[c][0] = static_cast<double>(wv[c].x);
+      wd[c][1] = static_cast<double>(wv[c].y);
+      wd[c][2] = static_cast<double>(wv[c].z);
+      wd[c][3] = static_cast<double>(wv[c].w);
+    }
     for (int tg = t0; tg < t1; tg += G) {
       uint2 xb[G][NC];
 #pragma unroll
@@ -91,10 +100,10 @@ __global__ __launch_bounds__(kRouteWaves* kWave) void route_logits_kernel(RouteP
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           const uint2 x2 = xb[j][c];
-          acc[j] = fma(static_cast<double>(wv[c].x), static_cast<double>(bf16_bits_to_f32(x2.x & 0xFFFFu)), acc[j]);
-          acc[j] = fma(static_cast<double>(wv[c].y), static_cast<double>(bf16_bits_to_f32(x2.x >> 16)), acc[j]);
-          acc[j] = fma(static_cast<double>(wv[c].z), static_cast<double>(bf16_bits_to_f32(x2.y & 0xFFFFu)), acc[j]);
-          acc[j] = fma(static_cast<double>(wv[c].w), static_cast<double>(bf16_bits_to_f32(x2.y >> 16)), acc[j]);
+          acc[j] = fma(wd[c][0], static_cast<double>(bf16_bits_to_f32(x2.x & 0xFFFFu)), acc[j]);
+          acc[j] = fma(wd[c][1], static_cast<double>(bf16_bits_to_f32(x2.x >> 16)), acc[j]);
+          acc[j] = fma(wd[c][2], static_cast<double>(bf16_bits_to_f32(x2.y & 0xFFFFu)), acc[j]);
+          acc[j] = fma(wd[c][3], static_cast<double>(bf16_bits_to_f32(x2.y >> 16)), acc[j]);
         }
       }
 #pragma unroll
@@ -261,6 +270,171 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteParams p) {
       p.logits[static_cast<size_t>(t) * p.E + e] = static_cast<float>(v);
     }
   }
+}
+
+// A few to a thousand tokens: the same fp64 MFMA product, split along K so that
+// the whole chip shares it (an fp64 MFMA takes 64 cycles, so one block per 64
+// experts would leave most CUs idle).  Block (row block, token block, split):
+// 4 waves x 16 rows (expert rows, then row E = the shared gate, bf16) x 32 tokens
+// (2 fragments of 16) over K [split * kc, (split + 1) * kc), into
+// part[split][t][row].  topk_split_kernel sums the splits in split order.
+constexpr int kRouteSplitRows = 64;
+constexpr int kRouteSplitTokens = 32;
+constexpr int kRouteSplitTargetBlocks = 512;
+constexpr int kRouteMaxSplits = 32;
+
+__global__ __launch_bounds__(256) void route_split_kernel(RouteParams p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int R = p.E + 1;
+  const int r0 = blockIdx.x * kRouteSplitRows + wave * 16;
+  const int t0 = blockIdx.y * kRouteSplitTokens;
+  const int kc = p.H / p.ksplit;
+  const int kbeg = blockIdx.z * kc;
+  const int H = p.H;
+  const int g = lane >> 4, i = lane & 15;
+  const int row = min(r0 + i, R - 1);  // rows past the end repeat the last (not stored)
+  const bool gate_row = row == p.E;
+  const bool zero_row = gate_row && p.shared_gate == nullptr;
+  const float* wrow = p.wr + static_cast<size_t>(gate_row ? 0 : row) * H + 16 * g;
+  const uint16_t* grow = p.shared_gate ? p.shared_gate + 16 * g : nullptr;
+  const uint16_t* xrow[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+    xrow[f] = p.x + static_cast<size_t>(min(t0 + 16 * f + i, p.T - 1)) * H + 16 * g;
+  f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+  for (int k0 = kbeg; k0 < kbeg + kc; k0 += 64) {
+    // lane group g holds K = k0 + 16 g + m in step m, for A and B alike
+    float w[16];
+    if (!gate_row) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 v = *reinterpret_cast<const float4*>(wrow + k0 + 4 * c);
+        w[4 * c] = v.x;
+        w[4 * c + 1] = v.y;
+        w[4 * c + 2] = v.z;
+        w[4 * c + 3] = v.w;
+      }
+    } else if (!zero_row) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint4 v = *reinterpret_cast<const uint4*>(grow + k0 + 8 * c);
+        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          w[8 * c + 2 * m] = bf16_bits_to_f32(q[m] & 0xFFFFu);
+          w[8 * c + 2 * m + 1] = bf16_bits_to_f32(q[m] >> 16);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) w[m] = 0.0f;
+    }
+    uint32_t xw[2][8];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const uint4 a = *reinterpret_cast<const uint4*>(xrow[f] + k0);
+      const uint4 b = *reinterpret_cast<const uint4*>(xrow[f] + k0 + 8);
+      xw[f][0] = a.x; xw[f][1] = a.y; xw[f][2] = a.z; xw[f][3] = a.w;
+      xw[f][4] = b.x; xw[f][5] = b.y; xw[f][6] = b.z; xw[f][7] = b.w;
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const double a = static_cast<double>(w[m]);
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const uint32_t pair = xw[f][m >> 1];
+        const double b =
+            static_cast<double>(bf16_bits_to_f32((m & 1) ? (pair >> 16) : (pair & 0xFFFFu)));
+        acc[f] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[f], 0, 0, 0);
+      }
+    }
+  }
+  // C lane l: rows r0 + l / 16 + 4 j of token t0 + 16 f + l % 16
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int t = t0 + 16 * f + i;
+    if (t >= p.T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = r0 + g + 4 * j;
+      if (r < R) p.part[(static_cast<size_t>(blockIdx.z) * p.T + t) * R + r] = acc[f][j];
+    }
+  }
+}
+
+// One block per token: the logits from the split partial sums (summed in split
+// order, the bias added in fp64, one fp32 rounding; row E gives the shared gate),
+// then the rank-count top-k.
+__global__ __launch_bounds__(kTopkWaves* kWave) void topk_split_kernel(RouteParams p) {
+  __shared__ float s_logit[kMaxExperts];
+  __shared__ __align__(16) uint64_t s_key[kTopkWaves][kWave];
+  __shared__ __align__(16) uint64_t s_cand[kTopkMaxChunks * kTopkMaxK];
+  __shared__ double s_d[kTopkMaxK];
+  __shared__ int s_ids[kTopkMaxK];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int R = p.E + 1;
+  const size_t stride = static_cast<size_t>(p.T) * R;
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    const double* src = p.part + static_cast<size_t>(t) * R + r;
+    // every split's load in flight at once (indices clamped), then the sum in
+    // split order
+    double pv[kRouteMaxSplits];
+#pragma unroll
+    for (int ks = 0; ks < kRouteMaxSplits; ++ks)
+      pv[ks] = src[static_cast<size_t>(ks < p.ksplit ? ks : p.ksplit - 1) * stride];
+    double v = 0.0;
+#pragma unroll
+    for (int ks = 0; ks < kRouteMaxSplits; ++ks) v = ks < p.ksplit ? v + pv[ks] : v;
+    if (r < p.E) {
+      if (p.bias) v += static_cast<double>(p.bias[r]);
+      const float lf = static_cast<float>(v);
+      s_logit[r] = lf;
+      if (p.logits) p.logits[static_cast<size_t>(t) * p.E + r] = lf;
+    } else if (p.gamma && p.shared_gate) {
+      p.gamma[t] = static_cast<float>(1.0 / (1.0 + exp(-v)));
+    }
+  }
+  __syncthreads();
+  block_topk_rank<kTopkWaves>(p.E, p.k, [&](int e) { return s_logit[e]; }, s_key, s_cand, s_d,
+                              s_ids);
+  if (threadIdx.x < kWave) {
+    const float wt = softmax_from_terms(s_d, p.k);
+    if (lane < p.k) {
+      const size_t o = static_cast<size_t>(t) * p.k + lane;
+      p.ids[o] = s_ids[lane];
+      p.w[o] = wt;
+      if (p.ids_copy) p.ids_copy[o] = s_ids[lane];
+      if (p.w_copy) p.w_copy[o] = wt;
+    }
+  }
+}
+
+int route_split_k(int E, int T, int H) {
+  const int nrb = (E + 1 + kRouteSplitRows - 1) / kRouteSplitRows;
+  const int ntb = (T + kRouteSplitTokens - 1) / kRouteSplitTokens;
+  const int kmax = H / 64;  // 64-K steps
+  int ks = 1;
+  // the largest power of two that divides H / 64 and keeps about the target blocks
+  while ((kmax % (2 * ks)) == 0 && 2 * ks <= kRouteMaxSplits &&
+         nrb * ntb * 2 * ks <= kRouteSplitTargetBlocks)
+    ks *= 2;
+  return ks;
+}
+
+size_t route_split_bytes(int E, int T, int H) {
+  return static_cast<size_t>(route_split_k(E, T, H)) * T * (E + 1) * sizeof(double);
+}
+
+hipError_t launch_route_split(const RouteParams& p0, hipStream_t s) {
+  RouteParams p = p0;
+  p.ksplit = route_split_k(p.E, p.T, p.H);
+  dim3 grid((p.E + 1 + kRouteSplitRows - 1) / kRouteSplitRows,
+            (p.T + kRouteSplitTokens - 1) / kRouteSplitTokens, p.ksplit);
+  route_split_kernel<<<grid, 256, 0, s>>>(p);
+  topk_split_kernel<<<dim3(p.T), dim3(kTopkWaves * kWave), 0, s>>>(p);
+  return hipGetLastError();
 }
 
 int route_fused_topk_tokens() { return kRouteWaves; }

@@ -128,6 +128,8 @@ def _check_routes(ids, w, ref_ids, ref_w, what):
                                          ("batched_decode_t32_hot64", 32),
                                          ("decode_e512_top10_shared", 64),
                                          ("decode_e512_top10_shared", 333),
+                                         # split-K router; 289 rows (not a multiple of 64)
+                                         ("decode_e288_top8", 100),
                                          # MFMA router; experts not a multiple of 64
                                          ("decode_e288_top8", 1100)])
 def test_route_matches_oracle(gpu, name, tokens):
@@ -142,7 +144,8 @@ def test_route_matches_oracle(gpu, name, tokens):
     _check_routes(ids, wt, ref_ids, ref_w, f"{name} T={tokens}")
 
 
-def test_route_ties_go_to_lowest_index(gpu):
+@pytest.mark.parametrize("tokens", [16, 40])  # row router, split-K router
+def test_route_ties_go_to_lowest_index(gpu, tokens):
     """Duplicated router rows give exactly equal logits; the lower index must win."""
     from nvfp4_mixture_experts_amd import ftmoe
     w = synth.dataclasses.replace(synth.WORKLOADS["decode_e288_top8"], num_experts=96)
@@ -150,18 +153,18 @@ def test_route_ties_go_to_lowest_index(gpu):
     wr = L.w_router.copy()
     wr[50:96] = wr[0:46]                      # experts 50.. duplicate 0..45
     wr[10] = wr[70]                           # and a tie inside the copy
-    x = synth.make_tokens(w, tokens=16, stream="ties")
+    x = synth.make_tokens(w, tokens=tokens, stream="ties")
     xd = gpu.tokens_to_device(x)
     desc = ftmoe.make_desc(96, w.hidden, w.inter, w.top_k, 1)
-    wsp = ftmoe.alloc_workspace(desc, 16, ftmoe.PATH_ROUTE)
-    ids = torch.empty((16, w.top_k), dtype=torch.int32, device="cuda")
-    wt = torch.empty((16, w.top_k), dtype=torch.float32, device="cuda")
+    wsp = ftmoe.alloc_workspace(desc, tokens, ftmoe.PATH_ROUTE)
+    ids = torch.empty((tokens, w.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((tokens, w.top_k), dtype=torch.float32, device="cuda")
     ftmoe.ft_moe_route(desc, xd, torch.from_numpy(wr).cuda(), None, ids, wt, wsp)
     torch.cuda.synchronize()
     ref_ids, ref_w = oracle.topk(oracle.router_logits(x, wr), w.top_k)
     # every token must have at least one tie inside its top-k for the test to bite
     lg = oracle.router_logits(x, wr)
-    ties = sum(len(set(lg[t, ref_ids[t]].tolist())) < w.top_k for t in range(16))
+    ties = sum(len(set(lg[t, ref_ids[t]].tolist())) < w.top_k for t in range(tokens))
     assert ties > 0
     _check_routes(ids, wt, ref_ids, ref_w, "ties")
 
