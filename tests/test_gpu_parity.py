@@ -260,7 +260,7 @@ def test_grouped_decode_pipelined_shapes(gpu, H, I, Is, T):
     assert_output_close(gpu.bf16_bits(y), ref["y"], f"grouped pipelined H={H} I={I}")
 
 
-@pytest.mark.parametrize("tokens", [4, 16])   # fused kernel, grouped path
+@pytest.mark.parametrize("tokens", [4, 16, 40])   # fused kernel, grouped path (row, split router)
 def test_decode_is_deterministic(gpu, tokens):
     """Same inputs -> same bits, across workspace addresses and streams."""
     from nvfp4_mixture_experts_amd import ftmoe
@@ -286,7 +286,7 @@ def test_decode_is_deterministic(gpu, tokens):
     assert torch.equal(y0.view(torch.int16), y2.view(torch.int16))
 
 
-@pytest.mark.parametrize("tokens", [1, 12])   # fused kernel, grouped path
+@pytest.mark.parametrize("tokens", [1, 12, 40])   # fused kernel, grouped path (row, split router)
 def test_decode_graph_replays_match_eager(gpu, tokens):
     from nvfp4_mixture_experts_amd import ftmoe
     name = "decode_e288_top8"
