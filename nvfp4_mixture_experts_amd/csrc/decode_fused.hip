@@ -23,10 +23,13 @@
 //      for each expert, the keys above its own: first inside its 64-expert
 //      chunk, then among the chunks' candidates (no serial select rounds; ties
 //      go to the lower index).
-//   W  every wave issues its gate|up loads, then the loads of its first
-//      down-projection chunks (kept in registers for D), then computes:
-//      e2m1 -> bf16 in registers, v_dot2_f32_bf16 against bf16 x, per-16 e4m3
-//      block scales, global scales, (clamped) SwiGLU; h published tagged.
+//   W  every wave issues its gate|up loads, takes the routing weights (in its
+//      own registers), then computes: e2m1 -> bf16 in registers,
+//      v_dot2_f32_bf16 against bf16 x, per-16 e4m3 block scales, global
+//      scales, (clamped) SwiGLU; h published tagged.  Only then does it issue
+//      the loads of its first down-projection chunks (kept in registers for D):
+//      the gate|up stream, which every h waits for, has HBM to itself, and the
+//      down loads travel while h crosses between blocks.
 //   D  down GEMV from the prefetched chunks (lane = output row, K-chunk-major
 //      codes; the h chunks of a wave's units polled together, one round trip,
 //      and broadcast from LDS), weighted by routing weight or

@@ -87,6 +87,22 @@ def test_workspace_bytes_and_desc_validation(ft):
         assert ft.ft_moe_workspace_bytes(d, 1, 1) == 0
 
 
+def test_workspace_bytes_never_shrink_with_tokens(ft):
+    """A workspace sized for T tokens serves every smaller T (the header's
+    contract): the size is non-decreasing in T on every path, across the token
+    counts where the router and the grouped path change form (4/5, 7/8, 23/24,
+    63/64/65, 1023/1024) and across the split router's token-block boundaries."""
+    descs = [ft.make_desc(288, 2048, 768, 8, 1),
+             ft.make_desc(512, 2048, 512, 10, 1, shared_inter=512),
+             ft.make_desc(1024, 4096, 1024, 16, 1, shared_inter=256),
+             ft.make_desc(8, 256, 128, 2, 0)]
+    Ts = list(range(0, 130)) + list(range(130, 1100, 7)) + [1023, 1024, 1025, 4096, 8192]
+    for d in descs:
+        for path in (0, 1, 2):
+            sizes = [ft.ft_moe_workspace_bytes(d, T, path) for T in sorted(set(Ts))]
+            assert all(b >= a for a, b in zip(sizes, sizes[1:])), (path, sizes[:8])
+
+
 def _raw(ft):
     return ft._lib
 
