@@ -34,6 +34,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 namespace {
 
 constexpr int kPfRows = 128;               // weight rows per block tile
+constexpr unsigned kPersistentBlocks = 256;  // one per CU of MI355X (LDS holds one)
 constexpr int kPfSlab = 64;                // K elements per LDS slab
 constexpr int kLdsRowU4 = kPfSlab / 8 + 1; // 16-byte words per LDS row (one of padding)
 
@@ -343,16 +344,18 @@ __device__ __forceinline__ void pf_mainloop(
 #pragma unroll
         for (int rf = 0; rf < 8; ++rf)
           a[rf] = tile[(rf * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + j];
+        // operand b outermost: consecutive MFMAs write different accumulators
+        // (an MFMA right after one into the same accumulator waits for it)
 #pragma unroll
-        for (int f = 0; f < FR; ++f) {
-          if (live && f < nfr) {
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int rf = 0; rf < 8; ++rf)
+          for (int f = 0; f < FR; ++f) {
+            if (live && f < nfr) {
 #pragma unroll
-              for (int b = 0; b < NB; ++b)
+              for (int rf = 0; rf < 8; ++rf)
                 acc[f][rf] = mfma_bf16(a[rf], xr[r % R][b][f][j], acc[f][rf]);
+            }
           }
-        }
       }
       // weights of slab s + 1 (its buffer was last read in iteration s - 1), then
       // the codes of slab s + 1 + RW into the freed ring slot
@@ -507,16 +510,17 @@ __device__ __forceinline__ void pf_mainloop_whole_a(
 #pragma unroll
       for (int rf = 0; rf < 8; ++rf)
         a[rf] = tile[(rf * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + j];
+      // operand b outermost: consecutive MFMAs write different accumulators
 #pragma unroll
-      for (int f = 0; f < FR; ++f) {
-        if (f < nfr) {
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int rf = 0; rf < 8; ++rf)
+        for (int f = 0; f < FR; ++f) {
+          if (f < nfr) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int rf = 0; rf < 8; ++rf)
               acc[f][rf] = mfma_bf16(a[rf], xr[s % R][b][f][j], acc[f][rf]);
+          }
         }
-      }
     }
   }
 }
@@ -789,6 +793,179 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(Pre
 
 // y[t] = bf16(sum over slots, in slot order); a pair whose expert id is out of
 // range was never computed and makes its token's row NaN.
+// The down product for I = 64 NS (both banks) as a persistent kernel: one block
+// per CU walks the work items (unit, 128-row tile) in the order of the
+// one-block-per-item launch (item b goes to block b mod grid, so a unit's tiles
+// stay on one XCD).  The whole weight tile of an item is dequantised into LDS;
+// while its MFMAs run, the next item's codes are already being loaded into
+// registers, so an item does not start with a memory latency.
+template <int NS, int R>
+__global__ __launch_bounds__(8 * kWave, 1) void pf_down_persistent_kernel(PrefillParams p,
+                                                                         int nitems) {
+  constexpr int W = 8, FR = 2;
+  using G = Geometry<W, FR>;
+  constexpr int KPT = G::kKpt;
+  constexpr int kI = 64 * NS;
+  __shared__ uint4 lds[NS][kPfRows * kLdsRowU4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = p.H;
+  const int nunits = *p.nunits;
+  const int drow = tid / G::kTpr, dpart = tid % G::kTpr;
+  const int kofs = dpart * G::kKpt;  // K offset within the slab
+
+  auto item_unit = [&](int it, int* u, int* tile) {
+    *u = (it / (8 * p.ntiles2)) * 8 + (it & 7);
+    *tile = (it >> 3) % p.ntiles2;
+  };
+  // the first item at or after `it` (stride: the grid) whose unit exists
+  auto next_item = [&](int it, int* u, int* tile) {
+    for (; it < nitems; it += gridDim.x) {
+      item_unit(it, u, tile);
+      if (*u < nunits) break;
+    }
+    // uniform across the block: the unit's descriptor is then a scalar load,
+    // which does not wait behind the vector loads in flight
+    *u = __builtin_amdgcn_readfirstlane(*u);
+    *tile = __builtin_amdgcn_readfirstlane(*tile);
+    return __builtin_amdgcn_readfirstlane(it);
+  };
+  // Loads of an item issued one item ahead.  The memory counter completes in
+  // issue order, so the (token, slot) pair indices go first: the dependent weight
+  // loads of the next item then wait for them alone, not for the codes.
+  Codes<KPT> cr[NS];
+  int pr[FR];
+  auto load_item = [&](const PfUnit& un, int tile) {
+#pragma unroll
+    for (int f = 0; f < FR; ++f) {
+      const int m = min(frag_token<W>(wave, f, lane), un.count - 1);
+      pr[f] = un.bank ? 0 : p.sorted[un.start + m];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const Bank bank = un.bank ? p.shared : p.routed;
+    const size_t chunk0 = static_cast<size_t>(un.expert) * (kI / 32) + (kofs >> 5);
+    const size_t row = static_cast<size_t>(tile) * kPfRows + drow;
+    const uint8_t* wc = bank.w2 + (chunk0 * H + row) * 16 + (kofs & 31) / 2;
+    const uint8_t* ws = bank.w2s + (chunk0 * H + row) * 2 + (kofs & 31) / 16;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      cr[s].load(wc + static_cast<size_t>(s) * 2 * H * 16, ws + static_cast<size_t>(s) * 2 * H * 2);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int u, tile;
+  int it = next_item(blockIdx.x, &u, &tile);
+  if (it >= nitems) return;
+  PfUnit un = p.units[u];
+  load_item(un, tile);
+  for (;;) {
+    const Bank bank = un.bank ? p.shared : p.routed;
+    const int h0 = tile * kPfRows;
+    __syncthreads();  // the previous item's MFMAs are done with the tile
+#pragma unroll
+    for (int s = 0; s < NS; ++s) cr[s].to_lds(&lds[s][drow * kLdsRowU4 + dpart * (KPT / 8)]);
+    // the next item (found before any load goes out: a loop with loads in flight
+    // would make the compiler wait for them at its head), this item's output
+    // places and weights (from its pair indices), then the next item's loads: all
+    // in flight during this item's MFMAs
+    int nu = 0, ntile = 0;
+    const int nit = next_item(it + gridDim.x, &nu, &ntile);
+    // read unconditionally (a valid index), so that it is a scalar load
+    const PfUnit nun = p.units[nit < nitems ? nu : u];
+    const int nfr = wave_fragments<W, FR>(un.count, wave);
+    const uint16_t* brow[2][FR];
+    int ot[FR], oslot[FR];
+    float owt[FR];
+#pragma unroll
+    for (int f = 0; f < FR; ++f) {
+      const int m = min(frag_token<W>(wave, f, lane), un.count - 1);
+      const size_t row = un.bank ? static_cast<size_t>(p.P) + un.start + m
+                                 : static_cast<size_t>(un.start) + m;
+      brow[0][f] = p.hhi + row * p.Imax + (lane >> 4) * 16;
+      brow[1][f] = p.hlo + row * p.Imax + (lane >> 4) * 16;
+      if (un.bank) {
+        ot[f] = un.start + m;
+        oslot[f] = p.k;
+        owt[f] = p.gamma[ot[f]];
+      } else {
+        ot[f] = pr[f] / p.k;
+        oslot[f] = pr[f] - ot[f] * p.k;
+        owt[f] = p.w[pr[f]];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (nit < nitems) load_item(nun, ntile);
+
+    uint4 xr[R][2][FR][2];
+    auto load_b = [&](int s, uint4 (&dst)[2][FR][2]) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int f = 0; f < FR; ++f) {
+          dst[b][f][0] = ld16(brow[b][f] + s * kPfSlab);
+          dst[b][f][1] = ld16(brow[b][f] + s * kPfSlab + 8);
+        }
+    };
+#pragma unroll
+    for (int r = 0; r < R - 1; ++r) load_b(r, xr[r]);
+    __syncthreads();  // the tile is in LDS
+
+    f32x4 acc[FR][8];
+#pragma unroll
+    for (int f = 0; f < FR; ++f)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + R - 1 < NS) load_b(s + R - 1, xr[(s + R - 1) % R]);
+      const uint4* t = lds[s];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint4 a[8];
+#pragma unroll
+        for (int rf = 0; rf < 8; ++rf)
+          a[rf] = t[(rf * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + j];
+        // h_hi products first, then h_lo: consecutive MFMAs write different
+        // accumulators (an MFMA right after one into the same accumulator waits)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int f = 0; f < FR; ++f) {
+            if (f < nfr) {
+#pragma unroll
+              for (int rf = 0; rf < 8; ++rf)
+                acc[f][rf] = mfma_bf16(a[rf], xr[s % R][b][f][j], acc[f][rf]);
+            }
+          }
+      }
+    }
+
+    // epilogue: output rows h0 + 16 r + 4 (lane / 16) + jj of token m
+    const float gd = bank.gsc[un.expert * 3 + 2];
+#pragma unroll
+    for (int f = 0; f < FR; ++f) {
+      const int m = frag_token<W>(wave, f, lane);
+      if (f >= nfr || m >= un.count) continue;
+      float* dst = p.out + (static_cast<size_t>(ot[f]) * p.nslots + oslot[f]) * H + h0 +
+                   (lane >> 4) * 4;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        float4 v;
+        v.x = (acc[f][r][0] * gd) * owt[f];
+        v.y = (acc[f][r][1] * gd) * owt[f];
+        v.z = (acc[f][r][2] * gd) * owt[f];
+        v.w = (acc[f][r][3] * gd) * owt[f];
+        *reinterpret_cast<float4*>(dst + r * 16) = v;
+      }
+    }
+    if (nit >= nitems) break;
+    it = nit;
+    u = nu;
+    tile = ntile;
+    un = nun;
+  }
+}
+
 __global__ __launch_bounds__(256) void pf_combine_kernel(PrefillParams p) {
   const int H4 = p.H / 4;
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -859,7 +1036,8 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
       default: pf_gateup_kernel<4, 2, 1, 1, 0><<<g1, 4 * kWave, 0, s>>>(p); break;
     }
     if (p.routed.inter == 512 && (p.shared.inter == 0 || p.shared.inter == 512))
-      pf_down_kernel<8, 2, 3, 4, 8><<<g2, 8 * kWave, 0, s>>>(p);
+      pf_down_persistent_kernel<8, 2><<<g2 < kPersistentBlocks ? g2 : kPersistentBlocks, 8 * kWave, 0, s>>>(
+          p, static_cast<int>(g2));
     else
       pf_down_kernel<8, 2, 2, 4, 0><<<g2, 8 * kWave, 0, s>>>(p);
   } else {
