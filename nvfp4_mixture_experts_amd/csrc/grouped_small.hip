@@ -481,24 +481,32 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_pipe_kernel(PrefillPara
       hs[which][n * kRowU4 + c8] = hv[r];
     }
     __syncthreads();
+    // the tiles step through K together: each h word is read once for all tiles,
+    // and consecutive MFMAs write different accumulators (h_hi products of every
+    // tile, then h_lo; each accumulator adds its terms in the same order)
     sg_f32x4 acc[kRT];
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
-      // the tiles read the same h words: re-read them per tile rather than let the
-      // compiler keep all of them live across the tiles (it would run out of registers)
-      asm volatile("" ::: "memory");
-      acc[rt] = sg_f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < kRT; ++rt) acc[rt] = sg_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NKC; ++s) {
+    for (int s = 0; s < NKC; ++s) {
+      float s0[kRT], s1[kRT];
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
         const uint32_t sw = sc[rt][s] >> (16 * (i & 1));  // rows are even + i
-        const float s0 = e4m3_byte_to_f32<0>(sw), s1 = e4m3_byte_to_f32<1>(sw);
+        s0[rt] = e4m3_byte_to_f32<0>(sw);
+        s1[rt] = e4m3_byte_to_f32<1>(sw);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint4 a = dq8(word(q[rt][s], j), j < 2 ? s0 : s1);
-          const int kk = (4 * s + g) * 4 + j;  // 16-byte word of the staged row
-          acc[rt] = mfma(a, hs[0][i * kRowU4 + kk], acc[rt]);
-          acc[rt] = mfma(a, hs[1][i * kRowU4 + kk], acc[rt]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int kk = (4 * s + g) * 4 + j;  // 16-byte word of the staged row
+        const uint4 bh = hs[0][i * kRowU4 + kk], bl = hs[1][i * kRowU4 + kk];
+        uint4 a[kRT];
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) a[rt] = dq8(word(q[rt][s], j), j < 2 ? s0[rt] : s1[rt]);
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) acc[rt] = mfma(a[rt], bh, acc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) acc[rt] = mfma(a[rt], bl, acc[rt]);
       }
     }
     if (m < un.count) {
