@@ -264,16 +264,14 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   __shared__ __align__(16) uint64_t s_cand[kTopkMaxChunks * kTopkMaxK];
   __shared__ double s_d[kMaxK];
   __shared__ __align__(16) float s_hb[kFWaves][32 * kUD];  // h values of a down batch
-  __shared__ uint32_t s_gen;
+  __shared__ uint32_t s_gen[kFWaves];
 
-  // generation of this call: this block's own call count
-  if (threadIdx.x == 0) {
-    const uint32_t g = ld_dev(&p.gen[blockIdx.x]) + 1u;
-    st_dev(&p.gen[blockIdx.x], g);
-    s_gen = g;
-  }
-  __syncthreads();
-  const uint32_t gen = s_gen;
+  // Generation of this call: this block's own call count.  Every wave reads the
+  // counter itself and nothing waits for it here, so the read travels together
+  // with the router loads instead of costing a round trip (and a barrier) before
+  // them.  The new count is stored after the selection's barrier; each wave puts
+  // its copy into LDS before that barrier, so every read has returned by then.
+  const uint32_t gen = ld_dev(&p.gen[blockIdx.x]) + 1u;
 
   // ---------------------------------------------------------------- R --
   {
@@ -325,6 +323,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   }
 
   // ---------------------------------------------------------------- S --
+  if (lane == 0) s_gen[wave] = gen;  // needs the counter read to have returned
   {
     const uint64_t* lgc = p.logits + static_cast<size_t>(blockIdx.x % kLogitCopies) * T * E1;
     const bool has_shared = p.shared_gate != nullptr;
@@ -351,6 +350,14 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         }
       }
     }
+  }
+  // past the selection's barrier: every wave of the block holds this call's count
+  // (all copies are equal; reading them all keeps each wave's LDS store live)
+  if (threadIdx.x == 0) {
+    uint32_t g = s_gen[0];
+#pragma unroll
+    for (int w = 1; w < kFWaves; ++w) g = s_gen[w] > g ? s_gen[w] : g;
+    st_dev(&p.gen[blockIdx.x], g);
   }
 
   // One token: the routing weights (lane i: place i) and the shared gate, taken
