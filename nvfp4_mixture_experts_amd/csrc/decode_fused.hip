@@ -243,7 +243,11 @@ __device__ __forceinline__ Unit2 unit2(int v, int k, FastDiv nch) {
 
 // ---------------------------------------------------------------- kernel --
 
-template <int LPR, int CPL>
+// ONE: the call has one token (T == 1).  That instantiation has no activation
+// loads inside the gate|up compute loop: vmcnt counts stores too and completes in
+// order, so a load there would make the next unit's wait cover the device-coherent
+// h stores issued before it, and every unit would wait for their acknowledgement.
+template <int LPR, int CPL, bool ONE>
 __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(FusedParams p) {
   constexpr int GPW = kWave / LPR;   // lane groups per wave
   constexpr int NC = LPR * CPL / 8;  // float4 pieces of a router row per lane (H / 256)
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   const int G = gridDim.x;
   const int gw = blockIdx.x * kFWaves + wave;
   const int NW = G * kFWaves;
-  const int H = p.H, E = p.E, T = p.T, k = p.k;
+  const int H = p.H, E = p.E, T = ONE ? 1 : p.T, k = p.k;
   const int nrg = H / kWave;
   const int E1 = E + 1;
 
@@ -360,21 +364,27 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     st_dev(&p.gen[blockIdx.x], g);
   }
 
-  // One token: the routing weights (lane i: place i) and the shared gate, taken
-  // by every wave in its own registers once its first expert loads are out.
+  // One token: the routing weights (lane i: place i), taken by every wave in its
+  // own registers once its first expert loads are out, and the shared gate.  The
+  // gate's tagged word is read once, with no wait, behind those loads (the router
+  // wrote it long before); its tag is checked, and polled only if it does not
+  // match, just before the down phase.  No memory access here is conditional:
+  // vmcnt completes in order, and a conditional access between the weight loads
+  // and their use would make the compiler's wait counts cover later stores.
   float w1 = 0.0f, gamma1 = 0.0f;
+  uint64_t gate_word = 0;
+  const uint64_t* gate_addr = p.logits + static_cast<size_t>(blockIdx.x % kLogitCopies) * E1 + E;
   bool have_w1 = T != 1;
   auto weights_one_token = [&]() {
     if (have_w1) return;
     have_w1 = true;
     w1 = softmax_from_terms(s_d, k);
-    gamma1 = p.shared_gate ? poll_gate(p.logits + static_cast<size_t>(blockIdx.x % kLogitCopies) * E1,
-                                       E, gen, p.spin_limit, p.err)
-                           : 0.0f;
-    if (blockIdx.x == 0 && wave == 0 && lane < k) {
-      if (p.ids_out) p.ids_out[lane] = s_ids[lane];
-      if (p.w_out) p.w_out[lane] = w1;
-    }
+    gate_word = ld_tag(gate_addr);  // word E exists (unused) without a shared expert
+  };
+  auto gate_one_token = [&]() {
+    if (T != 1 || !p.shared_gate) return;
+    if (!tag_is(gate_word, gen)) gate_word = tagged(poll_gate(gate_addr - E, E, gen, p.spin_limit, p.err), gen);
+    gamma1 = tag_value(gate_word);
   };
   // routing weight (or shared gate) of slot `slot` (k: the shared expert) of token t
   auto slot_weight = [&](int t, int slot) -> float {
@@ -437,11 +447,13 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   uint32_t ps[kUD];
   DownUnit pdu[kUD];
   const bool have_first = g_first < p.d_groups;
-  // issues the loads of this wave's first down units (kept in registers until D)
+  // issues the loads of this wave's first down units (kept in registers until D).
+  // A block with no down group loads group 0's (never used): the loads are not
+  // conditional, so the in-order wait counts after them stay exact.
   auto prefetch_down = [&]() {
-    if (!have_first) return;
-    const int t = fdiv(g_first, fd_nrg);
-    const int c = (g_first - t * nrg) * kWave + lane;
+    const int g0 = have_first ? g_first : 0;
+    const int t = fdiv(g0, fd_nrg);
+    const int c = (g0 - t * nrg) * kWave + lane;
 #pragma unroll
     for (int i = 0; i < kUD; ++i) {
       pdu[i] = down_unit(t, sub + bpg * (wave + kFWaves * i), c);
@@ -476,7 +488,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         }
       }
     };
-    if (T == 1) load_x(0);
+    if (ONE) load_x(0);
     bool prefetched = false;
     for (int j0 = 0; (gw * GPW) + NG * j0 < total; j0 += kUW) {
       Unit13 un[kUW];
@@ -511,9 +523,10 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         prefetched = true;
         weights_one_token();
       }
+      float hv[kUW];
 #pragma unroll
       for (int jj = 0; jj < kUW; ++jj) {
-        if (T != 1) load_x(un[jj].t);
+        if (!ONE) load_x(un[jj].t);
         float ag = 0.0f, au = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
@@ -522,12 +535,18 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         }
         ag = group_sum_last<LPR>(ag);
         au = group_sum_last<LPR>(au);
-        if (col == LPR - 1 && un[jj].valid) {
-          const float hv = swiglu(p.act, ag * g_gate[jj], au * g_up[jj], p.gate_max, p.up_absmax);
+        hv[jj] = swiglu(p.act, ag * g_gate[jj], au * g_up[jj], p.gate_max, p.up_absmax);
+      }
+      // the batch's h values, published after all of its units are computed: the
+      // stores are conditional, and one issued between a unit's loads and their use
+      // would make the compiler's in-order wait for that unit cover its
+      // acknowledgement
+#pragma unroll
+      for (int jj = 0; jj < kUW; ++jj) {
+        if (col == LPR - 1 && un[jj].valid)
           st_tag(&p.h[(static_cast<size_t>(un[jj].t) * p.nslots + un[jj].slot) * p.Imax +
                       un[jj].r],
-                 hv, gen);
-        }
+                 hv[jj], gen);
       }
     }
     // the down chunks only now: the gate|up stream (which every h, and so every
@@ -538,6 +557,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   }
 
   // ---------------------------------------------------------------- D --
+  gate_one_token();
   bool first = true;
   for (int g = g_first; g < p.d_groups; g += g_step) {
     const int t = fdiv(g, fd_nrg);
@@ -637,17 +657,36 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     }
     __syncthreads();
   }
+  // one token: the routing side outputs, last (stores issued earlier would enter
+  // the in-order wait counts of the loads above)
+  if (T == 1 && blockIdx.x == 0 && wave == 0 && lane < k) {
+    if (p.ids_out) p.ids_out[lane] = s_ids[lane];
+    if (p.w_out) p.w_out[lane] = w1;
+  }
 }
 
 template <int LPR>
 static hipError_t launch_fused_lpr(const FusedParams& p, int grid, hipStream_t s) {
   const int cpl = p.H / (32 * LPR);
   dim3 g(grid), b(kFWaves * kWave);
+  const bool one = p.T == 1;
   switch (cpl) {
-    case 1: moe_decode_fused_kernel<LPR, 1><<<g, b, 0, s>>>(p); break;
-    case 2: moe_decode_fused_kernel<LPR, 2><<<g, b, 0, s>>>(p); break;
-    case 3: moe_decode_fused_kernel<LPR, 3><<<g, b, 0, s>>>(p); break;
-    case 4: moe_decode_fused_kernel<LPR, 4><<<g, b, 0, s>>>(p); break;
+    case 1:
+      if (one) moe_decode_fused_kernel<LPR, 1, true><<<g, b, 0, s>>>(p);
+      else moe_decode_fused_kernel<LPR, 1, false><<<g, b, 0, s>>>(p);
+      break;
+    case 2:
+      if (one) moe_decode_fused_kernel<LPR, 2, true><<<g, b, 0, s>>>(p);
+      else moe_decode_fused_kernel<LPR, 2, false><<<g, b, 0, s>>>(p);
+      break;
+    case 3:
+      if (one) moe_decode_fused_kernel<LPR, 3, true><<<g, b, 0, s>>>(p);
+      else moe_decode_fused_kernel<LPR, 3, false><<<g, b, 0, s>>>(p);
+      break;
+    case 4:
+      if (one) moe_decode_fused_kernel<LPR, 4, true><<<g, b, 0, s>>>(p);
+      else moe_decode_fused_kernel<LPR, 4, false><<<g, b, 0, s>>>(p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

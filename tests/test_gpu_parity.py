@@ -260,6 +260,27 @@ def test_grouped_decode_pipelined_shapes(gpu, H, I, Is, T):
     assert_output_close(gpu.bf16_bits(y), ref["y"], f"grouped pipelined H={H} I={I}")
 
 
+@pytest.mark.parametrize("name,tokens", [("tiny_e8_top2", 1), ("tiny_e8_top2", 3),
+                                         ("decode_e512_top10_shared", 1)])
+def test_decode_consecutive_calls_on_one_workspace(gpu, name, tokens):
+    """Several fused calls in a row on one workspace, each with new tokens, each
+    against the oracle.  Every block of the fused kernel must advance its own call
+    counter on every call, also blocks with no gate|up rows (the tiny layer has
+    256 rows for 2048 waves), or the next call's hand-offs never match."""
+    from nvfp4_mixture_experts_amd import ftmoe
+    w = synth.WORKLOADS[name]
+    dl = dev_layer(gpu, name)
+    L = host_layer(name)
+    ws = ftmoe.alloc_workspace(dl.desc, tokens, ftmoe.PATH_DECODE)
+    for i in range(4):
+        x = synth.make_tokens(w, tokens=tokens, stream=f"seq{i}")
+        y, ids, _ = gpu.decode(dl, gpu.tokens_to_device(x), workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.moe_layer(L, x)
+        assert np.array_equal(ids.cpu().numpy(), ref["ids"]), i
+        assert_output_close(gpu.bf16_bits(y), ref["y"], f"{name} T={tokens} call {i}")
+
+
 @pytest.mark.parametrize("tokens", [4, 16, 40])   # fused kernel, grouped path (row, split router)
 def test_decode_is_deterministic(gpu, tokens):
     """Same inputs -> same bits, across workspace addresses and streams."""
