@@ -171,7 +171,8 @@ Layout layout(const ft_moe_desc& d, int64_t T, int path) {
     L.cursor = take(E * 4);
     L.offset = take(E * 4);
     L.units = take(static_cast<size_t>(prefill_max_units(d.num_experts, Ti, ki,
-                                                         d.shared_inter > 0)) * sizeof(PfUnit));
+                                                         d.shared_inter > 0) + kUnitSlack) *
+                   sizeof(PfUnit));
     L.nunits = take(4);
     L.sorted = take(P * 4);
     L.hhi = take((P + t) * imax * 2);

@@ -75,6 +75,11 @@ constexpr int kSmallCallTokens = 64;  // calls of at most this many tokens take 
 constexpr int kSmallUnitTokens = 16;  // kernels, with units of at most this many tokens (one
                                       // MFMA column block: a unit's tokens share one weight pass)
 
+// Spare entries after the last possible unit of the unit table: the expert kernels
+// read units[u] (u < 8 * ceil(units / 8)) together with the unit count, before
+// checking u against it.
+constexpr int kUnitSlack = 8;
+
 struct PfUnit {
   int bank;    // 0 routed, 1 shared
   int expert;  // routed expert id (0 for the shared bank)

@@ -87,8 +87,10 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_kernel(PrefillParams 
   __shared__ uint4 xs[16 * kRowU4];
   int u, tile;
   sg_unit_tile(p.ntiles1, &u, &tile);
-  if (u >= *p.nunits) return;
-  const PfUnit un = p.units[u];
+  const int nun = *p.nunits;  // both loads issued before either is waited for
+  const PfUnit un = p.units[u];  // in bounds: the table has kUnitSlack spare entries
+  __asm__ volatile("" ::: "memory");  // keeps them here (not sunk past the check)
+  if (u >= nun) return;
   const Bank bank = un.bank ? p.shared : p.routed;
   const int I = bank.inter;
   const int n0 = tile * 64;
@@ -119,7 +121,8 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_kernel(PrefillParams 
         const int v = min(tid + r * kSgThreads, 16 * (kb / 8) - 1);
         const int n = v / (kb / 8), c8 = v - n * (kb / 8);
         const int m = min(f0 + n, un.count - 1);
-        const int t = un.bank ? un.start + m : p.sorted[un.start + m] / p.k;
+        const int tq = p.sorted[un.start + m] / p.k;  // read for both banks (in bounds: a
+        const int t = un.bank ? un.start + m : tq;    // shared unit's start + m < T <= P)
         xv[r] = ldg16(p.x + static_cast<size_t>(t) * H + k0 + 8 * c8);
       }
       __builtin_amdgcn_sched_barrier(0);  // token rows first (the staging waits for them)
@@ -200,8 +203,10 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_pipe_kernel(PrefillPa
   __shared__ uint4 xs[16 * kRowU4];
   int u, tile;
   sg_unit_tile(p.ntiles1, &u, &tile);
-  if (u >= *p.nunits) return;
-  const PfUnit un = p.units[u];
+  const int nun = *p.nunits;  // both loads issued before either is waited for
+  const PfUnit un = p.units[u];  // in bounds: the table has kUnitSlack spare entries
+  __asm__ volatile("" ::: "memory");  // keeps them here (not sunk past the check)
+  if (u >= nun) return;
   const Bank bank = un.bank ? p.shared : p.routed;
   const int I = bank.inter;
   const int n0 = tile * 64;
@@ -224,7 +229,8 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_pipe_kernel(PrefillPa
 #pragma unroll
     for (int r = 0; r < kXL; ++r) {
       const int m = min(f0 + (tid >> 6) + 4 * r, un.count - 1);  // past the unit: its last token
-      const int t = un.bank ? un.start + m : p.sorted[un.start + m] / p.k;
+      const int tq = p.sorted[un.start + m] / p.k;  // read for both banks (in bounds: a
+      const int t = un.bank ? un.start + m : tq;    // shared unit's start + m < T <= P)
       xrow[r] = p.x + static_cast<size_t>(t) * H + 8 * c8;
     }
     uint4 xv[2][kXL], qg[2][4], qu[2][4];
@@ -301,8 +307,10 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_kernel(PrefillParams p)
   __shared__ uint4 hs[2][16 * kRowU4];
   int u, tile;
   sg_unit_tile(p.ntiles2, &u, &tile);
-  if (u >= *p.nunits) return;
-  const PfUnit un = p.units[u];
+  const int nun = *p.nunits;  // both loads issued before either is waited for
+  const PfUnit un = p.units[u];  // in bounds: the table has kUnitSlack spare entries
+  __asm__ volatile("" ::: "memory");  // keeps them here (not sunk past the check)
+  if (u >= nun) return;
   const Bank bank = un.bank ? p.shared : p.routed;
   const int I = bank.inter;
   const int H = p.H;
@@ -414,8 +422,10 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_pipe_kernel(PrefillPara
   __shared__ uint4 hs[2][16 * kRowU4];
   int u, tg;
   sg_unit_tile(p.ntiles2, &u, &tg);
-  if (u >= *p.nunits) return;
-  const PfUnit un = p.units[u];
+  const int nun = *p.nunits;  // both loads issued before either is waited for
+  const PfUnit un = p.units[u];  // in bounds: the table has kUnitSlack spare entries
+  __asm__ volatile("" ::: "memory");  // keeps them here (not sunk past the check)
+  if (u >= nun) return;
   const Bank bank = un.bank ? p.shared : p.routed;
   const int H = p.H;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -430,7 +440,8 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_pipe_kernel(PrefillPara
     // the h and code loads, so that neither waits in front of them.
     const int m = f0 + i;
     const int mm = min(m, un.count - 1);
-    const int pair = un.bank ? 0 : p.sorted[un.start + mm];
+    const int sv = p.sorted[un.start + mm];  // read for both banks (in bounds: a shared
+    const int pair = un.bank ? 0 : sv;        // unit's start + mm < T <= P)
     uint4 hv[kHL];
 #pragma unroll
     for (int r = 0; r < kHL; ++r) {

@@ -628,8 +628,10 @@ __global__ __launch_bounds__(256, BPC) void pf_gateup_kernel(PrefillParams p) {
   __shared__ uint4 tiles[NSS > 0 ? 8 : 4][kPfRows * kLdsRowU4];
   int u, tile;
   unit_tile(p.ntiles1, &u, &tile);
-  if (u >= *p.nunits) return;
-  const PfUnit un = p.units[u];
+  const int nun = *p.nunits;  // both loads issued before either is waited for
+  const PfUnit un = p.units[u];  // in bounds: the table has kUnitSlack spare entries
+  __asm__ volatile("" ::: "memory");  // keeps them here (not sunk past the check)
+  if (u >= nun) return;
   const Bank bank = un.bank ? p.shared : p.routed;
   const int I = bank.inter;
   const int n0 = tile * 64;
@@ -652,7 +654,8 @@ __global__ __launch_bounds__(256, BPC) void pf_gateup_kernel(PrefillParams p) {
 #pragma unroll
   for (int f = 0; f < FR; ++f) {
     const int m = min(frag_token<W>(wave, f, lane), un.count - 1);
-    const int t = un.bank ? un.start + m : p.sorted[un.start + m] / p.k;
+    const int tq = p.sorted[un.start + m] / p.k;  // read for both banks (in bounds: a
+    const int t = un.bank ? un.start + m : tq;    // shared unit's start + m < T <= P)
     brow[0][f] = p.x + static_cast<size_t>(t) * H + (lane >> 4) * 16;
   }
 
@@ -708,8 +711,10 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(Pre
   __shared__ uint4 lds[NS > 0 ? NS : 2][kPfRows * kLdsRowU4];
   int u, tile;
   unit_tile(p.ntiles2, &u, &tile);
-  if (u >= *p.nunits) return;
-  const PfUnit un = p.units[u];
+  const int nun = *p.nunits;  // both loads issued before either is waited for
+  const PfUnit un = p.units[u];  // in bounds: the table has kUnitSlack spare entries
+  __asm__ volatile("" ::: "memory");  // keeps them here (not sunk past the check)
+  if (u >= nun) return;
   const Bank bank = un.bank ? p.shared : p.routed;
   const int I = bank.inter;
   const int H = p.H;
@@ -839,7 +844,8 @@ __global__ __launch_bounds__(8 * kWave, 1) void pf_down_persistent_kernel(Prefil
 #pragma unroll
     for (int f = 0; f < FR; ++f) {
       const int m = min(frag_token<W>(wave, f, lane), un.count - 1);
-      pr[f] = un.bank ? 0 : p.sorted[un.start + m];
+      const int sv = p.sorted[un.start + m];  // read for both banks (in bounds: a shared
+      pr[f] = un.bank ? 0 : sv;              // unit's start + m < T <= P)
     }
     __builtin_amdgcn_sched_barrier(0);
     const Bank bank = un.bank ? p.shared : p.routed;
