@@ -122,18 +122,31 @@ __device__ void group_units(const PrefillParams& p, int count, int* cursor) {
   const int e = threadIdx.x;
   const int ut = p.unit_tokens;
   const int nu = (count + ut - 1) / ut;
-  s_cnt[e] = count;
-  s_units[e] = nu;
-  __syncthreads();
-  // inclusive scans (Hillis-Steele) of counts and unit counts
-  for (int off = 1; off < kMaxExperts; off <<= 1) {
-    const int a = (e >= off) ? s_cnt[e - off] : 0;
-    const int b = (e >= off) ? s_units[e - off] : 0;
-    __syncthreads();
-    s_cnt[e] += a;
-    s_units[e] += b;
-    __syncthreads();
+  // inclusive scans of counts and unit counts: within each wave by lane shuffles,
+  // then each wave adds the totals of the waves before it (two block barriers)
+  __shared__ int s_wa[kMaxExperts / kWave], s_wb[kMaxExperts / kWave];
+  const int lane = e & (kWave - 1), wv = e / kWave;
+  int a = count, b = nu;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int ta = __shfl_up(a, off, kWave), tb = __shfl_up(b, off, kWave);
+    if (lane >= off) {
+      a += ta;
+      b += tb;
+    }
   }
+  if (lane == kWave - 1) {
+    s_wa[wv] = a;
+    s_wb[wv] = b;
+  }
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) {
+    a += s_wa[w];
+    b += s_wb[w];
+  }
+  s_cnt[e] = a;
+  s_units[e] = b;
+  __syncthreads();
   if (e < p.E) {
     const int off = s_cnt[e] - count;
     const int ubase = s_units[e] - nu;
@@ -173,22 +186,29 @@ __device__ __forceinline__ int valid_expert(const PrefillParams& p, int pair) {
 
 // Whole grouping in one block (few pairs): LDS counts, offsets, LDS cursors.
 __global__ __launch_bounds__(kMaxExperts) void pf_group_one_block_kernel(PrefillParams p) {
+  constexpr int kPer = kGroupOneBlockPairs / kMaxExperts;  // pairs per thread, at most
   __shared__ int cnt[kMaxExperts];
   __shared__ int cur[kMaxExperts];
   const int tid = threadIdx.x;
   cnt[tid] = 0;
-  __syncthreads();
-  for (int pair = tid; pair < p.P; pair += kMaxExperts) {
-    const int e = valid_expert(p, pair);
-    if (e >= 0) atomicAdd(&cnt[e], 1);
+  // every id this thread handles, loaded at once and kept for the scatter (a reload
+  // after the unit table's stores would wait for them: vmcnt completes in order)
+  int ev[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int pair = tid + j * kMaxExperts;
+    ev[j] = pair < p.P ? valid_expert(p, pair) : -1;
   }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (ev[j] >= 0) atomicAdd(&cnt[ev[j]], 1);
   __syncthreads();
   group_units(p, cnt[tid], cur);
   __syncthreads();
-  for (int pair = tid; pair < p.P; pair += kMaxExperts) {
-    const int e = valid_expert(p, pair);
-    if (e >= 0) p.sorted[atomicAdd(&cur[e], 1)] = pair;
-  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (ev[j] >= 0) p.sorted[atomicAdd(&cur[ev[j]], 1)] = tid + j * kMaxExperts;
 }
 
 // Many pairs: per-block LDS histograms added into count[] ...
@@ -978,19 +998,31 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PrefillParams p) {
   if (i >= static_cast<size_t>(p.T) * H4) return;
   const int t = static_cast<int>(i / H4);
   const int c = static_cast<int>(i - static_cast<size_t>(t) * H4) * 4;
-  bool bad = false;
-  for (int s = 0; s < p.k; ++s) {
-    const int e = p.ids[static_cast<size_t>(t) * p.k + s];
-    bad |= (e < 0 || e >= p.E);
-  }
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // Every id and every slot row is loaded before any is used (indices clamped to
+  // the token's own entries), then the slots are summed in slot order: a runtime
+  // loop would wait for each load in turn, one memory round trip per slot.
+  constexpr int kMaxSlots = kTopkMaxK + 1;
+  const int32_t* idr = p.ids + static_cast<size_t>(t) * p.k;
+  int ev[kTopkMaxK];
+#pragma unroll
+  for (int s = 0; s < kTopkMaxK; ++s) ev[s] = idr[s < p.k ? s : p.k - 1];
   const float* src = p.out + static_cast<size_t>(t) * p.nslots * p.H + c;
-  for (int s = 0; s < p.nslots; ++s) {
-    const float4 v = *reinterpret_cast<const float4*>(src + static_cast<size_t>(s) * p.H);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+  float4 v[kMaxSlots];
+#pragma unroll
+  for (int s = 0; s < kMaxSlots; ++s)
+    v[s] = *reinterpret_cast<const float4*>(src + static_cast<size_t>(s < p.nslots ? s : p.nslots - 1) * p.H);
+  bool bad = false;
+#pragma unroll
+  for (int s = 0; s < kTopkMaxK; ++s) bad |= (ev[s] < 0 || ev[s] >= p.E);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < kMaxSlots; ++s) {
+    if (s < p.nslots) {
+      acc.x += v[s].x;
+      acc.y += v[s].y;
+      acc.z += v[s].z;
+      acc.w += v[s].w;
+    }
   }
   if (bad) acc = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                              __builtin_nanf(""));
