@@ -48,6 +48,7 @@ constexpr int kUW = 3;         // gate|up units per wave and batch
 constexpr int kUD = 3;         // down units per wave and batch (first batch prefetched)
 constexpr int kMaxTK = 64 * 16;
 constexpr int kMaxK = kTopkMaxK;
+constexpr int kRouterWaitSpins = 1 << 16;  // LDS polls of the router-done flag, at most
 
 // ------------------------------------------------------------ tagged words --
 
@@ -269,6 +270,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   __shared__ double s_d[kMaxK];
   __shared__ __align__(16) float s_hb[kFWaves][32 * kUD];  // h values of a down batch
   __shared__ uint32_t s_gen[kFWaves];
+  __shared__ uint32_t s_rdone;  // this call's generation once wave 0's router rows are out
 
   // Generation of this call: this block's own call count.  Every wave reads the
   // counter itself and nothing waits for it here, so the read travels together
@@ -326,12 +328,33 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     }
   }
 
+  if (wave == 0 && lane == 0)
+    __hip_atomic_store(&s_rdone, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+
   // ---------------------------------------------------------------- S --
   if (lane == 0) s_gen[wave] = gen;  // needs the counter read to have returned
   {
     const uint64_t* lgc = p.logits + static_cast<size_t>(blockIdx.x % kLogitCopies) * T * E1;
     const bool has_shared = p.shared_gate != nullptr;
     if (T == 1) {
+      // A wave with no router row waits for its block's wave 0 to have issued its
+      // router row's stores before its first poll of the logits (every block's
+      // router rows finish within a few hundred ns of each other; a short sleep
+      // covers their propagation).  Polling from the start instead sends thousands
+      // of device-coherent reads at a few replica lines while the router loads and
+      // stores are in flight, and slowed the whole call by about 1 us.  The flag
+      // holds the call's generation, so a value left in LDS by an earlier launch
+      // never matches; the wait is bounded.
+      const int rrows = E + (p.shared_gate ? 1 : 0);
+      if (wave * G + static_cast<int>(blockIdx.x) >= rrows &&
+          static_cast<int>(blockIdx.x) < rrows) {
+        for (int sp = 0; sp < kRouterWaitSpins; ++sp) {
+          if (__hip_atomic_load(&s_rdone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == gen)
+            break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
       block_topk_one_token(lgc, E, k, gen, p.spin_limit, p.err, s_key, s_cand, s_d, s_ids);
     } else {
       for (int t = wave; t < T; t += kFWaves) {
