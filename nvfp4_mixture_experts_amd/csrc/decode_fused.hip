@@ -336,25 +336,25 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   {
     const uint64_t* lgc = p.logits + static_cast<size_t>(blockIdx.x % kLogitCopies) * T * E1;
     const bool has_shared = p.shared_gate != nullptr;
-    if (T == 1) {
-      // A wave with no router row waits for its block's wave 0 to have issued its
-      // router row's stores before its first poll of the logits (every block's
-      // router rows finish within a few hundred ns of each other; a short sleep
-      // covers their propagation).  Polling from the start instead sends thousands
-      // of device-coherent reads at a few replica lines while the router loads and
-      // stores are in flight, and slowed the whole call by about 1 us.  The flag
-      // holds the call's generation, so a value left in LDS by an earlier launch
-      // never matches; the wait is bounded.
-      const int rrows = E + (p.shared_gate ? 1 : 0);
-      if (wave * G + static_cast<int>(blockIdx.x) >= rrows &&
-          static_cast<int>(blockIdx.x) < rrows) {
-        for (int sp = 0; sp < kRouterWaitSpins; ++sp) {
-          if (__hip_atomic_load(&s_rdone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == gen)
-            break;
-          __builtin_amdgcn_s_sleep(2);
-        }
-        __builtin_amdgcn_s_sleep(8);
+    // A wave with no router row waits for its block's wave 0 to have issued its
+    // router row's stores before its first poll of the logits (every block's
+    // router rows finish within a few hundred ns of each other; a short sleep
+    // covers their propagation).  Polling from the start instead sends thousands
+    // of device-coherent reads at a few replica lines while the router loads and
+    // stores are in flight, and slowed the whole call by about 1 us.  The flag
+    // holds the call's generation, so a value left in LDS by an earlier launch
+    // never matches; the wait is bounded.
+    const int rrows = E + (p.shared_gate ? 1 : 0);
+    if (wave * G + static_cast<int>(blockIdx.x) >= rrows &&
+        static_cast<int>(blockIdx.x) < rrows) {
+      for (int sp = 0; sp < kRouterWaitSpins; ++sp) {
+        if (__hip_atomic_load(&s_rdone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == gen)
+          break;
+        __builtin_amdgcn_s_sleep(2);
       }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    if (T == 1) {
       block_topk_one_token(lgc, E, k, gen, p.spin_limit, p.err, s_key, s_cand, s_d, s_ids);
     } else {
       for (int t = wave; t < T; t += kFWaves) {
