@@ -538,8 +538,16 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
           const int j = col + LPR * c;
           qg[jj][c] = *reinterpret_cast<const uint4*>(codes + rr * row_bytes + 16 * j);
           qu[jj][c] = *reinterpret_cast<const uint4*>(codes + (I + rr) * row_bytes + 16 * j);
-          sg[jj][c] = *reinterpret_cast<const uint16_t*>(scales + rr * srow_bytes + 2 * j);
-          su[jj][c] = *reinterpret_cast<const uint16_t*>(scales + (I + rr) * srow_bytes + 2 * j);
+          if constexpr (LPR == kWave && CPL == 1) {
+            // one dword load for both rows' scales: lanes 0..31 read the gate row's
+            // 128 bytes, lanes 32..63 the up row's; redistributed at compute time
+            const size_t srow = (lane < 32 ? rr : I + rr) * srow_bytes + 4 * (lane & 31);
+            sg[jj][c] = *reinterpret_cast<const uint32_t*>(scales + srow);
+            su[jj][c] = 0;
+          } else {
+            sg[jj][c] = *reinterpret_cast<const uint16_t*>(scales + rr * srow_bytes + 2 * j);
+            su[jj][c] = *reinterpret_cast<const uint16_t*>(scales + (I + rr) * srow_bytes + 2 * j);
+          }
         }
       }
       if (!prefetched) {  // behind the first gate|up loads, ahead of their use
@@ -553,6 +561,15 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         float ag = 0.0f, au = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
+          if constexpr (LPR == kWave && CPL == 1) {
+            const uint32_t d = sg[jj][c];
+            const uint32_t gd = static_cast<uint32_t>(
+                __builtin_amdgcn_ds_bpermute((lane >> 1) << 2, static_cast<int>(d)));
+            const uint32_t ud = static_cast<uint32_t>(
+                __builtin_amdgcn_ds_bpermute((32 + (lane >> 1)) << 2, static_cast<int>(d)));
+            sg[jj][c] = (gd >> (16 * (lane & 1))) & 0xFFFFu;
+            su[jj][c] = (ud >> (16 * (lane & 1))) & 0xFFFFu;
+          }
           ag += chunk_dot_bf16(qg[jj][c], sg[jj][c], xr[c]);
           au += chunk_dot_bf16(qu[jj][c], su[jj][c], xr[c]);
         }
