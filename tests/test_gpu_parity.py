@@ -176,6 +176,7 @@ def test_route_ties_go_to_lowest_index(gpu, tokens):
     ("decode_e288_top8", 1, None),
     ("decode_e512_top10_shared", 1, None),
     ("batched_decode_t32_hot64", 32, [0, 9, 22, 31]),
+    ("decode_e288_top8", 2, None),                # fused kernel, several tokens, I = 768
     ("batched_decode_t32_hot64", 7, [0, 6]),     # largest count on the fused kernel
     ("batched_decode_t32_hot64", 8, [0, 7]),     # smallest count on the grouped path
     ("tiny_e8_top2", 64, [0, 63]),
