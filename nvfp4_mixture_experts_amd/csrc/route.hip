@@ -365,7 +365,9 @@ __global__ __launch_bounds__(256) void route_split_kernel(RouteParams p) {
 
 // One block per token: the logits from the split partial sums (summed in split
 // order, the bias added in fp64, one fp32 rounding; row E gives the shared gate),
-// then the rank-count top-k.
+// then the rank-count top-k.  KS = the split count: with it fixed, every load of a
+// row is unconditional, so all of them are in flight before the first sum.
+template <int KS>
 __global__ __launch_bounds__(kTopkWaves* kWave) void topk_split_kernel(RouteParams p) {
   __shared__ float s_logit[kMaxExperts];
   __shared__ __align__(16) uint64_t s_key[kTopkWaves][kWave];
@@ -376,19 +378,27 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void topk_split_kernel(RoutePara
   const int lane = threadIdx.x & (kWave - 1);
   const int R = p.E + 1;
   const size_t stride = static_cast<size_t>(p.T) * R;
+  // without a bias the bias load reads the router weights (at least E floats) and
+  // its value is masked off: the load is unconditional, so that no branch waits
+  // for it, and it is issued ahead of the split loads
+  const float* bsrc = p.bias ? p.bias : p.wr;
   for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    const float b = bsrc[min(r, p.E - 1)];
     const double* src = p.part + static_cast<size_t>(t) * R + r;
-    // every split's load in flight at once (indices clamped), then the sum in
-    // split order
-    double pv[kRouteMaxSplits];
+    double pv[KS];
 #pragma unroll
-    for (int ks = 0; ks < kRouteMaxSplits; ++ks)
-      pv[ks] = src[static_cast<size_t>(ks < p.ksplit ? ks : p.ksplit - 1) * stride];
+    for (int ks = 0; ks < KS; ++ks) pv[ks] = src[static_cast<size_t>(ks) * stride];
     double v = 0.0;
 #pragma unroll
-    for (int ks = 0; ks < kRouteMaxSplits; ++ks) v = ks < p.ksplit ? v + pv[ks] : v;
+    for (int ks = 0; ks < KS; ++ks) v += pv[ks];
+    // The bias is added on every row, masked to +0.0 where there is none (no bias,
+    // or the shared-gate row): the sum starts from +0.0 and so is never -0.0, and
+    // adding +0.0 leaves it unchanged.  The mask is hidden from the optimiser, so
+    // that the add is not turned back into a branch that the load would sink into.
+    uint32_t keep = (p.bias != nullptr && r < p.E) ? 0xFFFFFFFFu : 0u;
+    __asm__ volatile("" : "+v"(keep));
+    v += static_cast<double>(__uint_as_float(__float_as_uint(b) & keep));
     if (r < p.E) {
-      if (p.bias) v += static_cast<double>(p.bias[r]);
       const float lf = static_cast<float>(v);
       s_logit[r] = lf;
       if (p.logits) p.logits[static_cast<size_t>(t) * p.E + r] = lf;
@@ -433,7 +443,15 @@ hipError_t launch_route_split(const RouteParams& p0, hipStream_t s) {
   dim3 grid((p.E + 1 + kRouteSplitRows - 1) / kRouteSplitRows,
             (p.T + kRouteSplitTokens - 1) / kRouteSplitTokens, p.ksplit);
   route_split_kernel<<<grid, 256, 0, s>>>(p);
-  topk_split_kernel<<<dim3(p.T), dim3(kTopkWaves * kWave), 0, s>>>(p);
+  const dim3 tgrid(p.T), tblock(kTopkWaves * kWave);
+  switch (p.ksplit) {  // a power of two up to kRouteMaxSplits (route_split_k)
+#define FTMOE_TOPK_SPLIT_CASE(ks) \
+  case ks: topk_split_kernel<ks><<<tgrid, tblock, 0, s>>>(p); break;
+    FTMOE_TOPK_SPLIT_CASE(1) FTMOE_TOPK_SPLIT_CASE(2) FTMOE_TOPK_SPLIT_CASE(4)
+    FTMOE_TOPK_SPLIT_CASE(8) FTMOE_TOPK_SPLIT_CASE(16) FTMOE_TOPK_SPLIT_CASE(32)
+#undef FTMOE_TOPK_SPLIT_CASE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
