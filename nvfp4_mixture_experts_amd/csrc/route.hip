@@ -366,8 +366,11 @@ __global__ __launch_bounds__(256) void route_split_kernel(RouteParams p) {
 // One block per token: the logits from the split partial sums (summed in split
 // order, the bias added in fp64, one fp32 rounding; row E gives the shared gate),
 // then the rank-count top-k.  KS = the split count: with it fixed, every load of a
-// row is unconditional, so all of them are in flight before the first sum.
-template <int KS>
+// row is unconditional, so all of them are in flight before the first sum.  GL:
+// E is a multiple of the block's thread count, so that the loop over rows would
+// take a pass of its own for row E alone; instead lane l of every wave loads split
+// l of row E ahead of the loop, and the wave sums them after it, in split order.
+template <int KS, bool GL>
 __global__ __launch_bounds__(kTopkWaves* kWave) void topk_split_kernel(RouteParams p) {
   __shared__ float s_logit[kMaxExperts];
   __shared__ __align__(16) uint64_t s_key[kTopkWaves][kWave];
@@ -382,12 +385,18 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void topk_split_kernel(RoutePara
   // its value is masked off: the load is unconditional, so that no branch waits
   // for it, and it is issued ahead of the split loads
   const float* bsrc = p.bias ? p.bias : p.wr;
-  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+  double gpart = 0.0, gsum = 0.0;
+  if constexpr (GL)
+    gpart = p.part[static_cast<size_t>(lane % KS) * stride + static_cast<size_t>(t) * R + p.E];
+  for (int r = threadIdx.x; r < (GL ? p.E : R); r += blockDim.x) {
     const float b = bsrc[min(r, p.E - 1)];
     const double* src = p.part + static_cast<size_t>(t) * R + r;
     double pv[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) pv[ks] = src[static_cast<size_t>(ks) * stride];
+    // no add is scheduled between the loads (it would wait for the first of them
+    // before the rest are issued)
+    __builtin_amdgcn_sched_barrier(0);
     double v = 0.0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) v += pv[ks];
@@ -398,6 +407,12 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void topk_split_kernel(RoutePara
     uint32_t keep = (p.bias != nullptr && r < p.E) ? 0xFFFFFFFFu : 0u;
     __asm__ volatile("" : "+v"(keep));
     v += static_cast<double>(__uint_as_float(__float_as_uint(b) & keep));
+    if constexpr (GL) {
+      // row E's sum, before this pass's stores (a wait after them would also wait
+      // for their completion); every pass forms the same value
+      gsum = 0.0;
+      for (int ks = 0; ks < KS; ++ks) gsum += readlane_f64(gpart, ks);
+    }
     if (r < p.E) {
       const float lf = static_cast<float>(v);
       s_logit[r] = lf;
@@ -405,6 +420,10 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void topk_split_kernel(RoutePara
     } else if (p.gamma && p.shared_gate) {
       p.gamma[t] = static_cast<float>(1.0 / (1.0 + exp(-v)));
     }
+  }
+  if constexpr (GL) {  // thread 0 made at least one pass (E >= the thread count)
+    if (threadIdx.x == 0 && p.gamma && p.shared_gate)
+      p.gamma[t] = static_cast<float>(1.0 / (1.0 + exp(-gsum)));
   }
   __syncthreads();
   block_topk_rank<kTopkWaves>(p.E, p.k, [&](int e) { return s_logit[e]; }, s_key, s_cand, s_d,
@@ -444,9 +463,15 @@ hipError_t launch_route_split(const RouteParams& p0, hipStream_t s) {
             (p.T + kRouteSplitTokens - 1) / kRouteSplitTokens, p.ksplit);
   route_split_kernel<<<grid, 256, 0, s>>>(p);
   const dim3 tgrid(p.T), tblock(kTopkWaves * kWave);
+  const bool gl = p.E % (kTopkWaves * kWave) == 0;
   switch (p.ksplit) {  // a power of two up to kRouteMaxSplits (route_split_k)
-#define FTMOE_TOPK_SPLIT_CASE(ks) \
-  case ks: topk_split_kernel<ks><<<tgrid, tblock, 0, s>>>(p); break;
+#define FTMOE_TOPK_SPLIT_CASE(ks)                                              \
+  case ks:                                                                     \
+    if (gl)                                                                    \
+      topk_split_kernel<ks, true><<<tgrid, tblock, 0, s>>>(p);                 \
+    else                                                                       \
+      topk_split_kernel<ks, false><<<tgrid, tblock, 0, s>>>(p);                \
+    break;
     FTMOE_TOPK_SPLIT_CASE(1) FTMOE_TOPK_SPLIT_CASE(2) FTMOE_TOPK_SPLIT_CASE(4)
     FTMOE_TOPK_SPLIT_CASE(8) FTMOE_TOPK_SPLIT_CASE(16) FTMOE_TOPK_SPLIT_CASE(32)
 #undef FTMOE_TOPK_SPLIT_CASE
