@@ -275,19 +275,31 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteParams p) {
 // A few to a thousand tokens: the same fp64 MFMA product, split along K so that
 // the whole chip shares it (an fp64 MFMA takes 64 cycles, so one block per 64
 // experts would leave most CUs idle).  Block (row block, token block, split):
-// 4 waves x 16 rows (expert rows, then row E = the shared gate, bf16) x 32 tokens
+// W waves x 16 rows (expert rows, then row E = the shared gate, bf16) x 32 tokens
 // (2 fragments of 16) over K [split * kc, (split + 1) * kc), into
 // part[split][t][row].  topk_split_kernel sums the splits in split order.
-constexpr int kRouteSplitRows = 64;
+// W (route_split_waves) is the fewest from 4 that give at most kRouteSplitMaxRowBlocks
+// row blocks: with the full 32 splits of a call of up to 32 tokens the grid then
+// fits one block per CU (E = 512 with the shared gate, 513 rows: 64-row blocks
+// would leave a ninth block of one row per split, 288 blocks, 32 CUs running two).
 constexpr int kRouteSplitTokens = 32;
 constexpr int kRouteSplitTargetBlocks = 512;
 constexpr int kRouteMaxSplits = 32;
+constexpr int kRouteSplitMinWaves = 4;
+constexpr int kRouteSplitMaxWaves = 8;
+constexpr int kRouteSplitMaxRowBlocks = 8;
 
-__global__ __launch_bounds__(256) void route_split_kernel(RouteParams p) {
+int route_split_waves(int R) {
+  int w = kRouteSplitMinWaves;
+  while (w < kRouteSplitMaxWaves && (R + 16 * w - 1) / (16 * w) > kRouteSplitMaxRowBlocks) ++w;
+  return w;
+}
+
+__global__ __launch_bounds__(kRouteSplitMaxWaves* kWave) void route_split_kernel(RouteParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int R = p.E + 1;
-  const int r0 = blockIdx.x * kRouteSplitRows + wave * 16;
+  const int r0 = blockIdx.x * (blockDim.x / kWave) * 16 + wave * 16;
   const int t0 = blockIdx.y * kRouteSplitTokens;
   const int kc = p.H / p.ksplit;
   const int kbeg = blockIdx.z * kc;
@@ -441,7 +453,9 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void topk_split_kernel(RoutePara
 }
 
 int route_split_k(int E, int T, int H) {
-  const int nrb = (E + 1 + kRouteSplitRows - 1) / kRouteSplitRows;
+  // chosen as for 64-row blocks whatever the block's wave count: more splits than
+  // that add partial sums for the top-k to read (measured slower at 64 tokens)
+  const int nrb = (E + 1 + 63) / 64;
   const int ntb = (T + kRouteSplitTokens - 1) / kRouteSplitTokens;
   const int kmax = H / 64;  // 64-K steps
   int ks = 1;
@@ -459,9 +473,10 @@ size_t route_split_bytes(int E, int T, int H) {
 hipError_t launch_route_split(const RouteParams& p0, hipStream_t s) {
   RouteParams p = p0;
   p.ksplit = route_split_k(p.E, p.T, p.H);
-  dim3 grid((p.E + 1 + kRouteSplitRows - 1) / kRouteSplitRows,
+  const int waves = route_split_waves(p.E + 1);
+  dim3 grid((p.E + 1 + 16 * waves - 1) / (16 * waves),
             (p.T + kRouteSplitTokens - 1) / kRouteSplitTokens, p.ksplit);
-  route_split_kernel<<<grid, 256, 0, s>>>(p);
+  route_split_kernel<<<grid, waves * kWave, 0, s>>>(p);
   const dim3 tgrid(p.T), tblock(kTopkWaves * kWave);
   const bool gl = p.E % (kTopkWaves * kWave) == 0;
   switch (p.ksplit) {  // a power of two up to kRouteMaxSplits (route_split_k)
