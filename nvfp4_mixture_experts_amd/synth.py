@@ -136,6 +136,21 @@ def _bank(seed: int, prefix: str, n: int, H: int, I: int, g: float):
     )
 
 
+def make_router(w: Workload, instance: int = 0, num_experts: Optional[int] = None):
+    """Router weights [E, H] and bias [E] (or None) of layer instance ``instance``:
+    the same values ``make_layer`` gives, without the expert banks."""
+    seed = w.seed + 7919 * instance
+    E = w.num_experts if num_experts is None else num_experts
+    wr = (_rng(seed, "w_router").standard_normal((E, w.hidden), dtype=np.float32)
+          * np.float32(w.router_std)).astype(np.float32)
+    bias = None
+    if w.hot_experts > 0:
+        bias = np.zeros(E, np.float32)
+        hot = _rng(seed, "hot").choice(E, size=min(w.hot_experts, E), replace=False)
+        bias[hot] = np.float32(w.hot_bias)
+    return wr, bias
+
+
 def make_layer(w: Workload, instance: int = 0, num_experts: Optional[int] = None) -> Layer:
     """Host (numpy) weights of layer instance ``instance``.
 
@@ -147,13 +162,7 @@ def make_layer(w: Workload, instance: int = 0, num_experts: Optional[int] = None
     if num_experts is not None:
         w = dataclasses.replace(w, num_experts=E)
     H, I = w.hidden, w.inter
-    wr = (_rng(seed, "w_router").standard_normal((E, H), dtype=np.float32)
-          * np.float32(w.router_std)).astype(np.float32)
-    bias = None
-    if w.hot_experts > 0:
-        bias = np.zeros(E, np.float32)
-        hot = _rng(seed, "hot").choice(E, size=min(w.hot_experts, E), replace=False)
-        bias[hot] = np.float32(w.hot_bias)
+    wr, bias = make_router(w, instance)
     bank = _bank(seed, "", E, H, I, w.global_scale)
     layer = Layer(workload=w, w_router=wr, bias=bias, **bank)
     if w.shared_inter > 0:

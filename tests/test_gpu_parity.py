@@ -169,6 +169,29 @@ def test_route_ties_go_to_lowest_index(gpu, tokens):
     _check_routes(ids, wt, ref_ids, ref_w, "ties")
 
 
+@pytest.mark.parametrize("num_experts", [1000, 1024])
+def test_route_many_experts_split_router(gpu, num_experts):
+    """40 tokens (split-K router) with 1000 and 1024 experts and a router bias: the
+    widest split-router blocks (8 waves), two row passes in the per-token top-k, and
+    for 1024 (a multiple of the top-k block's 512 threads) row E loaded by lanes."""
+    from nvfp4_mixture_experts_amd import ftmoe
+    tokens = 40
+    w = synth.dataclasses.replace(synth.WORKLOADS["batched_decode_t32_hot64"],
+                                  num_experts=num_experts)
+    wr, bias = synth.make_router(w)
+    assert bias is not None
+    x = synth.make_tokens(w, tokens=tokens, stream="many_experts")
+    desc = ftmoe.make_desc(num_experts, w.hidden, w.inter, w.top_k, 1)
+    wsp = ftmoe.alloc_workspace(desc, tokens, ftmoe.PATH_ROUTE)
+    ids = torch.empty((tokens, w.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((tokens, w.top_k), dtype=torch.float32, device="cuda")
+    ftmoe.ft_moe_route(desc, gpu.tokens_to_device(x), torch.from_numpy(wr).cuda(),
+                       torch.from_numpy(bias).cuda(), ids, wt, wsp)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.topk(oracle.router_logits(x, wr, bias), w.top_k)
+    _check_routes(ids, wt, ref_ids, ref_w, f"E={num_experts} T={tokens}")
+
+
 # ----------------------------------------------------------------- decode --
 
 @pytest.mark.parametrize("name,tokens,sample", [
