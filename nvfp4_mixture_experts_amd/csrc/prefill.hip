@@ -1011,18 +1011,25 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PrefillParams p) {
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s)
     v[s] = *reinterpret_cast<const float4*>(src + static_cast<size_t>(s < p.nslots ? s : p.nslots - 1) * p.H);
+  // nothing that uses a loaded value is scheduled between the loads (it would wait
+  // for the earlier loads before the later ones are issued)
+  __builtin_amdgcn_sched_barrier(0);
   bool bad = false;
 #pragma unroll
   for (int s = 0; s < kTopkMaxK; ++s) bad |= (ev[s] < 0 || ev[s] >= p.E);
+  // Every slot is added, a missing one (s >= nslots) masked to +0.0: the sum starts
+  // from +0.0 and so is never -0.0, and adding +0.0 leaves it unchanged.  The masks
+  // are hidden from the optimiser: a select there becomes a branch that the slot's
+  // load is deferred into, behind a wait for every earlier load.
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s) {
-    if (s < p.nslots) {
-      acc.x += v[s].x;
-      acc.y += v[s].y;
-      acc.z += v[s].z;
-      acc.w += v[s].w;
-    }
+    uint32_t keep = s < p.nslots ? 0xFFFFFFFFu : 0u;
+    __asm__ volatile("" : "+v"(keep));
+    acc.x += __uint_as_float(__float_as_uint(v[s].x) & keep);
+    acc.y += __uint_as_float(__float_as_uint(v[s].y) & keep);
+    acc.z += __uint_as_float(__float_as_uint(v[s].z) & keep);
+    acc.w += __uint_as_float(__float_as_uint(v[s].w) & keep);
   }
   if (bad) acc = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                              __builtin_nanf(""));
@@ -1085,7 +1092,9 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const size_t n4 = static_cast<size_t>(p.T) * (p.H / 4);
-  pf_combine_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, s>>>(p);
+  // small calls in 64-thread blocks, so that their slot rows are read by every CU
+  const unsigned cb = n4 < static_cast<size_t>(256) * 256 ? 64u : 256u;
+  pf_combine_kernel<<<static_cast<unsigned>((n4 + cb - 1) / cb), cb, 0, s>>>(p);
   return hipGetLastError();
 }
 
