@@ -233,35 +233,63 @@ def test_swiglu_clamps():
 
 # ---------------------------------------------------------- whole layer --
 
+def _bf16_to_f64(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+        torch.bfloat16).to(torch.float64).numpy()
+
+
+def _unpack(codes, scales, g):
+    """Dense fp32 [rows, K] from canonical codes/scales, by table lookup (numpy only)."""
+    rows = codes.shape[0]
+    nib = np.empty((rows, codes.shape[1] * 2), np.int64)
+    nib[:, 0::2] = codes & 0x0F
+    nib[:, 1::2] = codes >> 4
+    return (E2M1[nib] * E4M3[np.repeat(scales, 16, axis=1)]).astype(np.float32) * np.float32(g)
+
+
+def _dense_mlp(layer, xf, w13c, w13s, w2c, w2s, g3, I):
+    """One expert's MLP on fp64 token rows xf [T, H] with numpy matmuls and scipy's
+    expit; returns (output [T, H], whether a clamp engaged)."""
+    wg = _unpack(w13c[:I], w13s[:I], g3[0]).astype(np.float64)
+    wu = _unpack(w13c[I:], w13s[I:], g3[1]).astype(np.float64)
+    wd = _unpack(w2c, w2s, g3[2]).astype(np.float64)
+    gate = xf @ wg.T
+    up = xf @ wu.T
+    clamped = False
+    if layer.act == 1:
+        clamped = bool((gate > layer.gate_max).any() or (np.abs(up) > layer.up_absmax).any())
+        gate = np.minimum(gate, layer.gate_max)
+        up = np.clip(up, -layer.up_absmax, layer.up_absmax)
+    h = scipy.special.expit(gate) * gate * up
+    return h @ wd.T, clamped
+
+
+def _dense_shared(layer, xf):
+    """gamma [T] = expit(x . gate vector) and the shared expert's output [T, H]."""
+    gs = _bf16_to_f64(layer.shared_gate)
+    gamma = scipy.special.expit(xf @ gs)
+    o, _ = _dense_mlp(layer, xf, layer.s13_codes[0], layer.s13_scales[0], layer.s2_codes[0],
+                      layer.s2_scales[0], layer.s_global[0], layer.shared_inter)
+    return gamma, o
+
+
 def _dense_reference(layer, x):
-    """k = E: y = sum_e softmax_e(logits) * MLP_e(x), from library routines only."""
+    """k = E: y = sum_e softmax_e(logits) * MLP_e(x) (+ expit(gs . x) * MLP_s(x) with a
+    shared expert), from library routines only."""
     H, I, E = layer.hidden, layer.inter, layer.num_experts
-    xf = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    xf = _bf16_to_f64(x)
     logits = (xf @ layer.w_router.astype(np.float64).T).astype(np.float32)
     probs = scipy.special.softmax(logits.astype(np.float64), axis=1).astype(np.float32)
-
-    def unpack(codes, scales, g):
-        rows = codes.shape[0]
-        nib = np.empty((rows, codes.shape[1] * 2), np.int64)
-        nib[:, 0::2] = codes & 0x0F
-        nib[:, 1::2] = codes >> 4
-        return (E2M1[nib] * E4M3[np.repeat(scales, 16, axis=1)]).astype(np.float32) * np.float32(g)
-
     y = np.zeros((x.shape[0], H))
     clamped = False
     for e in range(E):
-        g13 = layer.global_scale[e]
-        wg = unpack(layer.w13_codes[e, :I], layer.w13_scales[e, :I], g13[0]).astype(np.float64)
-        wu = unpack(layer.w13_codes[e, I:], layer.w13_scales[e, I:], g13[1]).astype(np.float64)
-        wd = unpack(layer.w2_codes[e], layer.w2_scales[e], g13[2]).astype(np.float64)
-        gate = xf @ wg.T
-        up = xf @ wu.T
-        if layer.act == 1:
-            clamped |= bool((gate > layer.gate_max).any() or (np.abs(up) > layer.up_absmax).any())
-            gate = np.minimum(gate, layer.gate_max)
-            up = np.clip(up, -layer.up_absmax, layer.up_absmax)
-        h = scipy.special.expit(gate) * gate * up
-        y += probs[:, e:e + 1].astype(np.float64) * (h @ wd.T)
+        o, c = _dense_mlp(layer, xf, layer.w13_codes[e], layer.w13_scales[e], layer.w2_codes[e],
+                          layer.w2_scales[e], layer.global_scale[e], I)
+        clamped |= c
+        y += probs[:, e:e + 1].astype(np.float64) * o
+    if layer.shared_inter > 0:
+        gamma, o = _dense_shared(layer, xf)
+        y += gamma[:, None] * o
     return y, clamped
 
 
@@ -340,6 +368,59 @@ def test_shared_gate_of_zero_vector_is_one_half():
     diff = with_shared["y64"][0] - routed_only["y64"][0]
     assert np.allclose(diff, 0.5 * o_s, rtol=1e-9, atol=1e-12 * np.abs(o_s).max())
     assert np.array_equal(with_shared["ids"], routed_only["ids"])
+
+
+@pytest.mark.parametrize("z", [-4.0, -0.5, 1.5, 6.0])
+def test_shared_gate_direction_on_one_hot_token(z):
+    # x = e_{h0} (one-hot, 1.0) and gate vector entry gs[h0] = z (exact in bf16): the
+    # gate's argument is exactly z, so the shared expert enters y with weight
+    # expit(z), which is above 1/2 for z > 0 and below it for z < 0 (a sign slip in
+    # the sigmoid turns expit(z) into expit(-z) and fails here).
+    w = synth.dataclasses.replace(synth.WORKLOADS["decode_e512_top10_shared"], num_experts=12,
+                                  hidden=256, inter=128, shared_inter=128,
+                                  global_scale=2.0 ** -2)
+    layer = synth.make_layer(w)
+    h0 = 37
+    x = np.zeros((1, w.hidden), np.uint16)
+    x[0, h0] = 0x3F80                                  # bf16 1.0
+    gs = np.zeros(w.hidden, np.uint16)
+    gs[h0] = synth.bf16_bits_from_f32(np.array([z], np.float32))[0]
+    assert _bf16_to_f64(gs)[h0] == z
+    layer.shared_gate = gs
+    with_shared = oracle.moe_layer(layer, x)
+    w0 = synth.dataclasses.replace(w, shared_inter=0)
+    routed_only = oracle.moe_layer(synth.dataclasses.replace(layer, workload=w0), x)
+    diff = with_shared["y64"][0] - routed_only["y64"][0]
+    # the shared expert's output from numpy/scipy alone (not the oracle)
+    gamma, o_s = _dense_shared(layer, _bf16_to_f64(x))
+    want_gamma = scipy.special.expit(z)
+    assert gamma[0] == pytest.approx(want_gamma, rel=1e-15)
+    assert (want_gamma > 0.5) == (z > 0)
+    assert np.abs(o_s[0]).max() > 0
+    assert np.allclose(diff, want_gamma * o_s[0], rtol=1e-9, atol=1e-12 * np.abs(o_s).max())
+    # the ratio itself identifies the gate's value and direction
+    big = np.abs(o_s[0]) > 0.1 * np.abs(o_s[0]).max()
+    ratio = diff[big] / o_s[0][big]
+    assert np.allclose(ratio, want_gamma, rtol=1e-9)
+    assert np.array_equal(with_shared["ids"], routed_only["ids"])
+
+
+def test_all_experts_selected_with_shared_expert_equals_dense_layer():
+    # k = E plus a shared expert whose gate argument is far from 0 for every token
+    # (gate vector N(0, 0.5), so |z| is typically ~8): the whole layer, shared
+    # expert included, against a dense numpy/scipy reference.
+    w = synth.dataclasses.replace(synth.WORKLOADS["decode_e512_top10_shared"], num_experts=5,
+                                  top_k=5, hidden=256, inter=128, shared_inter=128,
+                                  global_scale=2.0 ** -3, shared_gate_std=0.5)
+    layer = synth.make_layer(w)
+    x = synth.make_tokens(w, tokens=3)
+    got = oracle.moe_layer(layer, x)
+    want, clamped = _dense_reference(layer, x)
+    gamma, _ = _dense_shared(layer, _bf16_to_f64(x))
+    assert np.all(np.abs(gamma - 0.5) > 0.05), gamma   # the gate is not near its midpoint
+    scale = np.abs(want).max()
+    assert np.abs(got["y64"] - want).max() <= 1e-12 * scale
+    assert clamped
 
 
 def test_given_routes_reproduce_computed_routes():
