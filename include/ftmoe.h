@@ -5,8 +5,8 @@
  * The layer (FreeToken commit log, page 2: the 288-expert NVFP4 MoE entry, and
  * the entry with 512 routed experts, top-10, plus a gated shared expert; the
  * clamped-SwiGLU entry; the MoE router / shared gate kernels and the
- * non-power-of-2 top-k router entry.  FreeToken fork PR #84, page 1: the bullet
- * on #631, the NVFP4 MoE decode GEMV run in every layer at every decode step,
+ * top-k router entry (k not a power of two).  FreeToken fork PR #84, page 1: the
+ * bullet on #631, the NVFP4 MoE decode GEMV on the per-token path of each layer,
  * and the bullet on #578, NVFP4 prefill experts):
  *
  *   logit[t,e] = sum_h Wr[e,h] x[t,h] (+ bias[e])          router, fp64 sum, one fp32 rounding
@@ -110,9 +110,9 @@ ft_status ft_init(int32_t device);
 size_t ft_nvfp4_repacked_bytes(int32_t hidden, int32_t inter, int32_t n_experts, int32_t part);
 
 /* Load-time layout conversion, from the canonical layout above into the layout
- * the compute entry points read ("avoid layout conversions in nvfp4 marlin
- * decode": FreeToken fork PR #84, bullet on #631 -- the conversion moves to
- * load time).  Byte-preserving: every code and scale byte is moved, none is
+ * the compute entry points read (FreeToken fork PR #84, page 1, bullet on #631:
+ * the decode GEMV stops converting layouts per call; here the conversion moves
+ * to load time).  Byte-preserving: every code and scale byte is moved, none is
  * changed.  The gate|up tensors stay row-major (one wave reads a row's codes as
  * contiguous 16-byte lanes); the down tensors become K-chunk-major, [n][I/32][H]
  * records of 16 code bytes and [n][I/32][H] records of 2 scale bytes, so that 64
@@ -136,7 +136,7 @@ ft_status ft_nvfp4_repack(int32_t hidden, int32_t inter, int32_t n_experts,
 size_t ft_moe_workspace_bytes(const ft_moe_desc *desc, int64_t tokens, int32_t path);
 
 /* Router only (FreeToken commit log, page 2: the MoE router / shared gate kernels
- * entry and the non-power-of-2 top-k router entry): logits with exact fp32 x bf16
+ * entry and the top-k router entry for k not a power of two): logits with exact fp32 x bf16
  * products summed in fp64 and rounded once to fp32 (from 24 tokens on the fp64
  * MFMA units, split along K below 1024 tokens; the splits summed in a fixed
  * order), top-k (ties to the lower index) and softmax weights of the selected

@@ -1,10 +1,11 @@
 // decode_fused.hip -- the whole NVFP4 MoE layer at decode time in ONE persistent
 // kernel launch on gfx950.
 //
-// FreeToken fork PR #84 (page 1), bullet on #631: the NVFP4 MoE decode GEMV runs
-// in every layer at every decode step.  FreeToken commit log (page 2): MoE router
-// and shared-gate kernels, non-power-of-2 top-k, clamped SwiGLU, 512 routed
-// experts with top-10 plus a gated shared expert, a "deep-K" decode config.
+// FreeToken fork PR #84 (page 1), bullet on #631: the NVFP4 MoE decode GEMV sits
+// on the per-token path of each MoE layer.  FreeToken commit log (page 2): the
+// router / shared-gate kernel entry, the top-k entry (k need not be a power of
+// two), the clamped-SwiGLU entry, the 512-expert top-10 entry with its gated
+// shared expert, and the decode configuration for long reduction rows.
 //
 // At batch 1 the layer moves ~24 MB: about 3 us of HBM time, the same order as
 // one kernel launch or one grid-wide barrier.  So the layer is one launch of one

@@ -1,8 +1,8 @@
 // repack.hip -- load-time NVFP4 layout conversion and the dequantisation test
 // export, gfx950.
 //
-// FreeToken fork PR #84 (page 1), bullet on #631 ("avoid layout conversions in
-// nvfp4 marlin decode"): the decode GEMV reads weights already arranged for it,
+// FreeToken fork PR #84 (page 1), bullet on #631 (the decode GEMV stops converting
+// its weight layout on the fly): the decode GEMV reads weights already arranged for it,
 // so the conversion happens once, when the weights are loaded.  The gate|up
 // tensors are already in the order the gate|up GEMV reads (row-major, 16-byte
 // chunks per lane); the down tensors are moved to K-chunk-major order so that 64

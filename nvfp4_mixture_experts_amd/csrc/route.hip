@@ -2,8 +2,8 @@
 // sigmoid gate, and top-k selection with softmax weights over the selected
 // logits.
 //
-// FreeToken commit log (page 2): "moe router / shared gate" kernels and the
-// "non-power-of-2 top-k router" (k = 10 of 512 experts); the 288-expert layer
+// FreeToken commit log (page 2): the entry on router and shared-gate kernels and
+// the entry on a top-k router whose k is not a power of two (k = 10 of 512); the 288-expert layer
 // routes top-8.  Logits are accumulated in fp64 (every fp32 x bf16 product is
 // exact in fp64) and rounded once to fp32, so the selection does not depend on
 // the summation order; ties go to the lower expert index.

@@ -13,12 +13,13 @@
  * binary64), and rounds once at the end where a narrower type is stored.
  *
  * Sources of the definitions:
- *  - "FreeToken fork PR #84" (page 1), bullet on #631: the NVFP4 MoE decode GEMV
- *    that runs in every layer at every decode step; bullet on #578: NVFP4 prefill
- *    experts dequantised by bit placement.
- *  - "FreeToken commit log" (page 2): 288-expert NVFP4 MoE; clamped-SwiGLU
- *    activation across the MoE stack; 512 routed experts, top-10, plus a gated
- *    shared expert; MoE router / shared gate kernels; non-power-of-2 top-k.
+ *  - FreeToken fork PR #84 (page 1), bullet on #631: the NVFP4 MoE decode GEMV on
+ *    the per-token path of each MoE layer; bullet on #578: NVFP4 prefill experts
+ *    dequantised by bit placement.
+ *  - FreeToken commit log (page 2): the 288-expert NVFP4 MoE entry; the
+ *    clamped-SwiGLU entry; the 512-routed-expert top-10 entry with a gated shared
+ *    expert; the router / shared-gate kernel entry; the top-k entry (k not a
+ *    power of two).
  *  - NVFP4 codec: e2m1 element codes (OCP Microscaling Formats v1.0, FP4 E2M1),
  *    one e4m3 scale per 16 consecutive K elements (OCP 8-bit Floating Point,
  *    E4M3: bias 7, no infinities, S.1111.111 is NaN), one fp32 global scale per
