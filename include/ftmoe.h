@@ -100,7 +100,8 @@ int32_t ft_abi_version(void);
 /* Message of the last failed call on this thread ("" if none).  Host string. */
 const char *ft_last_error(void);
 
-/* Makes `device` current and caches its properties (CU count).  Call once per
+/* Makes `device` current and caches its properties (CU count); checks that the
+ * one-launch decode kernel can keep a block resident on each CU.  Call once per
  * device before the compute calls, outside stream capture. */
 ft_status ft_init(int32_t device);
 
@@ -182,10 +183,40 @@ ft_status ft_moe_nvfp4_prefill(const ft_moe_desc *desc, int64_t tokens, const ui
                                const uint16_t *shared_gate, uint16_t *y, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Status of the device-side waits of ft_moe_nvfp4_decode on this workspace.
+ * The one-launch decode path (T < 8) runs one block per compute unit whose blocks
+ * hand values to each other; it therefore needs every block resident at once (one
+ * per CU: ft_init checks that the device can hold one, and work from other streams
+ * that occupies whole CUs breaks the assumption).  Every wait is bounded: a wait
+ * that gives up lets the kernel finish, leaves that call's y (and side outputs)
+ * invalid, and records why in the workspace.  This call enqueues one tiny kernel
+ * that copies the recorded reasons to *status (device int32) and clears them, so
+ * the hot call itself never synchronises; read *status after the stream reaches
+ * it.  0 = no give-up since the last read; otherwise an OR of 1 (router logits),
+ * 2 (shared gate), 4 (intermediate h values), 8 (partial output sums).
+ * `workspace` is a decode (path 1) workspace; graph-capturable. */
+ft_status ft_moe_device_status(void *workspace, size_t workspace_bytes, int32_t *status,
+                               void *stream);
+
+/* Test and diagnostic hook: the number of polls after which a device-side wait of
+ * ft_moe_nvfp4_decode gives up (0 restores the default, about one second).  It is
+ * process-wide and applies to calls enqueued afterwards.  A call in which one wait
+ * gives up makes its other waits stop within 16 polls. */
+ft_status ft_set_wait_limit(int32_t polls);
+
 /* Test export: dequantise tensor `tensor` (0 gate [I][H], 1 up [I][H],
- * 2 down [H][I]) of expert `expert` of a repacked bank into a row-major fp32
- * (out_dtype 0) or bf16 (out_dtype 1) matrix, with the same device routine the
- * compute kernels use.  `inter` is the bank's intermediate size. */
+ * 2 down [H][I]) of expert `expert` of a repacked bank into a row-major matrix
+ * `out` (16-byte aligned), through the device routines the compute kernels use.
+ * `inter` is the bank's intermediate size.  out_dtype selects the routine:
+ *   0  fp32 code x scale x global (the codes decoded as the one-launch decode
+ *      kernel's down GEMV decodes them);
+ *   1  the value of 0 rounded to bf16 (nearest-even);
+ *   2  bf16 code x scale WITHOUT the global scale, exactly as the grouped decode
+ *      and prefill kernels build their bf16 MFMA tiles (every such product is
+ *      exact in bf16);
+ *   3  fp32 code x scale x global with the codes decoded as the one-launch decode
+ *      kernel's gate|up GEMV decodes them (e2m1 pair -> bf16 pair).
+ * Every mode is exact: 0 and 3 equal one fp32 rounding of code x scale x global. */
 ft_status ft_nvfp4_dequant(int32_t hidden, int32_t inter, int32_t n_experts,
                            const ft_nvfp4_experts *bank, int32_t expert, int32_t tensor,
                            int32_t out_dtype, void *out, void *stream);

@@ -3,6 +3,7 @@
 // runs on the host; compute calls only enqueue kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -35,9 +36,20 @@ ft_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int kMaxDevices = 64;
-constexpr int kSpinLimit = 1 << 20;  // grid-barrier polls (~1 s) before the kernel gives up
+constexpr int kSpinLimit = 1 << 20;  // polls of one value (~1 s) before the kernel gives up
 
-// Per-device launch geometry of the fused decode kernel (one block per CU).
+// Polls of one value before a wait of the fused decode kernel gives up; 0 = kSpinLimit.
+// Set only through ft_set_wait_limit (a test and diagnostic hook).
+std::atomic<int> g_wait_limit{0};
+
+int wait_limit() {
+  const int v = g_wait_limit.load(std::memory_order_relaxed);
+  return v > 0 ? v : kSpinLimit;
+}
+
+// Per-device launch geometry of the fused decode kernel (one block per CU), set
+// once the device is known to keep one block of every instantiation resident per
+// CU (the kernel's blocks wait for each other, so all of them must run at once).
 int g_fused_grid[kMaxDevices] = {0};
 
 ft_status fused_grid(int* grid) {
@@ -50,6 +62,12 @@ ft_status fused_grid(int* grid) {
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     if (cus <= 0) return fail(FT_EHIP, "device reports %d compute units", cus);
+    int per_cu = 0;
+    e = decode_fused_min_occupancy(&per_cu);
+    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    if (per_cu < 1)
+      return fail(FT_EUNSUPPORTED,
+                  "the fused decode kernel cannot keep a block resident on a compute unit");
     g_fused_grid[dev] = cus < kMaxFusedGrid ? cus : kMaxFusedGrid;
   }
   *grid = g_fused_grid[dev];
@@ -146,7 +164,8 @@ struct Layout {
 };
 
 constexpr int kRouteCounterWord = 0;  // in the sync region
-constexpr int kErrorWord = 32;        // in the sync region (its own cache line)
+constexpr int kErrorWord = 32;        // in the sync region (its own cache line): reasons,
+                                      // then the generation of the latest give-up
 
 Layout layout(const ft_moe_desc& d, int64_t T, int path) {
   Layout L{};
@@ -488,7 +507,7 @@ ft_status ft_moe_nvfp4_decode(const ft_moe_desc* desc, int64_t tokens, const uin
   p.d_groups = T * nrg;
   const int upg = desc->top_k * (desc->inter / 32) + desc->shared_inter / 32;
   p.blocks_per_group = p.d_groups >= grid ? 1 : std::min(grid / p.d_groups, upg);
-  p.spin_limit = kSpinLimit;
+  p.spin_limit = wait_limit();
   hipError_t e = launch_decode_fused(p, grid, s);
   if (e != hipSuccess) return hip_fail(e, "fused decode kernel");
   return ok();
@@ -528,6 +547,26 @@ ft_status ft_moe_nvfp4_prefill(const ft_moe_desc* desc, int64_t tokens, const ui
   return ok();
 }
 
+ft_status ft_moe_device_status(void* workspace, size_t workspace_bytes, int32_t* status,
+                               void* stream) {
+  if (!workspace || !status) return fail(FT_EINVAL, "device_status: NULL pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(FT_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < 256) return fail(FT_EWORKSPACE, "workspace has %zu bytes", workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(status) & 3u)
+    return fail(FT_EINVAL, "device_status: status must be 4-byte aligned");
+  hipError_t e = launch_device_status(at<uint32_t>(workspace, 0) + kErrorWord, status,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "device status kernel");
+  return ok();
+}
+
+ft_status ft_set_wait_limit(int32_t polls) {
+  if (polls < 0) return fail(FT_EINVAL, "wait limit must be >= 0");
+  g_wait_limit.store(polls, std::memory_order_relaxed);
+  return ok();
+}
+
 ft_status ft_nvfp4_dequant(int32_t hidden, int32_t inter, int32_t n_experts,
                            const ft_nvfp4_experts* bank, int32_t expert, int32_t tensor,
                            int32_t out_dtype, void* out, void* stream) {
@@ -536,7 +575,8 @@ ft_status ft_nvfp4_dequant(int32_t hidden, int32_t inter, int32_t n_experts,
     return fail(FT_EUNSUPPORTED, "dequant: hidden %d / inter %d unsupported", hidden, inter);
   if (expert < 0 || expert >= n_experts) return fail(FT_EINVAL, "dequant: expert out of range");
   if (tensor < 0 || tensor > 2) return fail(FT_EINVAL, "dequant: tensor must be 0, 1 or 2");
-  if (out_dtype != 0 && out_dtype != 1) return fail(FT_EINVAL, "dequant: out_dtype must be 0 or 1");
+  if (out_dtype < 0 || out_dtype > 3) return fail(FT_EINVAL, "dequant: out_dtype must be 0..3");
+  if (!aligned16(out)) return fail(FT_EINVAL, "dequant: out must be 16-byte aligned");
   if (!out) return fail(FT_EINVAL, "dequant: out is NULL");
   ft_status st = check_bank(bank, "dequant");
   if (st != FT_OK) return st;

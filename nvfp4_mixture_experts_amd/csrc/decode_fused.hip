@@ -38,7 +38,8 @@
 //      of them sums them in a fixed order into bf16 y.
 //
 // Every poll is bounded: if a value never arrives (a grid that is not
-// co-resident), the kernel stops waiting, raises the error word and finishes.
+// co-resident), the kernel stops waiting, records why in the error word and
+// finishes; the caller reads the word with ft_moe_device_status.
 #include "ftmoe_device.hpp"
 #include "ftmoe_kernels.hpp"
 
@@ -69,15 +70,36 @@ __device__ __forceinline__ float tag_value(uint64_t w) {
   return __uint_as_float(static_cast<uint32_t>(w));
 }
 
+// ------------------------------------------------------------ give-ups --
+//
+// err[0] collects the reasons (kWait* bits) of every wait that gave up since the
+// caller last read the status (ft_moe_device_status reads and clears it); err[1]
+// holds the generation of the latest call with a give-up, so that every other
+// wait of that call stops within 16 polls instead of running to its own limit.
+enum : uint32_t { kWaitLogits = 1u, kWaitGate = 2u, kWaitH = 4u, kWaitPartial = 8u };
+
+__device__ __forceinline__ void give_up(uint32_t* err, uint32_t gen, uint32_t why) {
+  __hip_atomic_fetch_or(err, why, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  st_dev(err + 1, gen);
+}
+
+// True when the wait has polled `spin_limit` times, or (checked every 16th poll)
+// another wait of this call has already given up; records the first case.
+__device__ __forceinline__ bool stop_waiting(int spins, int spin_limit, uint32_t* err,
+                                             uint32_t gen, uint32_t why) {
+  if (spins >= spin_limit) {
+    give_up(err, gen, why);
+    return true;
+  }
+  return (spins & 15) == 15 && ld_dev(err + 1) == gen;
+}
+
 // Reads one tagged word per lane, polling until every lane's word carries `gen`.
 __device__ __forceinline__ uint64_t poll_tag(const uint64_t* p, uint32_t gen, int spin_limit,
                                              uint32_t* err) {
   uint64_t wd = ld_tag(p);
   for (int spins = 0; __ballot(!tag_is(wd, gen)) != 0; ++spins) {
-    if (spins >= spin_limit) {
-      st_dev(err, 1u);
-      break;
-    }
+    if (stop_waiting(spins, spin_limit, err, gen, kWaitLogits)) break;
     __builtin_amdgcn_s_sleep(1);
     if (!tag_is(wd, gen)) wd = ld_tag(p);
   }
@@ -113,10 +135,7 @@ __device__ __forceinline__ void poll_h_batch(const uint64_t* const (&hrow)[N],
 #pragma unroll
     for (int m = 0; m < kL; ++m) ok = ok && (!want[m] || tag_is(wd[m], gen));
     if (__ballot(!ok) == 0) break;
-    if (spins >= spin_limit) {
-      st_dev(err, 1u);
-      break;
-    }
+    if (stop_waiting(spins, spin_limit, err, gen, kWaitH)) break;
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
     for (int m = 0; m < kL; ++m)
@@ -136,10 +155,7 @@ __device__ __forceinline__ float poll_gate(const uint64_t* lg, int E, uint32_t g
                                            int spin_limit, uint32_t* err) {
   uint64_t wd = ld_tag(lg + E);
   for (int spins = 0; !tag_is(wd, gen); ++spins) {
-    if (spins >= spin_limit) {
-      st_dev(err, 1u);
-      break;
-    }
+    if (stop_waiting(spins, spin_limit, err, gen, kWaitGate)) break;
     __builtin_amdgcn_s_sleep(1);
     wd = ld_tag(lg + E);
   }
@@ -177,10 +193,7 @@ __device__ void wave_topk_tagged(const uint64_t* lg, int E, int k, uint32_t gen,
 #pragma unroll
     for (int m = 0; m < SLOTS; ++m) ok = ok && tag_is(wd[m], gen);
     if (__ballot(!ok) == 0) break;
-    if (spins >= spin_limit) {
-      st_dev(err, 1u);
-      break;
-    }
+    if (stop_waiting(spins, spin_limit, err, gen, kWaitLogits)) break;
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
     for (int m = 0; m < SLOTS; ++m) {
@@ -679,10 +692,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
 #pragma unroll
               for (int i = 0; i < 8; ++i) ok = ok && tag_is(pv[i], gen);
               if (__ballot(!ok) == 0) break;
-              if (spins >= p.spin_limit) {
-                st_dev(p.err, 1u);
-                break;
-              }
+              if (stop_waiting(spins, p.spin_limit, p.err, gen, kWaitPartial)) break;
               __builtin_amdgcn_s_sleep(1);
 #pragma unroll
               for (int i = 0; i < 8; ++i)
@@ -746,6 +756,44 @@ hipError_t launch_decode_fused(const FusedParams& p, int grid, hipStream_t s) {
 }
 
 int fused_block_threads() { return kFWaves * kWave; }
+
+// The fewest blocks per CU that any instantiation of the fused kernel can keep
+// resident (the kernel needs one on every CU at once).
+hipError_t decode_fused_min_occupancy(int* blocks_per_cu) {
+  using K = void (*)(FusedParams);
+  static const K kernels[] = {
+#define FT_FUSED_LPR(L)                                                                         \
+  moe_decode_fused_kernel<L, 1, true>, moe_decode_fused_kernel<L, 1, false>,                  \
+      moe_decode_fused_kernel<L, 2, true>, moe_decode_fused_kernel<L, 2, false>,              \
+      moe_decode_fused_kernel<L, 3, true>, moe_decode_fused_kernel<L, 3, false>,              \
+      moe_decode_fused_kernel<L, 4, true>, moe_decode_fused_kernel<L, 4, false>
+      FT_FUSED_LPR(64), FT_FUSED_LPR(32), FT_FUSED_LPR(16), FT_FUSED_LPR(8)
+#undef FT_FUSED_LPR
+  };
+  int lowest = 1 << 30;
+  for (K k : kernels) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &n, reinterpret_cast<const void*>(k), kFWaves * kWave, 0);
+    if (e != hipSuccess) return e;
+    lowest = n < lowest ? n : lowest;
+  }
+  *blocks_per_cu = lowest;
+  return hipSuccess;
+}
+
+// Reads the error word of a decode workspace into *status and clears it.
+__global__ void device_status_kernel(uint32_t* err, int32_t* status) {
+  if (threadIdx.x == 0) {
+    const uint32_t v = __hip_atomic_exchange(err, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *status = static_cast<int32_t>(v);
+  }
+}
+
+hipError_t launch_device_status(uint32_t* err, int32_t* status, hipStream_t s) {
+  device_status_kernel<<<dim3(1), dim3(64), 0, s>>>(err, status);
+  return hipGetLastError();
+}
 
 // The widest power of two <= 64 lanes per row that divides the H/32 chunks of a
 // gate|up row, and the chunks each lane then owns.

@@ -55,6 +55,26 @@ __device__ __forceinline__ float dequant_one(float code_value, float scale, floa
   return (code_value * scale) * g;
 }
 
+// Eight e2m1 codes (one 32-bit word, low nibble = first element) times one e4m3
+// block scale -> eight bf16 values packed in a uint4 (an MFMA A/B operand of
+// 8 bf16).  Every code x scale product has at most 6 significant bits, so it is
+// exact in fp32 and in bf16, and the bf16 is the upper half of the fp32 bits (a
+// truncation that loses nothing).  The global scale is not applied here (the
+// grouped kernels apply it to the fp32 accumulator).
+__device__ __forceinline__ uint32_t upper_halves(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+__device__ __forceinline__ uint4 dequant8_bf16(uint32_t codes, float scale) {
+  const f32x2 a = e2m1x2_to_f32<0>(codes), b = e2m1x2_to_f32<1>(codes);
+  const f32x2 c = e2m1x2_to_f32<2>(codes), d = e2m1x2_to_f32<3>(codes);
+  uint4 r;
+  r.x = upper_halves(a.x * scale, a.y * scale);
+  r.y = upper_halves(b.x * scale, b.y * scale);
+  r.z = upper_halves(c.x * scale, c.y * scale);
+  r.w = upper_halves(d.x * scale, d.y * scale);
+  return r;
+}
+
 // ------------------------------------------------------- small divisions --
 //
 // n / d for 0 <= n < 2^24 and d >= 1 through an fp32 reciprocal: the estimate is

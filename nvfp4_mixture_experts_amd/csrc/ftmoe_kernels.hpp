@@ -60,7 +60,8 @@ struct FusedParams {
   uint64_t* h;                  // tagged [T][nslots][Imax]
   uint64_t* part;               // tagged [d_groups][blocks_per_group][64]
   uint32_t* gen;                // per-block call counters [grid]
-  uint32_t* err;                // set when a poll gives up (the result is then invalid)
+  uint32_t* err;                // [0] reasons of give-ups (the result is then invalid),
+                                // [1] generation of the latest call that gave up
   int d_groups;                 // T * H / 64 (token, row group) pairs of the down GEMV
   int blocks_per_group;         // blocks sharing one group when d_groups < grid
   int spin_limit;               // polls of one value before giving up
@@ -122,6 +123,9 @@ hipError_t launch_grouped_small(const PrefillParams& p, int ugroups, hipStream_t
 // Launchers: return the launch status (hipGetLastError after the launch).
 hipError_t launch_decode_fused(const FusedParams& p, int grid, hipStream_t s);
 int fused_block_threads();
+hipError_t decode_fused_min_occupancy(int* blocks_per_cu);
+// copies the error word err[0] of a decode workspace to *status and clears it
+hipError_t launch_device_status(uint32_t* err, int32_t* status, hipStream_t s);
 hipError_t launch_route(const RouteParams& p, bool fuse_topk, hipStream_t s);
 int route_fused_topk_tokens();  // the fused top-k handles at most this many tokens
 // Split-K fp64 MFMA router (for a few to a thousand tokens): K splits it uses for

@@ -48,20 +48,6 @@ __device__ __forceinline__ sg_f32x4 mfma(uint4 a, uint4 b, sg_f32x4 c) {
                                                  __builtin_bit_cast(sg_bf16x8, b), c, 0, 0, 0);
 }
 
-// 8 codes x one e4m3 scale -> 8 bf16 (exact: the upper half of each fp32 product).
-__device__ __forceinline__ uint32_t hi16x2(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-__device__ __forceinline__ uint4 dq8(uint32_t codes, float s) {
-  const f32x2 a = e2m1x2_to_f32<0>(codes), b = e2m1x2_to_f32<1>(codes);
-  const f32x2 c = e2m1x2_to_f32<2>(codes), d = e2m1x2_to_f32<3>(codes);
-  uint4 r;
-  r.x = hi16x2(a.x * s, a.y * s);
-  r.y = hi16x2(b.x * s, b.y * s);
-  r.z = hi16x2(c.x * s, c.y * s);
-  r.w = hi16x2(d.x * s, d.y * s);
-  return r;
-}
 __device__ __forceinline__ uint32_t word(const uint4& q, int j) {
   return j == 0 ? q.x : (j == 1 ? q.y : (j == 2 ? q.z : q.w));
 }
@@ -157,8 +143,8 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_kernel(PrefillParams 
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint4 b = xs[i * kRowU4 + (4 * q + g) * 4 + j];
-            ag = mfma(dq8(word(qg[q], j), j < 2 ? g0 : g1), b, ag);
-            au = mfma(dq8(word(qu[q], j), j < 2 ? u0 : u1), b, au);
+            ag = mfma(dequant8_bf16(word(qg[q], j), j < 2 ? g0 : g1), b, ag);
+            au = mfma(dequant8_bf16(word(qu[q], j), j < 2 ? u0 : u1), b, au);
           }
         }
       }
@@ -268,8 +254,8 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_pipe_kernel(PrefillPa
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint4 bx = xs[i * kRowU4 + (4 * g + q) * 4 + j];
-          ag = mfma(dq8(word(qg[b][q], j), j < 2 ? g0 : g1), bx, ag);
-          au = mfma(dq8(word(qu[b][q], j), j < 2 ? u0 : u1), bx, au);
+          ag = mfma(dequant8_bf16(word(qg[b][q], j), j < 2 ? g0 : g1), bx, ag);
+          au = mfma(dequant8_bf16(word(qu[b][q], j), j < 2 ? u0 : u1), bx, au);
         }
       }
     }
@@ -371,7 +357,7 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_kernel(PrefillParams p)
           const float s0 = e4m3_byte_to_f32<0>(sc[s]), s1 = e4m3_byte_to_f32<1>(sc[s]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            uint4 a = dq8(word(q[s], j), j < 2 ? s0 : s1);
+            uint4 a = dequant8_bf16(word(q[s], j), j < 2 ? s0 : s1);
             const int kk = (4 * s + g) * 4 + j;  // 16-byte word of the staged row
             uint4 bh = hs[0][i * kRowU4 + min(kk, kb / 8 - 1)];
             uint4 bl = hs[1][i * kRowU4 + min(kk, kb / 8 - 1)];
@@ -513,7 +499,7 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_pipe_kernel(PrefillPara
         const uint4 bh = hs[0][i * kRowU4 + kk], bl = hs[1][i * kRowU4 + kk];
         uint4 a[kRT];
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) a[rt] = dq8(word(q[rt][s], j), j < 2 ? s0[rt] : s1[rt]);
+        for (int rt = 0; rt < kRT; ++rt) a[rt] = dequant8_bf16(word(q[rt][s], j), j < 2 ? s0[rt] : s1[rt]);
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) acc[rt] = mfma(a[rt], bh, acc[rt]);
 #pragma unroll

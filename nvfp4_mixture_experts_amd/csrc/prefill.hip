@@ -44,23 +44,6 @@ __device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// Eight e2m1 codes (one 32-bit word, low nibble first) times one e4m3 block scale
-// -> eight bf16 values.  The products are exact in fp32 and in bf16, so the bf16
-// is the upper half of the fp32 bits (a truncation that loses nothing).
-__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-__device__ __forceinline__ uint4 dequant8_bf16(uint32_t codes, float scale) {
-  const f32x2 a = e2m1x2_to_f32<0>(codes), b = e2m1x2_to_f32<1>(codes);
-  const f32x2 c = e2m1x2_to_f32<2>(codes), d = e2m1x2_to_f32<3>(codes);
-  uint4 r;
-  r.x = pack_hi16(a.x * scale, a.y * scale);
-  r.y = pack_hi16(b.x * scale, b.y * scale);
-  r.z = pack_hi16(c.x * scale, c.y * scale);
-  r.w = pack_hi16(d.x * scale, d.y * scale);
-  return r;
-}
-
 // KPT = 16 or 32 consecutive K elements of one row (KPT/2 code bytes, KPT/16 scale
 // bytes) -> KPT/8 x 16 B of bf16.
 template <int KPT> struct Codes;

@@ -48,8 +48,16 @@ hipError_t launch_repack_w2(int H, int I, int n, const uint8_t* w2, const uint8_
 
 // Dequantise one tensor of one expert of a repacked bank.  Each thread decodes
 // one 32-bit word of codes (8 elements, inside one 16-element scale block) with
-// the same routines the GEMV kernels use (e2m1x2_to_f32, e4m3_byte_to_f32).
-// out: row-major [rows][K], fp32 (out_dtype 0) or bf16 (out_dtype 1).
+// the routines the compute kernels use, chosen by out_dtype (out: row-major
+// [rows][K]):
+//   0  fp32 code x scale x global, codes through e2m1x2_to_f32 (the down GEMV of
+//      the one-launch decode kernel);
+//   1  the same value rounded to bf16 (nearest-even);
+//   2  bf16 code x scale, no global scale, as the grouped and prefill kernels build
+//      their MFMA tiles (dequant8_bf16);
+//   3  fp32 code x scale x global with the codes through e2m1x2_to_bf16 (the
+//      gate|up GEMV of the one-launch decode kernel, which multiplies those bf16
+//      codes with the activations and applies the scale per 16-element block).
 __global__ __launch_bounds__(256) void dequant_kernel(int H, int I, Bank b, int e, int tensor,
                                                       int out_dtype, void* out) {
   const bool down = (tensor == 2);
@@ -76,26 +84,40 @@ __global__ __launch_bounds__(256) void dequant_kernel(int H, int I, Bank b, int 
   }
   const float s = e4m3_byte_to_f32<0>(scale_byte);
   const float g = b.gsc[3 * e + tensor];
-  float v[8];
-  const f32x2 p0 = e2m1x2_to_f32<0>(code_word), p1 = e2m1x2_to_f32<1>(code_word);
-  const f32x2 p2 = e2m1x2_to_f32<2>(code_word), p3 = e2m1x2_to_f32<3>(code_word);
-  v[0] = dequant_one(p0.x, s, g);
-  v[1] = dequant_one(p0.y, s, g);
-  v[2] = dequant_one(p1.x, s, g);
-  v[3] = dequant_one(p1.y, s, g);
-  v[4] = dequant_one(p2.x, s, g);
-  v[5] = dequant_one(p2.y, s, g);
-  v[6] = dequant_one(p3.x, s, g);
-  v[7] = dequant_one(p3.y, s, g);
   const size_t o = static_cast<size_t>(r) * K + k0;
-  if (out_dtype == 0) {
-    float* of = static_cast<float*>(out) + o;
+  if (out_dtype == 2) {
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o) = dequant8_bf16(code_word, s);
+    return;
+  }
+  float v[8];
+  if (out_dtype == 3) {
+    const bf16x2 c[4] = {e2m1x2_to_bf16<0>(code_word), e2m1x2_to_bf16<1>(code_word),
+                         e2m1x2_to_bf16<2>(code_word), e2m1x2_to_bf16<3>(code_word)};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) of[i] = v[i];
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = dequant_one(static_cast<float>(c[i][0]), s, g);
+      v[2 * i + 1] = dequant_one(static_cast<float>(c[i][1]), s, g);
+    }
   } else {
+    const f32x2 p0 = e2m1x2_to_f32<0>(code_word), p1 = e2m1x2_to_f32<1>(code_word);
+    const f32x2 p2 = e2m1x2_to_f32<2>(code_word), p3 = e2m1x2_to_f32<3>(code_word);
+    v[0] = dequant_one(p0.x, s, g);
+    v[1] = dequant_one(p0.y, s, g);
+    v[2] = dequant_one(p1.x, s, g);
+    v[3] = dequant_one(p1.y, s, g);
+    v[4] = dequant_one(p2.x, s, g);
+    v[5] = dequant_one(p2.y, s, g);
+    v[6] = dequant_one(p3.x, s, g);
+    v[7] = dequant_one(p3.y, s, g);
+  }
+  if (out_dtype == 1) {
     uint16_t* ob = static_cast<uint16_t*>(out) + o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) ob[i] = f32_to_bf16_bits(v[i]);
+  } else {
+    float* of = static_cast<float*>(out) + o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) of[i] = v[i];
   }
 }
 

@@ -98,8 +98,10 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def decode(dl: DeviceLayer, x: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-           stream=None):
-    """Returns (y bf16 [T, H], topk_ids, topk_w) on the device."""
+           stream=None, status: Optional[torch.Tensor] = None):
+    """Returns (y bf16 [T, H], topk_ids, topk_w) on the device.  With ``status`` (int32
+    device tensor of one element), the workspace's give-up reasons are copied there
+    after the call (0 = every device-side wait completed)."""
     T = x.shape[0]
     if workspace is None:
         workspace = ftmoe.alloc_workspace(dl.desc, T, ftmoe.PATH_DECODE, x.device)
@@ -108,6 +110,8 @@ def decode(dl: DeviceLayer, x: torch.Tensor, workspace: Optional[torch.Tensor] =
     w = torch.empty((T, dl.top_k), dtype=torch.float32, device=x.device)
     ftmoe.ft_moe_nvfp4_decode(dl.desc, x, dl.w_router, dl.bias, dl.routed, dl.shared,
                               dl.shared_gate, y, workspace, ids, w, stream=stream)
+    if status is not None:
+        ftmoe.ft_moe_device_status(workspace, status, stream)
     return y, ids, w
 
 

@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
         "ft_moe_nvfp4_decode": (I32, [D, I64, P, P, P, B, B, P, P, P, P, P, SZ, P]),
         "ft_moe_nvfp4_prefill": (I32, [D, I64, P, P, P, B, B, P, P, P, SZ, P]),
         "ft_nvfp4_dequant": (I32, [I32, I32, I32, B, I32, I32, I32, P, P]),
+        "ft_moe_device_status": (I32, [P, SZ, P, P]),
+        "ft_set_wait_limit": (I32, [I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -80,7 +82,8 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 EXPORTED = ("ft_abi_version", "ft_last_error", "ft_init", "ft_nvfp4_repacked_bytes",
             "ft_nvfp4_repack", "ft_moe_workspace_bytes", "ft_moe_route", "ft_moe_nvfp4_decode",
-            "ft_moe_nvfp4_prefill", "ft_nvfp4_dequant")
+            "ft_moe_nvfp4_prefill", "ft_nvfp4_dequant", "ft_moe_device_status",
+            "ft_set_wait_limit")
 
 
 def library_path() -> str:
@@ -215,13 +218,50 @@ def ft_moe_nvfp4_prefill(desc: FtMoeDesc, x, topk_ids, topk_w, routed: Bank,
                                      _stream(stream)), "ft_moe_nvfp4_prefill")
 
 
-def ft_nvfp4_dequant(bank: Bank, expert: int, tensor: int, out, stream=None) -> None:
-    """out: fp32 or bf16 [rows][K] device tensor (gate/up [I][H], down [H][I])."""
-    if out.dtype == torch.float32:
-        dt = 0
-    elif out.dtype == torch.bfloat16:
-        dt = 1
-    else:
-        raise TypeError("out must be float32 or bfloat16")
+# ft_nvfp4_dequant modes (see include/ftmoe.h)
+DEQ_F32, DEQ_BF16, DEQ_TILE_BF16, DEQ_GATEUP_F32 = 0, 1, 2, 3
+
+
+def ft_nvfp4_dequant(bank: Bank, expert: int, tensor: int, out, stream=None,
+                     mode: Optional[int] = None) -> None:
+    """out: fp32 or bf16 [rows][K] device tensor (gate/up [I][H], down [H][I]).
+    ``mode`` defaults to DEQ_F32 for fp32 ``out`` and DEQ_BF16 for bf16 ``out``."""
+    want = {DEQ_F32: torch.float32, DEQ_BF16: torch.bfloat16, DEQ_TILE_BF16: torch.bfloat16,
+            DEQ_GATEUP_F32: torch.float32}
+    if mode is None:
+        if out.dtype == torch.float32:
+            mode = DEQ_F32
+        elif out.dtype == torch.bfloat16:
+            mode = DEQ_BF16
+        else:
+            raise TypeError("out must be float32 or bfloat16")
+    if mode not in want:
+        raise ValueError(f"unknown dequant mode {mode}")
+    if out.dtype != want[mode]:
+        raise TypeError(f"mode {mode} writes {want[mode]}, out is {out.dtype}")
+    dt = mode
     _check(_lib.ft_nvfp4_dequant(bank.hidden, bank.inter, bank.n, bank.ref(), expert, tensor, dt,
                                  _ptr(out, None, "out"), _stream(stream)), "ft_nvfp4_dequant")
+
+
+# reasons ft_moe_device_status reports (OR-ed)
+WAIT_LOGITS, WAIT_GATE, WAIT_H, WAIT_PARTIAL = 1, 2, 4, 8
+
+
+def ft_moe_device_status(workspace, status, stream=None) -> None:
+    """Enqueue: copy the decode workspace's give-up reasons to ``status`` (int32 device
+    tensor, one element) and clear them."""
+    _check(_lib.ft_moe_device_status(_ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                     _ptr(status, torch.int32, "status"), _stream(stream)),
+           "ft_moe_device_status")
+
+
+def device_status(workspace, stream=None) -> int:
+    """Reads and clears the give-up reasons of a decode workspace (synchronises)."""
+    st = torch.zeros(1, dtype=torch.int32, device=workspace.device)
+    ft_moe_device_status(workspace, st, stream)
+    return int(st.item())
+
+
+def ft_set_wait_limit(polls: int) -> None:
+    _check(_lib.ft_set_wait_limit(int(polls)), "ft_set_wait_limit")

@@ -50,3 +50,71 @@ def host_layer(name: str, **overrides):
     if overrides:
         w = synth.dataclasses.replace(w, **overrides)
     return synth.make_layer(w)
+
+
+def decode_checked(device, dl, x, workspace=None, stream=None):
+    """device.decode plus a check that every device-side wait of the call completed."""
+    import torch
+    st = torch.full((1,), -1, dtype=torch.int32, device=x.device)
+    out = device.decode(dl, x, workspace, stream, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0, f"device-side wait gave up (status {int(st.item()):#x})"
+    return out
+
+
+def _threads():
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_layer_rows(layer, x, rows):
+    """oracle.moe_layer on the token rows ``rows`` of ``x``, with the rows split over a
+    thread pool (ctypes releases the GIL; tokens are independent in the oracle)."""
+    import concurrent.futures
+    import oracle
+    rows = list(rows)
+    n = _threads()
+    chunks = [rows[i::n] for i in range(n) if rows[i::n]]
+    with concurrent.futures.ThreadPoolExecutor(len(chunks)) as ex:
+        parts = list(ex.map(lambda c: oracle.moe_layer(layer, x[c]), chunks))
+    out = {}
+    for key in ("ids", "weights", "y64", "y"):
+        full = np.empty((len(rows),) + parts[0][key].shape[1:], parts[0][key].dtype)
+        for i, part in enumerate(parts):
+            full[i::len(chunks)] = part[key]
+        out[key] = full
+    return out
+
+
+def oracle_routes(x, w_router, bias, k):
+    """oracle.topk(oracle.router_logits(...)) for every token, over a thread pool."""
+    import concurrent.futures
+    import oracle
+    T = x.shape[0]
+    n = min(_threads(), T)
+    bounds = np.linspace(0, T, n + 1).astype(int)
+    def run(i):
+        lo, hi = bounds[i], bounds[i + 1]
+        return oracle.topk(oracle.router_logits(x[lo:hi], w_router, bias), k)
+    with concurrent.futures.ThreadPoolExecutor(n) as ex:
+        parts = list(ex.map(run, range(n)))
+    return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
+
+
+def cover_rows(ids, num_experts, must=()):
+    """Token rows, starting with ``must``, chosen greedily until every expert id in
+    [0, num_experts) appears in some chosen row's routes."""
+    rows = list(dict.fromkeys(int(r) for r in must))
+    covered = np.zeros(num_experts, bool)
+    for r in rows:
+        covered[ids[r]] = True
+    gain = np.zeros(ids.shape[0], np.int64)
+    while not covered.all():
+        gain[:] = (~covered[ids]).sum(axis=1)
+        gain[rows] = -1
+        r = int(np.argmax(gain))
+        if gain[r] <= 0:
+            break
+        rows.append(r)
+        covered[ids[r]] = True
+    return rows

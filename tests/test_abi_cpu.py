@@ -145,11 +145,23 @@ def test_host_validation_status_codes(ft):
     # dequant argument checks
     assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 8, 0, 0, 16, None) == ft.FT_EINVAL
     assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 0, 3, 0, 16, None) == ft.FT_EINVAL
-    assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 0, 0, 2, 16, None) == ft.FT_EINVAL
+    assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 0, 0, 4, 16, None) == ft.FT_EINVAL
+    assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 0, 0, 2, 24, None) == ft.FT_EINVAL  # alignment
     assert lib.ft_nvfp4_dequant(2000, 768, 8, b, 0, 0, 0, 16, None) == ft.FT_EUNSUPPORTED
     # repack argument checks
     assert lib.ft_nvfp4_repack(2048, 768, 8, *([16] * 7), None, None) == ft.FT_EINVAL
     assert lib.ft_nvfp4_repack(2048, 100, 8, *([16] * 8), None) == ft.FT_EUNSUPPORTED
+
+
+def test_device_status_and_wait_limit_validation(ft):
+    lib = _raw(ft)
+    assert lib.ft_moe_device_status(None, 1 << 20, 16, None) == ft.FT_EINVAL
+    assert lib.ft_moe_device_status(256, 1 << 20, None, None) == ft.FT_EINVAL
+    assert lib.ft_moe_device_status(272, 1 << 20, 16, None) == ft.FT_EWORKSPACE
+    assert lib.ft_moe_device_status(256, 128, 16, None) == ft.FT_EWORKSPACE
+    assert lib.ft_moe_device_status(256, 1 << 20, 18, None) == ft.FT_EINVAL
+    assert lib.ft_set_wait_limit(-1) == ft.FT_EINVAL
+    assert lib.ft_set_wait_limit(0) == ft.FT_OK
 
 
 def test_zero_tokens_route_enqueues_nothing(ft):

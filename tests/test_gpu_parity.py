@@ -11,7 +11,8 @@ import torch
 
 import oracle
 from nvfp4_mixture_experts_amd import synth
-from tests.gpu_util import (assert_output_close, f32_ulp_diff, host_layer, say)
+from tests.gpu_util import (assert_output_close, decode_checked, f32_ulp_diff, host_layer,
+                            oracle_layer_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +91,25 @@ def test_dequant_bit_exact_all_codes_and_scales(gpu, tensor):
         gotb = outb.cpu().view(torch.int16).numpy().view(np.uint16)
         nanb = np.isnan(want)
         assert np.array_equal(gotb[~nanb], wantb[~nanb])
+        # the one-launch decode kernel's gate|up routine (codes -> bf16 pairs)
+        outg = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+        ftmoe.ft_nvfp4_dequant(bank, e, tensor, outg, mode=ftmoe.DEQ_GATEUP_F32)
+        # the grouped / prefill MFMA tile builder: bf16 code x scale, no global scale
+        outt = torch.empty((rows, K), dtype=torch.bfloat16, device="cuda")
+        ftmoe.ft_nvfp4_dequant(bank, e, tensor, outt, mode=ftmoe.DEQ_TILE_BF16)
+        torch.cuda.synchronize()
+        _bits_equal_with_nan(outg.cpu().numpy(), want)
+        if tensor == 2:
+            want1 = oracle.dequant_matrix(b["w2_codes"][e], b["w2_scales"][e], 1.0)
+        else:
+            want1 = oracle.dequant_matrix(b["w13_codes"][e, sl], b["w13_scales"][e, sl], 1.0)
+        n1 = np.isnan(want1)
+        # code x scale is exact in bf16: the oracle's fp32 value has empty low halves
+        assert np.all(want1[~n1].view(np.uint32) & 0xFFFF == 0)
+        gott = outt.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(gott[~n1], (want1[~n1].view(np.uint32) >> 16).astype(np.uint16))
+        tv = (gott.astype(np.uint32) << 16).view(np.float32)
+        assert np.array_equal(np.isnan(tv), n1)
 
 
 def test_dequant_bit_exact_workload_bank(gpu):
@@ -103,13 +123,22 @@ def test_dequant_bit_exact_workload_bank(gpu):
             rows, K = (H, I) if tensor == 2 else (I, H)
             out = torch.empty((rows, K), dtype=torch.float32, device="cuda")
             ftmoe.ft_nvfp4_dequant(dl.routed, e, tensor, out)
+            outg = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+            ftmoe.ft_nvfp4_dequant(dl.routed, e, tensor, outg, mode=ftmoe.DEQ_GATEUP_F32)
+            outt = torch.empty((rows, K), dtype=torch.bfloat16, device="cuda")
+            ftmoe.ft_nvfp4_dequant(dl.routed, e, tensor, outt, mode=ftmoe.DEQ_TILE_BF16)
             g = float(L.global_scale[e, tensor])
             if tensor == 2:
                 want = oracle.dequant_matrix(L.w2_codes[e], L.w2_scales[e], g)
+                want1 = oracle.dequant_matrix(L.w2_codes[e], L.w2_scales[e], 1.0)
             else:
                 sl = slice(0, I) if tensor == 0 else slice(I, 2 * I)
                 want = oracle.dequant_matrix(L.w13_codes[e, sl], L.w13_scales[e, sl], g)
+                want1 = oracle.dequant_matrix(L.w13_codes[e, sl], L.w13_scales[e, sl], 1.0)
             assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+            assert np.array_equal(outg.cpu().numpy().view(np.uint32), want.view(np.uint32))
+            gott = outt.cpu().view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(gott, (want1.view(np.uint32) >> 16).astype(np.uint16))
 
 
 # ------------------------------------------------------------------ route --
@@ -169,6 +198,79 @@ def test_route_ties_go_to_lowest_index(gpu, tokens):
     _check_routes(ids, wt, ref_ids, ref_w, "ties")
 
 
+def _zero_nan_router(E, H, rng):
+    """Router rows whose logits round to +0 or -0 (one tiny product of either sign,
+    or an all-zero row), NaN (a NaN weight), or clearly negative numbers, for tokens
+    whose elements are positive and whose element 0 is tiny."""
+    wr = -np.abs(rng.standard_normal((E, H)).astype(np.float32) * np.float32(0.02))
+    for e in range(10):                          # +0 / -0 / exact zero
+        wr[e] = 0.0
+        wr[e, 0] = [1e-30, -1e-30, 0.0][e % 3]
+    for e in range(10, 14):
+        wr[e, 5] = np.nan
+    return wr
+
+
+def _zero_nan_tokens(T, H, rng):
+    xf = np.abs(rng.standard_normal((T, H)).astype(np.float32)) + np.float32(0.05)
+    xf[:, 0] = np.float32(1e-30)
+    return synth.bf16_bits_from_f32(xf)
+
+
+def _routes_nan_aware(ids, w, ref_ids, ref_w, what):
+    ids = ids.cpu().numpy()
+    w = w.cpu().numpy()
+    assert np.array_equal(ids, ref_ids), f"{what}: ids differ\n{ids}\n{ref_ids}"
+    assert np.array_equal(np.isnan(w), np.isnan(ref_w)), what
+    ok = ~np.isnan(ref_w)
+    assert f32_ulp_diff(w[ok], ref_w[ok]).max(initial=0) <= 2, what
+    say(f"  {what}: ids exact")
+
+
+@pytest.mark.parametrize("E,k", [(24, 16), (18, 16), (64, 12)])
+@pytest.mark.parametrize("tokens", [1, 3, 16, 40, 1100])   # every router and top-k kernel
+def test_route_signed_zero_and_nan_logits(gpu, E, k, tokens):
+    """Logits of +0 and -0 compare equal (the lower index wins), a NaN logit ranks
+    below every number; the oracle decides."""
+    from nvfp4_mixture_experts_amd import ftmoe
+    H = 256
+    rng = np.random.default_rng(100 + E + tokens)
+    wr = _zero_nan_router(E, H, rng)
+    x = _zero_nan_tokens(tokens, H, rng)
+    logits = oracle.router_logits(x, wr)
+    assert np.all(np.signbit(logits[:, 1]) & (logits[:, 1] == 0))      # -0 logits
+    assert np.all((logits[:, 0] == 0) & ~np.signbit(logits[:, 0]))     # +0 logits
+    assert np.all(np.isnan(logits[:, 10:14]))
+    ref_ids, ref_w = oracle.topk(logits, k)
+    desc = ftmoe.make_desc(E, H, 128, k, 1)
+    ws = ftmoe.alloc_workspace(desc, tokens, ftmoe.PATH_ROUTE)
+    ids = torch.empty((tokens, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((tokens, k), dtype=torch.float32, device="cuda")
+    ftmoe.ft_moe_route(desc, gpu.tokens_to_device(x), torch.from_numpy(wr).cuda(), None, ids, wt,
+                       ws)
+    torch.cuda.synchronize()
+    _routes_nan_aware(ids, wt, ref_ids, ref_w, f"route E={E} k={k} T={tokens}")
+
+
+@pytest.mark.parametrize("E", [24, 18])        # 18: two NaN logits among the top 16
+@pytest.mark.parametrize("tokens", [1, 4, 12])   # fused kernel (one token, several), grouped
+def test_decode_routes_signed_zero_and_nan_logits(gpu, E, tokens):
+    k, H = 16, 256
+    w = synth.dataclasses.replace(synth.WORKLOADS["tiny_e8_top2"], num_experts=E, top_k=k,
+                                  hidden=H, inter=128)
+    layer = synth.make_layer(w)
+    rng = np.random.default_rng(7 + tokens)
+    layer.w_router = _zero_nan_router(E, H, rng)
+    x = _zero_nan_tokens(tokens, H, rng)
+    ref_ids, ref_w = oracle.topk(oracle.router_logits(x, layer.w_router), k)
+    dl = gpu.upload_layer(layer)
+    y, ids, wt = decode_checked(gpu, dl, gpu.tokens_to_device(x))
+    _routes_nan_aware(ids, wt, ref_ids, ref_w, f"decode E={E} k={k} T={tokens}")
+    if not np.isnan(ref_w).any():
+        ref = oracle.moe_layer(layer, x)
+        assert_output_close(gpu.bf16_bits(y), ref["y"], f"decode, zero logits, T={tokens}")
+
+
 @pytest.mark.parametrize("num_experts", [1000, 1024])
 def test_route_many_experts_split_router(gpu, num_experts):
     """40 tokens (split-K router) with 1000 and 1024 experts and a router bias: the
@@ -198,7 +300,7 @@ def test_route_many_experts_split_router(gpu, num_experts):
     ("tiny_e8_top2", 1, None),
     ("decode_e288_top8", 1, None),
     ("decode_e512_top10_shared", 1, None),
-    ("batched_decode_t32_hot64", 32, [0, 9, 22, 31]),
+    ("batched_decode_t32_hot64", 32, None),        # every token of the batched workload
     ("decode_e288_top8", 2, None),                # fused kernel, several tokens, I = 768
     ("batched_decode_t32_hot64", 7, [0, 6]),     # largest count on the fused kernel
     ("batched_decode_t32_hot64", 8, [0, 7]),     # smallest count on the grouped path
@@ -209,11 +311,11 @@ def test_decode_matches_oracle(gpu, name, tokens, sample):
     dl = dev_layer(gpu, name)
     L = host_layer(name)
     x = synth.make_tokens(w, tokens=tokens)
-    y, ids, wt = gpu.decode(dl, gpu.tokens_to_device(x))
+    y, ids, wt = decode_checked(gpu, dl, gpu.tokens_to_device(x))
     torch.cuda.synchronize()
     yb = gpu.bf16_bits(y)
     rows = list(range(tokens)) if sample is None else sample
-    ref = oracle.moe_layer(L, x[rows])
+    ref = oracle_layer_rows(L, x, rows)
     assert np.array_equal(ids.cpu().numpy()[rows], ref["ids"])
     assert f32_ulp_diff(wt.cpu().numpy()[rows], ref["weights"]).max() <= 2
     assert_output_close(yb[rows], ref["y"], f"{name} T={tokens}")
@@ -229,7 +331,7 @@ def test_decode_all_experts_selected(gpu):
     L = synth.make_layer(w)
     dl = gpu.upload_layer(L)
     x = synth.make_tokens(w, tokens=3)
-    y, ids, _ = gpu.decode(dl, gpu.tokens_to_device(x))
+    y, ids, _ = decode_checked(gpu, dl, gpu.tokens_to_device(x))
     torch.cuda.synchronize()
     ref = oracle.moe_layer(L, x)
     assert np.array_equal(np.sort(ids.cpu().numpy(), axis=1), np.tile(np.arange(16), (3, 1)))
@@ -243,7 +345,7 @@ def test_decode_shapes_outside_the_workloads(gpu):
     L = synth.make_layer(w)
     dl = gpu.upload_layer(L)
     x = synth.make_tokens(w)
-    y, ids, _ = gpu.decode(dl, gpu.tokens_to_device(x))
+    y, ids, _ = decode_checked(gpu, dl, gpu.tokens_to_device(x))
     torch.cuda.synchronize()
     ref = oracle.moe_layer(L, x)
     assert np.array_equal(ids.cpu().numpy(), ref["ids"])
@@ -259,7 +361,7 @@ def test_grouped_decode_shapes_outside_the_workloads(gpu):
         L = synth.make_layer(w)
         dl = gpu.upload_layer(L)
         x = synth.make_tokens(w)
-        y, ids, _ = gpu.decode(dl, gpu.tokens_to_device(x))
+        y, ids, _ = decode_checked(gpu, dl, gpu.tokens_to_device(x))
         torch.cuda.synchronize()
         ref = oracle.moe_layer(L, x)
         assert np.array_equal(ids.cpu().numpy(), ref["ids"])
@@ -277,7 +379,7 @@ def test_grouped_decode_pipelined_shapes(gpu, H, I, Is, T):
     L = synth.make_layer(w)
     dl = gpu.upload_layer(L)
     x = synth.make_tokens(w)
-    y, ids, _ = gpu.decode(dl, gpu.tokens_to_device(x))
+    y, ids, _ = decode_checked(gpu, dl, gpu.tokens_to_device(x))
     torch.cuda.synchronize()
     ref = oracle.moe_layer(L, x)
     assert np.array_equal(ids.cpu().numpy(), ref["ids"])
@@ -318,8 +420,8 @@ def test_decode_is_deterministic(gpu, tokens):
     big = torch.zeros(3 * span, dtype=torch.uint8, device="cuda")
     # disjoint workspaces at different offsets; calls ordered (a workspace is never
     # shared by calls that may run at the same time)
-    y0, _, _ = gpu.decode(dl, x)
-    y1, _, _ = gpu.decode(dl, x, workspace=big[1024:1024 + n])
+    y0, _, _ = decode_checked(gpu, dl, x)
+    y1, _, _ = decode_checked(gpu, dl, x, workspace=big[1024:1024 + n])
     main = torch.cuda.current_stream()
     s = torch.cuda.Stream()
     s.wait_stream(main)
@@ -342,7 +444,7 @@ def test_decode_graph_replays_match_eager(gpu, tokens):
     ws = ftmoe.alloc_workspace(dl.desc, tokens, ftmoe.PATH_DECODE)
     eager = []
     for x in xs:
-        y, _, _ = gpu.decode(dl, x, workspace=ws)
+        y, _, _ = decode_checked(gpu, dl, x, workspace=ws)
         eager.append(y.clone())
     torch.cuda.synchronize()
     xin = xs[0].clone()
@@ -363,8 +465,7 @@ def test_decode_graph_replays_match_eager(gpu, tokens):
         torch.cuda.synchronize()
         assert torch.equal(yout.view(torch.int16), eager[i].view(torch.int16)), rep
         # eager work between replays
-        gpu.decode(dl, xs[(i + 1) % 3], workspace=ws)
-        torch.cuda.synchronize()
+        decode_checked(gpu, dl, xs[(i + 1) % 3], workspace=ws)
 
 
 # ---------------------------------------------------------------- prefill --
@@ -411,8 +512,8 @@ def test_token_order_does_not_change_results(gpu, tokens):
     perm = np.random.default_rng(9).permutation(tokens)
     xd, xpd = gpu.tokens_to_device(x), gpu.tokens_to_device(x[perm])
     if tokens <= 64:
-        y, _, _ = gpu.decode(dl, xd)
-        yp, _, _ = gpu.decode(dl, xpd)
+        y, _, _ = decode_checked(gpu, dl, xd)
+        yp, _, _ = decode_checked(gpu, dl, xpd)
     else:
         ids, wt = gpu.route(dl, xd)
         y = gpu.prefill(dl, xd, ids, wt)

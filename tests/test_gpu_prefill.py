@@ -13,7 +13,8 @@ import torch
 
 import oracle
 from nvfp4_mixture_experts_amd import synth
-from tests.gpu_util import assert_output_close, host_layer, say
+from tests.gpu_util import (assert_output_close, cover_rows, f32_ulp_diff, host_layer,
+                            oracle_layer_rows, oracle_routes, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -144,8 +145,10 @@ def test_prefill_unrolled_widths(gpu, H, Is):
 
 @pytest.mark.slow
 def test_prefill_full_chunk_sampled(gpu):
-    """The 8192-token chunk at full size: routes of sampled tokens bit-exact, and
-    their outputs against the oracle; every output finite."""
+    """The 8192-token chunk at full size: the routes of every token bit-exact against
+    the oracle router; outputs against the oracle on rows that together reach every
+    one of the 512 experts and both ends of every 256-token unit of the shared
+    expert; every output finite."""
     name = "prefill_t8192"
     w = synth.WORKLOADS[name]
     L = host_layer(name)
@@ -159,9 +162,16 @@ def test_prefill_full_chunk_sampled(gpu):
     yf = (yb.astype(np.uint32) << 16).view(np.float32)
     assert np.all(np.isfinite(yf))
     ids_np = ids.cpu().numpy()
+    ref_ids, ref_w = oracle_routes(x, L.w_router, L.bias, w.top_k)
+    assert np.array_equal(ids_np, ref_ids)
+    assert f32_ulp_diff(wt.cpu().numpy(), ref_w).max() <= 2
     counts = np.bincount(ids_np.ravel(), minlength=w.num_experts)
-    say(f"  tokens per expert: min {counts.min()} max {counts.max()} mean {counts.mean():.1f}")
-    rows = [0, 1, 4095, 8190, 8191, 2742]
-    ref = oracle.moe_layer(L, x[rows])
+    say(f"  routes of all {w.tokens} tokens exact; tokens per expert: min {counts.min()} "
+        f"max {counts.max()} mean {counts.mean():.1f}")
+    ends = [t for j in range(w.tokens // 256) for t in (256 * j, 256 * j + 255)]
+    rows = cover_rows(ids_np, w.num_experts, must=ends)
+    say(f"  comparing {len(rows)} rows with the oracle (all {w.num_experts} experts reached)")
+    assert len(np.unique(ids_np[rows])) == w.num_experts
+    ref = oracle_layer_rows(L, x, rows)
     assert np.array_equal(ids_np[rows], ref["ids"])
-    assert_output_close(yb[rows], ref["y"], "prefill T=8192 sampled")
+    assert_output_close(yb[rows], ref["y"], f"prefill T=8192, {len(rows)} rows")

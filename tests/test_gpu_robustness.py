@@ -38,3 +38,51 @@ def test_prefill_out_of_range_ids_poison_only_their_token():
     assert np.isnan(b[2]).all() and np.isnan(b[4]).all()
     keep = [0, 1, 3, 5]
     assert np.array_equal(b[keep], g[keep])
+
+
+def test_decode_wait_give_up_is_reported_and_the_next_workspace_is_clean():
+    """The one-launch decode kernel's blocks agree on a call's generation by each
+    counting its own calls; values handed between blocks carry that generation.
+    Here the per-block counters of one workspace are set to unequal values from
+    the host, so no hand-off can complete: with a small wait limit every wait
+    gives up after a bounded number of polls, the kernel finishes, and
+    ft_moe_device_status reports it (and clears it).  A fresh workspace then
+    gives the oracle's result with a clean status."""
+    import oracle
+    from nvfp4_mixture_experts_amd import device, ftmoe
+    from tests.gpu_util import assert_output_close
+    assert torch.cuda.is_available()
+    ftmoe.ft_init(0)
+    w = synth.dataclasses.replace(synth.WORKLOADS["decode_e512_top10_shared"], num_experts=32,
+                                  hidden=256, inter=128, shared_inter=128)
+    L = synth.make_layer(w)
+    dl = device.upload_layer(L)
+    xh = synth.make_tokens(w, tokens=1)
+    x = device.tokens_to_device(xh)
+    ref = oracle.moe_layer(L, xh)
+
+    ws = ftmoe.alloc_workspace(dl.desc, 1, ftmoe.PATH_DECODE, "cuda")
+    y, ids, _ = device.decode(dl, x, ws)
+    assert ftmoe.device_status(ws) == 0
+    # per-block call counters: bytes [256, 256 + 4 * 1024) of a decode workspace
+    rng = np.random.default_rng(11)
+    ws[256:256 + 4096] = torch.from_numpy(rng.integers(0, 256, 4096, dtype=np.uint8)).cuda()
+    say("  desynchronised the block counters; wait limit 64 polls")
+    try:
+        ftmoe.ft_set_wait_limit(64)
+        device.decode(dl, x, ws)
+        torch.cuda.synchronize()
+    finally:
+        ftmoe.ft_set_wait_limit(0)
+    st = ftmoe.device_status(ws)
+    say(f"  status after the desynchronised call: {st:#x}")
+    assert st != 0 and (st & ~0xF) == 0
+    assert ftmoe.device_status(ws) == 0           # the read cleared it
+
+    ws2 = ftmoe.alloc_workspace(dl.desc, 1, ftmoe.PATH_DECODE, "cuda")
+    y2, ids2, _ = device.decode(dl, x, ws2)
+    torch.cuda.synchronize()
+    assert ftmoe.device_status(ws2) == 0
+    assert np.array_equal(ids2.cpu().numpy(), ref["ids"])
+    assert_output_close(device.bf16_bits(y2), ref["y"], "fresh workspace after a give-up")
+    assert np.array_equal(device.bf16_bits(y2), device.bf16_bits(y))
