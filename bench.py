@@ -86,26 +86,37 @@ def measured_traffic(workload: str):
     return {"bytes": fetch + write, "fetch": fetch, "write": write}
 
 
+def _time_oracle(layer, x, tokens: int, seconds: float, openmp: bool):
+    import oracle
+    oracle.moe_layer(layer, x[:1], openmp=openmp)        # warm-up (and library load)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        i = (n * tokens) % x.shape[0]
+        oracle.moe_layer(layer, x[i:i + tokens], openmp=openmp)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return n, el
+
+
 def cpu_baseline(w, seconds: float = 12.0) -> dict:
-    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    """The CPU oracle, as it stands, on a bounded sample of the same workload: its
+    OpenMP build (independent rows spread over every host core; same bits as the
+    plain build) and, for reference, the plain single-threaded build."""
     import oracle
     from nvfp4_mixture_experts_amd import synth
     layer = synth.make_layer(w)
     x = synth.make_tokens(w, tokens=64, stream="cpu_baseline")
-    oracle.moe_layer(layer, x[:1])                    # warm-up (and library load)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        i = n % x.shape[0]
-        oracle.moe_layer(layer, x[i:i + w.tokens])
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": n / el, "unit": "calls/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} single-token calls of {w.name} on instance 0, {el:.1f} s, "
-                      f"single-threaded C oracle (fp64), host {platform.processor() or 'cpu'}, "
-                      f"nproc {os.cpu_count()}"}
+    cores = oracle.threads(openmp=True)
+    n, el = _time_oracle(layer, x, w.tokens, seconds / 2, openmp=True)
+    n1, el1 = _time_oracle(layer, x, w.tokens, seconds / 2, openmp=False)
+    return {"value": n / el, "unit": "calls/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} calls of {w.name} ({w.tokens} token(s) each) on instance 0 in "
+                      f"{el:.1f} s, C oracle (fp64) built with OpenMP on {cores} threads; "
+                      f"host {platform.processor() or 'cpu'}, nproc {os.cpu_count()}",
+            "single_thread_value": n1 / el1,
+            "single_thread_sample": f"{n1} calls in {el1:.1f} s, plain single-threaded build"}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
@@ -124,18 +135,15 @@ def cpu_baseline_prefill(w, seconds: float) -> dict:
     from nvfp4_mixture_experts_amd import synth
     layer = synth.make_layer(w)
     x = synth.make_tokens(w, tokens=64, stream="cpu_baseline")
-    oracle.moe_layer(layer, x[:1])
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.moe_layer(layer, x[n % 64:n % 64 + 1])
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} tokens of {w.name} (routing, experts, shared expert) one at a time on "
-                      f"instance 0, {el:.1f} s, single-threaded C oracle (fp64), nproc {os.cpu_count()}"}
+    cores = oracle.threads(openmp=True)
+    n, el = _time_oracle(layer, x, 1, seconds / 2, openmp=True)
+    n1, el1 = _time_oracle(layer, x, 1, seconds / 2, openmp=False)
+    return {"value": n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} tokens of {w.name} (routing, experts, shared expert) one at a time "
+                      f"on instance 0 in {el:.1f} s, C oracle (fp64) built with OpenMP on "
+                      f"{cores} threads; nproc {os.cpu_count()}",
+            "single_thread_value": n1 / el1,
+            "single_thread_sample": f"{n1} tokens in {el1:.1f} s, plain single-threaded build"}
 
 
 def run_prefill(args, w) -> int:
@@ -207,37 +215,37 @@ def run_prefill(args, w) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4800)
-    ap.add_argument("--warmup", type=int, default=480)
-    ap.add_argument("--workload", default="decode_e288_top8")
-    ap.add_argument("--instances", type=int, default=0,
-                    help="distinct layer instances to cycle (0 = enough to exceed 4x the MALL)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="after timing, run one plain elementwise copy (negation) of this many "
-                         "MiB, as the known-size reference for HBM byte counters")
-    args = ap.parse_args()
+def stream_read_probe(dev) -> dict:
+    """Achievable HBM read bandwidth for context: torch's sum over 4 GiB of fp32 (a
+    read-bound library reduction), best of 5."""
+    import torch
+    n = 1 << 30
+    t = torch.ones(n, dtype=torch.float32, device=dev)
+    out = torch.empty((), dtype=torch.float32, device=dev)
+    torch.sum(t, out=out)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(5):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.sum(t, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del t
+    torch.cuda.empty_cache()
+    return {"op": "torch.sum over 4 GiB fp32, best of 5", "gbps": round(4 * 2 ** 30 / (best * 1e-3) / 1e9, 1)}
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the layer's sharding is described in DESIGN.md); run with --gpus 1",
-              file=sys.stderr)
-        return 2
 
+def measure_decode(args, w, steps: int, warmup: int, reps: int) -> dict:
+    """Decode calls of workload ``w`` cycling over L layer instances (enough that the
+    bytes touched per cycle exceed 4x the Infinity Cache).  Each repetition is one HIP
+    graph of exactly ``steps`` calls, continuing the cycle; the median repetition is
+    reported.  Inputs are resident in HBM before timing starts."""
     import torch
     from nvfp4_mixture_experts_amd import device, ftmoe, synth
-
-    w = synth.WORKLOADS[args.workload]
-    ftmoe.ft_init(0)
-    if w.tokens > 64:
-        return run_prefill(args, w)
     dev = torch.device("cuda:0")
-
-    # ---- layer instances, generated and repacked on the device
     per_call_guess = algorithmic_bytes(w, np.zeros((w.tokens, w.top_k)) + np.arange(w.top_k))
     L = args.instances or max(2, math.ceil(4 * MALL_BYTES / per_call_guess))
     layers, xs = [], []
@@ -260,53 +268,56 @@ def main() -> int:
     wts = torch.empty((w.tokens, w.top_k), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def call(i):
+    def call(i, s):
         dl = layers[i % L]
         ftmoe.ft_moe_nvfp4_decode(desc, xs[i % L], dl.w_router, dl.bias, dl.routed, dl.shared,
-                                  dl.shared_gate, y, ws, ids_all[i % L], wts, stream=stream)
+                                  dl.shared_gate, y, ws, ids_all[i % L], wts, stream=s)
 
-    for i in range(max(args.warmup, L)):
-        call(i)
+    for i in range(max(warmup, L)):
+        call(i, stream)
     torch.cuda.synchronize()
 
     # eager launches (one host call per step), for reference
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    n_eager = min(args.steps, 20 * L)
+    n_eager = min(steps, 20 * L)
     start.record(stream)
     for i in range(n_eager):
-        call(i)
+        call(i, stream)
     end.record(stream)
     torch.cuda.synchronize()
     eager_ms = start.elapsed_time(end) / n_eager
 
-    # timed region: one HIP graph holding one call per layer instance (a decode
-    # loop is captured once and replayed); replays cover exactly `steps` calls
-    cycles = max(1, args.steps // L)
-    steps = cycles * L
-    graph = torch.cuda.CUDAGraph()
+    # timed region: repetition r replays a graph of exactly `steps` calls on
+    # instances (r * steps + i) mod L (a decode loop captured once and replayed)
+    graphs = []
     cap = torch.cuda.Stream()
     cap.wait_stream(stream)
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(L):
-                ftmoe.ft_moe_nvfp4_decode(desc, xs[i], layers[i].w_router, layers[i].bias,
-                                          layers[i].routed, layers[i].shared,
-                                          layers[i].shared_gate, y, ws, ids_all[i], wts,
-                                          stream=cap)
+    for r in range(reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(steps):
+                    call(r * steps + i, cap)
+        graphs.append(g)
     torch.cuda.synchronize()
-    for _ in range(3):
-        graph.replay()
+    for g in graphs:
+        g.replay()
     torch.cuda.synchronize()
+    rep_ms = []
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(cycles):
-        graph.replay()
-    end.record(stream)
-    torch.cuda.synchronize()
+    for g in graphs:
+        torch.cuda.synchronize()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        rep_ms.append(start.elapsed_time(end) / steps)
     wall = time.perf_counter() - t0
-    ms_total = start.elapsed_time(end)
-    ms_per_step = ms_total / steps
+    status = ftmoe.device_status(ws)
+    if status != 0:
+        raise RuntimeError(f"a device-side wait gave up during timing (status {status:#x})")
+    ms_per_step = float(np.median(rep_ms))
     calls_per_s = 1000.0 / ms_per_step
 
     if args.copy_calibration_mib > 0:
@@ -321,29 +332,25 @@ def main() -> int:
     ids_np = ids_all.cpu().numpy()
     bytes_per_call = float(np.mean([algorithmic_bytes(w, ids_np[l]) for l in range(L)]))
     gbps = bytes_per_call / (ms_per_step * 1e-3) / 1e9
-    touched = bytes_per_call * L
     grouped = w.tokens >= ftmoe.GROUPED_DECODE_MIN_TOKENS
     traffic = None if grouped else measured_traffic(w.name)
     kernel = ("grouped decode path: route, grouping, gate|up, down, combine (whole call)"
               if grouped else DECODE_KERNEL)
-
-    out = {
-        "metric": METRIC,
+    del graphs, layers, xs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {
+        "workload": w.name,
         "value": round(calls_per_s, 1),
         "unit": "calls/s",
-        "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
+        "reps": reps,
         "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp32",
-        "data": "synthetic",
+        "ms_per_step_reps": [round(v, 6) for v in rep_ms],
         "config": {"workload": w.name, "experts": w.num_experts, "hidden": w.hidden,
                    "inter": w.inter, "top_k": w.top_k, "tokens": w.tokens,
                    "shared_inter": w.shared_inter, "layer_instances": L,
-                   "bytes_touched_per_cycle": int(touched)},
+                   "bytes_touched_per_cycle": int(bytes_per_call * L)},
         "achieved_gbps": round(gbps, 1),
         "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"kernel": kernel, "bound": "hbm",
@@ -354,12 +361,84 @@ def main() -> int:
                      "traffic_write": None if traffic is None else int(round(traffic["write"])),
                      "algorithmic_bytes_per_launch": int(round(bytes_per_call))},
         "wall_s_timed": round(wall, 3),
-        "launch": "hip graph of one call per layer instance, replayed",
+        "launch": f"{reps} HIP graphs of {steps} calls each (one call per layer instance in "
+                  "turn), each replayed once and timed; median reported",
         "eager_ms_per_step": round(eager_ms, 6),
+        "device_status": status,
     }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000,
+                    help="calls per timed repetition")
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--reps", type=int, default=5, help="timed repetitions (median reported)")
+    ap.add_argument("--workload", default="decode_e288_top8")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated further decode workloads measured into the same line "
+                         "(default: decode_e512_top10_shared with the default workload)")
+    ap.add_argument("--instances", type=int, default=0,
+                    help="distinct layer instances to cycle (0 = enough to exceed 4x the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
+    ap.add_argument("--no-stream-probe", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one plain elementwise copy (negation) of this many "
+                         "MiB, as the known-size reference for HBM byte counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer runs on one MI355X in this build (no "
+              "multi-GPU path; its sharding is described in DESIGN.md); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.reps < 1:
+        print("--steps and --reps must be positive", file=sys.stderr)
+        return 2
+
+    import torch
+    from nvfp4_mixture_experts_amd import ftmoe, synth
+
+    w = synth.WORKLOADS[args.workload]
+    ftmoe.ft_init(0)
+    if w.tokens > 64:
+        return run_prefill(args, w)
+    also = args.also
+    if also is None:
+        also = "decode_e512_top10_shared" if args.workload == "decode_e288_top8" else ""
+    also = [a for a in also.split(",") if a]
+
+    main_m = measure_decode(args, w, args.steps, args.warmup, args.reps)
+    extra = [measure_decode(args, synth.WORKLOADS[a], args.steps, args.warmup, args.reps)
+             for a in also]
+    out = {
+        "metric": METRIC,
+        "value": main_m["value"],
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": main_m["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": main_m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+    }
+    for key in ("config", "roofline", "achieved_gbps", "hbm_peak_frac", "reps",
+                "ms_per_step_reps", "wall_s_timed", "launch", "eager_ms_per_step",
+                "device_status"):
+        out[key] = main_m[key]
+    if extra:
+        out["also"] = extra
+    if not args.no_stream_probe:
+        probe = stream_read_probe(torch.device("cuda:0"))
+        probe["decode_frac_of_probe"] = round(main_m["achieved_gbps"] / probe["gbps"], 4)
+        out["hbm_stream_probe"] = probe
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(w, args.cpu_seconds)
-        out["cpu_baseline"] = cb
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -22,7 +22,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ftmoe_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "_ftmoe_oracle.so")
-_lib = None
+# the same source built with OpenMP: only for timing the oracle on every host core
+_OMP_LIB_PATH = os.path.join(_HERE, "_ftmoe_oracle_omp.so")
+_libs = {}
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -31,22 +33,29 @@ _F32 = ctypes.c_float
 _F64 = ctypes.c_double
 
 
+_CFLAGS = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared"]
+
+
 def build() -> str:
-    """Compile the oracle into ``oracle/_ftmoe_oracle.so`` (gcc, no fast-math, no contraction)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
+    """Compile the oracle into ``oracle/_ftmoe_oracle.so`` (gcc, no fast-math, no contraction;
+    the OpenMP pragmas ignored) and the OpenMP timing copy ``oracle/_ftmoe_oracle_omp.so``."""
+    cmd = _CFLAGS + ["-Wno-unknown-pragmas", _SRC, "-o", _LIB_PATH + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    cmd = _CFLAGS + ["-fopenmp", _SRC, "-o", _OMP_LIB_PATH + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_OMP_LIB_PATH + ".tmp", _OMP_LIB_PATH)
     return _LIB_PATH
 
 
-def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
+def _load(omp: bool = False):
+    if omp in _libs:
+        return _libs[omp]
+    path = _OMP_LIB_PATH if omp else _LIB_PATH
+    if not os.path.exists(path):
         build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     lib.or_e2m1.restype = _F64
     lib.or_e2m1.argtypes = [ctypes.c_uint32]
     lib.or_e4m3.restype = _F64
@@ -70,10 +79,12 @@ def _load():
     lib.or_expert_output.restype = None
     lib.or_expert_output.argtypes = [_I32, _I32, _I64, _P, _P, _P, _P, _P, _I32, _F32, _F32,
                                      _P, _P]
+    lib.or_threads.restype = _I32
+    lib.or_threads.argtypes = []
     lib.or_moe_layer.restype = _I32
     lib.or_moe_layer.argtypes = ([_I32, _I32, _I32, _I32, _I32, _F32, _F32, _I64, _P, _P, _P]
                                  + [_P] * 5 + [_I32] + [_P] * 6 + [_P] * 6)
-    _lib = lib
+    _libs[omp] = lib
     return lib
 
 
@@ -86,6 +97,11 @@ def _ptr(a):
 
 def _c(a, dtype):
     return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def threads(openmp: bool = False) -> int:
+    """Threads the oracle's row loops use (1 for the plain build)."""
+    return int(_load(openmp).or_threads())
 
 
 # ------------------------------------------------------------------ codecs --
@@ -174,12 +190,13 @@ def expert_output(layer, e: int, x_row: np.ndarray, shared: bool = False) -> np.
     return out
 
 
-def moe_layer(layer, x: np.ndarray, ids=None, weights=None) -> dict:
+def moe_layer(layer, x: np.ndarray, ids=None, weights=None, openmp: bool = False) -> dict:
     """Run the whole layer for the tokens in ``x`` (bf16 bits u16 [T, H]).
 
     ``layer`` carries the weights (see ``nvfp4_mixture_experts_amd.synth.Layer``).
     With ``ids``/``weights`` given, those routes are used instead of the router.
-    Returns ``{"ids", "weights", "y64", "y"}``.
+    ``openmp`` runs the OpenMP build of the same source (for timing on all cores;
+    same bits).  Returns ``{"ids", "weights", "y64", "y"}``.
     """
     x = _c(x, np.uint16)
     T = x.shape[0]
@@ -201,7 +218,7 @@ def moe_layer(layer, x: np.ndarray, ids=None, weights=None) -> dict:
             _c(layer.global_scale, np.float32)]
     wr = _c(layer.w_router, np.float32)
     bias = _c(layer.bias, np.float32)
-    rc = _load().or_moe_layer(layer.num_experts, layer.hidden, layer.inter, k, layer.act,
+    rc = _load(openmp).or_moe_layer(layer.num_experts, layer.hidden, layer.inter, k, layer.act,
                               layer.gate_max, layer.up_absmax, T, _ptr(x), _ptr(wr), _ptr(bias),
                               *[_ptr(a) for a in bank], Is, *[_ptr(a) for a in sh],
                               _ptr(ids_in), _ptr(w_in), _ptr(ids_out), _ptr(w_out), _ptr(y64),

@@ -8,6 +8,11 @@
  * table or helper with the HIP library; the two meet only in the seeded input
  * arrays that the tests hand to both.
  *
+ * The "omp parallel for" pragmas only spread independent rows (each with its
+ * own serial sum) over threads in a second build used to time the oracle on
+ * every host core; the checker is the plain build, where they are ignored, and
+ * the two give identical bits.
+ *
  * Every function computes the plain definition, one element at a time, in
  * IEEE binary64 (products of the fp32/bf16/e2m1/e4m3 operands are exact in
  * binary64), and rounds once at the end where a narrower type is stored.
@@ -49,6 +54,19 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the row loops use: 1 in the plain build. */
+int32_t or_threads(void)
+{
+#ifdef _OPENMP
+    return (int32_t)omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------- codecs -- */
 
@@ -107,6 +125,7 @@ static uint32_t row_code(const uint8_t *row_codes, int64_t k)
 void or_dequant_matrix(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
                        float g, float *out)
 {
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         const uint8_t *rc = codes + r * (K / 2);
         const uint8_t *rs = scales + r * (K / 16);
@@ -159,6 +178,7 @@ uint16_t or_bf16_from_double(double v)
 void or_router_logits(int64_t T, int32_t E, int32_t H, const uint16_t *x, const float *W,
                       const float *bias, float *logits)
 {
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t t = 0; t < T; ++t) {
         for (int32_t e = 0; e < E; ++e) {
             double acc = 0.0;
@@ -246,6 +266,7 @@ static void expert_forward(int32_t H, int32_t I, const float *wg, const float *w
                            int32_t act, double gate_max, double up_absmax, const double *x,
                            double *hbuf, double *o)
 {
+#pragma omp parallel for schedule(static)
     for (int32_t r = 0; r < I; ++r) {
         double g = 0.0, u = 0.0;
         for (int32_t h = 0; h < H; ++h) {
@@ -254,6 +275,7 @@ static void expert_forward(int32_t H, int32_t I, const float *wg, const float *w
         }
         hbuf[r] = or_swiglu(act, g, u, gate_max, up_absmax);
     }
+#pragma omp parallel for schedule(static)
     for (int32_t c = 0; c < H; ++c) {
         double acc = 0.0;
         for (int32_t r = 0; r < I; ++r)

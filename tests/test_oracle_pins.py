@@ -441,3 +441,15 @@ def test_expert_output_matches_layer_with_single_route():
     out = oracle.moe_layer(layer, x, ids=ids, weights=wts)
     o5 = oracle.expert_output(layer, 5, x[0])
     assert np.array_equal(out["y64"][0], o5)
+
+
+def test_openmp_timing_copy_gives_identical_bits():
+    # the OpenMP build only spreads independent rows over threads
+    w = synth.dataclasses.replace(synth.WORKLOADS["decode_e512_top10_shared"], num_experts=24)
+    layer = synth.make_layer(w)
+    x = synth.make_tokens(w, tokens=2)
+    a = oracle.moe_layer(layer, x)
+    b = oracle.moe_layer(layer, x, openmp=True)
+    for key in ("ids", "weights", "y64", "y"):
+        assert np.array_equal(a[key], b[key]), key
+    assert oracle.threads(False) == 1 and oracle.threads(True) >= 1
