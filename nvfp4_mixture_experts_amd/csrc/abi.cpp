@@ -73,60 +73,15 @@ ft_status fused_grid(int* grid) {
   *grid = g_fused_grid[dev];
   return FT_OK;
 }
-constexpr int kMaxTopK = 16;
-constexpr int kMaxDecodeTokens = 64;
-// Decode calls of at least this many tokens run the grouped path (route, grouping,
-// gate|up and down grouped GEMMs, combine), where every selected expert's weights
-// are read once for all of its tokens; fewer tokens run the fused one-launch kernel.
-constexpr int kGroupedDecodeMinTokens = 8;
-// Router calls of at least this many tokens compute the logits on the MFMA units.
-constexpr int kRouteMfmaMinTokens = 1024;
-// From this many tokens (and below kRouteMfmaMinTokens) the router is the split-K
-// fp64 MFMA product; below it the row kernel (its last block selecting up to
-// route_fused_topk_tokens() tokens, else a top-k kernel).  Measured on the batched
-// decode workload: the split router saves 2-5 us from 32 tokens on and costs
-// 1-2 us at 8 and 16 (its two kernels each pay a memory round trip).
-int route_split_min_tokens() { return 24; }
-
-// Bytes of the split router's partial sums for up to T tokens (the largest over
-// every token count it serves, so that a workspace for T serves smaller T).
-size_t route_split_cap(const ft_moe_desc& d, int64_t T) {
-  size_t cap = 0;
-  const int64_t hi = T < kRouteMfmaMinTokens ? T : kRouteMfmaMinTokens - 1;
-  for (int64_t t = route_split_min_tokens(); t <= hi; ++t) {
-    const size_t b = route_split_bytes(d.num_experts, static_cast<int>(t), d.hidden);
-    cap = b > cap ? b : cap;
-  }
-  return cap;
-}
-constexpr int kRowGroup = 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-bool inter_ok(int I) { return I >= 64 && I <= 4096 && I % 64 == 0; }
 
 ft_status check_desc(const ft_moe_desc* d) {
-  if (!d) return fail(FT_EINVAL, "desc is NULL");
-  if (d->num_experts <= 0 || d->hidden <= 0 || d->inter <= 0 || d->top_k <= 0 ||
-      d->shared_inter < 0)
-    return fail(FT_EINVAL, "desc has a non-positive size");
-  if (d->top_k > d->num_experts)
-    return fail(FT_EINVAL, "top_k %d exceeds num_experts %d", d->top_k, d->num_experts);
-  if (d->act != 0 && d->act != 1) return fail(FT_EINVAL, "act must be 0 or 1");
-  if (d->num_experts > kMaxExperts)
-    return fail(FT_EUNSUPPORTED, "num_experts %d > %d", d->num_experts, kMaxExperts);
-  if (d->top_k > kMaxTopK) return fail(FT_EUNSUPPORTED, "top_k %d > %d", d->top_k, kMaxTopK);
-  int lpr = 0, cpl = 0;
-  gateup_geometry(d->hidden, &lpr, &cpl);
-  if (d->hidden % 256 != 0 || d->hidden > 8192 || lpr == 0 || cpl < 1 || cpl > 4)
-    return fail(FT_EUNSUPPORTED, "hidden %d unsupported (multiple of 256, <= 8192)", d->hidden);
-  if (!inter_ok(d->inter))
-    return fail(FT_EUNSUPPORTED, "inter %d unsupported (multiple of 64 in [64, 4096])", d->inter);
-  if (d->shared_inter != 0 && !inter_ok(d->shared_inter))
-    return fail(FT_EUNSUPPORTED, "shared_inter %d unsupported", d->shared_inter);
-  return FT_OK;
+  char msg[160];
+  const ft_status st = desc_problem(d, msg, sizeof msg);
+  return st == FT_OK ? FT_OK : fail(st, "%s", msg);
 }
 
 ft_status check_bank(const ft_nvfp4_experts* b, const char* name) {
@@ -152,76 +107,6 @@ Bank to_bank(const ft_nvfp4_experts* b, int inter) {
   return r;
 }
 
-// Workspace regions.  The route counter sits at offset 0 for every path and is
-// reset by the kernel that uses it, so a route workspace may be reused across
-// token counts once it has been zero-filled.
-struct Layout {
-  size_t sync, gen, logits, h, part;                                 // route / fused decode
-  size_t rsplit;                                                     // split-K router partials
-  size_t ids, w;                                                     // routes of a grouped decode
-  size_t gamma, count, cursor, offset, units, nunits, sorted, hhi, hlo, out;  // grouped experts
-  size_t total;
-};
-
-constexpr int kRouteCounterWord = 0;  // in the sync region
-constexpr int kErrorWord = 32;        // in the sync region (its own cache line): reasons,
-                                      // then the generation of the latest give-up
-
-Layout layout(const ft_moe_desc& d, int64_t T, int path) {
-  Layout L{};
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off += align256(bytes);
-    return o;
-  };
-  const size_t t = static_cast<size_t>(T);
-  const size_t k = static_cast<size_t>(d.top_k);
-  const size_t E = static_cast<size_t>(d.num_experts);
-  const size_t H = static_cast<size_t>(d.hidden);
-  const size_t imax = static_cast<size_t>(d.inter > d.shared_inter ? d.inter : d.shared_inter);
-  const size_t nslots = k + (d.shared_inter > 0 ? 1 : 0);
-  L.sync = take(256);  // route counter, error word
-  auto grouped = [&]() {
-    const int Ti = static_cast<int>(T), ki = d.top_k;
-    const size_t P = t * k;
-    L.gamma = take(t * 4);
-    L.count = take(E * 4);
-    L.cursor = take(E * 4);
-    L.offset = take(E * 4);
-    L.units = take(static_cast<size_t>(prefill_max_units(d.num_experts, Ti, ki,
-                                                         d.shared_inter > 0) + kUnitSlack) *
-                   sizeof(PfUnit));
-    L.nunits = take(4);
-    L.sorted = take(P * 4);
-    L.hhi = take((P + t) * imax * 2);
-    L.hlo = take((P + t) * imax * 2);
-    L.out = take(t * nslots * H * 4);
-  };
-  if (path == 0) {
-    L.logits = take(t * E * 4);
-    L.rsplit = take(route_split_cap(d, T));
-  } else if (path == 1) {
-    // the fused kernel's regions, then (for token counts that take the grouped
-    // path) router logits, routes and the grouped regions
-    L.gen = take(static_cast<size_t>(kMaxFusedGrid) * 4);
-    const size_t fused_logits = static_cast<size_t>(kLogitCopies) * t * (E + 1) * 8;
-    const size_t route_logits = t * E * 4;
-    L.logits = take(fused_logits > route_logits ? fused_logits : route_logits);
-    L.h = take(t * nslots * imax * 8);
-    L.part = take(static_cast<size_t>(kMaxFusedGrid) * kRowGroup * 8);
-    if (T >= kGroupedDecodeMinTokens) {
-      L.ids = take(t * k * 4);
-      L.w = take(t * k * 4);
-      L.rsplit = take(route_split_cap(d, T));
-      grouped();
-    }
-  } else {
-    grouped();
-  }
-  L.total = off;
-  return L;
-}
 
 ft_status check_ws(const ft_moe_desc* d, int64_t T, int path, void* ws, size_t ws_bytes,
                           Layout* L) {
@@ -293,7 +178,7 @@ ft_status run_route(const ft_moe_desc* desc, int T, const uint16_t* x, const flo
     if (e != hipSuccess) return hip_fail(e, "top-k kernel");
     return FT_OK;
   }
-  if (T >= route_split_min_tokens()) {
+  if (T >= kRouteSplitMinTokens) {
     // split-K fp64 MFMA partial sums, then a block per token sums them (in split
     // order), rounds once to fp32 and selects
     p.part = split_part;

@@ -795,14 +795,5 @@ hipError_t launch_device_status(uint32_t* err, int32_t* status, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The widest power of two <= 64 lanes per row that divides the H/32 chunks of a
-// gate|up row, and the chunks each lane then owns.
-void gateup_geometry(int H, int* lpr, int* cpl) {
-  const int chunks = H / 32;
-  int l = 64;
-  while (l > 8 && chunks % l != 0) l >>= 1;
-  *lpr = (chunks % l == 0) ? l : 0;
-  *cpl = (*lpr > 0) ? chunks / l : 0;
-}
 
 }  // namespace ftmoe

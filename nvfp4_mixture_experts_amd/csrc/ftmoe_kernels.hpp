@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "host_layout.hpp"
+
 namespace ftmoe {
 
 // One repacked NVFP4 expert bank (see ft_nvfp4_repack for the layout).
@@ -41,8 +43,6 @@ struct RouteParams {
 // handed from one block to another are "tagged": an 8-byte word holding the fp32
 // value in its low half and the call's generation number in its high half,
 // written and read with single 8-byte device-coherent accesses.
-constexpr int kLogitCopies = 16;    // replicas of the router logits (spreads the reads)
-constexpr int kMaxFusedGrid = 1024;
 
 struct FusedParams {
   const uint16_t* x;            // bf16 [T][H]
@@ -67,26 +67,6 @@ struct FusedParams {
   int spin_limit;               // polls of one value before giving up
 };
 
-// Many-token path (grouped GEMMs over the routed (token, slot) pairs).
-constexpr int kMaxExperts = 1024;   // experts per bank supported by the grouping kernels
-constexpr int kGroupPairs = 1024;   // pairs per histogram block
-constexpr int kGroupOneBlockPairs = 16384;  // up to this many pairs are grouped by one block
-constexpr int kPfUnitTokens = 256;    // tokens per work unit of a many-token call
-constexpr int kSmallCallTokens = 64;  // calls of at most this many tokens take the few-token
-constexpr int kSmallUnitTokens = 16;  // kernels, with units of at most this many tokens (one
-                                      // MFMA column block: a unit's tokens share one weight pass)
-
-// Spare entries after the last possible unit of the unit table: the expert kernels
-// read units[u] (u < 8 * ceil(units / 8)) together with the unit count, before
-// checking u against it.
-constexpr int kUnitSlack = 8;
-
-struct PfUnit {
-  int bank;    // 0 routed, 1 shared
-  int expert;  // routed expert id (0 for the shared bank)
-  int start;   // routed: first position in `sorted`; shared: first token
-  int count;   // 1 .. unit_tokens
-};
 
 struct PrefillParams {
   const uint16_t* x;       // bf16 [T][H]
@@ -113,9 +93,6 @@ struct PrefillParams {
   uint16_t* y;             // bf16 [T][H]
 };
 
-int prefill_unit_tokens(int T);
-int prefill_max_units(int E, int T, int k, bool shared);
-int prefill_group_blocks(int T, int k);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 // expert GEMMs of the grouped path for few tokens (after grouping, before combine)
 hipError_t launch_grouped_small(const PrefillParams& p, int ugroups, hipStream_t s);
@@ -128,17 +105,10 @@ hipError_t decode_fused_min_occupancy(int* blocks_per_cu);
 hipError_t launch_device_status(uint32_t* err, int32_t* status, hipStream_t s);
 hipError_t launch_route(const RouteParams& p, bool fuse_topk, hipStream_t s);
 int route_fused_topk_tokens();  // the fused top-k handles at most this many tokens
-// Split-K fp64 MFMA router (for a few to a thousand tokens): K splits it uses for
-// (E, T, H), and the bytes of its partial sums.
-int route_split_k(int E, int T, int H);
-size_t route_split_bytes(int E, int T, int H);
 hipError_t launch_route_split(const RouteParams& p, hipStream_t s);
 hipError_t launch_topk(const RouteParams& p, hipStream_t s);
 // logits only (no shared gate, no top-k), as an fp64 MFMA product; H % 64 == 0
 hipError_t launch_route_mfma(const RouteParams& p, hipStream_t s);
-// Lanes per row and chunks per lane of the decode gate|up GEMV for hidden size H
-// (supported when lpr > 0 and 1 <= cpl <= 4).
-void gateup_geometry(int H, int* lpr, int* cpl);
 hipError_t launch_repack_w2(int H, int I, int n, const uint8_t* w2, const uint8_t* w2s,
                             uint8_t* out_w2, uint8_t* out_w2s, hipStream_t s);
 hipError_t launch_dequant(int H, int I, const Bank& b, int expert, int tensor, int out_dtype,

@@ -1023,20 +1023,6 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PrefillParams p) {
 
 // ------------------------------------------------------------ launchers --
 
-int prefill_unit_tokens(int T) { return T <= kSmallCallTokens ? kSmallUnitTokens : kPfUnitTokens; }
-
-int prefill_max_units(int E, int T, int k, bool shared) {
-  // sum over experts of ceil(n_e / ut) <= (experts with a pair) + P / ut
-  const long long P = static_cast<long long>(T) * k;
-  const int ut = prefill_unit_tokens(T);
-  long long n = (P < E ? P : E) + P / ut + (shared ? (T + ut - 1) / ut : 0);
-  return static_cast<int>(n);
-}
-
-int prefill_group_blocks(int T, int k) {
-  const long long P = static_cast<long long>(T) * k;
-  return static_cast<int>((P + kGroupPairs - 1) / kGroupPairs);
-}
 
 hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
   PrefillParams p = p0;

@@ -282,9 +282,6 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteParams p) {
 // row blocks: with the full 32 splits of a call of up to 32 tokens the grid then
 // fits one block per CU (E = 512 with the shared gate, 513 rows: 64-row blocks
 // would leave a ninth block of one row per split, 288 blocks, 32 CUs running two).
-constexpr int kRouteSplitTokens = 32;
-constexpr int kRouteSplitTargetBlocks = 512;
-constexpr int kRouteMaxSplits = 32;
 constexpr int kRouteSplitMinWaves = 4;
 constexpr int kRouteSplitMaxWaves = 8;
 constexpr int kRouteSplitMaxRowBlocks = 8;
@@ -452,23 +449,6 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void topk_split_kernel(RoutePara
   }
 }
 
-int route_split_k(int E, int T, int H) {
-  // chosen as for 64-row blocks whatever the block's wave count: more splits than
-  // that add partial sums for the top-k to read (measured slower at 64 tokens)
-  const int nrb = (E + 1 + 63) / 64;
-  const int ntb = (T + kRouteSplitTokens - 1) / kRouteSplitTokens;
-  const int kmax = H / 64;  // 64-K steps
-  int ks = 1;
-  // the largest power of two that divides H / 64 and keeps about the target blocks
-  while ((kmax % (2 * ks)) == 0 && 2 * ks <= kRouteMaxSplits &&
-         nrb * ntb * 2 * ks <= kRouteSplitTargetBlocks)
-    ks *= 2;
-  return ks;
-}
-
-size_t route_split_bytes(int E, int T, int H) {
-  return static_cast<size_t>(route_split_k(E, T, H)) * T * (E + 1) * sizeof(double);
-}
 
 hipError_t launch_route_split(const RouteParams& p0, hipStream_t s) {
   RouteParams p = p0;
