@@ -198,6 +198,27 @@ ft_status ft_moe_nvfp4_prefill(const ft_moe_desc *desc, int64_t tokens, const ui
 ft_status ft_moe_device_status(void *workspace, size_t workspace_bytes, int32_t *status,
                                void *stream);
 
+/* ft_moe_nvfp4_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture that may not call hipMalloc, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments and results as ft_moe_nvfp4_decode for
+ * 1 <= tokens <= 7 (the one-launch kernel), without a workspace: the call uses a
+ * fixed 4 MiB array of device memory that the library holds on each GPU it runs
+ * on until the process ends, located and zero-filled by ft_init (call it first on
+ * each device; otherwise FT_EINVAL).  Shapes whose decode workspace
+ * (ft_moe_workspace_bytes, path 1) exceeds 4 MiB return FT_EWORKSPACE; 8 or more
+ * tokens return FT_EUNSUPPORTED.  It allocates nothing and only enqueues work on
+ * `stream` (capturable).  Every call on one GPU shares that array and it keeps
+ * the last call's contents: calls on one GPU must not overlap (two streams
+ * running this call at once race).  status: optional device int32 that receives
+ * what ft_moe_device_status would report for the call's waits (NULL = not read). */
+ft_status ft_moe_nvfp4_decode_noalloc(const ft_moe_desc *desc, int64_t tokens, const uint16_t *x,
+                                      const float *w_router, const float *bias,
+                                      const ft_nvfp4_experts *routed,
+                                      const ft_nvfp4_experts *shared,
+                                      const uint16_t *shared_gate, int32_t *topk_ids_out,
+                                      float *topk_w_out, uint16_t *y, int32_t *status,
+                                      void *stream);
+
 /* Test and diagnostic hook: the number of polls after which a device-side wait of
  * ft_moe_nvfp4_decode gives up (0 restores the default, about one second).  It is
  * process-wide and applies to calls enqueued afterwards.  A call in which one wait

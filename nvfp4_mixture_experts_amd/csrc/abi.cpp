@@ -9,6 +9,7 @@
 #include <cstring>
 #include <algorithm>
 
+#include "abi_internal.hpp"
 #include "ftmoe.h"
 #include "ftmoe_kernels.hpp"
 
@@ -240,6 +241,17 @@ ft_status run_grouped(const ft_moe_desc* desc, int T, const uint16_t* x, const i
 
 }  // namespace
 
+namespace ftmoe {
+ft_status abi_fail(ft_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+ft_status abi_hip_fail(hipError_t e, const char* what) { return hip_fail(e, what); }
+}  // namespace ftmoe
+
 extern "C" {
 
 int32_t ft_abi_version(void) { return FT_ABI_VERSION; }
@@ -261,6 +273,8 @@ ft_status ft_init(int32_t device) {
                 prop.gcnArchName);
   int grid = 0;
   ft_status st = fused_grid(&grid);
+  if (st != FT_OK) return st;
+  st = scratch_setup(device);
   if (st != FT_OK) return st;
   return ok();
 }

@@ -69,6 +69,7 @@ def _load() -> ctypes.CDLL:
         "ft_nvfp4_dequant": (I32, [I32, I32, I32, B, I32, I32, I32, P, P]),
         "ft_moe_device_status": (I32, [P, SZ, P, P]),
         "ft_set_wait_limit": (I32, [I32]),
+        "ft_moe_nvfp4_decode_noalloc": (I32, [D, I64, P, P, P, B, B, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -83,7 +84,7 @@ _lib = _load()
 EXPORTED = ("ft_abi_version", "ft_last_error", "ft_init", "ft_nvfp4_repacked_bytes",
             "ft_nvfp4_repack", "ft_moe_workspace_bytes", "ft_moe_route", "ft_moe_nvfp4_decode",
             "ft_moe_nvfp4_prefill", "ft_nvfp4_dequant", "ft_moe_device_status",
-            "ft_set_wait_limit")
+            "ft_set_wait_limit", "ft_moe_nvfp4_decode_noalloc")
 
 
 def library_path() -> str:
@@ -265,3 +266,17 @@ def device_status(workspace, stream=None) -> int:
 
 def ft_set_wait_limit(polls: int) -> None:
     _check(_lib.ft_set_wait_limit(int(polls)), "ft_set_wait_limit")
+
+
+def ft_moe_nvfp4_decode_noalloc(desc: FtMoeDesc, x, w_router, bias, routed: Bank,
+                                shared: Optional[Bank], shared_gate, y, topk_ids_out=None,
+                                topk_w_out=None, status=None, stream=None) -> None:
+    """ft_moe_nvfp4_decode on the library's static scratch (1..7 tokens, no workspace)."""
+    _check(_lib.ft_moe_nvfp4_decode_noalloc(
+        ctypes.byref(desc), x.shape[0], _ptr(x, torch.bfloat16, "x"),
+        _ptr(w_router, torch.float32, "w_router"), _ptr(bias, torch.float32, "bias"),
+        routed.ref(), shared.ref() if shared is not None else None,
+        _ptr(shared_gate, torch.bfloat16, "shared_gate"),
+        _ptr(topk_ids_out, torch.int32, "topk_ids_out"),
+        _ptr(topk_w_out, torch.float32, "topk_w_out"), _ptr(y, torch.bfloat16, "y"),
+        _ptr(status, torch.int32, "status"), _stream(stream)), "ft_moe_nvfp4_decode_noalloc")
