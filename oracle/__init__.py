@@ -84,6 +84,9 @@ def _load(omp: bool = False):
     lib.or_moe_layer.restype = _I32
     lib.or_moe_layer.argtypes = ([_I32, _I32, _I32, _I32, _I32, _F32, _F32, _I64, _P, _P, _P]
                                  + [_P] * 5 + [_I32] + [_P] * 6 + [_P] * 6)
+    lib.or_moe_layer_slots.restype = _I32
+    lib.or_moe_layer_slots.argtypes = ([_I32, _I32, _I32, _I32, _I32, _F32, _F32, _I64, _P, _P, _P,
+                                        _I32, _P] + [_P] * 5 + [_I32] + [_P] * 6 + [_P] * 5)
     _libs[omp] = lib
     return lib
 
@@ -226,3 +229,41 @@ def moe_layer(layer, x: np.ndarray, ids=None, weights=None, openmp: bool = False
     if rc != 0:
         raise ValueError("oracle rejected the layer shape")
     return {"ids": ids_out, "weights": w_out, "y64": y64, "y": y}
+
+
+def moe_layer_slots(layer, x: np.ndarray, slot_of: np.ndarray, slot_bank: dict,
+                    openmp: bool = False) -> dict:
+    """The layer with its routed experts in a bank of expert slots: ``slot_bank`` holds
+    canonical arrays of n_slots experts (w13_codes, w13_scales, w2_codes, w2_scales,
+    global_scale); ``slot_of`` int32 [E] names the slot of each expert, or a value
+    outside [0, n_slots) when it is not resident.  Routing uses ``layer``'s router.
+    Returns ``{"ids", "weights", "miss", "y64", "y"}``; ``miss[t, i]`` is the id of a
+    selected expert that is not resident, else -1."""
+    x = _c(x, np.uint16)
+    T = x.shape[0]
+    k = layer.top_k
+    slot_of = _c(slot_of, np.int32)
+    assert slot_of.shape == (layer.num_experts,)
+    bank = [_c(slot_bank["w13_codes"], np.uint8), _c(slot_bank["w13_scales"], np.uint8),
+            _c(slot_bank["w2_codes"], np.uint8), _c(slot_bank["w2_scales"], np.uint8),
+            _c(slot_bank["global_scale"], np.float32)]
+    n_slots = bank[0].shape[0]
+    Is = layer.shared_inter
+    sh = [None] * 6
+    if Is > 0:
+        sh = [_c(layer.s13_codes, np.uint8), _c(layer.s13_scales, np.uint8),
+              _c(layer.s2_codes, np.uint8), _c(layer.s2_scales, np.uint8),
+              _c(layer.s_global, np.float32), _c(layer.shared_gate, np.uint16)]
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    miss = np.empty((T, k), np.int32)
+    y64 = np.empty((T, layer.hidden), np.float64)
+    y = np.empty((T, layer.hidden), np.uint16)
+    rc = _load(openmp).or_moe_layer_slots(
+        layer.num_experts, layer.hidden, layer.inter, k, layer.act, layer.gate_max,
+        layer.up_absmax, T, _ptr(x), _ptr(_c(layer.w_router, np.float32)),
+        _ptr(_c(layer.bias, np.float32)), n_slots, _ptr(slot_of), *[_ptr(a) for a in bank], Is,
+        *[_ptr(a) for a in sh], _ptr(ids), _ptr(w), _ptr(miss), _ptr(y64), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle rejected the layer shape")
+    return {"ids": ids, "weights": w, "miss": miss, "y64": y64, "y": y}

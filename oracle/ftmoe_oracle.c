@@ -399,3 +399,90 @@ int32_t or_moe_layer(int32_t E, int32_t H, int32_t I, int32_t k, int32_t act, fl
     free(xd); free(hb); free(o); free(acc);
     return 0;
 }
+
+/* ------------------------------------------------- expert-slot indirection -- */
+
+/* The layer with its routed experts held in a bank of expert SLOTS (FreeToken fork
+ * PR #84, page 1, the interleaved A/B table: the production configuration keeps
+ * 2100 expert slots and reports expert-cache misses per token; FreeToken commit
+ * log, page 2: the expert banks plan their residency).
+ *   slot_of[e] is the slot of the bank holding expert e's weights, or any value
+ *   outside [0, n_slots) when expert e is not resident.  Routing is unchanged
+ *   (it reads only the router).  Reading taken here: a selected expert that is not
+ *   resident contributes nothing to y, its routing weight is kept (the others are
+ *   not renormalised), and its id is reported in miss[t * k + i] (-1 when the
+ *   expert of that place is resident), so that the caller can page it in and
+ *   recompute.  The bank (w13c .. gsc) is a canonical bank of n_slots experts. */
+int32_t or_moe_layer_slots(int32_t E, int32_t H, int32_t I, int32_t k, int32_t act,
+                           float gate_max, float up_absmax, int64_t T, const uint16_t *x,
+                           const float *Wr, const float *bias, int32_t n_slots,
+                           const int32_t *slot_of, const uint8_t *w13c, const uint8_t *w13s,
+                           const uint8_t *w2c, const uint8_t *w2s, const float *gsc, int32_t Is,
+                           const uint8_t *s13c, const uint8_t *s13s, const uint8_t *s2c,
+                           const uint8_t *s2s, const float *sgsc, const uint16_t *sgate,
+                           int32_t *ids_out, float *w_out, int32_t *miss, double *y64,
+                           uint16_t *y)
+{
+    if (E <= 0 || H <= 0 || I <= 0 || k <= 0 || k > E || T < 0 || H % 16 || I % 16 ||
+        n_slots <= 0 || !slot_of || (Is > 0 && Is % 16))
+        return -1;
+    int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1) * k);
+    float *wts = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * k);
+    float *logits = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * E);
+    or_router_logits(T, E, H, x, Wr, bias, logits);
+    or_topk(T, E, k, logits, ids, wts);
+    free(logits);
+    if (ids_out)
+        memcpy(ids_out, ids, sizeof(int32_t) * (size_t)T * k);
+    if (w_out)
+        memcpy(w_out, wts, sizeof(float) * (size_t)T * k);
+
+    int32_t Imax = (Is > I) ? Is : I;
+    float *wg = (float *)malloc(sizeof(float) * (size_t)Imax * H);
+    float *wu = (float *)malloc(sizeof(float) * (size_t)Imax * H);
+    float *wd = (float *)malloc(sizeof(float) * (size_t)Imax * H);
+    double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+    double *hb = (double *)malloc(sizeof(double) * (size_t)Imax);
+    double *o = (double *)malloc(sizeof(double) * (size_t)H);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)H);
+
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            xd[h] = or_bf16_to_double(x[t * H + h]);
+            acc[h] = 0.0;
+        }
+        for (int32_t i = 0; i < k; ++i) {
+            int32_t e = ids[t * k + i];
+            int32_t s = slot_of[e];
+            int resident = (s >= 0 && s < n_slots);
+            if (miss)
+                miss[t * k + i] = resident ? -1 : e;
+            if (!resident)
+                continue;
+            dequant_expert(H, I, s, w13c, w13s, w2c, w2s, gsc, wg, wu, wd);
+            expert_forward(H, I, wg, wu, wd, act, gate_max, up_absmax, xd, hb, o);
+            double wi = (double)wts[t * k + i];
+            for (int32_t h = 0; h < H; ++h)
+                acc[h] += wi * o[h];
+        }
+        if (Is > 0) {
+            double z = 0.0;
+            for (int32_t h = 0; h < H; ++h)
+                z += or_bf16_to_double(sgate[h]) * xd[h];
+            double gamma = 1.0 / (1.0 + exp(-z));
+            dequant_expert(H, Is, 0, s13c, s13s, s2c, s2s, sgsc, wg, wu, wd);
+            expert_forward(H, Is, wg, wu, wd, act, gate_max, up_absmax, xd, hb, o);
+            for (int32_t h = 0; h < H; ++h)
+                acc[h] += gamma * o[h];
+        }
+        for (int32_t h = 0; h < H; ++h) {
+            if (y64)
+                y64[t * H + h] = acc[h];
+            if (y)
+                y[t * H + h] = or_bf16_from_double(acc[h]);
+        }
+    }
+    free(ids); free(wts); free(wg); free(wu); free(wd);
+    free(xd); free(hb); free(o); free(acc);
+    return 0;
+}

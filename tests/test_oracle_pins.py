@@ -453,3 +453,78 @@ def test_openmp_timing_copy_gives_identical_bits():
     for key in ("ids", "weights", "y64", "y"):
         assert np.array_equal(a[key], b[key]), key
     assert oracle.threads(False) == 1 and oracle.threads(True) >= 1
+
+
+# ------------------------------------------------- expert-slot indirection --
+
+def _bank_of(layer):
+    return dict(w13_codes=layer.w13_codes, w13_scales=layer.w13_scales,
+                w2_codes=layer.w2_codes, w2_scales=layer.w2_scales,
+                global_scale=layer.global_scale)
+
+
+def _slot_bank(layer, experts):
+    """A bank whose slot s holds expert experts[s]."""
+    b = _bank_of(layer)
+    return {key: np.ascontiguousarray(v[np.asarray(experts)]) for key, v in b.items()}
+
+
+def _slot_case(tokens=3):
+    w = synth.dataclasses.replace(synth.WORKLOADS["decode_e512_top10_shared"], num_experts=40,
+                                  hidden=256, inter=128, shared_inter=128, global_scale=2.0 ** -3)
+    return synth.make_layer(w), synth.make_tokens(w, tokens=tokens)
+
+
+def test_slots_identity_map_is_the_plain_layer():
+    layer, x = _slot_case()
+    E = layer.num_experts
+    got = oracle.moe_layer_slots(layer, x, np.arange(E, dtype=np.int32), _bank_of(layer))
+    want = oracle.moe_layer(layer, x)
+    for key in ("ids", "weights", "y64", "y"):
+        assert np.array_equal(got[key], want[key]), key
+    assert np.all(got["miss"] == -1)
+
+
+def test_slots_permuted_partial_bank_is_the_plain_layer():
+    # only the selected experts resident, in a shuffled order, in a bank smaller than E
+    layer, x = _slot_case()
+    E = layer.num_experts
+    sel = np.unique(oracle.moe_layer(layer, x)["ids"])
+    rng = np.random.default_rng(3)
+    order = rng.permutation(sel)
+    slot_of = np.full(E, -1, np.int32)
+    slot_of[order] = np.arange(len(order), dtype=np.int32)
+    got = oracle.moe_layer_slots(layer, x, slot_of, _slot_bank(layer, order))
+    want = oracle.moe_layer(layer, x)
+    assert len(order) < E
+    for key in ("ids", "weights", "y64", "y"):
+        assert np.array_equal(got[key], want[key]), key
+    assert np.all(got["miss"] == -1)
+
+
+def test_slots_missing_experts_contribute_nothing_and_are_reported():
+    # a missing expert equals a resident one whose codes are all zero (every weight
+    # +0, so its output is exactly 0): routing and every other term unchanged
+    layer, x = _slot_case(tokens=4)
+    E = layer.num_experts
+    ids = oracle.moe_layer(layer, x)["ids"]
+    missing = np.unique(ids[:, [1, 4]])            # some experts of places 1 and 4
+    slot_of = np.arange(E, dtype=np.int32)
+    slot_of[missing[0::2]] = -1
+    slot_of[missing[1::2]] = E + 7                 # outside [0, n_slots) as well
+    got = oracle.moe_layer_slots(layer, x, slot_of, _bank_of(layer))
+    zeroed = synth.dataclasses.replace(layer, w13_codes=layer.w13_codes.copy(),
+                                       w2_codes=layer.w2_codes.copy())
+    zeroed.w13_codes[missing] = 0
+    zeroed.w2_codes[missing] = 0
+    want = oracle.moe_layer(zeroed, x)
+    assert np.array_equal(got["ids"], want["ids"])
+    assert np.array_equal(got["weights"], want["weights"])
+    assert np.array_equal(got["y64"], want["y64"])
+    assert np.array_equal(got["y"], want["y"])
+    expect_miss = np.where(np.isin(ids, missing), ids, -1)
+    assert np.array_equal(got["miss"], expect_miss)
+    assert (got["miss"] >= 0).sum() >= 2
+    # and the output differs from the full layer (the dropped terms were not zero)
+    full = oracle.moe_layer(layer, x)
+    assert not np.array_equal(got["y64"], full["y64"])
