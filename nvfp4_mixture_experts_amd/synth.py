@@ -12,7 +12,9 @@ Distributions (per workload):
   * block scales: one e4m3 byte per 16 K-elements, uniform over the encodings
     of 2^-4 .. 2^2 (exponent field n + 7, mantissa 0);
   * per-tensor global scales (gate, up, down) all equal to ``global_scale``;
-  * shared-expert gate vector: bf16 draws of N(0, 0.02).
+  * shared-expert gate vector: bf16 draws of N(0, 0.02);
+  * block-fp8 workloads (codec "fp8"): e4m3 code bytes uniform over the 254 finite
+    encodings, one fp32 scale per 128 x 128 block drawn as 2^-11 * (1 + U[0, 1)).
 
 Canonical weight layout (what ``ft_nvfp4_repack`` takes):
   w13 codes [n, 2I, H/2] (gate rows 0..I-1, then up rows), w13 scales [n, 2I, H/16],
@@ -51,6 +53,7 @@ class Workload:
     up_absmax: float = 7.0
     router_std: float = 0.02
     shared_gate_std: float = 0.02
+    codec: str = "nvfp4"          # routed/shared expert weights: "nvfp4" or "fp8" (block-fp8)
 
     @property
     def act(self) -> int:
@@ -73,8 +76,81 @@ WORKLOADS = {
         # Prefill chunk of 8192 tokens through the 512-expert layer.
         Workload("prefill_t8192", 512, 2048, 512, 10, 8192, True, 2.0 ** -6, seed=1004,
                  shared_inter=512),
+        # The 512-expert decode layer with block-fp8 routed and shared experts.
+        Workload("decode_e512_top10_shared_fp8", 512, 2048, 512, 10, 1, True, 1.0, seed=1005,
+                 shared_inter=512, codec="fp8"),
     ]
 }
+
+# ---------------------------------------------------------------- block-fp8 --
+
+FP8_BLOCK = 128
+# every e4m3 byte but the two NaN encodings (S.1111.111)
+FP8_FINITE_BYTES = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+@dataclasses.dataclass
+class Fp8Layer:
+    """One layer with block-fp8 experts (canonical layout): codes are e4m3 bytes, one
+    fp32 scale per 128 x 128 block (bank [n][ceil(rows/128)][ceil(K/128)])."""
+    workload: Workload
+    w_router: np.ndarray
+    bias: Optional[np.ndarray]
+    w13_codes: np.ndarray    # u8 [E, 2I, H]
+    w13_scales: np.ndarray   # f32 [E, 2I/128, H/128]
+    w2_codes: np.ndarray     # u8 [E, H, I]
+    w2_scales: np.ndarray    # f32 [E, H/128, I/128]
+    s13_codes: Optional[np.ndarray] = None
+    s13_scales: Optional[np.ndarray] = None
+    s2_codes: Optional[np.ndarray] = None
+    s2_scales: Optional[np.ndarray] = None
+    shared_gate: Optional[np.ndarray] = None
+
+    num_experts = property(lambda s: s.workload.num_experts)
+    hidden = property(lambda s: s.workload.hidden)
+    inter = property(lambda s: s.workload.inter)
+    top_k = property(lambda s: s.workload.top_k)
+    act = property(lambda s: s.workload.act)
+    gate_max = property(lambda s: s.workload.gate_max)
+    up_absmax = property(lambda s: s.workload.up_absmax)
+    shared_inter = property(lambda s: s.workload.shared_inter)
+
+
+def _blocks(n: int) -> int:
+    return -(-n // FP8_BLOCK)
+
+
+def _fp8_codes(rng, shape):
+    return FP8_FINITE_BYTES[rng.integers(0, len(FP8_FINITE_BYTES), size=shape)]
+
+
+def _fp8_scales(rng, shape):
+    # 2^-11 * (1 + u), u ~ U[0, 1): pre-activations of a few units at H = 2048
+    return (np.float32(2.0 ** -11) * (1 + rng.random(shape, dtype=np.float32))).astype(np.float32)
+
+
+def _fp8_bank(seed: int, prefix: str, n: int, H: int, I: int):
+    return dict(
+        w13_codes=_fp8_codes(_rng(seed, prefix + "w13_codes"), (n, 2 * I, H)),
+        w13_scales=_fp8_scales(_rng(seed, prefix + "w13_scales"), (n, _blocks(2 * I), _blocks(H))),
+        w2_codes=_fp8_codes(_rng(seed, prefix + "w2_codes"), (n, H, I)),
+        w2_scales=_fp8_scales(_rng(seed, prefix + "w2_scales"), (n, _blocks(H), _blocks(I))),
+    )
+
+
+def make_fp8_layer(w: Workload, instance: int = 0) -> Fp8Layer:
+    """Host (numpy) block-fp8 weights of layer instance ``instance``."""
+    seed = w.seed + 7919 * instance
+    wr, bias = make_router(w, instance)
+    layer = Fp8Layer(workload=w, w_router=wr, bias=bias,
+                     **_fp8_bank(seed, "fp8_", w.num_experts, w.hidden, w.inter))
+    if w.shared_inter > 0:
+        sb = _fp8_bank(seed, "fp8_shared_", 1, w.hidden, w.shared_inter)
+        layer.s13_codes, layer.s13_scales = sb["w13_codes"], sb["w13_scales"]
+        layer.s2_codes, layer.s2_scales = sb["w2_codes"], sb["w2_scales"]
+        gs = _rng(seed, "shared_gate").standard_normal(w.hidden, dtype=np.float32)
+        layer.shared_gate = bf16_bits_from_f32(gs * np.float32(w.shared_gate_std))
+    return layer
 
 
 @dataclasses.dataclass

@@ -87,6 +87,13 @@ def _load(omp: bool = False):
     lib.or_moe_layer_slots.restype = _I32
     lib.or_moe_layer_slots.argtypes = ([_I32, _I32, _I32, _I32, _I32, _F32, _F32, _I64, _P, _P, _P,
                                         _I32, _P] + [_P] * 5 + [_I32] + [_P] * 6 + [_P] * 5)
+    lib.or_fp8_dequant_value.restype = _F32
+    lib.or_fp8_dequant_value.argtypes = [ctypes.c_uint32, _F32]
+    lib.or_fp8_dequant_matrix.restype = None
+    lib.or_fp8_dequant_matrix.argtypes = [_P, _P, _I64, _I64, _P]
+    lib.or_moe_layer_fp8.restype = _I32
+    lib.or_moe_layer_fp8.argtypes = ([_I32, _I32, _I32, _I32, _I32, _F32, _F32, _I64, _P, _P, _P]
+                                     + [_P] * 4 + [_I32] + [_P] * 5 + [_P] * 4)
     _libs[omp] = lib
     return lib
 
@@ -267,3 +274,53 @@ def moe_layer_slots(layer, x: np.ndarray, slot_of: np.ndarray, slot_bank: dict,
     if rc != 0:
         raise ValueError("oracle rejected the layer shape")
     return {"ids": ids, "weights": w, "miss": miss, "y64": y64, "y": y}
+
+
+# --------------------------------------------------------- block-fp8 codec --
+
+FP8_BLOCK = 128
+
+
+def fp8_dequant_value(byte: int, scale: float) -> np.float32:
+    return np.float32(_load().or_fp8_dequant_value(int(byte), float(scale)))
+
+
+def fp8_dequant_matrix(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """codes u8 [rows, K], scales f32 [ceil(rows/128), ceil(K/128)] -> fp32 [rows, K]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    rows, K = codes.shape
+    assert scales.shape == (-(-rows // FP8_BLOCK), -(-K // FP8_BLOCK))
+    out = np.empty((rows, K), np.float32)
+    _load().or_fp8_dequant_matrix(_ptr(codes), _ptr(scales), rows, K, _ptr(out))
+    return out
+
+
+def moe_layer_fp8(layer, x: np.ndarray, openmp: bool = False) -> dict:
+    """The layer with block-fp8 experts: ``layer`` is a ``synth.Fp8Layer`` (routed bank
+    w13_codes u8 [E, 2I, H], w13_scales f32 [E, 2I/128, H/128], w2_codes u8 [E, H, I],
+    w2_scales f32 [E, H/128, I/128], and the shared expert likewise with n = 1).
+    Returns ``{"ids", "weights", "y64", "y"}``."""
+    x = _c(x, np.uint16)
+    T = x.shape[0]
+    k = layer.top_k
+    bank = [_c(layer.w13_codes, np.uint8), _c(layer.w13_scales, np.float32),
+            _c(layer.w2_codes, np.uint8), _c(layer.w2_scales, np.float32)]
+    Is = layer.shared_inter
+    sh = [None] * 5
+    if Is > 0:
+        sh = [_c(layer.s13_codes, np.uint8), _c(layer.s13_scales, np.float32),
+              _c(layer.s2_codes, np.uint8), _c(layer.s2_scales, np.float32),
+              _c(layer.shared_gate, np.uint16)]
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    y64 = np.empty((T, layer.hidden), np.float64)
+    y = np.empty((T, layer.hidden), np.uint16)
+    rc = _load(openmp).or_moe_layer_fp8(
+        layer.num_experts, layer.hidden, layer.inter, k, layer.act, layer.gate_max,
+        layer.up_absmax, T, _ptr(x), _ptr(_c(layer.w_router, np.float32)),
+        _ptr(_c(layer.bias, np.float32)), *[_ptr(a) for a in bank], Is, *[_ptr(a) for a in sh],
+        _ptr(ids), _ptr(w), _ptr(y64), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle rejected the layer shape")
+    return {"ids": ids, "weights": w, "y64": y64, "y": y}

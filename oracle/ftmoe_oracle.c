@@ -486,3 +486,120 @@ int32_t or_moe_layer_slots(int32_t E, int32_t H, int32_t I, int32_t k, int32_t a
     free(xd); free(hb); free(o); free(acc);
     return 0;
 }
+
+/* ----------------------------------------------------------- block-fp8 codec -- */
+
+/* The second routed-expert codec of the 512-expert layer (FreeToken commit log,
+ * page 2: the entry with 512 NVFP4 / block-fp8 routed experts, and its fp8 scale-bank
+ * padding rule).  The pages do not give the block shape; reading taken here: each
+ * weight is one OCP e4m3 byte, and each 128 x 128 block of a [rows, K] matrix
+ * (rows r..r+127, columns c..c+127) shares one fp32 scale; a matrix dimension that is
+ * not a multiple of 128 ends in a partial block that still has its own scale, so the
+ * scale bank is [ceil(rows/128)][ceil(K/128)].  There is no separate global scale.
+ * The dequantised weight is fp32(e4m3 * scale): one rounding of the exact product
+ * (4 significant bits times 24 fit in binary64). */
+#define OR_FP8_BLOCK 128
+
+float or_fp8_dequant_value(uint32_t byte, float scale)
+{
+    return (float)(or_e4m3(byte) * (double)scale);
+}
+
+/* codes u8 [rows, K], scales f32 [ceil(rows/128), ceil(K/128)] -> fp32 out [rows, K]. */
+void or_fp8_dequant_matrix(const uint8_t *codes, const float *scales, int64_t rows, int64_t K,
+                           float *out)
+{
+    int64_t kb = (K + OR_FP8_BLOCK - 1) / OR_FP8_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < K; ++c)
+            out[r * K + c] = or_fp8_dequant_value(codes[r * K + c],
+                                                  scales[(r / OR_FP8_BLOCK) * kb + c / OR_FP8_BLOCK]);
+}
+
+/* Expert e of a canonical block-fp8 bank: w13 codes [n][2I][H] (gate rows 0..I-1,
+ * then up), w13 scales [n][ceil(2I/128)][ceil(H/128)], w2 codes [n][H][I], w2 scales
+ * [n][ceil(H/128)][ceil(I/128)].  With I % 128 == 0 no scale block straddles gate and
+ * up. */
+static void dequant_expert_fp8(int32_t H, int32_t I, int64_t e, const uint8_t *w13c,
+                               const float *w13s, const uint8_t *w2c, const float *w2s,
+                               float *wg, float *wu, float *wd)
+{
+    int64_t rb13 = (2 * (int64_t)I + OR_FP8_BLOCK - 1) / OR_FP8_BLOCK;
+    int64_t kb13 = ((int64_t)H + OR_FP8_BLOCK - 1) / OR_FP8_BLOCK;
+    int64_t rb2 = ((int64_t)H + OR_FP8_BLOCK - 1) / OR_FP8_BLOCK;
+    int64_t kb2 = ((int64_t)I + OR_FP8_BLOCK - 1) / OR_FP8_BLOCK;
+    const uint8_t *c13 = w13c + e * 2 * (int64_t)I * H;
+    const float *s13 = w13s + e * rb13 * kb13;
+    or_fp8_dequant_matrix(c13, s13, I, H, wg);
+    or_fp8_dequant_matrix(c13 + (int64_t)I * H, s13 + ((int64_t)I / OR_FP8_BLOCK) * kb13, I, H,
+                          wu);
+    or_fp8_dequant_matrix(w2c + e * (int64_t)H * I, w2s + e * rb2 * kb2, H, I, wd);
+}
+
+/* The whole layer with block-fp8 routed experts and (when Is > 0) a block-fp8 shared
+ * expert; everything else as or_moe_layer (routes computed here).  Needs
+ * I % 128 == 0 and Is % 128 == 0. */
+int32_t or_moe_layer_fp8(int32_t E, int32_t H, int32_t I, int32_t k, int32_t act,
+                         float gate_max, float up_absmax, int64_t T, const uint16_t *x,
+                         const float *Wr, const float *bias, const uint8_t *w13c,
+                         const float *w13s, const uint8_t *w2c, const float *w2s, int32_t Is,
+                         const uint8_t *s13c, const float *s13s, const uint8_t *s2c,
+                         const float *s2s, const uint16_t *sgate, int32_t *ids_out,
+                         float *w_out, double *y64, uint16_t *y)
+{
+    if (E <= 0 || H <= 0 || I <= 0 || k <= 0 || k > E || T < 0 || I % OR_FP8_BLOCK ||
+        (Is > 0 && Is % OR_FP8_BLOCK))
+        return -1;
+    int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1) * k);
+    float *wts = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * k);
+    float *logits = (float *)malloc(sizeof(float) * (size_t)(T > 0 ? T : 1) * E);
+    or_router_logits(T, E, H, x, Wr, bias, logits);
+    or_topk(T, E, k, logits, ids, wts);
+    free(logits);
+    if (ids_out)
+        memcpy(ids_out, ids, sizeof(int32_t) * (size_t)T * k);
+    if (w_out)
+        memcpy(w_out, wts, sizeof(float) * (size_t)T * k);
+
+    int32_t Imax = (Is > I) ? Is : I;
+    float *wg = (float *)malloc(sizeof(float) * (size_t)Imax * H);
+    float *wu = (float *)malloc(sizeof(float) * (size_t)Imax * H);
+    float *wd = (float *)malloc(sizeof(float) * (size_t)Imax * H);
+    double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+    double *hb = (double *)malloc(sizeof(double) * (size_t)Imax);
+    double *o = (double *)malloc(sizeof(double) * (size_t)H);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)H);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            xd[h] = or_bf16_to_double(x[t * H + h]);
+            acc[h] = 0.0;
+        }
+        for (int32_t i = 0; i < k; ++i) {
+            dequant_expert_fp8(H, I, ids[t * k + i], w13c, w13s, w2c, w2s, wg, wu, wd);
+            expert_forward(H, I, wg, wu, wd, act, gate_max, up_absmax, xd, hb, o);
+            double wi = (double)wts[t * k + i];
+            for (int32_t h = 0; h < H; ++h)
+                acc[h] += wi * o[h];
+        }
+        if (Is > 0) {
+            double z = 0.0;
+            for (int32_t h = 0; h < H; ++h)
+                z += or_bf16_to_double(sgate[h]) * xd[h];
+            double gamma = 1.0 / (1.0 + exp(-z));
+            dequant_expert_fp8(H, Is, 0, s13c, s13s, s2c, s2s, wg, wu, wd);
+            expert_forward(H, Is, wg, wu, wd, act, gate_max, up_absmax, xd, hb, o);
+            for (int32_t h = 0; h < H; ++h)
+                acc[h] += gamma * o[h];
+        }
+        for (int32_t h = 0; h < H; ++h) {
+            if (y64)
+                y64[t * H + h] = acc[h];
+            if (y)
+                y[t * H + h] = or_bf16_from_double(acc[h]);
+        }
+    }
+    free(ids); free(wts); free(wg); free(wu); free(wd);
+    free(xd); free(hb); free(o); free(acc);
+    return 0;
+}

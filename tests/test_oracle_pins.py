@@ -528,3 +528,82 @@ def test_slots_missing_experts_contribute_nothing_and_are_reported():
     # and the output differs from the full layer (the dropped terms were not zero)
     full = oracle.moe_layer(layer, x)
     assert not np.array_equal(got["y64"], full["y64"])
+
+
+# ------------------------------------------------------------- block-fp8 --
+
+def test_fp8_dequant_is_one_rounding_matching_torch():
+    # torch's float8_e4m3fn decode (library routine) times the fp32 scale in fp32
+    # (one rounding), for every finite byte and scales that make the product round
+    rng = np.random.default_rng(8)
+    scales = np.concatenate([np.float32([1.0, 2.0 ** -9, 448.0]),
+                             (rng.random(40) * 3e-3 + 1e-4).astype(np.float32)])
+    bytes_ = synth.FP8_FINITE_BYTES
+    dec = torch.from_numpy(bytes_.copy()).view(torch.float8_e4m3fn).to(torch.float32)
+    rounded = 0
+    for sc in scales:
+        want = (dec * torch.tensor(sc, dtype=torch.float32)).numpy()
+        got = np.array([oracle.fp8_dequant_value(int(b), float(sc)) for b in bytes_], np.float32)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), sc
+        exact = E4M3[bytes_] * np.float64(sc)
+        rounded += int(np.sum(exact != got.astype(np.float64)))
+    assert rounded > 1000          # the products do round: the single rounding is exercised
+
+
+def test_fp8_dequant_matrix_block_index_and_partial_blocks():
+    rng = np.random.default_rng(9)
+    rows, K = 300, 200                     # partial blocks in both directions
+    codes = synth.FP8_FINITE_BYTES[rng.integers(0, 254, (rows, K))]
+    scales = (rng.random((3, 2)) + 0.5).astype(np.float32)
+    got = oracle.fp8_dequant_matrix(codes, scales)
+    full = np.repeat(np.repeat(scales, 128, axis=0), 128, axis=1)[:rows, :K]
+    want = (E4M3[codes].astype(np.float32) * full).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # a transposed scale index would read scales[c // 128, r // 128]: it differs here
+    assert not np.array_equal(scales[:2, :2], scales[:2, :2].T)
+
+
+def _dense_fp8_mlp(layer, xf, w13c, w13s, w2c, w2s, I):
+    def dq(c, s):
+        full = np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)[:c.shape[0], :c.shape[1]]
+        return (E4M3[c].astype(np.float32) * full).astype(np.float64)
+    wg = dq(w13c[:I], w13s[: I // 128])
+    wu = dq(w13c[I:], w13s[I // 128:])
+    wd = dq(w2c, w2s)
+    gate = np.minimum(xf @ wg.T, layer.gate_max)
+    up = np.clip(xf @ wu.T, -layer.up_absmax, layer.up_absmax)
+    return (scipy.special.expit(gate) * gate * up) @ wd.T
+
+
+def test_fp8_layer_all_experts_selected_equals_dense_layer():
+    w = synth.dataclasses.replace(synth.WORKLOADS["decode_e512_top10_shared_fp8"], num_experts=4,
+                                  top_k=4, hidden=256, inter=128, shared_inter=128,
+                                  shared_gate_std=0.5)
+    layer = synth.make_fp8_layer(w)
+    x = synth.make_tokens(w, tokens=2)
+    got = oracle.moe_layer_fp8(layer, x)
+    xf = _bf16_to_f64(x)
+    logits = (xf @ layer.w_router.astype(np.float64).T).astype(np.float32)
+    probs = scipy.special.softmax(logits.astype(np.float64), axis=1).astype(np.float32)
+    want = np.zeros((2, w.hidden))
+    for e in range(w.num_experts):
+        want += probs[:, e:e + 1].astype(np.float64) * _dense_fp8_mlp(
+            layer, xf, layer.w13_codes[e], layer.w13_scales[e], layer.w2_codes[e],
+            layer.w2_scales[e], w.inter)
+    gamma = scipy.special.expit(xf @ _bf16_to_f64(layer.shared_gate))
+    want += gamma[:, None] * _dense_fp8_mlp(layer, xf, layer.s13_codes[0], layer.s13_scales[0],
+                                            layer.s2_codes[0], layer.s2_scales[0],
+                                            w.shared_inter)
+    assert np.abs(got["y64"] - want).max() <= 1e-12 * np.abs(want).max()
+
+
+def test_fp8_workload_clamps_engage():
+    # the synthetic fp8 draws put pre-activations in the range where the clamps act
+    w = synth.WORKLOADS["decode_e512_top10_shared_fp8"]
+    layer = synth.make_fp8_layer(synth.dataclasses.replace(w, num_experts=12))
+    x = synth.make_tokens(w, tokens=1)
+    xf = _bf16_to_f64(x)
+    c = layer.w13_codes[0]
+    full = np.repeat(np.repeat(layer.w13_scales[0], 128, 0), 128, 1)
+    pre = xf @ (E4M3[c] * full).T
+    assert 0.3 < np.std(pre) < 30 and np.mean(np.abs(pre) > 7) > 0.001
