@@ -222,14 +222,14 @@ def stream_read_probe(dev) -> dict:
     n = 1 << 30
     t = torch.ones(n, dtype=torch.float32, device=dev)
     out = torch.empty((), dtype=torch.float32, device=dev)
-    torch.sum(t, out=out)
+    torch.sum(t, dim=0, out=out)
     torch.cuda.synchronize()
     best = float("inf")
     for _ in range(5):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        torch.sum(t, out=out)
+        torch.sum(t, dim=0, out=out)
         b.record()
         torch.cuda.synchronize()
         best = min(best, a.elapsed_time(b))

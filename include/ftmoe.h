@@ -168,6 +168,29 @@ ft_status ft_moe_nvfp4_decode(const ft_moe_desc *desc, int64_t tokens, const uin
                               float *topk_w_out, uint16_t *y, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* ft_moe_nvfp4_decode with the routed experts held in a bank of expert SLOTS
+ * (FreeToken fork PR #84, page 1, the interleaved A/B table: the deployment keeps
+ * a fixed number of expert slots and counts expert-cache misses per token;
+ * FreeToken commit log, page 2: the expert banks plan their residency).
+ *   slots     repacked bank of n_slots experts (any n_slots >= 1 for 1..7 tokens;
+ *             n_slots <= num_experts for 8..64 tokens, else FT_EUNSUPPORTED)
+ *   slot_of   i32 [E] device: the slot holding expert e, or any value outside
+ *             [0, n_slots) when expert e is not resident
+ *   miss_out  i32 [T][k] device, optional: for each selected place, the expert id
+ *             when that expert is not resident, else -1
+ * Routing is computed as by ft_moe_nvfp4_decode (topk_ids_out holds expert ids).
+ * A selected expert that is not resident contributes nothing to y (the routing
+ * weights of the others are not renormalised): the caller sees it in miss_out and
+ * may page the expert in and call again.  Other arguments as ft_moe_nvfp4_decode
+ * (the workspace is sized by ft_moe_workspace_bytes for path 1). */
+ft_status ft_moe_nvfp4_decode_slots(const ft_moe_desc *desc, int64_t tokens, const uint16_t *x,
+                                    const float *w_router, const float *bias,
+                                    const ft_nvfp4_experts *slots, int32_t n_slots,
+                                    const int32_t *slot_of, const ft_nvfp4_experts *shared,
+                                    const uint16_t *shared_gate, int32_t *topk_ids_out,
+                                    float *topk_w_out, int32_t *miss_out, uint16_t *y,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* The expert part of the layer for prefill chunks (FreeToken fork PR #84,
  * page 1, the bullet on #578), given routes (for example from ft_moe_route):
  * pairs grouped by expert, gate|up and down as grouped bf16 MFMA GEMMs (exact

@@ -344,12 +344,17 @@ ft_status ft_moe_route(const ft_moe_desc* desc, int64_t tokens, const uint16_t* 
   return ok();
 }
 
-ft_status ft_moe_nvfp4_decode(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,
-                              const float* w_router, const float* bias,
-                              const ft_nvfp4_experts* routed, const ft_nvfp4_experts* shared,
-                              const uint16_t* shared_gate, int32_t* topk_ids_out,
-                              float* topk_w_out, uint16_t* y, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode call; with slot_of set, `routed` is a bank of n_slots expert slots.
+ft_status decode_impl(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,
+                      const float* w_router, const float* bias, const ft_nvfp4_experts* routed,
+                      const int32_t* slot_of, int32_t n_slots, int32_t* miss_out,
+                      const ft_nvfp4_experts* shared, const uint16_t* shared_gate,
+                      int32_t* topk_ids_out, float* topk_w_out, uint16_t* y, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   ft_status st = check_desc(desc);
   if (st != FT_OK) return st;
   if (tokens < 1 || tokens > kMaxDecodeTokens)
@@ -374,7 +379,14 @@ ft_status ft_moe_nvfp4_decode(const ft_moe_desc* desc, int64_t tokens, const uin
                    topk_w_out, at<uint32_t>(workspace, L.sync) + kRouteCounterWord,
                    at<double>(workspace, L.rsplit), s);
     if (st != FT_OK) return st;
-    st = run_grouped(desc, T, x, ids, wts, routed, shared, y, workspace, L, s);
+    ft_moe_desc gd = *desc;
+    if (slot_of) {
+      // routes -> slot ids (a missing expert: slot 0, weight 0); group by slot
+      hipError_t e = launch_map_slots(ids, wts, T * desc->top_k, slot_of, n_slots, miss_out, s);
+      if (e != hipSuccess) return hip_fail(e, "slot map kernel");
+      gd.num_experts = n_slots;
+    }
+    st = run_grouped(&gd, T, x, ids, wts, routed, shared, y, workspace, L, s);
     if (st != FT_OK) return st;
     return ok();
   }
@@ -407,9 +419,48 @@ ft_status ft_moe_nvfp4_decode(const ft_moe_desc* desc, int64_t tokens, const uin
   const int upg = desc->top_k * (desc->inter / 32) + desc->shared_inter / 32;
   p.blocks_per_group = p.d_groups >= grid ? 1 : std::min(grid / p.d_groups, upg);
   p.spin_limit = wait_limit();
+  p.slot_of = slot_of;
+  p.n_slots = n_slots;
+  p.miss_out = miss_out;
   hipError_t e = launch_decode_fused(p, grid, s);
   if (e != hipSuccess) return hip_fail(e, "fused decode kernel");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ft_status ft_moe_nvfp4_decode(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,
+                              const float* w_router, const float* bias,
+                              const ft_nvfp4_experts* routed, const ft_nvfp4_experts* shared,
+                              const uint16_t* shared_gate, int32_t* topk_ids_out,
+                              float* topk_w_out, uint16_t* y, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return decode_impl(desc, tokens, x, w_router, bias, routed, nullptr, 0, nullptr, shared,
+                     shared_gate, topk_ids_out, topk_w_out, y, workspace, workspace_bytes, stream);
+}
+
+ft_status ft_moe_nvfp4_decode_slots(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,
+                                    const float* w_router, const float* bias,
+                                    const ft_nvfp4_experts* slots, int32_t n_slots,
+                                    const int32_t* slot_of, const ft_nvfp4_experts* shared,
+                                    const uint16_t* shared_gate, int32_t* topk_ids_out,
+                                    float* topk_w_out, int32_t* miss_out, uint16_t* y,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  ft_status st = check_desc(desc);
+  if (st != FT_OK) return st;
+  if (!slot_of) return fail(FT_EINVAL, "slot_of is NULL");
+  if (reinterpret_cast<uintptr_t>(slot_of) & 3u) return fail(FT_EINVAL, "slot_of must be 4-byte aligned");
+  if (miss_out && (reinterpret_cast<uintptr_t>(miss_out) & 3u))
+    return fail(FT_EINVAL, "miss_out must be 4-byte aligned");
+  if (n_slots < 1) return fail(FT_EINVAL, "n_slots must be >= 1");
+  if (tokens >= kGroupedDecodeMinTokens && n_slots > desc->num_experts)
+    return fail(FT_EUNSUPPORTED,
+                "decode_slots with %d or more tokens needs n_slots <= num_experts (%d > %d)",
+                kGroupedDecodeMinTokens, n_slots, desc->num_experts);
+  return decode_impl(desc, tokens, x, w_router, bias, slots, slot_of, n_slots, miss_out, shared,
+                     shared_gate, topk_ids_out, topk_w_out, y, workspace, workspace_bytes, stream);
 }
 
 ft_status ft_moe_nvfp4_prefill(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,

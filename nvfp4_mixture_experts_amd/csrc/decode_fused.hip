@@ -262,7 +262,18 @@ __device__ __forceinline__ Unit2 unit2(int v, int k, FastDiv nch) {
 // loads inside the gate|up compute loop: vmcnt counts stores too and completes in
 // order, so a load there would make the next unit's wait cover the device-coherent
 // h stores issued before it, and every unit would wait for their acknowledgement.
-template <int LPR, int CPL, bool ONE>
+//
+// SLOTS: the routed experts live in a bank of expert slots (p.slot_of maps expert
+// -> slot; a slot outside [0, p.n_slots) means the expert is not resident).  The
+// map is read into LDS together with the router loads, so looking a selected
+// expert up costs no memory round trip.  A non-resident expert's units read slot
+// 0's weights (every access stays unconditional and in range), produce h = 0 and
+// enter the down GEMV with weight 0; its id goes to p.miss_out.
+//
+// FP8: the experts use the block-fp8 codec (e4m3 bytes, one fp32 scale per 128 x 128
+// block, no global scale): a 32-element chunk is 32 code bytes (two 16-byte loads per
+// lane), gate|up rows stay row-major, down records are 32 bytes (K-chunk-major).
+template <int LPR, int CPL, bool ONE, bool SLOTS, bool FP8>
 __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(FusedParams p) {
   constexpr int GPW = kWave / LPR;   // lane groups per wave
   constexpr int NC = LPR * CPL / 8;  // float4 pieces of a router row per lane (H / 256)
@@ -285,6 +296,25 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   __shared__ __align__(16) float s_hb[kFWaves][32 * kUD];  // h values of a down batch
   __shared__ uint32_t s_gen[kFWaves];
   __shared__ uint32_t s_rdone;  // this call's generation once wave 0's router rows are out
+  __shared__ int s_map[SLOTS ? kMaxExperts : 1];  // expert -> slot (SLOTS)
+
+  // SLOTS: the expert -> slot map, two entries per thread (E <= 1024), loaded now
+  // and stored to LDS before the selection's barriers
+  int map0 = 0, map1 = 0;
+  if constexpr (SLOTS) {
+    const int i0 = static_cast<int>(threadIdx.x), i1 = i0 + kFWaves * kWave;
+    map0 = p.slot_of[i0 < E ? i0 : E - 1];
+    map1 = p.slot_of[i1 < E ? i1 : E - 1];
+  }
+  // slot of expert e, or -1 when it is not resident
+  auto slot_of = [&](int e) -> int {
+    if constexpr (!SLOTS) {
+      return e;
+    } else {
+      const int sl = s_map[e];
+      return (sl >= 0 && sl < p.n_slots) ? sl : -1;
+    }
+  };
 
   // Generation of this call: this block's own call count.  Every wave reads the
   // counter itself and nothing waits for it here, so the read travels together
@@ -347,6 +377,11 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
 
   // ---------------------------------------------------------------- S --
   if (lane == 0) s_gen[wave] = gen;  // needs the counter read to have returned
+  if constexpr (SLOTS) {
+    const int i0 = static_cast<int>(threadIdx.x), i1 = i0 + kFWaves * kWave;
+    if (i0 < E) s_map[i0] = map0;
+    if (i1 < E) s_map[i1] = map1;
+  }
   {
     const uint64_t* lgc = p.logits + static_cast<size_t>(blockIdx.x % kLogitCopies) * T * E1;
     const bool has_shared = p.shared_gate != nullptr;
@@ -456,11 +491,13 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   struct DownUnit {
     const uint8_t* cp;
     const uint8_t* sp;
+    const float* spf;      // FP8: the unit's block scale
     const uint64_t* hrow;  // 32 tagged h values of this unit
     int slot;              // the unit's slot (k: the shared expert)
     float gdown;           // down global scale of the unit's expert (multiplied at use:
                            // using a load result at issue time would wait for every
                            // load issued before it)
+    bool present;          // the unit's expert is resident (always, without SLOTS)
     bool valid;
   };
   auto down_unit = [&](int t, int v, int c) {
@@ -469,19 +506,32 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     const int vv = d.valid ? v : upg - 1;  // clamped: addresses stay in range
     const Unit2 u = unit2(vv, k, fd_nch);
     const bool sh = (u.slot == k);
-    const int e = __builtin_amdgcn_readfirstlane(sh ? 0 : s_ids[t * k + u.slot]);
+    const int sl = sh ? 0 : slot_of(s_ids[t * k + u.slot]);
+    const int e = __builtin_amdgcn_readfirstlane(SLOTS && sl < 0 ? 0 : sl);
     const int nu = sh ? nch_s : nch;
     const size_t rec = (static_cast<size_t>(e) * nu + u.chunk) * H + c;
-    d.cp = (sh ? p.shared.w2 : p.routed.w2) + rec * 16;
-    d.sp = (sh ? p.shared.w2s : p.routed.w2s) + rec * 2;
     d.hrow = p.h + (static_cast<size_t>(t) * p.nslots + u.slot) * p.Imax + 32 * u.chunk;
     d.slot = u.slot;
-    d.gdown = ld_vmem_f32(sh ? p.shared.gsc : p.routed.gsc, 3 * e + 2);
+    if constexpr (FP8) {
+      const int kb = nu / 4;  // 128-element scale blocks along K
+      d.cp = (sh ? p.shared.w2 : p.routed.w2) + rec * 32;
+      d.sp = nullptr;
+      d.spf = reinterpret_cast<const float*>(sh ? p.shared.w2s : p.routed.w2s) +
+              (static_cast<size_t>(e) * (H / 128) + c / 128) * kb + u.chunk / 4;
+      d.gdown = 1.0f;
+    } else {
+      d.cp = (sh ? p.shared.w2 : p.routed.w2) + rec * 16;
+      d.sp = (sh ? p.shared.w2s : p.routed.w2s) + rec * 2;
+      d.spf = nullptr;
+      d.gdown = ld_vmem_f32(sh ? p.shared.gsc : p.routed.gsc, 3 * e + 2);
+    }
+    d.present = sl >= 0;  // multiplied in at use (a missing expert's term is 0)
     return d;
   };
 
-  uint4 pq[kUD];
+  uint4 pq[kUD], pq2[FP8 ? kUD : 1];
   uint32_t ps[kUD];
+  float psf[FP8 ? kUD : 1];
   DownUnit pdu[kUD];
   const bool have_first = g_first < p.d_groups;
   // issues the loads of this wave's first down units (kept in registers until D).
@@ -495,7 +545,13 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     for (int i = 0; i < kUD; ++i) {
       pdu[i] = down_unit(t, sub + bpg * (wave + kFWaves * i), c);
       pq[i] = *reinterpret_cast<const uint4*>(pdu[i].cp);
-      ps[i] = *reinterpret_cast<const uint16_t*>(pdu[i].sp);
+      if constexpr (FP8) {
+        pq2[i] = *reinterpret_cast<const uint4*>(pdu[i].cp + 16);
+        psf[i] = *pdu[i].spf;
+        ps[i] = 0;
+      } else {
+        ps[i] = *reinterpret_cast<const uint16_t*>(pdu[i].sp);
+      }
     }
   };
 
@@ -529,16 +585,49 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     bool prefetched = false;
     for (int j0 = 0; (gw * GPW) + NG * j0 < total; j0 += kUW) {
       Unit13 un[kUW];
+      bool present[kUW];
       float g_gate[kUW], g_up[kUW];
       uint4 qg[kUW][CPL], qu[kUW][CPL];
       uint32_t sg[kUW][CPL], su[kUW][CPL];
+      uint4 qg2[FP8 ? kUW : 1][CPL], qu2[FP8 ? kUW : 1][CPL];  // FP8: second 16 bytes
+      float fsg[FP8 ? kUW : 1][CPL], fsu[FP8 ? kUW : 1][CPL];    // FP8: block scales
 #pragma unroll
       for (int jj = 0; jj < kUW; ++jj) {
         un[jj] = unit13(gw * GPW + group + NG * (j0 + jj), total, k, kI, fd_ppt, fd_inter);
         const bool sh = (un[jj].slot == k);
         const int I = sh ? p.shared.inter : p.routed.inter;
-        int e = sh ? 0 : s_ids[un[jj].t * k + un[jj].slot];
+        int e = sh ? 0 : slot_of(s_ids[un[jj].t * k + un[jj].slot]);
+        present[jj] = true;
+        if constexpr (SLOTS) {
+          present[jj] = e >= 0;
+          e = e < 0 ? 0 : e;
+        }
         if (LPR == kWave) e = __builtin_amdgcn_readfirstlane(e);  // one unit per wave
+        const size_t rr = static_cast<size_t>(un[jj].r);
+        if constexpr (FP8) {
+          const uint8_t* __restrict__ codes =
+              (sh ? p.shared.w13 : p.routed.w13) + static_cast<size_t>(e) * 2 * I * H;
+          const int kb = H / 128;
+          const float* __restrict__ sc = reinterpret_cast<const float*>(
+                                             sh ? p.shared.w13s : p.routed.w13s) +
+                                         static_cast<size_t>(e) * (2 * I / 128) * kb;
+          g_gate[jj] = 1.0f;
+          g_up[jj] = 1.0f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const int j = col + LPR * c;
+            const uint8_t* gr = codes + rr * H + 32 * j;
+            const uint8_t* ur = codes + (I + rr) * H + 32 * j;
+            qg[jj][c] = *reinterpret_cast<const uint4*>(gr);
+            qg2[jj][c] = *reinterpret_cast<const uint4*>(gr + 16);
+            qu[jj][c] = *reinterpret_cast<const uint4*>(ur);
+            qu2[jj][c] = *reinterpret_cast<const uint4*>(ur + 16);
+            fsg[jj][c] = sc[(rr / 128) * kb + j / 4];
+            fsu[jj][c] = sc[((I + rr) / 128) * kb + j / 4];
+            sg[jj][c] = su[jj][c] = 0;
+          }
+          continue;
+        }
         const uint8_t* __restrict__ codes =
             (sh ? p.shared.w13 : p.routed.w13) + static_cast<size_t>(e) * 2 * I * row_bytes;
         const uint8_t* __restrict__ scales =
@@ -546,7 +635,6 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         const float* gsc = sh ? p.shared.gsc : p.routed.gsc;
         g_gate[jj] = ld_vmem_f32(gsc, 3 * e + 0);
         g_up[jj] = ld_vmem_f32(gsc, 3 * e + 1);
-        const size_t rr = static_cast<size_t>(un[jj].r);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           const int j = col + LPR * c;
@@ -575,6 +663,11 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         float ag = 0.0f, au = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
+          if constexpr (FP8) {
+            ag += chunk_dot_fp8_bf16(qg[jj][c], qg2[jj][c], xr[c]) * fsg[jj][c];
+            au += chunk_dot_fp8_bf16(qu[jj][c], qu2[jj][c], xr[c]) * fsu[jj][c];
+            continue;
+          }
           if constexpr (LPR == kWave && CPL == 1) {
             const uint32_t d = sg[jj][c];
             const uint32_t gd = static_cast<uint32_t>(
@@ -590,6 +683,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         ag = group_sum_last<LPR>(ag);
         au = group_sum_last<LPR>(au);
         hv[jj] = swiglu(p.act, ag * g_gate[jj], au * g_up[jj], p.gate_max, p.up_absmax);
+        if constexpr (SLOTS) hv[jj] = present[jj] ? hv[jj] : 0.0f;
       }
       // the batch's h values, published after all of its units are computed: the
       // stores are conditional, and one issued between a unit's loads and their use
@@ -619,14 +713,19 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     const int c = rg * kWave + lane;
     float acc = 0.0f;
     for (int i0 = 0; sub + bpg * (wave + kFWaves * i0) < upg; i0 += kUD) {
-      uint4 q[kUD];
+      uint4 q[kUD], q2[FP8 ? kUD : 1];
       uint32_t sc[kUD];
+      float scf[FP8 ? kUD : 1];
       DownUnit du[kUD];
       if (first && i0 == 0) {
 #pragma unroll
         for (int ii = 0; ii < kUD; ++ii) {
           q[ii] = pq[ii];
           sc[ii] = ps[ii];
+          if constexpr (FP8) {
+            q2[ii] = pq2[ii];
+            scf[ii] = psf[ii];
+          }
           du[ii] = pdu[ii];
         }
       } else {
@@ -634,7 +733,13 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         for (int ii = 0; ii < kUD; ++ii) {
           du[ii] = down_unit(t, sub + bpg * (wave + kFWaves * (i0 + ii)), c);
           q[ii] = *reinterpret_cast<const uint4*>(du[ii].cp);
-          sc[ii] = *reinterpret_cast<const uint16_t*>(du[ii].sp);
+          if constexpr (FP8) {
+            q2[ii] = *reinterpret_cast<const uint4*>(du[ii].cp + 16);
+            scf[ii] = *du[ii].spf;
+            sc[ii] = 0;
+          } else {
+            sc[ii] = *reinterpret_cast<const uint16_t*>(du[ii].sp);
+          }
         }
       }
       {
@@ -661,8 +766,14 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
             hv[4 * m + 2] = v.z;
             hv[4 * m + 3] = v.w;
           }
-          acc = fmaf(chunk_dot_f32(q[ii], sc[ii], hv), slot_weight(t, du[ii].slot) * du[ii].gdown,
-                     acc);
+          const float wgt = slot_weight(t, du[ii].slot) * du[ii].gdown;
+          float dot;
+          if constexpr (FP8) {
+            dot = chunk_dot_fp8_f32(q[ii], q2[ii], hv) * scf[ii];
+          } else {
+            dot = chunk_dot_f32(q[ii], sc[ii], hv);
+          }
+          acc = fmaf(dot, (!SLOTS || du[ii].present) ? wgt : 0.0f, acc);
         }
       }
       wave_lds_sync();  // the next batch rewrites s_hb[wave]
@@ -714,45 +825,52 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
     if (p.ids_out) p.ids_out[lane] = s_ids[lane];
     if (p.w_out) p.w_out[lane] = w1;
   }
+  if constexpr (SLOTS) {
+    if (blockIdx.x == 0 && p.miss_out) {
+      for (int i = threadIdx.x; i < T * k; i += blockDim.x)
+        p.miss_out[i] = slot_of(s_ids[i]) < 0 ? s_ids[i] : -1;
+    }
+  }
 }
 
-template <int LPR>
+template <int LPR, bool SLOTS, bool FP8>
 static hipError_t launch_fused_lpr(const FusedParams& p, int grid, hipStream_t s) {
   const int cpl = p.H / (32 * LPR);
   dim3 g(grid), b(kFWaves * kWave);
   const bool one = p.T == 1;
   switch (cpl) {
-    case 1:
-      if (one) moe_decode_fused_kernel<LPR, 1, true><<<g, b, 0, s>>>(p);
-      else moe_decode_fused_kernel<LPR, 1, false><<<g, b, 0, s>>>(p);
-      break;
-    case 2:
-      if (one) moe_decode_fused_kernel<LPR, 2, true><<<g, b, 0, s>>>(p);
-      else moe_decode_fused_kernel<LPR, 2, false><<<g, b, 0, s>>>(p);
-      break;
-    case 3:
-      if (one) moe_decode_fused_kernel<LPR, 3, true><<<g, b, 0, s>>>(p);
-      else moe_decode_fused_kernel<LPR, 3, false><<<g, b, 0, s>>>(p);
-      break;
-    case 4:
-      if (one) moe_decode_fused_kernel<LPR, 4, true><<<g, b, 0, s>>>(p);
-      else moe_decode_fused_kernel<LPR, 4, false><<<g, b, 0, s>>>(p);
-      break;
+#define FT_FUSED_CPL(C)                                                        \
+  case C:                                                                      \
+    if (one) moe_decode_fused_kernel<LPR, C, true, SLOTS, FP8><<<g, b, 0, s>>>(p); \
+    else moe_decode_fused_kernel<LPR, C, false, SLOTS, FP8><<<g, b, 0, s>>>(p);    \
+    break;
+    FT_FUSED_CPL(1)
+    FT_FUSED_CPL(2)
+    FT_FUSED_CPL(3)
+    FT_FUSED_CPL(4)
+#undef FT_FUSED_CPL
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode_fused(const FusedParams& p, int grid, hipStream_t s) {
+template <bool SLOTS, bool FP8>
+static hipError_t launch_fused(const FusedParams& p, int grid, hipStream_t s) {
   int lpr = 0, cpl = 0;
   gateup_geometry(p.H, &lpr, &cpl);
   switch (lpr) {
-    case 64: return launch_fused_lpr<64>(p, grid, s);
-    case 32: return launch_fused_lpr<32>(p, grid, s);
-    case 16: return launch_fused_lpr<16>(p, grid, s);
-    case 8: return launch_fused_lpr<8>(p, grid, s);
+    case 64: return launch_fused_lpr<64, SLOTS, FP8>(p, grid, s);
+    case 32: return launch_fused_lpr<32, SLOTS, FP8>(p, grid, s);
+    case 16: return launch_fused_lpr<16, SLOTS, FP8>(p, grid, s);
+    case 8: return launch_fused_lpr<8, SLOTS, FP8>(p, grid, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// slot indirection is for the NVFP4 banks; block-fp8 banks are read directly
+hipError_t launch_decode_fused(const FusedParams& p, int grid, hipStream_t s) {
+  if (p.fp8) return launch_fused<false, true>(p, grid, s);
+  return p.slot_of ? launch_fused<true, false>(p, grid, s) : launch_fused<false, false>(p, grid, s);
 }
 
 int fused_block_threads() { return kFWaves * kWave; }
@@ -762,12 +880,17 @@ int fused_block_threads() { return kFWaves * kWave; }
 hipError_t decode_fused_min_occupancy(int* blocks_per_cu) {
   using K = void (*)(FusedParams);
   static const K kernels[] = {
-#define FT_FUSED_LPR(L)                                                                         \
-  moe_decode_fused_kernel<L, 1, true>, moe_decode_fused_kernel<L, 1, false>,                  \
-      moe_decode_fused_kernel<L, 2, true>, moe_decode_fused_kernel<L, 2, false>,              \
-      moe_decode_fused_kernel<L, 3, true>, moe_decode_fused_kernel<L, 3, false>,              \
-      moe_decode_fused_kernel<L, 4, true>, moe_decode_fused_kernel<L, 4, false>
-      FT_FUSED_LPR(64), FT_FUSED_LPR(32), FT_FUSED_LPR(16), FT_FUSED_LPR(8)
+#define FT_FUSED_LPR(L, S, F)                                                                   \
+  moe_decode_fused_kernel<L, 1, true, S, F>, moe_decode_fused_kernel<L, 1, false, S, F>,      \
+      moe_decode_fused_kernel<L, 2, true, S, F>, moe_decode_fused_kernel<L, 2, false, S, F>,  \
+      moe_decode_fused_kernel<L, 3, true, S, F>, moe_decode_fused_kernel<L, 3, false, S, F>,  \
+      moe_decode_fused_kernel<L, 4, true, S, F>, moe_decode_fused_kernel<L, 4, false, S, F>
+      FT_FUSED_LPR(64, false, false), FT_FUSED_LPR(32, false, false),
+      FT_FUSED_LPR(16, false, false), FT_FUSED_LPR(8, false, false),
+      FT_FUSED_LPR(64, true, false), FT_FUSED_LPR(32, true, false),
+      FT_FUSED_LPR(16, true, false), FT_FUSED_LPR(8, true, false),
+      FT_FUSED_LPR(64, false, true), FT_FUSED_LPR(32, false, true),
+      FT_FUSED_LPR(16, false, true), FT_FUSED_LPR(8, false, true)
 #undef FT_FUSED_LPR
   };
   int lowest = 1 << 30;
@@ -780,6 +903,30 @@ hipError_t decode_fused_min_occupancy(int* blocks_per_cu) {
   }
   *blocks_per_cu = lowest;
   return hipSuccess;
+}
+
+// Routes of a grouped decode call over a slot bank: expert ids become slot ids; a
+// non-resident expert becomes slot 0 with weight 0 (its pair still runs, and
+// contributes exactly 0), and its id goes to the miss list.
+__global__ __launch_bounds__(256) void map_slots_kernel(int32_t* ids, float* w, int pairs,
+                                                        const int32_t* slot_of, int n_slots,
+                                                        int32_t* miss_out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= pairs) return;
+  const int e = ids[i];
+  const int sl = slot_of[e];
+  const bool present = sl >= 0 && sl < n_slots;
+  ids[i] = present ? sl : 0;
+  if (!present) w[i] = 0.0f;
+  if (miss_out) miss_out[i] = present ? -1 : e;
+}
+
+hipError_t launch_map_slots(int32_t* ids, float* w, int pairs, const int32_t* slot_of,
+                            int n_slots, int32_t* miss_out, hipStream_t s) {
+  if (pairs <= 0) return hipSuccess;
+  map_slots_kernel<<<dim3((pairs + 255) / 256), dim3(256), 0, s>>>(ids, w, pairs, slot_of,
+                                                                    n_slots, miss_out);
+  return hipGetLastError();
 }
 
 // Reads the error word of a decode workspace into *status and clears it.

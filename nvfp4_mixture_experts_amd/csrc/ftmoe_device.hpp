@@ -201,6 +201,69 @@ __device__ __forceinline__ float chunk_dot_f32(const uint4 q, uint32_t sc2, cons
   return b0 * e4m3_byte_to_f32<0>(sc2) + b1 * e4m3_byte_to_f32<1>(sc2);
 }
 
+// ------------------------------------------------------- block-fp8 chunks --
+//
+// The block-fp8 codec: one OCP e4m3 byte per weight and one fp32 scale per 128 x 128
+// block.  A chunk is again 32 consecutive K elements of one row: 32 code bytes (two
+// uint4; element 4m + i in byte i of word m) inside one scale block.
+
+// Bytes Sel*2, Sel*2+1 of `w` (two e4m3 codes) -> a bf16 pair, exactly (an e4m3 value
+// has 4 significant bits and an exponent inside bf16's normal range).
+template <bool Hi>
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, Hi);
+}
+// The same two codes -> fp32, exactly.
+template <bool Hi>
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, Hi);
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& a, const uint4& b, int m) {
+  const uint4& q = m < 4 ? a : b;
+  const int i = m & 3;
+  return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
+}
+
+// sum_k code_k * x_k over one chunk (bf16 activations x2[m] = elements 2m, 2m+1):
+// exact products, fp32 accumulation in two chains; the block scale is applied by
+// the caller.
+__device__ __forceinline__ float chunk_dot_fp8_bf16(const uint4 q0, const uint4 q1,
+                                                    const bf16x2* x2) {
+  float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    b0 = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16<false>(word_of(q0, q1, m)), x2[2 * m],
+                                         b0, false);
+    b0 = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16<true>(word_of(q0, q1, m)),
+                                         x2[2 * m + 1], b0, false);
+  }
+#pragma unroll
+  for (int m = 4; m < 8; ++m) {
+    b1 = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16<false>(word_of(q0, q1, m)), x2[2 * m],
+                                         b1, false);
+    b1 = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16<true>(word_of(q0, q1, m)),
+                                         x2[2 * m + 1], b1, false);
+  }
+  return b0 + b1;
+}
+
+// sum_k code_k * h_k over one chunk with fp32 activations h[0..31].
+__device__ __forceinline__ float chunk_dot_fp8_f32(const uint4 q0, const uint4 q1, const float* h) {
+  float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const uint32_t w = word_of(q0, q1, m);
+    const f32x2 lo = e4m3x2_to_f32<false>(w), hi = e4m3x2_to_f32<true>(w);
+    float& b = m < 4 ? b0 : b1;
+    b = fmaf(lo.x, h[4 * m], b);
+    b = fmaf(lo.y, h[4 * m + 1], b);
+    b = fmaf(hi.x, h[4 * m + 2], b);
+    b = fmaf(hi.y, h[4 * m + 3], b);
+  }
+  return b0 + b1;
+}
+
 // ------------------------------------------- device-coherent hand-offs --
 //
 // Data that one block of a kernel hands to another block of the same kernel is

@@ -65,6 +65,11 @@ struct FusedParams {
   int d_groups;                 // T * H / 64 (token, row group) pairs of the down GEMV
   int blocks_per_group;         // blocks sharing one group when d_groups < grid
   int spin_limit;               // polls of one value before giving up
+  const int32_t* slot_of;       // optional [E] expert -> slot of `routed` (null: identity)
+  int n_slots;                  // slots of `routed` when slot_of is set
+  int32_t* miss_out;            // optional [T][k]: id of a non-resident selected expert, or -1
+  int fp8;                      // 1: both banks are block-fp8 (w13s / w2s point at fp32 block
+                                // scales, gsc unused), 0: NVFP4
 };
 
 
@@ -103,6 +108,10 @@ int fused_block_threads();
 hipError_t decode_fused_min_occupancy(int* blocks_per_cu);
 // copies the error word err[0] of a decode workspace to *status and clears it
 hipError_t launch_device_status(uint32_t* err, int32_t* status, hipStream_t s);
+// Rewrites routes [T*k] in place from expert ids to slot ids (a non-resident expert:
+// slot 0 and weight 0) and writes the miss list (expert id or -1) when given.
+hipError_t launch_map_slots(int32_t* ids, float* w, int pairs, const int32_t* slot_of,
+                            int n_slots, int32_t* miss_out, hipStream_t s);
 hipError_t launch_route(const RouteParams& p, bool fuse_topk, hipStream_t s);
 int route_fused_topk_tokens();  // the fused top-k handles at most this many tokens
 hipError_t launch_route_split(const RouteParams& p, hipStream_t s);
@@ -113,5 +122,10 @@ hipError_t launch_repack_w2(int H, int I, int n, const uint8_t* w2, const uint8_
                             uint8_t* out_w2, uint8_t* out_w2s, hipStream_t s);
 hipError_t launch_dequant(int H, int I, const Bank& b, int expert, int tensor, int out_dtype,
                           void* out, hipStream_t s);
+// block-fp8 banks (Bank.w13s / w2s hold fp32 block scales; gsc unused)
+hipError_t launch_repack_fp8_w2(int H, int I, int n, const uint8_t* w2, uint8_t* out_w2,
+                                hipStream_t s);
+hipError_t launch_fp8_dequant(int H, int I, const Bank& b, int expert, int tensor, int mode,
+                              float* out, hipStream_t s);
 
 }  // namespace ftmoe

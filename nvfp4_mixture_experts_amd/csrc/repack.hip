@@ -35,6 +35,90 @@ __global__ __launch_bounds__(256) void repack_w2_kernel(int H, int I, int n,
   }
 }
 
+// block-fp8 down codes: canonical [n][H][I] -> [n][I/32][H][32] (32 e4m3 bytes of one
+// row's K-chunk per record, so 64 lanes owning 64 consecutive rows read 2 KiB contiguous)
+__global__ __launch_bounds__(256) void repack_fp8_w2_kernel(int H, int I, int n,
+                                                            const uint8_t* __restrict__ w2,
+                                                            uint8_t* __restrict__ out_w2) {
+  const int nch = I / 32;
+  const size_t total = static_cast<size_t>(n) * H * nch;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const size_t c = i % H;
+    const size_t j = (i / H) % nch;
+    const size_t e = i / (static_cast<size_t>(H) * nch);
+    const uint4* src = reinterpret_cast<const uint4*>(w2 + (e * H + c) * I + 32 * j);
+    uint4* dst = reinterpret_cast<uint4*>(out_w2 + i * 32);
+    dst[0] = src[0];
+    dst[1] = src[1];
+  }
+}
+
+hipError_t launch_repack_fp8_w2(int H, int I, int n, const uint8_t* w2, uint8_t* out_w2,
+                                hipStream_t s) {
+  const size_t total = static_cast<size_t>(n) * H * (I / 32);
+  if (total == 0) return hipSuccess;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  repack_fp8_w2_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(H, I, n, w2,
+                                                                                out_w2);
+  return hipGetLastError();
+}
+
+// Dequantise one tensor of one block-fp8 expert (repacked bank) to fp32 [rows][K]
+// with the routines the one-launch decode kernel uses: mode 0 decodes the codes as
+// its down GEMV does (e4m3 pair -> fp32 pair), mode 1 as its gate|up GEMV does
+// (e4m3 pair -> bf16 pair); both then multiply by the block scale (one rounding).
+__global__ __launch_bounds__(256) void fp8_dequant_kernel(int H, int I, Bank b, int e,
+                                                          int tensor, int mode, float* out) {
+  const bool down = (tensor == 2);
+  const int rows = down ? H : I;
+  const int K = down ? I : H;
+  const size_t total = static_cast<size_t>(rows) * (K / 4);
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int r = static_cast<int>(idx / (K / 4));
+  const int k0 = 4 * static_cast<int>(idx % (K / 4));
+  uint32_t word;
+  float scale;
+  const float* sc13 = reinterpret_cast<const float*>(b.w13s);
+  const float* sc2 = reinterpret_cast<const float*>(b.w2s);
+  if (!down) {
+    const size_t row = static_cast<size_t>(tensor == 1 ? I : 0) + r;
+    word = *reinterpret_cast<const uint32_t*>(b.w13 + (static_cast<size_t>(e) * 2 * I + row) * H + k0);
+    scale = sc13[(static_cast<size_t>(e) * (2 * I / 128) + row / 128) * (H / 128) + k0 / 128];
+  } else {
+    const size_t rec = (static_cast<size_t>(e) * (I / 32) + k0 / 32) * H + r;
+    word = *reinterpret_cast<const uint32_t*>(b.w2 + rec * 32 + (k0 % 32));
+    scale = sc2[(static_cast<size_t>(e) * (H / 128) + r / 128) * (I / 128) + k0 / 128];
+  }
+  float v[4];
+  if (mode == 1) {
+    const bf16x2 lo = e4m3x2_to_bf16<false>(word), hi = e4m3x2_to_bf16<true>(word);
+    v[0] = static_cast<float>(lo[0]);
+    v[1] = static_cast<float>(lo[1]);
+    v[2] = static_cast<float>(hi[0]);
+    v[3] = static_cast<float>(hi[1]);
+  } else {
+    const f32x2 lo = e4m3x2_to_f32<false>(word), hi = e4m3x2_to_f32<true>(word);
+    v[0] = lo.x;
+    v[1] = lo.y;
+    v[2] = hi.x;
+    v[3] = hi.y;
+  }
+  float* o = out + static_cast<size_t>(r) * K + k0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = v[i] * scale;
+}
+
+hipError_t launch_fp8_dequant(int H, int I, const Bank& b, int expert, int tensor, int mode,
+                              float* out, hipStream_t s) {
+  const size_t total = static_cast<size_t>(H) * I / 4;
+  fp8_dequant_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
+      H, I, b, expert, tensor, mode, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_repack_w2(int H, int I, int n, const uint8_t* w2, const uint8_t* w2s,
                             uint8_t* out_w2, uint8_t* out_w2s, hipStream_t s) {
   const size_t total = static_cast<size_t>(n) * H * (I / 32);

@@ -70,6 +70,8 @@ def _load() -> ctypes.CDLL:
         "ft_moe_device_status": (I32, [P, SZ, P, P]),
         "ft_set_wait_limit": (I32, [I32]),
         "ft_moe_nvfp4_decode_noalloc": (I32, [D, I64, P, P, P, B, B, P, P, P, P, P, P]),
+        "ft_moe_nvfp4_decode_slots": (I32, [D, I64, P, P, P, B, I32, P, B, P, P, P, P, P, P,
+                                            SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -84,7 +86,7 @@ _lib = _load()
 EXPORTED = ("ft_abi_version", "ft_last_error", "ft_init", "ft_nvfp4_repacked_bytes",
             "ft_nvfp4_repack", "ft_moe_workspace_bytes", "ft_moe_route", "ft_moe_nvfp4_decode",
             "ft_moe_nvfp4_prefill", "ft_nvfp4_dequant", "ft_moe_device_status",
-            "ft_set_wait_limit", "ft_moe_nvfp4_decode_noalloc")
+            "ft_set_wait_limit", "ft_moe_nvfp4_decode_noalloc", "ft_moe_nvfp4_decode_slots")
 
 
 def library_path() -> str:
@@ -280,3 +282,20 @@ def ft_moe_nvfp4_decode_noalloc(desc: FtMoeDesc, x, w_router, bias, routed: Bank
         _ptr(topk_ids_out, torch.int32, "topk_ids_out"),
         _ptr(topk_w_out, torch.float32, "topk_w_out"), _ptr(y, torch.bfloat16, "y"),
         _ptr(status, torch.int32, "status"), _stream(stream)), "ft_moe_nvfp4_decode_noalloc")
+
+
+def ft_moe_nvfp4_decode_slots(desc: FtMoeDesc, x, w_router, bias, slots: Bank, slot_of,
+                              shared: Optional[Bank], shared_gate, y, workspace,
+                              topk_ids_out=None, topk_w_out=None, miss_out=None,
+                              stream=None) -> None:
+    """ft_moe_nvfp4_decode over a bank of expert slots; ``slot_of`` int32 [E] device."""
+    _check(_lib.ft_moe_nvfp4_decode_slots(
+        ctypes.byref(desc), x.shape[0], _ptr(x, torch.bfloat16, "x"),
+        _ptr(w_router, torch.float32, "w_router"), _ptr(bias, torch.float32, "bias"),
+        slots.ref(), slots.n, _ptr(slot_of, torch.int32, "slot_of"),
+        shared.ref() if shared is not None else None,
+        _ptr(shared_gate, torch.bfloat16, "shared_gate"),
+        _ptr(topk_ids_out, torch.int32, "topk_ids_out"),
+        _ptr(topk_w_out, torch.float32, "topk_w_out"), _ptr(miss_out, torch.int32, "miss_out"),
+        _ptr(y, torch.bfloat16, "y"), _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream)), "ft_moe_nvfp4_decode_slots")
