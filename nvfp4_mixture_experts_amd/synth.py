@@ -82,6 +82,60 @@ WORKLOADS = {
     ]
 }
 
+
+# ------------------------------------------------------ fp8 W8A8 projections --
+
+@dataclasses.dataclass(frozen=True)
+class LinearWorkload:
+    """A fused per-tensor-FP8 projection: parts of `parts` output rows each (q, k, v)
+    stacked along N, input width `hidden`, `tokens` rows of activations."""
+    name: str
+    hidden: int
+    parts: tuple
+    tokens: int
+    seed: int
+
+    @property
+    def out_rows(self) -> int:
+        return int(sum(self.parts))
+
+
+@dataclasses.dataclass
+class Fp8Linear:
+    workload: LinearWorkload
+    w: np.ndarray              # u8 [N, K] e4m3 codes (parts stacked)
+    part_scales: np.ndarray    # f32 [n_parts] per-part (per-tensor) weight scales
+
+    def part_ranges(self):
+        edges = np.concatenate([[0], np.cumsum(self.workload.parts)])
+        return [(int(a), int(b)) for a, b in zip(edges[:-1], edges[1:])]
+
+    def row_scales(self) -> np.ndarray:
+        """The per-row scale vector (each row carries its part's scale)."""
+        return np.repeat(self.part_scales, self.workload.parts).astype(np.float32)
+
+
+def make_fp8_linear(w: LinearWorkload) -> Fp8Linear:
+    """Uniform e4m3 weight codes over the finite encodings; per-part scales drawn as
+    2^-9 * (1 + U[0, 1)) (distinct parts, so a wrong part boundary changes rows)."""
+    rng = _rng(w.seed, "fp8_linear_w")
+    codes = _fp8_codes(rng, (w.out_rows, w.hidden))
+    scales = (np.float32(2.0 ** -9) * (1 + _rng(w.seed, "fp8_linear_s").random(
+        len(w.parts), dtype=np.float32))).astype(np.float32)
+    return Fp8Linear(w, codes, scales)
+
+
+LINEAR_WORKLOADS = {
+    lw.name: lw
+    for lw in [
+        # q (32 heads x 128) | k (4 x 128) | v (4 x 128) over hidden 2048
+        LinearWorkload("fp8_linear_qkv_t1", 2048, (4096, 512, 512), 1, seed=2001),
+        LinearWorkload("fp8_linear_qkv_t32", 2048, (4096, 512, 512), 32, seed=2002),
+        LinearWorkload("fp8_linear_qkv_t8192", 2048, (4096, 512, 512), 8192, seed=2003),
+    ]
+}
+WORKLOADS.update(LINEAR_WORKLOADS)
+
 # ---------------------------------------------------------------- block-fp8 --
 
 FP8_BLOCK = 128

@@ -94,6 +94,12 @@ def _load(omp: bool = False):
     lib.or_moe_layer_fp8.restype = _I32
     lib.or_moe_layer_fp8.argtypes = ([_I32, _I32, _I32, _I32, _I32, _F32, _F32, _I64, _P, _P, _P]
                                      + [_P] * 4 + [_I32] + [_P] * 5 + [_P] * 4)
+    lib.or_e4m3_encode.restype = ctypes.c_uint32
+    lib.or_e4m3_encode.argtypes = [_F32]
+    lib.or_fp8_quantize.restype = None
+    lib.or_fp8_quantize.argtypes = [_I64, _I64, _P, _P, _P]
+    lib.or_fp8_linear.restype = None
+    lib.or_fp8_linear.argtypes = [_I64, _I64, _I64, _P, _F32, _P, _P, _P, _P]
     _libs[omp] = lib
     return lib
 
@@ -324,3 +330,35 @@ def moe_layer_fp8(layer, x: np.ndarray, openmp: bool = False) -> dict:
     if rc != 0:
         raise ValueError("oracle rejected the layer shape")
     return {"ids": ids, "weights": w, "y64": y64, "y": y}
+
+
+# ---------------------------------------------- fp8 per-tensor W8A8 linear --
+
+def e4m3_encode(v: float) -> int:
+    return int(_load().or_e4m3_encode(float(v)))
+
+
+def fp8_quantize(x: np.ndarray, openmp: bool = False):
+    """bf16 bits u16 [M, K] -> (e4m3 codes u8 [M, K], fp32 per-tensor scale)."""
+    x = _c(x, np.uint16)
+    M, K = x.shape
+    codes = np.empty((M, K), np.uint8)
+    scale = np.empty(1, np.float32)
+    _load(openmp).or_fp8_quantize(M, K, _ptr(x), _ptr(codes), _ptr(scale))
+    return codes, np.float32(scale[0])
+
+
+def fp8_linear(xq: np.ndarray, s_x: float, w: np.ndarray, w_scale_rows: np.ndarray,
+               openmp: bool = False) -> dict:
+    """y = bf16(s_x * s_w[n] * sum_k e4m3(xq[m,k]) e4m3(w[n,k])): returns {"y64", "y"}."""
+    xq = _c(xq, np.uint8)
+    w = _c(w, np.uint8)
+    ws = _c(w_scale_rows, np.float32)
+    M, K = xq.shape
+    N = w.shape[0]
+    assert w.shape == (N, K) and ws.shape == (N,)
+    y64 = np.empty((M, N), np.float64)
+    y = np.empty((M, N), np.uint16)
+    _load(openmp).or_fp8_linear(M, N, K, _ptr(xq), float(s_x), _ptr(w), _ptr(ws), _ptr(y64),
+                                _ptr(y))
+    return {"y64": y64, "y": y}

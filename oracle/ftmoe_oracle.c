@@ -603,3 +603,75 @@ int32_t or_moe_layer_fp8(int32_t E, int32_t H, int32_t I, int32_t k, int32_t act
     free(xd); free(hb); free(o); free(acc);
     return 0;
 }
+
+/* ------------------------------------------------ fp8 per-tensor W8A8 linear -- */
+
+/* FreeToken commit log (page 2), the paragraph on row-wise FP8 scaled matrix products:
+ * the fused per-tensor-FP8 projections (q/k/v parts stacked along the output rows)
+ * run as W8A8 products, either one row-wise-scaled GEMM or, as a fallback, one
+ * tensor-wise GEMM per part over its row slice, the parts found from the run-lengths
+ * of the per-row weight scales.  Readings taken here: activations are quantised per
+ * tensor with scale s_x = amax|x| / 448 (fp32 division) and codes
+ * e4m3(x / s_x) (the quotient in fp32, then round to the nearest e4m3 value, ties to
+ * the even code, magnitudes above 448 saturating to 448; s_x = 1 for an all-zero x);
+ * y[m, n] = bf16( s_x * s_w[n] * sum_k e4m3(xq[m, k]) * e4m3(w[n, k]) ), where s_w[n]
+ * is the scale of the part holding row n.  The e4m3 x e4m3 products have at most 8
+ * significant bits, so the sum is exact in binary64 for K < 2^17. */
+
+/* fp32 value -> e4m3 byte: the nearest of the 254 finite e4m3 values by exhaustive
+ * search (ties to the code with an even mantissa), saturating at +-448; NaN -> 0x7F. */
+uint32_t or_e4m3_encode(float v)
+{
+    if (isnan(v))
+        return 0x7F;
+    double a = fabs((double)v);
+    uint32_t sign = signbit(v) ? 0x80u : 0u;
+    uint32_t best = 0;
+    double best_d = INFINITY;
+    for (uint32_t b = 0; b < 0x7F; ++b) { /* magnitudes 0 .. 448 */
+        double d = fabs(or_e4m3(b) - a);
+        if (d < best_d || (d == best_d && (b & 1u) == 0u)) {
+            best_d = d;
+            best = b;
+        }
+    }
+    return sign | best;
+}
+
+/* Per-tensor activation quantisation: s_x and the codes of x (bf16 [M, K]). */
+void or_fp8_quantize(int64_t M, int64_t K, const uint16_t *x, uint8_t *codes, float *scale)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < M * K; ++i) {
+        float a = (float)fabs(or_bf16_to_double(x[i]));
+        if (a > amax)
+            amax = a;
+    }
+    float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    *scale = s;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M * K; ++i) {
+        float q = (float)or_bf16_to_double(x[i]) / s;
+        codes[i] = (uint8_t)or_e4m3_encode(q);
+    }
+}
+
+/* y = bf16( s_x * s_w[n] * sum_k e4m3(xq[m,k]) e4m3(w[n,k]) ), binary64 throughout;
+ * xq [M, K], w [N, K] e4m3 bytes, w_scale fp32 [N]; y64 (optional) the unrounded value. */
+void or_fp8_linear(int64_t M, int64_t N, int64_t K, const uint8_t *xq, float s_x,
+                   const uint8_t *w, const float *w_scale, double *y64, uint16_t *y)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += or_e4m3(xq[m * K + k]) * or_e4m3(w[n * K + k]);
+            double v = acc * (double)s_x * (double)w_scale[n];
+            if (y64)
+                y64[m * N + n] = v;
+            if (y)
+                y[m * N + n] = or_bf16_from_double(v);
+        }
+    }
+}

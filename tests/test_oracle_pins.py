@@ -607,3 +607,58 @@ def test_fp8_workload_clamps_engage():
     full = np.repeat(np.repeat(layer.w13_scales[0], 128, 0), 128, 1)
     pre = xf @ (E4M3[c] * full).T
     assert 0.3 < np.std(pre) < 30 and np.mean(np.abs(pre) > 7) > 0.001
+
+
+# ------------------------------------------------ fp8 per-tensor W8A8 linear --
+
+def _torch_e4m3(v):
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def test_e4m3_encoder_round_trip_and_torch_rounding():
+    finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F])
+    for b in finite:                                   # decode then encode is the identity
+        assert oracle.e4m3_encode(oracle.e4m3(b)) == b
+    # midpoints between neighbouring magnitudes (exact ties: round to the even code)
+    mags = np.array(sorted({abs(oracle.e4m3(b)) for b in range(0x7F)}))
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)
+    assert np.array_equal((mags[:-1] + mags[1:]) / 2, mids.astype(np.float64))   # exact in fp32
+    rng = np.random.default_rng(12)
+    vals = np.concatenate([mids, -mids, (rng.standard_normal(4000) * 40).astype(np.float32),
+                           (rng.random(1000) * 0.02).astype(np.float32), np.float32([0.0, -0.0])])
+    vals = vals[np.abs(vals) <= 448]
+    got = np.array([oracle.e4m3_encode(float(v)) for v in vals], np.uint8)
+    assert np.array_equal(got, _torch_e4m3(vals))
+    assert oracle.e4m3_encode(1e6) == 0x7E and oracle.e4m3_encode(-1e6) == 0xFE   # saturate
+
+
+def test_fp8_activation_quantisation():
+    w = synth.WORKLOADS["fp8_linear_qkv_t32"]
+    x = synth.make_tokens(w, tokens=6, stream="q")
+    codes, s = oracle.fp8_quantize(x)
+    xf = _bf16_to_f64(x).astype(np.float32)
+    amax = np.float32(np.abs(xf).max())
+    assert s == amax / np.float32(448.0)
+    assert np.array_equal(codes, _torch_e4m3(xf / s))
+    assert codes.view(np.int8).max() == 0x7E or (codes & 0x7F).max() == 0x7E   # amax -> 448
+
+
+def test_fp8_linear_equals_exact_matmul_and_per_part_concatenation():
+    w = synth.WORKLOADS["fp8_linear_qkv_t32"]
+    lin = synth.make_fp8_linear(synth.dataclasses.replace(w, hidden=512,
+                                                          parts=(256, 64, 64)))
+    x = synth.make_tokens(lin.workload, tokens=5, stream="lin")
+    xq, s_x = oracle.fp8_quantize(x)
+    rows = lin.row_scales()
+    got = oracle.fp8_linear(xq, s_x, lin.w, rows)
+    a = E4M3[xq].astype(np.float64)
+    b = E4M3[lin.w].astype(np.float64)
+    want = ((a @ b.T) * np.float64(s_x)) * rows.astype(np.float64)[None, :]
+    assert np.array_equal(got["y64"], want)            # the fp64 sums are exact
+    # one tensor-wise product per part over its row slice, concatenated
+    parts = []
+    for (r0, r1), sc in zip(lin.part_ranges(), lin.part_scales):
+        parts.append(oracle.fp8_linear(xq, s_x, lin.w[r0:r1],
+                                       np.full(r1 - r0, sc, np.float32))["y"])
+    assert np.array_equal(np.concatenate(parts, axis=1), got["y"])
