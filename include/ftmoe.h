@@ -94,6 +94,15 @@ typedef struct ft_nvfp4_experts {
     const float *global_scale; /* f32 [n][3]: gate, up, down */
 } ft_nvfp4_experts;
 
+/* One repacked block-fp8 expert bank (routed: n = num_experts; shared: n = 1): e4m3
+ * weights with one fp32 scale per 128 x 128 block (see ft_fp8_repack). */
+typedef struct ft_fp8_experts {
+    const uint8_t *w13;       /* repacked gate|up e4m3 codes */
+    const float *w13_scale;   /* f32 [n][2I/128][H/128] block scales */
+    const uint8_t *w2;        /* repacked down e4m3 codes */
+    const float *w2_scale;    /* f32 [n][H/128][I/128] block scales */
+} ft_fp8_experts;
+
 /* FT_ABI_VERSION of the library that was loaded. */
 int32_t ft_abi_version(void);
 
@@ -167,6 +176,48 @@ ft_status ft_moe_nvfp4_decode(const ft_moe_desc *desc, int64_t tokens, const uin
                               const uint16_t *shared_gate, int32_t *topk_ids_out,
                               float *topk_w_out, uint16_t *y, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/* Block-fp8 experts, the second routed-expert codec of the 512-expert layer
+ * (FreeToken commit log, page 2: the entry with NVFP4 / block-fp8 routed experts and
+ * its fp8 scale-bank padding rule).  The pages give no block shape; this library
+ * reads it as: one OCP e4m3 byte per weight and one fp32 scale per 128 x 128 block of
+ * each [rows][K] matrix, dequantised weight = fp32(e4m3 * scale) (one rounding), no
+ * separate global scale.  Canonical layout (the input of ft_fp8_repack):
+ *   w13 codes   u8  [n][2I][H]          gate rows 0..I-1, then up rows
+ *   w13 scales  f32 [n][2I/128][H/128]
+ *   w2 codes    u8  [n][H][I]
+ *   w2 scales   f32 [n][H/128][I/128]
+ * Needs hidden % 256 == 0 and inter % 128 == 0 (shared_inter likewise).
+ * ft_fp8_repacked_bytes: bytes of part 0..3 (codes, scales, codes, scales) of the
+ * repacked bank (0 for invalid arguments).  ft_fp8_repack: gate|up codes and every
+ * scale are copied; down codes become K-chunk-major [n][I/32][H] records of 32 bytes
+ * (64 lanes reading 64 consecutive rows read 2 KiB contiguous). */
+size_t ft_fp8_repacked_bytes(int32_t hidden, int32_t inter, int32_t n_experts, int32_t part);
+ft_status ft_fp8_repack(int32_t hidden, int32_t inter, int32_t n_experts, const uint8_t *w13,
+                        const float *w13_scale, const uint8_t *w2, const float *w2_scale,
+                        uint8_t *out_w13, float *out_w13_scale, uint8_t *out_w2,
+                        float *out_w2_scale, void *stream);
+
+/* The decode layer (as ft_moe_nvfp4_decode: routing, fused gate|up GEMV with in-register
+ * e4m3 -> bf16 conversion and the block scale applied per 32-element chunk, (clamped)
+ * SwiGLU, down GEMV, weighted combine, gated shared expert) over block-fp8 banks, for
+ * 1 <= tokens <= 7 (the one-launch kernel; 8 or more return FT_EUNSUPPORTED).  The
+ * shared expert, when desc->shared_inter > 0, is a block-fp8 bank of one expert.  The
+ * workspace is a decode workspace (ft_moe_workspace_bytes, path 1); its give-up status
+ * is read with ft_moe_device_status. */
+ft_status ft_moe_fp8_decode(const ft_moe_desc *desc, int64_t tokens, const uint16_t *x,
+                            const float *w_router, const float *bias, const ft_fp8_experts *routed,
+                            const ft_fp8_experts *shared, const uint16_t *shared_gate,
+                            int32_t *topk_ids_out, float *topk_w_out, uint16_t *y,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Test export: tensor `tensor` (0 gate, 1 up, 2 down) of expert `expert` of a repacked
+ * block-fp8 bank as fp32 [rows][K] (out 16-byte aligned), through the decode kernel's
+ * routines: mode 0 decodes codes as its down GEMV does (e4m3 pair -> fp32 pair), mode 1
+ * as its gate|up GEMV does (e4m3 pair -> bf16 pair); both multiply by the block scale. */
+ft_status ft_fp8_dequant(int32_t hidden, int32_t inter, int32_t n_experts,
+                         const ft_fp8_experts *bank, int32_t expert, int32_t tensor, int32_t mode,
+                         float *out, void *stream);
 
 /* ft_moe_nvfp4_decode with the routed experts held in a bank of expert SLOTS
  * (FreeToken fork PR #84, page 1, the interleaved A/B table: the deployment keeps

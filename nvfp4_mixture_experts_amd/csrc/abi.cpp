@@ -141,6 +141,29 @@ ft_status check_layer_args(const ft_moe_desc* desc, const uint16_t* x,
   return FT_OK;
 }
 
+ft_status check_fp8_bank(const ft_fp8_experts* b, const char* name) {
+  if (!b) return fail(FT_EINVAL, "%s fp8 bank is NULL", name);
+  if (!b->w13 || !b->w13_scale || !b->w2 || !b->w2_scale)
+    return fail(FT_EINVAL, "%s fp8 bank has a NULL pointer", name);
+  if (!aligned16(b->w13) || !aligned16(b->w13_scale) || !aligned16(b->w2) ||
+      !aligned16(b->w2_scale))
+    return fail(FT_EINVAL, "%s fp8 bank pointers must be 16-byte aligned", name);
+  return FT_OK;
+}
+
+Bank to_bank_fp8(const ft_fp8_experts* b, int inter) {
+  Bank r{};
+  if (b) {
+    r.w13 = b->w13;
+    r.w13s = reinterpret_cast<const uint8_t*>(b->w13_scale);
+    r.w2 = b->w2;
+    r.w2s = reinterpret_cast<const uint8_t*>(b->w2_scale);
+    r.gsc = nullptr;
+    r.inter = inter;
+  }
+  return r;
+}
+
 // Router logits (fp64, one fp32 rounding), the shared gate when `gamma` is set,
 // and top-k with softmax weights into ids / w (and the optional copies).
 ft_status run_route(const ft_moe_desc* desc, int T, const uint16_t* x, const float* w_router,
@@ -348,6 +371,52 @@ ft_status ft_moe_route(const ft_moe_desc* desc, int64_t tokens, const uint16_t* 
 
 namespace {
 
+// The one-launch decode kernel (1..7 tokens) on banks already converted to Bank.
+ft_status run_fused(const ft_moe_desc* desc, int T, const uint16_t* x, const float* w_router,
+                    const float* bias, const Bank& routed, const Bank& shared,
+                    const uint16_t* shared_gate, int32_t* topk_ids_out, float* topk_w_out,
+                    uint16_t* y, void* workspace, const Layout& L, int grid,
+                    const int32_t* slot_of, int32_t n_slots, int32_t* miss_out, int fp8,
+                    hipStream_t s) {
+  const bool has_shared = desc->shared_inter > 0;
+  const int nrg = desc->hidden / kRowGroup;
+  FusedParams p{};
+  p.x = x;
+  p.wr = w_router;
+  p.bias = bias;
+  p.shared_gate = has_shared ? shared_gate : nullptr;
+  p.T = T;
+  p.E = desc->num_experts;
+  p.H = desc->hidden;
+  p.k = desc->top_k;
+  p.act = desc->act;
+  p.gate_max = desc->gate_max;
+  p.up_absmax = desc->up_absmax;
+  p.routed = routed;
+  p.shared = has_shared ? shared : Bank{};
+  p.nslots = desc->top_k + (has_shared ? 1 : 0);
+  p.Imax = desc->inter > desc->shared_inter ? desc->inter : desc->shared_inter;
+  p.y = y;
+  p.ids_out = topk_ids_out;
+  p.w_out = topk_w_out;
+  p.logits = at<uint64_t>(workspace, L.logits);
+  p.h = at<uint64_t>(workspace, L.h);
+  p.part = at<uint64_t>(workspace, L.part);
+  p.gen = at<uint32_t>(workspace, L.gen);
+  p.err = at<uint32_t>(workspace, L.sync) + kErrorWord;
+  p.d_groups = T * nrg;
+  const int upg = desc->top_k * (desc->inter / 32) + desc->shared_inter / 32;
+  p.blocks_per_group = p.d_groups >= grid ? 1 : std::min(grid / p.d_groups, upg);
+  p.spin_limit = wait_limit();
+  p.slot_of = slot_of;
+  p.n_slots = n_slots;
+  p.miss_out = miss_out;
+  p.fp8 = fp8;
+  hipError_t e = launch_decode_fused(p, grid, s);
+  if (e != hipSuccess) return hip_fail(e, "fused decode kernel");
+  return ok();
+}
+
 // The decode call; with slot_of set, `routed` is a bank of n_slots expert slots.
 ft_status decode_impl(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,
                       const float* w_router, const float* bias, const ft_nvfp4_experts* routed,
@@ -370,7 +439,6 @@ ft_status decode_impl(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool has_shared = desc->shared_inter > 0;
   const int T = static_cast<int>(tokens);
-  const int nrg = desc->hidden / kRowGroup;
   if (T >= kGroupedDecodeMinTokens) {
     int32_t* ids = at<int32_t>(workspace, L.ids);
     float* wts = at<float>(workspace, L.w);
@@ -391,40 +459,10 @@ ft_status decode_impl(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x
     return ok();
   }
 
-  FusedParams p{};
-  p.x = x;
-  p.wr = w_router;
-  p.bias = bias;
-  p.shared_gate = has_shared ? shared_gate : nullptr;
-  p.T = T;
-  p.E = desc->num_experts;
-  p.H = desc->hidden;
-  p.k = desc->top_k;
-  p.act = desc->act;
-  p.gate_max = desc->gate_max;
-  p.up_absmax = desc->up_absmax;
-  p.routed = to_bank(routed, desc->inter);
-  p.shared = has_shared ? to_bank(shared, desc->shared_inter) : Bank{};
-  p.nslots = desc->top_k + (has_shared ? 1 : 0);
-  p.Imax = desc->inter > desc->shared_inter ? desc->inter : desc->shared_inter;
-  p.y = y;
-  p.ids_out = topk_ids_out;
-  p.w_out = topk_w_out;
-  p.logits = at<uint64_t>(workspace, L.logits);
-  p.h = at<uint64_t>(workspace, L.h);
-  p.part = at<uint64_t>(workspace, L.part);
-  p.gen = at<uint32_t>(workspace, L.gen);
-  p.err = at<uint32_t>(workspace, L.sync) + kErrorWord;
-  p.d_groups = T * nrg;
-  const int upg = desc->top_k * (desc->inter / 32) + desc->shared_inter / 32;
-  p.blocks_per_group = p.d_groups >= grid ? 1 : std::min(grid / p.d_groups, upg);
-  p.spin_limit = wait_limit();
-  p.slot_of = slot_of;
-  p.n_slots = n_slots;
-  p.miss_out = miss_out;
-  hipError_t e = launch_decode_fused(p, grid, s);
-  if (e != hipSuccess) return hip_fail(e, "fused decode kernel");
-  return ok();
+  return run_fused(desc, T, x, w_router, bias, to_bank(routed, desc->inter),
+                   has_shared ? to_bank(shared, desc->shared_inter) : Bank{}, shared_gate,
+                   topk_ids_out, topk_w_out, y, workspace, L, grid, slot_of, n_slots, miss_out, 0,
+                   s);
 }
 
 }  // namespace
@@ -461,6 +499,101 @@ ft_status ft_moe_nvfp4_decode_slots(const ft_moe_desc* desc, int64_t tokens, con
                 kGroupedDecodeMinTokens, n_slots, desc->num_experts);
   return decode_impl(desc, tokens, x, w_router, bias, slots, slot_of, n_slots, miss_out, shared,
                      shared_gate, topk_ids_out, topk_w_out, y, workspace, workspace_bytes, stream);
+}
+
+size_t ft_fp8_repacked_bytes(int32_t hidden, int32_t inter, int32_t n_experts, int32_t part) {
+  if (hidden <= 0 || inter <= 0 || n_experts <= 0 || hidden % 128 || inter % 128) return 0;
+  const size_t n = static_cast<size_t>(n_experts), H = static_cast<size_t>(hidden),
+               I = static_cast<size_t>(inter);
+  switch (part) {
+    case 0: return n * 2 * I * H;
+    case 1: return n * (2 * I / 128) * (H / 128) * 4;
+    case 2: return n * H * I;
+    case 3: return n * (H / 128) * (I / 128) * 4;
+    default: return 0;
+  }
+}
+
+ft_status ft_fp8_repack(int32_t hidden, int32_t inter, int32_t n_experts, const uint8_t* w13,
+                        const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                        uint8_t* out_w13, float* out_w13_scale, uint8_t* out_w2,
+                        float* out_w2_scale, void* stream) {
+  if (hidden <= 0 || inter <= 0 || n_experts <= 0)
+    return fail(FT_EINVAL, "fp8 repack: non-positive size");
+  if (hidden % 256 || inter % 128 || inter > 4096)
+    return fail(FT_EUNSUPPORTED, "fp8 repack: hidden %d / inter %d unsupported (hidden %% 256, "
+                "inter %% 128)", hidden, inter);
+  const void* ptrs[8] = {w13, w13_scale, w2, w2_scale, out_w13, out_w13_scale, out_w2, out_w2_scale};
+  for (const void* p : ptrs) {
+    if (!p) return fail(FT_EINVAL, "fp8 repack: NULL pointer");
+    if (!aligned16(p)) return fail(FT_EINVAL, "fp8 repack: pointers must be 16-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t b0 = ft_fp8_repacked_bytes(hidden, inter, n_experts, 0);
+  const size_t b1 = ft_fp8_repacked_bytes(hidden, inter, n_experts, 1);
+  const size_t b3 = ft_fp8_repacked_bytes(hidden, inter, n_experts, 3);
+  hipError_t e = hipMemcpyAsync(out_w13, w13, b0, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 repack w13");
+  e = hipMemcpyAsync(out_w13_scale, w13_scale, b1, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 repack w13 scales");
+  e = hipMemcpyAsync(out_w2_scale, w2_scale, b3, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 repack w2 scales");
+  e = launch_repack_fp8_w2(hidden, inter, n_experts, w2, out_w2, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 repack w2");
+  return ok();
+}
+
+ft_status ft_moe_fp8_decode(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,
+                            const float* w_router, const float* bias, const ft_fp8_experts* routed,
+                            const ft_fp8_experts* shared, const uint16_t* shared_gate,
+                            int32_t* topk_ids_out, float* topk_w_out, uint16_t* y,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  ft_status st = check_desc(desc);
+  if (st != FT_OK) return st;
+  if (tokens < 1 || tokens >= kGroupedDecodeMinTokens)
+    return fail(tokens < 1 ? FT_EINVAL : FT_EUNSUPPORTED,
+                "fp8 decode takes 1..%d tokens, got %lld", kGroupedDecodeMinTokens - 1,
+                static_cast<long long>(tokens));
+  if (desc->inter % 128 || desc->shared_inter % 128)
+    return fail(FT_EUNSUPPORTED, "fp8 decode needs inter and shared_inter multiples of 128");
+  if (!w_router) return fail(FT_EINVAL, "w_router is NULL");
+  if (!aligned16(w_router)) return fail(FT_EINVAL, "w_router must be 16-byte aligned");
+  if (!x || !y) return fail(FT_EINVAL, "x or y is NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(FT_EINVAL, "x and y must be 16-byte aligned");
+  if ((st = check_fp8_bank(routed, "routed")) != FT_OK) return st;
+  const bool has_shared = desc->shared_inter > 0;
+  if (has_shared) {
+    if ((st = check_fp8_bank(shared, "shared")) != FT_OK) return st;
+    if (!shared_gate) return fail(FT_EINVAL, "shared_gate is NULL with a shared expert");
+    if (!aligned16(shared_gate)) return fail(FT_EINVAL, "shared_gate must be 16-byte aligned");
+  }
+  Layout L;
+  if ((st = check_ws(desc, tokens, 1, workspace, workspace_bytes, &L)) != FT_OK) return st;
+  int grid = 0;
+  if ((st = fused_grid(&grid)) != FT_OK) return st;
+  return run_fused(desc, static_cast<int>(tokens), x, w_router, bias,
+                   to_bank_fp8(routed, desc->inter),
+                   has_shared ? to_bank_fp8(shared, desc->shared_inter) : Bank{}, shared_gate,
+                   topk_ids_out, topk_w_out, y, workspace, L, grid, nullptr, 0, nullptr, 1,
+                   static_cast<hipStream_t>(stream));
+}
+
+ft_status ft_fp8_dequant(int32_t hidden, int32_t inter, int32_t n_experts,
+                         const ft_fp8_experts* bank, int32_t expert, int32_t tensor, int32_t mode,
+                         float* out, void* stream) {
+  if (hidden <= 0 || inter <= 0 || n_experts <= 0) return fail(FT_EINVAL, "fp8 dequant: bad size");
+  if (hidden % 256 || inter % 128 || inter > 4096)
+    return fail(FT_EUNSUPPORTED, "fp8 dequant: hidden %d / inter %d unsupported", hidden, inter);
+  if (expert < 0 || expert >= n_experts) return fail(FT_EINVAL, "fp8 dequant: expert out of range");
+  if (tensor < 0 || tensor > 2) return fail(FT_EINVAL, "fp8 dequant: tensor must be 0, 1 or 2");
+  if (mode != 0 && mode != 1) return fail(FT_EINVAL, "fp8 dequant: mode must be 0 or 1");
+  if (!out || !aligned16(out)) return fail(FT_EINVAL, "fp8 dequant: out NULL or misaligned");
+  ft_status st = check_fp8_bank(bank, "dequant");
+  if (st != FT_OK) return st;
+  hipError_t e = launch_fp8_dequant(hidden, inter, to_bank_fp8(bank, inter), expert, tensor, mode,
+                                    out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 dequant kernel");
+  return ok();
 }
 
 ft_status ft_moe_nvfp4_prefill(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,

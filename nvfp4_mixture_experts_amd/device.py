@@ -135,3 +135,40 @@ def prefill(dl: DeviceLayer, x: torch.Tensor, ids: torch.Tensor, w: torch.Tensor
     ftmoe.ft_moe_nvfp4_prefill(dl.desc, x, ids, w, dl.routed, dl.shared, dl.shared_gate, y,
                                workspace, stream=stream)
     return y
+
+
+def upload_fp8_layer(layer, device="cuda") -> DeviceLayer:
+    """Upload a host ``synth.Fp8Layer`` (block-fp8 banks, repacked with ft_fp8_repack)."""
+    w = layer.workload
+    desc = desc_of(w)
+
+    def bank(c13, s13, c2, s2, inter, n):
+        d = lambda a: _dev(a, device).contiguous()
+        return ftmoe.ft_fp8_repack(w.hidden, inter, n, d(c13), d(s13), d(c2), d(s2))
+
+    r = bank(layer.w13_codes, layer.w13_scales, layer.w2_codes, layer.w2_scales, w.inter,
+             w.num_experts)
+    s = None
+    sg = None
+    if w.shared_inter > 0:
+        s = bank(layer.s13_codes, layer.s13_scales, layer.s2_codes, layer.s2_scales,
+                 w.shared_inter, 1)
+        sg = _dev(layer.shared_gate, device, torch.bfloat16).contiguous()
+    return DeviceLayer(desc, _dev(layer.w_router, device).contiguous(),
+                       _dev(layer.bias, device) if layer.bias is not None else None, r, s, sg)
+
+
+def decode_fp8(dl: DeviceLayer, x: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+               stream=None, status: Optional[torch.Tensor] = None):
+    """ft_moe_fp8_decode; returns (y, topk_ids, topk_w) on the device."""
+    T = x.shape[0]
+    if workspace is None:
+        workspace = ftmoe.alloc_workspace(dl.desc, T, ftmoe.PATH_DECODE, x.device)
+    y = torch.empty((T, dl.hidden), dtype=torch.bfloat16, device=x.device)
+    ids = torch.empty((T, dl.top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, dl.top_k), dtype=torch.float32, device=x.device)
+    ftmoe.ft_moe_fp8_decode(dl.desc, x, dl.w_router, dl.bias, dl.routed, dl.shared,
+                            dl.shared_gate, y, workspace, ids, w, stream=stream)
+    if status is not None:
+        ftmoe.ft_moe_device_status(workspace, status, stream)
+    return y, ids, w

@@ -48,6 +48,11 @@ class FtNvfp4Experts(ctypes.Structure):
                 ("global_scale", ctypes.c_void_p)]
 
 
+class FtFp8Experts(ctypes.Structure):
+    _fields_ = [("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built; run nvfp4_mixture_experts_amd.build.build() "
@@ -56,6 +61,7 @@ def _load() -> ctypes.CDLL:
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     D = ctypes.POINTER(FtMoeDesc)
     B = ctypes.POINTER(FtNvfp4Experts)
+    F8 = ctypes.POINTER(FtFp8Experts)
     sig = {
         "ft_abi_version": (I32, []),
         "ft_last_error": (ctypes.c_char_p, []),
@@ -72,6 +78,10 @@ def _load() -> ctypes.CDLL:
         "ft_moe_nvfp4_decode_noalloc": (I32, [D, I64, P, P, P, B, B, P, P, P, P, P, P]),
         "ft_moe_nvfp4_decode_slots": (I32, [D, I64, P, P, P, B, I32, P, B, P, P, P, P, P, P,
                                             SZ, P]),
+        "ft_fp8_repacked_bytes": (SZ, [I32, I32, I32, I32]),
+        "ft_fp8_repack": (I32, [I32, I32, I32] + [P] * 8 + [P]),
+        "ft_moe_fp8_decode": (I32, [D, I64, P, P, P, F8, F8, P, P, P, P, P, SZ, P]),
+        "ft_fp8_dequant": (I32, [I32, I32, I32, F8, I32, I32, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -86,7 +96,8 @@ _lib = _load()
 EXPORTED = ("ft_abi_version", "ft_last_error", "ft_init", "ft_nvfp4_repacked_bytes",
             "ft_nvfp4_repack", "ft_moe_workspace_bytes", "ft_moe_route", "ft_moe_nvfp4_decode",
             "ft_moe_nvfp4_prefill", "ft_nvfp4_dequant", "ft_moe_device_status",
-            "ft_set_wait_limit", "ft_moe_nvfp4_decode_noalloc", "ft_moe_nvfp4_decode_slots")
+            "ft_set_wait_limit", "ft_moe_nvfp4_decode_noalloc", "ft_moe_nvfp4_decode_slots",
+            "ft_fp8_repacked_bytes", "ft_fp8_repack", "ft_moe_fp8_decode", "ft_fp8_dequant")
 
 
 def library_path() -> str:
@@ -299,3 +310,59 @@ def ft_moe_nvfp4_decode_slots(desc: FtMoeDesc, x, w_router, bias, slots: Bank, s
         _ptr(topk_w_out, torch.float32, "topk_w_out"), _ptr(miss_out, torch.int32, "miss_out"),
         _ptr(y, torch.bfloat16, "y"), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), _stream(stream)), "ft_moe_nvfp4_decode_slots")
+
+
+# ------------------------------------------------------------- block-fp8 --
+
+class Fp8Bank:
+    """A repacked block-fp8 expert bank (device tensors) and its C view."""
+
+    def __init__(self, hidden: int, inter: int, n: int, w13, w13_scale, w2, w2_scale):
+        self.hidden, self.inter, self.n = hidden, inter, n
+        self.w13, self.w13_scale, self.w2, self.w2_scale = w13, w13_scale, w2, w2_scale
+        self.c = FtFp8Experts(_ptr(w13, torch.uint8, "w13"), _ptr(w13_scale, torch.float32),
+                              _ptr(w2, torch.uint8, "w2"), _ptr(w2_scale, torch.float32))
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def ft_fp8_repacked_bytes(hidden: int, inter: int, n_experts: int, part: int) -> int:
+    return _lib.ft_fp8_repacked_bytes(hidden, inter, n_experts, part)
+
+
+def ft_fp8_repack(hidden: int, inter: int, n_experts: int, w13, w13_scale, w2, w2_scale,
+                  stream=None) -> Fp8Bank:
+    """Repack a canonical block-fp8 bank (device tensors) into newly allocated buffers."""
+    dev = w13.device
+    nb = [ft_fp8_repacked_bytes(hidden, inter, n_experts, p) for p in range(4)]
+    outs = [torch.empty(nb[0], dtype=torch.uint8, device=dev),
+            torch.empty(nb[1] // 4, dtype=torch.float32, device=dev),
+            torch.empty(nb[2], dtype=torch.uint8, device=dev),
+            torch.empty(nb[3] // 4, dtype=torch.float32, device=dev)]
+    _check(_lib.ft_fp8_repack(hidden, inter, n_experts, _ptr(w13, torch.uint8, "w13"),
+                              _ptr(w13_scale, torch.float32, "w13_scale"),
+                              _ptr(w2, torch.uint8, "w2"), _ptr(w2_scale, torch.float32, "w2_scale"),
+                              *[o.data_ptr() for o in outs], _stream(stream)), "ft_fp8_repack")
+    return Fp8Bank(hidden, inter, n_experts, *outs)
+
+
+def ft_moe_fp8_decode(desc: FtMoeDesc, x, w_router, bias, routed: Fp8Bank,
+                      shared: Optional[Fp8Bank], shared_gate, y, workspace, topk_ids_out=None,
+                      topk_w_out=None, stream=None) -> None:
+    _check(_lib.ft_moe_fp8_decode(ctypes.byref(desc), x.shape[0], _ptr(x, torch.bfloat16, "x"),
+                                  _ptr(w_router, torch.float32, "w_router"),
+                                  _ptr(bias, torch.float32, "bias"), routed.ref(),
+                                  shared.ref() if shared is not None else None,
+                                  _ptr(shared_gate, torch.bfloat16, "shared_gate"),
+                                  _ptr(topk_ids_out, torch.int32, "topk_ids_out"),
+                                  _ptr(topk_w_out, torch.float32, "topk_w_out"),
+                                  _ptr(y, torch.bfloat16, "y"),
+                                  _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                  _stream(stream)), "ft_moe_fp8_decode")
+
+
+def ft_fp8_dequant(bank: Fp8Bank, expert: int, tensor: int, out, mode: int = 0,
+                   stream=None) -> None:
+    _check(_lib.ft_fp8_dequant(bank.hidden, bank.inter, bank.n, bank.ref(), expert, tensor, mode,
+                               _ptr(out, torch.float32, "out"), _stream(stream)), "ft_fp8_dequant")
