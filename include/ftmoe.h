@@ -219,6 +219,40 @@ ft_status ft_fp8_dequant(int32_t hidden, int32_t inter, int32_t n_experts,
                          const ft_fp8_experts *bank, int32_t expert, int32_t tensor, int32_t mode,
                          float *out, void *stream);
 
+/* Per-tensor FP8 W8A8 projection (FreeToken commit log, page 2, the paragraph on
+ * row-wise FP8 scaled matrix products: a fused projection stacks parts such as q, k
+ * and v along its output rows, each part with its own per-tensor weight scale; it
+ * runs as one row-wise-scaled GEMM or, as a fallback, one tensor-wise GEMM per part
+ * over its row slice, the parts taken at load time from the run-lengths of the
+ * per-row weight scales).
+ *   s_x = amax|x| / 448 (fp32, correctly rounded; 1 for x == 0)
+ *   xq  = e4m3(x / s_x) (fp32 quotient, round to nearest even)
+ *   y   = bf16( s_x * s_w[n] * sum_k xq[m,k] * w[n,k] ), fp32 accumulation
+ *   x   bf16 [M][K]; w e4m3 [N][K] row-major; y bf16 [M][N]; K % 64 == 0.
+ * ft_fp8_linear_workspace_bytes: device workspace for M x K activations (0 for
+ * unsupported sizes); no zero fill needed; calls sharing one must not overlap.
+ * ft_fp8_quantize: the activation step alone (codes u8 [M][K] and s_x, device).
+ * ft_fp8_linear: the row-wise form, w_scale_rows f32 [N] (device), one GEMM launch.
+ * ft_fp8_linear_parts: the per-part form; part_rows (HOST, [n_parts + 1], 0 first,
+ * strictly increasing, N last) and part_scales (HOST, [n_parts]); one GEMM launch
+ * per part, writing y's columns of that part (row stride N).  Both forms give the
+ * same bits for the same per-row scales.
+ * ft_fp8_scale_runs: HOST helper for load time: splits a host per-row scale vector
+ * into runs of equal bit patterns (part_rows [max_parts + 1], part_scales
+ * [max_parts]); returns the number of parts, or -1 (bad arguments, too many runs). */
+size_t ft_fp8_linear_workspace_bytes(int64_t M, int64_t K);
+ft_status ft_fp8_quantize(int64_t M, int64_t K, const uint16_t *x, uint8_t *xq, float *x_scale,
+                          void *workspace, size_t workspace_bytes, void *stream);
+ft_status ft_fp8_linear(int64_t M, int64_t N, int64_t K, const uint16_t *x, const uint8_t *w,
+                        const float *w_scale_rows, uint16_t *y, void *workspace,
+                        size_t workspace_bytes, void *stream);
+ft_status ft_fp8_linear_parts(int64_t M, int64_t K, const uint16_t *x, const uint8_t *w,
+                              int32_t n_parts, const int64_t *part_rows, const float *part_scales,
+                              uint16_t *y, void *workspace, size_t workspace_bytes,
+                              void *stream);
+int32_t ft_fp8_scale_runs(const float *w_scale_rows, int64_t N, int64_t *part_rows,
+                          float *part_scales, int32_t max_parts);
+
 /* ft_moe_nvfp4_decode with the routed experts held in a bank of expert SLOTS
  * (FreeToken fork PR #84, page 1, the interleaved A/B table: the deployment keeps
  * a fixed number of expert slots and counts expert-cache misses per token;

@@ -596,6 +596,113 @@ ft_status ft_fp8_dequant(int32_t hidden, int32_t inter, int32_t n_experts,
   return ok();
 }
 
+size_t ft_fp8_linear_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K <= 0 || K % 64 || M > (1LL << 30) || K > (1 << 20)) return 0;
+  return fp8_linear_workspace(M, K);
+}
+
+namespace {
+ft_status check_fp8_linear(int64_t M, int64_t K, const uint16_t* x, const uint8_t* w,
+                           const uint16_t* y, void* ws, size_t ws_bytes) {
+  if (M < 0 || K <= 0) return fail(FT_EINVAL, "fp8 linear: M < 0 or K <= 0");
+  if (K % 64 || M > (1LL << 30) || K > (1 << 20) || M * K > (1LL << 34))
+    return fail(FT_EUNSUPPORTED, "fp8 linear: K must be a multiple of 64 (M %lld, K %lld)",
+                static_cast<long long>(M), static_cast<long long>(K));
+  if (!x || !w || !y) return fail(FT_EINVAL, "fp8 linear: NULL pointer");
+  if (!aligned16(x) || !aligned16(w)) return fail(FT_EINVAL, "fp8 linear: x, w must be 16-byte aligned");
+  if (!ws) return fail(FT_EWORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255u)
+    return fail(FT_EWORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = fp8_linear_workspace(M, K);
+  if (ws_bytes < need) return fail(FT_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return FT_OK;
+}
+}  // namespace
+
+ft_status ft_fp8_quantize(int64_t M, int64_t K, const uint16_t* x, uint8_t* xq, float* x_scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  ft_status st = check_fp8_linear(M, K, x, xq, reinterpret_cast<const uint16_t*>(x_scale),
+                                  workspace, workspace_bytes);
+  if (st != FT_OK) return st;
+  if (M == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* q = nullptr;
+  float* sx = nullptr;
+  hipError_t e = launch_fp8_quantize(x, M, K, workspace, &q, &sx, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantise kernels");
+  e = hipMemcpyAsync(xq, q, static_cast<size_t>(M) * K, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(x_scale, sx, sizeof(float), hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantise copy-out");
+  return ok();
+}
+
+ft_status ft_fp8_linear(int64_t M, int64_t N, int64_t K, const uint16_t* x, const uint8_t* w,
+                        const float* w_scale_rows, uint16_t* y, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  ft_status st = check_fp8_linear(M, K, x, w, y, workspace, workspace_bytes);
+  if (st != FT_OK) return st;
+  if (N <= 0 || N > (1 << 30)) return fail(FT_EINVAL, "fp8 linear: N must be in [1, 2^30]");
+  if (!w_scale_rows) return fail(FT_EINVAL, "fp8 linear: w_scale_rows is NULL");
+  if (M == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* q = nullptr;
+  float* sx = nullptr;
+  hipError_t e = launch_fp8_quantize(x, M, K, workspace, &q, &sx, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantise kernels");
+  e = launch_fp8_gemm(q, w, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), sx,
+                      w_scale_rows, 0.0f, y, static_cast<int>(N), 0, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 gemm kernel");
+  return ok();
+}
+
+ft_status ft_fp8_linear_parts(int64_t M, int64_t K, const uint16_t* x, const uint8_t* w,
+                              int32_t n_parts, const int64_t* part_rows, const float* part_scales,
+                              uint16_t* y, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  ft_status st = check_fp8_linear(M, K, x, w, y, workspace, workspace_bytes);
+  if (st != FT_OK) return st;
+  if (n_parts < 1 || !part_rows || !part_scales)
+    return fail(FT_EINVAL, "fp8 linear parts: need n_parts >= 1 and host part arrays");
+  if (part_rows[0] != 0) return fail(FT_EINVAL, "fp8 linear parts: part_rows[0] must be 0");
+  for (int32_t p = 0; p < n_parts; ++p)
+    if (part_rows[p + 1] <= part_rows[p])
+      return fail(FT_EINVAL, "fp8 linear parts: part %d is empty or reversed", p);
+  const int64_t N = part_rows[n_parts];
+  if (N > (1 << 30)) return fail(FT_EINVAL, "fp8 linear parts: too many rows");
+  if (M == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* q = nullptr;
+  float* sx = nullptr;
+  hipError_t e = launch_fp8_quantize(x, M, K, workspace, &q, &sx, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantise kernels");
+  for (int32_t p = 0; p < n_parts; ++p) {
+    const int64_t r0 = part_rows[p], r1 = part_rows[p + 1];
+    e = launch_fp8_gemm(q, w + r0 * K, static_cast<int>(M), static_cast<int>(r1 - r0),
+                        static_cast<int>(K), sx, nullptr, part_scales[p], y, static_cast<int>(N),
+                        static_cast<int>(r0), s);
+    if (e != hipSuccess) return hip_fail(e, "fp8 gemm kernel (part)");
+  }
+  return ok();
+}
+
+int32_t ft_fp8_scale_runs(const float* w_scale_rows, int64_t N, int64_t* part_rows,
+                          float* part_scales, int32_t max_parts) {
+  if (!w_scale_rows || N <= 0 || !part_rows || !part_scales || max_parts < 1) return -1;
+  int32_t n = 0;
+  part_rows[0] = 0;
+  for (int64_t r = 0; r < N; ++r) {
+    const bool starts = r == 0 || std::memcmp(&w_scale_rows[r], &w_scale_rows[r - 1], 4) != 0;
+    if (starts) {
+      if (n == max_parts) return -1;
+      part_scales[n] = w_scale_rows[r];
+      if (n > 0) part_rows[n] = r;
+      ++n;
+    }
+  }
+  part_rows[n] = N;
+  return n;
+}
+
 ft_status ft_moe_nvfp4_prefill(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,
                                const int32_t* topk_ids, const float* topk_w,
                                const ft_nvfp4_experts* routed, const ft_nvfp4_experts* shared,

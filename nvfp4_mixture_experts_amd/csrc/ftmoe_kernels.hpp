@@ -122,6 +122,15 @@ hipError_t launch_repack_w2(int H, int I, int n, const uint8_t* w2, const uint8_
                             uint8_t* out_w2, uint8_t* out_w2s, hipStream_t s);
 hipError_t launch_dequant(int H, int I, const Bank& b, int expert, int tensor, int out_dtype,
                           void* out, hipStream_t s);
+// per-tensor FP8 W8A8 linear: workspace bytes (codes, amax partials, scale), the
+// activation quantisation (sets *xq and *s_x to their places in ws) and the GEMM
+// (row_scale [N] when set, else `scale` for every row; y columns col0.. of stride ldy)
+size_t fp8_linear_workspace(int64_t M, int64_t K);
+hipError_t launch_fp8_quantize(const uint16_t* x, int64_t M, int64_t K, void* ws, uint8_t** xq,
+                               float** s_x, hipStream_t s);
+hipError_t launch_fp8_gemm(const uint8_t* xq, const uint8_t* w, int M, int N, int K,
+                           const float* s_x, const float* row_scale, float scale, uint16_t* y,
+                           int ldy, int col0, hipStream_t s);
 // block-fp8 banks (Bank.w13s / w2s hold fp32 block scales; gsc unused)
 hipError_t launch_repack_fp8_w2(int H, int I, int n, const uint8_t* w2, uint8_t* out_w2,
                                 hipStream_t s);

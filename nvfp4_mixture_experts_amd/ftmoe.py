@@ -82,6 +82,11 @@ def _load() -> ctypes.CDLL:
         "ft_fp8_repack": (I32, [I32, I32, I32] + [P] * 8 + [P]),
         "ft_moe_fp8_decode": (I32, [D, I64, P, P, P, F8, F8, P, P, P, P, P, SZ, P]),
         "ft_fp8_dequant": (I32, [I32, I32, I32, F8, I32, I32, I32, P, P]),
+        "ft_fp8_linear_workspace_bytes": (SZ, [I64, I64]),
+        "ft_fp8_quantize": (I32, [I64, I64, P, P, P, P, SZ, P]),
+        "ft_fp8_linear": (I32, [I64, I64, I64, P, P, P, P, P, SZ, P]),
+        "ft_fp8_linear_parts": (I32, [I64, I64, P, P, I32, P, P, P, P, SZ, P]),
+        "ft_fp8_scale_runs": (I32, [P, I64, P, P, I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -97,7 +102,9 @@ EXPORTED = ("ft_abi_version", "ft_last_error", "ft_init", "ft_nvfp4_repacked_byt
             "ft_nvfp4_repack", "ft_moe_workspace_bytes", "ft_moe_route", "ft_moe_nvfp4_decode",
             "ft_moe_nvfp4_prefill", "ft_nvfp4_dequant", "ft_moe_device_status",
             "ft_set_wait_limit", "ft_moe_nvfp4_decode_noalloc", "ft_moe_nvfp4_decode_slots",
-            "ft_fp8_repacked_bytes", "ft_fp8_repack", "ft_moe_fp8_decode", "ft_fp8_dequant")
+            "ft_fp8_repacked_bytes", "ft_fp8_repack", "ft_moe_fp8_decode", "ft_fp8_dequant",
+            "ft_fp8_linear_workspace_bytes", "ft_fp8_quantize", "ft_fp8_linear",
+            "ft_fp8_linear_parts", "ft_fp8_scale_runs")
 
 
 def library_path() -> str:
@@ -366,3 +373,55 @@ def ft_fp8_dequant(bank: Fp8Bank, expert: int, tensor: int, out, mode: int = 0,
                    stream=None) -> None:
     _check(_lib.ft_fp8_dequant(bank.hidden, bank.inter, bank.n, bank.ref(), expert, tensor, mode,
                                _ptr(out, torch.float32, "out"), _stream(stream)), "ft_fp8_dequant")
+
+
+# ------------------------------------------------ per-tensor FP8 W8A8 linear --
+
+def fp8_linear_workspace(M: int, K: int, device="cuda") -> torch.Tensor:
+    n = _lib.ft_fp8_linear_workspace_bytes(M, K)
+    if n == 0:
+        raise FtError(FT_EUNSUPPORTED, "ft_fp8_linear_workspace_bytes", f"M={M} K={K}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def ft_fp8_quantize(x, xq, x_scale, workspace, stream=None) -> None:
+    M, K = x.shape
+    _check(_lib.ft_fp8_quantize(M, K, _ptr(x, torch.bfloat16, "x"), _ptr(xq, torch.uint8, "xq"),
+                                _ptr(x_scale, torch.float32, "x_scale"),
+                                _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                _stream(stream)), "ft_fp8_quantize")
+
+
+def ft_fp8_linear(x, w, w_scale_rows, y, workspace, stream=None) -> None:
+    M, K = x.shape
+    N = w.shape[0]
+    _check(_lib.ft_fp8_linear(M, N, K, _ptr(x, torch.bfloat16, "x"), _ptr(w, torch.uint8, "w"),
+                              _ptr(w_scale_rows, torch.float32, "w_scale_rows"),
+                              _ptr(y, torch.bfloat16, "y"), _ptr(workspace, torch.uint8,
+                                                                 "workspace"),
+                              workspace.numel(), _stream(stream)), "ft_fp8_linear")
+
+
+def ft_fp8_scale_runs(w_scale_rows, max_parts: int = 64):
+    """Host: (part_rows int64 [n + 1], part_scales float32 [n]) of a host scale vector."""
+    import numpy as np
+    rows = np.ascontiguousarray(np.asarray(w_scale_rows, dtype=np.float32))
+    pr = np.zeros(max_parts + 1, np.int64)
+    ps = np.zeros(max_parts, np.float32)
+    n = _lib.ft_fp8_scale_runs(rows.ctypes.data, rows.size, pr.ctypes.data, ps.ctypes.data,
+                               max_parts)
+    if n < 0:
+        raise FtError(FT_EINVAL, "ft_fp8_scale_runs", "bad arguments or too many runs")
+    return pr[:n + 1].copy(), ps[:n].copy()
+
+
+def ft_fp8_linear_parts(x, w, part_rows, part_scales, y, workspace, stream=None) -> None:
+    import numpy as np
+    M, K = x.shape
+    pr = np.ascontiguousarray(np.asarray(part_rows, dtype=np.int64))
+    ps = np.ascontiguousarray(np.asarray(part_scales, dtype=np.float32))
+    _check(_lib.ft_fp8_linear_parts(M, K, _ptr(x, torch.bfloat16, "x"), _ptr(w, torch.uint8, "w"),
+                                    len(ps), pr.ctypes.data, ps.ctypes.data,
+                                    _ptr(y, torch.bfloat16, "y"),
+                                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                    _stream(stream)), "ft_fp8_linear_parts")
