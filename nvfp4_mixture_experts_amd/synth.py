@@ -356,3 +356,39 @@ def make_layer_device(w: Workload, instance: int, device):
         out["shared_gate"] = (torch.randn(H, generator=gen, device=device)
                               * w.shared_gate_std).to(torch.bfloat16)
     return out
+
+
+# ------------------------------------------------- extend attention cases --
+
+# e4m3 bytes of magnitude at most 15 (exponent field <= 10), both signs, no NaN
+FP8_CACHE_BYTES = np.array([b for b in range(256) if ((b >> 3) & 15) <= 10], dtype=np.uint8)
+
+
+def make_attn_case(fmt: int, head_dim: int, prefix: int, n_new: int = 24, q_heads: int = 8,
+                   kv_heads: int = 2, seed: int = 3000) -> dict:
+    """One sequence for extend attention: q, k_new, v_new (bf16 bits, N(0, 1)) and a
+    cached prefix in format ``fmt`` (0 bf16 N(0, 1); 1 e4m3 bytes uniform over the
+    magnitudes <= 15 with tensor scales 1/8; 2 NVFP4: uniform codes, e4m3 block
+    scales 2^U{-4..0}, tensor scales 1/4)."""
+    rng = _rng(seed + 97 * fmt + 7 * head_dim + prefix, "attn")
+    d, Hq, Hkv = head_dim, q_heads, kv_heads
+
+    def bf16(shape):
+        return bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32))
+
+    case = {"q": bf16((n_new, Hq, d)), "k_new": bf16((n_new, Hkv, d)),
+            "v_new": bf16((n_new, Hkv, d)), "cache": {"format": fmt, "prefix": prefix}}
+    c = case["cache"]
+    if fmt == 0:
+        c["k"], c["v"] = bf16((prefix, Hkv, d)), bf16((prefix, Hkv, d))
+    elif fmt == 1:
+        pick = lambda: FP8_CACHE_BYTES[rng.integers(0, len(FP8_CACHE_BYTES), (prefix, Hkv, d))]
+        c["k"], c["v"] = pick(), pick()
+        c["k_scale"], c["v_scale"] = 0.125, 0.125
+    else:
+        codes = lambda: _codes(rng, (prefix, Hkv, d // 2))
+        bscale = lambda: SCALE_BYTES[rng.integers(0, 5, (prefix, Hkv, d // 16))]
+        c["k"], c["v"] = codes(), codes()
+        c["k_bscale"], c["v_bscale"] = bscale(), bscale()
+        c["k_scale"], c["v_scale"] = 0.25, 0.25
+    return case

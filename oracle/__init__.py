@@ -100,6 +100,9 @@ def _load(omp: bool = False):
     lib.or_fp8_quantize.argtypes = [_I64, _I64, _P, _P, _P]
     lib.or_fp8_linear.restype = None
     lib.or_fp8_linear.argtypes = [_I64, _I64, _I64, _P, _F32, _P, _P, _P, _P]
+    lib.or_attn_extend.restype = _I32
+    lib.or_attn_extend.argtypes = ([_I32] * 6 + [_P] * 3 + [_I32] + [_P] * 4 + [_F32, _F32]
+                                   + [_P, _P])
     _libs[omp] = lib
     return lib
 
@@ -362,3 +365,34 @@ def fp8_linear(xq: np.ndarray, s_x: float, w: np.ndarray, w_scale_rows: np.ndarr
     _load(openmp).or_fp8_linear(M, N, K, _ptr(xq), float(s_x), _ptr(w), _ptr(ws), _ptr(y64),
                                 _ptr(y))
     return {"y64": y64, "y": y}
+
+
+# ---------------------------------------------------- extend attention, cache --
+
+def attn_extend(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, cache: dict,
+                window: int = 0, openmp: bool = False) -> dict:
+    """Extend attention of n_new query tokens over a cached prefix and the new tokens.
+    q bf16 bits u16 [n_new, Hq, d]; k_new, v_new u16 [n_new, Hkv, d]; ``cache`` =
+    {"format": 0|1|2, "prefix": P, "k", "v" (codes), "k_bscale", "v_bscale" (NVFP4),
+    "k_scale", "v_scale"} (see the C source for the layouts).  Returns {"out64", "out"}
+    of shape [n_new, Hq, d]."""
+    q = _c(q, np.uint16)
+    k_new = _c(k_new, np.uint16)
+    v_new = _c(v_new, np.uint16)
+    n_new, Hq, d = q.shape
+    Hkv = k_new.shape[1]
+    fmt = int(cache["format"])
+    dt = np.uint16 if fmt == 0 else np.uint8
+    kc = _c(cache["k"], dt)
+    vc = _c(cache["v"], dt)
+    kb = _c(cache.get("k_bscale"), np.uint8)
+    vb = _c(cache.get("v_bscale"), np.uint8)
+    out64 = np.empty((n_new, Hq, d), np.float64)
+    out = np.empty((n_new, Hq, d), np.uint16)
+    rc = _load(openmp).or_attn_extend(n_new, int(cache["prefix"]), Hq, Hkv, d, int(window),
+                                      _ptr(q), _ptr(k_new), _ptr(v_new), fmt, _ptr(kc), _ptr(vc),
+                                      _ptr(kb), _ptr(vb), float(cache.get("k_scale", 1.0)),
+                                      float(cache.get("v_scale", 1.0)), _ptr(out64), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the attention shape")
+    return {"out64": out64, "out": out}

@@ -675,3 +675,102 @@ void or_fp8_linear(int64_t M, int64_t N, int64_t K, const uint8_t *xq, float s_x
         }
     }
 }
+
+/* ------------------------------------------------ extend attention, KV cache -- */
+
+/* FreeToken fork PR #84 (page 1), the bullet on the extend-attention kernel of the
+ * NVFP4 KV-cache step: new (extend) query tokens attend to a cached prefix held as a
+ * 16-bit, fp8 or NVFP4 cache, and to the new tokens themselves; the quantised-cache
+ * tile applies the fp8 scales to the dot outputs, and the check is against a
+ * dequantised-cache reference with head dims 64 and 128, prefixes 37, 200 and 1000,
+ * and windows 0 and 100.  This is that reference, written out plainly in binary64.
+ * Readings taken here:
+ *  - one sequence; q [n_new][Hq][d], new keys / values [n_new][Hkv][d] (bf16); query
+ *    head h reads kv head h / (Hq / Hkv);
+ *  - cache of `prefix` positions, [prefix][Hkv][d] per K and V:
+ *      format 0: bf16;
+ *      format 1: e4m3 bytes, one fp32 scale per tensor (k_scale, v_scale);
+ *      format 2: NVFP4: e2m1 codes [prefix][Hkv][d/2] (low nibble = even element),
+ *                one e4m3 scale per 16 elements [prefix][Hkv][d/16], and one fp32
+ *                scale per tensor (k_scale, v_scale);
+ *    a cached value is code (x block scale) x tensor scale, exact in binary64;
+ *  - positions: cache entry j is at j, new token t at prefix + t; query t sees key
+ *    position p iff p <= prefix + t and (window == 0 or prefix + t - p < window);
+ *  - scores (q . k) / sqrt(d), softmax over the visible keys, out = sum p v / sum p,
+ *    rounded once to bf16. */
+static double kv_value(int32_t format, const void *codes, const uint8_t *bscale, float tscale,
+                       int64_t pos, int32_t Hkv, int32_t d, int32_t kh, int32_t i)
+{
+    int64_t row = pos * Hkv + kh;
+    if (format == 0)
+        return or_bf16_to_double(((const uint16_t *)codes)[row * d + i]);
+    if (format == 1)
+        return or_e4m3(((const uint8_t *)codes)[row * d + i]) * (double)tscale;
+    uint8_t b = ((const uint8_t *)codes)[row * (d / 2) + i / 2];
+    uint32_t c = (i % 2 == 0) ? (uint32_t)(b & 0x0F) : (uint32_t)(b >> 4);
+    return or_e2m1(c) * or_e4m3(bscale[row * (d / 16) + i / 16]) * (double)tscale;
+}
+
+int32_t or_attn_extend(int32_t n_new, int32_t prefix, int32_t Hq, int32_t Hkv, int32_t d,
+                       int32_t window, const uint16_t *q, const uint16_t *k_new,
+                       const uint16_t *v_new, int32_t format, const void *k_cache,
+                       const void *v_cache, const uint8_t *k_bscale, const uint8_t *v_bscale,
+                       float k_scale, float v_scale, double *out64, uint16_t *out)
+{
+    if (n_new < 0 || prefix < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0 || d % 16 ||
+        window < 0 || format < 0 || format > 2)
+        return -1;
+    int32_t group = Hq / Hkv;
+    int64_t P = (int64_t)prefix + n_new;
+    double scale = 1.0 / sqrt((double)d);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int32_t t = 0; t < n_new; ++t) {
+        for (int32_t h = 0; h < Hq; ++h) {
+            int32_t kh = h / group;
+            int64_t qpos = (int64_t)prefix + t;
+            double *s = (double *)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1));
+            double smax = -INFINITY;
+            for (int64_t p = 0; p < P; ++p) {
+                int visible = p <= qpos && (window == 0 || qpos - p < window);
+                if (!visible) {
+                    s[p] = -INFINITY;
+                    continue;
+                }
+                double dot = 0.0;
+                for (int32_t i = 0; i < d; ++i) {
+                    double kv = p < prefix
+                                    ? kv_value(format, k_cache, k_bscale, k_scale, p, Hkv, d, kh, i)
+                                    : or_bf16_to_double(k_new[((p - prefix) * Hkv + kh) * d + i]);
+                    dot += or_bf16_to_double(q[((int64_t)t * Hq + h) * d + i]) * kv;
+                }
+                s[p] = dot * scale;
+                if (s[p] > smax)
+                    smax = s[p];
+            }
+            double l = 0.0;
+            for (int64_t p = 0; p < P; ++p) {
+                s[p] = (s[p] == -INFINITY) ? 0.0 : exp(s[p] - smax);
+                l += s[p];
+            }
+            for (int32_t i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int64_t p = 0; p < P; ++p) {
+                    if (s[p] == 0.0)
+                        continue;
+                    double vv = p < prefix
+                                    ? kv_value(format, v_cache, v_bscale, v_scale, p, Hkv, d, kh, i)
+                                    : or_bf16_to_double(v_new[((p - prefix) * Hkv + kh) * d + i]);
+                    acc += s[p] * vv;
+                }
+                double o = acc / l;
+                int64_t idx = ((int64_t)t * Hq + h) * d + i;
+                if (out64)
+                    out64[idx] = o;
+                if (out)
+                    out[idx] = or_bf16_from_double(o);
+            }
+            free(s);
+        }
+    }
+    return 0;
+}

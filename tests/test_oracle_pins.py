@@ -662,3 +662,75 @@ def test_fp8_linear_equals_exact_matmul_and_per_part_concatenation():
         parts.append(oracle.fp8_linear(xq, s_x, lin.w[r0:r1],
                                        np.full(r1 - r0, sc, np.float32))["y"])
     assert np.array_equal(np.concatenate(parts, axis=1), got["y"])
+
+
+# ---------------------------------------------- extend attention over a cache --
+
+def _cache_values(cache, key, Hkv, d):
+    """Dequantised cache K or V [P, Hkv, d] in fp64, from torch / numpy tables."""
+    c = cache[key]
+    if cache["format"] == 0:
+        return _bf16_to_f64(c)
+    if cache["format"] == 1:
+        dec = torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn).to(
+            torch.float64).numpy()
+        return dec * cache[key + "_scale"]
+    nib = np.empty(c.shape[:-1] + (d,), np.int64)
+    nib[..., 0::2] = c & 0x0F
+    nib[..., 1::2] = c >> 4
+    bs = E4M3[np.repeat(cache[key + "_bscale"], 16, axis=-1)]
+    return E2M1[nib] * bs * cache[key + "_scale"]
+
+
+def _sdpa_reference(case, window):
+    """torch's scaled_dot_product_attention in fp64 over [cache; new] with the visible
+    set as a boolean mask (key p visible to query t iff p <= P + t and, with a
+    window, P + t - p < window); kv heads repeated for the query-head groups."""
+    q = _bf16_to_f64(case["q"])
+    n_new, Hq, d = q.shape
+    Hkv = case["k_new"].shape[1]
+    P = case["cache"]["prefix"]
+    k = np.concatenate([_cache_values(case["cache"], "k", Hkv, d), _bf16_to_f64(case["k_new"])])
+    v = np.concatenate([_cache_values(case["cache"], "v", Hkv, d), _bf16_to_f64(case["v_new"])])
+    rep = Hq // Hkv
+    kt = torch.from_numpy(np.repeat(k, rep, axis=1)).permute(1, 0, 2)
+    vt = torch.from_numpy(np.repeat(v, rep, axis=1)).permute(1, 0, 2)
+    qt = torch.from_numpy(q).permute(1, 0, 2)
+    pos_q = P + np.arange(n_new)[:, None]
+    pos_k = np.arange(P + n_new)[None, :]
+    vis = pos_k <= pos_q
+    if window:
+        vis &= (pos_q - pos_k) < window
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt,
+                                                           attn_mask=torch.from_numpy(vis))
+    return out.permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("window", [0, 7])
+def test_attn_extend_equals_sdpa_over_dequantised_cache(fmt, window):
+    case = synth.make_attn_case(fmt, 64, prefix=37, n_new=9)
+    got = oracle.attn_extend(case["q"], case["k_new"], case["v_new"], case["cache"], window)
+    want = _sdpa_reference(case, window)
+    assert np.abs(got["out64"] - want).max() <= 1e-12 * np.abs(want).max()
+
+
+def test_attn_extend_without_prefix_is_library_causal_attention():
+    case = synth.make_attn_case(0, 64, prefix=0, n_new=11)
+    got = oracle.attn_extend(case["q"], case["k_new"], case["v_new"], case["cache"], 0)
+    q = torch.from_numpy(_bf16_to_f64(case["q"])).permute(1, 0, 2)
+    k = torch.from_numpy(np.repeat(_bf16_to_f64(case["k_new"]), 4, axis=1)).permute(1, 0, 2)
+    v = torch.from_numpy(np.repeat(_bf16_to_f64(case["v_new"]), 4, axis=1)).permute(1, 0, 2)
+    want = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+    assert np.allclose(got["out64"], want.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_attn_extend_window_special_cases():
+    case = synth.make_attn_case(2, 128, prefix=20, n_new=6)
+    args = (case["q"], case["k_new"], case["v_new"], case["cache"])
+    one = oracle.attn_extend(*args, window=1)      # each query sees only itself
+    v_self = np.repeat(_bf16_to_f64(case["v_new"]), 4, axis=1)
+    assert np.array_equal(one["out64"], v_self)
+    a = oracle.attn_extend(*args, window=0)
+    b = oracle.attn_extend(*args, window=1000)     # wider than every sequence position
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["out64"], b["out64"])
