@@ -103,6 +103,17 @@ typedef struct ft_fp8_experts {
     const float *w2_scale;    /* f32 [n][H/128][I/128] block scales */
 } ft_fp8_experts;
 
+/* A KV-cache prefix of one sequence for ft_attn_extend. */
+typedef struct ft_kv_cache {
+    int32_t format;                 /* 0 bf16, 1 fp8 (e4m3), 2 NVFP4 */
+    int32_t prefix;                 /* cached positions (0 = none) */
+    const void *k, *v;              /* bf16 [prefix][Hkv][d] | u8 [prefix][Hkv][d] |
+                                       e2m1 codes u8 [prefix][Hkv][d/2] (low nibble first) */
+    const uint8_t *k_block_scale;   /* NVFP4: e4m3 [prefix][Hkv][d/16]; else unused */
+    const uint8_t *v_block_scale;
+    float k_scale, v_scale;         /* fp8 / NVFP4: per-tensor scales; bf16: unused */
+} ft_kv_cache;
+
 /* FT_ABI_VERSION of the library that was loaded. */
 int32_t ft_abi_version(void);
 
@@ -252,6 +263,23 @@ ft_status ft_fp8_linear_parts(int64_t M, int64_t K, const uint16_t *x, const uin
                               void *stream);
 int32_t ft_fp8_scale_runs(const float *w_scale_rows, int64_t N, int64_t *part_rows,
                           float *part_scales, int32_t max_parts);
+
+/* Extend attention over a quantised KV cache (FreeToken fork PR #84, page 1, the
+ * bullet on the extend-attention kernel of the NVFP4 KV-cache step: the cache loops
+ * use a quantised twin of the attention tile with the per-tensor scales on the dot
+ * outputs and the softmax normaliser over the unscaled probabilities; the loops over
+ * the new tokens stay 16-bit).  For one sequence: n_new query tokens at positions
+ * prefix .. prefix + n_new - 1 attend to the cached positions and to the new tokens,
+ * key position p visible to query position t iff p <= t and (window == 0 or
+ * t - p < window); scores q.k / sqrt(head_dim); query head h reads kv head
+ * h / (q_heads / kv_heads).  A cached value is code x tensor scale (fp8) or
+ * e2m1 code x e4m3 block scale x tensor scale (NVFP4).
+ *   q bf16 [n_new][q_heads][d]; k_new, v_new bf16 [n_new][kv_heads][d];
+ *   out bf16 [n_new][q_heads][d]; head_dim 64 or 128. */
+ft_status ft_attn_extend(int32_t n_new, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                         int32_t window, const uint16_t *q, const uint16_t *k_new,
+                         const uint16_t *v_new, const ft_kv_cache *cache, uint16_t *out,
+                         void *stream);
 
 /* ft_moe_nvfp4_decode with the routed experts held in a bank of expert SLOTS
  * (FreeToken fork PR #84, page 1, the interleaved A/B table: the deployment keeps

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <cmath>
 
 #include "abi_internal.hpp"
 #include "ftmoe.h"
@@ -701,6 +702,54 @@ int32_t ft_fp8_scale_runs(const float* w_scale_rows, int64_t N, int64_t* part_ro
   }
   part_rows[n] = N;
   return n;
+}
+
+ft_status ft_attn_extend(int32_t n_new, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                         int32_t window, const uint16_t* q, const uint16_t* k_new,
+                         const uint16_t* v_new, const ft_kv_cache* cache, uint16_t* out,
+                         void* stream) {
+  if (n_new < 0 || window < 0 || q_heads <= 0 || kv_heads <= 0 || q_heads % kv_heads)
+    return fail(FT_EINVAL, "attn: bad n_new / window / head counts");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FT_EUNSUPPORTED, "attn: head_dim %d (64 or 128)", head_dim);
+  if (!cache) return fail(FT_EINVAL, "attn: cache is NULL");
+  if (cache->prefix < 0 || cache->format < 0 || cache->format > 2)
+    return fail(FT_EINVAL, "attn: bad cache prefix or format");
+  if (static_cast<int64_t>(n_new) * q_heads > (1LL << 30) || cache->prefix > (1 << 28))
+    return fail(FT_EUNSUPPORTED, "attn: too many tokens");
+  if (n_new == 0) return ok();
+  if (!q || !k_new || !v_new || !out) return fail(FT_EINVAL, "attn: NULL pointer");
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+    return fail(FT_EINVAL, "attn: q, k_new, v_new and out must be 16-byte aligned");
+  if (cache->prefix > 0) {
+    if (!cache->k || !cache->v) return fail(FT_EINVAL, "attn: cache k / v NULL");
+    if (!aligned16(cache->k) || !aligned16(cache->v))
+      return fail(FT_EINVAL, "attn: cache k / v must be 16-byte aligned");
+    if (cache->format == 2 && (!cache->k_block_scale || !cache->v_block_scale))
+      return fail(FT_EINVAL, "attn: NVFP4 cache needs its block scales");
+  }
+  AttnParams p{};
+  p.n_new = n_new;
+  p.prefix = cache->prefix;
+  p.Hq = q_heads;
+  p.Hkv = kv_heads;
+  p.D = head_dim;
+  p.window = window;
+  p.format = cache->format;
+  p.q = q;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_cache = cache->k;
+  p.v_cache = cache->v;
+  p.k_bscale = cache->k_block_scale;
+  p.v_bscale = cache->v_block_scale;
+  p.k_scale = cache->k_scale;
+  p.v_scale = cache->v_scale;
+  p.sm_scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(head_dim)));
+  p.out = out;
+  hipError_t e = launch_attn_extend(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  return ok();
 }
 
 ft_status ft_moe_nvfp4_prefill(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x,

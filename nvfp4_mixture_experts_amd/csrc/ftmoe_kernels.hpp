@@ -131,6 +131,22 @@ hipError_t launch_fp8_quantize(const uint16_t* x, int64_t M, int64_t K, void* ws
 hipError_t launch_fp8_gemm(const uint8_t* xq, const uint8_t* w, int M, int N, int K,
                            const float* s_x, const float* row_scale, float scale, uint16_t* y,
                            int ldy, int col0, hipStream_t s);
+// extend attention over a KV-cache prefix (format 0 bf16, 1 e4m3, 2 NVFP4) and the
+// new tokens (bf16), causal, optional window
+struct AttnParams {
+  int n_new, prefix, Hq, Hkv, D, window, format;
+  const uint16_t* q;        // [n_new][Hq][D]
+  const uint16_t* k_new;    // [n_new][Hkv][D]
+  const uint16_t* v_new;
+  const void* k_cache;      // [prefix][Hkv][D] bf16 / e4m3, or [prefix][Hkv][D/2] e2m1
+  const void* v_cache;
+  const uint8_t* k_bscale;  // NVFP4: e4m3 [prefix][Hkv][D/16]
+  const uint8_t* v_bscale;
+  float k_scale, v_scale;   // fp8 / NVFP4 tensor scales (on the dot outputs)
+  float sm_scale;           // 1 / sqrt(D)
+  uint16_t* out;            // [n_new][Hq][D]
+};
+hipError_t launch_attn_extend(const AttnParams& p, hipStream_t s);
 // block-fp8 banks (Bank.w13s / w2s hold fp32 block scales; gsc unused)
 hipError_t launch_repack_fp8_w2(int H, int I, int n, const uint8_t* w2, uint8_t* out_w2,
                                 hipStream_t s);

@@ -53,6 +53,13 @@ class FtFp8Experts(ctypes.Structure):
                 ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
 
 
+class FtKvCache(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("prefix", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_block_scale", ctypes.c_void_p), ("v_block_scale", ctypes.c_void_p),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built; run nvfp4_mixture_experts_amd.build.build() "
@@ -87,6 +94,8 @@ def _load() -> ctypes.CDLL:
         "ft_fp8_linear": (I32, [I64, I64, I64, P, P, P, P, P, SZ, P]),
         "ft_fp8_linear_parts": (I32, [I64, I64, P, P, I32, P, P, P, P, SZ, P]),
         "ft_fp8_scale_runs": (I32, [P, I64, P, P, I32]),
+        "ft_attn_extend": (I32, [I32, I32, I32, I32, I32, P, P, P,
+                                 ctypes.POINTER(FtKvCache), P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -104,7 +113,7 @@ EXPORTED = ("ft_abi_version", "ft_last_error", "ft_init", "ft_nvfp4_repacked_byt
             "ft_set_wait_limit", "ft_moe_nvfp4_decode_noalloc", "ft_moe_nvfp4_decode_slots",
             "ft_fp8_repacked_bytes", "ft_fp8_repack", "ft_moe_fp8_decode", "ft_fp8_dequant",
             "ft_fp8_linear_workspace_bytes", "ft_fp8_quantize", "ft_fp8_linear",
-            "ft_fp8_linear_parts", "ft_fp8_scale_runs")
+            "ft_fp8_linear_parts", "ft_fp8_scale_runs", "ft_attn_extend")
 
 
 def library_path() -> str:
@@ -425,3 +434,23 @@ def ft_fp8_linear_parts(x, w, part_rows, part_scales, y, workspace, stream=None)
                                     _ptr(y, torch.bfloat16, "y"),
                                     _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                     _stream(stream)), "ft_fp8_linear_parts")
+
+
+# -------------------------------------------------- extend attention, KV cache --
+
+def ft_attn_extend(q, k_new, v_new, cache_format: int, prefix: int, k_cache, v_cache, out,
+                   window: int = 0, k_block_scale=None, v_block_scale=None, k_scale: float = 1.0,
+                   v_scale: float = 1.0, stream=None) -> None:
+    """q bf16 [n_new, Hq, d]; k_new / v_new bf16 [n_new, Hkv, d]; cache tensors as in
+    include/ftmoe.h (None when prefix == 0); out bf16 [n_new, Hq, d]."""
+    n_new, Hq, d = q.shape
+    Hkv = k_new.shape[1]
+    cdt = torch.bfloat16 if cache_format == 0 else torch.uint8
+    c = FtKvCache(cache_format, prefix, _ptr(k_cache, cdt, "k_cache"), _ptr(v_cache, cdt, "v_cache"),
+                  _ptr(k_block_scale, torch.uint8, "k_block_scale"),
+                  _ptr(v_block_scale, torch.uint8, "v_block_scale"), k_scale, v_scale)
+    _check(_lib.ft_attn_extend(n_new, Hq, Hkv, d, window, _ptr(q, torch.bfloat16, "q"),
+                               _ptr(k_new, torch.bfloat16, "k_new"),
+                               _ptr(v_new, torch.bfloat16, "v_new"), ctypes.byref(c),
+                               _ptr(out, torch.bfloat16, "out"), _stream(stream)),
+           "ft_attn_extend")
