@@ -137,25 +137,39 @@ def prefill(dl: DeviceLayer, x: torch.Tensor, ids: torch.Tensor, w: torch.Tensor
     return y
 
 
+def upload_fp8_canonical(w, w_router, bias, routed: dict, shared: Optional[dict], shared_gate,
+                         device="cuda") -> DeviceLayer:
+    """Block-fp8 banks given as dicts of canonical arrays or device tensors (w13_codes,
+    w13_scales, w2_codes, w2_scales), repacked with ft_fp8_repack."""
+    desc = desc_of(w)
+
+    def bank(b, inter, n):
+        d = lambda a: _dev(a, device).contiguous()
+        return ftmoe.ft_fp8_repack(w.hidden, inter, n, d(b["w13_codes"]),
+                                   d(b["w13_scales"]).float(), d(b["w2_codes"]),
+                                   d(b["w2_scales"]).float())
+
+    r = bank(routed, w.inter, w.num_experts)
+    s = bank(shared, w.shared_inter, 1) if shared is not None else None
+    sg = _dev(shared_gate, device, torch.bfloat16) if shared_gate is not None else None
+    if sg is not None and sg.dtype != torch.bfloat16:
+        sg = sg.view(torch.bfloat16)
+    return DeviceLayer(desc, _dev(w_router, device).contiguous(),
+                       _dev(bias, device) if bias is not None else None, r, s,
+                       sg.contiguous() if sg is not None else None)
+
+
 def upload_fp8_layer(layer, device="cuda") -> DeviceLayer:
     """Upload a host ``synth.Fp8Layer`` (block-fp8 banks, repacked with ft_fp8_repack)."""
     w = layer.workload
-    desc = desc_of(w)
-
-    def bank(c13, s13, c2, s2, inter, n):
-        d = lambda a: _dev(a, device).contiguous()
-        return ftmoe.ft_fp8_repack(w.hidden, inter, n, d(c13), d(s13), d(c2), d(s2))
-
-    r = bank(layer.w13_codes, layer.w13_scales, layer.w2_codes, layer.w2_scales, w.inter,
-             w.num_experts)
-    s = None
-    sg = None
+    routed = dict(w13_codes=layer.w13_codes, w13_scales=layer.w13_scales,
+                  w2_codes=layer.w2_codes, w2_scales=layer.w2_scales)
+    shared = None
     if w.shared_inter > 0:
-        s = bank(layer.s13_codes, layer.s13_scales, layer.s2_codes, layer.s2_scales,
-                 w.shared_inter, 1)
-        sg = _dev(layer.shared_gate, device, torch.bfloat16).contiguous()
-    return DeviceLayer(desc, _dev(layer.w_router, device).contiguous(),
-                       _dev(layer.bias, device) if layer.bias is not None else None, r, s, sg)
+        shared = dict(w13_codes=layer.s13_codes, w13_scales=layer.s13_scales,
+                      w2_codes=layer.s2_codes, w2_scales=layer.s2_scales)
+    return upload_fp8_canonical(w, layer.w_router, layer.bias, routed, shared, layer.shared_gate,
+                                device)
 
 
 def decode_fp8(dl: DeviceLayer, x: torch.Tensor, workspace: Optional[torch.Tensor] = None,

@@ -392,3 +392,33 @@ def make_attn_case(fmt: int, head_dim: int, prefix: int, n_new: int = 24, q_head
         c["k_bscale"], c["v_bscale"] = bscale(), bscale()
         c["k_scale"], c["v_scale"] = 0.25, 0.25
     return case
+
+
+
+def make_fp8_layer_device(w: Workload, instance: int, device):
+    """A block-fp8 layer instance drawn on the device (torch's generator; the same
+    distributions as make_fp8_layer, different draws): canonical tensors."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed + 7919 * instance)
+    E, H, I = w.num_experts, w.hidden, w.inter
+    table = torch.tensor(FP8_FINITE_BYTES, dtype=torch.uint8, device=device)
+
+    def codes(shape):
+        return table[torch.randint(0, len(FP8_FINITE_BYTES), shape, generator=gen, device=device)]
+
+    def scales(shape):
+        return (2.0 ** -11) * (1 + torch.rand(shape, generator=gen, device=device))
+
+    def bank(n, inter):
+        return dict(w13_codes=codes((n, 2 * inter, H)),
+                    w13_scales=scales((n, _blocks(2 * inter), _blocks(H))),
+                    w2_codes=codes((n, H, inter)), w2_scales=scales((n, _blocks(H), _blocks(inter))))
+
+    out = dict(w_router=torch.randn((E, H), generator=gen, device=device) * w.router_std,
+               bias=None, routed=bank(E, I), shared=None, shared_gate=None)
+    if w.shared_inter > 0:
+        out["shared"] = bank(1, w.shared_inter)
+        out["shared_gate"] = (torch.randn(H, generator=gen, device=device)
+                              * w.shared_gate_std).to(torch.bfloat16)
+    return out
