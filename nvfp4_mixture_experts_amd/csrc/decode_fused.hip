@@ -165,15 +165,15 @@ __device__ __forceinline__ float poll_gate(const uint64_t* lg, int E, uint32_t g
 // The experts of one token's logits row (tagged, E + 1 words; word E is the
 // shared gate) by all waves of the block: block_topk_rank with each chunk's
 // logits polled until they carry this call's generation.  ids[place] and
-// s_d[place] are complete for every wave on return.
+// s_v[place] are complete for every wave on return.
 __device__ __forceinline__ void block_topk_one_token(const uint64_t* lg, int E, int k,
                                                      uint32_t gen, int spin_limit, uint32_t* err,
                                                      uint64_t (*s_key)[kWave], uint64_t* s_cand,
-                                                     double* s_d, int* ids) {
+                                                     double* s_v, int* ids) {
   block_topk_rank<kFWaves>(
       E, k,
       [&](int e) { return tag_value(poll_tag(lg + e, gen, spin_limit, err)); },
-      s_key, s_cand, s_d, ids);
+      s_key, s_cand, s_v, ids);
 }
 
 // One token's experts by one wave (used when the block handles several tokens).
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   __shared__ float s_red[kFWaves][kWave];
   __shared__ __align__(16) uint64_t s_key[kFWaves][kWave];
   __shared__ __align__(16) uint64_t s_cand[kTopkMaxChunks * kTopkMaxK];
-  __shared__ double s_d[kMaxK];
+  __shared__ double s_v[kMaxK];
   __shared__ __align__(16) float s_hb[kFWaves][32 * kUD];  // h values of a down batch
   __shared__ uint32_t s_gen[kFWaves];
   __shared__ uint32_t s_rdone;  // this call's generation once wave 0's router rows are out
@@ -325,40 +325,52 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
 
   // ---------------------------------------------------------------- R --
   {
-    // row r goes to block r % G, wave r / G: consecutive rows on different CUs
-    const int rows = E + (p.shared_gate ? 1 : 0);
+    // the bf16 shared-gate vector as fp32, the same pieces as a router row
+    auto gate_vector = [&](float4 (&wv)[NC]) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint2 g2 = *reinterpret_cast<const uint2*>(p.shared_gate + 4 * lane + 4 * kWave * c);
+        wv[c] = make_float4(bf16_bits_to_f32(g2.x & 0xFFFFu), bf16_bits_to_f32(g2.x >> 16),
+                            bf16_bits_to_f32(g2.y & 0xFFFFu), bf16_bits_to_f32(g2.y >> 16));
+      }
+    };
+    // fp64 dot product of a row with token t's activations (the whole wave's sum)
+    auto dot_x = [&](const float4 (&wv)[NC], int t) -> double {
+      const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
+      uint2 xv[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        xv[c] = *reinterpret_cast<const uint2*>(xt + 4 * lane + 4 * kWave * c);
+      double acc = 0.0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint2 xb = xv[c];
+        acc = fma(static_cast<double>(wv[c].x), static_cast<double>(bf16_bits_to_f32(xb.x & 0xFFFFu)), acc);
+        acc = fma(static_cast<double>(wv[c].y), static_cast<double>(bf16_bits_to_f32(xb.x >> 16)), acc);
+        acc = fma(static_cast<double>(wv[c].z), static_cast<double>(bf16_bits_to_f32(xb.y & 0xFFFFu)), acc);
+        acc = fma(static_cast<double>(wv[c].w), static_cast<double>(bf16_bits_to_f32(xb.y >> 16)), acc);
+      }
+      return wave_sum_f64(acc);
+    };
+    // Row r goes to block r % G, wave r / G: consecutive rows on different CUs.
+    // With several tokens the shared gate is row E; with one token every block
+    // takes the gate itself (its last wave, below), so that it needs no hand-off
+    // and no block's selection waits behind the gate row's first access.
+    const int rows = E + ((!ONE && p.shared_gate) ? 1 : 0);
     for (int row = wave * G + blockIdx.x; row < rows; row += kFWaves * G) {
       const bool gate_row = (row == E);
       float4 wv[NC];
+      if (!gate_row) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if (!gate_row) {
+        for (int c = 0; c < NC; ++c)
           wv[c] = *reinterpret_cast<const float4*>(p.wr + static_cast<size_t>(row) * H +
                                                    4 * lane + 4 * kWave * c);
-        } else {
-          const uint2 g2 =
-              *reinterpret_cast<const uint2*>(p.shared_gate + 4 * lane + 4 * kWave * c);
-          wv[c] = make_float4(bf16_bits_to_f32(g2.x & 0xFFFFu), bf16_bits_to_f32(g2.x >> 16),
-                              bf16_bits_to_f32(g2.y & 0xFFFFu), bf16_bits_to_f32(g2.y >> 16));
-        }
+      } else {
+        gate_vector(wv);
       }
       const double bias = (!gate_row && p.bias) ? static_cast<double>(ld_vmem_f32(p.bias, row)) : 0.0;
       for (int t = 0; t < T; ++t) {
-        const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
-        uint2 xv[NC];
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          xv[c] = *reinterpret_cast<const uint2*>(xt + 4 * lane + 4 * kWave * c);
-        double acc = 0.0;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const uint2 xb = xv[c];
-          acc = fma(static_cast<double>(wv[c].x), static_cast<double>(bf16_bits_to_f32(xb.x & 0xFFFFu)), acc);
-          acc = fma(static_cast<double>(wv[c].y), static_cast<double>(bf16_bits_to_f32(xb.x >> 16)), acc);
-          acc = fma(static_cast<double>(wv[c].z), static_cast<double>(bf16_bits_to_f32(xb.y & 0xFFFFu)), acc);
-          acc = fma(static_cast<double>(wv[c].w), static_cast<double>(bf16_bits_to_f32(xb.y >> 16)), acc);
-        }
-        acc = wave_sum_f64(acc);
+        double acc = dot_x(wv, t);
         float v;
         if (!gate_row) {
           if (p.bias) acc += bias;
@@ -369,6 +381,12 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
         if (lane < kLogitCopies)
           st_tag(&p.logits[(static_cast<size_t>(lane) * T + t) * E1 + row], v, gen);
       }
+    }
+    if (ONE && p.shared_gate && wave == kFWaves - 1) {
+      float4 wv[NC];
+      gate_vector(wv);
+      const double acc = dot_x(wv, 0);
+      if (lane == 0) s_gamma[0] = static_cast<float>(1.0 / (1.0 + exp(-acc)));
     }
   }
 
@@ -404,7 +422,7 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
       __builtin_amdgcn_s_sleep(8);
     }
     if (T == 1) {
-      block_topk_one_token(lgc, E, k, gen, p.spin_limit, p.err, s_key, s_cand, s_d, s_ids);
+      block_topk_one_token(lgc, E, k, gen, p.spin_limit, p.err, s_key, s_cand, s_v, s_ids);
     } else {
       for (int t = wave; t < T; t += kFWaves) {
         const uint64_t* lg = lgc + static_cast<size_t>(t) * E1;
@@ -437,26 +455,19 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
   }
 
   // One token: the routing weights (lane i: place i), taken by every wave in its
-  // own registers once its first expert loads are out, and the shared gate.  The
-  // gate's tagged word is read once, with no wait, behind those loads (the router
-  // wrote it long before); its tag is checked, and polled only if it does not
-  // match, just before the down phase.  No memory access here is conditional:
-  // vmcnt completes in order, and a conditional access between the weight loads
-  // and their use would make the compiler's wait counts cover later stores.
+  // own registers once its first expert loads are out (the exponentials then
+  // overlap those loads), and the shared gate, which the block's last wave left
+  // in LDS before the selection's barriers.
   float w1 = 0.0f, gamma1 = 0.0f;
-  uint64_t gate_word = 0;
-  const uint64_t* gate_addr = p.logits + static_cast<size_t>(blockIdx.x % kLogitCopies) * E1 + E;
   bool have_w1 = T != 1;
   auto weights_one_token = [&]() {
     if (have_w1) return;
     have_w1 = true;
-    w1 = softmax_from_terms(s_d, k);
-    gate_word = ld_tag(gate_addr);  // word E exists (unused) without a shared expert
+    w1 = softmax_of_places(s_v, k);
   };
   auto gate_one_token = [&]() {
     if (T != 1 || !p.shared_gate) return;
-    if (!tag_is(gate_word, gen)) gate_word = tagged(poll_gate(gate_addr - E, E, gen, p.spin_limit, p.err), gen);
-    gamma1 = tag_value(gate_word);
+    gamma1 = s_gamma[0];
   };
   // routing weight (or shared gate) of slot `slot` (k: the shared expert) of token t
   auto slot_weight = [&](int t, int slot) -> float {

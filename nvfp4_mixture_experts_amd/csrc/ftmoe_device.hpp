@@ -476,16 +476,15 @@ __device__ __forceinline__ int count_above64(const uint64_t* p, uint64_t key) {
 //    candidate (fewer than k keys lie above it in all), so the count is its
 //    place; any other candidate counts at least k (some chunk holds k candidates
 //    above it).  A count below k is the expert's place.
-// 3. Each candidate also takes exp(logit - top logit) in fp64 (the top logit is
-//    the largest chunk maximum).
-// Results: ids[place] and s_d[place] (the exp term), complete for every wave on
-// return.  The softmax itself (softmax_from_terms) is left to the caller (the
-// decode kernel needs only the ids to start streaming the experts' weights).
-// LDS: s_key[BW][64], s_cand[kTopkMaxChunks * kTopkMaxK] (16-byte aligned), s_d[k].
+// Results: ids[place] and s_v[place] (the place's logit, in fp64), complete for
+// every wave on return.  The softmax itself (softmax_of_places) is left to the
+// caller: the decode kernel needs only the ids to start streaming the experts'
+// weights, and takes the exponentials while those loads are in flight.
+// LDS: s_key[BW][64], s_cand[kTopkMaxChunks * kTopkMaxK] (16-byte aligned), s_v[k].
 template <int BW, class Fetch>
 __device__ __forceinline__ void block_topk_rank(int E, int k, Fetch fetch,
                                                 uint64_t (*s_key)[kWave], uint64_t* s_cand,
-                                                double* s_d, int* ids) {
+                                                double* s_v, int* ids) {
   static_assert(kTopkMaxChunks * kTopkMaxK <= BW * kWave, "one candidate per thread");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -513,14 +512,6 @@ __device__ __forceinline__ void block_topk_rank(int E, int k, Fetch fetch,
     const int cand = c0 + static_cast<int>(threadIdx.x >> 2);
     const int q = threadIdx.x & 3;
     const uint64_t mine = s_cand[cand < nc ? cand : 0];
-    uint64_t top = 0ull;
-#pragma unroll
-    for (int c = 0; c < kTopkMaxChunks; ++c) {  // chunk maxima sit at place 0 of each chunk
-      const uint64_t v = s_cand[(c < nchunks ? c : nchunks - 1) * k];
-      top = v > top ? v : top;
-    }
-    const double d = exp(static_cast<double>(key_value(static_cast<uint32_t>(mine >> 32))) -
-                         static_cast<double>(key_value(static_cast<uint32_t>(top >> 32))));
     int above = 0;  // zero entries count for nothing
     for (int j0 = 0; j0 < nc64; j0 += kWave) {
       const ulonglong2* p2 = reinterpret_cast<const ulonglong2*>(s_cand + j0 + 16 * q);
@@ -537,18 +528,21 @@ __device__ __forceinline__ void block_topk_rank(int E, int k, Fetch fetch,
     above += __builtin_amdgcn_update_dpp(0, above, 0x4E, 0xf, 0xf, false);  // lanes ^ 2
     if (cand < nc && q == 0 && mine != 0ull && above < k) {
       ids[above] = static_cast<int>(~static_cast<uint32_t>(mine));
-      s_d[above] = d;
+      s_v[above] = static_cast<double>(key_value(static_cast<uint32_t>(mine >> 32)));
     }
   }
   __syncthreads();
 }
 
-// The routing weights of one token from the exp terms d[0..k) in place order
-// (their sum in that order, then each term over it), by one wave in its own
-// registers: lane i returns the weight of place i (0 from lane k on).
-__device__ __forceinline__ float softmax_from_terms(const double* s_d, int k) {
+// The routing weights of one token from the logits v[0..k) of its places (place
+// 0 the largest): the terms exp(v[i] - v[0]) in fp64, their sum in place order,
+// then each term over it, by one wave in its own registers: lane i returns the
+// weight of place i (0 from lane k on).
+__device__ __forceinline__ float softmax_of_places(const double* s_v, int k) {
   const int lane = threadIdx.x & (kWave - 1);
-  const double d = (lane < k) ? s_d[lane] : 0.0;
+  const double v = (lane < k) ? s_v[lane] : 0.0;
+  const double top = readlane_f64(v, 0);
+  const double d = (lane < k) ? exp(v - top) : 0.0;
   double sum = 0.0;
   for (int i = 0; i < k; ++i) sum += readlane_f64(d, i);
   return (lane < k) ? static_cast<float>(d / sum) : 0.0f;

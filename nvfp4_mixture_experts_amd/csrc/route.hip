@@ -168,14 +168,14 @@ constexpr int kTopkBlockMaxTokens = 256;  // above this a wave per token (less w
 __global__ __launch_bounds__(kTopkWaves* kWave) void topk_block_kernel(RouteParams p) {
   __shared__ __align__(16) uint64_t s_key[kTopkWaves][kWave];
   __shared__ __align__(16) uint64_t s_cand[kTopkMaxChunks * kTopkMaxK];
-  __shared__ double s_d[kTopkMaxK];
+  __shared__ double s_v[kTopkMaxK];
   __shared__ int s_ids[kTopkMaxK];
   const int t = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
   const float* __restrict__ lg = p.logits + static_cast<size_t>(t) * p.E;
-  block_topk_rank<kTopkWaves>(p.E, p.k, [&](int e) { return lg[e]; }, s_key, s_cand, s_d, s_ids);
+  block_topk_rank<kTopkWaves>(p.E, p.k, [&](int e) { return lg[e]; }, s_key, s_cand, s_v, s_ids);
   if (threadIdx.x < kWave) {
-    const float wt = softmax_from_terms(s_d, p.k);
+    const float wt = softmax_of_places(s_v, p.k);
     if (lane < p.k) {
       const size_t o = static_cast<size_t>(t) * p.k + lane;
       p.ids[o] = s_ids[lane];
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void topk_split_kernel(RoutePara
   __shared__ float s_logit[kMaxExperts];
   __shared__ __align__(16) uint64_t s_key[kTopkWaves][kWave];
   __shared__ __align__(16) uint64_t s_cand[kTopkMaxChunks * kTopkMaxK];
-  __shared__ double s_d[kTopkMaxK];
+  __shared__ double s_v[kTopkMaxK];
   __shared__ int s_ids[kTopkMaxK];
   const int t = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
@@ -435,10 +435,10 @@ __global__ __launch_bounds__(kTopkWaves* kWave) void topk_split_kernel(RoutePara
       p.gamma[t] = static_cast<float>(1.0 / (1.0 + exp(-gsum)));
   }
   __syncthreads();
-  block_topk_rank<kTopkWaves>(p.E, p.k, [&](int e) { return s_logit[e]; }, s_key, s_cand, s_d,
+  block_topk_rank<kTopkWaves>(p.E, p.k, [&](int e) { return s_logit[e]; }, s_key, s_cand, s_v,
                               s_ids);
   if (threadIdx.x < kWave) {
-    const float wt = softmax_from_terms(s_d, p.k);
+    const float wt = softmax_of_places(s_v, p.k);
     if (lane < p.k) {
       const size_t o = static_cast<size_t>(t) * p.k + lane;
       p.ids[o] = s_ids[lane];
