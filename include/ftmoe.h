@@ -372,7 +372,11 @@ ft_status ft_set_wait_limit(int32_t polls);
  *      and prefill kernels build their bf16 MFMA tiles (every such product is
  *      exact in bf16);
  *   3  fp32 code x scale x global with the codes decoded as the one-launch decode
- *      kernel's gate|up GEMV decodes them (e2m1 pair -> bf16 pair).
+ *      kernel's gate|up GEMV decodes them (e2m1 pair -> bf16 pair);
+ *   4  fp16 code x scale WITHOUT the global scale, exactly as the grouped and
+ *      prefill down GEMMs build their fp16 MFMA tiles when h travels in fp16
+ *      (every such product is exact in fp16: at most 6 significant bits, and
+ *      within [2^-10, 2688] in magnitude, or zero).
  * Every mode is exact: 0 and 3 equal one fp32 rounding of code x scale x global. */
 ft_status ft_nvfp4_dequant(int32_t hidden, int32_t inter, int32_t n_experts,
                            const ft_nvfp4_experts *bank, int32_t expert, int32_t tensor,

@@ -257,6 +257,7 @@ ft_status run_grouped(const ft_moe_desc* desc, int T, const uint16_t* x, const i
   p.act = desc->act;
   p.gate_max = desc->gate_max;
   p.up_absmax = desc->up_absmax;
+  p.h16 = prefill_h16(desc->act, desc->gate_max, desc->up_absmax) ? 1 : 0;
   p.y = y;
   hipError_t e = launch_prefill(p, s);
   if (e != hipSuccess) return hip_fail(e, "grouped expert kernels");
@@ -814,7 +815,7 @@ ft_status ft_nvfp4_dequant(int32_t hidden, int32_t inter, int32_t n_experts,
     return fail(FT_EUNSUPPORTED, "dequant: hidden %d / inter %d unsupported", hidden, inter);
   if (expert < 0 || expert >= n_experts) return fail(FT_EINVAL, "dequant: expert out of range");
   if (tensor < 0 || tensor > 2) return fail(FT_EINVAL, "dequant: tensor must be 0, 1 or 2");
-  if (out_dtype < 0 || out_dtype > 3) return fail(FT_EINVAL, "dequant: out_dtype must be 0..3");
+  if (out_dtype < 0 || out_dtype > 4) return fail(FT_EINVAL, "dequant: out_dtype must be 0..4");
   if (!aligned16(out)) return fail(FT_EINVAL, "dequant: out must be 16-byte aligned");
   if (!out) return fail(FT_EINVAL, "dequant: out is NULL");
   ft_status st = check_bank(bank, "dequant");

@@ -17,6 +17,7 @@ namespace ftmoe {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -75,6 +76,37 @@ __device__ __forceinline__ uint4 dequant8_bf16(uint32_t codes, float scale) {
   return r;
 }
 
+// The same eight products as fp16 (an MFMA operand of 8 halves): the codes are
+// decoded straight to fp16 pairs and multiplied by the block scale as an fp16
+// pair (v_pk_mul_f16), two products per instruction.  Exact as well: every
+// product has at most 6 significant bits and lies in [2^-10, 2688] (or is 0),
+// inside fp16's normal range, and every e4m3 scale is an fp16 value.  (The
+// convert's own scale operand is not used for the block scale: it applies only
+// the exponent of its argument.)
+template <int Sel>
+__device__ __forceinline__ f16x2 e2m1x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, Sel);
+}
+template <int Sel>
+__device__ __forceinline__ _Float16 e4m3_byte_to_f16(uint32_t w) {
+  return static_cast<_Float16>(e4m3_byte_to_f32<Sel>(w));  // exact
+}
+__device__ __forceinline__ uint4 dequant8_f16(uint32_t codes, _Float16 scale) {
+  const f16x2 s2 = {scale, scale};
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, e2m1x2_to_f16<0>(codes) * s2);
+  r.y = __builtin_bit_cast(uint32_t, e2m1x2_to_f16<1>(codes) * s2);
+  r.z = __builtin_bit_cast(uint32_t, e2m1x2_to_f16<2>(codes) * s2);
+  r.w = __builtin_bit_cast(uint32_t, e2m1x2_to_f16<3>(codes) * s2);
+  return r;
+}
+// The tile builder of either 16-bit type (H16: fp16, else bf16), scale given as fp32.
+template <bool H16>
+__device__ __forceinline__ uint4 dequant8_tile(uint32_t codes, float scale) {
+  if constexpr (H16) return dequant8_f16(codes, static_cast<_Float16>(scale));
+  else return dequant8_bf16(codes, scale);
+}
+
 // ------------------------------------------------------- small divisions --
 //
 // n / d for 0 <= n < 2^24 and d >= 1 through an fp32 reciprocal: the estimate is
@@ -105,6 +137,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
   const uint32_t quiet_nan = (u >> 16) | 0x0040u;
   return static_cast<uint16_t>((u & 0x7FFFFFFFu) > 0x7F800000u ? quiet_nan : rounded);
+}
+
+// Four consecutive h values of one row, as the grouped expert GEMMs hand them from
+// the gate|up product to the down product: fp16, nearest-even (h16: the clamped
+// activation bounds |h| far inside fp16's range), or a bf16 (hi, lo) pair, hi =
+// bf16(h) and lo = bf16(h - hi), whose sum holds h to about 16 significant bits.
+__device__ __forceinline__ void store_h4(uint16_t* hhi, uint16_t* hlo, size_t off,
+                                         const float (&hv)[4], bool h16) {
+  if (h16) {
+    const f16x2 a = {static_cast<_Float16>(hv[0]), static_cast<_Float16>(hv[1])};
+    const f16x2 b = {static_cast<_Float16>(hv[2]), static_cast<_Float16>(hv[3])};
+    *reinterpret_cast<uint2*>(hhi + off) =
+        make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+    return;
+  }
+  uint32_t hi[2], lo[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t h0 = f32_to_bf16_bits(hv[2 * i]), h1 = f32_to_bf16_bits(hv[2 * i + 1]);
+    const uint32_t l0 = f32_to_bf16_bits(hv[2 * i] - __uint_as_float(h0 << 16));
+    const uint32_t l1 = f32_to_bf16_bits(hv[2 * i + 1] - __uint_as_float(h1 << 16));
+    hi[i] = h0 | (h1 << 16);
+    lo[i] = l0 | (l1 << 16);
+  }
+  *reinterpret_cast<uint2*>(hhi + off) = make_uint2(hi[0], hi[1]);
+  *reinterpret_cast<uint2*>(hlo + off) = make_uint2(lo[0], lo[1]);
 }
 
 // ------------------------------------------------------- wave reductions --

@@ -87,8 +87,9 @@ struct PrefillParams {
   PfUnit* units;           // [max units]
   int32_t* nunits;         // number of valid units
   int Imax;                // row stride of hhi / hlo
-  uint16_t* hhi;           // bf16 [P + T][Imax] h rounded to bf16 ...
-  uint16_t* hlo;           // bf16 [P + T][Imax] ... and the rounded remainder
+  int h16;                 // 1: h travels as fp16 in hhi (hlo unused); 0: as a bf16 pair
+  uint16_t* hhi;           // [P + T][Imax] h in fp16 (h16), or h rounded to bf16 ...
+  uint16_t* hlo;           // bf16 [P + T][Imax] ... and the rounded remainder (h16 = 0)
   float* out;              // f32 [T][nslots][H] weighted expert outputs
   int nslots;              // k (+1 with a shared expert)
   int act;

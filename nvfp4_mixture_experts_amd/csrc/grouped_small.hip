@@ -24,8 +24,10 @@
 // lane (token n, g) in step (q, j) is x[n][32 (4q + g) + 8 j .. + 8].  Which K a
 // lane group holds only has to agree between A and B.
 //
-//   sg_gateup_kernel  h = SwiGLU(gate . x, up . x), stored as a bf16 (hi, lo) pair
-//   sg_down_kernel    out[t][slot][row] = (W_down (h_hi + h_lo)) * g_down * weight
+//   sg_gateup_kernel  h = SwiGLU(gate . x, up . x), stored in fp16 when the clamped
+//                     activation bounds it (h16), else as a bf16 (hi, lo) pair
+//   sg_down_kernel    out[t][slot][row] = (W_down h) * g_down * weight, with fp16 weight
+//                     tiles against fp16 h, or bf16 tiles against h_hi and h_lo
 #include "ftmoe_device.hpp"
 #include "ftmoe_kernels.hpp"
 
@@ -46,6 +48,16 @@ __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast
 __device__ __forceinline__ sg_f32x4 mfma(uint4 a, uint4 b, sg_f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sg_bf16x8, a),
                                                  __builtin_bit_cast(sg_bf16x8, b), c, 0, 0, 0);
+}
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 sg_f16x8;
+// fp16 operands (H16: fp16 weight tile and fp16 h) or bf16
+template <bool H16>
+__device__ __forceinline__ sg_f32x4 mfma16(uint4 a, uint4 b, sg_f32x4 c) {
+  if constexpr (H16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(sg_f16x8, a),
+                                                  __builtin_bit_cast(sg_f16x8, b), c, 0, 0, 0);
+  else
+    return mfma(a, b, c);
 }
 
 __device__ __forceinline__ uint32_t word(const uint4& q, int j) {
@@ -155,21 +167,11 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_kernel(PrefillParams 
       const int t = un.bank ? un.start + m : 0;
       const size_t row = un.bank ? static_cast<size_t>(p.P) + t : static_cast<size_t>(un.start) + m;
       const int col = n0 + wave * 16 + 4 * g;
-      uint32_t hi[2], lo[2];
+      float hv[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; jj += 2) {
-        float hv[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          hv[e] = swiglu(p.act, ag[jj + e] * gg, au[jj + e] * gu, p.gate_max, p.up_absmax);
-        const uint32_t h0 = f32_to_bf16_bits(hv[0]), h1 = f32_to_bf16_bits(hv[1]);
-        const uint32_t l0 = f32_to_bf16_bits(hv[0] - bf16_bits_to_f32(h0));
-        const uint32_t l1 = f32_to_bf16_bits(hv[1] - bf16_bits_to_f32(h1));
-        hi[jj >> 1] = h0 | (h1 << 16);
-        lo[jj >> 1] = l0 | (l1 << 16);
-      }
-      *reinterpret_cast<uint2*>(p.hhi + row * p.Imax + col) = make_uint2(hi[0], hi[1]);
-      *reinterpret_cast<uint2*>(p.hlo + row * p.Imax + col) = make_uint2(lo[0], lo[1]);
+      for (int jj = 0; jj < 4; ++jj)
+        hv[jj] = swiglu(p.act, ag[jj] * gg, au[jj] * gu, p.gate_max, p.up_absmax);
+      store_h4(p.hhi, p.hlo, row * p.Imax + col, hv, p.h16);
     }
   }
 }
@@ -265,32 +267,24 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_pipe_kernel(PrefillPa
       const int t = un.bank ? un.start + m : 0;
       const size_t row = un.bank ? static_cast<size_t>(p.P) + t : static_cast<size_t>(un.start) + m;
       const int col = n0 + wave * 16 + 4 * g;
-      uint32_t hi[2], lo[2];
+      float hv[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; jj += 2) {
-        float hv[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          hv[e] = swiglu(p.act, ag[jj + e] * gg, au[jj + e] * gu, p.gate_max, p.up_absmax);
-        const uint32_t h0 = f32_to_bf16_bits(hv[0]), h1 = f32_to_bf16_bits(hv[1]);
-        const uint32_t l0 = f32_to_bf16_bits(hv[0] - bf16_bits_to_f32(h0));
-        const uint32_t l1 = f32_to_bf16_bits(hv[1] - bf16_bits_to_f32(h1));
-        hi[jj >> 1] = h0 | (h1 << 16);
-        lo[jj >> 1] = l0 | (l1 << 16);
-      }
-      *reinterpret_cast<uint2*>(p.hhi + row * p.Imax + col) = make_uint2(hi[0], hi[1]);
-      *reinterpret_cast<uint2*>(p.hlo + row * p.Imax + col) = make_uint2(lo[0], lo[1]);
+      for (int jj = 0; jj < 4; ++jj)
+        hv[jj] = swiglu(p.act, ag[jj] * gg, au[jj] * gu, p.gate_max, p.up_absmax);
+      store_h4(p.hhi, p.hlo, row * p.Imax + col, hv, p.h16);
     }
   }
 }
 
-// Block: 64 output rows (4 waves x 16) of one unit; LDS: 16 tokens' h (hi and lo)
-// for a K block of up to 1024.
+// Block: 64 output rows (4 waves x 16) of one unit; LDS: 16 tokens' h (fp16, or
+// hi and lo) for a K block of up to 1024.
+template <bool H16>
 __global__ __launch_bounds__(kSgThreads, 2) void sg_down_kernel(PrefillParams p) {
   constexpr int kKB = 512;
   constexpr int kQ = kKB / 128;
   constexpr int kRowU4 = kKB / 8 + 1;
-  __shared__ uint4 hs[2][16 * kRowU4];
+  constexpr int NB = H16 ? 1 : 2;  // staged h operands
+  __shared__ uint4 hs[NB][16 * kRowU4];
   int u, tile;
   sg_unit_tile(p.ntiles2, &u, &tile);
   const int nun = *p.nunits;  // both loads issued before either is waited for
@@ -312,11 +306,11 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_kernel(PrefillParams p)
       const int kb = min(kKB, I - k0);  // a multiple of 64
       const int nq = kb / 128;
       const int nhalf = (kb % 128) ? 1 : 0;  // a trailing 64-K piece: chunks 4 nq + {0, 1}
-      constexpr int kLoads = 2 * 16 * (kKB / 8) / kSgThreads;
+      constexpr int kLoads = NB * 16 * (kKB / 8) / kSgThreads;
       uint4 hv[kLoads];
 #pragma unroll
       for (int r = 0; r < kLoads; ++r) {
-        const int v = min(tid + r * kSgThreads, 2 * 16 * (kb / 8) - 1);
+        const int v = min(tid + r * kSgThreads, NB * 16 * (kb / 8) - 1);
         const int which = v / (16 * (kb / 8));
         const int rr = v - which * 16 * (kb / 8);
         const int n = rr / (kb / 8), c8 = rr - n * (kb / 8);
@@ -342,7 +336,7 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_kernel(PrefillParams p)
       __syncthreads();  // the previous block / fragment is done with hs
 #pragma unroll
       for (int r = 0; r < kLoads; ++r) {
-        const int v = min(tid + r * kSgThreads, 2 * 16 * (kb / 8) - 1);
+        const int v = min(tid + r * kSgThreads, NB * 16 * (kb / 8) - 1);
         const int which = v / (16 * (kb / 8));
         const int rr = v - which * 16 * (kb / 8);
         const int n = rr / (kb / 8), c8 = rr - n * (kb / 8);
@@ -357,13 +351,12 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_kernel(PrefillParams p)
           const float s0 = e4m3_byte_to_f32<0>(sc[s]), s1 = e4m3_byte_to_f32<1>(sc[s]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            uint4 a = dequant8_bf16(word(q[s], j), j < 2 ? s0 : s1);
+            uint4 a = dequant8_tile<H16>(word(q[s], j), j < 2 ? s0 : s1);
             const int kk = (4 * s + g) * 4 + j;  // 16-byte word of the staged row
-            uint4 bh = hs[0][i * kRowU4 + min(kk, kb / 8 - 1)];
-            uint4 bl = hs[1][i * kRowU4 + min(kk, kb / 8 - 1)];
+            const uint4 bh = hs[0][i * kRowU4 + min(kk, kb / 8 - 1)];
             if (half && g >= 2) a = make_uint4(0u, 0u, 0u, 0u);  // K past the block: zero
-            acc = mfma(a, bh, acc);
-            acc = mfma(a, bl, acc);
+            acc = mfma16<H16>(a, bh, acc);
+            if constexpr (!H16) acc = mfma(a, hs[NB - 1][i * kRowU4 + min(kk, kb / 8 - 1)], acc);
           }
         }
       }
@@ -398,14 +391,15 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_kernel(PrefillParams p)
 // 64: the fragment's h (hi and lo, all of K) is staged in LDS once and serves the
 // kRT tiles, and the codes of all kRT tiles are issued up front, so a block pays
 // one memory latency, not one per tile.
-template <int NKC>
+template <int NKC, bool H16>
 __global__ __launch_bounds__(kSgThreads, 2) void sg_down_pipe_kernel(PrefillParams p) {
   constexpr int kI = 128 * NKC;
   constexpr int kRowU4 = kI / 8 + 1;
   constexpr int kRT = kDownPipeTiles;                      // row tiles per block
-  constexpr int kHL = 2 * 16 * (kI / 8) / kSgThreads;      // h loads per thread
-  static_assert(kHL * kSgThreads == 2 * 16 * (kI / 8), "whole staging rounds");
-  __shared__ uint4 hs[2][16 * kRowU4];
+  constexpr int NB = H16 ? 1 : 2;                          // staged h operands
+  constexpr int kHL = NB * 16 * (kI / 8) / kSgThreads;     // h loads per thread
+  static_assert(kHL * kSgThreads == NB * 16 * (kI / 8), "whole staging rounds");
+  __shared__ uint4 hs[NB][16 * kRowU4];
   int u, tg;
   sg_unit_tile(p.ntiles2, &u, &tg);
   const int nun = *p.nunits;  // both loads issued before either is waited for
@@ -496,14 +490,18 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_pipe_kernel(PrefillPara
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int kk = (4 * s + g) * 4 + j;  // 16-byte word of the staged row
-        const uint4 bh = hs[0][i * kRowU4 + kk], bl = hs[1][i * kRowU4 + kk];
+        const uint4 bh = hs[0][i * kRowU4 + kk];
         uint4 a[kRT];
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) a[rt] = dequant8_bf16(word(q[rt][s], j), j < 2 ? s0[rt] : s1[rt]);
+        for (int rt = 0; rt < kRT; ++rt)
+          a[rt] = dequant8_tile<H16>(word(q[rt][s], j), j < 2 ? s0[rt] : s1[rt]);
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) acc[rt] = mfma(a[rt], bh, acc[rt]);
+        for (int rt = 0; rt < kRT; ++rt) acc[rt] = mfma16<H16>(a[rt], bh, acc[rt]);
+        if constexpr (!H16) {
+          const uint4 bl = hs[NB - 1][i * kRowU4 + kk];
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) acc[rt] = mfma(a[rt], bl, acc[rt]);
+          for (int rt = 0; rt < kRT; ++rt) acc[rt] = mfma(a[rt], bl, acc[rt]);
+        }
       }
     }
     if (m < un.count) {
@@ -540,11 +538,18 @@ hipError_t launch_grouped_small(const PrefillParams& p0, int ugroups, hipStream_
   if (nkc == 4 || nkc == 6 || nkc == 8) {
     p.ntiles2 = p.H / (64 * kDownPipeTiles);
     const dim3 g2(ugroups * 8 * p.ntiles2);
-    if (nkc == 4) sg_down_pipe_kernel<4><<<g2, blk, 0, s>>>(p);
-    else if (nkc == 6) sg_down_pipe_kernel<6><<<g2, blk, 0, s>>>(p);
-    else sg_down_pipe_kernel<8><<<g2, blk, 0, s>>>(p);
+    if (p.h16) {
+      if (nkc == 4) sg_down_pipe_kernel<4, true><<<g2, blk, 0, s>>>(p);
+      else if (nkc == 6) sg_down_pipe_kernel<6, true><<<g2, blk, 0, s>>>(p);
+      else sg_down_pipe_kernel<8, true><<<g2, blk, 0, s>>>(p);
+    } else {
+      if (nkc == 4) sg_down_pipe_kernel<4, false><<<g2, blk, 0, s>>>(p);
+      else if (nkc == 6) sg_down_pipe_kernel<6, false><<<g2, blk, 0, s>>>(p);
+      else sg_down_pipe_kernel<8, false><<<g2, blk, 0, s>>>(p);
+    }
   } else {
-    sg_down_kernel<<<ugroups * 8 * p.ntiles2, blk, 0, s>>>(p);
+    if (p.h16) sg_down_kernel<true><<<ugroups * 8 * p.ntiles2, blk, 0, s>>>(p);
+    else sg_down_kernel<false><<<ugroups * 8 * p.ntiles2, blk, 0, s>>>(p);
   }
   return hipGetLastError();
 }

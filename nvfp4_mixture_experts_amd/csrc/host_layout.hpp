@@ -99,6 +99,18 @@ inline size_t route_split_bytes(int E, int T, int H) {
 
 // -------------------------------------------------------- descriptors --
 
+// Whether the grouped expert GEMMs hand h from the gate|up product to the down
+// product in fp16 (one MFMA operand) rather than as a bf16 (hi, lo) pair (two):
+// only when the activation bounds |h| well inside fp16's range.  The clamped SwiGLU
+// gives |h| <= max(gate_max, 0.2785) * |up_absmax| (|silu(g)| < 0.2785 for g <= 0,
+// silu(g) < g for g > 0); the plain SwiGLU is unbounded.  NaN limits give the pair.
+inline bool prefill_h16(int act, float gate_max, float up_absmax) {
+  if (act != 1) return false;
+  const float gm = gate_max > 0.2785f ? gate_max : 0.2785f;
+  const float ua = up_absmax < 0.0f ? -up_absmax : up_absmax;
+  return gm * ua <= 32768.0f;
+}
+
 inline bool inter_ok(int I) { return I >= 64 && I <= 4096 && I % 64 == 0; }
 
 // FT_OK, or the status of the first problem of the descriptor, with its message

@@ -43,6 +43,16 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 __device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+// 16 x 16 x 32 product of 16-bit operands: fp16 (H16) or bf16
+template <bool H16>
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+  if constexpr (H16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return mfma_bf16(a, b, c);
+}
 
 // KPT = 16 or 32 consecutive K elements of one row (KPT/2 code bytes, KPT/16 scale
 // bytes) -> KPT/8 x 16 B of bf16.
@@ -54,10 +64,11 @@ template <> struct Codes<16> {
     q = *reinterpret_cast<const uint2*>(c);
     s = *sc;
   }
+  template <bool H16 = false>
   __device__ __forceinline__ void to_lds(uint4* dst) const {
     const float s0 = e4m3_byte_to_f32<0>(s);
-    dst[0] = dequant8_bf16(q.x, s0);
-    dst[1] = dequant8_bf16(q.y, s0);
+    dst[0] = dequant8_tile<H16>(q.x, s0);
+    dst[1] = dequant8_tile<H16>(q.y, s0);
   }
 };
 template <> struct Codes<32> {
@@ -67,12 +78,13 @@ template <> struct Codes<32> {
     q = *reinterpret_cast<const uint4*>(c);
     s = *reinterpret_cast<const uint16_t*>(sc);
   }
+  template <bool H16 = false>
   __device__ __forceinline__ void to_lds(uint4* dst) const {
     const float s0 = e4m3_byte_to_f32<0>(s), s1 = e4m3_byte_to_f32<1>(s);
-    dst[0] = dequant8_bf16(q.x, s0);
-    dst[1] = dequant8_bf16(q.y, s0);
-    dst[2] = dequant8_bf16(q.z, s1);
-    dst[3] = dequant8_bf16(q.w, s1);
+    dst[0] = dequant8_tile<H16>(q.x, s0);
+    dst[1] = dequant8_tile<H16>(q.y, s0);
+    dst[2] = dequant8_tile<H16>(q.z, s1);
+    dst[3] = dequant8_tile<H16>(q.w, s1);
   }
 };
 
@@ -274,15 +286,16 @@ __device__ __forceinline__ int frag_token(int wave, int f, int lane) {
   return (wave + W * f) * 16 + (lane & 15);
 }
 
-// The K loop shared by both GEMMs.  NB = 1: B is bf16 activations; NB = 2: B is a
-// (hi, lo) bf16 pair whose two products are accumulated into the same C.
+// The looped K loop of the down GEMM.  NB = 1: B is one 16-bit operand (fp16 h
+// with fp16 weight tiles when H16, else bf16); NB = 2: B is a (hi, lo) bf16 pair
+// whose two products are accumulated into the same C.
 // brow[b][f]: this lane's B row for fragment f (slab 0, lane group offset applied).
 // wc / ws: this thread's codes and scales of slab 0 (kKpt K elements of tile row
 // drow, part dpart of the slab); wc_step / ws_step: their slab strides.
 // Token rows run R - 1 slabs ahead (a ring of R), weight codes RW slabs ahead (a
 // ring of RW; RW is a multiple of R and even, and the loop is unrolled RW times so
 // that every ring slot and LDS buffer index is a compile-time constant).
-template <int W, int FR, int NB, int R, int RW>
+template <int W, int FR, int NB, int R, int RW, bool H16>
 __device__ __forceinline__ void pf_mainloop(
     const uint8_t* wc, size_t wc_step, const uint8_t* ws, size_t ws_step,
     const uint16_t* const (&brow)[NB][FR], int nfr, int nslab,
@@ -325,7 +338,7 @@ __device__ __forceinline__ void pf_mainloop(
     load_b(clampslab(r), xr[r]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  cr[0].to_lds(my0);
+  cr[0].template to_lds<H16>(my0);
   load_codes(RW, cr[0]);
   __builtin_amdgcn_sched_barrier(0);
 
@@ -356,14 +369,14 @@ __device__ __forceinline__ void pf_mainloop(
             if (live && f < nfr) {
 #pragma unroll
               for (int rf = 0; rf < 8; ++rf)
-                acc[f][rf] = mfma_bf16(a[rf], xr[r % R][b][f][j], acc[f][rf]);
+                acc[f][rf] = mfma16<H16>(a[rf], xr[r % R][b][f][j], acc[f][rf]);
             }
           }
       }
       // weights of slab s + 1 (its buffer was last read in iteration s - 1), then
       // the codes of slab s + 1 + RW into the freed ring slot
       const int c = (r + 1) % RW;
-      cr[c].to_lds((r & 1) ? my0 : my1);
+      cr[c].template to_lds<H16>((r & 1) ? my0 : my1);
       load_codes(s + 1 + RW, cr[c]);
     }
   }
@@ -474,7 +487,7 @@ __device__ __forceinline__ void pf_mainloop_rows(
 // codes of all NS slabs are loaded and dequantised up front (one barrier), then the
 // MFMAs run over the NS slabs with no further barrier, token rows (NB operands)
 // R - 1 slabs ahead in a ring whose slots are constants (the loop is unrolled).
-template <int W, int FR, int NB, int R, int NS>
+template <int W, int FR, int NB, int R, int NS, bool H16>
 __device__ __forceinline__ void pf_mainloop_whole_a(
     const uint8_t* wc, size_t wc_step, const uint8_t* ws, size_t ws_step,
     const uint16_t* const (&brow)[NB][FR], int nfr, uint4 (*lds)[kPfRows * kLdsRowU4],
@@ -501,7 +514,8 @@ __device__ __forceinline__ void pf_mainloop_whole_a(
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int s = 0; s < NS; ++s) cr[s].to_lds(&lds[s][drow * kLdsRowU4 + dpart * (KPT / 8)]);
+  for (int s = 0; s < NS; ++s)
+    cr[s].template to_lds<H16>(&lds[s][drow * kLdsRowU4 + dpart * (KPT / 8)]);
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -521,7 +535,7 @@ __device__ __forceinline__ void pf_mainloop_whole_a(
           if (f < nfr) {
 #pragma unroll
             for (int rf = 0; rf < 8; ++rf)
-              acc[f][rf] = mfma_bf16(a[rf], xr[s % R][b][f][j], acc[f][rf]);
+              acc[f][rf] = mfma16<H16>(a[rf], xr[s % R][b][f][j], acc[f][rf]);
           }
         }
     }
@@ -684,33 +698,22 @@ __global__ __launch_bounds__(256, BPC) void pf_gateup_kernel(PrefillParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int col = n0 + r * 16 + (lane >> 4) * 4;
-      uint32_t hi[2], lo[2];
+      float hv[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; jj += 2) {
-        float hv[2];
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          const float g = acc[f][r][jj + q2] * gg;
-          const float up = acc[f][r + 4][jj + q2] * gu;
-          hv[q2] = swiglu(p.act, g, up, p.gate_max, p.up_absmax);
-        }
-        const uint32_t h0 = f32_to_bf16_bits(hv[0]), h1 = f32_to_bf16_bits(hv[1]);
-        const uint32_t l0 = f32_to_bf16_bits(hv[0] - bf16_bits_to_f32(h0));
-        const uint32_t l1 = f32_to_bf16_bits(hv[1] - bf16_bits_to_f32(h1));
-        hi[jj >> 1] = h0 | (h1 << 16);
-        lo[jj >> 1] = l0 | (l1 << 16);
-      }
-      *reinterpret_cast<uint2*>(p.hhi + row * p.Imax + col) = make_uint2(hi[0], hi[1]);
-      *reinterpret_cast<uint2*>(p.hlo + row * p.Imax + col) = make_uint2(lo[0], lo[1]);
+      for (int jj = 0; jj < 4; ++jj)
+        hv[jj] = swiglu(p.act, acc[f][r][jj] * gg, acc[f][r + 4][jj] * gu, p.gate_max, p.up_absmax);
+      store_h4(p.hhi, p.hlo, row * p.Imax + col, hv, p.h16);
     }
   }
 }
 
 // NS > 0: I = 64 NS for both banks, the whole weight tile in LDS
 // (pf_mainloop_whole_a, R its token ring depth); NS = 0: any I, looped.
-template <int W, int FR, int R, int RW, int NS>
+// H16: h is fp16 (one operand, fp16 weight tiles), else a bf16 (hi, lo) pair.
+template <int W, int FR, int R, int RW, int NS, bool H16>
 __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(PrefillParams p) {
   using G = Geometry<W, FR>;
+  constexpr int NB = H16 ? 1 : 2;
   __shared__ uint4 lds[NS > 0 ? NS : 2][kPfRows * kLdsRowU4];
   int u, tile;
   unit_tile(p.ntiles2, &u, &tile);
@@ -735,14 +738,14 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(Pre
   const uint8_t* ws = bank.w2s + (chunk0 * H + h0 + drow) * 2 + (kofs & 31) / 16;
 
   const int nfr = wave_fragments<W, FR>(un.count, wave);
-  const uint16_t* brow[2][FR];
+  const uint16_t* brow[NB][FR];
 #pragma unroll
   for (int f = 0; f < FR; ++f) {
     const int m = min(frag_token<W>(wave, f, lane), un.count - 1);
     const size_t row = un.bank ? static_cast<size_t>(p.P) + un.start + m
                                : static_cast<size_t>(un.start) + m;
     brow[0][f] = p.hhi + row * p.Imax + (lane >> 4) * 16;
-    brow[1][f] = p.hlo + row * p.Imax + (lane >> 4) * 16;
+    if constexpr (!H16) brow[NB - 1][f] = p.hlo + row * p.Imax + (lane >> 4) * 16;
   }
 
   // where each fragment's outputs go, and their weights: looked up before the main
@@ -770,13 +773,13 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(Pre
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[f][r] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (NS > 0)
-    pf_mainloop_whole_a<W, FR, 2, R, NS>(wc, static_cast<size_t>(2) * H * 16, ws,
-                                         static_cast<size_t>(2) * H * 2, brow, nfr, lds, drow,
-                                         dpart, lane, acc);
+    pf_mainloop_whole_a<W, FR, NB, R, NS, H16>(wc, static_cast<size_t>(2) * H * 16, ws,
+                                               static_cast<size_t>(2) * H * 2, brow, nfr, lds,
+                                               drow, dpart, lane, acc);
   else
-    pf_mainloop<W, FR, 2, R, RW>(wc, static_cast<size_t>(2) * H * 16, ws,
-                                 static_cast<size_t>(2) * H * 2, brow, nfr, I / kPfSlab, lds, drow,
-                                 dpart, lane, acc);
+    pf_mainloop<W, FR, NB, R, RW, H16>(wc, static_cast<size_t>(2) * H * 16, ws,
+                                       static_cast<size_t>(2) * H * 2, brow, nfr, I / kPfSlab, lds,
+                                       drow, dpart, lane, acc);
 
   // epilogue: output rows h0 + 16 r + 4 (lane / 16) + jj of token m
   const float gd = bank.gsc[un.expert * 3 + 2];
@@ -807,10 +810,11 @@ __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(Pre
 // stay on one XCD).  The whole weight tile of an item is dequantised into LDS;
 // while its MFMAs run, the next item's codes are already being loaded into
 // registers, so an item does not start with a memory latency.
-template <int NS, int R>
+template <int NS, int R, bool H16>
 __global__ __launch_bounds__(8 * kWave, 1) void pf_down_persistent_kernel(PrefillParams p,
                                                                          int nitems) {
   constexpr int W = 8, FR = 2;
+  constexpr int NB = H16 ? 1 : 2;  // h operands: fp16 h, or the bf16 (hi, lo) pair
   using G = Geometry<W, FR>;
   constexpr int KPT = G::kKpt;
   constexpr int kI = 64 * NS;
@@ -872,7 +876,8 @@ __global__ __launch_bounds__(8 * kWave, 1) void pf_down_persistent_kernel(Prefil
     const int h0 = tile * kPfRows;
     __syncthreads();  // the previous item's MFMAs are done with the tile
 #pragma unroll
-    for (int s = 0; s < NS; ++s) cr[s].to_lds(&lds[s][drow * kLdsRowU4 + dpart * (KPT / 8)]);
+    for (int s = 0; s < NS; ++s)
+      cr[s].template to_lds<H16>(&lds[s][drow * kLdsRowU4 + dpart * (KPT / 8)]);
     // the next item (found before any load goes out: a loop with loads in flight
     // would make the compiler wait for them at its head), this item's output
     // places and weights (from its pair indices), then the next item's loads: all
@@ -882,7 +887,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void pf_down_persistent_kernel(Prefil
     // read unconditionally (a valid index), so that it is a scalar load
     const PfUnit nun = p.units[nit < nitems ? nu : u];
     const int nfr = wave_fragments<W, FR>(un.count, wave);
-    const uint16_t* brow[2][FR];
+    const uint16_t* brow[NB][FR];
     int ot[FR], oslot[FR];
     float owt[FR];
 #pragma unroll
@@ -891,7 +896,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void pf_down_persistent_kernel(Prefil
       const size_t row = un.bank ? static_cast<size_t>(p.P) + un.start + m
                                  : static_cast<size_t>(un.start) + m;
       brow[0][f] = p.hhi + row * p.Imax + (lane >> 4) * 16;
-      brow[1][f] = p.hlo + row * p.Imax + (lane >> 4) * 16;
+      if constexpr (!H16) brow[NB - 1][f] = p.hlo + row * p.Imax + (lane >> 4) * 16;
       if (un.bank) {
         ot[f] = un.start + m;
         oslot[f] = p.k;
@@ -905,10 +910,10 @@ __global__ __launch_bounds__(8 * kWave, 1) void pf_down_persistent_kernel(Prefil
     __builtin_amdgcn_sched_barrier(0);
     if (nit < nitems) load_item(nun, ntile);
 
-    uint4 xr[R][2][FR][2];
-    auto load_b = [&](int s, uint4 (&dst)[2][FR][2]) {
+    uint4 xr[R][NB][FR][2];
+    auto load_b = [&](int s, uint4 (&dst)[NB][FR][2]) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int f = 0; f < FR; ++f) {
           dst[b][f][0] = ld16(brow[b][f] + s * kPfSlab);
@@ -934,16 +939,16 @@ __global__ __launch_bounds__(8 * kWave, 1) void pf_down_persistent_kernel(Prefil
 #pragma unroll
         for (int rf = 0; rf < 8; ++rf)
           a[rf] = t[(rf * 16 + (lane & 15)) * kLdsRowU4 + (lane >> 4) * 2 + j];
-        // h_hi products first, then h_lo: consecutive MFMAs write different
+        // (pair) h_hi products first, then h_lo: consecutive MFMAs write different
         // accumulators (an MFMA right after one into the same accumulator waits)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int f = 0; f < FR; ++f) {
             if (f < nfr) {
 #pragma unroll
               for (int rf = 0; rf < 8; ++rf)
-                acc[f][rf] = mfma_bf16(a[rf], xr[s % R][b][f][j], acc[f][rf]);
+                acc[f][rf] = mfma16<H16>(a[rf], xr[s % R][b][f][j], acc[f][rf]);
             }
           }
       }
@@ -1049,11 +1054,14 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
       case 4096: pf_gateup_kernel<4, 4, 2, 1, 16><<<g1, 4 * kWave, 0, s>>>(p); break;
       default: pf_gateup_kernel<4, 2, 1, 1, 0><<<g1, 4 * kWave, 0, s>>>(p); break;
     }
-    if (p.routed.inter == 512 && (p.shared.inter == 0 || p.shared.inter == 512))
-      pf_down_persistent_kernel<8, 2><<<g2 < kPersistentBlocks ? g2 : kPersistentBlocks, 8 * kWave, 0, s>>>(
-          p, static_cast<int>(g2));
-    else
-      pf_down_kernel<8, 2, 2, 4, 0><<<g2, 8 * kWave, 0, s>>>(p);
+    const unsigned gp = g2 < kPersistentBlocks ? g2 : kPersistentBlocks;
+    if (p.routed.inter == 512 && (p.shared.inter == 0 || p.shared.inter == 512)) {
+      if (p.h16) pf_down_persistent_kernel<8, 2, true><<<gp, 8 * kWave, 0, s>>>(p, static_cast<int>(g2));
+      else pf_down_persistent_kernel<8, 2, false><<<gp, 8 * kWave, 0, s>>>(p, static_cast<int>(g2));
+    } else {
+      if (p.h16) pf_down_kernel<8, 2, 2, 4, 0, true><<<g2, 8 * kWave, 0, s>>>(p);
+      else pf_down_kernel<8, 2, 2, 4, 0, false><<<g2, 8 * kWave, 0, s>>>(p);
+    }
   } else {
     // few tokens per expert: units of at most 16 tokens, each a separate pass over
     // its expert's weights (the passes of one expert run side by side)

@@ -141,7 +141,9 @@ hipError_t launch_repack_w2(int H, int I, int n, const uint8_t* w2, const uint8_
 //      their MFMA tiles (dequant8_bf16);
 //   3  fp32 code x scale x global with the codes through e2m1x2_to_bf16 (the
 //      gate|up GEMV of the one-launch decode kernel, which multiplies those bf16
-//      codes with the activations and applies the scale per 16-element block).
+//      codes with the activations and applies the scale per 16-element block);
+//   4  fp16 code x scale, no global scale, as the down GEMMs of the grouped and
+//      prefill kernels build their fp16 tiles (dequant8_tile<true>).
 __global__ __launch_bounds__(256) void dequant_kernel(int H, int I, Bank b, int e, int tensor,
                                                       int out_dtype, void* out) {
   const bool down = (tensor == 2);
@@ -169,8 +171,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(int H, int I, Bank b, int 
   const float s = e4m3_byte_to_f32<0>(scale_byte);
   const float g = b.gsc[3 * e + tensor];
   const size_t o = static_cast<size_t>(r) * K + k0;
-  if (out_dtype == 2) {
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o) = dequant8_bf16(code_word, s);
+  if (out_dtype == 2 || out_dtype == 4) {
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o) =
+        out_dtype == 2 ? dequant8_tile<false>(code_word, s) : dequant8_tile<true>(code_word, s);
     return;
   }
   float v[8];

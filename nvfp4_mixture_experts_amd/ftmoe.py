@@ -249,15 +249,15 @@ def ft_moe_nvfp4_prefill(desc: FtMoeDesc, x, topk_ids, topk_w, routed: Bank,
 
 
 # ft_nvfp4_dequant modes (see include/ftmoe.h)
-DEQ_F32, DEQ_BF16, DEQ_TILE_BF16, DEQ_GATEUP_F32 = 0, 1, 2, 3
+DEQ_F32, DEQ_BF16, DEQ_TILE_BF16, DEQ_GATEUP_F32, DEQ_TILE_F16 = 0, 1, 2, 3, 4
 
 
 def ft_nvfp4_dequant(bank: Bank, expert: int, tensor: int, out, stream=None,
                      mode: Optional[int] = None) -> None:
-    """out: fp32 or bf16 [rows][K] device tensor (gate/up [I][H], down [H][I]).
+    """out: fp32, bf16 or fp16 [rows][K] device tensor (gate/up [I][H], down [H][I]).
     ``mode`` defaults to DEQ_F32 for fp32 ``out`` and DEQ_BF16 for bf16 ``out``."""
     want = {DEQ_F32: torch.float32, DEQ_BF16: torch.bfloat16, DEQ_TILE_BF16: torch.bfloat16,
-            DEQ_GATEUP_F32: torch.float32}
+            DEQ_GATEUP_F32: torch.float32, DEQ_TILE_F16: torch.float16}
     if mode is None:
         if out.dtype == torch.float32:
             mode = DEQ_F32

@@ -145,7 +145,7 @@ def test_host_validation_status_codes(ft):
     # dequant argument checks
     assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 8, 0, 0, 16, None) == ft.FT_EINVAL
     assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 0, 3, 0, 16, None) == ft.FT_EINVAL
-    assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 0, 0, 4, 16, None) == ft.FT_EINVAL
+    assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 0, 0, 5, 16, None) == ft.FT_EINVAL
     assert lib.ft_nvfp4_dequant(2048, 768, 8, b, 0, 0, 2, 24, None) == ft.FT_EINVAL  # alignment
     assert lib.ft_nvfp4_dequant(2000, 768, 8, b, 0, 0, 0, 16, None) == ft.FT_EUNSUPPORTED
     # repack argument checks

@@ -63,6 +63,22 @@ def _bits_equal_with_nan(got, want):
     assert np.array_equal(got[~gn].view(np.uint32), want[~wn].view(np.uint32))
 
 
+def _check_f16_tile(bank, e, tensor, rows, K, want1):
+    """ft_nvfp4_dequant mode 4 (the fp16 MFMA tile builder) against the oracle's
+    code x scale: every value is exactly representable in fp16, so the converted
+    oracle value must match bit for bit (NaN where the scale is NaN)."""
+    from nvfp4_mixture_experts_amd import ftmoe
+    out16 = torch.empty((rows, K), dtype=torch.float16, device="cuda")
+    ftmoe.ft_nvfp4_dequant(bank, e, tensor, out16, mode=ftmoe.DEQ_TILE_F16)
+    torch.cuda.synchronize()
+    got = out16.cpu().numpy()
+    n1 = np.isnan(want1)
+    want16 = want1.astype(np.float16)
+    assert np.array_equal(want16[~n1].astype(np.float32), want1[~n1])  # exact in fp16
+    assert np.array_equal(np.isnan(got), n1)
+    assert np.array_equal(got[~n1].view(np.uint16), want16[~n1].view(np.uint16))
+
+
 @pytest.mark.parametrize("tensor", [0, 1, 2])
 def test_dequant_bit_exact_all_codes_and_scales(gpu, tensor):
     from nvfp4_mixture_experts_amd import ftmoe
@@ -110,6 +126,9 @@ def test_dequant_bit_exact_all_codes_and_scales(gpu, tensor):
         assert np.array_equal(gott[~n1], (want1[~n1].view(np.uint32) >> 16).astype(np.uint16))
         tv = (gott.astype(np.uint32) << 16).view(np.float32)
         assert np.array_equal(np.isnan(tv), n1)
+        # the fp16 tile builder of the down GEMMs (h in fp16): code x scale is exact in
+        # fp16 as well, so its bits are the oracle's value converted
+        _check_f16_tile(bank, e, tensor, rows, K, want1)
 
 
 def test_dequant_bit_exact_workload_bank(gpu):
@@ -139,6 +158,7 @@ def test_dequant_bit_exact_workload_bank(gpu):
             assert np.array_equal(outg.cpu().numpy().view(np.uint32), want.view(np.uint32))
             gott = outt.cpu().view(torch.int16).numpy().view(np.uint16)
             assert np.array_equal(gott, (want1.view(np.uint32) >> 16).astype(np.uint16))
+            _check_f16_tile(dl.routed, e, tensor, rows, K, want1)
 
 
 # ------------------------------------------------------------------ route --

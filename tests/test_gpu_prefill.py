@@ -122,14 +122,17 @@ def test_prefill_is_deterministic(gpu):
     assert np.array_equal(a, b) and np.array_equal(a, c)
 
 
-@pytest.mark.parametrize("H,Is", [(1024, 512), (2048, 512), (4096, 0)])
-def test_prefill_unrolled_widths(gpu, H, Is):
+@pytest.mark.parametrize("H,Is,clamped", [(1024, 512, True), (2048, 512, True), (4096, 0, True),
+                                         (2048, 512, False)])
+def test_prefill_unrolled_widths(gpu, H, Is, clamped):
     """The many-token kernels with the unrolled gate|up K loop (H / 256 = 4, 8, 16
     super-slabs) and the whole-tile down product (I = 512 for both banks; one case
-    without a shared expert): T = 300, so the shared unit holds 256 tokens."""
+    without a shared expert): T = 300, so the shared unit holds 256 tokens.  The
+    clamped activation hands h to the down product in fp16, the plain one as a
+    bf16 (hi, lo) pair."""
     w = synth.dataclasses.replace(synth.WORKLOADS["prefill_t8192"], num_experts=16, top_k=4,
                                   tokens=300, hidden=H, inter=512, shared_inter=Is,
-                                  seed=600 + H + Is)
+                                  clamped=clamped, seed=600 + H + Is + int(clamped))
     L = synth.make_layer(w)
     x = synth.make_tokens(w)
     dl = gpu.upload_layer(L)
@@ -140,7 +143,30 @@ def test_prefill_unrolled_widths(gpu, H, Is):
     rows = [0, 1, 63, 64, 127, 128, 200, 255, 256, 299]
     ref = oracle.moe_layer(L, x[rows])
     assert np.array_equal(ids.cpu().numpy()[rows], ref["ids"])
-    assert_output_close(gpu.bf16_bits(y)[rows], ref["y"], f"prefill unrolled H={H}")
+    assert_output_close(gpu.bf16_bits(y)[rows], ref["y"],
+                        f"prefill unrolled H={H} clamped={clamped}")
+
+
+@pytest.mark.parametrize("clamped", [True, False])
+def test_grouped_few_tokens_both_h_forms(gpu, clamped):
+    """The few-token grouped kernels (units of at most 16 tokens) with h in fp16
+    (clamped activation) and as a bf16 pair (plain), every token against the oracle:
+    24 tokens over 32 experts, top-4, a shared expert, I = 512 (the pipelined down
+    product) and I = 192 (the looped one, with a trailing 64-K piece)."""
+    for inter in (512, 192):
+        w = synth.dataclasses.replace(synth.WORKLOADS["batched_decode_t32_hot64"], num_experts=32,
+                                      top_k=4, tokens=24, inter=inter, shared_inter=inter,
+                                      hot_experts=4, clamped=clamped, seed=700 + inter)
+        L = synth.make_layer(w)
+        x = synth.make_tokens(w)
+        dl = gpu.upload_layer(L)
+        xd = gpu.tokens_to_device(x)
+        ids, wt = gpu.route(dl, xd)
+        y = gpu.prefill(dl, xd, ids, wt)
+        torch.cuda.synchronize()
+        ref = oracle.moe_layer(L, x)
+        assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+        assert_output_close(gpu.bf16_bits(y), ref["y"], f"grouped T=24 I={inter} clamped={clamped}")
 
 
 @pytest.mark.slow
