@@ -170,7 +170,7 @@ Bank to_bank_fp8(const ft_fp8_experts* b, int inter) {
 ft_status run_route(const ft_moe_desc* desc, int T, const uint16_t* x, const float* w_router,
                     const float* bias, const uint16_t* shared_gate, float* logits, float* gamma,
                     int32_t* ids, float* w, int32_t* ids_copy, float* w_copy, uint32_t* counter,
-                    double* split_part, hipStream_t s) {
+                    double* split_part, uint16_t* wsplit, float* wnorm, hipStream_t s) {
   RouteParams p{};
   p.x = x;
   p.wr = w_router;
@@ -189,18 +189,30 @@ ft_status run_route(const ft_moe_desc* desc, int T, const uint16_t* x, const flo
   p.counter = counter;
   hipError_t e;
   if (T >= kRouteMfmaMinTokens) {
-    // many tokens: logits as an fp64 MFMA product, the shared gate by the row
-    // kernel (as its only row), then the top-k kernel
-    e = launch_route_mfma(p, s);
-    if (e != hipSuccess) return hip_fail(e, "route kernel");
+    // many tokens: bf16 MFMA approximations with a rigorous error bound, the exact
+    // fp64 logits of the experts the bound leaves in play and the top-k among them
+    // (with the row pieces and norms in the workspace); the shared gate by the row
+    // kernel (as its only row).  Without that scratch (callers other than
+    // ft_moe_route): the fp64 MFMA product of every logit, then the top-k kernel.
+    if (wsplit && wnorm) {
+      p.wsplit = wsplit;
+      p.wnorm = wnorm;
+      e = launch_route_bounded(p, s);
+      if (e != hipSuccess) return hip_fail(e, "bounded router kernels");
+    } else {
+      e = launch_route_mfma(p, s);
+      if (e != hipSuccess) return hip_fail(e, "route kernel");
+    }
     if (gamma) {
       RouteParams q = p;
       q.E = 0;
       e = launch_route(q, false, s);
       if (e != hipSuccess) return hip_fail(e, "shared gate kernel");
     }
-    e = launch_topk(p, s);
-    if (e != hipSuccess) return hip_fail(e, "top-k kernel");
+    if (!(wsplit && wnorm)) {
+      e = launch_topk(p, s);
+      if (e != hipSuccess) return hip_fail(e, "top-k kernel");
+    }
     return FT_OK;
   }
   if (T >= kRouteSplitMinTokens) {
@@ -364,7 +376,10 @@ ft_status ft_moe_route(const ft_moe_desc* desc, int64_t tokens, const uint16_t* 
   st = run_route(desc, static_cast<int>(tokens), x, w_router, bias, nullptr,
                  at<float>(workspace, L.logits), nullptr, topk_ids, topk_w, nullptr, nullptr,
                  at<uint32_t>(workspace, L.sync) + kRouteCounterWord,
-                 at<double>(workspace, L.rsplit), static_cast<hipStream_t>(stream));
+                 at<double>(workspace, L.rsplit),
+                 tokens >= kRouteMfmaMinTokens ? at<uint16_t>(workspace, L.wsplit) : nullptr,
+                 tokens >= kRouteMfmaMinTokens ? at<float>(workspace, L.wnorm) : nullptr,
+                 static_cast<hipStream_t>(stream));
   if (st != FT_OK) return st;
   return ok();
 }
@@ -447,7 +462,7 @@ ft_status decode_impl(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x
     st = run_route(desc, T, x, w_router, bias, shared_gate, at<float>(workspace, L.logits),
                    has_shared ? at<float>(workspace, L.gamma) : nullptr, ids, wts, topk_ids_out,
                    topk_w_out, at<uint32_t>(workspace, L.sync) + kRouteCounterWord,
-                   at<double>(workspace, L.rsplit), s);
+                   at<double>(workspace, L.rsplit), nullptr, nullptr, s);
     if (st != FT_OK) return st;
     ft_moe_desc gd = *desc;
     if (slot_of) {

@@ -37,6 +37,8 @@ struct RouteParams {
   int tok_tile;                 // tokens per wave (set by the launcher)
   double* part;                 // split-K router: f64 [ksplit][T][E + 1] partial sums
   int ksplit;                   // K splits (set by the launcher)
+  uint16_t* wsplit;             // many-token router: bf16 [E][2][H] pieces of each row
+  float* wnorm;                 // many-token router: f32 [E] 2-norm of each row, rounded up
 };
 
 // The whole decode layer in one persistent launch (one block per CU).  Values
@@ -119,6 +121,10 @@ hipError_t launch_route_split(const RouteParams& p, hipStream_t s);
 hipError_t launch_topk(const RouteParams& p, hipStream_t s);
 // logits only (no shared gate, no top-k), as an fp64 MFMA product; H % 64 == 0
 hipError_t launch_route_mfma(const RouteParams& p, hipStream_t s);
+// many tokens: approximate logits by a bf16 MFMA product with a rigorous error bound,
+// then per token the exact fp64 logits of the experts the bound cannot rule out and
+// the top-k among them (ids, w and their copies); p.wsplit / p.wnorm are scratch
+hipError_t launch_route_bounded(const RouteParams& p, hipStream_t s);
 hipError_t launch_repack_w2(int H, int I, int n, const uint8_t* w2, const uint8_t* w2s,
                             uint8_t* out_w2, uint8_t* out_w2s, hipStream_t s);
 hipError_t launch_dequant(int H, int I, const Bank& b, int expert, int tensor, int out_dtype,

@@ -166,6 +166,7 @@ inline ft_status desc_problem(const ft_moe_desc* d, char* buf, size_t n) {
 struct Layout {
   size_t sync, gen, logits, h, part;  // route / one-launch decode
   size_t rsplit;                      // split-K router partials
+  size_t wsplit, wnorm;               // many-token router: row pieces and norms
   size_t ids, w;                      // routes of a grouped decode
   size_t gamma, count, cursor, offset, units, nunits, sorted, hhi, hlo, out;  // grouped experts
   size_t total;
@@ -225,6 +226,10 @@ inline Layout layout(const ft_moe_desc& d, int64_t T, int path) {
   if (path == 0) {
     L.logits = take(t * E * 4);
     L.rsplit = take(route_split_cap(d, T));
+    if (T >= kRouteMfmaMinTokens) {
+      L.wsplit = take(E * H * 4);
+      L.wnorm = take(E * 4);
+    }
   } else if (path == 1) {
     // the one-launch kernel's regions, then (for token counts that take the
     // grouped path) router logits, routes and the grouped regions

@@ -477,6 +477,465 @@ hipError_t launch_route_split(const RouteParams& p0, hipStream_t s) {
 
 int route_fused_topk_tokens() { return kRouteWaves; }
 
+// ------------------------------------------- many tokens: bounded approximation --
+//
+// The router of the pages sums each logit in fp64 and rounds it once to fp32; the
+// k largest win, ties to the lower index.  For thousands of tokens the fp64 MFMA
+// product of every (token, expert) pair is replaced by three steps that select
+// exactly the same experts with exactly the same logits:
+//  1. route_prep_kernel: each fp32 router row w is split into two bf16 pieces,
+//     hi = bf16(w) and mid = bf16(w - hi) (nearest-even, so |w - hi - mid| <=
+//     2^-16 |w|), and its 2-norm is taken in fp64 and rounded up.
+//  2. route_approx_kernel: A[t][e] = fp32(x_t . (hi_e + mid_e)) + bias_e, a bf16
+//     MFMA product (x is bf16, so every product is exact) accumulated in fp32.
+//  3. route_recheck_kernel, one wave per token: a rigorous bound d_e >= |A[t][e] -
+//     logit[t][e]| (below); theta = the k-th largest of A - d; every expert with
+//     A + d >= theta keeps its place as a candidate (no other one can be among the
+//     k largest logits, nor tie with them); the candidates' logits are computed
+//     exactly as the other routers do (fp64 sum, one fp32 rounding) and the top k
+//     of those are selected.  A token whose approximations or bound are not finite
+//     (NaN or infinite inputs) takes every expert as a candidate.
+//
+// The bound.  The 2H products of step 2 are exact; any order of fp32 additions,
+// each with relative error <= 2^-23 (so truncation is covered too), errs by at most
+// g_n * sum|terms|, g_n = n 2^-23 / (1 - n 2^-23) with n = 2H, and sum|terms| <=
+// (1 + 2^-7) sum_h |x_h| |w_h| <= (1 + 2^-7) ||x_t|| ||w_e|| (Cauchy-Schwarz).  The
+// dropped third piece adds 2^-16 ||x_t|| ||w_e||, the bias addition and the final
+// rounding of the exact logit at most 2^-22 |A| between them.  Step 3 takes
+// d = 1.25 (g_n (1 + 2^-7) + 2^-16) ||x_t|| ||w_e|| + 2^-21 |A| + 2^-120.
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 rb_bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float rb_f32x4;
+typedef unsigned int rb_u32x4 __attribute__((ext_vector_type(4)));
+
+// the largest of the wave's 64 values (every lane gets it); no NaN among them
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const double o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// One wave per router row: the two bf16 pieces and the row's 2-norm (rounded up).
+__global__ __launch_bounds__(256) void route_prep_kernel(RouteParams p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int e = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (e >= p.E) return;
+  const int H = p.H;
+  const float* row = p.wr + static_cast<size_t>(e) * H;
+  uint16_t* hi = p.wsplit + static_cast<size_t>(e) * 2 * H;
+  uint16_t* mid = hi + H;
+  double ss = 0.0;
+  for (int k = 8 * lane; k < H; k += 8 * kWave) {  // H % 8 == 0: whole groups of 8
+    const float4 a = *reinterpret_cast<const float4*>(row + k);
+    const float4 b = *reinterpret_cast<const float4*>(row + k + 4);
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[4], m[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t hp = 0, mp = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float w = v[2 * i + j];
+        const uint32_t hb = f32_to_bf16_bits(w);
+        const uint32_t mb = f32_to_bf16_bits(w - __uint_as_float(hb << 16));
+        hp |= hb << (16 * j);
+        mp |= mb << (16 * j);
+        ss = fma(static_cast<double>(w), static_cast<double>(w), ss);
+      }
+      h[i] = hp;
+      m[i] = mp;
+    }
+    *reinterpret_cast<uint4*>(hi + k) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4*>(mid + k) = make_uint4(m[0], m[1], m[2], m[3]);
+  }
+  ss = wave_sum_f64(ss);
+  if (lane == 0) {
+    // sqrt in fp64 (error far below the factor), widened, rounded up to fp32
+    const double n = sqrt(ss) * (1.0 + 0x1p-40);
+    float f = static_cast<float>(n);
+    if (static_cast<double>(f) < n) f = __uint_as_float(__float_as_uint(f) + 1u);  // next up (n >= 0)
+    p.wnorm[e] = f;
+  }
+}
+
+// A[t][e] for a block of 64 experts x 256 tokens, 4 waves of 64 tokens each.  The
+// block's 64 rows (both pieces) are staged in LDS, 64 K at a time, and shared by
+// the 4 waves; each wave takes its own tokens straight from global memory into
+// registers (nothing to share), a stage ahead.  A wave computes 4 x 4 fragments of
+// 16 x 16 with both pieces of a row into the same fp32 accumulator.  Rows and
+// tokens past the end repeat the last one (their results are not stored).
+constexpr int kApproxE = 64;         // experts per block
+constexpr int kApproxT = 256;        // tokens per block (64 per wave)
+constexpr int kApproxRowU4 = 8 + 1;  // 16-byte words of a staged row of 64 K (one of padding)
+
+__global__ __launch_bounds__(256) void route_approx_kernel(RouteParams p) {
+  __shared__ uint4 sa[2][2 * kApproxE * kApproxRowU4];  // [stage][(piece * 64 + row) * 9 + word]
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = p.H;
+  const int e0 = blockIdx.x * kApproxE;
+  const int t0 = blockIdx.y * kApproxT + 64 * wave;
+  const int i = lane & 15, g = lane >> 4;
+  // staging: thread tid moves words tid + 256 j (j < 4) of the stage: row (w >> 4),
+  // piece ((w >> 3) & 1), word (w & 7) of the row's 64 K
+  const uint16_t* asrc[4];
+  int adst[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int w = tid + 256 * j;
+    const int row = w >> 4, pc = (w >> 3) & 1, c8 = w & 7;
+    asrc[j] = p.wsplit + static_cast<size_t>(min(e0 + row, p.E - 1)) * 2 * H + pc * H + 8 * c8;
+    adst[j] = (pc * kApproxE + row) * kApproxRowU4 + c8;
+  }
+  const uint16_t* bsrc[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+    bsrc[f] = p.x + static_cast<size_t>(min(t0 + 16 * f + i, p.T - 1)) * H + 8 * g;
+  rb_f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = rb_f32x4{0.f, 0.f, 0.f, 0.f};
+  rb_u32x4 ra[4];  // native vectors: a copy of HIP's uint4 between memory spaces stays a memcpy
+  uint4 rb[2][4][2];
+  auto load_a = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ra[j] = *reinterpret_cast<const rb_u32x4*>(asrc[j] + k0);
+  };
+  auto load_b = [&](int k0, uint4 (&dst)[4][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) dst[f][ks] = *reinterpret_cast<const uint4*>(bsrc[f] + k0 + 32 * ks);
+  };
+  auto store_a = [&](uint4* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) reinterpret_cast<rb_u32x4*>(dst)[adst[j]] = ra[j];
+  };
+  auto compute = [&](const uint4* sa_cur, const uint4 (&b)[4][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 af[2][4];
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+        for (int fa = 0; fa < 4; ++fa)
+          af[pc][fa] = sa_cur[(pc * kApproxE + 16 * fa + i) * kApproxRowU4 + 4 * ks + g];
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+        for (int fa = 0; fa < 4; ++fa)
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb)
+            acc[fa][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(rb_bf16x8, af[pc][fa]), __builtin_bit_cast(rb_bf16x8, b[fb][ks]),
+                acc[fa][fb], 0, 0, 0);
+    }
+  };
+  const int ns = H / 64;  // stages; H % 256 == 0, so ns is even
+  load_a(0);
+  load_b(0, rb[0]);
+  store_a(sa[0]);
+  __syncthreads();
+  // two stages per pass, so that the stage buffers are compile-time indices
+  for (int s = 0; s < ns; s += 2) {
+    // stage s (buffer 0); stage s + 1's loads in flight
+    load_a(64 * (s + 1));
+    load_b(64 * (s + 1), rb[1]);
+    compute(sa[0], rb[0]);
+    store_a(sa[1]);
+    __syncthreads();
+    // stage s + 1 (buffer 1); stage s + 2's loads in flight (the last pass reloads
+    // stage s + 1, in range and never used)
+    const int kn = s + 2 < ns ? 64 * (s + 2) : 64 * (s + 1);
+    load_a(kn);
+    load_b(kn, rb[0]);
+    compute(sa[1], rb[1]);
+    if (s + 2 < ns) store_a(sa[0]);
+    __syncthreads();
+  }
+  // C lane l: expert rows 4 (l / 16) + r of the fragment, token l % 16
+#pragma unroll
+  for (int fb = 0; fb < 4; ++fb) {
+    const int t = t0 + 16 * fb + i;
+    if (t >= p.T) continue;
+    float* out = p.logits + static_cast<size_t>(t) * p.E;
+#pragma unroll
+    for (int fa = 0; fa < 4; ++fa)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = e0 + 16 * fa + 4 * g + r;
+        if (e < p.E) out[e] = acc[fa][fb][r] + (p.bias ? p.bias[e] : 0.0f);
+      }
+  }
+}
+
+// One wave per token (see the section comment).  NC = H / 256 float4 pieces of a
+// row per lane, the token's activations held in registers in fp64, or 0: any H,
+// the activations re-read (from L1) for each candidate.  SL = slots of experts per
+// lane (E <= 64 SL).  With at most 64 candidates (the usual case) each lane holds
+// one candidate and the top k are found by counting, for each candidate, the
+// candidates above it (keys (rank_key(logit), ~expert): unique, larger wins, ties to
+// the lower index); otherwise every candidate's logit goes into its slot and the
+// wave's slot top-k selects.  Either way the weights are the softmax of the
+// selected logits exactly as the other routers take it.
+template <int NC, int SL>
+__global__ __launch_bounds__(kRouteWaves* kWave) void route_recheck_kernel(RouteParams p, float cbound) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * kRouteWaves + __builtin_amdgcn_readfirstlane(wv);
+  if (t >= p.T) return;
+  const int H = p.H, E = p.E, k = p.k;
+  const int nc = NC > 0 ? NC : H / (4 * kWave);
+  const uint16_t* __restrict__ xt = p.x + static_cast<size_t>(t) * H;
+  const float* __restrict__ at = p.logits + static_cast<size_t>(t) * E;
+  float av[SL], wn[SL];
+#pragma unroll
+  for (int m = 0; m < SL; ++m) {
+    const int e = min(lane + kWave * m, E - 1);
+    av[m] = at[e];
+    wn[m] = p.wnorm[e];
+  }
+  // the token's activations (in fp64 when held) and 2-norm, rounded up
+  double xd[NC > 0 ? NC : 1][4];
+  auto xpiece = [&](int c) -> uint2 { return *reinterpret_cast<const uint2*>(xt + 4 * lane + 4 * kWave * c); };
+  auto widen = [&](uint2 x2, double (&o)[4]) {
+    o[0] = bf16_bits_to_f32(x2.x & 0xFFFFu);
+    o[1] = bf16_bits_to_f32(x2.x >> 16);
+    o[2] = bf16_bits_to_f32(x2.y & 0xFFFFu);
+    o[3] = bf16_bits_to_f32(x2.y >> 16);
+  };
+  double ss = 0.0;
+  if constexpr (NC > 0) {
+    uint2 xr[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) xr[c] = xpiece(c);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      widen(xr[c], xd[c]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ss = fma(xd[c][q], xd[c][q], ss);
+    }
+  } else {
+    for (int c = 0; c < nc; ++c) {
+      double o[4];
+      widen(xpiece(c), o);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ss = fma(o[q], o[q], ss);
+    }
+  }
+  const double xnd = sqrt(wave_sum_f64(ss)) * (1.0 + 0x1p-40);
+  float xn = static_cast<float>(xnd);
+  if (static_cast<double>(xn) < xnd) xn = __uint_as_float(__float_as_uint(xn) + 1u);  // up
+  // bounds in fp32: the bound's own roundings (a few 2^-24 relative) are covered by
+  // the (1 + 2^-20) on its first term and 2^-20 instead of 2^-21 on |A|
+  float lo[SL], hi[SL];
+  bool finite = __builtin_isfinite(xn);
+#pragma unroll
+  for (int m = 0; m < SL; ++m) {
+    const bool valid = lane + kWave * m < E;
+    const float a = av[m];
+    const float d = (cbound * xn * wn[m]) * (1.0f + 0x1p-20f) + 0x1p-20f * __builtin_fabsf(a) + 0x1p-120f;
+    lo[m] = valid ? a - d : -__builtin_inff();
+    hi[m] = a + d;
+    if (valid) finite = finite && __builtin_isfinite(a) && __builtin_isfinite(d);
+  }
+  const bool all = __ballot(!finite) != 0;  // a non-finite value: every expert a candidate
+  float theta = -__builtin_inff();
+  if (!all) {
+    // k rounds on rank keys: the largest remaining lower end, one instance removed
+    uint32_t rk[SL];
+#pragma unroll
+    for (int m = 0; m < SL; ++m) rk[m] = rank_key(lo[m]);  // -inf (past E) still ranks
+    uint32_t kth = 0;
+    for (int r = 0; r < k; ++r) {
+      uint32_t lm = rk[0];
+#pragma unroll
+      for (int m = 1; m < SL; ++m) lm = rk[m] > lm ? rk[m] : lm;
+      kth = wave_max_u32(lm);
+      const uint64_t holders = __ballot(lm == kth);
+      if (lane == __ffsll(static_cast<unsigned long long>(holders)) - 1) {
+        bool done = false;
+#pragma unroll
+        for (int m = 0; m < SL; ++m)
+          if (!done && rk[m] == kth) {
+            rk[m] = 0u;
+            done = true;
+          }
+      }
+    }
+    theta = key_value(kth);
+  }
+  // candidates, listed in LDS in expert order
+  __shared__ int s_list[kRouteWaves][kMaxExperts];
+  int* list = s_list[wv];
+  int n = 0;
+#pragma unroll
+  for (int m = 0; m < SL; ++m) {
+    const bool c = (lane + kWave * m < E) && (all || hi[m] >= theta);
+    const uint64_t bits = __ballot(c);
+    if (c) list[n + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bits >> 32),
+                                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bits), 0))] =
+        lane + kWave * m;
+    n += __builtin_popcountll(bits);
+  }
+  wave_lds_sync();
+  // exact logit of expert e, as the row router sums it (per lane in piece order,
+  // then the wave's fixed tree), CB experts at a time with their loads together
+  constexpr int CB = 2;
+  auto exact = [&](const int (&ce)[CB], float (&out)[CB]) {
+    double acc[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[j] = 0.0;
+    if constexpr (NC > 0) {
+      float4 w4[CB][NC];
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          w4[j][c] = *reinterpret_cast<const float4*>(p.wr + static_cast<size_t>(ce[j]) * H + 4 * lane + 4 * kWave * c);
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          acc[j] = fma(static_cast<double>(w4[j][c].x), xd[c][0], acc[j]);
+          acc[j] = fma(static_cast<double>(w4[j][c].y), xd[c][1], acc[j]);
+          acc[j] = fma(static_cast<double>(w4[j][c].z), xd[c][2], acc[j]);
+          acc[j] = fma(static_cast<double>(w4[j][c].w), xd[c][3], acc[j]);
+        }
+    } else {
+      for (int c = 0; c < nc; ++c) {
+        double o[4];
+        widen(xpiece(c), o);
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+          const float4 w = *reinterpret_cast<const float4*>(p.wr + static_cast<size_t>(ce[j]) * H + 4 * lane + 4 * kWave * c);
+          acc[j] = fma(static_cast<double>(w.x), o[0], acc[j]);
+          acc[j] = fma(static_cast<double>(w.y), o[1], acc[j]);
+          acc[j] = fma(static_cast<double>(w.z), o[2], acc[j]);
+          acc[j] = fma(static_cast<double>(w.w), o[3], acc[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      double v = wave_sum_f64(acc[j]);
+      if (p.bias) v += static_cast<double>(p.bias[ce[j]]);
+      out[j] = static_cast<float>(v);
+    }
+  };
+  auto batch = [&](int j0, int (&ce)[CB]) {
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+      ce[j] = __builtin_amdgcn_readfirstlane(list[j0 + j < n ? j0 + j : n - 1]);  // past the end: repeat
+  };
+  int id = -1;
+  float wt = 0.0f;
+  if (!all && n <= kWave) {
+    // lane j: candidate j
+    float cv = 0.0f;
+    for (int j0 = 0; j0 < n; j0 += CB) {
+      int ce[CB];
+      float v[CB];
+      batch(j0, ce);
+      exact(ce, v);
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        if (lane == j0 + j) cv = v[j];
+    }
+    const int ce_mine = lane < n ? list[lane] : 0;
+    const uint64_t key = lane < n ? (static_cast<uint64_t>(rank_key(cv)) << 32) |
+                                        static_cast<uint32_t>(~ce_mine)
+                                  : 0ull;
+    int above = 0;
+    for (int i = 0; i < n; ++i) {
+      const uint64_t ki = (static_cast<uint64_t>(static_cast<uint32_t>(
+                               __builtin_amdgcn_readlane(static_cast<int>(key >> 32), i)))
+                           << 32) |
+                          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), i));
+      above += ki > key ? 1 : 0;
+    }
+    // place r -> lane r: the candidate with r candidates above it
+    __shared__ int s_pid[kRouteWaves][kTopkMaxK];
+    __shared__ float s_pv[kRouteWaves][kTopkMaxK];
+    if (lane < n && above < k) {
+      s_pid[wv][above] = ce_mine;
+      s_pv[wv][above] = key_value(rank_key(cv));
+    }
+    wave_lds_sync();
+    const double vd = lane < k ? static_cast<double>(s_pv[wv][lane]) : 0.0;
+    const double top = readlane_f64(vd, 0);
+    const double dd = lane < k ? exp(vd - top) : 0.0;
+    double sum = 0.0;
+    for (int i = 0; i < k; ++i) sum += readlane_f64(dd, i);
+    if (lane < k) {
+      id = s_pid[wv][lane];
+      wt = static_cast<float>(dd / sum);
+    }
+  } else {
+    float lv[SL];
+#pragma unroll
+    for (int m = 0; m < SL; ++m) lv[m] = -__builtin_inff();
+    for (int j0 = 0; j0 < n; j0 += CB) {
+      int ce[CB];
+      float v[CB];
+      batch(j0, ce);
+      exact(ce, v);
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        if (j0 + j < n) {
+#pragma unroll
+          for (int m = 0; m < SL; ++m)
+            if (lane + kWave * m == ce[j]) lv[m] = v[j];
+        }
+    }
+    wave_topk_vals<SL>(E, k, lv, &id, &wt);
+  }
+  if (lane < k) {
+    const size_t o = static_cast<size_t>(t) * k + lane;
+    p.ids[o] = id;
+    p.w[o] = wt;
+    if (p.ids_copy) p.ids_copy[o] = id;
+    if (p.w_copy) p.w_copy[o] = wt;
+  }
+}
+
+// 1.25 (g_n (1 + 2^-7) + 2^-16) for n = 2H products (see the section comment)
+static float route_bound_factor(int H) {
+  const double nu = 2.0 * H * 0x1p-23;
+  return static_cast<float>(1.25 * (nu / (1.0 - nu) * (1.0 + 0x1p-7) + 0x1p-16));
+}
+
+
+hipError_t launch_route_bounded(const RouteParams& p, hipStream_t s) {
+  if (p.T <= 0) return hipSuccess;
+  route_prep_kernel<<<dim3((p.E + 3) / 4), dim3(256), 0, s>>>(p);
+  route_approx_kernel<<<dim3((p.E + kApproxE - 1) / kApproxE, (p.T + kApproxT - 1) / kApproxT),
+                        dim3(256), 0, s>>>(p);
+  const float cb = route_bound_factor(p.H);
+  const dim3 grid((p.T + kRouteWaves - 1) / kRouteWaves), block(kRouteWaves * kWave);
+  const int nc = p.H / (4 * kWave);
+  const int sl = p.E <= 4 * kWave ? 4 : (p.E <= 8 * kWave ? 8 : 16);
+#define FTMOE_RECHECK(NCV)                                                         \
+  if (sl == 4) route_recheck_kernel<NCV, 4><<<grid, block, 0, s>>>(p, cb);        \
+  else if (sl == 8) route_recheck_kernel<NCV, 8><<<grid, block, 0, s>>>(p, cb);   \
+  else route_recheck_kernel<NCV, 16><<<grid, block, 0, s>>>(p, cb);
+  if (nc == 4) {
+    FTMOE_RECHECK(4)
+  } else if (nc == 8) {
+    FTMOE_RECHECK(8)
+  } else if (nc == 16) {
+    FTMOE_RECHECK(16)
+  } else {
+    FTMOE_RECHECK(0)
+  }
+#undef FTMOE_RECHECK
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const RouteParams& p0, bool fuse_topk, hipStream_t s) {
   RouteParams p = p0;
   const int rows = p.E + (p.shared_gate ? 1 : 0);

@@ -193,7 +193,7 @@ def test_route_matches_oracle(gpu, name, tokens):
     _check_routes(ids, wt, ref_ids, ref_w, f"{name} T={tokens}")
 
 
-@pytest.mark.parametrize("tokens", [16, 40])  # row router, split-K router
+@pytest.mark.parametrize("tokens", [16, 40, 1100])  # row, split-K and bounded routers
 def test_route_ties_go_to_lowest_index(gpu, tokens):
     """Duplicated router rows give exactly equal logits; the lower index must win."""
     from nvfp4_mixture_experts_amd import ftmoe
@@ -312,6 +312,56 @@ def test_route_many_experts_split_router(gpu, num_experts):
     torch.cuda.synchronize()
     ref_ids, ref_w = oracle.topk(oracle.router_logits(x, wr, bias), w.top_k)
     _check_routes(ids, wt, ref_ids, ref_w, f"E={num_experts} T={tokens}")
+
+
+@pytest.mark.parametrize("num_experts", [1000, 1024, 200])
+def test_route_bounded_many_tokens(gpu, num_experts):
+    """1100 tokens (the bounded router: bf16 approximations, exact recheck of the
+    experts the error bound leaves in play) with 1000, 1024 and 200 experts and a
+    router bias, every token against the oracle."""
+    from nvfp4_mixture_experts_amd import ftmoe
+    tokens = 1100
+    w = synth.dataclasses.replace(synth.WORKLOADS["batched_decode_t32_hot64"],
+                                  num_experts=num_experts, hot_experts=min(64, num_experts // 4))
+    wr, bias = synth.make_router(w)
+    assert bias is not None
+    x = synth.make_tokens(w, tokens=tokens, stream="bounded")
+    desc = ftmoe.make_desc(num_experts, w.hidden, w.inter, w.top_k, 1)
+    wsp = ftmoe.alloc_workspace(desc, tokens, ftmoe.PATH_ROUTE)
+    ids = torch.empty((tokens, w.top_k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((tokens, w.top_k), dtype=torch.float32, device="cuda")
+    ftmoe.ft_moe_route(desc, gpu.tokens_to_device(x), torch.from_numpy(wr).cuda(),
+                       torch.from_numpy(bias).cuda(), ids, wt, wsp)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.topk(oracle.router_logits(x, wr, bias), w.top_k)
+    _check_routes(ids, wt, ref_ids, ref_w, f"bounded E={num_experts} T={tokens}")
+
+
+def test_route_bounded_nonfinite_tokens(gpu):
+    """Tokens with an infinite or NaN activation among 1100 finite ones: those tokens
+    take every expert exactly (their logits are infinite or NaN), the others the
+    bounded candidates; the oracle decides ids (ties of +inf to the lower index) and
+    which weights are NaN."""
+    from nvfp4_mixture_experts_amd import ftmoe
+    tokens, E, k, H = 1100, 64, 6, 512
+    rng = np.random.default_rng(77)
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    xf = rng.standard_normal((tokens, H)).astype(np.float32)
+    xf[3, 10] = np.inf
+    xf[700, 0] = -np.inf
+    xf[5, 99] = np.nan
+    x = synth.bf16_bits_from_f32(xf)
+    logits = oracle.router_logits(x, wr)
+    ref_ids, ref_w = oracle.topk(logits, k)
+    assert np.isinf(logits[3]).all() and np.isnan(logits[5]).all()
+    desc = ftmoe.make_desc(E, H, 128, k, 1)
+    ws = ftmoe.alloc_workspace(desc, tokens, ftmoe.PATH_ROUTE)
+    ids = torch.empty((tokens, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((tokens, k), dtype=torch.float32, device="cuda")
+    ftmoe.ft_moe_route(desc, gpu.tokens_to_device(x), torch.from_numpy(wr).cuda(), None, ids, wt,
+                       ws)
+    torch.cuda.synchronize()
+    _routes_nan_aware(ids, wt, ref_ids, ref_w, "bounded router, non-finite tokens")
 
 
 # ----------------------------------------------------------------- decode --
