@@ -13,9 +13,12 @@
 //   y    = bf16( (sum_k xq * w) * s_x * s_w[n] )   fp32 accumulation on the MFMA units
 //
 // Kernels: per-block amax partials; quantisation (every block reduces the partials
-// itself, so there is no atomic and nothing to reset between calls); the GEMM on
-// v_mfma_f32_16x16x32_fp8_fp8, 64 x 64 output tiles per 4-wave block, 64-deep K slabs
-// staged in LDS.
+// itself, so there is no atomic and nothing to reset between calls), or for small
+// activations (M K <= 16 Ki) both in one block; the GEMM on v_mfma_f32_16x16x32_fp8_fp8,
+// 64 x 64 output tiles per 4-wave block, 64-deep K slabs staged in LDS, or for M <= 8
+// rows of activations (decode) a GEMV: a wave per 4 weight rows, each lane 32 K bytes
+// of them with all of its loads in flight at once, codes widened to bf16 pairs
+// (exactly: an e4m3 value has 4 significant bits) into v_dot2_f32_bf16.
 #include "ftmoe_device.hpp"
 #include "ftmoe_kernels.hpp"
 
@@ -23,6 +26,9 @@ namespace ftmoe {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// native vector: a HIP uint4 copied from global memory to LDS stays a memcpy through
+// private memory
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAmaxThreads = 256;
 constexpr int kTile = 64;       // output rows and columns of a block
@@ -107,17 +113,17 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemm_kernel(
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-  uint4 an = a_in ? *reinterpret_cast<const uint4*>(ag) : zero;
-  uint4 bn = b_in ? *reinterpret_cast<const uint4*>(bg) : zero;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 an = a_in ? *reinterpret_cast<const u32x4*>(ag) : zero;
+  u32x4 bn = b_in ? *reinterpret_cast<const u32x4*>(bg) : zero;
   for (int k0 = 0; k0 < K; k0 += kSlab) {
     __syncthreads();  // the previous slab's fragments have been read
-    *reinterpret_cast<uint4*>(&As[sr * kLdsRow + sk]) = an;
-    *reinterpret_cast<uint4*>(&Bs[sr * kLdsRow + sk]) = bn;
+    *reinterpret_cast<u32x4*>(&As[sr * kLdsRow + sk]) = an;
+    *reinterpret_cast<u32x4*>(&Bs[sr * kLdsRow + sk]) = bn;
     __syncthreads();
     if (k0 + kSlab < K) {  // next slab's loads travel during this slab's MFMAs
-      an = a_in ? *reinterpret_cast<const uint4*>(ag + k0 + kSlab) : zero;
-      bn = b_in ? *reinterpret_cast<const uint4*>(bg + k0 + kSlab) : zero;
+      an = a_in ? *reinterpret_cast<const u32x4*>(ag + k0 + kSlab) : zero;
+      bn = b_in ? *reinterpret_cast<const u32x4*>(bg + k0 + kSlab) : zero;
     }
 #pragma unroll
     for (int ks = 0; ks < kSlab; ks += 32) {
@@ -152,6 +158,124 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemm_kernel(
   }
 }
 
+// Small activations: amax, s_x and the codes in one block of 1024 threads (the
+// same arithmetic as the two kernels above).
+constexpr int kSmallQuantThreads = 1024;
+constexpr size_t kSmallQuantMax = 16384;  // M K handled by the one-block kernel
+
+__global__ __launch_bounds__(kSmallQuantThreads) void fp8_quantize_small_kernel(
+    const uint16_t* __restrict__ x, int n, uint8_t* __restrict__ q, float* scale_out) {
+  __shared__ float red[kSmallQuantThreads / kWave];
+  __shared__ float s_scale;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += kSmallQuantThreads) m = fmaxf(m, fabsf(bf16_at(x, i)));
+  m = __int_as_float(static_cast<int>(wave_max_u32(__float_as_uint(m))));
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = red[0];
+    for (int w = 1; w < kSmallQuantThreads / kWave; ++w) b = fmaxf(b, red[w]);
+    const float sc = b > 0.0f ? __fdiv_rn(b, 448.0f) : 1.0f;
+    s_scale = sc;
+    *scale_out = sc;
+  }
+  __syncthreads();
+  const float sc = s_scale;
+  for (int i = 4 * threadIdx.x; i < n; i += 4 * kSmallQuantThreads) {  // n % 4 == 0
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float t = __fdiv_rn(bf16_at(x, i + j), sc);
+      v[j] = fminf(fmaxf(t, -448.0f), 448.0f);
+    }
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0u, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+    *reinterpret_cast<uint32_t*>(q + i) = w;
+  }
+}
+
+// y[m, col0 + n] for M <= MM rows of activation codes: wave (block b, wave v) takes
+// weight rows n0 .. n0 + 3 (n0 = 4 (4 b + v)); lane l takes the 16-byte K chunks
+// l, l + 64, ... of each row (loaded for the 4 rows and the M activation rows, then
+// multiplied); per (row, m) the lanes' sums are added over the wave.  Rows past N
+// and chunks past K contribute nothing.
+constexpr int kGemvRows = 4;
+constexpr int kGemvMaxM = 8;
+constexpr int kGemvChunks = 2;  // 16-byte K chunks per lane and pass (K 2048 per pass)
+
+template <int MM>
+__global__ __launch_bounds__(4 * kWave) void fp8_gemv_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w, int M, int N, int K,
+    const float* __restrict__ s_x, const float* __restrict__ row_scale, float scale,
+    uint16_t* __restrict__ y, int ldy, int col0) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kGemvRows;
+  if (n0 >= N) return;
+  const int nch = K / 16;
+  float acc[kGemvRows][MM];
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+    for (int m = 0; m < MM; ++m) acc[r][m] = 0.0f;
+  for (int c0 = 0; c0 < nch; c0 += kGemvChunks * kWave) {
+    uint4 wv[kGemvRows][kGemvChunks], xv[MM][kGemvChunks];
+    bool ok[kGemvChunks];
+#pragma unroll
+    for (int j = 0; j < kGemvChunks; ++j) {
+      const int ci = c0 + j * kWave + lane;
+      ok[j] = ci < nch;
+      const int cc = ok[j] ? ci : nch - 1;  // in range; its terms are dropped below
+#pragma unroll
+      for (int r = 0; r < kGemvRows; ++r) {
+        const int n = n0 + r < N ? n0 + r : N - 1;
+        wv[r][j] = *reinterpret_cast<const uint4*>(w + static_cast<size_t>(n) * K + 16 * cc);
+      }
+#pragma unroll
+      for (int m = 0; m < MM; ++m) {
+        const int mm = m < M ? m : M - 1;
+        xv[m][j] = *reinterpret_cast<const uint4*>(xq + static_cast<size_t>(mm) * K + 16 * cc);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kGemvChunks; ++j) {
+      if (!ok[j]) continue;
+#pragma unroll
+      for (int m = 0; m < MM; ++m) {
+        bf16x2 xb[8];
+        const uint32_t xw[4] = {xv[m][j].x, xv[m][j].y, xv[m][j].z, xv[m][j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xb[2 * q] = e4m3x2_to_bf16<false>(xw[q]);
+          xb[2 * q + 1] = e4m3x2_to_bf16<true>(xw[q]);
+        }
+#pragma unroll
+        for (int r = 0; r < kGemvRows; ++r) {
+          const uint32_t ww[4] = {wv[r][j].x, wv[r][j].y, wv[r][j].z, wv[r][j].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[r][m] = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16<false>(ww[q]), xb[2 * q],
+                                                        acc[r][m], false);
+            acc[r][m] = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16<true>(ww[q]), xb[2 * q + 1],
+                                                        acc[r][m], false);
+          }
+        }
+      }
+    }
+  }
+  const float sx = *s_x;
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r) {
+    const int n = n0 + r;
+    const float sn = sx * (row_scale ? row_scale[n < N ? n : N - 1] : scale);
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      const float v = group_sum_last<kWave>(acc[r][m]);  // in lane 63
+      if (lane == kWave - 1 && n < N && m < M)
+        y[static_cast<size_t>(m) * ldy + col0 + n] = f32_to_bf16_bits(v * sn);
+    }
+  }
+}
+
 int amax_blocks(size_t n) {
   const size_t b = (n + kAmaxThreads * 16 - 1) / (kAmaxThreads * 16);
   return static_cast<int>(b < 1 ? 1 : (b > 1024 ? 1024 : b));
@@ -171,6 +295,11 @@ hipError_t launch_fp8_quantize(const uint16_t* x, int64_t M, int64_t K, void* ws
   *xq = base;
   float* partial = reinterpret_cast<float*>(base + align256(n));
   *s_x = reinterpret_cast<float*>(base + align256(n) + align256(1024 * sizeof(float)));
+  if (n <= kSmallQuantMax) {
+    fp8_quantize_small_kernel<<<dim3(1), dim3(kSmallQuantThreads), 0, s>>>(x, static_cast<int>(n),
+                                                                            *xq, *s_x);
+    return hipGetLastError();
+  }
   const int nb = amax_blocks(n);
   fp8_amax_kernel<<<dim3(nb), dim3(kAmaxThreads), 0, s>>>(x, n, partial);
   hipError_t e = hipGetLastError();
@@ -185,6 +314,14 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const uint8_t* w, int M, int N, in
                            const float* s_x, const float* row_scale, float scale, uint16_t* y,
                            int ldy, int col0, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (M <= kGemvMaxM) {
+    const dim3 g((N + 4 * kGemvRows - 1) / (4 * kGemvRows)), b(4 * kWave);
+    if (M == 1) fp8_gemv_kernel<1><<<g, b, 0, s>>>(xq, w, M, N, K, s_x, row_scale, scale, y, ldy, col0);
+    else if (M == 2) fp8_gemv_kernel<2><<<g, b, 0, s>>>(xq, w, M, N, K, s_x, row_scale, scale, y, ldy, col0);
+    else if (M <= 4) fp8_gemv_kernel<4><<<g, b, 0, s>>>(xq, w, M, N, K, s_x, row_scale, scale, y, ldy, col0);
+    else fp8_gemv_kernel<8><<<g, b, 0, s>>>(xq, w, M, N, K, s_x, row_scale, scale, y, ldy, col0);
+    return hipGetLastError();
+  }
   const dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
   fp8_gemm_kernel<<<grid, dim3(4 * kWave), 0, s>>>(xq, w, M, N, K, s_x, row_scale, scale, y, ldy,
                                                    col0);

@@ -67,7 +67,7 @@ def test_fp8_quantize_codes_bit_exact_with_ties(ft):
     assert s.item() == want_s
 
 
-@pytest.mark.parametrize("tokens", [1, 32, 77])
+@pytest.mark.parametrize("tokens", [1, 2, 8, 32, 77])   # GEMV (<= 8 rows), MFMA GEMM
 def test_fp8_linear_matches_oracle_and_parts_equal_rowwise(ft, tokens):
     w = synth.WORKLOADS["fp8_linear_qkv_t32"]
     lin = synth.make_fp8_linear(w)
@@ -94,10 +94,12 @@ def test_fp8_linear_matches_oracle_and_parts_equal_rowwise(ft, tokens):
     assert np.array_equal(_bits(yp), _bits(y))
 
 
-def test_fp8_linear_ragged_parts_and_rows(ft):
-    # parts whose row counts are not multiples of the 64-row tile
-    w = synth.dataclasses.replace(synth.WORKLOADS["fp8_linear_qkv_t32"], hidden=1024,
-                                  parts=(100, 37, 200), tokens=19)
+@pytest.mark.parametrize("tokens,hidden", [(19, 1024), (5, 1024), (3, 1088)])
+def test_fp8_linear_ragged_parts_and_rows(ft, tokens, hidden):
+    # parts whose row counts are not multiples of the 64-row tile (nor of the GEMV's
+    # 16 rows per block); K = 1088: 68 16-byte chunks, so most GEMV lanes hold one
+    w = synth.dataclasses.replace(synth.WORKLOADS["fp8_linear_qkv_t32"], hidden=hidden,
+                                  parts=(100, 37, 200), tokens=tokens)
     lin = synth.make_fp8_linear(w)
     x = synth.make_tokens(w, stream="ragged")
     xq, s_x = oracle.fp8_quantize(x)
@@ -111,7 +113,7 @@ def test_fp8_linear_ragged_parts_and_rows(ft):
     yp = torch.full_like(y, float("nan"))
     ft.ft_fp8_linear_parts(xd, wd, pr, ps, yp, ws)
     torch.cuda.synchronize()
-    assert_output_close(_bits(y), want, "fp8 linear ragged")
+    assert_output_close(_bits(y), want, f"fp8 linear ragged T={tokens} K={hidden}")
     assert np.array_equal(_bits(yp), _bits(y))
 
 
