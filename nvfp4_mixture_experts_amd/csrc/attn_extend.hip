@@ -15,15 +15,17 @@
 //   1. the chunk's keys and values are turned into bf16 in LDS (exact for every
 //      format: an e4m3 value, or an e2m1 code times its e4m3 block scale, has at most
 //      6 significant bits), keys as rows [key][dim], values transposed [dim][key];
-//   2. S = Q K^T on v_mfma_f32_16x16x32_bf16 (each wave its 16 rows x 64 keys, Q in
+//   2. S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (each wave 64 keys x its 16 rows, Q in
 //      registers), times the key tensor scale and 1/sqrt(d) on the dot outputs, keys
-//      outside a row's causal / window range masked;
-//   3. online softmax per row in fp32 (base-2 exponentials); the normaliser sums the
-//      unscaled probabilities; P times the value tensor scale goes through LDS to the
-//      MFMA operand layout as a bf16 pair (hi = bf16(p), lo = bf16(p - hi): about 16
+//      outside a row's causal / window range masked.  In the result's layout a lane
+//      holds 16 scores of ONE query row (keys 16 c + 4 (lane / 16) + r), which is the
+//      operand layout of P^T for v_mfma_f32_16x16x16_bf16: P never leaves registers;
+//   3. online softmax per row in fp32 (base-2 exponentials, the row spread over 4
+//      lanes); the normaliser sums the unscaled probabilities; P times the value
+//      tensor scale as a bf16 pair (hi = bf16(p), lo = bf16(p - hi): about 16
 //      significant bits; one bf16 alone costs the output about 2e-3 of relative L2);
-//   4. O = O * alpha + P V on the MFMA (each wave 16 rows x d; the hi and lo products
-//      into the same accumulator).
+//   4. O^T = O^T * alpha + V^T P^T on v_mfma_f32_16x16x16_bf16 (each wave d x 16 rows;
+//      the hi and lo products into the same accumulator).
 // At the end O / l is rounded to bf16.
 #include "ftmoe_device.hpp"
 #include "ftmoe_kernels.hpp"
@@ -34,6 +36,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 at_bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float at_f32x4;
 typedef unsigned int at_u32x4 __attribute__((ext_vector_type(4)));
+typedef short at_s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnWaves = 4;
 constexpr int kAttnRows = 16 * kAttnWaves;  // query rows per block
@@ -44,12 +47,16 @@ template <int D>
 struct AttnLds {
   uint16_t k[kChunk][D + 8];             // keys of the chunk, bf16 (8 of padding)
   uint16_t vt[D][kChunk + 8];            // values transposed, bf16
-  uint16_t p[kAttnWaves][2][16][kChunk + 8];  // a wave's probabilities, bf16 hi and lo
 };
 
 __device__ __forceinline__ at_f32x4 mfma(at_u32x4 a, at_u32x4 b, at_f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(at_bf16x8, a),
                                                  __builtin_bit_cast(at_bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ at_f32x4 mfma16(uint2 a, uint2 b, at_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(at_s16x4, a),
+                                                   __builtin_bit_cast(at_s16x4, b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t pk(bf16x2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -140,9 +147,9 @@ __device__ __forceinline__ void store_chunk(AttnLds<D>& lds, const ChunkRaw<D>& 
 
 template <int D>
 struct RowState {
-  float m[4], l[4];       // running max (base 2) and normaliser of the lane's 4 rows
-  at_f32x4 o[D / 16];     // output fragments (dims 16 f + lane % 16)
-  int lo[4], hi[4];       // visible key positions [lo, hi] of the lane's 4 rows
+  float m, l;             // running max (base 2) and normaliser of the lane's query row
+  at_f32x4 o[D / 16];     // O^T fragments: dims 16 f + 4 (lane / 16) + r of that row
+  int lo, hi;             // visible key positions [lo, hi] of the row
 };
 
 // One chunk [c0, end) (end - c0 <= 64) of one source against the wave's 16 rows.
@@ -151,76 +158,63 @@ template <int D, int FMT>
 __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)[D / 32], int c0,
                                            int end, float kscale2, float vscale, RowState<D>& st) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
-  // S = Q K^T: 4 key fragments of 16
+  // S^T = K Q^T: key fragments c of 16; lane: keys 16 c + 4 g + r of query row i
   at_f32x4 s[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     s[c] = at_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
-      s[c] = mfma(qf[ks], *reinterpret_cast<const at_u32x4*>(&lds.k[16 * c + i][32 * ks + 8 * g]),
+      s[c] = mfma(*reinterpret_cast<const at_u32x4*>(&lds.k[16 * c + i][32 * ks + 8 * g]), qf[ks],
                   s[c]);
   }
-  // lane: rows 4 g + r, keys 16 c + i
-  float alpha[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int kpos = c0 + 16 * c + i;
-      const bool vis = kpos < end && kpos >= st.lo[r] && kpos <= st.hi[r];
-      const float v = vis ? s[c][r] * kscale2 : -INFINITY;
-      s[c][r] = v;
-      mx = fmaxf(mx, v);
-    }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
-    const float mn = fmaxf(st.m[r], mx);
-    // no visible key so far: nothing to rescale, every probability 0
-    alpha[r] = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m[r] - mn);
-    float sum = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float pj = mn == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[c][r] - mn);
-      s[c][r] = pj;
-      sum += pj;
-    }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off, kWave);
-    st.l[r] = st.l[r] * alpha[r] + sum;
-    st.m[r] = mn;
-  }
-  // P (times the value scale) as a bf16 pair into the wave's LDS rows, read back as
-  // the A operand (row i, keys 32 ks + 8 g ..)
+  float mx = -INFINITY;
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float pv = s[c][r] * vscale;
-      const uint16_t hb = f32_to_bf16_bits(pv);
-      lds.p[wave][0][4 * g + r][16 * c + i] = hb;
-      lds.p[wave][1][4 * g + r][16 * c + i] = f32_to_bf16_bits(pv - bf16_bits_to_f32(hb));
+      const int kpos = c0 + 16 * c + 4 * g + r;
+      const bool vis = kpos < end && kpos >= st.lo && kpos <= st.hi;
+      const float v = vis ? s[c][r] * kscale2 : -INFINITY;
+      s[c][r] = v;
+      mx = fmaxf(mx, v);
     }
-  wave_lds_sync();
-  at_u32x4 pf[2][2];
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  const float mn = fmaxf(st.m, mx);
+  // no visible key so far: nothing to rescale, every probability 0
+  const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
+  float sum = 0.0f;
+  uint2 ph[4], pl[4];  // P^T operands: keys 16 c + 4 g .. + 3, bf16 hi and lo
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int c = 0; c < 4; ++c) {
+    uint32_t hb[4], lb[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      pf[h][ks] = *reinterpret_cast<const at_u32x4*>(&lds.p[wave][h][i][32 * ks + 8 * g]);
-  // O = O alpha + P V
+    for (int r = 0; r < 4; ++r) {
+      const float pj = mn == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[c][r] - mn);
+      sum += pj;
+      const float pv = pj * vscale;
+      hb[r] = f32_to_bf16_bits(pv);
+      lb[r] = f32_to_bf16_bits(pv - bf16_bits_to_f32(hb[r]));
+    }
+    ph[c] = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+    pl[c] = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+  }
+  sum += __shfl_xor(sum, 16, kWave);
+  sum += __shfl_xor(sum, 32, kWave);
+  st.l = st.l * alpha + sum;
+  st.m = mn;
+  // O^T = O^T alpha + V^T P^T (V^T operand: dims 16 f + i, keys 16 c + 4 g .. + 3)
 #pragma unroll
   for (int f = 0; f < D / 16; ++f) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st.o[f][r] *= alpha[r];
+    for (int r = 0; r < 4; ++r) st.o[f][r] *= alpha;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const at_u32x4 v = *reinterpret_cast<const at_u32x4*>(&lds.vt[16 * f + i][32 * ks + 8 * g]);
-      st.o[f] = mfma(pf[0][ks], v, st.o[f]);
-      st.o[f] = mfma(pf[1][ks], v, st.o[f]);
+    for (int c = 0; c < 4; ++c) {
+      const uint2 v = *reinterpret_cast<const uint2*>(&lds.vt[16 * f + i][16 * c + 4 * g]);
+      st.o[f] = mfma16(v, ph[c], st.o[f]);
+      st.o[f] = mfma16(v, pl[c], st.o[f]);
     }
   }
 }
@@ -263,15 +257,14 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_extend_kernel(AttnPara
     const int qpos = p.prefix + t;
     return p.window > 0 ? (qpos - p.window + 1 > 0 ? qpos - p.window + 1 : 0) : 0;
   };
-  // this lane's rows of S and O: 16 wave + 4 g + r; its row of the Q operand: 16 wave + i
+  // this lane's query row: 16 wave + i (its row of the Q operand and of S^T, O^T)
   RowState<D> st;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = token_of(r0 + 16 * wave + 4 * g + r);
-    st.m[r] = -INFINITY;
-    st.l[r] = 0.0f;
-    st.lo[r] = lo_of(t);
-    st.hi[r] = p.prefix + t;
+  {
+    const int t = token_of(r0 + 16 * wave + i);
+    st.m = -INFINITY;
+    st.l = 0.0f;
+    st.lo = lo_of(t);
+    st.hi = p.prefix + t;
   }
 #pragma unroll
   for (int f = 0; f < D / 16; ++f) st.o[f] = at_f32x4{0.f, 0.f, 0.f, 0.f};
@@ -295,16 +288,18 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_extend_kernel(AttnPara
   const int n0 = klo > p.prefix ? klo : p.prefix;
   attend_range<D, 0>(lds, qf, p.k_new, p.v_new, nullptr, nullptr, p.prefix, n0, khi, p.Hkv, kh, s2,
                      1.0f, st);
-  // O / l (every row sees its own position, so l > 0)
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = r0 + 16 * wave + 4 * g + r;
-    if (row >= nrows) continue;
+  // O / l (every row sees its own position, so l > 0); lane: dims 16 f + 4 g .. + 3
+  const int row = r0 + 16 * wave + i;
+  if (row < nrows) {
     const int t = row / G, h = kh * G + row % G;
     uint16_t* orow = p.out + (static_cast<size_t>(t) * p.Hq + h) * D;
-    const float inv = 1.0f / st.l[r];
+    const float inv = 1.0f / st.l;
 #pragma unroll
-    for (int f = 0; f < D / 16; ++f) orow[16 * f + i] = f32_to_bf16_bits(st.o[f][r] * inv);
+    for (int f = 0; f < D / 16; ++f) {
+      const uint32_t b0 = f32_to_bf16_bits(st.o[f][0] * inv), b1 = f32_to_bf16_bits(st.o[f][1] * inv);
+      const uint32_t b2 = f32_to_bf16_bits(st.o[f][2] * inv), b3 = f32_to_bf16_bits(st.o[f][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * f + 4 * g) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
   }
 }
 
