@@ -37,6 +37,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 at_bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float at_f32x4;
 typedef unsigned int at_u32x4 __attribute__((ext_vector_type(4)));
 typedef short at_s16x4 __attribute__((ext_vector_type(4)));
+typedef float at_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 at_bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kAttnWaves = 4;
 constexpr int kAttnRows = 16 * kAttnWaves;  // query rows per block
@@ -150,6 +152,7 @@ struct RowState {
   float m, l;             // running max (base 2) and normaliser of the lane's query row
   at_f32x4 o[D / 16];     // O^T fragments: dims 16 f + 4 (lane / 16) + r of that row
   int lo, hi;             // visible key positions [lo, hi] of the row
+  int all_lo, all_hi;     // keys in [all_lo, all_hi] are visible to every row of the block
 };
 
 // One chunk [c0, end) (end - c0 <= 64) of one source against the wave's 16 rows.
@@ -170,12 +173,14 @@ __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)
                   s[c]);
   }
   float mx = -INFINITY;
+  // a whole chunk inside every row's visible range needs no mask (most cache chunks)
+  const bool whole = end - c0 == kChunk && c0 >= st.all_lo && end - 1 <= st.all_hi;
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int kpos = c0 + 16 * c + 4 * g + r;
-      const bool vis = kpos < end && kpos >= st.lo && kpos <= st.hi;
+      const bool vis = whole || (kpos < end && kpos >= st.lo && kpos <= st.hi);
       const float v = vis ? s[c][r] * kscale2 : -INFINITY;
       s[c][r] = v;
       mx = fmaxf(mx, v);
@@ -189,17 +194,23 @@ __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)
   uint2 ph[4], pl[4];  // P^T operands: keys 16 c + 4 g .. + 3, bf16 hi and lo
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    uint32_t hb[4], lb[4];
+    uint32_t hw[2], lw[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float pj = mn == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[c][r] - mn);
-      sum += pj;
-      const float pv = pj * vscale;
-      hb[r] = f32_to_bf16_bits(pv);
-      lb[r] = f32_to_bf16_bits(pv - bf16_bits_to_f32(hb[r]));
+    for (int q = 0; q < 2; ++q) {  // two probabilities per packed conversion (nearest-even)
+      at_f32x2 pv;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float pj = mn == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[c][2 * q + e] - mn);
+        sum += pj;
+        pv[e] = pj * vscale;
+      }
+      const at_bf16x2 h = __builtin_convertvector(pv, at_bf16x2);
+      const at_bf16x2 l = __builtin_convertvector(pv - __builtin_convertvector(h, at_f32x2), at_bf16x2);
+      hw[q] = __builtin_bit_cast(uint32_t, h);
+      lw[q] = __builtin_bit_cast(uint32_t, l);
     }
-    ph[c] = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-    pl[c] = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+    ph[c] = make_uint2(hw[0], hw[1]);
+    pl[c] = make_uint2(lw[0], lw[1]);
   }
   sum += __shfl_xor(sum, 16, kWave);
   sum += __shfl_xor(sum, 32, kWave);
@@ -280,6 +291,8 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_extend_kernel(AttnPara
   // keys the block's rows can see: [lo of its first token, position of its last]
   const int t_first = token_of(r0), t_last = token_of(r0 + kAttnRows - 1);
   const int klo = lo_of(t_first), khi = p.prefix + t_last + 1;
+  st.all_lo = lo_of(t_last);          // lo grows with the token
+  st.all_hi = p.prefix + t_first;
   const float s2 = p.sm_scale * kLog2e;
   if (klo < p.prefix)
     attend_range<D, FMT>(lds, qf, p.k_cache, p.v_cache, p.k_bscale, p.v_bscale, 0, klo,
