@@ -173,9 +173,11 @@ ft_status ft_moe_route(const ft_moe_desc *desc, int64_t tokens, const uint16_t *
  * page 1, the bullet on #631): routing, the gate|up GEMV with in-register
  * dequantisation and (clamped) SwiGLU, the down GEMV, the weighted combine and
  * the gated shared expert.  T < 8 runs as one persistent kernel; T >= 8 routes,
- * groups the (token, slot) pairs by expert and runs the grouped kernels of
- * ft_moe_nvfp4_prefill, so each selected expert's weights are read once for all
- * of its tokens.
+ * selects and groups the (token, slot) pairs by expert in one persistent kernel
+ * (one block per CU, fp64 MFMA router split along K; the top-k and the grouping
+ * as in ft_moe_route and ft_moe_nvfp4_prefill) and then runs the grouped kernels
+ * of ft_moe_nvfp4_prefill, so each selected expert's weights are read once for
+ * all of its tokens.
  *   x bf16 [T][H]; w_router f32 [E][H]; bias f32 [E] or NULL
  *   routed: repacked bank of E experts; shared: repacked bank of 1 expert, or
  *   NULL when desc->shared_inter == 0; shared_gate bf16 [H] (NULL when no shared)
@@ -320,16 +322,18 @@ ft_status ft_moe_nvfp4_prefill(const ft_moe_desc *desc, int64_t tokens, const ui
                                size_t workspace_bytes, void *stream);
 
 /* Status of the device-side waits of ft_moe_nvfp4_decode on this workspace.
- * The one-launch decode path (T < 8) runs one block per compute unit whose blocks
- * hand values to each other; it therefore needs every block resident at once (one
- * per CU: ft_init checks that the device can hold one, and work from other streams
- * that occupies whole CUs breaks the assumption).  Every wait is bounded: a wait
+ * The one-launch decode path (T < 8) and the routing kernel of a decode batch
+ * (T >= 8) run one block per compute unit whose blocks hand values to each other;
+ * they therefore need every block resident at once (one per CU: ft_init checks
+ * that the device can hold one, and work from other streams that occupies whole
+ * CUs breaks the assumption).  Every wait is bounded: a wait
  * that gives up lets the kernel finish, leaves that call's y (and side outputs)
  * invalid, and records why in the workspace.  This call enqueues one tiny kernel
  * that copies the recorded reasons to *status (device int32) and clears them, so
  * the hot call itself never synchronises; read *status after the stream reaches
  * it.  0 = no give-up since the last read; otherwise an OR of 1 (router logits),
- * 2 (shared gate), 4 (intermediate h values), 8 (partial output sums).
+ * 2 (shared gate), 4 (intermediate h values), 8 (partial output sums), 16 (the
+ * routes of a decode batch, T >= 8, awaited by its grouping).
  * `workspace` is a decode (path 1) workspace; graph-capturable. */
 ft_status ft_moe_device_status(void *workspace, size_t workspace_bytes, int32_t *status,
                                void *stream);

@@ -70,6 +70,11 @@ ft_status fused_grid(int* grid) {
     if (per_cu < 1)
       return fail(FT_EUNSUPPORTED,
                   "the fused decode kernel cannot keep a block resident on a compute unit");
+    e = route_group_min_occupancy(&per_cu);
+    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    if (per_cu < 1)
+      return fail(FT_EUNSUPPORTED,
+                  "the decode routing kernel cannot keep a block resident on a compute unit");
     g_fused_grid[dev] = cus < kMaxFusedGrid ? cus : kMaxFusedGrid;
   }
   *grid = g_fused_grid[dev];
@@ -241,7 +246,7 @@ ft_status run_route(const ft_moe_desc* desc, int T, const uint16_t* x, const flo
 ft_status run_grouped(const ft_moe_desc* desc, int T, const uint16_t* x, const int32_t* ids,
                       const float* w, const ft_nvfp4_experts* routed,
                       const ft_nvfp4_experts* shared, uint16_t* y, void* workspace,
-                      const Layout& L, hipStream_t s) {
+                      const Layout& L, hipStream_t s, bool routes_grouped = false) {
   const bool has_shared = desc->shared_inter > 0;
   PrefillParams p{};
   p.x = x;
@@ -270,6 +275,7 @@ ft_status run_grouped(const ft_moe_desc* desc, int T, const uint16_t* x, const i
   p.gate_max = desc->gate_max;
   p.up_absmax = desc->up_absmax;
   p.h16 = prefill_h16(desc->act, desc->gate_max, desc->up_absmax) ? 1 : 0;
+  p.routes_grouped = routes_grouped ? 1 : 0;
   p.y = y;
   hipError_t e = launch_prefill(p, s);
   if (e != hipSuccess) return hip_fail(e, "grouped expert kernels");
@@ -459,6 +465,48 @@ ft_status decode_impl(const ft_moe_desc* desc, int64_t tokens, const uint16_t* x
   if (T >= kGroupedDecodeMinTokens) {
     int32_t* ids = at<int32_t>(workspace, L.ids);
     float* wts = at<float>(workspace, L.w);
+    const int n_group = slot_of ? n_slots : desc->num_experts;
+    if (route_group_fits(*desc, T, grid, n_group)) {
+      // routing, selection and grouping in one launch (one block per CU)
+      RouteGroupParams q{};
+      q.x = x;
+      q.wr = w_router;
+      q.bias = bias;
+      q.shared_gate = has_shared ? shared_gate : nullptr;
+      q.T = T;
+      q.E = desc->num_experts;
+      q.H = desc->hidden;
+      q.k = desc->top_k;
+      q.ksplit = route_group_splits(desc->num_experts, desc->hidden, grid);
+      q.ids = ids;
+      q.w = wts;
+      q.gamma = has_shared ? at<float>(workspace, L.gamma) : nullptr;
+      q.ids_copy = topk_ids_out;
+      q.w_copy = topk_w_out;
+      q.slot_of = slot_of;
+      q.n_slots = n_slots;
+      q.miss_out = miss_out;
+      q.group = 1;
+      q.n_group = n_group;
+      q.unit_tokens = prefill_unit_tokens(T);
+      q.shared_units = has_shared ? 1 : 0;
+      q.units = at<PfUnit>(workspace, L.units);
+      q.nunits = at<int32_t>(workspace, L.nunits);
+      q.sorted = at<int32_t>(workspace, L.sorted);
+      q.part = at<uint64_t>(workspace, L.logits);
+      q.lg = at<uint64_t>(workspace, L.part);
+      q.tids = at<uint64_t>(workspace, L.h);
+      q.gen = at<uint32_t>(workspace, L.gen);
+      q.err = at<uint32_t>(workspace, L.sync) + kErrorWord;
+      q.spin_limit = wait_limit();
+      hipError_t e = launch_route_group(q, grid, s);
+      if (e != hipSuccess) return hip_fail(e, "decode routing kernel");
+      ft_moe_desc gd = *desc;
+      gd.num_experts = n_group;
+      st = run_grouped(&gd, T, x, ids, wts, routed, shared, y, workspace, L, s, true);
+      if (st != FT_OK) return st;
+      return ok();
+    }
     st = run_route(desc, T, x, w_router, bias, shared_gate, at<float>(workspace, L.logits),
                    has_shared ? at<float>(workspace, L.gamma) : nullptr, ids, wts, topk_ids_out,
                    topk_w_out, at<uint32_t>(workspace, L.sync) + kRouteCounterWord,

@@ -75,6 +75,37 @@ struct FusedParams {
 };
 
 
+// The routing of a decode batch in one launch (route_group.hip).
+struct RouteGroupParams {
+  const uint16_t* x;            // bf16 [T][H]
+  const float* wr;              // f32 [E][H]
+  const float* bias;            // f32 [E] or null
+  const uint16_t* shared_gate;  // bf16 [H] or null
+  int T, E, H, k;
+  int ksplit;                   // K splits of the router product (route_group_splits)
+  int32_t* ids;                 // i32 [T][k] expert ids (slot ids over a slot bank)
+  float* w;                     // f32 [T][k] routing weights (0 for a non-resident expert)
+  float* gamma;                 // f32 [T] shared gate, or null
+  int32_t* ids_copy;            // optional i32 [T][k]: the expert ids
+  float* w_copy;                // optional f32 [T][k]: the softmax weights
+  const int32_t* slot_of;       // optional [E] expert -> slot
+  int n_slots;
+  int32_t* miss_out;            // optional [T][k]: non-resident selected expert, or -1
+  int group;                    // 1: also group the pairs (units, nunits, sorted)
+  int n_group;                  // experts (or slots) of the grouping, <= kMaxExperts
+  int unit_tokens;              // tokens per work unit
+  int shared_units;             // 1: append the shared expert's units
+  PfUnit* units;
+  int32_t* nunits;
+  int32_t* sorted;
+  uint64_t* part;               // tagged [ksplit][E / 16 tiles][16][T][2]: partial sums (low, high)
+  uint64_t* lg;                 // tagged [T][E]: fp32 logits (bias added)
+  uint64_t* tids;               // tagged [T * k]: the ids, for the grouping block
+  uint32_t* gen;                // per-block call counters [grid] (shared with the decode kernel)
+  uint32_t* err;                // error word (as FusedParams::err)
+  int spin_limit;
+};
+
 struct PrefillParams {
   const uint16_t* x;       // bf16 [T][H]
   int T, H, k, E, P;       // P = T * k routed pairs; pair = t * k + slot
@@ -90,6 +121,8 @@ struct PrefillParams {
   int32_t* nunits;         // number of valid units
   int Imax;                // row stride of hhi / hlo
   int h16;                 // 1: h travels as fp16 in hhi (hlo unused); 0: as a bf16 pair
+  int routes_grouped;      // 1: units, nunits and sorted are already written (by the routing
+                           // kernel of a decode batch): the grouping kernels are skipped
   uint16_t* hhi;           // [P + T][Imax] h in fp16 (h16), or h rounded to bf16 ...
   uint16_t* hlo;           // bf16 [P + T][Imax] ... and the rounded remainder (h16 = 0)
   float* out;              // f32 [T][nslots][H] weighted expert outputs
@@ -109,6 +142,8 @@ hipError_t launch_grouped_small(const PrefillParams& p, int ugroups, hipStream_t
 hipError_t launch_decode_fused(const FusedParams& p, int grid, hipStream_t s);
 int fused_block_threads();
 hipError_t decode_fused_min_occupancy(int* blocks_per_cu);
+hipError_t launch_route_group(const RouteGroupParams& p, int grid, hipStream_t s);
+hipError_t route_group_min_occupancy(int* blocks_per_cu);
 // copies the error word err[0] of a decode workspace to *status and clears it
 hipError_t launch_device_status(uint32_t* err, int32_t* status, hipStream_t s);
 // Rewrites routes [T*k] in place from expert ids to slot ids (a non-resident expert:

@@ -97,6 +97,41 @@ inline size_t route_split_bytes(int E, int T, int H) {
   return static_cast<size_t>(route_split_k(E, T, H)) * T * (E + 1) * sizeof(double);
 }
 
+// The one-launch routing of a decode batch (8..64 tokens): K splits of its fp64
+// router product, the largest power of two up to kRouteGroupMaxSplits that keeps
+// one (16-row tile, split) task per block of a `grid`-block launch, a whole number
+// of 16-K pieces for each of the block's 8 waves, and the partial sums (16 bytes
+// per row of every 16-row tile, token and split) inside the tagged logits region
+// of the decode workspace (kLogitCopies * T * (E + 1) words).
+constexpr int kRouteGroupMaxSplits = 8;
+
+inline int route_group_splits(int E, int H, int grid) {
+  const int nrt = (E + 15) / 16;
+  int ks = 1;
+  while (2 * ks <= kRouteGroupMaxSplits && nrt * 2 * ks <= grid && H % (128 * 2 * ks) == 0 &&
+         2 * (2 * ks) * nrt <= E + 1)
+    ks *= 2;
+  return ks;
+}
+
+// Whether a decode call of T tokens takes the one-launch routing: a block per
+// token for the selection and another for its shared gate fit the grid, the
+// partial sums fit the tagged logits region, the logits the partial-output region
+// and the ids the h region (path-1 layout).
+inline bool route_group_fits(const ft_moe_desc& d, int64_t T, int grid, int n_group) {
+  if (T < kGroupedDecodeMinTokens || T > kMaxDecodeTokens || 2 * T > grid) return false;
+  if (n_group < 1 || n_group > kMaxExperts || d.hidden % 128 != 0) return false;
+  const size_t t = static_cast<size_t>(T), E = static_cast<size_t>(d.num_experts);
+  const size_t ks = static_cast<size_t>(route_group_splits(d.num_experts, d.hidden, grid));
+  const size_t logits_bytes = static_cast<size_t>(kLogitCopies) * t * (E + 1) * 8;
+  const size_t imax = static_cast<size_t>(d.inter > d.shared_inter ? d.inter : d.shared_inter);
+  const size_t nslots = static_cast<size_t>(d.top_k) + (d.shared_inter > 0 ? 1 : 0);
+  const size_t part_bytes = static_cast<size_t>(kMaxFusedGrid) * kRowGroup * 8;
+  const size_t nrt = (E + 15) / 16;
+  return ks * nrt * 16 * t * 16 <= logits_bytes && t * E * 8 <= part_bytes &&
+         t * static_cast<size_t>(d.top_k) * 8 <= t * nslots * imax * 8;
+}
+
 // -------------------------------------------------------- descriptors --
 
 // Whether the grouped expert GEMMs hand h from the gate|up product to the down

@@ -1037,7 +1037,9 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
   p.unit_tokens = prefill_unit_tokens(p.T);
   p.ntiles1 = p.Imax / 64;
   p.ntiles2 = p.H / kPfRows;
-  if (p.P <= kGroupOneBlockPairs) {
+  if (p.routes_grouped) {
+    // units, nunits and sorted were written by the routing kernel
+  } else if (p.P <= kGroupOneBlockPairs) {
     pf_group_one_block_kernel<<<1, kMaxExperts, 0, s>>>(p);
   } else {
     pf_hist_kernel<<<nblk, 256, 0, s>>>(p);

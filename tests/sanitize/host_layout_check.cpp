@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <string>
 #include <vector>
 
 #include "host_layout.hpp"
@@ -97,6 +98,34 @@ void check(const ft_moe_desc& d, long long T, int path) {
   }
 }
 
+// The one-launch routing of a decode batch: every region its kernel writes lies
+// inside the decode layout's region it borrows, and the split count keeps whole
+// 16-K pieces per wave and one task per block.
+void check_route_group(const ft_moe_desc& d, long long T) {
+  const Layout L = layout(d, T, 1);
+  const std::vector<Region> r = regions(d, T, 1, L);
+  auto need_of = [&](const char* name) -> size_t {
+    for (const Region& a : r)
+      if (std::string(a.name) == name) return a.need;
+    return 0;
+  };
+  for (int grid : {16, 64, 128, 256, 304, 1024}) {
+    if (!route_group_fits(d, T, grid, d.num_experts)) continue;
+    const size_t t = static_cast<size_t>(T), E = static_cast<size_t>(d.num_experts);
+    const int ks = route_group_splits(d.num_experts, d.hidden, grid);
+    const size_t nrt = (E + 15) / 16;
+    if (ks < 1 || ks > kRouteGroupMaxSplits || (ks & (ks - 1)) != 0)
+      violation("route split count", d, T, 1, "ksplit");
+    if (ks > 1 && static_cast<int>(nrt) * ks > grid) violation("route tasks > grid", d, T, 1, "ksplit");
+    if (d.hidden % (128 * ks) != 0) violation("route pieces", d, T, 1, "ksplit");
+    if (2 * T > grid) violation("route blocks", d, T, 1, "grid");
+    if (static_cast<size_t>(ks) * nrt * 16 * t * 16 > need_of("logits"))
+      violation("route partial sums", d, T, 1, "logits");
+    if (t * E * 8 > need_of("part")) violation("route logits", d, T, 1, "part");
+    if (t * static_cast<size_t>(d.top_k) * 8 > need_of("h")) violation("route ids", d, T, 1, "h");
+  }
+}
+
 }  // namespace
 
 int main() {
@@ -127,6 +156,7 @@ int main() {
               for (long long T : Ts) {
                 if (T > tmax) continue;
                 check(d, T, path);
+                if (path == 1 && T >= 8) check_route_group(d, T);
                 ++checked;
                 const size_t tot = layout(d, T, path).total;
                 if (tot < prev) violation("total shrank", d, T, path, "total");

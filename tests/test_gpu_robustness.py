@@ -40,9 +40,11 @@ def test_prefill_out_of_range_ids_poison_only_their_token():
     assert np.array_equal(b[keep], g[keep])
 
 
-def test_decode_wait_give_up_is_reported_and_the_next_workspace_is_clean():
-    """The one-launch decode kernel's blocks agree on a call's generation by each
-    counting its own calls; values handed between blocks carry that generation.
+@pytest.mark.parametrize("tokens", [1, 16])   # one-launch decode kernel; decode routing kernel
+def test_decode_wait_give_up_is_reported_and_the_next_workspace_is_clean(tokens):
+    """The one-launch decode kernel's blocks (and those of the routing kernel of a
+    decode batch) agree on a call's generation by each counting its own calls;
+    values handed between blocks carry that generation.
     Here the per-block counters of one workspace are set to unequal values from
     the host, so no hand-off can complete: with a small wait limit every wait
     gives up after a bounded number of polls, the kernel finishes, and
@@ -57,11 +59,11 @@ def test_decode_wait_give_up_is_reported_and_the_next_workspace_is_clean():
                                   hidden=256, inter=128, shared_inter=128)
     L = synth.make_layer(w)
     dl = device.upload_layer(L)
-    xh = synth.make_tokens(w, tokens=1)
+    xh = synth.make_tokens(w, tokens=tokens)
     x = device.tokens_to_device(xh)
     ref = oracle.moe_layer(L, xh)
 
-    ws = ftmoe.alloc_workspace(dl.desc, 1, ftmoe.PATH_DECODE, "cuda")
+    ws = ftmoe.alloc_workspace(dl.desc, tokens, ftmoe.PATH_DECODE, "cuda")
     y, ids, _ = device.decode(dl, x, ws)
     assert ftmoe.device_status(ws) == 0
     # per-block call counters: bytes [256, 256 + 4 * 1024) of a decode workspace
@@ -76,10 +78,10 @@ def test_decode_wait_give_up_is_reported_and_the_next_workspace_is_clean():
         ftmoe.ft_set_wait_limit(0)
     st = ftmoe.device_status(ws)
     say(f"  status after the desynchronised call: {st:#x}")
-    assert st != 0 and (st & ~0xF) == 0
+    assert st != 0 and (st & ~0x1F) == 0
     assert ftmoe.device_status(ws) == 0           # the read cleared it
 
-    ws2 = ftmoe.alloc_workspace(dl.desc, 1, ftmoe.PATH_DECODE, "cuda")
+    ws2 = ftmoe.alloc_workspace(dl.desc, tokens, ftmoe.PATH_DECODE, "cuda")
     y2, ids2, _ = device.decode(dl, x, ws2)
     torch.cuda.synchronize()
     assert ftmoe.device_status(ws2) == 0
