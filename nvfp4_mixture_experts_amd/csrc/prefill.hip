@@ -37,6 +37,9 @@ constexpr int kPfRows = 128;               // weight rows per block tile
 constexpr unsigned kPersistentBlocks = 256;  // one per CU of MI355X (LDS holds one)
 constexpr int kPfSlab = 64;                // K elements per LDS slab
 constexpr int kLdsRowU4 = kPfSlab / 8 + 1; // 16-byte words per LDS row (one of padding)
+// 16-byte words per LDS slab tile: one of padding, so that tiles t and t + 1 start 4 banks
+// apart (threads writing the same row of different tiles at once do not collide)
+constexpr int kTileU4 = kPfRows * kLdsRowU4 + 1;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -299,7 +302,7 @@ template <int W, int FR, int NB, int R, int RW, bool H16>
 __device__ __forceinline__ void pf_mainloop(
     const uint8_t* wc, size_t wc_step, const uint8_t* ws, size_t ws_step,
     const uint16_t* const (&brow)[NB][FR], int nfr, int nslab,
-    uint4 (*lds)[kPfRows * kLdsRowU4], int drow, int dpart, int lane, f32x4 (&acc)[FR][8]) {
+    uint4 (*lds)[kTileU4], int drow, int dpart, int lane, f32x4 (&acc)[FR][8]) {
   static_assert(RW % R == 0 && RW % 2 == 0, "ring depths");
   constexpr int KPT = Geometry<W, FR>::kKpt;
   uint4 xr[R][NB][FR][2];
@@ -396,7 +399,7 @@ template <int FR, int R, int RS>
 __device__ __forceinline__ void pf_mainloop_rows(
     const uint8_t* wc, const uint8_t* ws, const long long (&rowoff)[4], int H,
     const uint16_t* const (&brow)[1][FR], int nfr, int nslab,
-    uint4 (*tiles)[kPfRows * kLdsRowU4], int lane, f32x4 (&acc)[FR][8]) {
+    uint4 (*tiles)[kTileU4], int lane, f32x4 (&acc)[FR][8]) {
   static_assert(4 % R == 0, "token ring depth divides the slabs of a super-slab");
   const int tid = threadIdx.x;
   const int seg = tid & 7;  // 32-K segment of the super-slab
@@ -490,7 +493,7 @@ __device__ __forceinline__ void pf_mainloop_rows(
 template <int W, int FR, int NB, int R, int NS, bool H16>
 __device__ __forceinline__ void pf_mainloop_whole_a(
     const uint8_t* wc, size_t wc_step, const uint8_t* ws, size_t ws_step,
-    const uint16_t* const (&brow)[NB][FR], int nfr, uint4 (*lds)[kPfRows * kLdsRowU4],
+    const uint16_t* const (&brow)[NB][FR], int nfr, uint4 (*lds)[kTileU4],
     int drow, int dpart, int lane, f32x4 (&acc)[FR][8]) {
   constexpr int KPT = Geometry<W, FR>::kKpt;
   static_assert(R >= 2 && R <= NS, "ring depth");
@@ -551,7 +554,7 @@ __device__ __forceinline__ void pf_mainloop_whole_a(
 template <int NSS, int FR, int R, int RS>
 __device__ __forceinline__ void pf_mainloop_rows_unrolled(
     const uint8_t* wc, const uint8_t* ws, const long long (&rowoff)[4], int H,
-    const uint16_t* const (&brow)[1][FR], int nfr, uint4 (*tiles)[kPfRows * kLdsRowU4],
+    const uint16_t* const (&brow)[1][FR], int nfr, uint4 (*tiles)[kTileU4],
     int lane, f32x4 (&acc)[FR][8]) {
   constexpr int NS = 4 * NSS;  // 64-K slabs
   static_assert(RS >= 1 && RS <= NSS && R >= 2, "ring depths");
@@ -642,7 +645,7 @@ constexpr int kBlocksPerCu = W == 4 ? 2 : 1;
 template <int FR, int R, int RS, int BPC, int NSS>
 __global__ __launch_bounds__(256, BPC) void pf_gateup_kernel(PrefillParams p) {
   constexpr int W = 4;
-  __shared__ uint4 tiles[NSS > 0 ? 8 : 4][kPfRows * kLdsRowU4];
+  __shared__ uint4 tiles[NSS > 0 ? 8 : 4][kTileU4];
   int u, tile;
   unit_tile(p.ntiles1, &u, &tile);
   const int nun = *p.nunits;  // both loads issued before either is waited for
@@ -714,7 +717,7 @@ template <int W, int FR, int R, int RW, int NS, bool H16>
 __global__ __launch_bounds__(W * kWave, kBlocksPerCu<W>) void pf_down_kernel(PrefillParams p) {
   using G = Geometry<W, FR>;
   constexpr int NB = H16 ? 1 : 2;
-  __shared__ uint4 lds[NS > 0 ? NS : 2][kPfRows * kLdsRowU4];
+  __shared__ uint4 lds[NS > 0 ? NS : 2][kTileU4];
   int u, tile;
   unit_tile(p.ntiles2, &u, &tile);
   const int nun = *p.nunits;  // both loads issued before either is waited for
@@ -818,7 +821,7 @@ __global__ __launch_bounds__(8 * kWave, 1) void pf_down_persistent_kernel(Prefil
   using G = Geometry<W, FR>;
   constexpr int KPT = G::kKpt;
   constexpr int kI = 64 * NS;
-  __shared__ uint4 lds[NS][kPfRows * kLdsRowU4];
+  __shared__ uint4 lds[NS][kTileU4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = p.H;
