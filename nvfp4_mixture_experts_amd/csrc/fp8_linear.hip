@@ -158,6 +158,100 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemm_kernel(
   }
 }
 
+// Many activation rows: 128 x 128 output tiles per 4-wave block on gfx950's
+// v_mfma_scale_f32_16x16x128_f8f6f4 (both operands e4m3, unit block scales: the
+// scale operand 127 is 2^0 in E8M0), 128-deep K slabs staged in LDS (rows padded by
+// 16 bytes: the 16 rows one read covers fall on 16 distinct bank quadruples), the
+// next slab's global loads in flight during the current slab's MFMAs.  A wave owns a
+// 64 x 64 quarter of the tile: 4 x 4 fragments, each MFMA lane (i, g) holding row /
+// column i and K 32 g .. 32 g + 31 of the slab for A and B alike.  K % 64 == 0: a
+// trailing half slab is read as zeros past K.
+constexpr int kBig = 128;              // output rows and columns of a block
+constexpr int kBigSlab = 128;          // K bytes per LDS slab
+constexpr int kBigRow = kBigSlab + 16; // bytes per LDS row
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(4 * kWave, 2) void fp8_gemm_big_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w, int M, int N, int K,
+    const float* __restrict__ s_x, const float* __restrict__ row_scale, float scale,
+    uint16_t* __restrict__ y, int ldy, int col0) {
+  __shared__ __align__(16) uint8_t As[kBig * kBigRow];
+  __shared__ __align__(16) uint8_t Bs[kBig * kBigRow];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int m0 = blockIdx.y * kBig, n0 = blockIdx.x * kBig;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  // staging: load j of thread t moves bytes 16 (t % 8) .. + 15 of tile row t / 8 + 32 j
+  // (8 lanes cover one 128-byte row segment)
+  const int sc = (tid & 7) * 16;
+  const uint8_t* ag[4];
+  const uint8_t* bg[4];
+  bool ain[4], bin[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = (tid >> 3) + 32 * j;
+    ain[j] = m0 + r < M;
+    bin[j] = n0 + r < N;
+    ag[j] = xq + static_cast<size_t>(ain[j] ? m0 + r : 0) * K + sc;
+    bg[j] = w + static_cast<size_t>(bin[j] ? n0 + r : 0) * K + sc;
+  }
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 an[4], bn[4];
+  auto load = [&](int k0) {
+    const bool kin = k0 + sc < K;  // K % 64 == 0: a 16-byte piece is wholly in or out
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      an[j] = (ain[j] && kin) ? *reinterpret_cast<const u32x4*>(ag[j] + k0) : zero;
+      bn[j] = (bin[j] && kin) ? *reinterpret_cast<const u32x4*>(bg[j] + k0) : zero;
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += kBigSlab) {
+    __syncthreads();  // the previous slab's fragments have been read
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = (tid >> 3) + 32 * j;
+      *reinterpret_cast<u32x4*>(&As[r * kBigRow + sc]) = an[j];
+      *reinterpret_cast<u32x4*>(&Bs[r * kBigRow + sc]) = bn[j];
+    }
+    __syncthreads();
+    if (k0 + kBigSlab < K) load(k0 + kBigSlab);  // travels during this slab's MFMAs
+    v8i af[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) af[a] = *reinterpret_cast<const v8i*>(&As[(wm + 16 * a + i) * kBigRow + 32 * g]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const v8i bf = *reinterpret_cast<const v8i*>(&Bs[(wn + 16 * b + i) * kBigRow + 32 * g]);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[a], bf, acc[a][b], 0, 0, 0,
+                                                                      127, 0, 127);
+    }
+  }
+  // C lane l: column l % 16, rows 4 (l / 16) + r of each 16 x 16 fragment
+  const float sx = *s_x;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int n = n0 + wn + 16 * b + i;
+    if (n >= N) continue;
+    const float sn = sx * (row_scale ? row_scale[n] : scale);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm + 16 * a + 4 * g + r;
+        if (m < M) y[static_cast<size_t>(m) * ldy + col0 + n] = f32_to_bf16_bits(acc[a][b][r] * sn);
+      }
+  }
+}
+
 // Small activations: amax, s_x and the codes in one block of 1024 threads (the
 // same arithmetic as the two kernels above).
 constexpr int kSmallQuantThreads = 1024;
@@ -320,6 +414,12 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const uint8_t* w, int M, int N, in
     else if (M == 2) fp8_gemv_kernel<2><<<g, b, 0, s>>>(xq, w, M, N, K, s_x, row_scale, scale, y, ldy, col0);
     else if (M <= 4) fp8_gemv_kernel<4><<<g, b, 0, s>>>(xq, w, M, N, K, s_x, row_scale, scale, y, ldy, col0);
     else fp8_gemv_kernel<8><<<g, b, 0, s>>>(xq, w, M, N, K, s_x, row_scale, scale, y, ldy, col0);
+    return hipGetLastError();
+  }
+  if (M >= kBig) {
+    const dim3 grid((N + kBig - 1) / kBig, (M + kBig - 1) / kBig);
+    fp8_gemm_big_kernel<<<grid, dim3(4 * kWave), 0, s>>>(xq, w, M, N, K, s_x, row_scale, scale, y,
+                                                         ldy, col0);
     return hipGetLastError();
   }
   const dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile);

@@ -67,7 +67,7 @@ def test_fp8_quantize_codes_bit_exact_with_ties(ft):
     assert s.item() == want_s
 
 
-@pytest.mark.parametrize("tokens", [1, 2, 8, 32, 77])   # GEMV (<= 8 rows), MFMA GEMM
+@pytest.mark.parametrize("tokens", [1, 2, 8, 32, 77, 128, 300])   # GEMV (<= 8 rows), 64- and 128-row MFMA GEMMs
 def test_fp8_linear_matches_oracle_and_parts_equal_rowwise(ft, tokens):
     w = synth.WORKLOADS["fp8_linear_qkv_t32"]
     lin = synth.make_fp8_linear(w)
@@ -94,10 +94,11 @@ def test_fp8_linear_matches_oracle_and_parts_equal_rowwise(ft, tokens):
     assert np.array_equal(_bits(yp), _bits(y))
 
 
-@pytest.mark.parametrize("tokens,hidden", [(19, 1024), (5, 1024), (3, 1088)])
+@pytest.mark.parametrize("tokens,hidden", [(19, 1024), (5, 1024), (3, 1088), (130, 1088)])
 def test_fp8_linear_ragged_parts_and_rows(ft, tokens, hidden):
-    # parts whose row counts are not multiples of the 64-row tile (nor of the GEMV's
-    # 16 rows per block); K = 1088: 68 16-byte chunks, so most GEMV lanes hold one
+    # parts whose row counts are not multiples of the 64- or 128-row tiles (nor of the
+    # GEMV's 16 rows per block); K = 1088: 68 16-byte chunks, so most GEMV lanes hold
+    # one, and the 128-row GEMM's last 128-byte K slab is half past K
     w = synth.dataclasses.replace(synth.WORKLOADS["fp8_linear_qkv_t32"], hidden=hidden,
                                   parts=(100, 37, 200), tokens=tokens)
     lin = synth.make_fp8_linear(w)
@@ -119,7 +120,8 @@ def test_fp8_linear_ragged_parts_and_rows(ft, tokens, hidden):
 
 def test_fp8_linear_prefill_chunk_sampled(ft):
     """8192 tokens x 2048 -> 5120: codes of every token bit-exact, outputs of sampled
-    rows (first, last, both ends of every 64-row tile band of 1024) against the oracle."""
+    rows (first, last, both ends of one 128-row tile in every band of 1024, and the
+    rows either side of a tile boundary) against the oracle."""
     w = synth.WORKLOADS["fp8_linear_qkv_t8192"]
     lin = synth.make_fp8_linear(w)
     x = synth.make_tokens(w)
@@ -134,7 +136,8 @@ def test_fp8_linear_prefill_chunk_sampled(ft):
     ft.ft_fp8_quantize(xd, q, s, ws)
     torch.cuda.synchronize()
     assert np.array_equal(q.cpu().numpy(), xq) and s.item() == s_x
-    sample = sorted({0, 8191} | {t for j in range(8) for t in (1024 * j, 1024 * j + 63)}
+    sample = sorted({0, 8191} | {t for j in range(8) for t in (1024 * j, 1024 * j + 63,
+                                                               1024 * j + 127, 1024 * j + 128)}
                     | {4321, 6000, 7777})
     want = _oracle_rows(xq, s_x, lin.w, rows, sample)
     say(f"  comparing {len(sample)} rows of the 8192-token chunk")
