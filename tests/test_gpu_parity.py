@@ -291,6 +291,47 @@ def test_decode_routes_signed_zero_and_nan_logits(gpu, E, tokens):
         assert_output_close(gpu.bf16_bits(y), ref["y"], f"decode, zero logits, T={tokens}")
 
 
+@pytest.mark.parametrize("tokens", [16, 64])   # the one-launch routing of a decode batch
+def test_decode_routes_ties_go_to_lowest_index(gpu, tokens):
+    """Duplicated router rows give exactly equal logits: the routing kernel of a decode
+    batch must pick the lower index, as the oracle does; the layer output follows."""
+    w = synth.dataclasses.replace(synth.WORKLOADS["tiny_e8_top2"], num_experts=96, top_k=8,
+                                  hidden=512, inter=128)
+    layer = synth.make_layer(w)
+    wr = layer.w_router.copy()
+    wr[50:96] = wr[0:46]                      # experts 50.. duplicate 0..45
+    wr[10] = wr[70]                           # and a tie inside the copy
+    layer.w_router = wr
+    x = synth.make_tokens(w, tokens=tokens, stream="ties")
+    lg = oracle.router_logits(x, wr)
+    ref_ids, ref_w = oracle.topk(lg, w.top_k)
+    assert sum(len(set(lg[t, ref_ids[t]].tolist())) < w.top_k for t in range(tokens)) > 0
+    dl = gpu.upload_layer(layer)
+    y, ids, wt = decode_checked(gpu, dl, gpu.tokens_to_device(x))
+    _check_routes(ids, wt, ref_ids, ref_w, f"decode ties T={tokens}")
+    ref = oracle.moe_layer(layer, x)
+    assert_output_close(gpu.bf16_bits(y), ref["y"], f"decode ties T={tokens}")
+
+
+@pytest.mark.parametrize("num_experts", [1000, 1024])
+def test_decode_batch_many_experts(gpu, num_experts):
+    """40 tokens over 1000 / 1024 experts with a router bias and a shared expert: the
+    routing kernel's two logits per selecting thread, four K splits over 63 / 64 row
+    tiles (the last one partial for 1000), and the grouping of 400 pairs."""
+    w = synth.dataclasses.replace(synth.WORKLOADS["decode_e512_top10_shared"],
+                                  num_experts=num_experts, hidden=512, inter=128,
+                                  shared_inter=128, tokens=40)
+    layer = synth.make_layer(w)
+    layer.bias = (np.random.default_rng(num_experts).standard_normal(num_experts)
+                  * 0.05).astype(np.float32)
+    x = synth.make_tokens(w)
+    dl = gpu.upload_layer(layer)
+    y, ids, wt = decode_checked(gpu, dl, gpu.tokens_to_device(x))
+    ref = oracle.moe_layer(layer, x)
+    _check_routes(ids, wt, ref["ids"], ref["weights"], f"decode E={num_experts} T=40")
+    assert_output_close(gpu.bf16_bits(y), ref["y"], f"decode E={num_experts} T=40")
+
+
 @pytest.mark.parametrize("num_experts", [1000, 1024])
 def test_route_many_experts_split_router(gpu, num_experts):
     """40 tokens (split-K router) with 1000 and 1024 experts and a router bias: the
