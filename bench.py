@@ -57,7 +57,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 DECODE_KERNEL = "moe_decode_fused_kernel"
 DECODE_SOURCES = ("nvfp4_mixture_experts_amd/csrc/decode_fused.hip",
                   "nvfp4_mixture_experts_amd/csrc/ftmoe_device.hpp",
-                  "nvfp4_mixture_experts_amd/csrc/ftmoe_kernels.hpp")
+                  "nvfp4_mixture_experts_amd/csrc/ftmoe_kernels.hpp",
+                  "nvfp4_mixture_experts_amd/csrc/handoff.hpp")
 
 
 def kernel_source_hash() -> str:
