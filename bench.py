@@ -569,9 +569,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the layer runs on one MI355X in this build (no "
-              "multi-GPU path; its sharding is described in DESIGN.md); run with --gpus 1",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the library runs the layer on one MI355X and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
         return 2
     if args.steps < 1 or args.reps < 1:
         print("--steps and --reps must be positive", file=sys.stderr)
