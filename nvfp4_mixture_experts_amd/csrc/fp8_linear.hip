@@ -31,6 +31,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAmaxThreads = 256;
+constexpr int kAmaxMaxBlocks = 1024;  // amax partials at most
+static_assert(kAmaxMaxBlocks % kAmaxThreads == 0, "partials per thread");
 constexpr int kTile = 64;       // output rows and columns of a block
 constexpr int kSlab = 64;       // K elements per LDS slab
 constexpr int kLdsRow = kSlab + 16;  // bytes per LDS row (16 bytes of padding)
@@ -39,14 +41,33 @@ __device__ __forceinline__ float bf16_at(const uint16_t* x, size_t i) {
   return bf16_bits_to_f32(x[i]);
 }
 
-__global__ __launch_bounds__(kAmaxThreads) void fp8_amax_kernel(const uint16_t* __restrict__ x,
-                                                                size_t n, float* partial) {
+// max(m, |v|) over the eight bf16 values of a 16-byte piece.
+__device__ __forceinline__ float absmax8(float m, const uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m = fmaxf(m, fabsf(__uint_as_float(w[j] << 16)));
+    m = fmaxf(m, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
+  }
+  return m;
+}
+
+// Per-block amax partials of x, read as n8 16-byte pieces (x is 16-byte aligned), four
+// pieces in flight per thread.
+__global__ __launch_bounds__(kAmaxThreads) void fp8_amax_kernel(const uint4* __restrict__ x,
+                                                                size_t n8, float* partial) {
   __shared__ float red[kAmaxThreads / kWave];
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   float m = 0.0f;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x)
-    m = fmaxf(m, fabsf(bf16_at(x, i)));
-  // max is order-independent: the result does not depend on timing
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = x[i + j * stride];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = absmax8(m, v[j]);
+  }
+  for (; i < n8; i += stride) m = absmax8(m, x[i]);
   m = __int_as_float(static_cast<int>(wave_max_u32(__float_as_uint(m))));
   if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
   __syncthreads();
@@ -57,37 +78,51 @@ __global__ __launch_bounds__(kAmaxThreads) void fp8_amax_kernel(const uint16_t* 
   }
 }
 
-// s_x from the partials (each block recomputes it), then codes of x.
-__global__ __launch_bounds__(kAmaxThreads) void fp8_quantize_kernel(
-    const uint16_t* __restrict__ x, size_t n, const float* __restrict__ partial, int nparts,
-    uint8_t* __restrict__ q, float* scale_out) {
-  __shared__ float s_scale;
-  if (threadIdx.x < kWave) {
-    float m = 0.0f;
-    for (int i = threadIdx.x; i < nparts; i += kWave) m = fmaxf(m, partial[i]);
-    m = __int_as_float(static_cast<int>(wave_max_u32(__float_as_uint(m))));
-    if (threadIdx.x == 0) {
-      const float s = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
-      s_scale = s;
-      if (blockIdx.x == 0) *scale_out = s;
-    }
-  }
-  __syncthreads();
-  const float s = s_scale;
-  // four elements per thread and step (n % 4 == 0)
-  for (size_t i = 4 * (static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x); i < n;
-       i += 4 * static_cast<size_t>(gridDim.x) * blockDim.x) {
-    float v[4];
+// Four bf16 values (two words) -> four e4m3 codes in one word, lowest value first.
+__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float s) {
+  const float x4[4] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xFFFF0000u),
+                       __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xFFFF0000u)};
+  float v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // |x / s| <= 448 up to the quotient's rounding; the clamp keeps the convert
-      // inside the finite range (it changes no value that rounds to a finite code)
-      const float t = __fdiv_rn(bf16_at(x, i + j), s);
-      v[j] = fminf(fmaxf(t, -448.0f), 448.0f);
-    }
-    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0u, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
-    *reinterpret_cast<uint32_t*>(q + i) = w;
+  for (int j = 0; j < 4; ++j) v[j] = fminf(fmaxf(__fdiv_rn(x4[j], s), -448.0f), 448.0f);
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0u, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+}
+
+// s_x from the partials (each block recomputes it: every thread loads at most
+// kAmaxMaxBlocks / kAmaxThreads of them, all at once), then the codes of x: n8 16-byte
+// pieces, each stored as one 8-byte word; a thread's first two pieces are loaded
+// before the partials, so they travel while the scale is formed.  |x / s| <= 448 up
+// to the quotient's rounding; the clamp keeps the convert inside the finite range (it
+// changes no value that rounds to a finite code).
+__global__ __launch_bounds__(kAmaxThreads) void fp8_quantize_kernel(
+    const uint4* __restrict__ x, size_t n8, const float* __restrict__ partial, int nparts,
+    uint2* __restrict__ q, float* scale_out) {
+  __shared__ float red[kAmaxThreads / kWave];
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  const size_t i0 = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  const uint4 a = i0 < n8 ? x[i0] : zero;
+  const uint4 b = i0 + stride < n8 ? x[i0 + stride] : zero;
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kAmaxMaxBlocks / kAmaxThreads; ++j) {
+    const int k = threadIdx.x + j * kAmaxThreads;
+    if (k < nparts) m = fmaxf(m, partial[k]);
+  }
+  m = __int_as_float(static_cast<int>(wave_max_u32(__float_as_uint(m))));
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  float mx = red[0];
+#pragma unroll
+  for (int w = 1; w < kAmaxThreads / kWave; ++w) mx = fmaxf(mx, red[w]);
+  const float s = mx > 0.0f ? __fdiv_rn(mx, 448.0f) : 1.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+  if (i0 < n8) q[i0] = make_uint2(quant4(a.x, a.y, s), quant4(a.z, a.w, s));
+  if (i0 + stride < n8) q[i0 + stride] = make_uint2(quant4(b.x, b.y, s), quant4(b.z, b.w, s));
+  for (size_t i = i0 + 2 * stride; i < n8; i += stride) {
+    const uint4 c = x[i];
+    q[i] = make_uint2(quant4(c.x, c.y, s), quant4(c.z, c.w, s));
   }
 }
 
@@ -372,14 +407,14 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemv_kernel(
 
 int amax_blocks(size_t n) {
   const size_t b = (n + kAmaxThreads * 16 - 1) / (kAmaxThreads * 16);
-  return static_cast<int>(b < 1 ? 1 : (b > 1024 ? 1024 : b));
+  return static_cast<int>(b < 1 ? 1 : (b > kAmaxMaxBlocks ? kAmaxMaxBlocks : b));
 }
 
 }  // namespace
 
 size_t fp8_linear_workspace(int64_t M, int64_t K) {
   const size_t n = static_cast<size_t>(M) * K;
-  return align256(n) + align256(1024 * sizeof(float)) + 256;
+  return align256(n) + align256(kAmaxMaxBlocks * sizeof(float)) + 256;
 }
 
 hipError_t launch_fp8_quantize(const uint16_t* x, int64_t M, int64_t K, void* ws, uint8_t** xq,
@@ -388,19 +423,23 @@ hipError_t launch_fp8_quantize(const uint16_t* x, int64_t M, int64_t K, void* ws
   uint8_t* base = static_cast<uint8_t*>(ws);
   *xq = base;
   float* partial = reinterpret_cast<float*>(base + align256(n));
-  *s_x = reinterpret_cast<float*>(base + align256(n) + align256(1024 * sizeof(float)));
+  *s_x = reinterpret_cast<float*>(base + align256(n) + align256(kAmaxMaxBlocks * sizeof(float)));
   if (n <= kSmallQuantMax) {
     fp8_quantize_small_kernel<<<dim3(1), dim3(kSmallQuantThreads), 0, s>>>(x, static_cast<int>(n),
                                                                             *xq, *s_x);
     return hipGetLastError();
   }
+  // x is 16-byte aligned and n = M K with K % 64 == 0 (checked by the caller)
   const int nb = amax_blocks(n);
-  fp8_amax_kernel<<<dim3(nb), dim3(kAmaxThreads), 0, s>>>(x, n, partial);
+  const size_t n8 = n / 8;
+  fp8_amax_kernel<<<dim3(nb), dim3(kAmaxThreads), 0, s>>>(reinterpret_cast<const uint4*>(x), n8,
+                                                          partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t qb = (n / 4 + kAmaxThreads - 1) / kAmaxThreads;
-  fp8_quantize_kernel<<<dim3(static_cast<unsigned>(qb < 2048 ? qb : 2048)), dim3(kAmaxThreads), 0,
-                        s>>>(x, n, partial, nb, *xq, *s_x);
+  const size_t qb = (n8 + 2 * kAmaxThreads - 1) / (2 * kAmaxThreads);
+  fp8_quantize_kernel<<<dim3(static_cast<unsigned>(qb < 4096 ? qb : 4096)), dim3(kAmaxThreads), 0,
+                        s>>>(reinterpret_cast<const uint4*>(x), n8, partial, nb,
+                             reinterpret_cast<uint2*>(*xq), *s_x);
   return hipGetLastError();
 }
 

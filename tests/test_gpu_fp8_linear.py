@@ -67,6 +67,34 @@ def test_fp8_quantize_codes_bit_exact_with_ties(ft):
     assert s.item() == want_s
 
 
+def test_fp8_quantize_many_rows_bit_exact_with_ties(ft):
+    # 77 x 1024 values: the e4m3 midpoints (exact ties at s_x = 1) spread over the rows,
+    # the amax 448 as the very last element, the rest normal * 30
+    mags = np.array(sorted({abs(oracle.e4m3(b)) for b in range(0x7F)}))
+    mids = ((mags[:-1] + mags[1:]) / 2)
+    M, K = 77, 1024
+    x = np.random.default_rng(11).standard_normal((M, K)).astype(np.float32) * 30
+    vals = np.concatenate([mids, -mids])
+    for j, r in enumerate((0, 38, 76)):
+        x[r, 100 * j: 100 * j + len(vals)] = vals
+    x[-1, -1] = -448.0
+    xb = synth.bf16_bits_from_f32(x)
+    want_q, want_s = oracle.fp8_quantize(xb)
+    assert want_s == 1.0
+    ws = ft.fp8_linear_workspace(M, K)
+    q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    s = torch.empty(1, dtype=torch.float32, device="cuda")
+    # the kernels read x in 16-byte pieces: an x one element off is refused
+    buf = torch.zeros(M * K + 8, dtype=torch.bfloat16, device="cuda")
+    buf[1: 1 + M * K] = _dev_bf16(xb.ravel())
+    with pytest.raises(ft.FtError, match="aligned"):
+        ft.ft_fp8_quantize(buf[1: 1 + M * K].view(M, K), q, s, ws)
+    ft.ft_fp8_quantize(_dev_bf16(xb), q, s, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), want_q)
+    assert s.item() == want_s
+
+
 @pytest.mark.parametrize("tokens", [1, 2, 8, 32, 77, 128, 300])   # GEMV (<= 8 rows), 64- and 128-row MFMA GEMMs
 def test_fp8_linear_matches_oracle_and_parts_equal_rowwise(ft, tokens):
     w = synth.WORKLOADS["fp8_linear_qkv_t32"]
