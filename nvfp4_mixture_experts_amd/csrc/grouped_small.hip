@@ -177,16 +177,21 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_kernel(PrefillParams 
 }
 
 // The same product for H = NKB * 512, software-pipelined: the K loop is unrolled
-// so that K block kb + 1's token rows and codes are in flight while K block kb is
-// computed (every block of the grid is resident at once for these sizes, so
-// without this all of them issue, drain and compute in lockstep and HBM idles
-// between K blocks).  K mapping inside a 512-K block: lane group g takes the four
-// consecutive 32-K chunks 4 g .. 4 g + 3 of its row (64 contiguous code bytes, 8
-// contiguous scale bytes: one 8-byte scale load per row instead of four).
+// so that K block kb + 1's codes are in flight while K block kb is computed (every
+// block of the grid is resident at once for these sizes, so without this all of
+// them issue, drain and compute in lockstep and HBM idles between K blocks).  For
+// H <= 2048 all of K of the 16 token rows is staged in LDS at once (66 KB: two
+// blocks per CU), behind one barrier, and the K loop has none; for larger H the
+// rows are staged per K block (two barriers each), loaded one K block ahead.  K
+// mapping inside a 512-K block: lane group g takes the four consecutive 32-K chunks
+// 4 g .. 4 g + 3 of its row (64 contiguous code bytes, 8 contiguous scale bytes: one
+// 8-byte scale load per row instead of four).
 template <int NKB>
 __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_pipe_kernel(PrefillParams p) {
   constexpr int kKB = 512;
-  constexpr int kRowU4 = kKB / 8 + 1;                  // 16-byte words per staged row (+1 pad)
+  constexpr bool kAll = NKB <= 4;                      // all of K staged at once
+  constexpr int kSt = kAll ? NKB : 1;                  // K blocks per staged row
+  constexpr int kRowU4 = kSt * kKB / 8 + 1;            // 16-byte words per staged row (+1 pad)
   constexpr int kXL = 16 * (kKB / 8) / kSgThreads;     // token-row loads per thread per K block
   __shared__ uint4 xs[16 * kRowU4];
   int u, tile;
@@ -210,7 +215,8 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_pipe_kernel(PrefillPa
   const uint8_t* gsp = bank.w13s + (ebase + grow) * (H / 16) + 8 * g;
   const uint8_t* usp = bank.w13s + (ebase + I + grow) * (H / 16) + 8 * g;
   const float gg = bank.gsc[un.expert * 3 + 0], gu = bank.gsc[un.expert * 3 + 1];
-  // staged layout: thread tid moves word c8 = tid % 64 of token rows n = tid / 64 + 4 r
+  // staged layout: thread tid moves word c8 = tid % 64 of each K block of token rows
+  // n = tid / 64 + 4 r
   const int c8 = tid & 63;
   for (int f0 = 0; f0 < un.count; f0 += 16) {
     const uint16_t* xrow[kXL];
@@ -221,12 +227,14 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_pipe_kernel(PrefillPa
       const int t = un.bank ? un.start + m : tq;    // shared unit's start + m < T <= P)
       xrow[r] = p.x + static_cast<size_t>(t) * H + 8 * c8;
     }
-    uint4 xv[2][kXL], qg[2][4], qu[2][4];
+    uint4 xv[kAll ? NKB : 2][kXL], qg[2][4], qu[2][4];
     uint2 sg[2], su[2];
     auto issue = [&](int kb, int b) {
+      if constexpr (!kAll) {
 #pragma unroll
-      for (int r = 0; r < kXL; ++r) xv[b][r] = ldg16(xrow[r] + kb * kKB);
-      __builtin_amdgcn_sched_barrier(0);  // token rows first: the staging waits for them
+        for (int r = 0; r < kXL; ++r) xv[b][r] = ldg16(xrow[r] + kb * kKB);
+        __builtin_amdgcn_sched_barrier(0);  // token rows first: the staging waits for them
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         qg[b][q] = ldg16(gc + kb * (kKB / 2) + 16 * q);
@@ -237,15 +245,34 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_pipe_kernel(PrefillPa
       __builtin_amdgcn_sched_barrier(0);
     };
     sg_f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-    issue(0, 0);
+    if constexpr (kAll) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < kXL; ++r) xv[kb][r] = ldg16(xrow[r] + kb * kKB);
+      __builtin_amdgcn_sched_barrier(0);  // token rows first: the staging waits for them
+      issue(0, 0);
+      if (f0 > 0) __syncthreads();  // the previous fragment is done with xs
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < kXL; ++r)
+          xs[((tid >> 6) + 4 * r) * kRowU4 + kb * (kKB / 8) + c8] = xv[kb][r];
+      __syncthreads();
+    } else {
+      issue(0, 0);
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int b = kb & 1;
       if (kb + 1 < NKB) issue(kb + 1, b ^ 1);
-      __syncthreads();  // the previous K block (or fragment) is done with xs
+      if constexpr (!kAll) {
+        __syncthreads();  // the previous K block (or fragment) is done with xs
 #pragma unroll
-      for (int r = 0; r < kXL; ++r) xs[((tid >> 6) + 4 * r) * kRowU4 + c8] = xv[b][r];
-      __syncthreads();
+        for (int r = 0; r < kXL; ++r) xs[((tid >> 6) + 4 * r) * kRowU4 + c8] = xv[b][r];
+        __syncthreads();
+      }
+      const int kx = kAll ? kb * (kKB / 8) : 0;  // the K block's first word in a staged row
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t gw = q < 2 ? sg[b].x : sg[b].y, uw = q < 2 ? su[b].x : su[b].y;
@@ -255,7 +282,7 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_gateup_pipe_kernel(PrefillPa
         const float u1 = (q & 1) ? e4m3_byte_to_f32<3>(uw) : e4m3_byte_to_f32<1>(uw);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint4 bx = xs[i * kRowU4 + (4 * g + q) * 4 + j];
+          const uint4 bx = xs[i * kRowU4 + kx + (4 * g + q) * 4 + j];
           ag = mfma(dequant8_bf16(word(qg[b][q], j), j < 2 ? g0 : g1), bx, ag);
           au = mfma(dequant8_bf16(word(qu[b][q], j), j < 2 ? u0 : u1), bx, au);
         }
