@@ -111,7 +111,8 @@ typedef struct ft_kv_cache {
                                        e2m1 codes u8 [prefix][Hkv][d/2] (low nibble first) */
     const uint8_t *k_block_scale;   /* NVFP4: e4m3 [prefix][Hkv][d/16]; else unused */
     const uint8_t *v_block_scale;
-    float k_scale, v_scale;         /* fp8 / NVFP4: per-tensor scales; bf16: unused */
+    float k_scale, v_scale;         /* fp8 / NVFP4: per-tensor scales, positive and finite
+                                       (else FT_EINVAL); bf16: unused */
 } ft_kv_cache;
 
 /* FT_ABI_VERSION of the library that was loaded. */

@@ -27,6 +27,15 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source extra flags.  attn_extend.hip: MFMA accumulators in ordinary VGPRs (the
+# online softmax rescales the output accumulators with vector multiplies, which cannot
+# read accumulation registers: with them there, every key chunk copied the whole
+# output tile out and back).
+FILE_FLAGS = {
+    "attn_extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -41,7 +50,7 @@ def sources() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(ln for ln in r.stderr.splitlines()
                      if "packed-fp32-ops" not in ln)   # host pass does not know the feature

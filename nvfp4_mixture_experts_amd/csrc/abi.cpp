@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 
 #include "abi_internal.hpp"
@@ -791,6 +792,9 @@ ft_status ft_attn_extend(int32_t n_new, int32_t q_heads, int32_t kv_heads, int32
       return fail(FT_EINVAL, "attn: cache k / v must be 16-byte aligned");
     if (cache->format == 2 && (!cache->k_block_scale || !cache->v_block_scale))
       return fail(FT_EINVAL, "attn: NVFP4 cache needs its block scales");
+    if (cache->format != 0 && !(cache->k_scale > 0.0f && cache->k_scale <= FLT_MAX &&
+                                cache->v_scale > 0.0f && cache->v_scale <= FLT_MAX))
+      return fail(FT_EINVAL, "attn: k_scale and v_scale must be positive and finite");
   }
   AttnParams p{};
   p.n_new = n_new;

@@ -21,11 +21,13 @@
 //      holds 16 scores of ONE query row (keys 16 c + 4 (lane / 16) + r), which is the
 //      operand layout of P^T for v_mfma_f32_16x16x16_bf16: P never leaves registers;
 //   3. online softmax per row in fp32 (base-2 exponentials, the row spread over 4
-//      lanes); the normaliser sums the unscaled probabilities; P times the value
-//      tensor scale as a bf16 pair (hi = bf16(p), lo = bf16(p - hi): about 16
-//      significant bits; one bf16 alone costs the output about 2e-3 of relative L2);
-//   4. O^T = O^T * alpha + V^T P^T on v_mfma_f32_16x16x16_bf16 (each wave d x 16 rows;
-//      the hi and lo products into the same accumulator).
+//      lanes), relative to a reference max that moves only when a chunk exceeds it
+//      by more than 2^8 (O and l are rescaled then, and only then); the normaliser
+//      sums the unscaled probabilities; P times the value tensor scale as a bf16 pair
+//      (hi = bf16(p), lo = bf16(p - hi): about 16 significant bits; one bf16 alone
+//      costs the output about 2e-3 of relative L2);
+//   4. O^T += V^T P^T on v_mfma_f32_16x16x16_bf16 (each wave d x 16 rows; the hi and
+//      lo products into the same accumulator).
 // At the end O / l is rounded to bf16.
 #include "ftmoe_device.hpp"
 #include "ftmoe_kernels.hpp"
@@ -149,17 +151,26 @@ __device__ __forceinline__ void store_chunk(AttnLds<D>& lds, const ChunkRaw<D>& 
 
 template <int D>
 struct RowState {
-  float m, l;             // running max (base 2) and normaliser of the lane's query row
+  float m, l;             // reference max (base 2, -inf before any visible key) of the lane's
+                          // query row, and its normaliser relative to that reference
   at_f32x4 o[D / 16];     // O^T fragments: dims 16 f + 4 (lane / 16) + r of that row
   int lo, hi;             // visible key positions [lo, hi] of the row
   int all_lo, all_hi;     // keys in [all_lo, all_hi] are visible to every row of the block
 };
 
+// O and l stay relative to a row's reference max until a chunk's max exceeds it by
+// more than this (base 2): probabilities are then at most 2^8, and most chunks need
+// no rescaling of O at all.
+constexpr float kRescaleSlack = 8.0f;
+
 // One chunk [c0, end) (end - c0 <= 64) of one source against the wave's 16 rows.
-// kscale2 = key tensor scale x 1/sqrt(d) x log2(e); vscale multiplies P.
+// kscale2 = key tensor scale x 1/sqrt(d) x log2(e) (> 0); lvs = log2 of the value
+// tensor scale (added to the exponent, so P comes out multiplied by the scale) and
+// ivs its reciprocal (the normaliser sums the unscaled probabilities).
 template <int D, int FMT>
 __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)[D / 32], int c0,
-                                           int end, float kscale2, float vscale, RowState<D>& st) {
+                                           int end, float kscale2, float lvs, float ivs,
+                                           RowState<D>& st) {
   const int lane = threadIdx.x & (kWave - 1);
   const int i = lane & 15, g = lane >> 4;
   // S^T = K Q^T: key fragments c of 16; lane: keys 16 c + 4 g + r of query row i
@@ -172,24 +183,40 @@ __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)
       s[c] = mfma(*reinterpret_cast<const at_u32x4*>(&lds.k[16 * c + i][32 * ks + 8 * g]), qf[ks],
                   s[c]);
   }
-  float mx = -INFINITY;
-  // a whole chunk inside every row's visible range needs no mask (most cache chunks)
+  // a whole chunk inside every row's visible range needs no mask (most cache chunks);
+  // the test is the same for the whole block
   const bool whole = end - c0 == kChunk && c0 >= st.all_lo && end - 1 <= st.all_hi;
+  if (!whole) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kpos = c0 + 16 * c + 4 * g + r;
+        const bool vis = (kpos < end) & (kpos >= st.lo) & (kpos <= st.hi);
+        s[c][r] = vis ? s[c][r] : -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kpos = c0 + 16 * c + 4 * g + r;
-      const bool vis = whole || (kpos < end && kpos >= st.lo && kpos <= st.hi);
-      const float v = vis ? s[c][r] * kscale2 : -INFINITY;
-      s[c][r] = v;
-      mx = fmaxf(mx, v);
-    }
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[c][r]);
   mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
   mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-  const float mn = fmaxf(st.m, mx);
-  // no visible key so far: nothing to rescale, every probability 0
-  const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m - mn);
+  mx *= kscale2;  // the chunk's max of the row's scaled scores (scaling by kscale2 > 0 keeps order)
+  // first visible key (reference -inf), or the max moved past the slack: new reference
+  const bool grow = mx > st.m + kRescaleSlack;
+  if (__ballot(grow) != 0) {
+    const float alpha = grow ? __builtin_amdgcn_exp2f(st.m - mx) : 1.0f;  // 0 from -inf: O, l are 0
+#pragma unroll
+    for (int f = 0; f < D / 16; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.o[f][r] *= alpha;
+    st.l *= alpha;
+    st.m = grow ? mx : st.m;
+  }
+  // a row with no visible key so far has only -inf scores: any finite reference gives 0
+  const float bias = (st.m == -INFINITY ? 0.0f : -st.m) + lvs;
   float sum = 0.0f;
   uint2 ph[4], pl[4];  // P^T operands: keys 16 c + 4 g .. + 3, bf16 hi and lo
 #pragma unroll
@@ -200,9 +227,8 @@ __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)
       at_f32x2 pv;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const float pj = mn == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[c][2 * q + e] - mn);
-        sum += pj;
-        pv[e] = pj * vscale;
+        pv[e] = __builtin_amdgcn_exp2f(fmaf(s[c][2 * q + e], kscale2, bias));
+        sum += pv[e];
       }
       const at_bf16x2 h = __builtin_convertvector(pv, at_bf16x2);
       const at_bf16x2 l = __builtin_convertvector(pv - __builtin_convertvector(h, at_f32x2), at_bf16x2);
@@ -214,13 +240,10 @@ __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)
   }
   sum += __shfl_xor(sum, 16, kWave);
   sum += __shfl_xor(sum, 32, kWave);
-  st.l = st.l * alpha + sum;
-  st.m = mn;
-  // O^T = O^T alpha + V^T P^T (V^T operand: dims 16 f + i, keys 16 c + 4 g .. + 3)
+  st.l += sum * ivs;
+  // O^T += V^T P^T (V^T operand: dims 16 f + i, keys 16 c + 4 g .. + 3)
 #pragma unroll
   for (int f = 0; f < D / 16; ++f) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) st.o[f][r] *= alpha;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint2 v = *reinterpret_cast<const uint2*>(&lds.vt[16 * f + i][16 * c + 4 * g]);
@@ -237,8 +260,8 @@ template <int D, int FMT>
 __device__ __forceinline__ void attend_range(AttnLds<D>& lds, const at_u32x4 (&qf)[D / 32],
                                              const void* kc, const void* vc, const uint8_t* kbs,
                                              const uint8_t* vbs, int first, int k0, int k1,
-                                             int Hkv, int kh, float kscale2, float vscale,
-                                             RowState<D>& st) {
+                                             int Hkv, int kh, float kscale2, float lvs,
+                                             float ivs, RowState<D>& st) {
   if (k0 >= k1) return;
   ChunkRaw<D> raw;
   fetch_chunk<D, FMT>(raw, kc, vc, kbs, vbs, k0, first, k0 + kChunk < k1 ? k0 + kChunk : k1, Hkv, kh);
@@ -249,7 +272,7 @@ __device__ __forceinline__ void attend_range(AttnLds<D>& lds, const at_u32x4 (&q
     const int n0 = c0 + kChunk;
     if (n0 < k1) fetch_chunk<D, FMT>(raw, kc, vc, kbs, vbs, n0, first, n0 + kChunk < k1 ? n0 + kChunk : k1, Hkv, kh);
     __syncthreads();
-    chunk_step<D, FMT>(lds, qf, c0, end, kscale2, vscale, st);
+    chunk_step<D, FMT>(lds, qf, c0, end, kscale2, lvs, ivs, st);
   }
 }
 
@@ -294,13 +317,15 @@ __global__ __launch_bounds__(kAttnWaves* kWave) void attn_extend_kernel(AttnPara
   st.all_lo = lo_of(t_last);          // lo grows with the token
   st.all_hi = p.prefix + t_first;
   const float s2 = p.sm_scale * kLog2e;
-  if (klo < p.prefix)
+  if (klo < p.prefix) {
+    const float vs = FMT == 0 ? 1.0f : p.v_scale;
     attend_range<D, FMT>(lds, qf, p.k_cache, p.v_cache, p.k_bscale, p.v_bscale, 0, klo,
                          p.prefix < khi ? p.prefix : khi, p.Hkv, kh,
-                         (FMT == 0 ? 1.0f : p.k_scale) * s2, FMT == 0 ? 1.0f : p.v_scale, st);
+                         (FMT == 0 ? 1.0f : p.k_scale) * s2, __log2f(vs), 1.0f / vs, st);
+  }
   const int n0 = klo > p.prefix ? klo : p.prefix;
   attend_range<D, 0>(lds, qf, p.k_new, p.v_new, nullptr, nullptr, p.prefix, n0, khi, p.Hkv, kh, s2,
-                     1.0f, st);
+                     0.0f, 1.0f, st);
   // O / l (every row sees its own position, so l > 0); lane: dims 16 f + 4 g .. + 3
   const int row = r0 + 16 * wave + i;
   if (row < nrows) {

@@ -153,6 +153,15 @@ def test_host_validation_status_codes(ft):
     assert lib.ft_nvfp4_repack(2048, 100, 8, *([16] * 8), None) == ft.FT_EUNSUPPORTED
 
 
+def test_attn_cache_scale_validation(ft):
+    lib = _raw(ft)
+    for fmt, ks, vs in ((1, 0.0, 1.0), (2, 1.0, -0.5), (2, float("inf"), 1.0), (1, 1.0, float("nan"))):
+        c = ft.FtKvCache(fmt, 64, 256, 256, 256, 256, ks, vs)
+        assert lib.ft_attn_extend(8, 8, 2, 64, 0, 256, 256, 256, ctypes.byref(c), 256,
+                                  None) == ft.FT_EINVAL
+        assert "k_scale and v_scale" in ft.ft_last_error()
+
+
 def test_device_status_and_wait_limit_validation(ft):
     lib = _raw(ft)
     assert lib.ft_moe_device_status(None, 1 << 20, 16, None) == ft.FT_EINVAL
