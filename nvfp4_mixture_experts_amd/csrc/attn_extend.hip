@@ -49,8 +49,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
 struct AttnLds {
-  uint16_t k[kChunk][D + 8];             // keys of the chunk, bf16 (8 of padding)
-  uint16_t vt[D][kChunk + 8];            // values transposed, bf16
+  uint16_t k[kChunk][D + 16];            // keys of the chunk, bf16 (16 of padding)
+  uint16_t vt[D][kChunk + 4];            // values transposed, bf16 (4 of padding)
 };
 
 __device__ __forceinline__ at_f32x4 mfma(at_u32x4 a, at_u32x4 b, at_f32x4 c) {
