@@ -68,3 +68,39 @@ def test_attn_extend_edges(ft, fmt):
         ref = oracle.attn_extend(case["q"], case["k_new"], case["v_new"], case["cache"], window)
         assert_output_close(got.reshape(-1, 64), ref["out"].reshape(-1, 64),
                             f"attn edge fmt={fmt} prefix={prefix} window={window} n={n_new}")
+
+
+@pytest.mark.parametrize("window", [0, 100])
+@pytest.mark.parametrize("fmt", [0, 2])
+def test_attn_extend_scores_that_keep_growing(ft, fmt, window):
+    """Scores that rise along the cache, so that a row's running maximum moves by far
+    more than 2^8 from one 64-key chunk to the next (and, for the NVFP4 cache, barely
+    moves over its first chunks): every rescaling of the output and normaliser, and
+    long stretches of none, against the reference."""
+    rng = np.random.default_rng(41 + fmt + window)
+    prefix, n_new, Hq, Hkv, d = 1000, 24, 8, 2, 64
+    q = np.ones((n_new, Hq, d), np.float32) * (1.0 + 0.5 * rng.random((n_new, Hq, 1), np.float32))
+    case = {"q": synth.bf16_bits_from_f32(q),
+            "k_new": synth.bf16_bits_from_f32(rng.standard_normal((n_new, Hkv, d), np.float32)),
+            "v_new": synth.bf16_bits_from_f32(rng.standard_normal((n_new, Hkv, d), np.float32)),
+            "cache": {"format": fmt, "prefix": prefix}}
+    c = case["cache"]
+    pos = np.arange(prefix, dtype=np.float32)[:, None, None]
+    if fmt == 0:
+        # score ~ q x position / 8: +8 q (natural), 11.5 q (base 2) or more per chunk
+        k = np.broadcast_to(pos / 64.0, (prefix, Hkv, d)) * (1.0 + 0.1 * rng.random((prefix, Hkv, d), np.float32))
+        c["k"] = synth.bf16_bits_from_f32(k.astype(np.float32))
+        c["v"] = synth.bf16_bits_from_f32(rng.standard_normal((prefix, Hkv, d), np.float32))
+    else:
+        # every key code +6 (0x7 in both nibbles), block scales rising one e4m3 step per
+        # 8 positions from 2^-6 to 448: tiny scores first, then jumps of ~2.5x a chunk
+        c["k"] = np.full((prefix, Hkv, d // 2), 0x77, np.uint8)
+        steps = np.minimum(0x08 + np.arange(prefix) // 8, 0x7E).astype(np.uint8)
+        c["k_bscale"] = np.ascontiguousarray(np.broadcast_to(steps[:, None, None], (prefix, Hkv, d // 16)))
+        c["v"] = synth._codes(rng, (prefix, Hkv, d // 2))
+        c["v_bscale"] = synth.SCALE_BYTES[rng.integers(0, 5, (prefix, Hkv, d // 16))]
+        c["k_scale"], c["v_scale"] = 0.25, 0.25
+    got = _run(ft, case, window)
+    ref = oracle.attn_extend(case["q"], case["k_new"], case["v_new"], c, window)
+    assert_output_close(got.reshape(-1, d), ref["out"].reshape(-1, d),
+                        f"attn growing scores fmt={fmt} window={window}")
