@@ -175,14 +175,29 @@ __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)
   const int i = lane & 15, g = lane >> 4;
   // S^T = K Q^T: key fragments c of 16; lane: keys 16 c + 4 g + r of query row i
   at_f32x4 s[4];
+  {
+    at_u32x4 kf[4][D / 32];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    s[c] = at_f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        kf[c][ks] = *reinterpret_cast<const at_u32x4*>(&lds.k[16 * c + i][32 * ks + 8 * g]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[c] = at_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
-      s[c] = mfma(*reinterpret_cast<const at_u32x4*>(&lds.k[16 * c + i][32 * ks + 8 * g]), qf[ks],
-                  s[c]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[c] = mfma(kf[c][ks], qf[ks], s[c]);
   }
+  // the values' fragments travel while the softmax runs
+  uint2 vf[D / 16][4];
+#pragma unroll
+  for (int f = 0; f < D / 16; ++f)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      vf[f][c] = *reinterpret_cast<const uint2*>(&lds.vt[16 * f + i][16 * c + 4 * g]);
+  __builtin_amdgcn_sched_barrier(0);
   // a whole chunk inside every row's visible range needs no mask (most cache chunks);
   // the test is the same for the whole block
   const bool whole = end - c0 == kChunk && c0 >= st.all_lo && end - 1 <= st.all_hi;
@@ -243,14 +258,13 @@ __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)
   st.l += sum * ivs;
   // O^T += V^T P^T (V^T operand: dims 16 f + i, keys 16 c + 4 g .. + 3)
 #pragma unroll
-  for (int f = 0; f < D / 16; ++f) {
+  for (int c = 0; c < 4; ++c)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint2 v = *reinterpret_cast<const uint2*>(&lds.vt[16 * f + i][16 * c + 4 * g]);
-      st.o[f] = mfma16(v, ph[c], st.o[f]);
-      st.o[f] = mfma16(v, pl[c], st.o[f]);
-    }
-  }
+    for (int f = 0; f < D / 16; ++f) st.o[f] = mfma16(vf[f][c], ph[c], st.o[f]);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int f = 0; f < D / 16; ++f) st.o[f] = mfma16(vf[f][c], pl[c], st.o[f]);
 }
 
 // Keys [k0, k1) of one source (the cache in format FMT, or the new tokens in bf16;
