@@ -65,6 +65,23 @@ __device__ __forceinline__ at_f32x4 mfma16(uint2 a, uint2 b, at_f32x4 c) {
 
 __device__ __forceinline__ uint32_t pk(bf16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// max and sum of v over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the 16-lane rows of a
+// wave), in registers: v_permlane16_swap with one register as both operands yields the
+// values of lanes l and l ^ 16, v_permlane32_swap those of l and l ^ 32, in the same
+// order on both lanes of a pair (so both get the same bits)
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Staging of keys [c0, c0 + 64) of one source into LDS, in two halves: fetch_chunk
 // issues the global loads (into registers, so that the next chunk's loads travel
 // while this chunk is multiplied) and store_chunk turns them into bf16 in LDS.  Rows
@@ -216,8 +233,7 @@ __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[c][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  mx = rows_max(mx);
   mx *= kscale2;  // the chunk's max of the row's scaled scores (scaling by kscale2 > 0 keeps order)
   // first visible key (reference -inf), or the max moved past the slack: new reference
   const bool grow = mx > st.m + kRescaleSlack;
@@ -253,8 +269,7 @@ __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)
     ph[c] = make_uint2(hw[0], hw[1]);
     pl[c] = make_uint2(lw[0], lw[1]);
   }
-  sum += __shfl_xor(sum, 16, kWave);
-  sum += __shfl_xor(sum, 32, kWave);
+  sum = rows_sum(sum);
   st.l += sum * ivs;
   // O^T += V^T P^T (V^T operand: dims 16 f + i, keys 16 c + 4 g .. + 3)
 #pragma unroll
