@@ -711,6 +711,13 @@ ft_status ft_fp8_linear(int64_t M, int64_t N, int64_t K, const uint16_t* x, cons
   if (!w_scale_rows) return fail(FT_EINVAL, "fp8 linear: w_scale_rows is NULL");
   if (M == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp8_linear_fused_fits(M, K)) {  // one launch: codes of x formed in every block
+    const hipError_t e = launch_fp8_linear_fused(x, w, static_cast<int>(M), static_cast<int>(N),
+                                                 static_cast<int>(K), w_scale_rows, y,
+                                                 static_cast<int>(N), 0, s);
+    if (e != hipSuccess) return hip_fail(e, "fp8 fused quantise + GEMV kernel");
+    return ok();
+  }
   uint8_t* q = nullptr;
   float* sx = nullptr;
   hipError_t e = launch_fp8_quantize(x, M, K, workspace, &q, &sx, s);

@@ -18,7 +18,9 @@
 // 64 x 64 output tiles per 4-wave block, 64-deep K slabs staged in LDS, or for M <= 8
 // rows of activations (decode) a GEMV: a wave per 4 weight rows, each lane 32 K bytes
 // of them with all of its loads in flight at once, codes widened to bf16 pairs
-// (exactly: an e4m3 value has 4 significant bits) into v_dot2_f32_bf16.
+// (exactly: an e4m3 value has 4 significant bits) into v_dot2_f32_bf16.  The row-wise
+// call with at most 8 rows of at most 2048 (and M K <= 16 Ki) runs as ONE kernel: every
+// GEMV block forms the scale and the codes of x itself, in LDS.
 #include "ftmoe_device.hpp"
 #include "ftmoe_kernels.hpp"
 
@@ -405,6 +407,102 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemv_kernel(
   }
 }
 
+// Few activation rows with all of x small (M <= kGemvMaxM, M K <= kSmallQuantMax, K <=
+// kGemvChunks * kWave * 16: one pass): the quantisation and the GEMV in ONE launch.  Every
+// block reads all of x, forms s_x and the codes of x itself with the arithmetic of the
+// quantisation kernels (the same bits), keeps the codes in LDS, and multiplies as
+// fp8_gemv_kernel does; its weight loads are issued first, so they travel meanwhile.
+template <int MM>
+__global__ __launch_bounds__(4 * kWave) void fp8_gemv_fused_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w, int M, int N, int K,
+    const float* __restrict__ row_scale, uint16_t* __restrict__ y, int ldy, int col0) {
+  constexpr int kXP = kSmallQuantMax / 8 / (4 * kWave);  // 16-byte pieces of x per thread
+  __shared__ __align__(16) uint8_t xs[kSmallQuantMax];   // codes of x, [M][K]
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int n0 = (blockIdx.x * 4 + wave) * kGemvRows;  // may be >= N: the wave still
+  const int nch = K / 16;                              // takes part in the barriers
+  uint4 wv[kGemvRows][kGemvChunks];
+  bool ok[kGemvChunks];
+#pragma unroll
+  for (int j = 0; j < kGemvChunks; ++j) {
+    const int ci = j * kWave + lane;
+    ok[j] = ci < nch;
+    const int cc = ok[j] ? ci : nch - 1;  // in range; its terms are dropped below
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+      const int n = n0 + r < N ? n0 + r : N - 1;
+      wv[r][j] = *reinterpret_cast<const uint4*>(w + static_cast<size_t>(n) * K + 16 * cc);
+    }
+  }
+  const int n8 = M * K / 8;  // K % 64 == 0
+  uint4 xp[kXP];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kXP; ++i) {
+    const int pc = tid + 4 * kWave * i;
+    xp[i] = pc < n8 ? reinterpret_cast<const uint4*>(x)[pc] : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < kXP; ++i) m = absmax8(m, xp[i]);
+  m = __int_as_float(static_cast<int>(wave_max_u32(__float_as_uint(m))));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sx = mx > 0.0f ? __fdiv_rn(mx, 448.0f) : 1.0f;
+#pragma unroll
+  for (int i = 0; i < kXP; ++i) {
+    const int pc = tid + 4 * kWave * i;
+    if (pc < n8)
+      reinterpret_cast<uint2*>(xs)[pc] = make_uint2(quant4(xp[i].x, xp[i].y, sx), quant4(xp[i].z, xp[i].w, sx));
+  }
+  __syncthreads();
+  float acc[kGemvRows][MM];
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) acc[r][mm] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kGemvChunks; ++j) {
+    if (!ok[j]) continue;
+    const int cc = j * kWave + lane;
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) {
+      const int mr = mm < M ? mm : M - 1;
+      const uint4 xv = *reinterpret_cast<const uint4*>(xs + mr * K + 16 * cc);
+      bf16x2 xb[8];
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xb[2 * q] = e4m3x2_to_bf16<false>(xw[q]);
+        xb[2 * q + 1] = e4m3x2_to_bf16<true>(xw[q]);
+      }
+#pragma unroll
+      for (int r = 0; r < kGemvRows; ++r) {
+        const uint32_t ww[4] = {wv[r][j].x, wv[r][j].y, wv[r][j].z, wv[r][j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[r][mm] = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16<false>(ww[q]), xb[2 * q],
+                                                       acc[r][mm], false);
+          acc[r][mm] = __builtin_amdgcn_fdot2_f32_bf16(e4m3x2_to_bf16<true>(ww[q]), xb[2 * q + 1],
+                                                       acc[r][mm], false);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kGemvRows; ++r) {
+    const int n = n0 + r;
+    const float sn = sx * row_scale[n < N ? n : N - 1];
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) {
+      const float v = group_sum_last<kWave>(acc[r][mm]);  // in lane 63
+      if (lane == kWave - 1 && n < N && mm < M)
+        y[static_cast<size_t>(mm) * ldy + col0 + n] = f32_to_bf16_bits(v * sn);
+    }
+  }
+}
+
 int amax_blocks(size_t n) {
   const size_t b = (n + kAmaxThreads * 16 - 1) / (kAmaxThreads * 16);
   return static_cast<int>(b < 1 ? 1 : (b > kAmaxMaxBlocks ? kAmaxMaxBlocks : b));
@@ -440,6 +538,24 @@ hipError_t launch_fp8_quantize(const uint16_t* x, int64_t M, int64_t K, void* ws
   fp8_quantize_kernel<<<dim3(static_cast<unsigned>(qb < 4096 ? qb : 4096)), dim3(kAmaxThreads), 0,
                         s>>>(reinterpret_cast<const uint4*>(x), n8, partial, nb,
                              reinterpret_cast<uint2*>(*xq), *s_x);
+  return hipGetLastError();
+}
+
+bool fp8_linear_fused_fits(int64_t M, int64_t K) {
+  return M >= 1 && M <= kGemvMaxM && static_cast<size_t>(M * K) <= kSmallQuantMax &&
+         K <= kGemvChunks * kWave * 16;
+}
+
+hipError_t launch_fp8_linear_fused(const uint16_t* x, const uint8_t* w, int M, int N, int K,
+                                   const float* row_scale, uint16_t* y, int ldy, int col0,
+                                   hipStream_t s) {
+  if (!fp8_linear_fused_fits(M, K) || !row_scale) return hipErrorInvalidValue;
+  if (N <= 0) return hipSuccess;
+  const dim3 g((N + 4 * kGemvRows - 1) / (4 * kGemvRows)), b(4 * kWave);
+  if (M == 1) fp8_gemv_fused_kernel<1><<<g, b, 0, s>>>(x, w, M, N, K, row_scale, y, ldy, col0);
+  else if (M == 2) fp8_gemv_fused_kernel<2><<<g, b, 0, s>>>(x, w, M, N, K, row_scale, y, ldy, col0);
+  else if (M <= 4) fp8_gemv_fused_kernel<4><<<g, b, 0, s>>>(x, w, M, N, K, row_scale, y, ldy, col0);
+  else fp8_gemv_fused_kernel<8><<<g, b, 0, s>>>(x, w, M, N, K, row_scale, y, ldy, col0);
   return hipGetLastError();
 }
 

@@ -167,6 +167,11 @@ hipError_t launch_dequant(int H, int I, const Bank& b, int expert, int tensor, i
 // per-tensor FP8 W8A8 linear: workspace bytes (codes, amax partials, scale), the
 // activation quantisation (sets *xq and *s_x to their places in ws) and the GEMM
 // (row_scale [N] when set, else `scale` for every row; y columns col0.. of stride ldy)
+// Quantisation and GEMV in one launch for few, short activation rows (row-wise scales).
+bool fp8_linear_fused_fits(int64_t M, int64_t K);
+hipError_t launch_fp8_linear_fused(const uint16_t* x, const uint8_t* w, int M, int N, int K,
+                                   const float* row_scale, uint16_t* y, int ldy, int col0,
+                                   hipStream_t s);
 size_t fp8_linear_workspace(int64_t M, int64_t K);
 hipError_t launch_fp8_quantize(const uint16_t* x, int64_t M, int64_t K, void* ws, uint8_t** xq,
                                float** s_x, hipStream_t s);

@@ -122,7 +122,8 @@ def test_fp8_linear_matches_oracle_and_parts_equal_rowwise(ft, tokens):
     assert np.array_equal(_bits(yp), _bits(y))
 
 
-@pytest.mark.parametrize("tokens,hidden", [(19, 1024), (5, 1024), (3, 1088), (130, 1088)])
+@pytest.mark.parametrize("tokens,hidden", [(19, 1024), (5, 1024), (3, 1088), (130, 1088),
+                                          (2, 4096), (8, 3072)])   # few rows past the one-launch form
 def test_fp8_linear_ragged_parts_and_rows(ft, tokens, hidden):
     # parts whose row counts are not multiples of the 64- or 128-row tiles (nor of the
     # GEMV's 16 rows per block); K = 1088: 68 16-byte chunks, so most GEMV lanes hold
