@@ -11,7 +11,8 @@
 //
 // A block of 4 waves takes 64 query rows of one kv head: row r is (token, head of the
 // kv head's group) number 64 b + r in token-major order, so the query heads that
-// share a kv head share every staged key and value.  Per chunk of 64 keys:
+// share a kv head share every staged key and value.  Chunks alternate between two LDS
+// buffers: chunk j + 1 is staged between chunk j's P V products.  Per chunk of 64 keys:
 //   1. the chunk's keys and values are turned into bf16 in LDS (exact for every
 //      format: an e4m3 value, or an e2m1 code times its e4m3 block scale, has at most
 //      6 significant bits), keys as rows [key][dim], values transposed [dim][key];
@@ -184,10 +185,10 @@ constexpr float kRescaleSlack = 8.0f;
 // kscale2 = key tensor scale x 1/sqrt(d) x log2(e) (> 0); lvs = log2 of the value
 // tensor scale (added to the exponent, so P comes out multiplied by the scale) and
 // ivs its reciprocal (the normaliser sums the unscaled probabilities).
-template <int D, int FMT>
+template <int D, int FMT, class Stage>
 __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)[D / 32], int c0,
                                            int end, float kscale2, float lvs, float ivs,
-                                           RowState<D>& st) {
+                                           RowState<D>& st, Stage&& stage) {
   const int lane = threadIdx.x & (kWave - 1);
   const int i = lane & 15, g = lane >> 4;
   // S^T = K Q^T: key fragments c of 16; lane: keys 16 c + 4 g + r of query row i
@@ -276,6 +277,7 @@ __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int f = 0; f < D / 16; ++f) st.o[f] = mfma16(vf[f][c], ph[c], st.o[f]);
+  stage();  // vector work that runs while the matrix cores take the products above
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -286,28 +288,38 @@ __device__ __forceinline__ void chunk_step(AttnLds<D>& lds, const at_u32x4 (&qf)
 // `first` = the position of the source's row 0), 64 at a time, each chunk's loads
 // issued while the previous chunk is multiplied.
 template <int D, int FMT>
-__device__ __forceinline__ void attend_range(AttnLds<D>& lds, const at_u32x4 (&qf)[D / 32],
+__device__ __forceinline__ void attend_range(AttnLds<D> (&lds)[2], const at_u32x4 (&qf)[D / 32],
                                              const void* kc, const void* vc, const uint8_t* kbs,
                                              const uint8_t* vbs, int first, int k0, int k1,
                                              int Hkv, int kh, float kscale2, float lvs,
                                              float ivs, RowState<D>& st) {
   if (k0 >= k1) return;
+  auto chunk_end = [&](int c) { return c + kChunk < k1 ? c + kChunk : k1; };
   ChunkRaw<D> raw;
-  fetch_chunk<D, FMT>(raw, kc, vc, kbs, vbs, k0, first, k0 + kChunk < k1 ? k0 + kChunk : k1, Hkv, kh);
+  fetch_chunk<D, FMT>(raw, kc, vc, kbs, vbs, k0, first, chunk_end(k0), Hkv, kh);
+  // both buffers are free: every chunk step ends with a barrier
+  store_chunk<D, FMT>(lds[0], raw);
+  if (k0 + kChunk < k1) fetch_chunk<D, FMT>(raw, kc, vc, kbs, vbs, k0 + kChunk, first, chunk_end(k0 + kChunk), Hkv, kh);
+  __syncthreads();
+  int buf = 0;
   for (int c0 = k0; c0 < k1; c0 += kChunk) {
-    const int end = c0 + kChunk < k1 ? c0 + kChunk : k1;
-    __syncthreads();  // the previous chunk's keys and values have been read
-    store_chunk<D, FMT>(lds, raw);
-    const int n0 = c0 + kChunk;
-    if (n0 < k1) fetch_chunk<D, FMT>(raw, kc, vc, kbs, vbs, n0, first, n0 + kChunk < k1 ? n0 + kChunk : k1, Hkv, kh);
+    const int n1 = c0 + kChunk, n2 = c0 + 2 * kChunk;
+    // the next chunk goes to the other buffer (last read by the previous chunk, before
+    // the previous barrier), between this chunk's P V products
+    chunk_step<D, FMT>(lds[buf], qf, c0, chunk_end(c0), kscale2, lvs, ivs, st, [&]() {
+      if (n1 < k1) {
+        store_chunk<D, FMT>(lds[buf ^ 1], raw);
+        if (n2 < k1) fetch_chunk<D, FMT>(raw, kc, vc, kbs, vbs, n2, first, chunk_end(n2), Hkv, kh);
+      }
+    });
     __syncthreads();
-    chunk_step<D, FMT>(lds, qf, c0, end, kscale2, lvs, ivs, st);
+    buf ^= 1;
   }
 }
 
 template <int D, int FMT>
 __global__ __launch_bounds__(kAttnWaves* kWave) void attn_extend_kernel(AttnParams p) {
-  __shared__ AttnLds<D> lds;
+  __shared__ AttnLds<D> lds[2];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
