@@ -482,6 +482,9 @@ def measure_decode(args, w, steps: int, warmup: int, reps: int, variant: str = "
         torch.cuda.synchronize()
         rep_ms.append(start.elapsed_time(end) / steps)
     wall = time.perf_counter() - t0
+    # secondary, not an HBM figure: every call on layer instance 0, whose weights then
+    # stay in the Infinity Cache (untimed by the headline; reported beside it)
+    warm_ms = float(np.median(_graph_reps(torch, min(steps, 200), lambda i, s: call(0, s), 3)))
     status = ftmoe.device_status(ws)
     if status != 0:
         raise RuntimeError(f"a device-side wait gave up during timing (status {status:#x})")
@@ -535,6 +538,9 @@ def measure_decode(args, w, steps: int, warmup: int, reps: int, variant: str = "
         "launch": f"{reps} HIP graphs of {steps} calls each (one call per layer instance in "
                   "turn), each replayed once and timed; median reported",
         "eager_ms_per_step": round(eager_ms, 6),
+        "mall_warm_l1_ms_per_step": round(warm_ms, 6),
+        "mall_warm_l1_note": "every call on one layer instance (weights resident in the Infinity "
+                             "Cache): not an HBM figure",
         "device_status": status,
     }
 
@@ -633,7 +639,7 @@ def main() -> int:
     }
     for key in ("config", "roofline", "achieved_gbps", "hbm_peak_frac", "reps",
                 "ms_per_step_reps", "wall_s_timed", "launch", "eager_ms_per_step",
-                "device_status"):
+                "mall_warm_l1_ms_per_step", "mall_warm_l1_note", "device_status"):
         out[key] = main_m[key]
     if extra:
         out["also"] = extra
