@@ -435,6 +435,43 @@ def test_decode_matches_oracle(gpu, name, tokens, sample):
         assert np.array_equal(ids.cpu().numpy(), ref_ids)
 
 
+def _host_layer_of(w, d):
+    """The oracle's inputs (a host Layer) from a layer instance drawn on the device."""
+    def host(t):
+        return None if t is None else t.cpu().numpy()
+    L = synth.Layer(workload=w, w_router=host(d["w_router"]).astype(np.float32),
+                    bias=host(d["bias"]), **{k: host(v) for k, v in d["routed"].items()})
+    if d["shared"] is not None:
+        sb = d["shared"]
+        L.s13_codes, L.s13_scales = host(sb["w13_codes"]), host(sb["w13_scales"])
+        L.s2_codes, L.s2_scales = host(sb["w2_codes"]), host(sb["w2_scales"])
+        L.s_global = host(sb["global_scale"])
+        L.shared_gate = d["shared_gate"].cpu().view(torch.int16).numpy().view(np.uint16)
+    return L
+
+
+@pytest.mark.parametrize("name", ["decode_e288_top8", "decode_e512_top10_shared"])
+def test_decode_timed_instances_match_oracle(gpu, name):
+    """Layer instances that the benchmark times (drawn on the device; the last of its 46
+    among them), downloaded as the oracle's inputs: the routes, routing weights and output
+    of one token each, as in the timed calls."""
+    w = synth.WORKLOADS[name]
+    for inst in (1, 23, 45):
+        d = synth.make_layer_device(w, inst, torch.device("cuda"))
+        dl = gpu.upload_canonical(w, d["w_router"], d["bias"], d["routed"], d["shared"],
+                                  d["shared_gate"], "cuda")
+        L = _host_layer_of(w, d)
+        del d
+        x = synth.make_tokens(w, instance=inst, tokens=1)
+        y, ids, wt = decode_checked(gpu, dl, gpu.tokens_to_device(x))
+        ref = oracle_layer_rows(L, x, [0])
+        assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+        assert f32_ulp_diff(wt.cpu().numpy(), ref["weights"]).max() <= 2
+        assert_output_close(gpu.bf16_bits(y), ref["y"], f"{name} instance {inst}")
+        del dl, L
+        torch.cuda.empty_cache()
+
+
 def test_decode_all_experts_selected(gpu):
     """k = E: the layer is the dense softmax mixture of every expert."""
     w = synth.dataclasses.replace(synth.WORKLOADS["decode_e512_top10_shared"], num_experts=16,
