@@ -450,24 +450,31 @@ def _host_layer_of(w, d):
     return L
 
 
-@pytest.mark.parametrize("name", ["decode_e288_top8", "decode_e512_top10_shared"])
-def test_decode_timed_instances_match_oracle(gpu, name):
-    """Layer instances that the benchmark times (drawn on the device; the last of its 46
-    among them), downloaded as the oracle's inputs: the routes, routing weights and output
-    of one token each, as in the timed calls."""
+@pytest.mark.parametrize("name,instances,tokens,rows", [
+    ("decode_e288_top8", (1, 23, 45), 1, [0]),
+    ("decode_e512_top10_shared", (1, 23, 45), 1, [0]),
+    ("batched_decode_t32_hot64", (1, 11), 32, [0, 5, 13, 31]),
+])
+def test_decode_timed_instances_match_oracle(gpu, name, instances, tokens, rows):
+    """Layer instances that the benchmark times (drawn on the device; the last of them
+    among these), downloaded as the oracle's inputs: the routes of every token, and the
+    routing weights and outputs of the sampled ones."""
     w = synth.WORKLOADS[name]
-    for inst in (1, 23, 45):
+    for inst in instances:
         d = synth.make_layer_device(w, inst, torch.device("cuda"))
         dl = gpu.upload_canonical(w, d["w_router"], d["bias"], d["routed"], d["shared"],
                                   d["shared_gate"], "cuda")
         L = _host_layer_of(w, d)
         del d
-        x = synth.make_tokens(w, instance=inst, tokens=1)
+        x = synth.make_tokens(w, instance=inst, tokens=tokens)
         y, ids, wt = decode_checked(gpu, dl, gpu.tokens_to_device(x))
-        ref = oracle_layer_rows(L, x, [0])
-        assert np.array_equal(ids.cpu().numpy(), ref["ids"])
-        assert f32_ulp_diff(wt.cpu().numpy(), ref["weights"]).max() <= 2
-        assert_output_close(gpu.bf16_bits(y), ref["y"], f"{name} instance {inst}")
+        ref = oracle_layer_rows(L, x, rows)
+        assert np.array_equal(ids.cpu().numpy()[rows], ref["ids"])
+        assert f32_ulp_diff(wt.cpu().numpy()[rows], ref["weights"]).max() <= 2
+        assert_output_close(gpu.bf16_bits(y)[rows], ref["y"], f"{name} instance {inst}")
+        if tokens > 1:
+            ref_ids, _ = oracle.topk(oracle.router_logits(x, L.w_router, L.bias), w.top_k)
+            assert np.array_equal(ids.cpu().numpy(), ref_ids)
         del dl, L
         torch.cuda.empty_cache()
 
