@@ -1001,7 +1001,11 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PrefillParams p) {
   float4 v[kMaxSlots];
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s)
-    v[s] = *reinterpret_cast<const float4*>(src + static_cast<size_t>(s < p.nslots ? s : p.nslots - 1) * p.H);
+    {
+      typedef float nt_f4 __attribute__((ext_vector_type(4)));
+      const nt_f4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(src + static_cast<size_t>(s < p.nslots ? s : p.nslots - 1) * p.H));
+      v[s] = make_float4(t.x, t.y, t.z, t.w);
+    }
   // nothing that uses a loaded value is scheduled between the loads (it would wait
   // for the earlier loads before the later ones are issued)
   __builtin_amdgcn_sched_barrier(0);
