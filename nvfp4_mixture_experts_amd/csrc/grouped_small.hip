@@ -44,6 +44,13 @@ constexpr int kSgKBlock = 512;  // K elements of a row held in registers at once
 constexpr int kSgQ = kSgKBlock / 128;  // 16-byte code loads per lane per row and K block
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Non-temporal: for the down codes of a decode batch (measured: 12.2 -> 11.8 us at T = 32;
+// the gate|up codes, which hot experts' units share, were slower so).
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+  typedef unsigned int nt_u4 __attribute__((ext_vector_type(4)));
+  const nt_u4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ sg_f32x4 mfma(uint4 a, uint4 b, sg_f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sg_bf16x8, a),
@@ -472,7 +479,7 @@ __global__ __launch_bounds__(kSgThreads, 2) void sg_down_pipe_kernel(PrefillPara
 #pragma unroll
       for (int s = 0; s < NKC; ++s) {
         const size_t c = cbase + 4 * s + g;  // chunk 4 s + g of 32 K
-        q[rt][s] = ldg16(bank.w2 + (c * H + row) * 16);
+        q[rt][s] = ldg16_nt(bank.w2 + (c * H + row) * 16);
         sc[rt][s] = *reinterpret_cast<const uint32_t*>(bank.w2s + (c * H + (row & ~1)) * 2);
       }
     }
