@@ -484,7 +484,8 @@ def measure_decode(args, w, steps: int, warmup: int, reps: int, variant: str = "
     wall = time.perf_counter() - t0
     # secondary, not an HBM figure: every call on layer instance 0, whose weights then
     # stay in the Infinity Cache (untimed by the headline; reported beside it)
-    warm_ms = float(np.median(_graph_reps(torch, min(steps, 200), lambda i, s: call(0, s), 3)))
+    warm_ms = (None if args.no_mall_warm else
+               float(np.median(_graph_reps(torch, min(steps, 200), lambda i, s: call(0, s), 3))))
     status = ftmoe.device_status(ws)
     if status != 0:
         raise RuntimeError(f"a device-side wait gave up during timing (status {status:#x})")
@@ -538,7 +539,7 @@ def measure_decode(args, w, steps: int, warmup: int, reps: int, variant: str = "
         "launch": f"{reps} HIP graphs of {steps} calls each (one call per layer instance in "
                   "turn), each replayed once and timed; median reported",
         "eager_ms_per_step": round(eager_ms, 6),
-        "mall_warm_l1_ms_per_step": round(warm_ms, 6),
+        "mall_warm_l1_ms_per_step": None if warm_ms is None else round(warm_ms, 6),
         "mall_warm_l1_note": "every call on one layer instance (weights resident in the Infinity "
                              "Cache): not an HBM figure",
         "device_status": status,
@@ -571,6 +572,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-stream-probe", action="store_true")
+    ap.add_argument("--no-mall-warm", action="store_true",
+                    help="skip the Infinity-Cache-warm secondary decode figure (profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain elementwise copy (negation) of this many "
                          "MiB, as the known-size reference for HBM byte counters")
