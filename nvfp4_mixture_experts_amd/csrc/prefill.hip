@@ -238,12 +238,35 @@ __global__ __launch_bounds__(kMaxExperts) void pf_scan_kernel(PrefillParams p) {
   group_units(p, c, p.cursor);
 }
 
-// ... and a scatter through global cursors.
+// ... and a scatter through global cursors: a block ranks its kScatterPairs pairs per
+// expert in LDS, reserves each expert's run with ONE global atomic (one per pair
+// serialised ~160 device-scope atomics on every expert's cursor), and writes its
+// pairs there.
+constexpr int kScatterPairs = 2048;
+
 __global__ __launch_bounds__(256) void pf_scatter_kernel(PrefillParams p) {
-  const int pair = blockIdx.x * blockDim.x + threadIdx.x;
-  if (pair >= p.P) return;
-  const int e = valid_expert(p, pair);
-  if (e >= 0) p.sorted[atomicAdd(&p.cursor[e], 1)] = pair;
+  constexpr int kPer = kScatterPairs / 256;
+  __shared__ int cnt[kMaxExperts];
+  for (int e = threadIdx.x; e < p.E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * kScatterPairs;
+  int ev[kPer], rk[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int pair = p0 + threadIdx.x + 256 * j;
+    ev[j] = pair < p.P ? valid_expert(p, pair) : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) rk[j] = ev[j] >= 0 ? atomicAdd(&cnt[ev[j]], 1) : 0;
+  __syncthreads();
+  for (int e = threadIdx.x; e < p.E; e += 256) {  // one thread per expert: no race
+    const int c = cnt[e];
+    cnt[e] = c ? atomicAdd(&p.cursor[e], c) : 0;   // where the block's run of e starts
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (ev[j] >= 0) p.sorted[cnt[ev[j]] + rk[j]] = p0 + threadIdx.x + 256 * j;
 }
 
 // --------------------------------------------------------------- GEMMs --
@@ -1051,7 +1074,7 @@ hipError_t launch_prefill(const PrefillParams& p0, hipStream_t s) {
   } else {
     pf_hist_kernel<<<nblk, 256, 0, s>>>(p);
     pf_scan_kernel<<<1, kMaxExperts, 0, s>>>(p);
-    pf_scatter_kernel<<<(p.P + 255) / 256, 256, 0, s>>>(p);
+    pf_scatter_kernel<<<(p.P + kScatterPairs - 1) / kScatterPairs, 256, 0, s>>>(p);
   }
   const unsigned g1 = ugroups * 8 * p.ntiles1, g2 = ugroups * 8 * p.ntiles2;
   if (p.unit_tokens == kPfUnitTokens) {
