@@ -568,7 +568,8 @@ __global__ __launch_bounds__(256) void route_prep_kernel(RouteParams p) {
 // 16 x 16 with both pieces of a row into the same fp32 accumulator.  Rows and
 // tokens past the end repeat the last one (their results are not stored).
 constexpr int kApproxE = 64;         // experts per block
-constexpr int kApproxT = 256;        // tokens per block (64 per wave)
+constexpr int kApproxT = 128;        // tokens per block (32 per wave)
+constexpr int kApproxFB = kApproxT / (4 * 16);  // token fragments per wave
 constexpr int kApproxRowU4 = 8 + 1;  // 16-byte words of a staged row of 64 K (one of padding)
 
 __global__ __launch_bounds__(256) void route_approx_kernel(RouteParams p) {
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(256) void route_approx_kernel(RouteParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = p.H;
   const int e0 = blockIdx.x * kApproxE;
-  const int t0 = blockIdx.y * kApproxT + 64 * wave;
+  const int t0 = blockIdx.y * kApproxT + 16 * kApproxFB * wave;
   const int i = lane & 15, g = lane >> 4;
   // staging: thread tid moves words tid + 256 j (j < 4) of the stage: row (w >> 4),
   // piece ((w >> 3) & 1), word (w & 7) of the row's 64 K
@@ -590,24 +591,24 @@ __global__ __launch_bounds__(256) void route_approx_kernel(RouteParams p) {
     asrc[j] = p.wsplit + static_cast<size_t>(min(e0 + row, p.E - 1)) * 2 * H + pc * H + 8 * c8;
     adst[j] = (pc * kApproxE + row) * kApproxRowU4 + c8;
   }
-  const uint16_t* bsrc[4];
+  const uint16_t* bsrc[kApproxFB];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < kApproxFB; ++f)
     bsrc[f] = p.x + static_cast<size_t>(min(t0 + 16 * f + i, p.T - 1)) * H + 8 * g;
-  rb_f32x4 acc[4][4];
+  rb_f32x4 acc[4][kApproxFB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = rb_f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < kApproxFB; ++b) acc[a][b] = rb_f32x4{0.f, 0.f, 0.f, 0.f};
   rb_u32x4 ra[4];  // native vectors: a copy of HIP's uint4 between memory spaces stays a memcpy
-  uint4 rb[2][4][2];
+  uint4 rb[2][kApproxFB][2];
   auto load_a = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) ra[j] = *reinterpret_cast<const rb_u32x4*>(asrc[j] + k0);
   };
-  auto load_b = [&](int k0, uint4 (&dst)[4][2]) __attribute__((always_inline)) {
+  auto load_b = [&](int k0, uint4 (&dst)[kApproxFB][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < kApproxFB; ++f)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) dst[f][ks] = *reinterpret_cast<const uint4*>(bsrc[f] + k0 + 32 * ks);
   };
@@ -615,7 +616,7 @@ __global__ __launch_bounds__(256) void route_approx_kernel(RouteParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) reinterpret_cast<rb_u32x4*>(dst)[adst[j]] = ra[j];
   };
-  auto compute = [&](const uint4* sa_cur, const uint4 (&b)[4][2]) __attribute__((always_inline)) {
+  auto compute = [&](const uint4* sa_cur, const uint4 (&b)[kApproxFB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       uint4 af[2][4];
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(256) void route_approx_kernel(RouteParams p) {
 #pragma unroll
         for (int fa = 0; fa < 4; ++fa)
 #pragma unroll
-          for (int fb = 0; fb < 4; ++fb)
+          for (int fb = 0; fb < kApproxFB; ++fb)
             acc[fa][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(rb_bf16x8, af[pc][fa]), __builtin_bit_cast(rb_bf16x8, b[fb][ks]),
                 acc[fa][fb], 0, 0, 0);
@@ -659,7 +660,7 @@ __global__ __launch_bounds__(256) void route_approx_kernel(RouteParams p) {
   }
   // C lane l: expert rows 4 (l / 16) + r of the fragment, token l % 16
 #pragma unroll
-  for (int fb = 0; fb < 4; ++fb) {
+  for (int fb = 0; fb < kApproxFB; ++fb) {
     const int t = t0 + 16 * fb + i;
     if (t >= p.T) continue;
     float* out = p.logits + static_cast<size_t>(t) * p.E;
