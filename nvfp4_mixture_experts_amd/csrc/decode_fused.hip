@@ -45,8 +45,9 @@
 #include "handoff.hpp"
 
 namespace {
-// Non-temporal 16-byte load (no cache allocation) for the gate|up codes, each read once
-// per call: ~1% per call at both batch-1 shapes; for the down codes it was slower.
+// Non-temporal 16-byte load (no cache allocation) for the NVFP4 gate|up codes, each read
+// once per call: ~1% per call at both batch-1 shapes; for the down codes, and for the
+// block-fp8 codes (15.9 -> 17.0 us), it was slower.
 __device__ __forceinline__ uint4 ldnt16(const void* a) {
   typedef unsigned int nt_u4 __attribute__((ext_vector_type(4)));
   const nt_u4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(a));
@@ -586,10 +587,10 @@ __global__ __launch_bounds__(kFWaves* kWave, 1) void moe_decode_fused_kernel(Fus
             const int j = col + LPR * c;
             const uint8_t* gr = codes + rr * H + 32 * j;
             const uint8_t* ur = codes + (I + rr) * H + 32 * j;
-            qg[jj][c] = ldnt16(gr);
-            qg2[jj][c] = ldnt16(gr + 16);
-            qu[jj][c] = ldnt16(ur);
-            qu2[jj][c] = ldnt16(ur + 16);
+            qg[jj][c] = *reinterpret_cast<const uint4*>(gr);
+            qg2[jj][c] = *reinterpret_cast<const uint4*>(gr + 16);
+            qu[jj][c] = *reinterpret_cast<const uint4*>(ur);
+            qu2[jj][c] = *reinterpret_cast<const uint4*>(ur + 16);
             fsg[jj][c] = sc[(rr / 128) * kb + j / 4];
             fsu[jj][c] = sc[((I + rr) / 128) * kb + j / 4];
             sg[jj][c] = su[jj][c] = 0;
