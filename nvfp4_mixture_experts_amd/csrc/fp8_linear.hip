@@ -27,6 +27,13 @@
 namespace ftmoe {
 namespace {
 
+// 16-byte load without cache allocation (for weights read once per call)
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+  typedef unsigned int nt_u4 __attribute__((ext_vector_type(4)));
+  const nt_u4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 // native vector: a HIP uint4 copied from global memory to LDS stays a memcpy through
 // private memory
@@ -412,6 +419,13 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemv_kernel(
 // block reads all of x, forms s_x and the codes of x itself with the arithmetic of the
 // quantisation kernels (the same bits), keeps the codes in LDS, and multiplies as
 // fp8_gemv_kernel does; its weight loads are issued first, so they travel meanwhile.
+// Each wave takes kFusedRows weight rows (2, not 4: twice the blocks, so more CUs share
+// the stream), and the weights, read once per call, are loaded non-temporally (no cache
+// allocation).  Measured on the 1-token q|k|v projection (K 2048, N 5120): 6.01 us per call
+// with 4 rows and plain loads, 5.59 with 2 rows, 5.65 with non-temporal loads, 5.30 with
+// both (1 row and non-temporal loads: 5.60).
+constexpr int kFusedRows = 2;
+
 template <int MM>
 __global__ __launch_bounds__(4 * kWave) void fp8_gemv_fused_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w, int M, int N, int K,
@@ -420,9 +434,9 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemv_fused_kernel(
   __shared__ __align__(16) uint8_t xs[kSmallQuantMax];   // codes of x, [M][K]
   __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int n0 = (blockIdx.x * 4 + wave) * kGemvRows;  // may be >= N: the wave still
+  const int n0 = (blockIdx.x * 4 + wave) * kFusedRows;  // may be >= N: the wave still
   const int nch = K / 16;                              // takes part in the barriers
-  uint4 wv[kGemvRows][kGemvChunks];
+  uint4 wv[kFusedRows][kGemvChunks];
   bool ok[kGemvChunks];
 #pragma unroll
   for (int j = 0; j < kGemvChunks; ++j) {
@@ -430,9 +444,9 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemv_fused_kernel(
     ok[j] = ci < nch;
     const int cc = ok[j] ? ci : nch - 1;  // in range; its terms are dropped below
 #pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) {
+    for (int r = 0; r < kFusedRows; ++r) {
       const int n = n0 + r < N ? n0 + r : N - 1;
-      wv[r][j] = *reinterpret_cast<const uint4*>(w + static_cast<size_t>(n) * K + 16 * cc);
+      wv[r][j] = ldg16_nt(w + static_cast<size_t>(n) * K + 16 * cc);
     }
   }
   const int n8 = M * K / 8;  // K % 64 == 0
@@ -457,9 +471,9 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemv_fused_kernel(
       reinterpret_cast<uint2*>(xs)[pc] = make_uint2(quant4(xp[i].x, xp[i].y, sx), quant4(xp[i].z, xp[i].w, sx));
   }
   __syncthreads();
-  float acc[kGemvRows][MM];
+  float acc[kFusedRows][MM];
 #pragma unroll
-  for (int r = 0; r < kGemvRows; ++r)
+  for (int r = 0; r < kFusedRows; ++r)
 #pragma unroll
     for (int mm = 0; mm < MM; ++mm) acc[r][mm] = 0.0f;
 #pragma unroll
@@ -478,7 +492,7 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemv_fused_kernel(
         xb[2 * q + 1] = e4m3x2_to_bf16<true>(xw[q]);
       }
 #pragma unroll
-      for (int r = 0; r < kGemvRows; ++r) {
+      for (int r = 0; r < kFusedRows; ++r) {
         const uint32_t ww[4] = {wv[r][j].x, wv[r][j].y, wv[r][j].z, wv[r][j].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -491,7 +505,7 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemv_fused_kernel(
     }
   }
 #pragma unroll
-  for (int r = 0; r < kGemvRows; ++r) {
+  for (int r = 0; r < kFusedRows; ++r) {
     const int n = n0 + r;
     const float sn = sx * row_scale[n < N ? n : N - 1];
 #pragma unroll
@@ -551,7 +565,7 @@ hipError_t launch_fp8_linear_fused(const uint16_t* x, const uint8_t* w, int M, i
                                    hipStream_t s) {
   if (!fp8_linear_fused_fits(M, K) || !row_scale) return hipErrorInvalidValue;
   if (N <= 0) return hipSuccess;
-  const dim3 g((N + 4 * kGemvRows - 1) / (4 * kGemvRows)), b(4 * kWave);
+  const dim3 g((N + 4 * kFusedRows - 1) / (4 * kFusedRows)), b(4 * kWave);
   if (M == 1) fp8_gemv_fused_kernel<1><<<g, b, 0, s>>>(x, w, M, N, K, row_scale, y, ldy, col0);
   else if (M == 2) fp8_gemv_fused_kernel<2><<<g, b, 0, s>>>(x, w, M, N, K, row_scale, y, ldy, col0);
   else if (M <= 4) fp8_gemv_fused_kernel<4><<<g, b, 0, s>>>(x, w, M, N, K, row_scale, y, ldy, col0);
