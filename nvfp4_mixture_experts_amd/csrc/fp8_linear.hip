@@ -419,22 +419,23 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemv_kernel(
 // block reads all of x, forms s_x and the codes of x itself with the arithmetic of the
 // quantisation kernels (the same bits), keeps the codes in LDS, and multiplies as
 // fp8_gemv_kernel does; its weight loads are issued first, so they travel meanwhile.
-// Each wave takes kFusedRows weight rows (2, not 4: twice the blocks, so more CUs share
-// the stream), and the weights, read once per call, are loaded non-temporally (no cache
-// allocation).  Measured on the 1-token q|k|v projection (K 2048, N 5120): 6.01 us per call
-// with 4 rows and plain loads, 5.59 with 2 rows, 5.65 with non-temporal loads, 5.30 with
-// both (1 row and non-temporal loads: 5.60).
+// Blocks of 8 waves; each wave takes kFusedRows weight rows (2, not 4: twice the waves, so
+// more CUs share the stream), and the weights, read once per call, are loaded
+// non-temporally (no cache allocation).  Measured on the 1-token q|k|v projection (K 2048,
+// N 5120): 6.01 us per call with 4-wave blocks, 4 rows and plain loads; 5.59 with 2 rows,
+// 5.65 with non-temporal loads, 5.30 with both (1 row and non-temporal loads: 5.60); 8-wave
+// blocks (half the blocks reducing x) 5.18 against 5.23.
 constexpr int kFusedRows = 2;
 
 template <int MM>
-__global__ __launch_bounds__(4 * kWave) void fp8_gemv_fused_kernel(
+__global__ __launch_bounds__(8 * kWave) void fp8_gemv_fused_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w, int M, int N, int K,
     const float* __restrict__ row_scale, uint16_t* __restrict__ y, int ldy, int col0) {
-  constexpr int kXP = kSmallQuantMax / 8 / (4 * kWave);  // 16-byte pieces of x per thread
+  constexpr int kXP = kSmallQuantMax / 8 / (8 * kWave);  // 16-byte pieces of x per thread
   __shared__ __align__(16) uint8_t xs[kSmallQuantMax];   // codes of x, [M][K]
-  __shared__ float red[4];
+  __shared__ float red[8];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int n0 = (blockIdx.x * 4 + wave) * kFusedRows;  // may be >= N: the wave still
+  const int n0 = (blockIdx.x * 8 + wave) * kFusedRows;  // may be >= N: the wave still
   const int nch = K / 16;                              // takes part in the barriers
   uint4 wv[kFusedRows][kGemvChunks];
   bool ok[kGemvChunks];
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemv_fused_kernel(
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < kXP; ++i) {
-    const int pc = tid + 4 * kWave * i;
+    const int pc = tid + 8 * kWave * i;
     xp[i] = pc < n8 ? reinterpret_cast<const uint4*>(x)[pc] : make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
@@ -462,11 +463,11 @@ __global__ __launch_bounds__(4 * kWave) void fp8_gemv_fused_kernel(
   m = __int_as_float(static_cast<int>(wave_max_u32(__float_as_uint(m))));
   if (lane == 0) red[wave] = m;
   __syncthreads();
-  const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float mx = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
   const float sx = mx > 0.0f ? __fdiv_rn(mx, 448.0f) : 1.0f;
 #pragma unroll
   for (int i = 0; i < kXP; ++i) {
-    const int pc = tid + 4 * kWave * i;
+    const int pc = tid + 8 * kWave * i;
     if (pc < n8)
       reinterpret_cast<uint2*>(xs)[pc] = make_uint2(quant4(xp[i].x, xp[i].y, sx), quant4(xp[i].z, xp[i].w, sx));
   }
@@ -565,7 +566,7 @@ hipError_t launch_fp8_linear_fused(const uint16_t* x, const uint8_t* w, int M, i
                                    hipStream_t s) {
   if (!fp8_linear_fused_fits(M, K) || !row_scale) return hipErrorInvalidValue;
   if (N <= 0) return hipSuccess;
-  const dim3 g((N + 4 * kFusedRows - 1) / (4 * kFusedRows)), b(4 * kWave);
+  const dim3 g((N + 8 * kFusedRows - 1) / (8 * kFusedRows)), b(8 * kWave);
   if (M == 1) fp8_gemv_fused_kernel<1><<<g, b, 0, s>>>(x, w, M, N, K, row_scale, y, ldy, col0);
   else if (M == 2) fp8_gemv_fused_kernel<2><<<g, b, 0, s>>>(x, w, M, N, K, row_scale, y, ldy, col0);
   else if (M <= 4) fp8_gemv_fused_kernel<4><<<g, b, 0, s>>>(x, w, M, N, K, row_scale, y, ldy, col0);
