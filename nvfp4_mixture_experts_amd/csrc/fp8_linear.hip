@@ -101,7 +101,9 @@ __device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float s) {
 // s_x from the partials (each block recomputes it: every thread loads at most
 // kAmaxMaxBlocks / kAmaxThreads of them, all at once), then the codes of x: n8 16-byte
 // pieces, each stored as one 8-byte word; a thread's first two pieces are loaded
-// before the partials, so they travel while the scale is formed.  |x / s| <= 448 up
+// before the partials, so they travel while the scale is formed.  x is read for the last
+// time here, without cache allocation (at 8192 x 2048: 16.1 -> 13.4 us; the same loads in
+// the amax kernel, whose reads this kernel follows, were slower).  |x / s| <= 448 up
 // to the quotient's rounding; the clamp keeps the convert inside the finite range (it
 // changes no value that rounds to a finite code).
 __global__ __launch_bounds__(kAmaxThreads) void fp8_quantize_kernel(
@@ -111,8 +113,8 @@ __global__ __launch_bounds__(kAmaxThreads) void fp8_quantize_kernel(
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
   const size_t i0 = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-  const uint4 a = i0 < n8 ? x[i0] : zero;
-  const uint4 b = i0 + stride < n8 ? x[i0 + stride] : zero;
+  const uint4 a = i0 < n8 ? ldg16_nt(x + i0) : zero;
+  const uint4 b = i0 + stride < n8 ? ldg16_nt(x + i0 + stride) : zero;
   float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < kAmaxMaxBlocks / kAmaxThreads; ++j) {
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(kAmaxThreads) void fp8_quantize_kernel(
   if (i0 < n8) q[i0] = make_uint2(quant4(a.x, a.y, s), quant4(a.z, a.w, s));
   if (i0 + stride < n8) q[i0 + stride] = make_uint2(quant4(b.x, b.y, s), quant4(b.z, b.w, s));
   for (size_t i = i0 + 2 * stride; i < n8; i += stride) {
-    const uint4 c = x[i];
+    const uint4 c = ldg16_nt(x + i);
     q[i] = make_uint2(quant4(c.x, c.y, s), quant4(c.z, c.w, s));
   }
 }
